@@ -1,0 +1,221 @@
+"""CPU oracle for the paged decode path.
+
+TEST INFRASTRUCTURE ONLY: only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of bench.py may import this package. The product path
+(paged_kv_cache_28_amd) never imports, links or calls anything here, and this
+package imports nothing from it. Inputs come from the ``workloads`` module (random
+draws only).
+
+Contents
+  oracle.c       plain C, IEEE binary64: textbook attention over K/V gathered through
+                 the block table, per-partition results and their merge, the slot-mapped
+                 cache write.  Built with gcc into liboracle.so by ``build()``.
+  allocator.py   Python model of the block pool (FIFO free queue, reference counts).
+
+Parity status: every function here is pinned by tests/test_oracle_*.py against
+something other than itself (the pages' worked examples, closed forms, a library
+routine on the same data, exact brute force on tiny inputs, structural invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from .allocator import PoolError, PoolModel, bytes_per_token  # noqa: F401
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile oracle.c with gcc (OpenMP, no fast-math)."""
+    src = os.path.join(HERE, "oracle.c")
+    tmp = LIB_PATH + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
+                    "-shared", "-fPIC", "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_to_f64.argtypes = [P, P, I64, I32]
+        L.oracle_to_f64.restype = None
+        L.oracle_attend.argtypes = [P, P, P, P, P, P, I64, I32, D]
+        L.oracle_attend.restype = None
+        L.oracle_gather.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I64, I32]
+        L.oracle_gather.restype = ctypes.c_int
+        L.oracle_decode.argtypes = [P, P, I32, P, I64, P, P, P, P, I32, I32, I32, I32, I32,
+                                    I64, D, I32, I32]
+        L.oracle_decode.restype = ctypes.c_int
+        L.oracle_decode_partitions.argtypes = [P, P, P, P, I32, P, I64, P, P, P, P, I32, I32,
+                                               I32, I32, I32, I64, D, I32, I32, I32, I32]
+        L.oracle_decode_partitions.restype = ctypes.c_int
+        L.oracle_merge.argtypes = [P, P, P, P, P, I32, I32, I32]
+        L.oracle_merge.restype = None
+        L.oracle_cache_write.argtypes = [P, P, P, P, P, I32, I32, I32, I64, I64, I64, I32]
+        L.oracle_cache_write.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def raw(x) -> np.ndarray:
+    """torch tensor / numpy array -> numpy array of its raw storage (fp32 as float32,
+    fp16/bf16 as uint16 bit patterns), C-contiguous, on the host."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype in (torch.float16, torch.bfloat16):
+                return x.view(torch.int16).numpy().view(np.uint16)
+            return x.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(x)
+
+
+def to_f64(x, dtype: str) -> np.ndarray:
+    a = raw(x)
+    out = np.empty(a.shape, dtype=np.float64)
+    lib().oracle_to_f64(_ptr(out), _ptr(a), a.size, DTYPE_CODE[dtype])
+    return out
+
+
+def attend(q, K, V, scale: float):
+    """Textbook attention of one fp64 query over contiguous fp64 K/V [n][d].
+    Returns (o[d], m, l)."""
+    q, K, V = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, K, V))
+    n, d = K.shape
+    o = np.empty(d, dtype=np.float64)
+    m, l = ctypes.c_double(), ctypes.c_double()
+    lib().oracle_attend(_ptr(o), ctypes.byref(m), ctypes.byref(l), _ptr(q), _ptr(K), _ptr(V),
+                        n, d, scale)
+    return o, m.value, l.value
+
+
+def gather(k_cache, v_cache, table_row, t0: int, t1: int, g: int, num_kv_heads: int,
+           head_dim: int, dtype: str):
+    """Rows [t0, t1) of KV head g gathered through one block-table row -> fp64 (K, V)."""
+    kc, vc = raw(k_cache), raw(v_cache)
+    tr = np.ascontiguousarray(table_row, dtype=np.int32)
+    K = np.empty((t1 - t0, head_dim), dtype=np.float64)
+    V = np.empty_like(K)
+    nb = kc.shape[0]
+    rc = lib().oracle_gather(_ptr(K), _ptr(V), _ptr(kc), _ptr(vc), _ptr(tr), t0, t1, g,
+                             num_kv_heads, head_dim, nb, DTYPE_CODE[dtype])
+    if rc != 0:
+        raise ValueError("block table points outside the pool")
+    return K, V
+
+
+def _rows_arg(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+    return r, r.shape[0]
+
+
+def decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype: str,
+           rows=None, nthreads: int = 0) -> np.ndarray:
+    """Single-pass paged decode in fp64.
+
+    q [B][Hq][d]; k_cache/v_cache in the documented block layout; block_tables int32
+    [B][max_blocks]; seq_lens int32 [B]. Returns fp64 [B][Hq][d] (rows=None) or
+    [len(rows)][d] for the (b, h) pairs in rows."""
+    qa, kc, vc = raw(q), raw(k_cache), raw(v_cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, Hq, d = qa.shape
+    Hkv = kc.shape[1]
+    r, nr = _rows_arg(rows)
+    out = np.empty((B * Hq if r is None else nr, d), dtype=np.float64)
+    rc = lib().oracle_decode(_ptr(out), None if r is None else _ptr(r), nr, _ptr(qa), Hq * d,
+                             _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Hq, Hkv, d,
+                             bt.shape[1], kc.shape[0], scale, DTYPE_CODE[dtype], nthreads)
+    if rc != 0:
+        raise ValueError("oracle_decode: bad arguments")
+    return out.reshape(B, Hq, d) if r is None else out
+
+
+def decode_partitions(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype: str,
+                      partition_size: int, max_partitions: int, rows=None, nthreads: int = 0):
+    """Per-partition fp64 results (o [R][P][d], m [R][P], l [R][P]), R = B*Hq or len(rows)."""
+    qa, kc, vc = raw(q), raw(k_cache), raw(v_cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, Hq, d = qa.shape
+    Hkv = kc.shape[1]
+    r, nr = _rows_arg(rows)
+    R = B * Hq if r is None else nr
+    o = np.empty((R, max_partitions, d), dtype=np.float64)
+    m = np.empty((R, max_partitions), dtype=np.float64)
+    l = np.empty((R, max_partitions), dtype=np.float64)
+    rc = lib().oracle_decode_partitions(
+        _ptr(o), _ptr(m), _ptr(l), None if r is None else _ptr(r), nr, _ptr(qa), Hq * d,
+        _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Hq, Hkv, d, bt.shape[1], kc.shape[0], scale,
+        DTYPE_CODE[dtype], partition_size, max_partitions, nthreads)
+    if rc != 0:
+        raise ValueError("oracle_decode_partitions: bad arguments")
+    return o, m, l
+
+
+def merge(o, m, l, n_parts) -> np.ndarray:
+    """Merge per-partition results o [R][P][d], m/l [R][P] with n_parts[R] live ones."""
+    o, m, l = (np.ascontiguousarray(a, dtype=np.float64) for a in (o, m, l))
+    npt = np.ascontiguousarray(n_parts, dtype=np.int32)
+    R, P, d = o.shape
+    out = np.empty((R, d), dtype=np.float64)
+    lib().oracle_merge(_ptr(out), _ptr(o), _ptr(m), _ptr(l), _ptr(npt), R, P, d)
+    return out
+
+
+def cache_write(key, value, k_cache: np.ndarray, v_cache: np.ndarray, slot_mapping,
+                dtype: str) -> None:
+    """In-place slot-mapped bit copy of key/value [T][Hkv][d] into host caches
+    (numpy arrays of raw storage in the documented layout)."""
+    ka, va = raw(key), raw(value)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    T, Hkv, d = ka.shape
+    assert k_cache.flags["C_CONTIGUOUS"] and v_cache.flags["C_CONTIGUOUS"]
+    rc = lib().oracle_cache_write(_ptr(ka), _ptr(va), _ptr(k_cache), _ptr(v_cache), _ptr(sm),
+                                  T, Hkv, d, k_cache.shape[0], Hkv * d, Hkv * d,
+                                  DTYPE_CODE[dtype])
+    if rc != 0:
+        raise ValueError("slot outside the pool")
+
+
+def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
+    """Shapes of the K and V caches in the documented layout (x = 16 / element bytes)."""
+    x = 16 // (4 if dtype == "f32" else 2)
+    return ((num_blocks, num_kv_heads, head_dim // x, 16, x),
+            (num_blocks, num_kv_heads, head_dim, 16))
+
+
+def empty_caches(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
+                 fill_nan: bool = True):
+    """Host caches of raw storage, every element NaN (so unwritten slots poison reads)."""
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, dtype)
+    if dtype == "f32":
+        kc = np.full(ks, np.nan if fill_nan else 0, dtype=np.float32)
+        vc = np.full(vs, np.nan if fill_nan else 0, dtype=np.float32)
+    else:
+        nan_bits = 0x7E00 if dtype == "f16" else 0x7FC0
+        kc = np.full(ks, nan_bits if fill_nan else 0, dtype=np.uint16)
+        vc = np.full(vs, nan_bits if fill_nan else 0, dtype=np.uint16)
+    return kc, vc
