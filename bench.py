@@ -1,0 +1,232 @@
+"""Benchmark: one decode step of a Llama-3-8B-shaped batch through the paged KV path.
+
+A step is the whole hot path for one new token of every sequence:
+  host:   allocate_slots for each sequence (kv_pool_append_batch) and the dense block
+          tables (kv_pool_build_tables) into pinned buffers, then their copy to HBM;
+  device: for each of the 32 layers, reshape_and_cache of the new tokens' K/V into
+          that layer's pool, paged_attention_decode over the whole context, and the
+          partition reduce.
+Every layer has its own K/V pool (about 313 MB, more than the 256 MB Infinity Cache),
+so each layer's context streams from HBM. Inputs are synthetic (seeded draws of the
+8B-shaped workload) and resident in HBM before timing starts.
+
+Printed: one JSON line. `value` is KV GB/s over the whole step (algorithmic KV bytes
+read by the decode kernels / step time); `roofline` is the decode kernel alone, timed
+with HIP events on its stream; `cpu_baseline` is the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--config llama8b]
+                       [--partition P] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama8b")
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged decode path has no multi-GPU "
+              "component in this build (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_28_amd as pkv
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.config]
+    P = w.partition_size if args.partition is None else args.partition
+    L, B, Hq, Hkv, d = w.layers, w.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    e = w.elem_bytes
+    tdt = pkv.torch_dtype(w.dtype)
+
+    # ---------------------------------------------------------------- setup
+    lens0 = workloads.draw_seq_lens(w)                 # context at the first step
+    total_steps = args.warmup + args.steps
+    nb = workloads.pool_blocks_for(lens0, growth_tokens=total_steps)
+    order = workloads.draw_free_order(nb, workloads.rng(w.seed, 1))
+    pool = pkv.kv_pool_create(nb, L, Hkv, d, w.dtype, free_order=order)
+    ids = np.arange(B, dtype=np.int64)
+    for b in range(B):
+        pool.add_seq(int(b))
+        pool.append(int(b), int(lens0[b]) - 1)        # the cached prompt
+    max_blocks = int(-(-(int(lens0.max()) + total_steps) // 16))
+    maxp = pkv.max_partitions_for(max_blocks, P) if P > 0 else 0
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    caches = []
+    for _ in range(L):
+        kc, vc = pkv.alloc_caches(nb, Hkv, d, tdt, dev)
+        kc.normal_(generator=g)
+        vc.normal_(generator=g)
+        caches.append((kc, vc))
+    q = [torch.randn((B, Hq, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    k_new = [torch.randn((B, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    v_new = [torch.randn((B, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    out = [torch.empty((B, Hq, d), device=dev, dtype=tdt) for _ in range(L)]
+    parts = pkv.alloc_partials(B, Hq, d, maxp, dev) if P > 0 else None
+
+    # double-buffered pinned metadata; an event guards each buffer's reuse
+    h_tab = [torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    h_len = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    h_slot = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    copied = [torch.cuda.Event() for _ in range(2)]
+    d_tab = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    d_len = torch.empty(B, dtype=torch.int32, device=dev)
+    d_slot = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    kv_bytes_steps = []
+
+    def step(s: int, events=None):
+        k = s & 1
+        copied[k].synchronize()                       # H2D of two steps ago has finished
+        pool.append_batch(ids, out=h_slot[k].numpy())
+        pool.build_tables(ids, max_blocks, h_tab[k].numpy(), h_len[k].numpy())
+        kv_bytes_steps.append(int(h_len[k].numpy().astype(np.int64).sum()) * Hkv * d * 2 * e * L)
+        d_slot.copy_(h_slot[k], non_blocking=True)
+        d_tab.copy_(h_tab[k], non_blocking=True)
+        d_len.copy_(h_len[k], non_blocking=True)
+        copied[k].record(stream)
+        for layer in range(L):
+            kc, vc = caches[layer]
+            pkv.reshape_and_cache(k_new[layer], v_new[layer], kc, vc, d_slot)
+            if events is not None:
+                events[layer][0].record(stream)
+            if P > 0:
+                po, pm, ps = parts
+                pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
+                                           P, po, pm, ps, maxp)
+                if events is not None:
+                    events[layer][1].record(stream)
+                pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P)
+            else:
+                pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale)
+                if events is not None:
+                    events[layer][1].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    kv_bytes_steps.clear()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+          for _ in range(args.steps)]
+    lens_steps = []
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s, ev[s])
+        lens_steps.append(h_len[(args.warmup + s) & 1].numpy().copy())
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+
+    dec_ms = [ev[s][layer][0].elapsed_time(ev[s][layer][1]) for s in range(args.steps)
+              for layer in range(L)]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    kv_total = sum(kv_bytes_steps)
+    # algorithmic bytes of one decode launch: KV once per (seq, KV head), q, out, table rows
+    alg = []
+    for ln in lens_steps:
+        ln = ln.astype(np.int64)
+        alg.append(int(ln.sum()) * Hkv * d * 2 * e + 2 * B * Hq * d * e +
+                   int((-(-ln // 16)).sum()) * 4 + 4 * B)
+    alg_per_launch = sum(alg) / len(alg)
+    achieved = alg_per_launch / dec_avg_s / 1e9
+    value = kv_total / elapsed / 1e9
+    result = {
+        "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + decode tokens/s/layer",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded draws of the workload's shapes and length mix)",
+        "config": {"workload": f"{w.name}-decode", "layers": L, "batch": B, "num_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": d, "block_size": 16,
+                   "seq_len_range": [w.len_lo, w.len_hi], "partition_size": P,
+                   "pool_blocks": nb, "pool_gb_per_layer": round(nb * w.block_bytes_per_layer / 1e9, 3)},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),
+        "decode_kernel_us": round(dec_avg_s * 1e6, 3),
+        "cache_state": f"{L} distinct per-layer pools cycled; warm-up {args.warmup} steps excluded",
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attention_decode",
+                     "alg_bytes_per_launch": int(alg_per_launch)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, caches[0], q[0], d_tab, d_len, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, cache0, q0, d_tab, d_len, budget_s: float):
+    """The CPU oracle (fp64, as it stands) on a bounded sample of layer 0: the first
+    sequences of the batch, as many as fit the time budget."""
+    import numpy as np
+
+    import oracle
+
+    kc, vc = cache0
+    kc_h, vc_h = oracle.raw(kc), oracle.raw(vc)
+    q_h = oracle.raw(q0)
+    tab = d_tab.cpu().numpy()
+    lens = d_len.cpu().numpy()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    cores = min(cores, 64)
+
+    def run(nseq):
+        t = time.perf_counter()
+        oracle.decode(q_h[:nseq], kc_h, vc_h, tab[:nseq], lens[:nseq], w.scale, w.dtype,
+                      nthreads=cores)
+        return time.perf_counter() - t
+
+    t_one = run(1)
+    per_seq = max(t_one, 1e-3)
+    nseq = int(max(1, min(len(lens), budget_s / per_seq)))
+    t = run(nseq)
+    kv = int(lens[:nseq].astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
+    return {"value": round(kv / t / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "tok_s_per_layer": round(nseq / t, 2), "seconds": round(t, 2),
+            "sample": f"layer 0, sequences 0..{nseq - 1} of {len(lens)} "
+                      f"({int(lens[:nseq].sum())} context tokens), fp64 oracle, {cores} threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,251 @@
+/*
+ * pkv.h - C ABI of the paged KV cache decode library (libpkv.so) for AMD MI355X (gfx950).
+ *
+ * The library implements the decode hot path of PagedAttention:
+ *   - a host-side block pool: fixed 16-token KV blocks, a per-sequence block table,
+ *     on-demand allocation, a free queue and reference-counted sharing
+ *     ("vLLM ve Triton ile maliyet optimizasyonu", §03 Yöntem, steps 1-3 and the
+ *     paragraph on sharing; "vLLM Nedir? PagedAttention ile Production LLM Serving",
+ *     sections "PagedAttention" and "Bir istek motorun içinde");
+ *   - reshape_and_cache: the slot-mapped write of each new token's K/V;
+ *   - paged_attention_decode: single-query attention of a batch of sequences whose
+ *     K/V are gathered through their block tables, with grouped-query attention;
+ *   - paged_attention_reduce: the merge of per-partition results when the context
+ *     is split into partitions.
+ *
+ * General rules
+ *   - Every function returns PKV_OK (0) or a negative PKV_E* code; pkv_last_error()
+ *     returns a thread-local message for the last failure on the calling thread.
+ *   - Device pointers are borrowed: the library never allocates, frees, copies or
+ *     synchronises device memory. Kernels are enqueued on the caller's HIP stream
+ *     (hipStream_t passed as void*; NULL = the null stream) and run asynchronously.
+ *   - All host-side validation happens before any launch: an error return means
+ *     nothing was enqueued. Values that live in device memory (slots, block ids,
+ *     sequence lengths) are preconditions; the kernels never read or write outside
+ *     the buffers whose sizes the arguments describe, but the results of rows that
+ *     break a precondition are unspecified.
+ *   - The pool object is not thread-safe; use one per thread or lock around it.
+ *
+ * Cache layout (per layer; the pages do not fix one). x = 16 / element_bytes,
+ * i.e. 8 for fp16/bf16 and 4 for fp32:
+ *   k_cache: [num_blocks][num_kv_heads][head_dim / x][16][x]
+ *   v_cache: [num_blocks][num_kv_heads][head_dim][16]
+ * Token t of a sequence lives in physical block table[t / 16], row t % 16. One
+ * (block, KV head) tile of K or V is one contiguous run of 16 * head_dim elements;
+ * K keeps 16-byte groups of x dimensions per token together, V keeps the 16 tokens
+ * of each dimension together. Both match the operand layout of the gfx950 matrix
+ * instructions, so the decode kernel loads tiles straight into registers.
+ * A slot is physical_block * 16 + row.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------- */
+#define PKV_OK 0
+#define PKV_EINVAL (-1)  /* bad argument: null, shape, stride, alignment, range      */
+#define PKV_ENOTSUP (-2) /* valid request that this build does not implement          */
+#define PKV_ENOMEM (-3)  /* block pool exhausted (the call changed nothing)           */
+#define PKV_ENOENT (-4)  /* unknown sequence id                                       */
+#define PKV_EHIP (-5)    /* the HIP runtime reported an error at launch               */
+
+/* ---- element types ----------------------------------------------------------- */
+#define PKV_F32 0
+#define PKV_F16 1
+#define PKV_BF16 2
+
+#define PKV_BLOCK_SIZE 16
+
+/* Message for the last failing call on this thread ("" if none). Owned by the
+ * library; valid until the next call on this thread. */
+const char* pkv_last_error(void);
+
+/* Library version string, e.g. "pkv 0.1.0 gfx950". */
+const char* pkv_version(void);
+
+/* ---- KV bytes per token ------------------------------------------------------------
+ * 2 (K and V) x layers x KV heads x head_dim x bytes per element
+ * ("Yerel LLM sistemlerinde backpressure ve ölçekleme", section "KV bütçesi": the
+ * formula, with 327,680 bytes for an 80-layer, 8-KV-head, head_dim 128 FP16 model;
+ * "vLLM Nedir? ...", section "Asıl şişen şey ağırlık değil, KV cache": about 128 KB
+ * for 32 layers). Returns -1 for a bad argument. */
+int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t dtype);
+
+/* ==== host block pool ========================================================= */
+
+typedef struct kv_pool kv_pool;
+
+typedef struct {
+    int64_t total_blocks;   /* num_blocks                                     */
+    int64_t free_blocks;    /* blocks in the free queue                       */
+    int64_t used_blocks;    /* blocks with reference count >= 1              */
+    int64_t shared_blocks;  /* blocks with reference count >= 2              */
+    int64_t alloc_failures; /* appends refused with PKV_ENOMEM so far         */
+    int64_t num_seqs;       /* live sequences                                 */
+} kv_pool_stats_t;
+
+/* Create a pool of num_blocks physical blocks of block_size (must be 16) tokens for
+ * a model with num_layers layers, num_kv_heads KV heads of head_dim elements of
+ * type dtype. One block id addresses the same block in every layer's cache.
+ *   free_order: NULL for 0, 1, ..., num_blocks-1, else a permutation of those ids
+ *               (copied) giving the initial order of the free queue.
+ * The pool holds no device memory: the caller reserves the caches up front (for
+ * each layer one K and one V buffer of kv_pool_cache_shape() elements), which is
+ * the one-time reservation of "Yerel LLM ...", section "3. VRAM fragmantasyonu".
+ * Errors: EINVAL (sizes, block_size != 16, dtype, not a permutation). */
+int kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t num_layers,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                   const int32_t* free_order, kv_pool** out);
+
+/* Free the host state. NULL is a no-op. */
+void kv_pool_destroy(kv_pool* pool);
+
+/* kv_bytes_per_token() of the pool's model shape. */
+int64_t kv_pool_bytes_per_token(const kv_pool* pool);
+
+/* Shapes (in elements) of one layer's K and V cache in the layout above. */
+int kv_pool_cache_shape(const kv_pool* pool, int64_t k_shape[5], int64_t v_shape[4]);
+
+/* Register a new, empty sequence. EINVAL if seq_id is already live. */
+int kv_pool_add_seq(kv_pool* pool, int64_t seq_id);
+
+/* Make empty sequence seq_id start with the first n_tokens tokens of src_seq_id by
+ * pointing its table at the same physical blocks (reference count + 1 each), as for
+ * a shared system prompt or parallel samples ("vLLM Nedir? ...", section
+ * "PagedAttention", on block sharing; §03 on sharing). n_tokens must be a multiple
+ * of 16 and at most src's length, so a shared block is full and never written again
+ * (copy-on-write of partly filled shared blocks is not provided).
+ * Errors: ENOENT (unknown id), EINVAL (seq not empty, n_tokens not allowed). */
+int kv_pool_share_prefix(kv_pool* pool, int64_t seq_id, int64_t src_seq_id, int32_t n_tokens);
+
+/* allocate_slots: reserve n_tokens new positions at the end of seq_id and write
+ * their slot ids to slot_mapping_out[0..n_tokens). A new physical block is popped
+ * from the front of the free queue only when the sequence's last block is full
+ * (§03 step 3; 17 new tokens in 16-token blocks take 2 blocks: "vLLM Nedir? ...",
+ * section "Bir istek motorun içinde", step 2). If the free queue is too short the
+ * call returns ENOMEM and changes nothing, so the caller can free (preempt) other
+ * sequences and retry. Errors: ENOENT, EINVAL (n_tokens < 0, null output). */
+int kv_pool_append(kv_pool* pool, int64_t seq_id, int32_t n_tokens, int32_t* slot_mapping_out);
+
+/* Decode step: one new position for each of the n distinct sequences in seq_ids;
+ * slot_mapping_out[i] is the slot of seq_ids[i]. All or nothing: ENOMEM leaves
+ * every sequence unchanged. Errors: ENOENT, EINVAL (duplicate ids, nulls). */
+int kv_pool_append_batch(kv_pool* pool, const int64_t* seq_ids, int32_t n,
+                         int32_t* slot_mapping_out);
+
+/* Release seq_id: each of its blocks loses one reference; blocks that reach zero
+ * are pushed to the back of the free queue in table order ("vLLM Nedir? ...",
+ * section "Bir istek motorun içinde", step 5). Errors: ENOENT. */
+int kv_pool_free_seq(kv_pool* pool, int64_t seq_id);
+
+/* Length (tokens) of seq_id. Errors: ENOENT, EINVAL. */
+int kv_pool_seq_len(const kv_pool* pool, int64_t seq_id, int64_t* len_out);
+
+/* Copy seq_id's block table (at most capacity entries) to blocks_out; *n_out gets
+ * the table length. Errors: ENOENT, EINVAL (capacity too small). */
+int kv_pool_seq_blocks(const kv_pool* pool, int64_t seq_id, int32_t* blocks_out,
+                       int32_t capacity, int32_t* n_out);
+
+/* Copy the free queue, front first (at most capacity entries); *n_out gets its
+ * length. Errors: EINVAL (capacity too small). */
+int kv_pool_free_queue(const kv_pool* pool, int32_t* blocks_out, int64_t capacity,
+                       int64_t* n_out);
+
+/* Reference count of block blk (0 for a free block). Errors: EINVAL. */
+int kv_pool_refcount(const kv_pool* pool, int64_t blk, int32_t* ref_out);
+
+/* Dense block tables for the n sequences in seq_ids: tables_out is int32
+ * [n][max_blocks], row i holding seq_ids[i]'s physical blocks then -1 padding;
+ * seq_lens_out[i] is its length. Host memory (pinned or not).
+ * Errors: ENOENT, EINVAL (a table longer than max_blocks, nulls). */
+int kv_pool_build_tables(const kv_pool* pool, const int64_t* seq_ids, int32_t n,
+                         int32_t max_blocks, int32_t* tables_out, int32_t* seq_lens_out);
+
+/* Counters of the pool. */
+int kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
+
+/* ==== device kernels ========================================================== */
+
+/* reshape_and_cache: for every token t in [0, num_tokens) with s = slot_mapping[t]
+ * in [0, num_blocks * 16), copy the raw bits of key[t][g][:] and value[t][g][:] for
+ * every KV head g into row s % 16 of block s / 16 of k_cache / v_cache (layout
+ * above). Tokens with a negative slot are skipped. Nothing else is written. This is
+ * how a new token's K/V enter the block that on-demand allocation gave it (§03
+ * step 3). Duplicate slots in one call are a caller error (which write wins is
+ * unspecified); slots at or past num_blocks * 16 are ignored.
+ *   key, value:   device, dtype, element (t, g, i) at t * key_stride + g * head_dim + i
+ *                 (resp. value_stride); 16-byte aligned, strides multiples of x.
+ *   slot_mapping: device int32 [num_tokens].
+ *   dtype: PKV_F32, PKV_F16 or PKV_BF16 (a bit copy: the type only sets the size).
+ * Errors: EINVAL (nulls, alignment, block_size != 16, head_dim not a positive
+ * multiple of x, sizes), EHIP. num_tokens == 0 is a no-op. */
+int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                      int64_t key_stride, int64_t value_stride, int32_t dtype, void* stream);
+
+/* paged_attention_decode: for each sequence b with context length n = seq_lens[b]
+ * and query head h (KV head g = h / (num_heads / num_kv_heads), contiguous groups):
+ *     s_t = scale * q[b][h] . K_b[t],  t < n,  K_b[t] read through block_tables[b]
+ *     out[b][h] = sum_t softmax(s)_t V_b[t]
+ * i.e. scaled dot-product attention with K/V gathered from scattered blocks (§03,
+ * closing paragraphs: the math is unchanged, only the place K and V are read from
+ * changes). Softmax is accumulated online in fp32; n counts the token being
+ * decoded (write it with reshape_and_cache first). n == 0 gives a zero row.
+ *
+ *   q:            device [num_seqs][num_heads][head_dim], in_dtype; sequence stride
+ *                 q_stride elements (>= num_heads * head_dim, multiple of x).
+ *   k_cache/v_cache: device, layout above, num_blocks blocks, in_dtype.
+ *   block_tables: device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(n / 16) are not read. seq_lens: device int32 [num_seqs].
+ *   out:          device [num_seqs][num_heads][head_dim], out_dtype (in_dtype or
+ *                 PKV_F32), written with round-to-nearest-even.
+ *   partition_size == 0: one pass over the whole context; part_* may be NULL.
+ *   partition_size  > 0 (a multiple of 16): the context is cut into partitions of
+ *                 partition_size tokens and one workgroup handles each (sequence,
+ *                 KV head, partition). A sequence with a single partition writes out
+ *                 directly; otherwise each partition p < ceil(n / partition_size)
+ *                 writes, for every query head of the group,
+ *                   part_out[b][h][p][:] = attention restricted to the partition (fp32),
+ *                   part_max[b][h][p]    = max of its s_t (natural-log units),
+ *                   part_sum[b][h][p]    = sum of exp(s_t - part_max),
+ *                 and paged_attention_reduce() produces out for those rows.
+ *                 Requires part_* non-null and max_partitions >=
+ *                 ceil(max_blocks_per_seq * 16 / partition_size).
+ * Supported: head_dim in {64, 128}; in_dtype F16/BF16 with num_heads/num_kv_heads
+ * <= 16; in_dtype F32 with num_heads/num_kv_heads <= 8.
+ * Errors: EINVAL (nulls, alignment, num_heads % num_kv_heads, block_size != 16,
+ * partition arguments, sizes), ENOTSUP (head_dim, group size, dtype pair), EHIP.
+ * num_seqs == 0 is a no-op. */
+int paged_attention_decode(void* out, float* part_out, float* part_max, float* part_sum,
+                           const void* q, int64_t q_stride, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                           int32_t partition_size, int32_t max_partitions, int32_t in_dtype,
+                           int32_t out_dtype, void* stream);
+
+/* paged_attention_reduce: for every (b, h) whose sequence has more than one
+ * partition (np = ceil(seq_lens[b] / partition_size) > 1):
+ *     M = max_p part_max,  w_p = exp(part_max[p] - M) * part_sum[p],
+ *     out[b][h] = sum_p w_p part_out[p] / sum_p w_p        (p < np only)
+ * Rows with np <= 1 are not touched (the decode kernel wrote them). Buffers are
+ * those of paged_attention_decode with the same partition_size/max_partitions;
+ * out_dtype in {F32, F16, BF16}. Errors: EINVAL, ENOTSUP, EHIP. */
+int paged_attention_reduce(void* out, const float* part_out, const float* part_max,
+                           const float* part_sum, const int32_t* seq_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t head_dim, int32_t partition_size,
+                           int32_t max_partitions, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,358 @@
+"""Python binding of libpkv.so: paged KV cache decode for AMD MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI declared in include/pkv.h; every step of the
+path runs in the library (host block pool in C++, kernels in HIP). PyTorch supplies
+device memory and the current HIP stream only. The functions keep the C names:
+
+  kv_pool_create(...)            -> KVPool (host block pool: allocate_slots, tables)
+  kv_bytes_per_token(...)
+  reshape_and_cache(...)         slot-mapped write of new tokens' K/V
+  paged_attention_decode(...)    GQA decode attention through block tables
+  paged_attention_reduce(...)    merge of per-partition results
+
+There is no fallback: if libpkv.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_ENOTSUP, PKV_ENOMEM, PKV_ENOENT, PKV_EHIP = 0, -1, -2, -3, -4, -5
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+BLOCK_SIZE = 16
+_CODE_NAMES = {PKV_EINVAL: "EINVAL", PKV_ENOTSUP: "ENOTSUP", PKV_ENOMEM: "ENOMEM",
+               PKV_ENOENT: "ENOENT", PKV_EHIP: "EHIP"}
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODE_NAMES.get(code, code)}: {msg}")
+        self.code = code
+        self.name = _CODE_NAMES.get(code, str(code))
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("total_blocks", "free_blocks", "used_blocks",
+                                              "shared_blocks", "alloc_failures", "num_seqs")]
+
+
+def lib():
+    """Load libpkv.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "pkv_last_error": ([], ctypes.c_char_p),
+        "pkv_version": ([], ctypes.c_char_p),
+        "kv_bytes_per_token": ([I32, I32, I32, I32], I64),
+        "kv_pool_create": ([I64, I32, I32, I32, I32, I32, P, PP], ctypes.c_int),
+        "kv_pool_destroy": ([P], None),
+        "kv_pool_bytes_per_token": ([P], I64),
+        "kv_pool_cache_shape": ([P, P, P], ctypes.c_int),
+        "kv_pool_add_seq": ([P, I64], ctypes.c_int),
+        "kv_pool_share_prefix": ([P, I64, I64, I32], ctypes.c_int),
+        "kv_pool_append": ([P, I64, I32, P], ctypes.c_int),
+        "kv_pool_append_batch": ([P, P, I32, P], ctypes.c_int),
+        "kv_pool_free_seq": ([P, I64], ctypes.c_int),
+        "kv_pool_seq_len": ([P, I64, P], ctypes.c_int),
+        "kv_pool_seq_blocks": ([P, I64, P, I32, P], ctypes.c_int),
+        "kv_pool_free_queue": ([P, P, I64, P], ctypes.c_int),
+        "kv_pool_refcount": ([P, I64, P], ctypes.c_int),
+        "kv_pool_build_tables": ([P, P, I32, I32, P, P], ctypes.c_int),
+        "kv_pool_stats": ([P, P], ctypes.c_int),
+        "reshape_and_cache": ([P, P, P, P, P, I32, I32, I32, I32, I64, I64, I64, I32, P],
+                              ctypes.c_int),
+        "paged_attention_decode": ([P, P, P, P, P, I64, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                    I64, F, I32, I32, I32, I32, P], ctypes.c_int),
+        "paged_attention_reduce": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, P],
+                                   ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_create",
+            "kv_pool_destroy", "kv_pool_bytes_per_token", "kv_pool_cache_shape",
+            "kv_pool_add_seq", "kv_pool_share_prefix", "kv_pool_append", "kv_pool_append_batch",
+            "kv_pool_free_seq", "kv_pool_seq_len", "kv_pool_seq_blocks", "kv_pool_free_queue",
+            "kv_pool_refcount", "kv_pool_build_tables", "kv_pool_stats", "reshape_and_cache",
+            "paged_attention_decode", "paged_attention_reduce")
+
+
+def _check(rc: int):
+    if rc != PKV_OK:
+        raise PkvError(rc, lib().pkv_last_error().decode())
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+# ------------------------------------------------------------------ dtypes / torch
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dt) -> int:
+    torch = _torch()
+    m = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+         "f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16}
+    if dt not in m:
+        raise ValueError(f"unsupported dtype {dt}")
+    return m[dt]
+
+
+def torch_dtype(code_or_name):
+    torch = _torch()
+    return {PKV_F32: torch.float32, PKV_F16: torch.float16, PKV_BF16: torch.bfloat16,
+            "f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[code_or_name]
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype) -> int:
+    v = lib().kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype_code(dtype))
+    if v < 0:
+        _check(PKV_EINVAL)
+    return v
+
+
+def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype):
+    """(k_shape, v_shape) of one layer's caches: [nb][Hkv][d/x][16][x], [nb][Hkv][d][16]."""
+    x = 16 // (4 if dtype_code(dtype) == PKV_F32 else 2)
+    return ((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x),
+            (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE))
+
+
+def alloc_caches(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda",
+                 fill=None):
+    """Allocate one layer's (k_cache, v_cache) through PyTorch (uninitialised, or filled)."""
+    torch = _torch()
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, dtype)
+    td = torch_dtype(dtype) if not isinstance(dtype, torch.dtype) else dtype
+    kc = torch.empty(ks, dtype=td, device=device)
+    vc = torch.empty(vs, dtype=td, device=device)
+    if fill is not None:
+        kc.fill_(fill)
+        vc.fill_(fill)
+    return kc, vc
+
+
+# --------------------------------------------------------------------- block pool
+class KVPool:
+    """Host block pool (C++). seq ids are arbitrary 64-bit integers."""
+
+    def __init__(self, num_blocks: int, num_layers: int, num_kv_heads: int, head_dim: int,
+                 dtype, free_order=None, block_size: int = BLOCK_SIZE):
+        import numpy as np
+        self._np = np
+        h = ctypes.c_void_p()
+        fo = None
+        if free_order is not None:
+            self._order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if self._order.shape != (num_blocks,):
+                raise ValueError("free_order must have num_blocks entries")
+            fo = self._order.ctypes.data_as(ctypes.c_void_p)
+        _check(lib().kv_pool_create(num_blocks, block_size, num_layers, num_kv_heads, head_dim,
+                                    dtype_code(dtype), fo, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
+        self.dtype = dtype
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().kv_pool_destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def bytes_per_token(self) -> int:
+        return lib().kv_pool_bytes_per_token(self._h)
+
+    def cache_shape(self):
+        ks = (ctypes.c_int64 * 5)()
+        vs = (ctypes.c_int64 * 4)()
+        _check(lib().kv_pool_cache_shape(self._h, ks, vs))
+        return tuple(ks), tuple(vs)
+
+    def add_seq(self, seq_id: int):
+        _check(lib().kv_pool_add_seq(self._h, seq_id))
+
+    def share_prefix(self, seq_id: int, src_seq_id: int, n_tokens: int):
+        _check(lib().kv_pool_share_prefix(self._h, seq_id, src_seq_id, n_tokens))
+
+    def append(self, seq_id: int, n_tokens: int, out=None):
+        """allocate_slots for n_tokens new tokens; returns int32 slot ids (numpy)."""
+        np = self._np
+        slots = np.empty(max(n_tokens, 0), dtype=np.int32) if out is None else out
+        _check(lib().kv_pool_append(self._h, seq_id, n_tokens,
+                                    slots.ctypes.data_as(ctypes.c_void_p)))
+        return slots
+
+    def append_batch(self, seq_ids, out=None):
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        slots = np.empty(len(ids), dtype=np.int32) if out is None else out
+        _check(lib().kv_pool_append_batch(self._h, ids.ctypes.data_as(ctypes.c_void_p),
+                                          len(ids), slots.ctypes.data_as(ctypes.c_void_p)))
+        return slots
+
+    def free_seq(self, seq_id: int):
+        _check(lib().kv_pool_free_seq(self._h, seq_id))
+
+    def seq_len(self, seq_id: int) -> int:
+        v = ctypes.c_int64()
+        _check(lib().kv_pool_seq_len(self._h, seq_id, ctypes.byref(v)))
+        return v.value
+
+    def seq_blocks(self, seq_id: int):
+        np = self._np
+        n = ctypes.c_int32()
+        cap = self.num_blocks
+        buf = np.empty(cap, dtype=np.int32)
+        _check(lib().kv_pool_seq_blocks(self._h, seq_id, buf.ctypes.data_as(ctypes.c_void_p),
+                                        cap, ctypes.byref(n)))
+        return buf[:n.value].tolist()
+
+    def free_queue(self):
+        np = self._np
+        n = ctypes.c_int64()
+        buf = np.empty(self.num_blocks, dtype=np.int32)
+        _check(lib().kv_pool_free_queue(self._h, buf.ctypes.data_as(ctypes.c_void_p),
+                                        self.num_blocks, ctypes.byref(n)))
+        return buf[:n.value].tolist()
+
+    def refcount(self, blk: int) -> int:
+        v = ctypes.c_int32()
+        _check(lib().kv_pool_refcount(self._h, blk, ctypes.byref(v)))
+        return v.value
+
+    def build_tables(self, seq_ids, max_blocks: int, tables_out=None, lens_out=None):
+        """Dense int32 [n][max_blocks] tables (-1 padded) and int32 lengths, on the host
+        (pass pinned numpy/torch-backed buffers to fill them in place)."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        t = np.empty((len(ids), max_blocks), dtype=np.int32) if tables_out is None else tables_out
+        l = np.empty(len(ids), dtype=np.int32) if lens_out is None else lens_out
+        _check(lib().kv_pool_build_tables(self._h, ids.ctypes.data_as(ctypes.c_void_p), len(ids),
+                                          max_blocks, t.ctypes.data_as(ctypes.c_void_p),
+                                          l.ctypes.data_as(ctypes.c_void_p)))
+        return t, l
+
+    def stats(self) -> dict:
+        s = _Stats()
+        _check(lib().kv_pool_stats(self._h, ctypes.byref(s)))
+        return {"total": s.total_blocks, "free": s.free_blocks, "used": s.used_blocks,
+                "shared": s.shared_blocks, "alloc_failures": s.alloc_failures,
+                "num_seqs": s.num_seqs}
+
+
+def kv_pool_create(num_blocks, num_layers, num_kv_heads, head_dim, dtype, free_order=None,
+                   block_size=BLOCK_SIZE) -> KVPool:
+    return KVPool(num_blocks, num_layers, num_kv_heads, head_dim, dtype, free_order, block_size)
+
+
+# ------------------------------------------------------------------------ kernels
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
+    """key/value: device [T][Hkv][d] (token stride free, head/dim dense); caches in the
+    documented layout; slot_mapping: device int32 [T]."""
+    T, hkv, d = key.shape
+    for t, nm in ((key, "key"), (value, "value")):
+        if t.dim() != 3 or t.shape != key.shape or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{nm} must be [T][Hkv][d] with dense heads/dims")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    if slot_mapping.numel() < T:
+        raise ValueError("slot_mapping shorter than the token count")
+    _check(lib().reshape_and_cache(
+        _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, BLOCK_SIZE,
+        k_cache.shape[0], key.stride(0), value.stride(0), dtype_code(key.dtype),
+        _stream(key, stream)))
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                           partition_size: int = 0, part_out=None, part_max=None, part_sum=None,
+                           max_partitions: int = 0, num_kv_heads: int | None = None,
+                           stream=None):
+    """out/q: device [B][Hq][d] (q's sequence stride is free); block_tables int32
+    [B][max_blocks]; seq_lens int32 [B]. With partition_size > 0 pass the fp32
+    partial buffers part_out [B][Hq][P][d], part_max/part_sum [B][Hq][P]."""
+    B, Hq, d = q.shape
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must have dense heads/dims")
+    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
+    if not (block_tables.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("block_tables and seq_lens must be contiguous")
+    hkv = k_cache.shape[1] if num_kv_heads is None else num_kv_heads
+    _check(lib().paged_attention_decode(
+        _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
+        _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
+        B, Hq, hkv, d, BLOCK_SIZE, block_tables.shape[1], k_cache.shape[0], float(scale),
+        partition_size, max_partitions, dtype_code(q.dtype), dtype_code(out.dtype),
+        _stream(q, stream)))
+
+
+def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partition_size: int,
+                           stream=None):
+    B, Hq, d = out.shape
+    P = part_out.shape[2]
+    _check(lib().paged_attention_reduce(
+        _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
+        _dev(part_sum, "part_sum"), _dev(seq_lens, "seq_lens"), B, Hq, d, partition_size, P,
+        dtype_code(out.dtype), _stream(out, stream)))
+
+
+def max_partitions_for(max_blocks: int, partition_size: int) -> int:
+    return -(-max_blocks * BLOCK_SIZE // partition_size)
+
+
+def alloc_partials(B: int, Hq: int, d: int, max_partitions: int, device="cuda"):
+    torch = _torch()
+    return (torch.empty((B, Hq, max_partitions, d), dtype=torch.float32, device=device),
+            torch.empty((B, Hq, max_partitions), dtype=torch.float32, device=device),
+            torch.empty((B, Hq, max_partitions), dtype=torch.float32, device=device))
+
+
+def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+           partition_size: int = 0, partials=None, stream=None):
+    """Decode + (if partitioned) reduce, the two launches of one layer's attention."""
+    if partition_size > 0:
+        po, pm, ps = partials
+        paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
+                               partition_size, po, pm, ps, po.shape[2], stream=stream)
+        paged_attention_reduce(out, po, pm, ps, seq_lens, partition_size, stream=stream)
+    else:
+        paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
+                               stream=stream)

@@ -1,0 +1,99 @@
+// reshape_and_cache: place each new token's K and V rows in the slot the block pool
+// gave it. A new token goes into the sequence's current block, a fresh block being
+// taken only when the last one is full ("vLLM ve Triton ile maliyet optimizasyonu",
+// §03 Yöntem, step 3); this kernel is the device half of that step.
+//
+// One thread moves one 16-byte group of x = 16 / element_bytes dimensions of one
+// (token, KV head): K keeps the group together (cache layout [blk][g][d/x][16][x]),
+// V spreads it over x rows of its [blk][g][d][16] tile. A pure bit copy.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "status.hpp"
+
+namespace pkv {
+
+template <int E>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, char* __restrict__ kc,
+    char* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens, int32_t hkv,
+    int32_t d, int64_t num_blocks, int64_t key_stride_b, int64_t value_stride_b) {
+    constexpr int X = 16 / E;
+    const int nchunk = d / X;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = int64_t(num_tokens) * hkv * nchunk;
+    if (idx >= total) return;
+    const int c = int(idx % nchunk);
+    const int g = int((idx / nchunk) % hkv);
+    const int64_t t = idx / (int64_t(nchunk) * hkv);
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_blocks * 16) return;
+    const int64_t blk = slot >> 4;
+    const int off = int(slot & 15);
+    const int64_t src_k = t * key_stride_b + (int64_t(g) * d + int64_t(c) * X) * E;
+    const int64_t src_v = t * value_stride_b + (int64_t(g) * d + int64_t(c) * X) * E;
+    const uint4 kv = *reinterpret_cast<const uint4*>(key + src_k);
+    const uint4 vv = *reinterpret_cast<const uint4*>(value + src_v);
+    const int64_t tile = blk * hkv + g;
+    *reinterpret_cast<uint4*>(kc + ((tile * nchunk + c) * 16 + off) * 16) = kv;
+    // V: element k of the group is dimension c*X + k, row `off` of that dimension
+    char* vdst = vc + ((tile * d + int64_t(c) * X) * 16 + off) * E;
+    if constexpr (E == 2) {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(&vv);
+#pragma unroll
+        for (int k = 0; k < X; ++k) reinterpret_cast<uint16_t*>(vdst + k * 16 * E)[0] = h[k];
+    } else {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&vv);
+#pragma unroll
+        for (int k = 0; k < X; ++k) reinterpret_cast<uint32_t*>(vdst + k * 16 * E)[0] = w[k];
+    }
+}
+
+}  // namespace pkv
+
+extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                 void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, int64_t key_stride, int64_t value_stride,
+                                 int32_t dtype, void* stream) {
+    using pkv::fail;
+    const int e = pkv::elem_bytes(dtype);
+    if (e == 0) return fail(PKV_EINVAL, "reshape_and_cache: unknown dtype %d", dtype);
+    if (num_tokens < 0) return fail(PKV_EINVAL, "reshape_and_cache: negative num_tokens");
+    if (block_size != PKV_BLOCK_SIZE)
+        return fail(PKV_EINVAL, "reshape_and_cache: block_size must be 16, got %d", block_size);
+    const int x = 16 / e;
+    if (num_kv_heads <= 0 || head_dim <= 0 || head_dim % x != 0 || num_blocks <= 0)
+        return fail(PKV_EINVAL, "reshape_and_cache: bad shape (Hkv %d, head_dim %d, blocks %lld)",
+                    num_kv_heads, head_dim, (long long)num_blocks);
+    if (key_stride < int64_t(num_kv_heads) * head_dim ||
+        value_stride < int64_t(num_kv_heads) * head_dim || key_stride % x || value_stride % x)
+        return fail(PKV_EINVAL, "reshape_and_cache: token strides must cover Hkv*head_dim and be "
+                                "multiples of %d elements", x);
+    if (num_tokens == 0) return pkv::ok();
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+        return fail(PKV_EINVAL, "reshape_and_cache: NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) |
+         reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
+        return fail(PKV_EINVAL, "reshape_and_cache: buffers must be 16-byte aligned");
+    const int64_t total = int64_t(num_tokens) * num_kv_heads * (head_dim / x);
+    const int64_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffff) return fail(PKV_EINVAL, "reshape_and_cache: too many tokens");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const char* kp = static_cast<const char*>(key);
+    const char* vp = static_cast<const char*>(value);
+    char* kcp = static_cast<char*>(k_cache);
+    char* vcp = static_cast<char*>(v_cache);
+    if (e == 2)
+        hipLaunchKernelGGL(pkv::reshape_and_cache_kernel<2>, dim3(unsigned(grid)), dim3(256), 0, s,
+                           kp, vp, kcp, vcp, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                           num_blocks, key_stride * 2, value_stride * 2);
+    else
+        hipLaunchKernelGGL(pkv::reshape_and_cache_kernel<4>, dim3(unsigned(grid)), dim3(256), 0, s,
+                           kp, vp, kcp, vcp, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                           num_blocks, key_stride * 4, value_stride * 4);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return fail(PKV_EHIP, "reshape_and_cache: launch failed: %s", hipGetErrorString(err));
+    return pkv::ok();
+}

@@ -1,0 +1,466 @@
+// paged_attention_decode: single-query attention for a batch of sequences whose K/V
+// live in scattered 16-token blocks reached through per-sequence block tables.
+//
+// The attention math is ordinary scaled dot-product attention; paging only changes
+// where K and V are read from ("vLLM ve Triton ile maliyet optimizasyonu", §03 Yöntem,
+// closing paragraphs; the block table is step 2 there). Grouped-query attention lets
+// the query heads of a group share one KV head ("Yerel LLM sistemlerinde backpressure
+// ve ölçekleme", section "KV bütçesi"), so every KV tile is loaded once and used for
+// all G = Hq / Hkv query heads of its group.
+//
+// Work decomposition: one workgroup per (context partition, KV head, sequence); its
+// W waves take the partition's blocks round-robin, each keeping its own online
+// softmax state, and merge through LDS at the end. A sequence with one partition
+// writes its output; otherwise the partition writes (o_p, m_p, l_p) for the reduce.
+//
+// fp16/bf16 path, one wave per block of 16 tokens (matrix instructions, wave64):
+//   S^T[16 tokens][16 cols] = K_tile[16][d] x Q^T[d][16 cols]   (16x16x32, d/32 steps)
+//      A = K tile: lane l holds token l%16, dims 32c + 8(l/16) .. +7. In the cache
+//          layout [d/8][16][8] that is the 16 bytes at (64c + l) * 16: each step
+//          reads 1 KiB contiguous.
+//      B = Q^T: lane l holds query head l%16 of the group (zero past G), same dims.
+//      C: lane l holds head l%16 for tokens 4(l/16) + e, e = 0..3.
+//   online softmax on those 4 values (cross-lane max over lanes l^16, l^32, which
+//   hold the other tokens of the same head);
+//   O^T[d][16 cols] += V^T[d][16 tokens] x P^T[16 tokens][16 cols]  (16x16x16, d/16)
+//      A = V^T: lane l holds dim 16c + l%16, tokens 4(l/16) + e: 8 bytes at
+//          (16c + l%16) * 32 + 8 (l/16) in the [d][16] layout (512 B per step).
+//      B = P^T: exactly the C layout of the first product, so no data movement.
+//      P is split into a high and a low part in the input type (two products), so
+//      the weights keep ~16 significant bits instead of 8 (bf16) or 11 (fp16).
+//   C: lane l holds head l%16, dims 16c + 4(l/16) + e: its rescale factor is the
+//      lane's own running max, so the online softmax needs no transposes.
+// fp32 path: plain vector arithmetic, one wave per workgroup (correctness path).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "device.hpp"
+#include "status.hpp"
+
+namespace pkv {
+
+struct DecodeArgs {
+    void* out;
+    float* part_out;
+    float* part_max;
+    float* part_sum;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int64_t q_stride;      // elements between sequences in q
+    int64_t num_blocks;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t group;         // G = num_heads / num_kv_heads
+    int32_t max_blocks;    // block-table row length
+    int32_t part_blocks;   // blocks per partition
+    int32_t max_partitions;
+    float scale_log2;      // scale * log2(e): logits in base-2 units
+};
+
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Write the zero row of an empty sequence (n == 0) for the G heads of group g.
+template <typename OutT, int D>
+__device__ void write_zero_rows(const DecodeArgs& a, int b, int g) {
+    for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) {
+        const int h = g * a.group + i / D;
+        OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + h) * D + i % D, 0.0f);
+    }
+}
+
+// Merge the per-wave states held in LDS and write out or the partition result.
+// sm_m / sm_l: [W][16], sm_o: [W][G][D] (unnormalised accumulators).
+template <typename OutT, int D, int W>
+__device__ void merge_and_store(const DecodeArgs& a, const float* sm_m, const float* sm_l,
+                                const float* sm_o, int b, int g, int p, bool direct) {
+    const int G = a.group;
+    for (int i = threadIdx.x; i < G * D; i += W * 64) {
+        const int h = i / D, dim = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * 16 + h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float f = exp2_fast(sm_m[w * 16 + h] - M);  // 0 for a wave with no block
+            L += f * sm_l[w * 16 + h];
+            O += f * sm_o[(w * G + h) * D + dim];
+        }
+        const float o = O / L;
+        const int hq = g * G + h;
+        if (direct) {
+            OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + hq) * D + dim, o);
+        } else {
+            const int64_t row = (int64_t(b) * a.num_heads + hq) * a.max_partitions + p;
+            a.part_out[row * D + dim] = o;
+            if (dim == 0) {
+                a.part_max[row] = M * kLn2;   // back to natural-log units
+                a.part_sum[row] = L;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- fp16 / bf16
+template <typename T, int D, typename OutT, int W>
+__global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
+    static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
+    constexpr int NQK = D / 32;   // 16x16x32 steps for S
+    constexpr int NPV = D / 16;   // 16x16x16 steps for O
+    extern __shared__ float lds[];
+    float* sm_m = lds;                  // [W][16]
+    float* sm_l = lds + W * 16;         // [W][16]
+    float* sm_o = lds + 2 * W * 16;     // [W][G][D]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int G = a.group;
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > a.max_blocks * 16 ? a.max_blocks * 16 : n);
+    const int nblk = (n + 15) >> 4;
+    const int blk_begin = p * a.part_blocks;
+    if (blk_begin >= nblk) {
+        if (p == 0) write_zero_rows<OutT, D>(a, b, g);
+        return;
+    }
+    const int blk_end = min(nblk, blk_begin + a.part_blocks);
+    const bool direct = nblk <= a.part_blocks;
+
+    // Q^T operand (B of the first product): head l%16 of the group, 8 dims per step.
+    const int col = lane & 15, quad = lane >> 4;
+    uint4 qf[NQK];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(b) * a.q_stride +
+                               int64_t(g * G + col) * D + 8 * quad;
+#pragma unroll
+        for (int c = 0; c < NQK; ++c)
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + 32 * c) : make_uint4(0, 0, 0, 0);
+    }
+
+    f32x4 acc[NPV];
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache);
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache);
+    const int64_t tile_elems = int64_t(D) * 16;
+
+    for (int j = blk_begin + wave; j < blk_end; j += W) {
+        const int64_t phys = table[j];
+        if (phys < 0 || phys >= a.num_blocks) continue;   // broken precondition: skip
+        const int64_t tile = phys * a.num_kv_heads + g;
+        const uint16_t* kt = kbase + tile * tile_elems;
+        const uint16_t* vt = vbase + tile * tile_elems;
+        uint4 kr[NQK];
+        uint2 vr[NPV];
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) kr[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 8);
+#pragma unroll
+        for (int c = 0; c < NPV; ++c)
+            vr[c] = *reinterpret_cast<const uint2*>(vt + (16 * c + col) * 16 + 4 * quad);
+
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(kr[c], qf[c], s);
+
+        const int tok0 = j * 16 + 4 * quad;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = tok0 + e < n ? s[e] * a.scale_log2 : -INFINITY;
+        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        bm = wave_max_xor(bm, 16);
+        bm = wave_max_xor(bm, 32);
+        const float mn = fmaxf(m, bm);
+        const float alpha = exp2_fast(m - mn);
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = exp2_fast(x[e] - mn);
+        lsum = lsum * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
+        m = mn;
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) acc[c] *= alpha;
+
+        if (j * 16 + 16 > n) {   // partly filled last block: rows past n may hold anything
+            uint32_t keep_lo = (tok0 + 0 < n ? 0x0000ffffu : 0u) | (tok0 + 1 < n ? 0xffff0000u : 0u);
+            uint32_t keep_hi = (tok0 + 2 < n ? 0x0000ffffu : 0u) | (tok0 + 3 < n ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) {
+                vr[c].x &= keep_lo;
+                vr[c].y &= keep_hi;
+            }
+        }
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
+        const uint2 phi = make_uint2(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                                     uint32_t(hi[2]) | (uint32_t(hi[3]) << 16));
+        const uint2 plo = make_uint2(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                                     uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) {
+            acc[c] = Mfma<T>::pv(vr[c], phi, acc[c]);
+            acc[c] = Mfma<T>::pv(vr[c], plo, acc[c]);
+        }
+    }
+
+    // lanes l, l^16, l^32, l^48 hold the same head: total its running sum
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+
+    if (lane < 16) {
+        sm_m[wave * 16 + lane] = m;
+        sm_l[wave * 16 + lane] = lsum;
+    }
+    if (col < G) {
+#pragma unroll
+        for (int c = 0; c < NPV; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm_o[(wave * G + col) * D + 16 * c + 4 * quad + e] = acc[c][e];
+    }
+    __syncthreads();
+    merge_and_store<OutT, D, W>(a, sm_m, sm_l, sm_o, b, g, p, direct);
+}
+
+// ---------------------------------------------------------------------- fp32
+// One wave per (partition, KV head, sequence). Lane l scores token l%16 for query
+// heads l/16 and l/16 + 4 of the group; for the weighted sum it owns dimensions
+// l and l + 64 of every head.
+template <int D, typename OutT>
+__global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
+    constexpr int GMAX = 8;
+    constexpr int ND = (D + 63) / 64;
+    __shared__ float sq[GMAX][D];
+    __shared__ float sp[GMAX][16];
+    __shared__ float salpha[GMAX];
+    __shared__ float sm[1][16], sl[1][16];
+
+    const int lane = threadIdx.x;
+    const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int G = a.group;
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > a.max_blocks * 16 ? a.max_blocks * 16 : n);
+    const int nblk = (n + 15) >> 4;
+    const int blk_begin = p * a.part_blocks;
+    if (blk_begin >= nblk) {
+        if (p == 0) write_zero_rows<OutT, D>(a, b, g);
+        return;
+    }
+    const int blk_end = min(nblk, blk_begin + a.part_blocks);
+    const bool direct = nblk <= a.part_blocks;
+
+    const float* qrow = static_cast<const float*>(a.q) + int64_t(b) * a.q_stride + int64_t(g) * G * D;
+    for (int i = lane; i < G * D; i += 64) sq[i / D][i % D] = qrow[i];
+    __syncthreads();
+
+    const int t = lane & 15, hs = lane >> 4;
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    float acc[GMAX][ND];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+        for (int k = 0; k < ND; ++k) acc[h][k] = 0.f;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    const float* kbase = static_cast<const float*>(a.k_cache);
+    const float* vbase = static_cast<const float*>(a.v_cache);
+    for (int j = blk_begin; j < blk_end; ++j) {
+        const int64_t phys = table[j];
+        if (phys < 0 || phys >= a.num_blocks) continue;
+        const int64_t tile = (phys * a.num_kv_heads + g) * int64_t(D) * 16;
+        const float* kt = kbase + tile;   // [D/4][16][4]
+        const float* vt = vbase + tile;   // [D][16]
+        const bool valid = j * 16 + t < n;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int h = hs + 4 * r;
+            float x = -INFINITY;
+            if (h < G && valid) {
+                float dot = 0.f;
+                for (int i = 0; i < D; ++i) dot += sq[h][i] * kt[((i >> 2) * 16 + t) * 4 + (i & 3)];
+                x = dot * a.scale_log2;
+            }
+            float bm = x;
+#pragma unroll
+            for (int s = 1; s < 16; s <<= 1) bm = wave_max_xor(bm, s);
+            const float mn = fmaxf(m[r], bm);
+            // a head with no valid token yet keeps -inf; guard the 0 * inf case
+            const float alpha = mn == -INFINITY ? 1.f : exp2_fast(m[r] - mn);
+            const float pv = x == -INFINITY ? 0.f : exp2_fast(x - mn);
+            float ps = pv;
+#pragma unroll
+            for (int s = 1; s < 16; s <<= 1) ps += __shfl_xor(ps, s, 64);
+            l[r] = l[r] * alpha + ps;
+            m[r] = mn;
+            if (h < G) {
+                sp[h][t] = pv;
+                if (t == 0) salpha[h] = alpha;
+            }
+        }
+        __syncthreads();
+        const int nvalid = min(16, n - j * 16);
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h >= G) break;
+            const float al = salpha[h];
+#pragma unroll
+            for (int k = 0; k < ND; ++k) {
+                const int dim = lane + 64 * k;
+                if (dim >= D) continue;
+                float s = acc[h][k] * al;
+                for (int tt = 0; tt < nvalid; ++tt) s += sp[h][tt] * vt[dim * 16 + tt];
+                acc[h][k] = s;
+            }
+        }
+        __syncthreads();
+    }
+    // publish each head's (m, l)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int h = hs + 4 * r;
+        if (h < G && t == 0) {
+            sm[0][h] = m[r];
+            sl[0][h] = l[r];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) break;
+        const float M = sm[0][h], L = sl[0][h];
+        const int hq = g * G + h;
+#pragma unroll
+        for (int k = 0; k < ND; ++k) {
+            const int dim = lane + 64 * k;
+            if (dim >= D) continue;
+            const float o = acc[h][k] / L;
+            if (direct) {
+                OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + hq) * D + dim, o);
+            } else {
+                const int64_t row = (int64_t(b) * a.num_heads + hq) * a.max_partitions + p;
+                a.part_out[row * D + dim] = o;
+                if (dim == 0) {
+                    a.part_max[row] = M * kLn2;
+                    a.part_sum[row] = L;
+                }
+            }
+        }
+    }
+}
+
+constexpr int kWaves = 4;
+
+template <typename T, int D, typename OutT>
+hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+    const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves>), grid, dim3(kWaves * 64), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int D, typename OutT>
+hipError_t launch_f32(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((decode_f32_kernel<D, OutT>), grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid, hipStream_t s) {
+    if (in_dtype == PKV_BF16)
+        return out_dtype == PKV_F32 ? launch_mfma<bf16_t, D, float>(a, grid, s)
+                                    : launch_mfma<bf16_t, D, bf16_t>(a, grid, s);
+    if (in_dtype == PKV_F16)
+        return out_dtype == PKV_F32 ? launch_mfma<f16_t, D, float>(a, grid, s)
+                                    : launch_mfma<f16_t, D, f16_t>(a, grid, s);
+    return launch_f32<D, float>(a, grid, s);
+}
+
+}  // namespace pkv
+
+extern "C" int paged_attention_decode(void* out, float* part_out, float* part_max,
+                                      float* part_sum, const void* q, int64_t q_stride,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                      int32_t partition_size, int32_t max_partitions,
+                                      int32_t in_dtype, int32_t out_dtype, void* stream) {
+    using pkv::fail;
+    const int e = pkv::elem_bytes(in_dtype);
+    if (e == 0) return fail(PKV_EINVAL, "paged_attention_decode: unknown in_dtype %d", in_dtype);
+    if (pkv::elem_bytes(out_dtype) == 0)
+        return fail(PKV_EINVAL, "paged_attention_decode: unknown out_dtype %d", out_dtype);
+    if (out_dtype != in_dtype && out_dtype != PKV_F32)
+        return fail(PKV_ENOTSUP, "paged_attention_decode: out_dtype must be in_dtype or F32");
+    if (num_seqs < 0) return fail(PKV_EINVAL, "paged_attention_decode: negative num_seqs");
+    if (block_size != PKV_BLOCK_SIZE)
+        return fail(PKV_EINVAL, "paged_attention_decode: block_size must be 16, got %d", block_size);
+    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+        return fail(PKV_EINVAL, "paged_attention_decode: num_heads %d not a multiple of "
+                                "num_kv_heads %d", num_heads, num_kv_heads);
+    if (num_seqs > 65535 || num_kv_heads > 65535)
+        return fail(PKV_EINVAL, "paged_attention_decode: num_seqs / num_kv_heads above 65535");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKV_ENOTSUP, "paged_attention_decode: head_dim %d (built: 64, 128)", head_dim);
+    const int G = num_heads / num_kv_heads;
+    if ((in_dtype == PKV_F32 && G > 8) || G > 16)
+        return fail(PKV_ENOTSUP, "paged_attention_decode: group size %d too large", G);
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return fail(PKV_EINVAL, "paged_attention_decode: bad max_blocks_per_seq / num_blocks");
+    const int x = 16 / e;
+    if (q_stride < int64_t(num_heads) * head_dim || q_stride % x)
+        return fail(PKV_EINVAL, "paged_attention_decode: q_stride must cover num_heads*head_dim "
+                                "and be a multiple of %d", x);
+    if (!std::isfinite(scale)) return fail(PKV_EINVAL, "paged_attention_decode: scale not finite");
+    int part_blocks = max_blocks_per_seq, grid_parts = 1;
+    if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE)
+        return fail(PKV_EINVAL, "paged_attention_decode: partition_size must be 0 or a positive "
+                                "multiple of 16");
+    if (partition_size > 0) {
+        part_blocks = partition_size / PKV_BLOCK_SIZE;
+        grid_parts = (max_blocks_per_seq + part_blocks - 1) / part_blocks;
+        if (max_partitions < grid_parts)
+            return fail(PKV_EINVAL, "paged_attention_decode: max_partitions %d < %d",
+                        max_partitions, grid_parts);
+    }
+    if (num_seqs == 0) return pkv::ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
+        return fail(PKV_EINVAL, "paged_attention_decode: NULL pointer");
+    if (grid_parts > 1 && (!part_out || !part_max || !part_sum))
+        return fail(PKV_EINVAL, "paged_attention_decode: partitioned mode needs part_* buffers");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+         reinterpret_cast<uintptr_t>(v_cache)) & 15)
+        return fail(PKV_EINVAL, "paged_attention_decode: q and caches must be 16-byte aligned");
+
+    pkv::DecodeArgs a;
+    a.out = out;
+    a.part_out = part_out;
+    a.part_max = part_max;
+    a.part_sum = part_sum;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.q_stride = q_stride;
+    a.num_blocks = num_blocks;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = G;
+    a.max_blocks = max_blocks_per_seq;
+    a.part_blocks = part_blocks;
+    a.max_partitions = partition_size > 0 ? max_partitions : 1;
+    a.scale_log2 = scale * pkv::kLog2e;
+    const dim3 grid{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = head_dim == 128 ? pkv::dispatch<128>(a, in_dtype, out_dtype, grid, s)
+                                           : pkv::dispatch<64>(a, in_dtype, out_dtype, grid, s);
+    if (err != hipSuccess)
+        return fail(PKV_EHIP, "paged_attention_decode: launch failed: %s", hipGetErrorString(err));
+    return pkv::ok();
+}

@@ -1,0 +1,99 @@
+// Device-side helpers for the gfx950 kernels: element types, conversions with
+// round-to-nearest-even, the exp2 instruction, and the matrix-instruction wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Storage tags: the caches hold raw 16-bit patterns.
+struct bf16_t {};
+struct f16_t {};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> 16-bit patterns, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+    _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __builtin_bit_cast(float, uint32_t(h) << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Output stores in the three supported output types.
+template <typename OutT> struct OutStore;
+template <> struct OutStore<float> {
+    __device__ __forceinline__ static void st(void* base, int64_t i, float v) {
+        static_cast<float*>(base)[i] = v;
+    }
+};
+template <> struct OutStore<bf16_t> {
+    __device__ __forceinline__ static void st(void* base, int64_t i, float v) {
+        static_cast<uint16_t*>(base)[i] = f32_to_bf16_bits(v);
+    }
+};
+template <> struct OutStore<f16_t> {
+    __device__ __forceinline__ static void st(void* base, int64_t i, float v) {
+        static_cast<uint16_t*>(base)[i] = f32_to_f16_bits(v);
+    }
+};
+
+// Matrix-instruction wrappers per input type.
+//   qk(a, b, c):  16x16x32, A and B are 8 elements per lane (one uint4)
+//   pv(a, b, c):  16x16x16, A and B are 4 elements per lane (one uint2)
+//   split(p, hi, lo): p ~= hi + lo with both parts in the input type, so the
+//                     probabilities keep ~16 significant bits through the product
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16_t> {
+    __device__ __forceinline__ static f32x4 qk(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 pv(uint2 a, uint2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                         __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static void split(float p, uint16_t& hi, uint16_t& lo) {
+        hi = f32_to_bf16_bits(p);
+        lo = f32_to_bf16_bits(p - bf16_bits_to_f32(hi));
+    }
+};
+
+template <> struct Mfma<f16_t> {
+    __device__ __forceinline__ static f32x4 qk(uint4 a, uint4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 pv(uint2 a, uint2 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static void split(float p, uint16_t& hi, uint16_t& lo) {
+        hi = f32_to_f16_bits(p);
+        lo = f32_to_f16_bits(p - f16_bits_to_f32(hi));
+    }
+};
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+    return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+}  // namespace pkv

@@ -1,0 +1,68 @@
+"""Builds the HIP-side twin of an OracleBatch: the same workload draws go through the
+library's own block pool and reshape_and_cache on the GPU. Only the random inputs are
+shared with the oracle side; slots, tables and caches are produced independently and
+compared by the tests."""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+import paged_kv_cache_28_amd as pkv
+
+
+@dataclasses.dataclass
+class GpuBatch:
+    pool: pkv.KVPool
+    prompt_slots: np.ndarray
+    new_slots: np.ndarray
+    tables: np.ndarray
+    lens: np.ndarray
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    q: torch.Tensor
+    tables_d: torch.Tensor
+    lens_d: torch.Tensor
+
+
+def build(ob, device="cuda", fill=float("nan")) -> GpuBatch:
+    w = ob.w
+    B = len(ob.lens)
+    pool = pkv.kv_pool_create(ob.num_blocks, 1, w.num_kv_heads, w.head_dim, w.dtype,
+                              free_order=ob.free_order)
+    prompt = []
+    for b in range(B):
+        pool.add_seq(b)
+        prompt.append(pool.append(b, max(int(ob.lens[b]) - 1, 0)))
+    prompt_slots = np.concatenate(prompt) if prompt else np.zeros(0, np.int32)
+    live = [b for b in range(B) if ob.lens[b] > 0]
+    new = np.full(B, -1, dtype=np.int32)
+    if live:
+        new[live] = pool.append_batch(live)
+    tables, lens = pool.build_tables(list(range(B)), ob.max_blocks)
+
+    kc, vc = pkv.alloc_caches(ob.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, device,
+                              fill=fill)
+    if len(prompt_slots):
+        pkv.reshape_and_cache(ob.prompt_k.to(device), ob.prompt_v.to(device), kc, vc,
+                              torch.from_numpy(prompt_slots).to(device))
+    pkv.reshape_and_cache(ob.new_k.to(device), ob.new_v.to(device), kc, vc,
+                          torch.from_numpy(new).to(device))
+    return GpuBatch(pool, prompt_slots, new, tables, lens, kc, vc, ob.q.to(device),
+                    torch.from_numpy(tables).to(device), torch.from_numpy(lens).to(device))
+
+
+def run_decode(gb: GpuBatch, w, partition_size=0, out_dtype=torch.float32, max_partitions=None):
+    """One layer's attention (decode, and reduce when partitioned). Returns out and, when
+    partitioned, the partial buffers."""
+    B, Hq, d = gb.q.shape
+    dev = gb.q.device
+    out = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=dev)
+    parts = None
+    if partition_size > 0:
+        maxp = max_partitions or pkv.max_partitions_for(gb.tables.shape[1], partition_size)
+        parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, dev))
+    pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale,
+               partition_size, parts)
+    return out, parts

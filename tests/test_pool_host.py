@@ -1,0 +1,226 @@
+"""Host side of libpkv.so, on the CPU: exported symbols, the C++ block pool against the
+oracle's pool model (integer for integer), and argument validation of the kernel entry
+points (every case here fails validation before any launch, so no GPU is touched)."""
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import paged_kv_cache_28_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)) - {"defined"})
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "paged_attention_decode" in names and "kv_pool_create" in names
+    assert len(names) == len(pkv.EXPORTED) and set(names) == set(pkv.EXPORTED)
+    L = pkv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout.split()
+    for n in names:
+        assert n in dyn, f"{n} not exported"
+    assert pkv.version().startswith("pkv ")
+
+
+def test_library_does_not_link_the_oracle():
+    libs = subprocess.run(["ldd", pkv.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in libs
+    syms = subprocess.run(["nm", "-D", pkv.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle_" not in syms
+
+
+def test_bytes_per_token_worked_examples():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "kv_bytes_per_token.json")))
+    c = {x["name"]: x for x in g["cases"]}
+    assert pkv.kv_bytes_per_token(80, 8, 128, "f16") == c["llama3-70b-fp16"]["bytes_per_token"]
+    assert pkv.kv_bytes_per_token(32, 8, 128, "bf16") == c["gqa-32layer-bf16"]["bytes_per_token_approx"]
+    pool = pkv.kv_pool_create(16, 80, 8, 128, "f16")
+    assert pool.bytes_per_token() == 327680
+    assert pool.cache_shape() == ((16, 8, 16, 16, 8), (16, 8, 128, 16))
+    with pytest.raises(pkv.PkvError):
+        pkv.kv_bytes_per_token(0, 8, 128, "f16")
+
+
+def test_seventeen_tokens_take_two_blocks():
+    pool = pkv.kv_pool_create(64, 1, 8, 128, "bf16", free_order=np.arange(63, -1, -1))
+    pool.add_seq(11)
+    slots = pool.append(11, 17)
+    assert pool.seq_blocks(11) == [63, 62]
+    assert slots.tolist() == [63 * 16 + i for i in range(16)] + [62 * 16]
+
+
+def _same_state(pool, model, ids):
+    assert pool.free_queue() == list(model.free)
+    st_ = pool.stats()
+    ms = model.stats()
+    assert (st_["free"], st_["used"], st_["shared"], st_["alloc_failures"], st_["num_seqs"]) == \
+        (ms["free"], ms["used"], ms["shared"], ms["alloc_failures"], ms["num_seqs"])
+    for b in range(model.num_blocks):
+        assert pool.refcount(b) == model.ref[b]
+    live = [i for i in ids if i in model.seqs]
+    if live:
+        mb = max(1, max(len(model.seq_blocks(i)) for i in live))
+        t, l = pool.build_tables(live, mb)
+        mt, ml = model.tables(live, mb)
+        assert np.array_equal(t, mt) and np.array_equal(l, ml)
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.lists(st.tuples(st.sampled_from(["add", "append", "batch", "free", "share"]),
+                          st.integers(0, 9), st.integers(0, 90)), max_size=120),
+       st.integers(0, 2 ** 31 - 1))
+def test_pool_matches_oracle_model(ops, seed):
+    nb = 48
+    order = np.random.default_rng(seed).permutation(nb)
+    pool = pkv.kv_pool_create(nb, 2, 2, 64, "bf16", free_order=order)
+    model = oracle.PoolModel(nb, order)
+    ids = list(range(10))
+    codes = {"EINVAL": pkv.PKV_EINVAL, "ENOMEM": pkv.PKV_ENOMEM, "ENOENT": pkv.PKV_ENOENT}
+    for op, sid, n in ops:
+        if op == "add":
+            fn_p, fn_m = (lambda: pool.add_seq(sid)), (lambda: model.add_seq(sid))
+        elif op == "append":
+            fn_p, fn_m = (lambda: pool.append(sid, n).tolist()), (lambda: model.append(sid, n))
+        elif op == "batch":
+            sel = [i for i in ids if (i + n) % 3 == 0]
+
+            def fn_m(sel=sel):
+                # all or nothing, one token each
+                for i in sel:
+                    if i not in model.seqs:
+                        raise oracle.PoolError("ENOENT")
+                need = sum(1 for i in sel if model.seq_len(i) % 16 == 0)
+                if need > len(model.free):
+                    model.alloc_failures += 1
+                    raise oracle.PoolError("ENOMEM")
+                return [model.append(i, 1)[0] for i in sel]
+            fn_p = (lambda sel=sel: pool.append_batch(sel).tolist())
+        elif op == "free":
+            fn_p, fn_m = (lambda: pool.free_seq(sid)), (lambda: model.free_seq(sid))
+        else:
+            src = (sid + 3) % 10
+            k = (n // 16) * 16
+            fn_p, fn_m = (lambda: pool.share_prefix(sid, src, k)), \
+                (lambda: model.share_prefix(sid, src, k))
+        try:
+            rm, em = fn_m(), None
+        except oracle.PoolError as e:
+            rm, em = None, e.code
+        try:
+            rp, ep = fn_p(), None
+        except pkv.PkvError as e:
+            rp, ep = None, e.code
+        assert (ep is None) == (em is None), (op, sid, n, ep, em)
+        if em is not None:
+            assert ep == codes[em], (op, ep, em)
+        else:
+            assert rp == rm
+        _same_state(pool, model, ids)
+
+
+def test_exhaustion_is_atomic_and_counted():
+    pool = pkv.kv_pool_create(4, 1, 1, 64, "f16")
+    pool.add_seq(0)
+    pool.append(0, 20)
+    before = (pool.free_queue(), pool.seq_blocks(0), pool.seq_len(0))
+    with pytest.raises(pkv.PkvError) as e:
+        pool.append(0, 64)
+    assert e.value.code == pkv.PKV_ENOMEM
+    assert (pool.free_queue(), pool.seq_blocks(0), pool.seq_len(0)) == before
+    pool.add_seq(1)
+    pool.append(1, 16)
+    pool.add_seq(2)
+    pool.append(2, 16)
+    pool.append(0, 12)                      # fills block 2 of seq 0, no new block
+    with pytest.raises(pkv.PkvError):
+        pool.append_batch([0, 1, 2])        # 3 new blocks needed, 0 free
+    assert pool.seq_len(0) == 32 and pool.seq_len(1) == 16
+    assert pool.stats()["alloc_failures"] == 2
+    with pytest.raises(pkv.PkvError) as e:
+        pool.append_batch([1, 1])
+    assert e.value.code == pkv.PKV_EINVAL
+
+
+def test_invalid_pool_arguments():
+    with pytest.raises(pkv.PkvError):
+        pkv.kv_pool_create(16, 1, 8, 128, "bf16", block_size=32)
+    with pytest.raises(pkv.PkvError):
+        pkv.kv_pool_create(4, 1, 8, 128, "bf16", free_order=[0, 1, 1, 2])
+    with pytest.raises(pkv.PkvError):
+        pkv.kv_pool_create(0, 1, 8, 128, "bf16")
+
+
+# --------------------------------------------- kernel entry points: validation only
+def _decode_rc(**kw):
+    import ctypes
+    a = dict(out=1 << 20, po=None, pm=None, ps=None, q=1 << 20, q_stride=4096, kc=1 << 20,
+             vc=1 << 20, bt=1 << 20, sl=1 << 20, B=4, Hq=32, Hkv=8, d=128, bs=16, mb=8, nb=64,
+             scale=0.1, P=0, maxp=0, ind=pkv.PKV_BF16, outd=pkv.PKV_F32)
+    a.update(kw)
+    V = ctypes.c_void_p
+    return pkv.lib().paged_attention_decode(
+        V(a["out"]), V(a["po"]), V(a["pm"]), V(a["ps"]), V(a["q"]), a["q_stride"], V(a["kc"]),
+        V(a["vc"]), V(a["bt"]), V(a["sl"]), a["B"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["mb"],
+        a["nb"], a["scale"], a["P"], a["maxp"], a["ind"], a["outd"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=30), pkv.PKV_EINVAL),                      # not a multiple of Hkv
+    (dict(bs=32), pkv.PKV_EINVAL),
+    (dict(d=96), pkv.PKV_ENOTSUP),
+    (dict(Hq=8 * 17), pkv.PKV_ENOTSUP),                 # group of 17
+    (dict(ind=pkv.PKV_F32, Hq=8 * 9, q_stride=9 * 8 * 128), pkv.PKV_ENOTSUP),
+    (dict(outd=pkv.PKV_F16), pkv.PKV_ENOTSUP),          # bf16 in, f16 out
+    (dict(P=100, maxp=8), pkv.PKV_EINVAL),              # not a multiple of 16
+    (dict(P=32, maxp=3), pkv.PKV_EINVAL),               # too few partition slots
+    (dict(P=32, maxp=4), pkv.PKV_EINVAL),               # partitioned without buffers
+    (dict(q=(1 << 20) + 2), pkv.PKV_EINVAL),            # misaligned
+    (dict(q_stride=100), pkv.PKV_EINVAL),
+    (dict(kc=None), pkv.PKV_EINVAL),
+    (dict(scale=float("inf")), pkv.PKV_EINVAL),
+    (dict(ind=7), pkv.PKV_EINVAL),
+])
+def test_decode_rejects_bad_arguments_before_launch(kw, code):
+    assert _decode_rc(**kw) == code
+    assert pkv.lib().pkv_last_error().decode()
+
+
+def test_zero_sequences_is_a_no_op():
+    assert _decode_rc(B=0, out=None, q=None) == pkv.PKV_OK
+
+
+def test_cache_write_and_reduce_reject_bad_arguments():
+    import ctypes
+    V = ctypes.c_void_p
+    L = pkv.lib()
+    good = dict(k=V(1 << 20), v=V(1 << 20), kc=V(1 << 20), vc=V(1 << 20), s=V(1 << 20))
+    assert L.reshape_and_cache(good["k"], good["v"], good["kc"], good["vc"], good["s"], 4, 8,
+                               128, 8, 64, 1024, 1024, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    assert L.reshape_and_cache(good["k"], good["v"], good["kc"], good["vc"], good["s"], 4, 8,
+                               100, 16, 64, 1024, 1024, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    assert L.reshape_and_cache(good["k"], good["v"], good["kc"], good["vc"], good["s"], 4, 8,
+                               128, 16, 64, 1000, 1024, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    assert L.reshape_and_cache(V(2), good["v"], good["kc"], good["vc"], good["s"], 4, 8,
+                               128, 16, 64, 1024, 1024, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    assert L.reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 64, 1024, 1024,
+                               pkv.PKV_BF16, None) == pkv.PKV_OK
+    assert L.paged_attention_reduce(good["k"], good["k"], good["k"], good["k"], good["s"], 4, 32,
+                                    96, 512, 8, pkv.PKV_F32, None) == pkv.PKV_ENOTSUP
+    assert L.paged_attention_reduce(good["k"], good["k"], good["k"], good["k"], good["s"], 4, 32,
+                                    128, 500, 8, pkv.PKV_F32, None) == pkv.PKV_EINVAL
