@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama8b")
-    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--partition", default="auto",
+                    help="auto (balanced split), 0 (single pass) or a multiple of 16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
@@ -62,7 +63,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.config]
-    P = w.partition_size if args.partition is None else args.partition
+    P = pkv.PKV_PARTITION_AUTO if args.partition == "auto" else int(args.partition)
     L, B, Hq, Hkv, d = w.layers, w.batch, w.num_heads, w.num_kv_heads, w.head_dim
     e = w.elem_bytes
     tdt = pkv.torch_dtype(w.dtype)
@@ -78,7 +79,7 @@ def main():
         pool.add_seq(int(b))
         pool.append(int(b), int(lens0[b]) - 1)        # the cached prompt
     max_blocks = int(-(-(int(lens0.max()) + total_steps) // 16))
-    maxp = pkv.max_partitions_for(max_blocks, P) if P > 0 else 0
+    maxp = pkv.max_partitions_for(max_blocks, P) if P != 0 else 0
 
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
@@ -92,7 +93,7 @@ def main():
     k_new = [torch.randn((B, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
     v_new = [torch.randn((B, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
     out = [torch.empty((B, Hq, d), device=dev, dtype=tdt) for _ in range(L)]
-    parts = pkv.alloc_partials(B, Hq, d, maxp, dev) if P > 0 else None
+    parts = pkv.alloc_partials(B, Hq, d, maxp, dev) if P != 0 else None
 
     # double-buffered pinned metadata; an event guards each buffer's reuse
     h_tab = [torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True) for _ in range(2)]
@@ -121,13 +122,13 @@ def main():
             pkv.reshape_and_cache(k_new[layer], v_new[layer], kc, vc, d_slot)
             if events is not None:
                 events[layer][0].record(stream)
-            if P > 0:
+            if P != 0:
                 po, pm, ps = parts
                 pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
                                            P, po, pm, ps, maxp)
                 if events is not None:
                     events[layer][1].record(stream)
-                pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P)
+                pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P, Hkv, max_blocks)
             else:
                 pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale)
                 if events is not None:
@@ -176,7 +177,8 @@ def main():
         "data": "synthetic (seeded draws of the workload's shapes and length mix)",
         "config": {"workload": f"{w.name}-decode", "layers": L, "batch": B, "num_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": d, "block_size": 16,
-                   "seq_len_range": [w.len_lo, w.len_hi], "partition_size": P,
+                   "seq_len_range": [w.len_lo, w.len_hi],
+                   "partition_size": "auto" if P == pkv.PKV_PARTITION_AUTO else P,
                    "pool_blocks": nb, "pool_gb_per_layer": round(nb * w.block_bytes_per_layer / 1e9, 3)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),

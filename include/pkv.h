@@ -61,6 +61,9 @@ extern "C" {
 
 #define PKV_BLOCK_SIZE 16
 
+/* partition_size value asking paged_attention_decode for the balanced split */
+#define PKV_PARTITION_AUTO (-1)
+
 /* Message for the last failing call on this thread ("" if none). Owned by the
  * library; valid until the next call on this thread. */
 const char* pkv_last_error(void);
@@ -213,8 +216,20 @@ int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v
  *                 directly; otherwise each partition p < ceil(n / partition_size)
  *                 writes, for every query head of the group,
  *                   part_out[b][h][p][:] = attention restricted to the partition (fp32),
- *                   part_max[b][h][p]    = max of its s_t (natural-log units),
- *                   part_sum[b][h][p]    = sum of exp(s_t - part_max),
+ *                   part_max[b][h][p]    = a reference logit m_p (natural-log units)
+ *                                          within 8 ln 2 of the partition's largest s_t,
+ *                   part_sum[b][h][p]    = sum of exp(s_t - m_p) over the partition,
+ *                 so that part_max + log(part_sum) is the partition's log-sum-exp;
+ *   partition_size == PKV_PARTITION_AUTO (fp16/bf16, num_seqs <= 1024): balanced
+ *                 split. All (sequence, KV head, block) tiles form one list that is cut
+ *                 into equal runs, one per wave of the launch, so ragged lengths do
+ *                 not leave the device idle. A (sequence, KV head) whose blocks all fall
+ *                 in one run writes out; otherwise each run's share ("piece" k) writes
+ *                 part_out/part_max/part_sum at index k as above. Pieces per (b, h) stay
+ *                 <= max_partitions (>= 2 required): each run spans at least
+ *                 ceil(max_blocks_per_seq / (max_partitions - 1)) tiles.
+ *                 paged_attention_reduce must follow, with the same arguments: it
+ *                 merges the split rows and writes the zero rows of empty sequences.
  *                 and paged_attention_reduce() produces out for those rows.
  *                 Requires part_* non-null and max_partitions >=
  *                 ceil(max_blocks_per_seq * 16 / partition_size).
@@ -233,15 +248,19 @@ int paged_attention_decode(void* out, float* part_out, float* part_max, float* p
                            int32_t out_dtype, void* stream);
 
 /* paged_attention_reduce: for every (b, h) whose sequence has more than one
- * partition (np = ceil(seq_lens[b] / partition_size) > 1):
+ * partition (np = ceil(seq_lens[b] / partition_size) > 1; with PKV_PARTITION_AUTO, np
+ * is the number of pieces of the balanced split, and rows of empty sequences are
+ * written as zeros):
  *     M = max_p part_max,  w_p = exp(part_max[p] - M) * part_sum[p],
  *     out[b][h] = sum_p w_p part_out[p] / sum_p w_p        (p < np only)
- * Rows with np <= 1 are not touched (the decode kernel wrote them). Buffers are
- * those of paged_attention_decode with the same partition_size/max_partitions;
- * out_dtype in {F32, F16, BF16}. Errors: EINVAL, ENOTSUP, EHIP. */
+ * Rows with np <= 1 are not touched (the decode kernel wrote them). Buffers and
+ * num_kv_heads, max_blocks_per_seq, partition_size, max_partitions are those of the
+ * paged_attention_decode call; out_dtype in {F32, F16, BF16}. Errors: EINVAL,
+ * ENOTSUP, EHIP. */
 int paged_attention_reduce(void* out, const float* part_out, const float* part_max,
                            const float* part_sum, const int32_t* seq_lens, int32_t num_seqs,
-                           int32_t num_heads, int32_t head_dim, int32_t partition_size,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, int32_t partition_size,
                            int32_t max_partitions, int32_t out_dtype, void* stream);
 
 #ifdef __cplusplus

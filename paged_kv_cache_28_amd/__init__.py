@@ -18,10 +18,12 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpkv.so")
+# PKV_LIBRARY selects another build of the same ABI (for example a debug build)
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(HERE, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOTSUP, PKV_ENOMEM, PKV_ENOENT, PKV_EHIP = 0, -1, -2, -3, -4, -5
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_PARTITION_AUTO = -1
 BLOCK_SIZE = 16
 _CODE_NAMES = {PKV_EINVAL: "EINVAL", PKV_ENOTSUP: "ENOTSUP", PKV_ENOMEM: "ENOMEM",
                PKV_ENOENT: "ENOENT", PKV_EHIP: "EHIP"}
@@ -74,7 +76,7 @@ def lib():
                               ctypes.c_int),
         "paged_attention_decode": ([P, P, P, P, P, I64, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                     I64, F, I32, I32, I32, I32, P], ctypes.c_int),
-        "paged_attention_reduce": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, P],
+        "paged_attention_reduce": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P],
                                    ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -305,8 +307,10 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
                            max_partitions: int = 0, num_kv_heads: int | None = None,
                            stream=None):
     """out/q: device [B][Hq][d] (q's sequence stride is free); block_tables int32
-    [B][max_blocks]; seq_lens int32 [B]. With partition_size > 0 pass the fp32
-    partial buffers part_out [B][Hq][P][d], part_max/part_sum [B][Hq][P]."""
+    [B][max_blocks]; seq_lens int32 [B]. partition_size: 0 (single pass), a multiple
+    of 16 (fixed partitions) or PKV_PARTITION_AUTO (balanced split); the last two
+    need fp32 partial buffers part_out [B][Hq][P][d], part_max/part_sum [B][Hq][P]
+    and a paged_attention_reduce call with the same arguments."""
     B, Hq, d = q.shape
     if q.stride(2) != 1 or q.stride(1) != d:
         raise ValueError("q must have dense heads/dims")
@@ -325,16 +329,20 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
 
 
 def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partition_size: int,
-                           stream=None):
+                           num_kv_heads: int, max_blocks_per_seq: int, stream=None):
     B, Hq, d = out.shape
     P = part_out.shape[2]
     _check(lib().paged_attention_reduce(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
-        _dev(part_sum, "part_sum"), _dev(seq_lens, "seq_lens"), B, Hq, d, partition_size, P,
-        dtype_code(out.dtype), _stream(out, stream)))
+        _dev(part_sum, "part_sum"), _dev(seq_lens, "seq_lens"), B, Hq, num_kv_heads, d,
+        max_blocks_per_seq, partition_size, P, dtype_code(out.dtype), _stream(out, stream)))
 
 
 def max_partitions_for(max_blocks: int, partition_size: int) -> int:
+    """Partial slots per (b, h): ceil(max_blocks*16 / P) for fixed partitions; for the
+    balanced split a bound that keeps every piece at least 4 blocks long."""
+    if partition_size == PKV_PARTITION_AUTO:
+        return max(2, -(-max_blocks // 4) + 1)
     return -(-max_blocks * BLOCK_SIZE // partition_size)
 
 
@@ -347,12 +355,13 @@ def alloc_partials(B: int, Hq: int, d: int, max_partitions: int, device="cuda"):
 
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
            partition_size: int = 0, partials=None, stream=None):
-    """Decode + (if partitioned) reduce, the two launches of one layer's attention."""
-    if partition_size > 0:
+    """Decode + (if partitioned or balanced) reduce: the launches of one layer's attention."""
+    if partition_size != 0:
         po, pm, ps = partials
         paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
                                partition_size, po, pm, ps, po.shape[2], stream=stream)
-        paged_attention_reduce(out, po, pm, ps, seq_lens, partition_size, stream=stream)
+        paged_attention_reduce(out, po, pm, ps, seq_lens, partition_size, k_cache.shape[1],
+                               block_tables.shape[1], stream=stream)
     else:
         paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
                                stream=stream)

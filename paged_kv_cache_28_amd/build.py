@@ -32,6 +32,9 @@ def hipcc() -> str:
 def common_flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-instruction accumulators in ordinary VGPRs: the online softmax
+            # rescales them, which would otherwise copy them out of and back into AGPRs
+            "-mllvm", "--amdgpu-mfma-vgpr-form",
             "-Wno-unused-command-line-argument"]
 
 

@@ -26,14 +26,15 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const int c = int(idx % nchunk);
     const int g = int((idx / nchunk) % hkv);
     const int64_t t = idx / (int64_t(nchunk) * hkv);
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_blocks * 16) return;
-    const int64_t blk = slot >> 4;
-    const int off = int(slot & 15);
+    // the rows and the slot are independent reads: issue them together
     const int64_t src_k = t * key_stride_b + (int64_t(g) * d + int64_t(c) * X) * E;
     const int64_t src_v = t * value_stride_b + (int64_t(g) * d + int64_t(c) * X) * E;
     const uint4 kv = *reinterpret_cast<const uint4*>(key + src_k);
     const uint4 vv = *reinterpret_cast<const uint4*>(value + src_v);
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_blocks * 16) return;
+    const int64_t blk = slot >> 4;
+    const int off = int(slot & 15);
     const int64_t tile = blk * hkv + g;
     *reinterpret_cast<uint4*>(kc + ((tile * nchunk + c) * 16 + off) * 16) = kv;
     // V: element k of the group is dimension c*X + k, row `off` of that dimension

@@ -34,8 +34,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
+#include <mutex>
 
 #include "device.hpp"
+#include "split.hpp"
 #include "status.hpp"
 
 namespace pkv {
@@ -59,6 +62,8 @@ struct DecodeArgs {
     int32_t part_blocks;   // blocks per partition
     int32_t max_partitions;
     float scale_log2;      // scale * log2(e): logits in base-2 units
+    int32_t num_seqs;
+    SplitParams split;     // balanced mode only
 };
 
 constexpr float kLn2 = 0.693147180559945309417f;
@@ -107,6 +112,13 @@ __device__ void merge_and_store(const DecodeArgs& a, const float* sm_m, const fl
 }
 
 // ---------------------------------------------------------------- fp16 / bf16
+// K and V of one (block, KV head) tile as this lane holds them for the two products.
+template <int D>
+struct KvTile {
+    uint4 k[D / 32];
+    uint2 v[D / 16];
+};
+
 template <typename T, int D, typename OutT, int W>
 __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
@@ -120,6 +132,19 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int G = a.group;
+    const int col = lane & 15, quad = lane >> 4;
+
+    // Q^T operand (B of the first product): head l%16 of the group, 8 dims per step.
+    // Issued first so its latency overlaps the sequence-length read.
+    uint4 qf[NQK];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(b) * a.q_stride +
+                               int64_t(g * G + col) * D + 8 * quad;
+#pragma unroll
+        for (int c = 0; c < NQK; ++c)
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + 32 * c) : make_uint4(0, 0, 0, 0);
+    }
+
     int n = a.seq_lens[b];
     n = n < 0 ? 0 : (n > a.max_blocks * 16 ? a.max_blocks * 16 : n);
     const int nblk = (n + 15) >> 4;
@@ -131,69 +156,76 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int blk_end = min(nblk, blk_begin + a.part_blocks);
     const bool direct = nblk <= a.part_blocks;
 
-    // Q^T operand (B of the first product): head l%16 of the group, 8 dims per step.
-    const int col = lane & 15, quad = lane >> 4;
-    uint4 qf[NQK];
-    {
-        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(b) * a.q_stride +
-                               int64_t(g * G + col) * D + 8 * quad;
-#pragma unroll
-        for (int c = 0; c < NQK; ++c)
-            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + 32 * c) : make_uint4(0, 0, 0, 0);
-    }
+    // This wave takes blocks first, first + W, ... (nmine of them).
+    const int first = blk_begin + wave;
+    const int nmine = first < blk_end ? (blk_end - first + W - 1) / W : 0;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
 
     f32x4 acc[NPV];
 #pragma unroll
     for (int c = 0; c < NPV; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Softmax state per head (lane l: head l%16), in base-2 logit units: m is the
+    // reference point of the exponentials, lsum = sum of 2^(x - m) over this lane's
+    // tokens. m is the running maximum, except that it is only moved when a block's
+    // maximum exceeds it by more than kSlack, so the rescale of acc is rare; every
+    // 2^(x - m) stays below 2^kSlack, far from overflow.
+    constexpr float kSlack = 8.0f;
     float m = -INFINITY, lsum = 0.f;
 
-    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache);
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache);
     const int64_t tile_elems = int64_t(D) * 16;
+    int tab = 0;   // block ids of the current segment: lane k holds block k
 
-    for (int j = blk_begin + wave; j < blk_end; j += W) {
-        const int64_t phys = table[j];
-        if (phys < 0 || phys >= a.num_blocks) continue;   // broken precondition: skip
+    // Issue the loads of block k of the segment; false if its id breaks the
+    // precondition (then a safe address is read and the block is skipped).
+    auto load = [&](KvTile<D>& t, int k) -> bool {
+        int64_t phys = __builtin_amdgcn_readlane(tab, k);
+        const bool ok = phys >= 0 && phys < a.num_blocks;
+        phys = ok ? phys : 0;
         const int64_t tile = phys * a.num_kv_heads + g;
         const uint16_t* kt = kbase + tile * tile_elems;
         const uint16_t* vt = vbase + tile * tile_elems;
-        uint4 kr[NQK];
-        uint2 vr[NPV];
 #pragma unroll
-        for (int c = 0; c < NQK; ++c) kr[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 8);
+        for (int c = 0; c < NQK; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 8);
 #pragma unroll
         for (int c = 0; c < NPV; ++c)
-            vr[c] = *reinterpret_cast<const uint2*>(vt + (16 * c + col) * 16 + 4 * quad);
+            t.v[c] = *reinterpret_cast<const uint2*>(vt + (16 * c + col) * 16 + 4 * quad);
+        return ok;
+    };
 
+    auto compute = [&](KvTile<D>& t, int j, bool ok) {
+        if (!ok) return;
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(kr[c], qf[c], s);
+        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(t.k[c], qf[c], s);
 
         const int tok0 = j * 16 + 4 * quad;
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = tok0 + e < n ? s[e] * a.scale_log2 : -INFINITY;
-        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        bm = wave_max_xor(bm, 16);
-        bm = wave_max_xor(bm, 32);
-        const float mn = fmaxf(m, bm);
-        const float alpha = exp2_fast(m - mn);
+        const float bm = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const bool move = bm > m + kSlack;          // true on the first block (m = -inf)
+        if (__builtin_amdgcn_ballot_w64(move)) {    // wave-uniform, rare after the first block
+            const float mn = move ? bm : m;
+            const float alpha = exp2_fast(m - mn);   // 1 where m stays, 0 from -inf
+            lsum *= alpha;
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) acc[c] *= alpha;
+            m = mn;
+        }
         float pe[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = exp2_fast(x[e] - mn);
-        lsum = lsum * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-        m = mn;
-#pragma unroll
-        for (int c = 0; c < NPV; ++c) acc[c] *= alpha;
+        for (int e = 0; e < 4; ++e) pe[e] = exp2_fast(x[e] - m);
+        lsum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
 
         if (j * 16 + 16 > n) {   // partly filled last block: rows past n may hold anything
-            uint32_t keep_lo = (tok0 + 0 < n ? 0x0000ffffu : 0u) | (tok0 + 1 < n ? 0xffff0000u : 0u);
-            uint32_t keep_hi = (tok0 + 2 < n ? 0x0000ffffu : 0u) | (tok0 + 3 < n ? 0xffff0000u : 0u);
+            const uint32_t keep_lo = (tok0 + 0 < n ? 0x0000ffffu : 0u) | (tok0 + 1 < n ? 0xffff0000u : 0u);
+            const uint32_t keep_hi = (tok0 + 2 < n ? 0x0000ffffu : 0u) | (tok0 + 3 < n ? 0xffff0000u : 0u);
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
-                vr[c].x &= keep_lo;
-                vr[c].y &= keep_hi;
+                t.v[c].x &= keep_lo;
+                t.v[c].y &= keep_hi;
             }
         }
         uint16_t hi[4], lo[4];
@@ -205,8 +237,26 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                                      uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
 #pragma unroll
         for (int c = 0; c < NPV; ++c) {
-            acc[c] = Mfma<T>::pv(vr[c], phi, acc[c]);
-            acc[c] = Mfma<T>::pv(vr[c], plo, acc[c]);
+            acc[c] = Mfma<T>::pv(t.v[c], phi, acc[c]);
+            acc[c] = Mfma<T>::pv(t.v[c], plo, acc[c]);
+        }
+    };
+
+    // Segments of up to 64 blocks (one block id per lane). Inside a segment two tiles
+    // are in flight: the next block's loads are always issued (the last one re-reads
+    // the final block, which is then in cache) before the current block is used, so
+    // the wait for the current tile never waits for the next.
+    for (int k0 = 0; k0 < nmine; k0 += 64) {
+        const int cnt = min(64, nmine - k0);
+        tab = lane < cnt ? table[first + (k0 + lane) * W] : 0;
+        KvTile<D> A, B;
+        bool okA = load(A, 0), okB;
+        for (int k = 0; k < cnt; k += 2) {
+            okB = load(B, min(k + 1, cnt - 1));
+            compute(A, first + (k0 + k) * W, okA);
+            if (k + 1 >= cnt) break;
+            okA = load(A, min(k + 2, cnt - 1));
+            compute(B, first + (k0 + k + 1) * W, okB);
         }
     }
 
@@ -226,6 +276,248 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
     __syncthreads();
     merge_and_store<OutT, D, W>(a, sm_m, sm_l, sm_o, b, g, p, direct);
+}
+
+// ------------------------------------------------------- fp16 / bf16, balanced split
+// Same per-tile arithmetic as decode_mfma_kernel; the work is cut as described in
+// split.hpp. Each wave is independent: it reads the block ids of up to 64 of its tiles
+// with one vector load (lane k: tile k), then streams the tiles two deep, switching
+// (sequence, KV head) at piece boundaries. A piece covering all of its (b, g) writes
+// out; any other piece writes its (o, m, l) record at piece index u - floor(start / s).
+constexpr int kSplitPiecesPerBatch = 4;   // queries staged in LDS per wave and batch
+
+template <typename T, int D, typename OutT>
+__global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a) {
+    constexpr int NQK = D / 32, NPV = D / 16;
+    constexpr int kWaves = kSplitThreads / 64;
+    __shared__ int32_t s_end[kSplitMaxSeqs];
+    __shared__ int32_t s_len[kSplitMaxSeqs];
+    __shared__ int32_t s_wave[kWaves];
+    extern __shared__ uint16_t s_q[];   // [wave][piece][G][D] staged queries
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, quad = lane >> 4;
+    const int G = a.group, hkv = a.num_kv_heads;
+    const int total = split_scan(a.seq_lens, a.num_seqs, hkv, a.max_blocks * 16, s_end, s_len, s_wave);
+    const int share = split_share(total, a.split);
+    const int u = blockIdx.x * kWaves + wave;
+    const int64_t t0l = int64_t(u) * share;
+    if (t0l >= total) return;
+    const int t0 = int(t0l);
+    const int t1 = min(total, t0 + share);
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache);
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache);
+    const int64_t tile_elems = int64_t(D) * 16;
+    const int qpiece = G * D;                              // elements per staged query set
+    uint16_t* my_q = s_q + wave * kSplitPiecesPerBatch * qpiece;
+    constexpr float kSlack = 8.0f;
+
+    // state of the current piece
+    uint4 qf[NQK];
+    f32x4 acc[NPV];
+    float m = -INFINITY, lsum = 0.f;
+    int cur_bg = -1, seg_b = 0, seg_g = 0, seg_n = 0, seg_nblk = 0, seg_start = 0;
+    int first_j = 0, last_j = 0, piece_slot = -1;
+
+    auto begin_piece = [&](int bg, int j) {
+        seg_b = bg / hkv;
+        seg_g = bg - seg_b * hkv;
+        seg_n = s_len[seg_b];
+        seg_nblk = (seg_n + 15) >> 4;
+        seg_start = (seg_b ? s_end[seg_b - 1] : 0) + seg_g * seg_nblk;
+        first_j = j;
+        cur_bg = bg;
+        ++piece_slot;
+        const uint16_t* qs = my_q + piece_slot * qpiece + (col < G ? col : 0) * D + 8 * quad;
+#pragma unroll
+        for (int c = 0; c < NQK; ++c)
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qs + 32 * c) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        lsum = 0.f;
+    };
+
+    auto end_piece = [&]() {
+        float L = lsum;
+        L += __shfl_xor(L, 16, 64);
+        L += __shfl_xor(L, 32, 64);
+        if (col >= G) return;
+        const float inv = 1.0f / L;
+        const int hq = seg_g * G + col;
+        if (first_j == 0 && last_j == seg_nblk - 1) {
+            const int64_t o = (int64_t(seg_b) * a.num_heads + hq) * D + 4 * quad;
+#pragma unroll
+            for (int c = 0; c < NPV; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) OutStore<OutT>::st(a.out, o + 16 * c + e, acc[c][e] * inv);
+        } else {
+            const int piece = u - seg_start / share;
+            const int64_t row = (int64_t(seg_b) * a.num_heads + hq) * a.max_partitions + piece;
+            float* po = a.part_out + row * D + 4 * quad;
+#pragma unroll
+            for (int c = 0; c < NPV; ++c)
+                *reinterpret_cast<float4*>(po + 16 * c) =
+                    make_float4(acc[c][0] * inv, acc[c][1] * inv, acc[c][2] * inv, acc[c][3] * inv);
+            if (quad == 0) {
+                a.part_max[row] = m * kLn2;
+                a.part_sum[row] = L;
+            }
+        }
+    };
+
+    int tphys = 0, tbg = 0, tj = 0;   // per-lane metadata of the current batch
+    auto load = [&](KvTile<D>& t, int k) -> bool {
+        int64_t phys = __builtin_amdgcn_readlane(tphys, k);
+        const bool ok = phys >= 0 && phys < a.num_blocks;
+        phys = ok ? phys : 0;
+        const int g = __builtin_amdgcn_readlane(tbg, k) % hkv;
+        const int64_t tile = phys * hkv + g;
+        const uint16_t* kt = kbase + tile * tile_elems;
+        const uint16_t* vt = vbase + tile * tile_elems;
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 8);
+#pragma unroll
+        for (int c = 0; c < NPV; ++c)
+            t.v[c] = *reinterpret_cast<const uint2*>(vt + (16 * c + col) * 16 + 4 * quad);
+        return ok;
+    };
+
+    auto compute = [&](KvTile<D>& t, int k, bool ok) {   // ok == false: tile masked out
+        const int bg = __builtin_amdgcn_readlane(tbg, k);
+        const int j = __builtin_amdgcn_readlane(tj, k);
+        if (bg != cur_bg) {
+            if (cur_bg >= 0) end_piece();
+            begin_piece(bg, j);
+        }
+        last_j = j;
+        // A tile whose block id broke the precondition is read from block 0 and then
+        // masked out entirely (arithmetic, not a branch, so every loaded register is
+        // consumed and the waits stay per tile).
+        const int n = ok ? seg_n : 0;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(t.k[c], qf[c], s);
+        const int tok0 = j * 16 + 4 * quad;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = tok0 + e < n ? s[e] * a.scale_log2 : -INFINITY;
+        const float bm = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const bool move = bm > m + kSlack;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float mn = move ? bm : m;
+            const float alpha = exp2_fast(m - mn);
+            lsum *= alpha;
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) acc[c] *= alpha;
+            m = mn;
+        }
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m);
+        lsum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+        if (j * 16 + 16 > n) {
+            const uint32_t keep_lo = (tok0 + 0 < n ? 0x0000ffffu : 0u) | (tok0 + 1 < n ? 0xffff0000u : 0u);
+            const uint32_t keep_hi = (tok0 + 2 < n ? 0x0000ffffu : 0u) | (tok0 + 3 < n ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) {
+                t.v[c].x &= keep_lo;
+                t.v[c].y &= keep_hi;
+            }
+        }
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
+        const uint2 phi = make_uint2(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                                     uint32_t(hi[2]) | (uint32_t(hi[3]) << 16));
+        const uint2 plo = make_uint2(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                                     uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) {
+            acc[c] = Mfma<T>::pv(t.v[c], phi, acc[c]);
+            acc[c] = Mfma<T>::pv(t.v[c], plo, acc[c]);
+        }
+    };
+
+    // Batches of up to 64 tiles spanning up to kSplitPiecesPerBatch (b, g) pieces.
+    // Per batch: lane k finds tile k's (b, g, j) by binary search, then the block ids
+    // and the pieces' queries are fetched together (one wait), the queries staged in
+    // this wave's LDS slots; the tiles then stream two deep with no other load.
+    for (int tb = t0; tb < t1;) {
+        int cnt = min(64, t1 - tb);
+        int lb = 0, lg = 0, lj = 0;
+        if (lane < cnt) {
+            const int t = tb + lane;
+            int lo = 0, hi = a.num_seqs - 1;   // first b with s_end[b] > t
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_end[mid] > t) hi = mid; else lo = mid + 1;
+            }
+            const int nb = (s_len[lo] + 15) >> 4;
+            const int r = t - (lo ? s_end[lo - 1] : 0);
+            lb = lo;
+            lg = r / nb;
+            lj = r - lg * nb;
+        }
+        const int lbg = lb * hkv + lg;
+        // lanes that open a new piece; cut the batch before the fifth one
+        const int prev = __shfl_up(lbg, 1, 64);
+        const bool opens = lane < cnt && (lane == 0 || prev != lbg);
+        uint64_t opens_mask = __builtin_amdgcn_ballot_w64(opens);
+        for (int c = 0; c < kSplitPiecesPerBatch && opens_mask; ++c) opens_mask &= opens_mask - 1;
+        if (opens_mask) cnt = __builtin_ctzll(opens_mask);
+        tbg = lbg;
+        tj = lj;
+        // One round trip for all metadata: the block ids of the batch and the queries
+        // of its pieces (piece p opens at the p-th set bit of pm) are loaded together,
+        // then the queries are staged in this wave's LDS slots.
+        tphys = lane < cnt ? a.block_tables[int64_t(lb) * a.max_blocks + lj] : 0;
+        const uint64_t pm = __builtin_amdgcn_ballot_w64(opens && lane < cnt);
+        constexpr int kQChunks = (16 * D * 2 + 1023) / 1024;   // 1 KiB per lane-chunk, G <= 16
+        uint4 qv[kSplitPiecesPerBatch][kQChunks];
+        {
+            uint64_t mm = pm;
+#pragma unroll
+            for (int p = 0; p < kSplitPiecesPerBatch; ++p) {
+                const int src = mm ? __builtin_ctzll(mm) : 0;
+                mm &= mm ? mm - 1 : 0;
+                const int pbg = __builtin_amdgcn_readlane(lbg, src);
+                const int pb = pbg / hkv, pg = pbg - pb * hkv;
+                const uint16_t* qg = static_cast<const uint16_t*>(a.q) + int64_t(pb) * a.q_stride +
+                                     int64_t(pg) * G * D;
+#pragma unroll
+                for (int c = 0; c < kQChunks; ++c) {
+                    const int i = (c * 64 + lane) * 8;
+                    qv[p][c] = i < qpiece ? *reinterpret_cast<const uint4*>(qg + i) : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < kSplitPiecesPerBatch; ++p)
+#pragma unroll
+            for (int c = 0; c < kQChunks; ++c) {
+                const int i = (c * 64 + lane) * 8;
+                if (i < qpiece) *reinterpret_cast<uint4*>(my_q + p * qpiece + i) = qv[p][c];
+            }
+        piece_slot = -1;
+        if (cur_bg >= 0 && __builtin_amdgcn_readlane(tbg, 0) == cur_bg) {
+            // the batch continues the previous piece: keep its state, re-point the slot
+            piece_slot = 0;
+        }
+        // Two tiles per step, both loaded before either is used. An odd count repeats
+        // the last tile with every token masked, so the step has no branch and each
+        // tile's wait covers only its own loads.
+        for (int k = 0; k < cnt; k += 2) {
+            const int k1 = min(k + 1, cnt - 1);
+            KvTile<D> A, B;
+            const bool okA = load(A, k);
+            const bool okB = load(B, k1);
+            compute(A, k, okA);
+            compute(B, k1, okB && k + 1 < cnt);
+        }
+        tb += cnt;
+    }
+    if (cur_bg >= 0) end_piece();
 }
 
 // ---------------------------------------------------------------------- fp32
@@ -362,6 +654,14 @@ hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <typename T, int D, typename OutT>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
+    const int groups = (a.split.units + kSplitThreads / 64 - 1) / (kSplitThreads / 64);
+    const size_t lds = sizeof(uint16_t) * (kSplitThreads / 64) * kSplitPiecesPerBatch * a.group * D;
+    hipLaunchKernelGGL((decode_split_kernel<T, D, OutT>), dim3(groups), dim3(kSplitThreads), lds, s, a);
+    return hipGetLastError();
+}
+
 template <int D, typename OutT>
 hipError_t launch_f32(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((decode_f32_kernel<D, OutT>), grid, dim3(64), 0, s, a);
@@ -369,7 +669,15 @@ hipError_t launch_f32(const DecodeArgs& a, dim3 grid, hipStream_t s) {
 }
 
 template <int D>
-hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid, hipStream_t s) {
+hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid, hipStream_t s,
+                    bool split) {
+    if (split) {
+        if (in_dtype == PKV_BF16)
+            return out_dtype == PKV_F32 ? launch_split<bf16_t, D, float>(a, s)
+                                        : launch_split<bf16_t, D, bf16_t>(a, s);
+        return out_dtype == PKV_F32 ? launch_split<f16_t, D, float>(a, s)
+                                    : launch_split<f16_t, D, f16_t>(a, s);
+    }
     if (in_dtype == PKV_BF16)
         return out_dtype == PKV_F32 ? launch_mfma<bf16_t, D, float>(a, grid, s)
                                     : launch_mfma<bf16_t, D, bf16_t>(a, grid, s);
@@ -377,6 +685,30 @@ hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid,
         return out_dtype == PKV_F32 ? launch_mfma<f16_t, D, float>(a, grid, s)
                                     : launch_mfma<f16_t, D, f16_t>(a, grid, s);
     return launch_f32<D, float>(a, grid, s);
+}
+
+// Waves per compute unit that the balanced split plans for: the resident capacity of
+// the fp16/bf16 kernel (3 waves per SIMD at its register count). PKV_SPLIT_WAVES_PER_CU
+// overrides it (a tuning knob; it must not change between a decode and its reduce).
+int split_units() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        int per = 12;
+        if (const char* env = std::getenv("PKV_SPLIT_WAVES_PER_CU")) {
+            const int v = std::atoi(env);
+            if (v > 0 && v <= 64) per = v;
+        }
+        cache[dev] = cus * per;
+    }
+    return cache[dev];
 }
 
 }  // namespace pkv
@@ -418,10 +750,23 @@ extern "C" int paged_attention_decode(void* out, float* part_out, float* part_ma
                                 "and be a multiple of %d", x);
     if (!std::isfinite(scale)) return fail(PKV_EINVAL, "paged_attention_decode: scale not finite");
     int part_blocks = max_blocks_per_seq, grid_parts = 1;
-    if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE)
-        return fail(PKV_EINVAL, "paged_attention_decode: partition_size must be 0 or a positive "
-                                "multiple of 16");
-    if (partition_size > 0) {
+    const bool split = partition_size == PKV_PARTITION_AUTO;
+    if (!split && (partition_size < 0 || partition_size % PKV_BLOCK_SIZE))
+        return fail(PKV_EINVAL, "paged_attention_decode: partition_size must be 0, "
+                                "PKV_PARTITION_AUTO or a positive multiple of 16");
+    if (split) {
+        if (in_dtype == PKV_F32)
+            return fail(PKV_ENOTSUP, "paged_attention_decode: PKV_PARTITION_AUTO needs fp16/bf16");
+        if (num_seqs > pkv::kSplitMaxSeqs)
+            return fail(PKV_ENOTSUP, "paged_attention_decode: PKV_PARTITION_AUTO takes at most %d "
+                                     "sequences", pkv::kSplitMaxSeqs);
+        if (int64_t(num_seqs) * num_kv_heads * max_blocks_per_seq >= (int64_t(1) << 31))
+            return fail(PKV_ENOTSUP, "paged_attention_decode: too many tiles for PKV_PARTITION_AUTO");
+        if (max_partitions < 2)
+            return fail(PKV_EINVAL, "paged_attention_decode: PKV_PARTITION_AUTO needs "
+                                    "max_partitions >= 2");
+        grid_parts = 2;   // partial buffers are required below
+    } else if (partition_size > 0) {
         part_blocks = partition_size / PKV_BLOCK_SIZE;
         grid_parts = (max_blocks_per_seq + part_blocks - 1) / part_blocks;
         if (max_partitions < grid_parts)
@@ -454,12 +799,16 @@ extern "C" int paged_attention_decode(void* out, float* part_out, float* part_ma
     a.group = G;
     a.max_blocks = max_blocks_per_seq;
     a.part_blocks = part_blocks;
-    a.max_partitions = partition_size > 0 ? max_partitions : 1;
+    a.max_partitions = partition_size != 0 ? max_partitions : 1;
     a.scale_log2 = scale * pkv::kLog2e;
+    a.num_seqs = num_seqs;
+    a.split.units = split ? pkv::split_units() : 0;
+    a.split.min_share = split ? (max_blocks_per_seq + max_partitions - 2) / (max_partitions - 1) : 0;
     const dim3 grid{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t err = head_dim == 128 ? pkv::dispatch<128>(a, in_dtype, out_dtype, grid, s)
-                                           : pkv::dispatch<64>(a, in_dtype, out_dtype, grid, s);
+    const hipError_t err = head_dim == 128
+                               ? pkv::dispatch<128>(a, in_dtype, out_dtype, grid, s, split)
+                               : pkv::dispatch<64>(a, in_dtype, out_dtype, grid, s, split);
     if (err != hipSuccess)
         return fail(PKV_EHIP, "paged_attention_decode: launch failed: %s", hipGetErrorString(err));
     return pkv::ok();

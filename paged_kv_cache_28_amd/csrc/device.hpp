@@ -71,9 +71,10 @@ template <> struct Mfma<bf16_t> {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                          __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
     }
+    // p is finite here, so the hardware conversion (round to nearest even) applies.
     __device__ __forceinline__ static void split(float p, uint16_t& hi, uint16_t& lo) {
-        hi = f32_to_bf16_bits(p);
-        lo = f32_to_bf16_bits(p - bf16_bits_to_f32(hi));
+        hi = __builtin_bit_cast(uint16_t, (__bf16)p);
+        lo = __builtin_bit_cast(uint16_t, (__bf16)(p - bf16_bits_to_f32(hi)));
     }
 };
 
@@ -94,6 +95,21 @@ template <> struct Mfma<f16_t> {
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
     return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+// max over the four lanes l, l^16, l^32, l^48 with the gfx950 row-swap instructions:
+// permlane16_swap exchanges the odd 16-lane rows of one operand with the even rows of
+// the other, permlane32_swap the upper half of one with the lower half of the other;
+// fed the same value twice, each yields the pair {x[l], x[l^16]} (resp. x[l^32]).
+__device__ __forceinline__ float max_over_rows(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__builtin_bit_cast(float, (unsigned)r16[0]),
+                          __builtin_bit_cast(float, (unsigned)r16[1]));
+    const unsigned v = __builtin_bit_cast(unsigned, y);
+    auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r32[0]),
+                 __builtin_bit_cast(float, (unsigned)r32[1]));
 }
 
 }  // namespace pkv

@@ -60,7 +60,7 @@ def run_decode(gb: GpuBatch, w, partition_size=0, out_dtype=torch.float32, max_p
     dev = gb.q.device
     out = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=dev)
     parts = None
-    if partition_size > 0:
+    if partition_size != 0:
         maxp = max_partitions or pkv.max_partitions_for(gb.tables.shape[1], partition_size)
         parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, dev))
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale,

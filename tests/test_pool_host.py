@@ -195,6 +195,11 @@ def _decode_rc(**kw):
     (dict(kc=None), pkv.PKV_EINVAL),
     (dict(scale=float("inf")), pkv.PKV_EINVAL),
     (dict(ind=7), pkv.PKV_EINVAL),
+    (dict(P=-2, maxp=8), pkv.PKV_EINVAL),
+    (dict(P=pkv.PKV_PARTITION_AUTO, maxp=8), pkv.PKV_EINVAL),          # no partial buffers
+    (dict(P=pkv.PKV_PARTITION_AUTO, maxp=1, po=1 << 20, pm=1 << 20, ps=1 << 20), pkv.PKV_EINVAL),
+    (dict(P=pkv.PKV_PARTITION_AUTO, maxp=8, B=1025), pkv.PKV_ENOTSUP),
+    (dict(P=pkv.PKV_PARTITION_AUTO, maxp=8, ind=pkv.PKV_F32, q_stride=8192), pkv.PKV_ENOTSUP),
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, code):
     assert _decode_rc(**kw) == code
@@ -220,7 +225,10 @@ def test_cache_write_and_reduce_reject_bad_arguments():
                                128, 16, 64, 1024, 1024, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
     assert L.reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 64, 1024, 1024,
                                pkv.PKV_BF16, None) == pkv.PKV_OK
-    assert L.paged_attention_reduce(good["k"], good["k"], good["k"], good["k"], good["s"], 4, 32,
-                                    96, 512, 8, pkv.PKV_F32, None) == pkv.PKV_ENOTSUP
-    assert L.paged_attention_reduce(good["k"], good["k"], good["k"], good["k"], good["s"], 4, 32,
-                                    128, 500, 8, pkv.PKV_F32, None) == pkv.PKV_EINVAL
+    r = lambda *a: L.paged_attention_reduce(good["k"], good["k"], good["k"], good["k"],
+                                            good["s"], *a, None)
+    assert r(4, 32, 8, 96, 64, 512, 8, pkv.PKV_F32) == pkv.PKV_ENOTSUP       # head_dim
+    assert r(4, 32, 8, 128, 64, 500, 8, pkv.PKV_F32) == pkv.PKV_EINVAL       # P % 16
+    assert r(4, 30, 8, 128, 64, 512, 8, pkv.PKV_F32) == pkv.PKV_EINVAL       # Hq % Hkv
+    assert r(4, 32, 8, 128, 64, pkv.PKV_PARTITION_AUTO, 1, pkv.PKV_F32) == pkv.PKV_EINVAL
+    assert r(2000, 32, 8, 128, 64, pkv.PKV_PARTITION_AUTO, 8, pkv.PKV_F32) == pkv.PKV_EINVAL
