@@ -285,6 +285,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
 // (sequence, KV head) at piece boundaries. A piece covering all of its (b, g) writes
 // out; any other piece writes its (o, m, l) record at piece index u - floor(start / s).
 constexpr int kSplitPiecesPerBatch = 4;   // queries staged in LDS per wave and batch
+constexpr int kSplitStage = 2;            // tiles per pipeline stage (two stages per wave)
 
 template <typename T, int D, typename OutT>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a) {
@@ -504,16 +505,28 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
             // the batch continues the previous piece: keep its state, re-point the slot
             piece_slot = 0;
         }
-        // Two tiles per step, both loaded before either is used. An odd count repeats
-        // the last tile with every token masked, so the step has no branch and each
-        // tile's wait covers only its own loads.
-        for (int k = 0; k < cnt; k += 2) {
-            const int k1 = min(k + 1, cnt - 1);
-            KvTile<D> A, B;
-            const bool okA = load(A, k);
-            const bool okB = load(B, k1);
-            compute(A, k, okA);
-            compute(B, k1, okB && k + 1 < cnt);
+        // Two stages of kSplitStage tiles: the loads of the next stage are issued
+        // before the current one is used, so a wave keeps tiles in flight while it
+        // computes. Tiles past the end repeat the last one with every token masked:
+        // the loop has no data-dependent branch, and each wait covers only the
+        // loads it needs.
+        KvTile<D> X[kSplitStage], Y[kSplitStage];
+        bool okX[kSplitStage], okY[kSplitStage];
+        auto load_stage = [&](KvTile<D>* t, bool* ok, int k) {
+#pragma unroll
+            for (int i = 0; i < kSplitStage; ++i) ok[i] = load(t[i], min(k + i, cnt - 1));
+        };
+        auto compute_stage = [&](KvTile<D>* t, const bool* ok, int k) {
+#pragma unroll
+            for (int i = 0; i < kSplitStage; ++i)
+                compute(t[i], min(k + i, cnt - 1), ok[i] && k + i < cnt);
+        };
+        load_stage(X, okX, 0);
+        for (int k = 0; k < cnt; k += 2 * kSplitStage) {
+            load_stage(Y, okY, k + kSplitStage);
+            compute_stage(X, okX, k);
+            load_stage(X, okX, k + 2 * kSplitStage);
+            compute_stage(Y, okY, k + kSplitStage);
         }
         tb += cnt;
     }
@@ -687,9 +700,10 @@ hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid,
     return launch_f32<D, float>(a, grid, s);
 }
 
-// Waves per compute unit that the balanced split plans for: the resident capacity of
-// the fp16/bf16 kernel (3 waves per SIMD at its register count). PKV_SPLIT_WAVES_PER_CU
-// overrides it (a tuning knob; it must not change between a decode and its reduce).
+// Waves per compute unit that the balanced split plans for: one workgroup of four waves
+// (one per SIMD) on every unit. A second workgroup on a unit is served after the first,
+// so its share would finish late. PKV_SPLIT_WAVES_PER_CU overrides the count (a tuning
+// knob; it must not change between a decode and its reduce).
 int split_units() {
     static std::mutex mu;
     static int cache[64] = {0};
@@ -701,7 +715,7 @@ int split_units() {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        int per = 12;
+        int per = 4;
         if (const char* env = std::getenv("PKV_SPLIT_WAVES_PER_CU")) {
             const int v = std::atoi(env);
             if (v > 0 && v <= 64) per = v;

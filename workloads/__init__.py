@@ -51,6 +51,8 @@ class Workload:
     long_frac: float = 0.0
     long_lo: int = 0
     long_hi: int = 0
+    # decode launch: 0 one pass per (sequence, KV head), > 0 fixed context partitions of
+    # that many tokens, -1 the balanced split
     partition_size: int = 0
     num_blocks: int = 0          # 0: sized from the drawn lengths
     # churn
@@ -86,7 +88,7 @@ WORKLOADS = {
     # Llama-3-8B shape: 32 layers, 32q/8kv, d 128, bf16, B 64, n ~ U{128..2048}.
     "llama8b": Workload("llama8b", layers=32, batch=64, num_heads=32, num_kv_heads=8,
                         head_dim=128, dtype="bf16", seed=28002, len_lo=128, len_hi=2048,
-                        partition_size=256),
+                        partition_size=0),
     # Llama-3-70B shape: 80 layers, 64q/8kv, d 128, fp16, B 128; 90% short
     # (300 prompt + up to 100 generated), 10% long (30,000 + up to 4,000).
     "llama70b": Workload("llama70b", layers=80, batch=128, num_heads=64, num_kv_heads=8,
@@ -101,7 +103,7 @@ WORKLOADS = {
     "churn": Workload("churn", layers=32, batch=256, num_heads=32, num_kv_heads=8,
                       head_dim=128, dtype="bf16", seed=28005, pool_bytes=200e9,
                       retire_frac=0.05, share_frac=0.2, prefix_tokens=1024,
-                      prompt_lo=16, prompt_hi=32768, partition_size=512),
+                      prompt_lo=16, prompt_hi=32768, partition_size=-1),
 }
 
 
