@@ -186,13 +186,14 @@ class KVPool:
         _check(lib().kv_pool_create(num_blocks, block_size, num_layers, num_kv_heads, head_dim,
                                     dtype_code(dtype), fo, ctypes.byref(h)))
         self._h = h
+        self._destroy = lib().kv_pool_destroy   # kept: module globals may be gone at exit
         self.num_blocks = num_blocks
         self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
         self.dtype = dtype
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
-            lib().kv_pool_destroy(self._h)
+            self._destroy(self._h)
             self._h = None
 
     __del__ = close

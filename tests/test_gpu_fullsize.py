@@ -1,0 +1,165 @@
+"""Full-size parity: one layer of each workload at its real size, in the launch mode the
+bench uses for it and in the balanced split, checked on sampled outputs.
+
+* slots and block tables: every one, bit-exact against the oracle's pool model;
+* cache write: a random sample of tokens read back through the documented layout,
+  bit-exact against the rows that were written;
+* attention: sampled (sequence, head) rows against the oracle's textbook attention over
+  the sequence's logical K/V (paged equals contiguous is pinned in the oracle tests),
+  max |err| <= 2e-3 on fp32 output (inputs fp16/bf16) and max|err|/max|ref| <= 1e-3.
+
+Inputs are drawn on the GPU by workloads.draw_*_device and copied to the host for the
+oracle; nothing the oracle reads comes from the HIP path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_28_amd as pkv
+import workloads
+
+pytestmark = pytest.mark.gpu
+W = workloads.WORKLOADS
+AUTO = pkv.PKV_PARTITION_AUTO
+
+
+@pytest.fixture(scope="module")
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+class Layer:
+    """One layer of a workload through the library, with its oracle-side twin state."""
+
+    def __init__(self, w, device, layer=0):
+        self.w = w
+        lens = workloads.draw_seq_lens(w).astype(np.int64)
+        B, Hkv, d = len(lens), w.num_kv_heads, w.head_dim
+        nb = workloads.pool_blocks_for(lens)
+        order = workloads.draw_free_order(nb, workloads.rng(w.seed, 1, layer))
+        pool = pkv.kv_pool_create(nb, 1, Hkv, d, w.dtype, free_order=order)
+        model = oracle.PoolModel(nb, order)
+        prompt = np.maximum(lens - 1, 0)
+        ps_p, ps_m = [], []
+        for b in range(B):
+            pool.add_seq(b)
+            model.add_seq(b)
+            ps_p.append(pool.append(b, int(prompt[b])))
+            ps_m += model.append(b, int(prompt[b]))
+        self.prompt_slots = np.concatenate(ps_p).astype(np.int32)
+        assert np.array_equal(self.prompt_slots, np.asarray(ps_m, np.int32)), "prompt slots"
+        self.new_slots = pool.append_batch(list(range(B)))
+        assert self.new_slots.tolist() == [model.append(b, 1)[0] for b in range(B)], "new slots"
+        self.max_blocks = int(-(-lens.max() // 16))
+        self.tables, self.lens = pool.build_tables(list(range(B)), self.max_blocks)
+        mt, ml = model.tables(list(range(B)), self.max_blocks)
+        assert np.array_equal(self.tables, mt) and np.array_equal(self.lens, ml), "tables"
+        self.offsets = np.concatenate([[0], np.cumsum(prompt)])
+        # inputs, on the device
+        self.pk = workloads.draw_tokens_device(int(prompt.sum()), w, (2, layer, 0), device)
+        self.pv = workloads.draw_tokens_device(int(prompt.sum()), w, (2, layer, 1), device)
+        self.nk = workloads.draw_tokens_device(B, w, (2, layer, 2), device)
+        self.nv = workloads.draw_tokens_device(B, w, (2, layer, 3), device)
+        self.q = workloads.draw_q_device(w, (3, layer), device)
+        self.kc, self.vc = pkv.alloc_caches(nb, Hkv, d, w.dtype, device, fill=float("nan"))
+        pkv.reshape_and_cache(self.pk, self.pv, self.kc, self.vc,
+                              torch.from_numpy(self.prompt_slots).to(device))
+        pkv.reshape_and_cache(self.nk, self.nv, self.kc, self.vc,
+                              torch.from_numpy(self.new_slots).to(device))
+        self.tables_d = torch.from_numpy(self.tables).to(device)
+        self.lens_d = torch.from_numpy(self.lens).to(device)
+        self.num_blocks = nb
+        self.device = device
+
+    def decode(self, P):
+        w, dev = self.w, self.device
+        B = len(self.lens)
+        out = torch.full((B, w.num_heads, w.head_dim), float("nan"), dtype=torch.float32,
+                         device=dev)
+        parts = None
+        if P != 0:
+            maxp = pkv.max_partitions_for(self.max_blocks, P)
+            parts = pkv.alloc_partials(B, w.num_heads, w.head_dim, maxp, dev)
+        pkv.decode(out, self.q, self.kc, self.vc, self.tables_d, self.lens_d, w.scale, P, parts)
+        torch.cuda.synchronize()
+        return out
+
+    def logical_kv(self, b, g):
+        """fp64 logical K, V [n_b][d] of (sequence b, KV head g) from the drawn inputs."""
+        lo, hi = int(self.offsets[b]), int(self.offsets[b + 1])
+        k = torch.cat([self.pk[lo:hi, g], self.nk[b:b + 1, g]]).cpu()
+        v = torch.cat([self.pv[lo:hi, g], self.nv[b:b + 1, g]]).cpu()
+        return oracle.to_f64(k, self.w.dtype), oracle.to_f64(v, self.w.dtype)
+
+    def check_cache_sample(self, n=4096, seed=0):
+        """Read a random sample of written tokens back through the documented layout."""
+        w = self.w
+        x = 8 if w.elem_bytes == 2 else 4
+        gen = np.random.default_rng(seed)
+        T = len(self.prompt_slots)
+        pick = gen.choice(T, size=min(n, T), replace=False) if T else np.zeros(0, np.int64)
+        slots = torch.from_numpy(self.prompt_slots[pick].astype(np.int64)).to(self.device)
+        blk, off = slots // 16, slots % 16
+        kv = self.kc.view(self.num_blocks, w.num_kv_heads, w.head_dim // x, 16, x)
+        got_k = kv[blk, :, :, off, :].reshape(len(pick), w.num_kv_heads, w.head_dim)
+        got_v = self.vc[blk, :, :, off]
+        idx = torch.from_numpy(pick).to(self.device)
+        assert torch.equal(got_k.view(torch.int16), self.pk[idx].view(torch.int16))
+        assert torch.equal(got_v.view(torch.int16), self.pv[idx].view(torch.int16))
+        nslots = torch.from_numpy(self.new_slots.astype(np.int64)).to(self.device)
+        got_nk = kv[nslots // 16, :, :, nslots % 16, :].reshape(-1, w.num_kv_heads, w.head_dim)
+        assert torch.equal(got_nk.view(torch.int16), self.nk.view(torch.int16))
+        assert torch.equal(self.vc[nslots // 16, :, :, nslots % 16].view(torch.int16),
+                           self.nv.view(torch.int16))
+
+    def sample_rows(self, n_random, seed=1):
+        w = self.w
+        gen = np.random.default_rng(seed)
+        B = len(self.lens)
+        longest, shortest = int(np.argmax(self.lens)), int(np.argmin(self.lens))
+        rows = {(longest, h) for h in range(w.num_heads)}
+        rows |= {(shortest, h) for h in range(0, w.num_heads, max(1, w.group // 2))}
+        for _ in range(n_random):
+            rows.add((int(gen.integers(B)), int(gen.integers(w.num_heads))))
+        return sorted(rows)
+
+    def check_rows(self, out, rows):
+        w = self.w
+        qf = oracle.to_f64(self.q.cpu(), w.dtype)
+        got = out.cpu().double().numpy()
+        errs, refs = [], []
+        kv_key, K, V = None, None, None      # rows are sorted: reuse one (b, g) at a time
+        for b, h in rows:
+            g = h // w.group
+            if kv_key != (b, g):
+                kv_key = (b, g)
+                K, V = self.logical_kv(b, g)
+            ref, _, _ = oracle.attend(qf[b, h], K, V, w.scale)
+            errs.append(np.abs(got[b, h] - ref).max())
+            refs.append(np.abs(ref).max())
+        err, scale = max(errs), max(refs)
+        assert np.all(np.isfinite(got)), "non-finite output"
+        assert err <= 2e-3, f"max|err| {err:.3e} over {len(rows)} sampled rows"
+        assert err / scale <= 1e-3, f"normalised error {err / scale:.3e}"
+        return err
+
+
+CASES = [("llama8b", 0, 0), ("llama8b", AUTO, 0), ("llama70b", 512, 96), ("llama70b", AUTO, 96),
+         ("long", 512, 24), ("long", AUTO, 24)]
+
+
+@pytest.mark.parametrize("name,P,n_random", CASES,
+                         ids=[f"{n}-{'auto' if p == AUTO else p}" for n, p, _ in CASES])
+def test_full_size_layer(name, P, n_random, device):
+    w = W[name]
+    layer = Layer(w, device)
+    layer.check_cache_sample()
+    out = layer.decode(P)
+    if name == "llama8b":
+        rows = [(b, h) for b in range(w.batch) for h in range(w.num_heads)]
+    else:
+        rows = layer.sample_rows(n_random)
+    layer.check_rows(out, rows)

@@ -156,6 +156,39 @@ def draw_q(w: Workload, gen: np.random.Generator, batch: int | None = None):
     return _cast(x, w.dtype)
 
 
+def _torch_seed(seed: int, stream) -> int:
+    """A 63-bit seed for torch's generator derived from (seed, *stream) via PCG64."""
+    return int(rng(seed, *stream).integers(0, 2 ** 63 - 1))
+
+
+def draw_tokens_device(n_tokens: int, w: Workload, stream, device, std: float | None = None):
+    """K or V rows [n_tokens, num_kv_heads, head_dim] drawn directly on a device with a
+    torch generator seeded from (w.seed, *stream); for the multi-GB workloads. The same
+    (seed, stream, device type) always gives the same values."""
+    import torch
+    std = w.kv_std if std is None else std
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(w.seed, tuple(stream)))
+    x = torch.randn((n_tokens, w.num_kv_heads, w.head_dim), generator=g, device=device,
+                    dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to({"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype])
+
+
+def draw_q_device(w: Workload, stream, device, batch: int | None = None):
+    """Queries [batch, num_heads, head_dim] drawn on a device (see draw_tokens_device)."""
+    import torch
+    b = w.batch if batch is None else batch
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(w.seed, tuple(stream)))
+    x = torch.randn((b, w.num_heads, w.head_dim), generator=g, device=device,
+                    dtype=torch.float32)
+    if w.q_std != 1.0:
+        x.mul_(w.q_std)
+    return x.to({"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype])
+
+
 def pool_blocks_for(lens, growth_tokens: int = 0, slack: float = 0.10) -> int:
     """Pool size (blocks) that holds every sequence plus growth_tokens more each,
     plus a slack fraction of unused blocks."""
