@@ -11,8 +11,11 @@ so each layer's context streams from HBM. Inputs are synthetic (seeded draws of 
 8B-shaped workload) and resident in HBM before timing starts.
 
 Printed: one JSON line. `value` is KV GB/s over the whole step (algorithmic KV bytes
-read by the decode kernels / step time); `roofline` is the decode kernel alone, timed
-with HIP events on its stream; `cpu_baseline` is the CPU oracle on a bounded sample.
+read by the decode kernels / step time), timed with no per-launch instrumentation;
+`roofline` is the decode kernel alone, from a second pass of the same number of steps in
+which the library binds HIP start/stop events to each of its kernel launches
+(pkv_timer_*: the events carry the kernel's own begin/end timestamps); `cpu_baseline`
+is the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--config llama8b]
                        [--partition P] [--no-cpu-baseline]
@@ -42,6 +45,8 @@ def parse():
                     help="auto (balanced split), 0 (single pass) or a multiple of 16; "
                          "default: the workload's setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timer", action="store_true",
+                    help="skip the kernel-timing pass (no roofline figure)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer 8 times (a plain copy of known size, to "
@@ -110,7 +115,7 @@ def main():
 
     # ---------------------------------------------------------------- setup
     lens0 = workloads.draw_seq_lens(w)                 # context at the first step
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + 2 * args.steps        # timed steps + kernel-timing pass
     nb = workloads.pool_blocks_for(lens0, growth_tokens=total_steps)
     order = workloads.draw_free_order(nb, workloads.rng(w.seed, 1))
     pool = pkv.kv_pool_create(nb, L, Hkv, d, w.dtype, free_order=order)
@@ -147,7 +152,7 @@ def main():
 
     kv_bytes_steps = []
 
-    def step(s: int, events=None):
+    def step(s: int):
         k = s & 1
         copied[k].synchronize()                       # H2D of two steps ago has finished
         pool.append_batch(ids, out=h_slot[k].numpy())
@@ -160,46 +165,52 @@ def main():
         for layer in range(L):
             kc, vc = caches[layer]
             pkv.reshape_and_cache(k_new[layer], v_new[layer], kc, vc, d_slot)
-            if events is not None:
-                events[layer][0].record(stream)
             if P != 0:
                 po, pm, ps = parts
                 pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
                                            P, po, pm, ps, maxp)
-                if events is not None:
-                    events[layer][1].record(stream)
                 pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P, Hkv, max_blocks)
             else:
                 pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale)
-                if events is not None:
-                    events[layer][1].record(stream)
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
     kv_bytes_steps.clear()
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
-          for _ in range(args.steps)]
     lens_steps = []
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(args.warmup + s, ev[s])
+        step(args.warmup + s)
         lens_steps.append(h_len[(args.warmup + s) & 1].numpy().copy())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    kv_total = sum(kv_bytes_steps)                # KV bytes of the timed steps only
 
-    dec_ms = [ev[s][layer][0].elapsed_time(ev[s][layer][1]) for s in range(args.steps)
-              for layer in range(L)]
-    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
-    kv_total = sum(kv_bytes_steps)
+    # kernel-timing pass: the same steps again (the contexts keep growing), every launch
+    # carrying its own start/stop events
+    kernel_us = {"decode": None, "reduce": None, "cache_write": None}
+    timing_lens = []
+    if not args.no_kernel_timer:
+        pkv.timer_enable(True)
+        base = args.warmup + args.steps
+        for s in range(args.steps):
+            step(base + s)
+            timing_lens.append(h_len[(base + s) & 1].numpy().copy())
+        torch.cuda.synchronize()
+        for name, entry in (("decode", pkv.PKV_TIMER_DECODE), ("reduce", pkv.PKV_TIMER_REDUCE),
+                            ("cache_write", pkv.PKV_TIMER_CACHE_WRITE)):
+            ms, n = pkv.timer_read(entry)
+            kernel_us[name] = round(ms / n * 1e3, 3) if n else None
+        pkv.timer_enable(False)
+    dec_avg_s = kernel_us["decode"] / 1e6 if kernel_us["decode"] else float("nan")
     # algorithmic bytes of one decode launch: KV once per (seq, KV head), q, out, table rows
     alg = []
-    for ln in lens_steps:
+    for ln in timing_lens:
         ln = ln.astype(np.int64)
         alg.append(int(ln.sum()) * Hkv * d * 2 * e + 2 * B * Hq * d * e +
                    int((-(-ln // 16)).sum()) * 4 + 4 * B)
-    alg_per_launch = sum(alg) / len(alg)
+    alg_per_launch = sum(alg) / len(alg) if alg else float("nan")
     achieved = alg_per_launch / dec_avg_s / 1e9
     value = kv_total / elapsed / 1e9
     result = {
@@ -222,12 +233,17 @@ def main():
                    "pool_blocks": nb, "pool_gb_per_layer": round(nb * w.block_bytes_per_layer / 1e9, 3)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),
-        "decode_kernel_us": round(dec_avg_s * 1e6, 3),
+        "decode_kernel_us": kernel_us["decode"],
+        "reduce_kernel_us": kernel_us["reduce"],
+        "cache_write_kernel_us": kernel_us["cache_write"],
+        "kernel_timing": "HIP start/stop events bound to each kernel launch (library timer), "
+                         "averaged over every launch of the timed steps",
         "cache_state": f"{L} distinct per-layer pools cycled; warm-up {args.warmup} steps excluded",
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1) if alg else None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4) if alg else None, "traffic": None,
                      "kernel": "paged_attention_decode",
-                     "alg_bytes_per_launch": int(alg_per_launch)},
+                     "alg_bytes_per_launch": int(alg_per_launch) if alg else None},
         "cpu_baseline": None,
     }
     result["roofline"]["traffic"] = measured_traffic(w.name, P)

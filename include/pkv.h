@@ -71,6 +71,22 @@ const char* pkv_last_error(void);
 /* Library version string, e.g. "pkv 0.1.0 gfx950". */
 const char* pkv_version(void);
 
+/* ---- kernel timer ----------------------------------------------------------------
+ * Not part of the method: a measuring aid. While enabled, every launch of the timed
+ * entry points carries a HIP start/stop event pair bound to the kernel itself
+ * (hipExtLaunchKernelGGL), so the pair measures that kernel alone without adding
+ * packets to the stream. pkv_timer_read(entry, ...) waits for the pairs recorded since
+ * the last read (or enable) of that entry, returns their summed milliseconds and count,
+ * and resets them. For paged_attention_decode only its main kernel is timed.
+ * Enabling or disabling clears every entry. The events belong to the device that was
+ * current at their first use; time one device per process. Errors: EINVAL, EHIP. */
+#define PKV_TIMER_DECODE 0
+#define PKV_TIMER_REDUCE 1
+#define PKV_TIMER_CACHE_WRITE 2
+#define PKV_TIMER_ENTRIES 3
+int pkv_timer_enable(int32_t enable);
+int pkv_timer_read(int32_t entry, double* total_ms, int64_t* launches);
+
 /* ---- KV bytes per token ------------------------------------------------------------
  * 2 (K and V) x layers x KV heads x head_dim x bytes per element
  * ("Yerel LLM sistemlerinde backpressure ve ölçekleme", section "KV bütçesi": the
@@ -230,9 +246,10 @@ int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v
  *                 ceil(max_blocks_per_seq / (max_partitions - 1)) tiles.
  *                 paged_attention_reduce must follow, with the same arguments: it
  *                 merges the split rows and writes the zero rows of empty sequences.
- *                 and paged_attention_reduce() produces out for those rows.
- *                 Requires part_* non-null and max_partitions >=
- *                 ceil(max_blocks_per_seq * 16 / partition_size).
+ *                 out and part_out must be 16-byte aligned in this mode.
+ *   For partition_size > 0, part_* must be non-null with max_partitions >=
+ *   ceil(max_blocks_per_seq * 16 / partition_size), and paged_attention_reduce()
+ *   produces out for the rows with more than one partition.
  * Supported: head_dim in {64, 128}; in_dtype F16/BF16 with num_heads/num_kv_heads
  * <= 16; in_dtype F32 with num_heads/num_kv_heads <= 8.
  * Errors: EINVAL (nulls, alignment, num_heads % num_kv_heads, block_size != 16,

@@ -78,6 +78,8 @@ def lib():
                                     I64, F, I32, I32, I32, I32, P], ctypes.c_int),
         "paged_attention_reduce": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P],
                                    ctypes.c_int),
+        "pkv_timer_enable": ([I32], ctypes.c_int),
+        "pkv_timer_read": ([I32, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -92,7 +94,8 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "kv_pool_add_seq", "kv_pool_share_prefix", "kv_pool_append", "kv_pool_append_batch",
             "kv_pool_free_seq", "kv_pool_seq_len", "kv_pool_seq_blocks", "kv_pool_free_queue",
             "kv_pool_refcount", "kv_pool_build_tables", "kv_pool_stats", "reshape_and_cache",
-            "paged_attention_decode", "paged_attention_reduce")
+            "paged_attention_decode", "paged_attention_reduce", "pkv_timer_enable",
+            "pkv_timer_read")
 
 
 def _check(rc: int):
@@ -337,6 +340,22 @@ def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partitio
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(seq_lens, "seq_lens"), B, Hq, num_kv_heads, d,
         max_blocks_per_seq, partition_size, P, dtype_code(out.dtype), _stream(out, stream)))
+
+
+# ------------------------------------------------------------------ kernel timer
+PKV_TIMER_DECODE, PKV_TIMER_REDUCE, PKV_TIMER_CACHE_WRITE = 0, 1, 2
+
+
+def timer_enable(on: bool = True):
+    """Bind HIP start/stop events to every later launch of the library's kernels."""
+    _check(lib().pkv_timer_enable(1 if on else 0))
+
+
+def timer_read(entry: int):
+    """(summed kernel milliseconds, launches) of one entry since its last read."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib().pkv_timer_read(entry, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def max_partitions_for(max_blocks: int, partition_size: int) -> int:

@@ -6,10 +6,12 @@
 // One thread moves one 16-byte group of x = 16 / element_bytes dimensions of one
 // (token, KV head): K keeps the group together (cache layout [blk][g][d/x][16][x]),
 // V spreads it over x rows of its [blk][g][d][16] tile. A pure bit copy.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
 #include "status.hpp"
+#include "timer.hpp"
 
 namespace pkv {
 
@@ -85,14 +87,15 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
     const char* vp = static_cast<const char*>(value);
     char* kcp = static_cast<char*>(k_cache);
     char* vcp = static_cast<char*>(v_cache);
+    const pkv::LaunchEvents ev = pkv::timer_events(PKV_TIMER_CACHE_WRITE);
     if (e == 2)
-        hipLaunchKernelGGL(pkv::reshape_and_cache_kernel<2>, dim3(unsigned(grid)), dim3(256), 0, s,
-                           kp, vp, kcp, vcp, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                           num_blocks, key_stride * 2, value_stride * 2);
+        hipExtLaunchKernelGGL(pkv::reshape_and_cache_kernel<2>, dim3(unsigned(grid)), dim3(256), 0,
+                              s, ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
+                              num_kv_heads, head_dim, num_blocks, key_stride * 2, value_stride * 2);
     else
-        hipLaunchKernelGGL(pkv::reshape_and_cache_kernel<4>, dim3(unsigned(grid)), dim3(256), 0, s,
-                           kp, vp, kcp, vcp, slot_mapping, num_tokens, num_kv_heads, head_dim,
-                           num_blocks, key_stride * 4, value_stride * 4);
+        hipExtLaunchKernelGGL(pkv::reshape_and_cache_kernel<4>, dim3(unsigned(grid)), dim3(256), 0,
+                              s, ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
+                              num_kv_heads, head_dim, num_blocks, key_stride * 4, value_stride * 4);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return fail(PKV_EHIP, "reshape_and_cache: launch failed: %s", hipGetErrorString(err));

@@ -31,8 +31,10 @@
 //   C: lane l holds head l%16, dims 16c + 4(l/16) + e: its rescale factor is the
 //      lane's own running max, so the online softmax needs no transposes.
 // fp32 path: plain vector arithmetic, one wave per workgroup (correctness path).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <mutex>
@@ -40,6 +42,7 @@
 #include "device.hpp"
 #include "split.hpp"
 #include "status.hpp"
+#include "timer.hpp"
 
 namespace pkv {
 
@@ -64,6 +67,7 @@ struct DecodeArgs {
     float scale_log2;      // scale * log2(e): logits in base-2 units
     int32_t num_seqs;
     SplitParams split;     // balanced mode only
+    int32_t slots;         // balanced mode: result slots per wave
 };
 
 constexpr float kLn2 = 0.693147180559945309417f;
@@ -281,11 +285,27 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
 // ------------------------------------------------------- fp16 / bf16, balanced split
 // Same per-tile arithmetic as decode_mfma_kernel; the work is cut as described in
 // split.hpp. Each wave is independent: it reads the block ids of up to 64 of its tiles
-// with one vector load (lane k: tile k), then streams the tiles two deep, switching
-// (sequence, KV head) at piece boundaries. A piece covering all of its (b, g) writes
-// out; any other piece writes its (o, m, l) record at piece index u - floor(start / s).
+// with one vector load (lane k: tile k), then streams the tiles, switching (sequence,
+// KV head) at piece boundaries. A piece covering all of its (b, g) is written to out;
+// any other piece becomes an (o, m, l) record at piece index u - floor(start / s).
+//
+// Finished pieces are parked in LDS result slots of the wave and written to HBM only
+// after its last tile (or when the slots are full). On gfx950 one counter tracks both
+// outstanding loads and outstanding stores, so a store issued between tile loads makes
+// every later tile wait for the store's completion as well; parking the results keeps
+// the stream of tile loads free of stores.
 constexpr int kSplitPiecesPerBatch = 4;   // queries staged in LDS per wave and batch
-constexpr int kSplitStage = 2;            // tiles per pipeline stage (two stages per wave)
+constexpr int kSplitStage = 1;            // tiles per pipeline stage (two stages per wave)
+constexpr int kSplitMaxSlots = 8;         // result slots per wave (upper bound)
+constexpr int kSplitWaveLds = 17920;      // LDS bytes per wave: staged queries + slots
+
+// Per-wave LDS of the balanced split: staged queries, then `slots` result slots of
+// (G*D outputs, G reference points, G sums) floats, then 4 ints of metadata per slot.
+__host__ __device__ constexpr int split_q_bytes(int G, int D) { return kSplitPiecesPerBatch * G * D * 2; }
+__host__ __device__ constexpr int split_slot_floats(int G, int D) { return (G * D + 2 * G + 3) & ~3; }
+__host__ __device__ constexpr int split_wave_bytes(int G, int D, int slots) {
+    return split_q_bytes(G, D) + slots * (split_slot_floats(G, D) * 4 + 16);
+}
 
 template <typename T, int D, typename OutT>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a) {
@@ -294,7 +314,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     __shared__ int32_t s_end[kSplitMaxSeqs];
     __shared__ int32_t s_len[kSplitMaxSeqs];
     __shared__ int32_t s_wave[kWaves];
-    extern __shared__ uint16_t s_q[];   // [wave][piece][G][D] staged queries
+    extern __shared__ uint4 s_dyn[];    // per wave: see split_wave_bytes
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, quad = lane >> 4;
     const int G = a.group, hkv = a.num_kv_heads;
@@ -310,7 +330,12 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache);
     const int64_t tile_elems = int64_t(D) * 16;
     const int qpiece = G * D;                              // elements per staged query set
-    uint16_t* my_q = s_q + wave * kSplitPiecesPerBatch * qpiece;
+    char* my_lds = reinterpret_cast<char*>(s_dyn) + wave * split_wave_bytes(G, D, a.slots);
+    uint16_t* my_q = reinterpret_cast<uint16_t*>(my_lds);
+    const int slot_floats = split_slot_floats(G, D);
+    float* slots = reinterpret_cast<float*>(my_lds + split_q_bytes(G, D));
+    int32_t* slot_meta = reinterpret_cast<int32_t*>(slots + a.slots * slot_floats);
+    int nused = 0;   // result slots in use (wave-uniform)
     constexpr float kSlack = 8.0f;
 
     // state of the current piece
@@ -339,32 +364,59 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
         lsum = 0.f;
     };
 
+    // Write the parked results: G*D outputs per slot, four consecutive ones per lane
+    // and store (the G heads of a group are consecutive rows of out).
+    auto flush = [&]() {
+        __builtin_amdgcn_wave_barrier();
+        for (int sl = 0; sl < nused; ++sl) {
+            const float* so = slots + sl * slot_floats;
+            const int b = slot_meta[4 * sl], g = slot_meta[4 * sl + 1], piece = slot_meta[4 * sl + 2];
+            const int64_t head0 = int64_t(b) * a.num_heads + g * G;
+            for (int i = 4 * lane; i < G * D; i += 256) {
+                const float4 v = *reinterpret_cast<const float4*>(so + i);
+                if (piece < 0) {
+                    OutStore<OutT>::st4(a.out, head0 * D + i, v);
+                } else {
+                    const int64_t row = (head0 + i / D) * a.max_partitions + piece;
+                    *reinterpret_cast<float4*>(a.part_out + row * D + i % D) = v;
+                }
+            }
+            if (piece >= 0 && lane < G) {
+                const int64_t row = (head0 + lane) * a.max_partitions + piece;
+                a.part_max[row] = so[G * D + lane];
+                a.part_sum[row] = so[G * D + G + lane];
+            }
+        }
+        nused = 0;
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // Park the finished piece in the next result slot (normalised outputs; the
+    // reference point in natural-log units and the sum for the reduce).
     auto end_piece = [&]() {
         float L = lsum;
         L += __shfl_xor(L, 16, 64);
         L += __shfl_xor(L, 32, 64);
-        if (col >= G) return;
-        const float inv = 1.0f / L;
-        const int hq = seg_g * G + col;
-        if (first_j == 0 && last_j == seg_nblk - 1) {
-            const int64_t o = (int64_t(seg_b) * a.num_heads + hq) * D + 4 * quad;
+        if (nused == a.slots) flush();
+        float* so = slots + nused * slot_floats;
+        if (col < G) {
+            const float inv = 1.0f / L;
 #pragma unroll
             for (int c = 0; c < NPV; ++c)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) OutStore<OutT>::st(a.out, o + 16 * c + e, acc[c][e] * inv);
-        } else {
-            const int piece = u - seg_start / share;
-            const int64_t row = (int64_t(seg_b) * a.num_heads + hq) * a.max_partitions + piece;
-            float* po = a.part_out + row * D + 4 * quad;
-#pragma unroll
-            for (int c = 0; c < NPV; ++c)
-                *reinterpret_cast<float4*>(po + 16 * c) =
+                *reinterpret_cast<float4*>(so + col * D + 16 * c + 4 * quad) =
                     make_float4(acc[c][0] * inv, acc[c][1] * inv, acc[c][2] * inv, acc[c][3] * inv);
             if (quad == 0) {
-                a.part_max[row] = m * kLn2;
-                a.part_sum[row] = L;
+                so[G * D + col] = m * kLn2;
+                so[G * D + G + col] = L;
             }
         }
+        if (lane == 0) {
+            const bool whole = first_j == 0 && last_j == seg_nblk - 1;
+            slot_meta[4 * nused] = seg_b;
+            slot_meta[4 * nused + 1] = seg_g;
+            slot_meta[4 * nused + 2] = whole ? -1 : u - seg_start / share;
+        }
+        ++nused;
     };
 
     int tphys = 0, tbg = 0, tj = 0;   // per-lane metadata of the current batch
@@ -531,6 +583,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
         tb += cnt;
     }
     if (cur_bg >= 0) end_piece();
+    flush();
 }
 
 // ---------------------------------------------------------------------- fp32
@@ -663,21 +716,26 @@ constexpr int kWaves = 4;
 template <typename T, int D, typename OutT>
 hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves>), grid, dim3(kWaves * 64), lds, s, a);
+    const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
+    hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves>), grid, dim3(kWaves * 64), lds, s,
+                          ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
 template <typename T, int D, typename OutT>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
     const int groups = (a.split.units + kSplitThreads / 64 - 1) / (kSplitThreads / 64);
-    const size_t lds = sizeof(uint16_t) * (kSplitThreads / 64) * kSplitPiecesPerBatch * a.group * D;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, OutT>), dim3(groups), dim3(kSplitThreads), lds, s, a);
+    const size_t lds = size_t(kSplitThreads / 64) * split_wave_bytes(a.group, D, a.slots);
+    const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
+    hipExtLaunchKernelGGL((decode_split_kernel<T, D, OutT>), dim3(groups), dim3(kSplitThreads), lds, s,
+                          ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
 template <int D, typename OutT>
 hipError_t launch_f32(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((decode_f32_kernel<D, OutT>), grid, dim3(64), 0, s, a);
+    const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
+    hipExtLaunchKernelGGL((decode_f32_kernel<D, OutT>), grid, dim3(64), 0, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
@@ -700,10 +758,12 @@ hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid,
     return launch_f32<D, float>(a, grid, s);
 }
 
-// Waves per compute unit that the balanced split plans for: one workgroup of four waves
-// (one per SIMD) on every unit. A second workgroup on a unit is served after the first,
-// so its share would finish late. PKV_SPLIT_WAVES_PER_CU overrides the count (a tuning
-// knob; it must not change between a decode and its reduce).
+// Waves per compute unit that the balanced split plans for: two workgroups of four
+// waves (two waves per SIMD) on every unit. With two tiles in flight per wave this keeps
+// enough reads queued to saturate HBM; deeper queues measured slower (the extra reads
+// only add queueing delay and spread the finishing times of the waves).
+// PKV_SPLIT_WAVES_PER_CU overrides the count (a tuning knob; it must not change between
+// a decode and its reduce).
 int split_units() {
     static std::mutex mu;
     static int cache[64] = {0};
@@ -715,7 +775,7 @@ int split_units() {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        int per = 4;
+        int per = 8;
         if (const char* env = std::getenv("PKV_SPLIT_WAVES_PER_CU")) {
             const int v = std::atoi(env);
             if (v > 0 && v <= 64) per = v;
@@ -795,6 +855,9 @@ extern "C" int paged_attention_decode(void* out, float* part_out, float* part_ma
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
          reinterpret_cast<uintptr_t>(v_cache)) & 15)
         return fail(PKV_EINVAL, "paged_attention_decode: q and caches must be 16-byte aligned");
+    if (split && ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(part_out)) & 15))
+        return fail(PKV_EINVAL, "paged_attention_decode: PKV_PARTITION_AUTO needs 16-byte "
+                                "aligned out and part_out");
 
     pkv::DecodeArgs a;
     a.out = out;
@@ -818,6 +881,11 @@ extern "C" int paged_attention_decode(void* out, float* part_out, float* part_ma
     a.num_seqs = num_seqs;
     a.split.units = split ? pkv::split_units() : 0;
     a.split.min_share = split ? (max_blocks_per_seq + max_partitions - 2) / (max_partitions - 1) : 0;
+    {
+        const int slot_bytes = pkv::split_slot_floats(G, head_dim) * 4 + 16;
+        const int room = pkv::kSplitWaveLds - pkv::split_q_bytes(G, head_dim);
+        a.slots = std::min(pkv::kSplitMaxSlots, std::max(1, room / slot_bytes));
+    }
     const dim3 grid{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = head_dim == 128

@@ -39,19 +39,33 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 
 // Output stores in the three supported output types.
 template <typename OutT> struct OutStore;
+// st4 writes elements i .. i + 3 (i a multiple of 4, base 16-byte aligned) in one store.
 template <> struct OutStore<float> {
     __device__ __forceinline__ static void st(void* base, int64_t i, float v) {
         static_cast<float*>(base)[i] = v;
+    }
+    __device__ __forceinline__ static void st4(void* base, int64_t i, float4 v) {
+        *reinterpret_cast<float4*>(static_cast<float*>(base) + i) = v;
     }
 };
 template <> struct OutStore<bf16_t> {
     __device__ __forceinline__ static void st(void* base, int64_t i, float v) {
         static_cast<uint16_t*>(base)[i] = f32_to_bf16_bits(v);
     }
+    __device__ __forceinline__ static void st4(void* base, int64_t i, float4 v) {
+        const uint2 w = make_uint2(uint32_t(f32_to_bf16_bits(v.x)) | (uint32_t(f32_to_bf16_bits(v.y)) << 16),
+                                   uint32_t(f32_to_bf16_bits(v.z)) | (uint32_t(f32_to_bf16_bits(v.w)) << 16));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + i) = w;
+    }
 };
 template <> struct OutStore<f16_t> {
     __device__ __forceinline__ static void st(void* base, int64_t i, float v) {
         static_cast<uint16_t*>(base)[i] = f32_to_f16_bits(v);
+    }
+    __device__ __forceinline__ static void st4(void* base, int64_t i, float4 v) {
+        const uint2 w = make_uint2(uint32_t(f32_to_f16_bits(v.x)) | (uint32_t(f32_to_f16_bits(v.y)) << 16),
+                                   uint32_t(f32_to_f16_bits(v.z)) | (uint32_t(f32_to_f16_bits(v.w)) << 16));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + i) = w;
     }
 };
 

@@ -8,6 +8,7 @@
 //
 // Each query head's row is merged by one wave: lane l owns head_dim / 64
 // consecutive dimensions and the partitions are folded in online.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -15,6 +16,7 @@
 #include "device.hpp"
 #include "split.hpp"
 #include "status.hpp"
+#include "timer.hpp"
 
 namespace pkv {
 
@@ -125,15 +127,16 @@ __global__ __launch_bounds__(kSplitThreads) void reduce_split_kernel(ReduceArgs 
 
 template <int D, typename OutT>
 hipError_t launch_reduce(const ReduceArgs& a, bool split, hipStream_t s) {
+    const LaunchEvents ev = timer_events(PKV_TIMER_REDUCE);
     if (split)
-        hipLaunchKernelGGL((reduce_split_kernel<D, OutT>),
-                           dim3(unsigned(a.num_kv_heads), unsigned(a.num_seqs), 1u),
-                           dim3(kSplitThreads), 0, s, a);
+        hipExtLaunchKernelGGL((reduce_split_kernel<D, OutT>),
+                              dim3(unsigned(a.num_kv_heads), unsigned(a.num_seqs), 1u),
+                              dim3(kSplitThreads), 0, s, ev.start, ev.stop, 0, a);
     else
-        hipLaunchKernelGGL((reduce_kernel<D, OutT>),
-                           dim3(unsigned((a.num_heads + kReduceWaves - 1) / kReduceWaves),
-                                unsigned(a.num_seqs), 1u),
-                           dim3(kSplitThreads), 0, s, a);
+        hipExtLaunchKernelGGL((reduce_kernel<D, OutT>),
+                              dim3(unsigned((a.num_heads + kReduceWaves - 1) / kReduceWaves),
+                                   unsigned(a.num_seqs), 1u),
+                              dim3(kSplitThreads), 0, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
