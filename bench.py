@@ -3,9 +3,10 @@
 A step is the whole hot path for one new token of every sequence:
   host:   allocate_slots for each sequence (kv_pool_append_batch) and the dense block
           tables (kv_pool_build_tables) into pinned buffers, then their copy to HBM;
-  device: for each of the 32 layers, reshape_and_cache of the new tokens' K/V into
-          that layer's pool, paged_attention_decode over the whole context, and the
-          partition reduce.
+  device: for each of the 32 layers, the new tokens' K/V written into that layer's pool
+          and paged_attention_decode over the whole context, in one fused launch
+          (paged_attention_decode_append; --unfused: reshape_and_cache then
+          paged_attention_decode), and the partition reduce when partitioned.
 Every layer has its own K/V pool (about 313 MB, more than the 256 MB Infinity Cache),
 so each layer's context streams from HBM. Inputs are synthetic (seeded draws of the
 8B-shaped workload) and resident in HBM before timing starts.
@@ -45,6 +46,8 @@ def parse():
                     help="auto (balanced split), 0 (single pass) or a multiple of 16; "
                          "default: the workload's setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate reshape_and_cache and paged_attention_decode launches")
     ap.add_argument("--no-kernel-timer", action="store_true",
                     help="skip the kernel-timing pass (no roofline figure)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -162,16 +165,19 @@ def main():
         d_tab.copy_(h_tab[k], non_blocking=True)
         d_len.copy_(h_len[k], non_blocking=True)
         copied[k].record(stream)
+        po, pm, ps = parts if P != 0 else (None, None, None)
         for layer in range(L):
             kc, vc = caches[layer]
-            pkv.reshape_and_cache(k_new[layer], v_new[layer], kc, vc, d_slot)
-            if P != 0:
-                po, pm, ps = parts
+            if args.unfused:
+                pkv.reshape_and_cache(k_new[layer], v_new[layer], kc, vc, d_slot)
                 pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
                                            P, po, pm, ps, maxp)
-                pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P, Hkv, max_blocks)
             else:
-                pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale)
+                pkv.paged_attention_decode_append(out[layer], q[layer], k_new[layer],
+                                                  v_new[layer], d_slot, kc, vc, d_tab, d_len,
+                                                  w.scale, P, po, pm, ps, maxp)
+            if P != 0:
+                pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P, Hkv, max_blocks)
 
     for s in range(args.warmup):
         step(s)
@@ -204,12 +210,14 @@ def main():
             kernel_us[name] = round(ms / n * 1e3, 3) if n else None
         pkv.timer_enable(False)
     dec_avg_s = kernel_us["decode"] / 1e6 if kernel_us["decode"] else float("nan")
-    # algorithmic bytes of one decode launch: KV once per (seq, KV head), q, out, table rows
+    # algorithmic bytes of one decode launch: KV once per (seq, KV head), q, out, table rows;
+    # fused, also the new rows read from the inputs and written to the pool
+    new_rows = 0 if args.unfused else 2 * (2 * B * Hkv * d * e) + 4 * B
     alg = []
     for ln in timing_lens:
         ln = ln.astype(np.int64)
         alg.append(int(ln.sum()) * Hkv * d * 2 * e + 2 * B * Hq * d * e +
-                   int((-(-ln // 16)).sum()) * 4 + 4 * B)
+                   int((-(-ln // 16)).sum()) * 4 + 4 * B + new_rows)
     alg_per_launch = sum(alg) / len(alg) if alg else float("nan")
     achieved = alg_per_launch / dec_avg_s / 1e9
     value = kv_total / elapsed / 1e9
@@ -230,6 +238,7 @@ def main():
                    "num_kv_heads": Hkv, "head_dim": d, "block_size": 16,
                    "seq_len_range": [w.len_lo, w.len_hi],
                    "partition_size": "auto" if P == pkv.PKV_PARTITION_AUTO else P,
+                   "cache_write": "separate launch" if args.unfused else "fused into decode",
                    "pool_blocks": nb, "pool_gb_per_layer": round(nb * w.block_bytes_per_layer / 1e9, 3)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),
@@ -242,7 +251,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1) if alg else None,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4) if alg else None, "traffic": None,
-                     "kernel": "paged_attention_decode",
+                     "kernel": ("paged_attention_decode" if args.unfused
+                                else "paged_attention_decode_append (fused cache write + decode)"),
                      "alg_bytes_per_launch": int(alg_per_launch) if alg else None},
         "cpu_baseline": None,
     }

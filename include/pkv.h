@@ -264,6 +264,40 @@ int paged_attention_decode(void* out, float* part_out, float* part_max, float* p
                            int32_t partition_size, int32_t max_partitions, int32_t in_dtype,
                            int32_t out_dtype, void* stream);
 
+/* paged_attention_decode_append: the decode step of one new token per sequence in one
+ * call: reshape_and_cache of key/value rows b (one token each, num_tokens = num_seqs)
+ * into slot_mapping[b], then paged_attention_decode over seq_lens[b] tokens, which
+ * include the new one (the write-then-attend order of "vLLM ve Triton ile maliyet
+ * optimizasyonu", §03 Yöntem, steps 3-4; the new token attends to itself).
+ *   key, value: [num_seqs][num_kv_heads][head_dim] rows of in_dtype, sequence strides
+ *               key_stride / value_stride in elements (>= num_kv_heads * head_dim,
+ *               multiples of 16 bytes), 16-byte aligned. Borrowed, read only.
+ *   slot_mapping: int32 [num_seqs], device. The result equals the two separate calls
+ *               when slot_mapping[b] is the slot of position seq_lens[b] - 1 of
+ *               sequence b (what kv_pool_append / kv_pool_append_batch return) or is
+ *               negative (nothing written). For any other slot the row is still written
+ *               (slots outside the pool are skipped), but whether position
+ *               seq_lens[b] - 1 then sees the new row or the cache's earlier content is
+ *               unspecified.
+ * For fp16/bf16 with partition_size >= 0 the write is fused into the decode launch:
+ * the workgroup holding the newest position stores the row into the caches and takes it
+ * for the attention from key/value instead of reading it back (as a separate one-row
+ * step, so the fp32 sums run in another order than the two calls'). With fp32 inputs
+ * or PKV_PARTITION_AUTO the write is a separate launch ahead of the decode on the same
+ * stream. The other arguments, the outputs and the errors are those of
+ * paged_attention_decode (and of reshape_and_cache for the new rows); with
+ * partition_size != 0, paged_attention_reduce must follow as for paged_attention_decode. */
+int paged_attention_decode_append(void* out, float* part_out, float* part_max, float* part_sum,
+                                  const void* q, int64_t q_stride, const void* key,
+                                  const void* value, int64_t key_stride, int64_t value_stride,
+                                  const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, float scale, int32_t partition_size,
+                                  int32_t max_partitions, int32_t in_dtype, int32_t out_dtype,
+                                  void* stream);
+
 /* paged_attention_reduce: for every (b, h) whose sequence has more than one
  * partition (np = ceil(seq_lens[b] / partition_size) > 1; with PKV_PARTITION_AUTO, np
  * is the number of pieces of the balanced split, and rows of empty sequences are

@@ -78,6 +78,9 @@ def lib():
                                     I64, F, I32, I32, I32, I32, P], ctypes.c_int),
         "paged_attention_reduce": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P],
                                    ctypes.c_int),
+        "paged_attention_decode_append": ([P, P, P, P, P, I64, P, P, I64, I64, P, P, P, P, P,
+                                           I32, I32, I32, I32, I32, I32, I64, F, I32, I32, I32,
+                                           I32, P], ctypes.c_int),
         "pkv_timer_enable": ([I32], ctypes.c_int),
         "pkv_timer_read": ([I32, P, P], ctypes.c_int),
     }
@@ -94,8 +97,8 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "kv_pool_add_seq", "kv_pool_share_prefix", "kv_pool_append", "kv_pool_append_batch",
             "kv_pool_free_seq", "kv_pool_seq_len", "kv_pool_seq_blocks", "kv_pool_free_queue",
             "kv_pool_refcount", "kv_pool_build_tables", "kv_pool_stats", "reshape_and_cache",
-            "paged_attention_decode", "paged_attention_reduce", "pkv_timer_enable",
-            "pkv_timer_read")
+            "paged_attention_decode", "paged_attention_reduce", "paged_attention_decode_append",
+            "pkv_timer_enable", "pkv_timer_read")
 
 
 def _check(rc: int):
@@ -332,6 +335,38 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
         _stream(q, stream)))
 
 
+def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_cache,
+                                  block_tables, seq_lens, scale: float, partition_size: int = 0,
+                                  part_out=None, part_max=None, part_sum=None,
+                                  max_partitions: int = 0, stream=None):
+    """reshape_and_cache of one new token per sequence (key/value [B][Hkv][d], their
+    slots in slot_mapping int32 [B]) fused with paged_attention_decode over seq_lens,
+    which count the new token. Same outputs and follow-up reduce as
+    paged_attention_decode."""
+    B, Hq, d = q.shape
+    hkv = k_cache.shape[1]
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must have dense heads/dims")
+    for t, nm in ((key, "key"), (value, "value")):
+        if tuple(t.shape) != (B, hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{nm} must be [B][Hkv][d] with dense heads/dims")
+    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
+    if not (block_tables.is_contiguous() and seq_lens.is_contiguous() and
+            slot_mapping.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("block_tables, seq_lens, slot_mapping and the caches must be contiguous")
+    if slot_mapping.numel() < B:
+        raise ValueError("slot_mapping shorter than the batch")
+    _check(lib().paged_attention_decode_append(
+        _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
+        _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(key, "key"),
+        _dev(value, "value"), key.stride(0), value.stride(0), _dev(slot_mapping, "slot_mapping"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, BLOCK_SIZE, block_tables.shape[1],
+        k_cache.shape[0], float(scale), partition_size, max_partitions, dtype_code(q.dtype),
+        dtype_code(out.dtype), _stream(q, stream)))
+
+
 def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partition_size: int,
                            num_kv_heads: int, max_blocks_per_seq: int, stream=None):
     B, Hq, d = out.shape
@@ -374,14 +409,20 @@ def alloc_partials(B: int, Hq: int, d: int, max_partitions: int, device="cuda"):
 
 
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
-           partition_size: int = 0, partials=None, stream=None):
-    """Decode + (if partitioned or balanced) reduce: the launches of one layer's attention."""
-    if partition_size != 0:
-        po, pm, ps = partials
-        paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
-                               partition_size, po, pm, ps, po.shape[2], stream=stream)
-        paged_attention_reduce(out, po, pm, ps, seq_lens, partition_size, k_cache.shape[1],
-                               block_tables.shape[1], stream=stream)
+           partition_size: int = 0, partials=None, stream=None, append=None):
+    """Decode + (if partitioned or balanced) reduce: the launches of one layer's attention.
+    append=(key, value, slot_mapping) writes one new token per sequence first, fused
+    (paged_attention_decode_append)."""
+    po, pm, ps = partials if partition_size != 0 else (None, None, None)
+    maxp = po.shape[2] if po is not None else 0
+    if append is not None:
+        key, value, slots = append
+        paged_attention_decode_append(out, q, key, value, slots, k_cache, v_cache, block_tables,
+                                      seq_lens, scale, partition_size, po, pm, ps, maxp,
+                                      stream=stream)
     else:
         paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
-                               stream=stream)
+                               partition_size, po, pm, ps, maxp, stream=stream)
+    if partition_size != 0:
+        paged_attention_reduce(out, po, pm, ps, seq_lens, partition_size, k_cache.shape[1],
+                               block_tables.shape[1], stream=stream)

@@ -68,6 +68,13 @@ struct DecodeArgs {
     int32_t num_seqs;
     SplitParams split;     // balanced mode only
     int32_t slots;         // balanced mode: result slots per wave
+    // fused append (paged_attention_decode_append): the new token of sequence b has
+    // rows new_k/new_v + b * new_*_stride ([Hkv][D]) and goes to slot_mapping[b]
+    const void* new_k;
+    const void* new_v;
+    const int32_t* slot_mapping;
+    int64_t new_k_stride;
+    int64_t new_v_stride;
 };
 
 constexpr float kLn2 = 0.693147180559945309417f;
@@ -80,6 +87,26 @@ __device__ void write_zero_rows(const DecodeArgs& a, int b, int g) {
         const int h = g * a.group + i / D;
         OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + h) * D + i % D, 0.0f);
     }
+}
+
+// Fused append: copy the new token's K and V rows of KV head g into its slot (the
+// reshape_and_cache layout), with the threads of the calling workgroup. A slot outside
+// the pool (or negative) is skipped, as reshape_and_cache does.
+template <int D>
+__device__ void write_new_token(const DecodeArgs& a, int b, int g, int slot) {
+    if (slot < 0 || int64_t(slot) >= a.num_blocks * 16) return;
+    const int64_t tile = (int64_t(slot) >> 4) * a.num_kv_heads + g;
+    const int off = slot & 15;
+    const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride + int64_t(g) * D;
+    const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride + int64_t(g) * D;
+    uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k_cache));
+    uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v_cache));
+    const int t = threadIdx.x;
+    if (t < D / 8)   // K: [tile][d/8][16][8], one 16-byte group per thread
+        *reinterpret_cast<uint4*>(kc + ((tile * (D / 8) + t) * 16 + off) * 8) =
+            *reinterpret_cast<const uint4*>(krow + 8 * t);
+    for (int d = t; d < D; d += blockDim.x)   // V: [tile][d][16]
+        vc[(tile * D + d) * 16 + off] = vrow[d];
 }
 
 // Merge the per-wave states held in LDS and write out or the partition result.
@@ -123,7 +150,7 @@ struct KvTile {
     uint2 v[D / 16];
 };
 
-template <typename T, int D, typename OutT, int W>
+template <typename T, int D, typename OutT, int W, bool Append>
 __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
     constexpr int NQK = D / 32;   // 16x16x32 steps for S
@@ -148,13 +175,33 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         for (int c = 0; c < NQK; ++c)
             qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + 32 * c) : make_uint4(0, 0, 0, 0);
     }
+    // Fused append: the new token's rows, every lane its share: K dims 32c + 8 quad .. + 7
+    // (as the A operand holds them), V dim 16c + l%16. Kept in registers: reading them
+    // from LDS inside the tile loop made the compiler move the tiles to scratch.
+    int slot = -1;
+    uint4 nk[Append ? NQK : 1];
+    uint32_t nv[Append ? NPV : 1];
+    if constexpr (Append) {
+        slot = a.slot_mapping[b];
+        const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
+                               int64_t(g) * D + 8 * quad;
+        const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
+                               int64_t(g) * D + col;
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) nk[c] = *reinterpret_cast<const uint4*>(krow + 32 * c);
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c];
+    }
 
     int n = a.seq_lens[b];
     n = n < 0 ? 0 : (n > a.max_blocks * 16 ? a.max_blocks * 16 : n);
     const int nblk = (n + 15) >> 4;
     const int blk_begin = p * a.part_blocks;
+    const int jl = n > 0 ? (n - 1) >> 4 : -1;     // block of the newest token
     if (blk_begin >= nblk) {
         if (p == 0) write_zero_rows<OutT, D>(a, b, g);
+        if constexpr (Append)
+            if (p == 0 && n == 0) write_new_token<D>(a, b, g, slot);
         return;
     }
     const int blk_end = min(nblk, blk_begin + a.part_blocks);
@@ -164,6 +211,44 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int first = blk_begin + wave;
     const int nmine = first < blk_end ? (blk_end - first + W - 1) / W : 0;
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    // The wave that holds block jl (w_new) stores the new rows into the slot. When the
+    // slot is the newest position's (what the block pool hands out), the tiles stop one
+    // row short (row n-1 is masked like a row past the end, so it does not matter whether
+    // the store has landed when block jl is read) and w_new adds the new token after its
+    // last tile as a one-row tile from the key/value inputs. Otherwise the cache is read
+    // as it is. lim: rows below it are valid.
+    bool subst = false;
+    int lim = n;
+    int64_t phys_l = 0;
+    const bool own_new = jl >= blk_begin && jl < blk_end;   // this workgroup holds block jl
+    const int w_new = own_new ? (jl - blk_begin) % W : -1;
+    if constexpr (Append) {
+        phys_l = table[jl];
+        subst = slot >= 0 && phys_l >= 0 && phys_l < a.num_blocks &&
+                int64_t(slot) == phys_l * 16 + ((n - 1) & 15);
+        lim = subst ? n - 1 : n;
+    }
+    // The row stores, issued right after w_new's first tile loads: those loads are older,
+    // so their wait does not include the stores, and the stores complete while the wave
+    // streams (issued at the end of the stream they would lengthen the kernel's tail).
+    auto store_new_row = [&]() {
+        if constexpr (Append) {
+            if (wave != w_new || slot < 0 || int64_t(slot) >= a.num_blocks * 16) return;
+            const int64_t tile = (int64_t(slot) >> 4) * a.num_kv_heads + g;
+            const int off = slot & 15;
+            uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k_cache));
+            uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v_cache));
+            if (col == 0) {   // K: group 4c + quad holds dims 32c + 8 quad .. + 7
+#pragma unroll
+                for (int c = 0; c < NQK; ++c)
+                    *reinterpret_cast<uint4*>(kc + ((tile * (D / 8) + 4 * c + quad) * 16 + off) * 8) = nk[c];
+            }
+            if (quad == 0) {  // V: dims 16c + col
+#pragma unroll
+                for (int c = 0; c < NPV; ++c) vc[(tile * D + 16 * c + col) * 16 + off] = uint16_t(nv[c]);
+            }
+        }
+    };
 
     f32x4 acc[NPV];
 #pragma unroll
@@ -207,7 +292,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         const int tok0 = j * 16 + 4 * quad;
         float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = tok0 + e < n ? s[e] * a.scale_log2 : -INFINITY;
+        for (int e = 0; e < 4; ++e) x[e] = tok0 + e < lim ? s[e] * a.scale_log2 : -INFINITY;
         const float bm = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
         const bool move = bm > m + kSlack;          // true on the first block (m = -inf)
         if (__builtin_amdgcn_ballot_w64(move)) {    // wave-uniform, rare after the first block
@@ -218,14 +303,14 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
             for (int c = 0; c < NPV; ++c) acc[c] *= alpha;
             m = mn;
         }
-        float pe[4];
+        float pe[4];   // a masked row gives 0, also while m is still -inf
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = exp2_fast(x[e] - m);
+        for (int e = 0; e < 4; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m);
         lsum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
 
-        if (j * 16 + 16 > n) {   // partly filled last block: rows past n may hold anything
-            const uint32_t keep_lo = (tok0 + 0 < n ? 0x0000ffffu : 0u) | (tok0 + 1 < n ? 0xffff0000u : 0u);
-            const uint32_t keep_hi = (tok0 + 2 < n ? 0x0000ffffu : 0u) | (tok0 + 3 < n ? 0xffff0000u : 0u);
+        if (j * 16 + 16 > lim) {   // partly filled block: rows from lim on may hold anything
+            const uint32_t keep_lo = (tok0 + 0 < lim ? 0x0000ffffu : 0u) | (tok0 + 1 < lim ? 0xffff0000u : 0u);
+            const uint32_t keep_hi = (tok0 + 2 < lim ? 0x0000ffffu : 0u) | (tok0 + 3 < lim ? 0xffff0000u : 0u);
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
                 t.v[c].x &= keep_lo;
@@ -255,12 +340,27 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         tab = lane < cnt ? table[first + (k0 + lane) * W] : 0;
         KvTile<D> A, B;
         bool okA = load(A, 0), okB;
+        if (k0 == 0) store_new_row();
         for (int k = 0; k < cnt; k += 2) {
             okB = load(B, min(k + 1, cnt - 1));
             compute(A, first + (k0 + k) * W, okA);
             if (k + 1 >= cnt) break;
             okA = load(A, min(k + 2, cnt - 1));
             compute(B, first + (k0 + k + 1) * W, okB);
+        }
+    }
+
+    // Fused append, in w_new after its last tile: the new token as a tile whose only
+    // valid row is row 0.
+    if constexpr (Append) {
+        if (wave == w_new && subst) {
+            KvTile<D> t;
+#pragma unroll
+            for (int c = 0; c < NQK; ++c) t.k[c] = col == 0 ? nk[c] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) t.v[c] = make_uint2(quad == 0 ? nv[c] & 0xffffu : 0u, 0u);
+            lim = 1;
+            compute(t, 0, true);
         }
     }
 
@@ -717,8 +817,12 @@ template <typename T, int D, typename OutT>
 hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
     const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
-    hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves>), grid, dim3(kWaves * 64), lds, s,
-                          ev.start, ev.stop, 0, a);
+    if (a.new_k)
+        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true>), grid, dim3(kWaves * 64),
+                              lds, s, ev.start, ev.stop, 0, a);
+    else
+        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, false>), grid, dim3(kWaves * 64),
+                              lds, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
@@ -787,77 +891,109 @@ int split_units() {
 
 }  // namespace pkv
 
-extern "C" int paged_attention_decode(void* out, float* part_out, float* part_max,
-                                      float* part_sum, const void* q, int64_t q_stride,
-                                      const void* k_cache, const void* v_cache,
-                                      const int32_t* block_tables, const int32_t* seq_lens,
-                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, int32_t block_size,
-                                      int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                                      int32_t partition_size, int32_t max_partitions,
-                                      int32_t in_dtype, int32_t out_dtype, void* stream) {
+namespace {
+
+// The new tokens of a fused append (null key: plain decode).
+struct AppendIn {
+    const void* key;
+    const void* value;
+    int64_t key_stride;
+    int64_t value_stride;
+    const int32_t* slot_mapping;
+};
+
+int decode_impl(const char* who, void* out, float* part_out, float* part_max, float* part_sum,
+                const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                int32_t partition_size, int32_t max_partitions, int32_t in_dtype,
+                int32_t out_dtype, const AppendIn& app, void* stream) {
     using pkv::fail;
     const int e = pkv::elem_bytes(in_dtype);
-    if (e == 0) return fail(PKV_EINVAL, "paged_attention_decode: unknown in_dtype %d", in_dtype);
+    if (e == 0) return fail(PKV_EINVAL, "%s: unknown in_dtype %d", who, in_dtype);
     if (pkv::elem_bytes(out_dtype) == 0)
-        return fail(PKV_EINVAL, "paged_attention_decode: unknown out_dtype %d", out_dtype);
+        return fail(PKV_EINVAL, "%s: unknown out_dtype %d", who, out_dtype);
     if (out_dtype != in_dtype && out_dtype != PKV_F32)
-        return fail(PKV_ENOTSUP, "paged_attention_decode: out_dtype must be in_dtype or F32");
-    if (num_seqs < 0) return fail(PKV_EINVAL, "paged_attention_decode: negative num_seqs");
+        return fail(PKV_ENOTSUP, "%s: out_dtype must be in_dtype or F32", who);
+    if (num_seqs < 0) return fail(PKV_EINVAL, "%s: negative num_seqs", who);
     if (block_size != PKV_BLOCK_SIZE)
-        return fail(PKV_EINVAL, "paged_attention_decode: block_size must be 16, got %d", block_size);
+        return fail(PKV_EINVAL, "%s: block_size must be 16, got %d", who, block_size);
     if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
-        return fail(PKV_EINVAL, "paged_attention_decode: num_heads %d not a multiple of "
-                                "num_kv_heads %d", num_heads, num_kv_heads);
+        return fail(PKV_EINVAL, "%s: num_heads %d not a multiple of "
+                                "num_kv_heads %d", who, num_heads, num_kv_heads);
     if (num_seqs > 65535 || num_kv_heads > 65535)
-        return fail(PKV_EINVAL, "paged_attention_decode: num_seqs / num_kv_heads above 65535");
+        return fail(PKV_EINVAL, "%s: num_seqs / num_kv_heads above 65535", who);
     if (head_dim != 64 && head_dim != 128)
-        return fail(PKV_ENOTSUP, "paged_attention_decode: head_dim %d (built: 64, 128)", head_dim);
+        return fail(PKV_ENOTSUP, "%s: head_dim %d (built: 64, 128)", who, head_dim);
     const int G = num_heads / num_kv_heads;
     if ((in_dtype == PKV_F32 && G > 8) || G > 16)
-        return fail(PKV_ENOTSUP, "paged_attention_decode: group size %d too large", G);
+        return fail(PKV_ENOTSUP, "%s: group size %d too large", who, G);
     if (max_blocks_per_seq <= 0 || num_blocks <= 0)
-        return fail(PKV_EINVAL, "paged_attention_decode: bad max_blocks_per_seq / num_blocks");
+        return fail(PKV_EINVAL, "%s: bad max_blocks_per_seq / num_blocks", who);
     const int x = 16 / e;
     if (q_stride < int64_t(num_heads) * head_dim || q_stride % x)
-        return fail(PKV_EINVAL, "paged_attention_decode: q_stride must cover num_heads*head_dim "
-                                "and be a multiple of %d", x);
-    if (!std::isfinite(scale)) return fail(PKV_EINVAL, "paged_attention_decode: scale not finite");
+        return fail(PKV_EINVAL, "%s: q_stride must cover num_heads*head_dim "
+                                "and be a multiple of %d", who, x);
+    if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale not finite", who);
     int part_blocks = max_blocks_per_seq, grid_parts = 1;
     const bool split = partition_size == PKV_PARTITION_AUTO;
     if (!split && (partition_size < 0 || partition_size % PKV_BLOCK_SIZE))
-        return fail(PKV_EINVAL, "paged_attention_decode: partition_size must be 0, "
-                                "PKV_PARTITION_AUTO or a positive multiple of 16");
+        return fail(PKV_EINVAL, "%s: partition_size must be 0, "
+                                "PKV_PARTITION_AUTO or a positive multiple of 16", who);
     if (split) {
         if (in_dtype == PKV_F32)
-            return fail(PKV_ENOTSUP, "paged_attention_decode: PKV_PARTITION_AUTO needs fp16/bf16");
+            return fail(PKV_ENOTSUP, "%s: PKV_PARTITION_AUTO needs fp16/bf16", who);
         if (num_seqs > pkv::kSplitMaxSeqs)
-            return fail(PKV_ENOTSUP, "paged_attention_decode: PKV_PARTITION_AUTO takes at most %d "
-                                     "sequences", pkv::kSplitMaxSeqs);
+            return fail(PKV_ENOTSUP, "%s: PKV_PARTITION_AUTO takes at most %d "
+                                     "sequences", who, pkv::kSplitMaxSeqs);
         if (int64_t(num_seqs) * num_kv_heads * max_blocks_per_seq >= (int64_t(1) << 31))
-            return fail(PKV_ENOTSUP, "paged_attention_decode: too many tiles for PKV_PARTITION_AUTO");
+            return fail(PKV_ENOTSUP, "%s: too many tiles for PKV_PARTITION_AUTO", who);
         if (max_partitions < 2)
-            return fail(PKV_EINVAL, "paged_attention_decode: PKV_PARTITION_AUTO needs "
-                                    "max_partitions >= 2");
+            return fail(PKV_EINVAL, "%s: PKV_PARTITION_AUTO needs "
+                                    "max_partitions >= 2", who);
         grid_parts = 2;   // partial buffers are required below
     } else if (partition_size > 0) {
         part_blocks = partition_size / PKV_BLOCK_SIZE;
         grid_parts = (max_blocks_per_seq + part_blocks - 1) / part_blocks;
         if (max_partitions < grid_parts)
-            return fail(PKV_EINVAL, "paged_attention_decode: max_partitions %d < %d",
+            return fail(PKV_EINVAL, "%s: max_partitions %d < %d", who,
                         max_partitions, grid_parts);
     }
     if (num_seqs == 0) return pkv::ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
-        return fail(PKV_EINVAL, "paged_attention_decode: NULL pointer");
+        return fail(PKV_EINVAL, "%s: NULL pointer", who);
     if (grid_parts > 1 && (!part_out || !part_max || !part_sum))
-        return fail(PKV_EINVAL, "paged_attention_decode: partitioned mode needs part_* buffers");
+        return fail(PKV_EINVAL, "%s: partitioned mode needs part_* buffers", who);
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
          reinterpret_cast<uintptr_t>(v_cache)) & 15)
-        return fail(PKV_EINVAL, "paged_attention_decode: q and caches must be 16-byte aligned");
+        return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned", who);
     if (split && ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(part_out)) & 15))
-        return fail(PKV_EINVAL, "paged_attention_decode: PKV_PARTITION_AUTO needs 16-byte "
-                                "aligned out and part_out");
+        return fail(PKV_EINVAL, "%s: PKV_PARTITION_AUTO needs 16-byte "
+                                "aligned out and part_out", who);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Fused append: validated like reshape_and_cache. The fp32 and balanced-split kernels
+    // take it as a cache-write launch ahead of the decode launch (same result).
+    bool fused = false;
+    if (app.key) {
+        if (!app.value || !app.slot_mapping)
+            return fail(PKV_EINVAL, "%s: NULL key/value/slot_mapping", who);
+        if (app.key_stride < int64_t(num_kv_heads) * head_dim ||
+            app.value_stride < int64_t(num_kv_heads) * head_dim || app.key_stride % x ||
+            app.value_stride % x)
+            return fail(PKV_EINVAL, "%s: key/value sequence strides must cover "
+                                    "num_kv_heads*head_dim and be multiples of %d", who, x);
+        if ((reinterpret_cast<uintptr_t>(app.key) | reinterpret_cast<uintptr_t>(app.value)) & 15)
+            return fail(PKV_EINVAL, "%s: key and value must be 16-byte aligned", who);
+        fused = in_dtype != PKV_F32 && !split;
+        if (!fused) {
+            const int rc = reshape_and_cache(app.key, app.value, const_cast<void*>(k_cache),
+                                             const_cast<void*>(v_cache), app.slot_mapping, num_seqs,
+                                             num_kv_heads, head_dim, block_size, num_blocks,
+                                             app.key_stride, app.value_stride, in_dtype, stream);
+            if (rc != PKV_OK) return rc;
+        }
+    }
 
     pkv::DecodeArgs a;
     a.out = out;
@@ -886,12 +1022,51 @@ extern "C" int paged_attention_decode(void* out, float* part_out, float* part_ma
         const int room = pkv::kSplitWaveLds - pkv::split_q_bytes(G, head_dim);
         a.slots = std::min(pkv::kSplitMaxSlots, std::max(1, room / slot_bytes));
     }
+    a.new_k = fused ? app.key : nullptr;
+    a.new_v = fused ? app.value : nullptr;
+    a.slot_mapping = fused ? app.slot_mapping : nullptr;
+    a.new_k_stride = app.key_stride;
+    a.new_v_stride = app.value_stride;
     const dim3 grid{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
-    hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = head_dim == 128
                                ? pkv::dispatch<128>(a, in_dtype, out_dtype, grid, s, split)
                                : pkv::dispatch<64>(a, in_dtype, out_dtype, grid, s, split);
     if (err != hipSuccess)
-        return fail(PKV_EHIP, "paged_attention_decode: launch failed: %s", hipGetErrorString(err));
+        return fail(PKV_EHIP, "%s: launch failed: %s", who, hipGetErrorString(err));
     return pkv::ok();
+}
+
+}  // namespace
+
+extern "C" int paged_attention_decode(void* out, float* part_out, float* part_max,
+                                      float* part_sum, const void* q, int64_t q_stride,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                      int32_t partition_size, int32_t max_partitions,
+                                      int32_t in_dtype, int32_t out_dtype, void* stream) {
+    return decode_impl("paged_attention_decode", out, part_out, part_max, part_sum, q, q_stride,
+                       k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                       head_dim, block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
+                       max_partitions, in_dtype, out_dtype, AppendIn{nullptr, nullptr, 0, 0, nullptr},
+                       stream);
+}
+
+extern "C" int paged_attention_decode_append(
+    void* out, float* part_out, float* part_max, float* part_sum, const void* q, int64_t q_stride,
+    const void* key, const void* value, int64_t key_stride, int64_t value_stride,
+    const int32_t* slot_mapping, void* k_cache, void* v_cache, const int32_t* block_tables,
+    const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    float scale, int32_t partition_size, int32_t max_partitions, int32_t in_dtype,
+    int32_t out_dtype, void* stream) {
+    if (num_seqs > 0 && !key)
+        return pkv::fail(PKV_EINVAL, "paged_attention_decode_append: NULL key");
+    return decode_impl("paged_attention_decode_append", out, part_out, part_max, part_sum, q,
+                       q_stride, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       partition_size, max_partitions, in_dtype, out_dtype,
+                       AppendIn{key, value, key_stride, value_stride, slot_mapping}, stream);
 }

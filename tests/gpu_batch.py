@@ -26,7 +26,8 @@ class GpuBatch:
     lens_d: torch.Tensor
 
 
-def build(ob, device="cuda", fill=float("nan")) -> GpuBatch:
+def build(ob, device="cuda", fill=float("nan"), write_new: bool = True) -> GpuBatch:
+    """write_new=False leaves the new tokens' slots unwritten (for the fused append)."""
     w = ob.w
     B = len(ob.lens)
     pool = pkv.kv_pool_create(ob.num_blocks, 1, w.num_kv_heads, w.head_dim, w.dtype,
@@ -47,8 +48,9 @@ def build(ob, device="cuda", fill=float("nan")) -> GpuBatch:
     if len(prompt_slots):
         pkv.reshape_and_cache(ob.prompt_k.to(device), ob.prompt_v.to(device), kc, vc,
                               torch.from_numpy(prompt_slots).to(device))
-    pkv.reshape_and_cache(ob.new_k.to(device), ob.new_v.to(device), kc, vc,
-                          torch.from_numpy(new).to(device))
+    if write_new:
+        pkv.reshape_and_cache(ob.new_k.to(device), ob.new_v.to(device), kc, vc,
+                              torch.from_numpy(new).to(device))
     return GpuBatch(pool, prompt_slots, new, tables, lens, kc, vc, ob.q.to(device),
                     torch.from_numpy(tables).to(device), torch.from_numpy(lens).to(device))
 
