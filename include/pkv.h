@@ -306,8 +306,9 @@ int paged_attention_decode_append(void* out, float* part_out, float* part_max, f
  *     out[b][h] = sum_p w_p part_out[p] / sum_p w_p        (p < np only)
  * Rows with np <= 1 are not touched (the decode kernel wrote them). Buffers and
  * num_kv_heads, max_blocks_per_seq, partition_size, max_partitions are those of the
- * paged_attention_decode call; out_dtype in {F32, F16, BF16}. Errors: EINVAL,
- * ENOTSUP, EHIP. */
+ * paged_attention_decode call; out_dtype in {F32, F16, BF16}; out and part_out must be
+ * 16-byte aligned. Each row is merged in 32-dimension slices, one workgroup per
+ * (slice, head, sequence), reading every record once. Errors: EINVAL, ENOTSUP, EHIP. */
 int paged_attention_reduce(void* out, const float* part_out, const float* part_max,
                            const float* part_sum, const int32_t* seq_lens, int32_t num_seqs,
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -27,6 +27,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return uint16_t(u >> 16);
 }
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+    // The empty asm pins f as an fp32 value: without it the compiler may fuse the
+    // multiply that produced f into the conversion (v_fma_mix*), rounding once from
+    // the exact product instead of from the fp32 result.
+    asm("" : "+v"(f));
     _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
     return __builtin_bit_cast(uint16_t, h);
 }

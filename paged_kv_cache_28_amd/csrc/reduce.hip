@@ -6,8 +6,8 @@
 // softmax, evaluated piecewise: the attention math itself is unchanged
 // ("vLLM ve Triton ile maliyet optimizasyonu", §03 Yöntem, closing paragraphs).
 //
-// Each query head's row is merged by one wave: lane l owns head_dim / 64
-// consecutive dimensions and the partitions are folded in online.
+// Each query head's row is merged in 32-dimension slices, one workgroup per slice; the
+// records are folded in online by 32 groups of threads and combined through LDS.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -36,107 +36,126 @@ struct ReduceArgs {
 };
 
 constexpr float kLog2eR = 1.44269504088896340736f;
-constexpr int kReduceWaves = kSplitThreads / 64;
 
-// Merge the np partial records of row (b, h) with one wave: lane l owns D / 64
-// consecutive dimensions; the records' reference points and sums are read 64 at a
-// time, one per lane, and merged online (running maximum of the reference points).
-template <int D, typename OutT>
-__device__ void merge_row(const ReduceArgs& a, int b, int h, int np) {
-    constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t(b) * a.num_heads + h) * a.max_partitions;
-    float acc[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    float M = -INFINITY, wsum = 0.f;
-    for (int p0 = 0; p0 < np; p0 += 64) {
-        const int cnt = min(64, np - p0);
-        const bool live = lane < cnt;
-        const float pm = live ? a.part_max[row + p0 + lane] : -INFINITY;
-        const float ps = live ? a.part_sum[row + p0 + lane] : 0.f;
-        float mc = pm;
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) mc = fmaxf(mc, __shfl_xor(mc, s, 64));
-        const float mn = fmaxf(M, mc);
-        const float alpha = exp2_fast((M - mn) * kLog2eR);   // 0 on the first chunk
-#pragma unroll
-        for (int k = 0; k < PER; ++k) acc[k] *= alpha;
-        wsum *= alpha;
-        M = mn;
-        const float w = live ? exp2_fast((pm - M) * kLog2eR) * ps : 0.f;
-        wsum += w;
-        const float* o = a.part_out + (row + p0) * D + lane * PER;
-#pragma unroll 8
-        for (int k = 0; k < cnt; ++k) {
-            const float wk = __builtin_bit_cast(float,
-                __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-            if constexpr (PER == 2) {
-                const float2 v = *reinterpret_cast<const float2*>(o + int64_t(k) * D);
-                acc[0] += wk * v.x;
-                acc[1] += wk * v.y;
-            } else {
-#pragma unroll
-                for (int e = 0; e < PER; ++e) acc[e] += wk * o[int64_t(k) * D + e];
-            }
+// Row (b, h) is cut into slices of S dimensions, one workgroup each. Thread t owns the
+// four dimensions 4 (t % (S/4)) .. + 3 of the slice for the records p = t / (S/4)
+// (mod 256 / (S/4)): it folds them in online (running maximum of the reference points),
+// and the record groups are then combined through LDS. Every record is read once, in
+// one pass, with many records in flight per workgroup. Fixed partitions (many records
+// per row) use S = 32; the balanced split (few records per row, and a plan prefix to
+// compute per workgroup) uses whole rows, S = D.
+template <int D, typename OutT, bool Split, int S>
+__global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceArgs a) {
+    constexpr int kDimLanes = S / 4;                // threads per record (float4 each)
+    constexpr int kRecGroups = 256 / kDimLanes;     // record groups per workgroup
+    __shared__ float s_m[kRecGroups][kDimLanes];
+    __shared__ float s_w[kRecGroups][kDimLanes];
+    __shared__ float4 s_o[kRecGroups][kDimLanes];
+    __shared__ int32_t s_red[2 * 4];
+    const int slice = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int t = threadIdx.x, dl = t % kDimLanes, rg = t / kDimLanes;
+    const int dim0 = slice * S + 4 * dl;
+    const int hkv = a.num_kv_heads, G = a.num_heads / hkv, g = h / G;
+    const int max_len = a.max_blocks * 16;
+
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > max_len ? max_len : n);
+    int np;
+    if constexpr (Split) {
+        // the plan of the decode launch: this (b, g)'s first tile and the share s
+        int before = 0, total = 0;
+        for (int i = t; i < a.num_seqs; i += 256) {
+            int m = a.seq_lens[i];
+            m = m < 0 ? 0 : (m > max_len ? max_len : m);
+            const int tiles = hkv * ((m + 15) >> 4);
+            total += tiles;
+            before += i < b ? tiles : 0;
         }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            total += __shfl_xor(total, d, 64);
+            before += __shfl_xor(before, d, 64);
+        }
+        if ((t & 63) == 0) {
+            s_red[t >> 6] = total;
+            s_red[4 + (t >> 6)] = before;
+        }
+        __syncthreads();
+        total = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+        before = s_red[4] + s_red[5] + s_red[6] + s_red[7];
+        if (n == 0) {   // empty sequence: no tile, so no piece wrote its row
+            if (rg == 0) OutStore<OutT>::st4(a.out, (int64_t(b) * a.num_heads + h) * D + dim0,
+                                              make_float4(0.f, 0.f, 0.f, 0.f));
+            return;
+        }
+        const int share = split_share(total, a.split);
+        const int nblk = (n + 15) >> 4;
+        const int start = before + g * nblk;
+        np = (start + nblk - 1) / share - start / share + 1;
+    } else {
+        if (n <= a.part_tokens) return;   // one partition (or none): decode wrote out
+        np = (n + a.part_tokens - 1) / a.part_tokens;
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) wsum += __shfl_xor(wsum, s, 64);
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-        OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + h) * D + lane * PER + k, acc[k] * inv);
-}
-
-// Fixed partitions: each wave merges one query head, np = ceil(n / P).
-template <int D, typename OutT>
-__global__ __launch_bounds__(kSplitThreads) void reduce_kernel(ReduceArgs a) {
-    const int h = blockIdx.x * kReduceWaves + (threadIdx.x >> 6), b = blockIdx.y;
-    if (h >= a.num_heads) return;
-    const int n = a.seq_lens[b];
-    if (n <= a.part_tokens) return;   // one partition (or none): decode wrote out
-    int np = (n + a.part_tokens - 1) / a.part_tokens;
     np = np > a.max_partitions ? a.max_partitions : np;
-    merge_row<D, OutT>(a, b, h, np);
-}
-
-// Balanced split: one workgroup per (KV head, sequence); its waves merge the G query
-// heads of the group; pieces come from the same plan as the decode launch.
-template <int D, typename OutT>
-__global__ __launch_bounds__(kSplitThreads) void reduce_split_kernel(ReduceArgs a) {
-    __shared__ int32_t s_end[kSplitMaxSeqs];
-    __shared__ int32_t s_len[kSplitMaxSeqs];
-    __shared__ int32_t s_wave[kReduceWaves];
-    const int g = blockIdx.x, b = blockIdx.y;
-    const int hkv = a.num_kv_heads, G = a.num_heads / hkv;
-    const int total = split_scan(a.seq_lens, a.num_seqs, hkv, a.max_blocks * 16, s_end, s_len, s_wave);
-    const int share = split_share(total, a.split);
-    const int n = s_len[b];
-    if (n == 0) {   // empty sequence: no tile, so no piece wrote its rows
-        for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-            OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + g * G + i / D) * D + i % D, 0.f);
-        return;
-    }
-    const int nblk = (n + 15) >> 4;
-    const int start = (b ? s_end[b - 1] : 0) + g * nblk;
-    const int np = (start + nblk - 1) / share - start / share + 1;
     if (np <= 1) return;
-    for (int hh = threadIdx.x >> 6; hh < G; hh += kReduceWaves) merge_row<D, OutT>(a, b, g * G + hh, np);
+
+    const int64_t row = (int64_t(b) * a.num_heads + h) * a.max_partitions;
+    float m = -INFINITY, w = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+    for (int p = rg; p < np; p += kRecGroups) {
+        const float mp = a.part_max[row + p] * kLog2eR;   // base-2 units
+        const float lp = a.part_sum[row + p];
+        const float4 v = *reinterpret_cast<const float4*>(a.part_out + (row + p) * D + dim0);
+        const float mn = fmaxf(m, mp);
+        const float s1 = m == -INFINITY ? 0.f : exp2_fast(m - mn);
+        const float s2 = (mp == -INFINITY ? 0.f : exp2_fast(mp - mn)) * lp;
+        o.x = o.x * s1 + s2 * v.x;
+        o.y = o.y * s1 + s2 * v.y;
+        o.z = o.z * s1 + s2 * v.z;
+        o.w = o.w * s1 + s2 * v.w;
+        w = w * s1 + s2;
+        m = mn;
+    }
+    s_m[rg][dl] = m;
+    s_w[rg][dl] = w;
+    s_o[rg][dl] = o;
+    __syncthreads();
+    if (rg != 0) return;
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int r = 0; r < kRecGroups; ++r) M = fmaxf(M, s_m[r][dl]);
+    float W = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int r = 0; r < kRecGroups; ++r) {
+        const float mr = s_m[r][dl];
+        const float f = mr == -INFINITY ? 0.f : exp2_fast(mr - M);   // groups with no record
+        const float4 v = s_o[r][dl];
+        W += f * s_w[r][dl];
+        O.x += f * v.x;
+        O.y += f * v.y;
+        O.z += f * v.z;
+        O.w += f * v.w;
+    }
+    const float inv = 1.f / W;
+    OutStore<OutT>::st4(a.out, (int64_t(b) * a.num_heads + h) * D + dim0,
+                        make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv));
 }
 
 template <int D, typename OutT>
 hipError_t launch_reduce(const ReduceArgs& a, bool split, hipStream_t s) {
     const LaunchEvents ev = timer_events(PKV_TIMER_REDUCE);
+    constexpr int kFixedSlice = 32;
     if (split)
-        hipExtLaunchKernelGGL((reduce_split_kernel<D, OutT>),
-                              dim3(unsigned(a.num_kv_heads), unsigned(a.num_seqs), 1u),
-                              dim3(kSplitThreads), 0, s, ev.start, ev.stop, 0, a);
+        hipExtLaunchKernelGGL((reduce_rows_kernel<D, OutT, true, D>),
+                              dim3(1u, unsigned(a.num_heads), unsigned(a.num_seqs)), dim3(256), 0, s,
+                              ev.start, ev.stop, 0, a);
     else
-        hipExtLaunchKernelGGL((reduce_kernel<D, OutT>),
-                              dim3(unsigned((a.num_heads + kReduceWaves - 1) / kReduceWaves),
-                                   unsigned(a.num_seqs), 1u),
-                              dim3(kSplitThreads), 0, s, ev.start, ev.stop, 0, a);
+        hipExtLaunchKernelGGL((reduce_rows_kernel<D, OutT, false, kFixedSlice>),
+                              dim3(unsigned(D / kFixedSlice), unsigned(a.num_heads),
+                                   unsigned(a.num_seqs)),
+                              dim3(256), 0, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
@@ -158,7 +177,7 @@ extern "C" int paged_attention_reduce(void* out, const float* part_out, const fl
     using pkv::fail;
     if (pkv::elem_bytes(out_dtype) == 0)
         return fail(PKV_EINVAL, "paged_attention_reduce: unknown out_dtype %d", out_dtype);
-    if (num_seqs < 0 || num_seqs > 65535 || num_heads <= 0 || num_kv_heads <= 0 ||
+    if (num_seqs < 0 || num_seqs > 65535 || num_heads <= 0 || num_heads > 65535 || num_kv_heads <= 0 ||
         num_heads % num_kv_heads || max_blocks_per_seq <= 0)
         return fail(PKV_EINVAL, "paged_attention_reduce: bad num_seqs / heads / max_blocks");
     if (head_dim != 64 && head_dim != 128)
@@ -175,8 +194,8 @@ extern "C" int paged_attention_reduce(void* out, const float* part_out, const fl
     if (num_seqs == 0) return pkv::ok();
     if (!out || !part_out || !part_max || !part_sum || !seq_lens)
         return fail(PKV_EINVAL, "paged_attention_reduce: NULL pointer");
-    if (reinterpret_cast<uintptr_t>(part_out) & 7)
-        return fail(PKV_EINVAL, "paged_attention_reduce: part_out must be 8-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(part_out) | reinterpret_cast<uintptr_t>(out)) & 15)
+        return fail(PKV_EINVAL, "paged_attention_reduce: part_out and out must be 16-byte aligned");
     pkv::ReduceArgs a;
     a.out = out;
     a.part_out = part_out;

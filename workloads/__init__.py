@@ -90,10 +90,11 @@ WORKLOADS = {
                         head_dim=128, dtype="bf16", seed=28002, len_lo=128, len_hi=2048,
                         partition_size=0),
     # Llama-3-70B shape: 80 layers, 64q/8kv, d 128, fp16, B 128; 90% short
-    # (300 prompt + up to 100 generated), 10% long (30,000 + up to 4,000).
+    # (300 prompt + up to 100 generated), 10% long (30,000 + up to 4,000). The ragged mix
+    # runs best in the balanced split.
     "llama70b": Workload("llama70b", layers=80, batch=128, num_heads=64, num_kv_heads=8,
                          head_dim=128, dtype="f16", seed=28003, len_lo=300, len_hi=400,
-                         long_frac=0.1, long_lo=30000, long_hi=34000, partition_size=512),
+                         long_frac=0.1, long_lo=30000, long_hi=34000, partition_size=-1),
     # Long-context split-K: 1 layer, B 4, 32q/8kv, bf16, n ~ U{131072..262144},
     # 512-token partitions, K/V ~ N(0, 0.5^2).
     "long": Workload("long", layers=1, batch=4, num_heads=32, num_kv_heads=8, head_dim=128,
