@@ -57,15 +57,17 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(workload: str, partition_size: int):
+def measured_traffic(workload: str, partition_size: int, fused: bool):
     """HBM bytes per decode launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE runs recorded in
     profiles/ (scaled by the copy calibration), or None if those counters were taken for
     another workload/mode or for kernel sources other than the ones built now."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
-    if partition_size != 0 or not os.path.exists(path):
+    if partition_size != 0 or not fused or not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if rec.get("mode") != "single pass, fused append":
+        return None
     csrc = os.path.join(ROOT, "paged_kv_cache_28_amd", "csrc")
     src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("decode.hip", "device.hpp"))
     if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
@@ -238,7 +240,9 @@ def main():
                    "num_kv_heads": Hkv, "head_dim": d, "block_size": 16,
                    "seq_len_range": [w.len_lo, w.len_hi],
                    "partition_size": "auto" if P == pkv.PKV_PARTITION_AUTO else P,
-                   "cache_write": "separate launch" if args.unfused else "fused into decode",
+                   "cache_write": ("separate launch" if args.unfused else
+                                   "paged_attention_decode_append: separate launch in the balanced split"
+                                   if P == pkv.PKV_PARTITION_AUTO else "fused into the decode launch"),
                    "pool_blocks": nb, "pool_gb_per_layer": round(nb * w.block_bytes_per_layer / 1e9, 3)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),
@@ -256,7 +260,7 @@ def main():
                      "alg_bytes_per_launch": int(alg_per_launch) if alg else None},
         "cpu_baseline": None,
     }
-    result["roofline"]["traffic"] = measured_traffic(w.name, P)
+    result["roofline"]["traffic"] = measured_traffic(w.name, P, not args.unfused)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, caches[0], q[0], d_tab, d_len, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -193,10 +193,17 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c];
     }
 
+    // This wave takes blocks first, first + W, ... of its partition. The block ids of its
+    // first 64 are read before the length is known (the table row has max_blocks
+    // entries): the id load does not wait for the length load.
+    const int blk_begin = p * a.part_blocks;
+    const int first = blk_begin + wave;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    const int tab0 = first + lane * W < a.max_blocks ? table[first + lane * W] : -1;
+
     int n = a.seq_lens[b];
     n = n < 0 ? 0 : (n > a.max_blocks * 16 ? a.max_blocks * 16 : n);
     const int nblk = (n + 15) >> 4;
-    const int blk_begin = p * a.part_blocks;
     const int jl = n > 0 ? (n - 1) >> 4 : -1;     // block of the newest token
     if (blk_begin >= nblk) {
         if (p == 0) write_zero_rows<OutT, D>(a, b, g);
@@ -207,27 +214,18 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int blk_end = min(nblk, blk_begin + a.part_blocks);
     const bool direct = nblk <= a.part_blocks;
 
-    // This wave takes blocks first, first + W, ... (nmine of them).
-    const int first = blk_begin + wave;
     const int nmine = first < blk_end ? (blk_end - first + W - 1) / W : 0;
-    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
     // The wave that holds block jl (w_new) stores the new rows into the slot. When the
     // slot is the newest position's (what the block pool hands out), the tiles stop one
     // row short (row n-1 is masked like a row past the end, so it does not matter whether
     // the store has landed when block jl is read) and w_new adds the new token after its
     // last tile as a one-row tile from the key/value inputs. Otherwise the cache is read
     // as it is. lim: rows below it are valid.
-    bool subst = false;
+    bool subst = false;   // set by w_new when it reaches the table segment holding jl
     int lim = n;
-    int64_t phys_l = 0;
     const bool own_new = jl >= blk_begin && jl < blk_end;   // this workgroup holds block jl
     const int w_new = own_new ? (jl - blk_begin) % W : -1;
-    if constexpr (Append) {
-        phys_l = table[jl];
-        subst = slot >= 0 && phys_l >= 0 && phys_l < a.num_blocks &&
-                int64_t(slot) == phys_l * 16 + ((n - 1) & 15);
-        lim = subst ? n - 1 : n;
-    }
+    const int k_new = own_new ? (jl - first) / W : -1;      // jl's index in w_new's list
     // The row stores, issued right after w_new's first tile loads: those loads are older,
     // so their wait does not include the stores, and the stores complete while the wave
     // streams (issued at the end of the stream they would lengthen the kernel's tail).
@@ -337,7 +335,15 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     // the wait for the current tile never waits for the next.
     for (int k0 = 0; k0 < nmine; k0 += 64) {
         const int cnt = min(64, nmine - k0);
-        tab = lane < cnt ? table[first + (k0 + lane) * W] : 0;
+        tab = k0 == 0 ? tab0 : (lane < cnt ? table[first + (k0 + lane) * W] : 0);
+        if constexpr (Append) {
+            if (wave == w_new && k_new >= k0 && k_new < k0 + 64) {   // wave-uniform
+                const int64_t phys_l = __builtin_amdgcn_readlane(tab, k_new - k0);
+                subst = slot >= 0 && phys_l >= 0 && phys_l < a.num_blocks &&
+                        int64_t(slot) == phys_l * 16 + ((n - 1) & 15);
+                lim = subst ? n - 1 : n;
+            }
+        }
         KvTile<D> A, B;
         bool okA = load(A, 0), okB;
         if (k0 == 0) store_new_row();
