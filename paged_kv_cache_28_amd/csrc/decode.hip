@@ -68,6 +68,12 @@ struct DecodeArgs {
     int32_t num_seqs;
     SplitParams split;     // balanced mode only
     int32_t slots;         // balanced mode: result slots per wave
+    // Grid order of the single-pass / partitioned kernels. Consecutive workgroups go to
+    // different XCDs. With fewer than 8 partitions per sequence, partition-fastest order
+    // would put every partition 0 on the same few XCDs, so the grid is (KV head, sequence,
+    // partition); with 8 or more it is (partition, KV head, sequence), which measured
+    // faster on long contexts.
+    int32_t heads_fastest;
     // fused append (paged_attention_decode_append): the new token of sequence b has
     // rows new_k/new_v + b * new_*_stride ([Hkv][D]) and goes to slot_mapping[b]
     const void* new_k;
@@ -161,7 +167,9 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     float* sm_o = lds + 2 * W * 16;     // [W][G][D]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
+    const int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
+    const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
     const int G = a.group;
     const int col = lane & 15, quad = lane >> 4;
 
@@ -706,7 +714,9 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     __shared__ float sm[1][16], sl[1][16];
 
     const int lane = threadIdx.x;
-    const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
+    const int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
+    const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
     const int G = a.group;
     int n = a.seq_lens[b];
     n = n < 0 ? 0 : (n > a.max_blocks * 16 ? a.max_blocks * 16 : n);
@@ -965,6 +975,7 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
         if (max_partitions < grid_parts)
             return fail(PKV_EINVAL, "%s: max_partitions %d < %d", who,
                         max_partitions, grid_parts);
+
     }
     if (num_seqs == 0) return pkv::ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
@@ -1033,7 +1044,10 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
     a.slot_mapping = fused ? app.slot_mapping : nullptr;
     a.new_k_stride = app.key_stride;
     a.new_v_stride = app.value_stride;
-    const dim3 grid{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
+    a.heads_fastest = grid_parts < 8;
+    const dim3 grid = a.heads_fastest
+                          ? dim3{unsigned(num_kv_heads), unsigned(num_seqs), unsigned(grid_parts)}
+                          : dim3{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
     const hipError_t err = head_dim == 128
                                ? pkv::dispatch<128>(a, in_dtype, out_dtype, grid, s, split)
                                : pkv::dispatch<64>(a, in_dtype, out_dtype, grid, s, split);
