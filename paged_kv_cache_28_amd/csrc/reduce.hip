@@ -33,30 +33,41 @@ struct ReduceArgs {
     int32_t part_tokens;
     int32_t max_partitions;
     SplitParams split;
+    int32_t heads_per_wg;   // consecutive heads merged by one workgroup (1 or G)
+    int32_t grouped;        // 1: grid (KV head, 1, sequence), heads_per_wg = G
 };
 
 constexpr float kLog2eR = 1.44269504088896340736f;
 
-// Row (b, h) is cut into slices of S dimensions, one workgroup each. Thread t owns the
-// four dimensions 4 (t % (S/4)) .. + 3 of the slice for the records p = t / (S/4)
-// (mod 256 / (S/4)): it folds them in online (running maximum of the reference points),
-// and the record groups are then combined through LDS. Every record is read once, in
-// one pass, with many records in flight per workgroup. Fixed partitions (many records
-// per row) use S = 32; the balanced split (few records per row, and a plan prefix to
-// compute per workgroup) uses whole rows, S = D.
+// Row (b, h) is cut into slices of S dimensions. A workgroup takes one slice of hw
+// consecutive heads of one sequence: thread t owns the four dimensions 4 (t % (S/4)) .. + 3
+// of head t / (S/4) % hw, for the records p = rg (mod RG), rg = t / (hw S/4). It folds
+// them in online (running maximum of the reference points), and the RG record groups are
+// then combined through LDS. Every record is read once, in one pass, with many records in
+// flight per workgroup. Fixed partitions (many records per row) use 32-dimension slices
+// of single heads; the balanced split uses whole rows, of single heads when there are
+// few (sequence, KV head) pairs, else of all G heads of a KV head, so the plan prefix is
+// computed once per (sequence, KV head).
 template <int D, typename OutT, bool Split, int S>
 __global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceArgs a) {
-    constexpr int kDimLanes = S / 4;                // threads per record (float4 each)
-    constexpr int kRecGroups = 256 / kDimLanes;     // record groups per workgroup
-    __shared__ float s_m[kRecGroups][kDimLanes];
-    __shared__ float s_w[kRecGroups][kDimLanes];
-    __shared__ float4 s_o[kRecGroups][kDimLanes];
+    constexpr int kDimLanes = S / 4;                // threads per record and head (float4 each)
+    __shared__ float s_m[256];
+    __shared__ float s_w[256];
+    __shared__ float4 s_o[256];
     __shared__ int32_t s_red[2 * 4];
-    const int slice = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int t = threadIdx.x, dl = t % kDimLanes, rg = t / kDimLanes;
+    const int hw = a.heads_per_wg;
+    const int per = kDimLanes * hw;                 // threads per record group
+    const int RG = 256 / per;                       // record groups
+    const int t = threadIdx.x, dl = t % kDimLanes, hh = (t / kDimLanes) % hw, rg = t / per;
+    // grouped grid (KV head, 1, sequence): whole rows of heads g*hw ..; otherwise
+    // (slice, head, sequence)
+    const int slice = a.grouped ? 0 : blockIdx.x;
+    const int h = a.grouped ? blockIdx.x * hw + hh : blockIdx.y;
+    const int b = blockIdx.z;
     const int dim0 = slice * S + 4 * dl;
     const int hkv = a.num_kv_heads, G = a.num_heads / hkv, g = h / G;
     const int max_len = a.max_blocks * 16;
+    const int64_t out_at = (int64_t(b) * a.num_heads + h) * D + dim0;
 
     int n = a.seq_lens[b];
     n = n < 0 ? 0 : (n > max_len ? max_len : n);
@@ -84,8 +95,7 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceArgs a) {
         total = s_red[0] + s_red[1] + s_red[2] + s_red[3];
         before = s_red[4] + s_red[5] + s_red[6] + s_red[7];
         if (n == 0) {   // empty sequence: no tile, so no piece wrote its row
-            if (rg == 0) OutStore<OutT>::st4(a.out, (int64_t(b) * a.num_heads + h) * D + dim0,
-                                              make_float4(0.f, 0.f, 0.f, 0.f));
+            if (rg == 0) OutStore<OutT>::st4(a.out, out_at, make_float4(0.f, 0.f, 0.f, 0.f));
             return;
         }
         const int share = split_share(total, a.split);
@@ -103,7 +113,7 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceArgs a) {
     float m = -INFINITY, w = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
-    for (int p = rg; p < np; p += kRecGroups) {
+    for (int p = rg; p < np; p += RG) {   // rg >= RG (idle threads): no record
         const float mp = a.part_max[row + p] * kLog2eR;   // base-2 units
         const float lp = a.part_sum[row + p];
         const float4 v = *reinterpret_cast<const float4*>(a.part_out + (row + p) * D + dim0);
@@ -117,45 +127,51 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceArgs a) {
         w = w * s1 + s2;
         m = mn;
     }
-    s_m[rg][dl] = m;
-    s_w[rg][dl] = w;
-    s_o[rg][dl] = o;
+    s_m[t] = m;
+    s_w[t] = w;
+    s_o[t] = o;
     __syncthreads();
     if (rg != 0) return;
     float M = -INFINITY;
-#pragma unroll 8
-    for (int r = 0; r < kRecGroups; ++r) M = fmaxf(M, s_m[r][dl]);
+    for (int r = 0; r < RG; ++r) M = fmaxf(M, s_m[r * per + t]);
     float W = 0.f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-    for (int r = 0; r < kRecGroups; ++r) {
-        const float mr = s_m[r][dl];
+    for (int r = 0; r < RG; ++r) {
+        const float mr = s_m[r * per + t];
         const float f = mr == -INFINITY ? 0.f : exp2_fast(mr - M);   // groups with no record
-        const float4 v = s_o[r][dl];
-        W += f * s_w[r][dl];
+        const float4 v = s_o[r * per + t];
+        W += f * s_w[r * per + t];
         O.x += f * v.x;
         O.y += f * v.y;
         O.z += f * v.z;
         O.w += f * v.w;
     }
     const float inv = 1.f / W;
-    OutStore<OutT>::st4(a.out, (int64_t(b) * a.num_heads + h) * D + dim0,
-                        make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv));
+    OutStore<OutT>::st4(a.out, out_at, make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv));
 }
 
 template <int D, typename OutT>
-hipError_t launch_reduce(const ReduceArgs& a, bool split, hipStream_t s) {
+hipError_t launch_reduce(ReduceArgs a, bool split, hipStream_t s) {
     const LaunchEvents ev = timer_events(PKV_TIMER_REDUCE);
     constexpr int kFixedSlice = 32;
-    if (split)
-        hipExtLaunchKernelGGL((reduce_rows_kernel<D, OutT, true, D>),
-                              dim3(1u, unsigned(a.num_heads), unsigned(a.num_seqs)), dim3(256), 0, s,
+    const int G = a.num_heads / a.num_kv_heads;
+    if (split) {
+        // whole rows; all G heads of a KV head per workgroup when that fills the device
+        const bool grouped = G * (D / 4) <= 256 && int64_t(a.num_seqs) * a.num_kv_heads >= 256;
+        a.heads_per_wg = grouped ? G : 1;
+        a.grouped = grouped;
+        const dim3 grid = grouped ? dim3{unsigned(a.num_kv_heads), 1u, unsigned(a.num_seqs)}
+                                  : dim3{1u, unsigned(a.num_heads), unsigned(a.num_seqs)};
+        hipExtLaunchKernelGGL((reduce_rows_kernel<D, OutT, true, D>), grid, dim3(256), 0, s,
                               ev.start, ev.stop, 0, a);
-    else
+    } else {
+        a.heads_per_wg = 1;
+        a.grouped = 0;
         hipExtLaunchKernelGGL((reduce_rows_kernel<D, OutT, false, kFixedSlice>),
                               dim3(unsigned(D / kFixedSlice), unsigned(a.num_heads),
                                    unsigned(a.num_seqs)),
                               dim3(256), 0, s, ev.start, ev.stop, 0, a);
+    }
     return hipGetLastError();
 }
 
