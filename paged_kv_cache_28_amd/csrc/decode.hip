@@ -74,6 +74,11 @@ struct DecodeArgs {
     // partition); with 8 or more it is (partition, KV head, sequence), which measured
     // faster on long contexts.
     int32_t heads_fastest;
+    // Single pass with at most kLptMaxSeqs sequences: workgroup slot i of the sequence
+    // dimension takes the i-th longest sequence, and the launch holds one workgroup per
+    // CU, so the longest (sequence, KV head) pairs start first and the hardware hands
+    // the shorter ones to CUs as they free up (longest-processing-time-first order).
+    int32_t lpt;
     // fused append (paged_attention_decode_append): the new token of sequence b has
     // rows new_k/new_v + b * new_*_stride ([Hkv][D]) and goes to slot_mapping[b]
     const void* new_k;
@@ -83,6 +88,7 @@ struct DecodeArgs {
     int64_t new_v_stride;
 };
 
+constexpr int kLptMaxSeqs = 256;
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -168,8 +174,30 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
-    const int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
+    int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
     const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
+    if (a.lpt) {   // rank the lengths (ties by index); slot b takes rank b
+        __shared__ int s_n[kLptMaxSeqs];
+        __shared__ int s_pick;
+        const int t = threadIdx.x;
+        const int max_len = a.max_blocks * 16;
+        for (int i = t; i < a.num_seqs; i += W * 64) {
+            const int v = a.seq_lens[i];
+            s_n[i] = v < 0 ? 0 : (v > max_len ? max_len : v);
+        }
+        __syncthreads();
+        for (int i = t; i < a.num_seqs; i += W * 64) {
+            const int mine = s_n[i];
+            int rank = 0;
+            for (int k = 0; k < a.num_seqs; ++k) {
+                const int o = s_n[k];
+                rank += (o > mine) || (o == mine && k < i);
+            }
+            if (rank == b) s_pick = i;
+        }
+        __syncthreads();
+        b = s_pick;
+    }
     const int G = a.group;
     const int col = lane & 15, quad = lane >> 4;
 
@@ -829,9 +857,37 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 
 constexpr int kWaves = 4;
 
+// LDS per CU of the current device (160 KiB on gfx950), cached per device.
+int lds_per_cu() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess || v <= 0)
+            v = 160 * 1024;
+        cache[dev] = v;
+    }
+    return cache[dev];
+}
+
 template <typename T, int D, typename OutT>
 hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-    const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
+    size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
+    if (a.lpt) {
+        // more than half of the CU's LDS: one workgroup per CU at a time
+        lds = std::max(lds, size_t(lds_per_cu() / 2 + 1024));
+        static std::once_flag once;   // allow the dynamic LDS size above the default limit
+        std::call_once(once, [&] {
+            (void)hipFuncSetAttribute((const void*)decode_mfma_kernel<T, D, OutT, kWaves, true>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+            (void)hipFuncSetAttribute((const void*)decode_mfma_kernel<T, D, OutT, kWaves, false>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        });
+    }
     const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
     if (a.new_k)
         hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true>), grid, dim3(kWaves * 64),
@@ -1045,6 +1101,7 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
     a.new_k_stride = app.key_stride;
     a.new_v_stride = app.value_stride;
     a.heads_fastest = grid_parts < 8;
+    a.lpt = !split && grid_parts == 1 && num_seqs <= pkv::kLptMaxSeqs && in_dtype != PKV_F32;
     const dim3 grid = a.heads_fastest
                           ? dim3{unsigned(num_kv_heads), unsigned(num_seqs), unsigned(grid_parts)}
                           : dim3{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
