@@ -74,11 +74,13 @@ struct DecodeArgs {
     // partition); with 8 or more it is (partition, KV head, sequence), which measured
     // faster on long contexts.
     int32_t heads_fastest;
-    // Single pass with at most kLptMaxSeqs sequences: workgroup slot i of the sequence
-    // dimension takes the i-th longest sequence, and the launch holds one workgroup per
-    // CU, so the longest (sequence, KV head) pairs start first and the hardware hands
-    // the shorter ones to CUs as they free up (longest-processing-time-first order).
-    int32_t lpt;
+    // Single pass with at most kLptMaxSeqs sequences: workgroups are dispatched one CU
+    // after the other, one round of lpt_round sequences (x KV heads) per sweep over the
+    // CUs, and a CU keeps the workgroups of all rounds. The sequences are handed out by
+    // length in serpentine order (round 0 takes ranks 0 .. R-1, round 1 ranks 2R-1 .. R,
+    // ...), so a CU that holds one of the longest also holds one of the shortest and the
+    // CUs finish together. 0: sequences in index order.
+    int32_t lpt_round;
     // fused append (paged_attention_decode_append): the new token of sequence b has
     // rows new_k/new_v + b * new_*_stride ([Hkv][D]) and goes to slot_mapping[b]
     const void* new_k;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
     int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
     const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
-    if (a.lpt) {   // rank the lengths (ties by index); slot b takes rank b
+    if (a.lpt_round > 0) {   // rank the lengths (ties by index); slot b takes a serpentine rank
         __shared__ int s_n[kLptMaxSeqs];
         __shared__ int s_pick;
         const int t = threadIdx.x;
@@ -193,7 +195,9 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                 const int o = s_n[k];
                 rank += (o > mine) || (o == mine && k < i);
             }
-            if (rank == b) s_pick = i;
+            const int R = a.lpt_round, r = b / R, pos = b - r * R;
+            const int hi = min(R, a.num_seqs - r * R);   // sequences in this round
+            if (rank == r * R + ((r & 1) ? hi - 1 - pos : pos)) s_pick = i;
         }
         __syncthreads();
         b = s_pick;
@@ -857,37 +861,9 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 
 constexpr int kWaves = 4;
 
-// LDS per CU of the current device (160 KiB on gfx950), cached per device.
-int lds_per_cu() {
-    static std::mutex mu;
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    std::lock_guard<std::mutex> lock(mu);
-    if (cache[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-                hipSuccess || v <= 0)
-            v = 160 * 1024;
-        cache[dev] = v;
-    }
-    return cache[dev];
-}
-
 template <typename T, int D, typename OutT>
 hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-    size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
-    if (a.lpt) {
-        // more than half of the CU's LDS: one workgroup per CU at a time
-        lds = std::max(lds, size_t(lds_per_cu() / 2 + 1024));
-        static std::once_flag once;   // allow the dynamic LDS size above the default limit
-        std::call_once(once, [&] {
-            (void)hipFuncSetAttribute((const void*)decode_mfma_kernel<T, D, OutT, kWaves, true>,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-            (void)hipFuncSetAttribute((const void*)decode_mfma_kernel<T, D, OutT, kWaves, false>,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        });
-    }
+    const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
     const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
     if (a.new_k)
         hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true>), grid, dim3(kWaves * 64),
@@ -940,6 +916,22 @@ hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid,
 // only add queueing delay and spread the finishing times of the waves).
 // PKV_SPLIT_WAVES_PER_CU overrides the count (a tuning knob; it must not change between
 // a decode and its reduce).
+int device_cus() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
 int split_units() {
     static std::mutex mu;
     static int cache[64] = {0};
@@ -1101,7 +1093,9 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
     a.new_k_stride = app.key_stride;
     a.new_v_stride = app.value_stride;
     a.heads_fastest = grid_parts < 8;
-    a.lpt = !split && grid_parts == 1 && num_seqs <= pkv::kLptMaxSeqs && in_dtype != PKV_F32;
+    a.lpt_round = 0;
+    if (!split && grid_parts == 1 && num_seqs <= pkv::kLptMaxSeqs && in_dtype != PKV_F32)
+        a.lpt_round = std::max(1, pkv::device_cus() / num_kv_heads);
     const dim3 grid = a.heads_fastest
                           ? dim3{unsigned(num_kv_heads), unsigned(num_seqs), unsigned(grid_parts)}
                           : dim3{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
