@@ -8,10 +8,18 @@
 // ve ölçekleme", section "KV bütçesi"), so every KV tile is loaded once and used for
 // all G = Hq / Hkv query heads of its group.
 //
-// Work decomposition: one workgroup per (context partition, KV head, sequence); its
-// W waves take the partition's blocks round-robin, each keeping its own online
-// softmax state, and merge through LDS at the end. A sequence with one partition
-// writes its output; otherwise the partition writes (o_p, m_p, l_p) for the reduce.
+// Work decomposition, three launch modes:
+//   single pass / fixed partitions (decode_mfma_kernel): one workgroup per (context
+//     partition, KV head, sequence); its W waves take the partition's blocks
+//     round-robin, each keeping its own online softmax state, and merge through LDS at
+//     the end. A sequence with one partition writes its output; otherwise the partition
+//     writes (o_p, m_p, l_p) for the reduce.
+//   balanced split (decode_split_kernel): all tiles of the batch cut into equal runs,
+//     one per wave (split.hpp); pieces that do not cover their (sequence, KV head) leave
+//     records for the reduce.
+//   fp32 inputs (decode_f32_kernel): plain vector arithmetic, the correctness path.
+// The fused append (paged_attention_decode_append) also stores each sequence's new K/V
+// row and, in the first two modes, attends to it from the key/value inputs.
 //
 // fp16/bf16 path, one wave per block of 16 tokens (matrix instructions, wave64):
 //   S^T[16 tokens][16 cols] = K_tile[16][d] x Q^T[d][16 cols]   (16x16x32, d/32 steps)
@@ -30,7 +38,6 @@
 //      the weights keep ~16 significant bits instead of 8 (bf16) or 11 (fp16).
 //   C: lane l holds head l%16, dims 16c + 4(l/16) + e: its rescale factor is the
 //      lane's own running max, so the online softmax needs no transposes.
-// fp32 path: plain vector arithmetic, one wave per workgroup (correctness path).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 

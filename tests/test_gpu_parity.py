@@ -39,6 +39,7 @@ SHAPES = {
     "70b-f16": dataclasses.replace(W["llama70b"], num_blocks=0),
     "bf16-d64-g1": _shape("8b", num_heads=8, num_kv_heads=8, head_dim=64),
     "f16-d64-g16": _shape("8b", dtype="f16", num_heads=32, num_kv_heads=2, head_dim=64),
+    "bf16-d128-g16": _shape("8b", num_heads=32, num_kv_heads=2),
     "f32-d128-g8": _shape("tiny", num_heads=16, num_kv_heads=2, head_dim=128, num_blocks=0),
 }
 RAGGED = [0, 1, 2, 15, 16, 17, 31, 33, 100, 255, 256, 257, 700]
@@ -121,7 +122,7 @@ def test_single_pass_decode_matches_oracle(name, device):
     assert np.array_equal(got[0], np.zeros_like(got[0]))       # n = 0 -> zero row
 
 
-@pytest.mark.parametrize("name", ["8b-bf16", "70b-f16", "tiny-f32", "f16-d64-g16"])
+@pytest.mark.parametrize("name", ["8b-bf16", "70b-f16", "tiny-f32", "f16-d64-g16", "bf16-d128-g16"])
 @pytest.mark.parametrize("P", [16, 32, 256, 512])
 def test_partitioned_decode_and_reduce_match_oracle(name, P, device):
     w = SHAPES[name]
@@ -238,7 +239,7 @@ SPLIT_LENS = {
 }
 
 
-@pytest.mark.parametrize("name", ["8b-bf16", "70b-f16", "f16-d64-g16", "bf16-d64-g1"])
+@pytest.mark.parametrize("name", ["8b-bf16", "70b-f16", "f16-d64-g16", "bf16-d64-g1", "bf16-d128-g16"])
 @pytest.mark.parametrize("lens", list(SPLIT_LENS))
 @pytest.mark.parametrize("maxp", [2, 5, None])
 def test_balanced_split_matches_oracle(name, lens, maxp, device):
@@ -251,5 +252,22 @@ def test_balanced_split_matches_oracle(name, lens, maxp, device):
     ref = oracle.decode(ob.q, ob.k_cache, ob.v_cache, ob.tables, ob.lens, w.scale, w.dtype)
     got = out.cpu().double().numpy()
     check_close(got, ref, w.dtype, f"{name} {lens} maxp={maxp}")
+    for b in np.flatnonzero(ob.lens == 0):
+        assert np.array_equal(got[b], np.zeros_like(got[b]))
+
+
+# ------------------------------------------------------------- batch sizes
+@pytest.mark.parametrize("B,P", [(256, 0), (300, 0), (300, 64), (1024, AUTO)])
+def test_many_sequences(B, P, device):
+    """Batch sizes around the single pass's length-ordering limit (256 sequences) and
+    the balanced split's maximum (1024), with short ragged lengths including empty ones."""
+    w = SHAPES["8b-bf16"]
+    lens = workloads.rng(77, B).integers(0, 160, size=B, endpoint=True)
+    ob = paged_batch.build(w, lens=lens)
+    gb = gpu_batch.build(ob, device)
+    out, _ = gpu_batch.run_decode(gb, w, P)
+    ref = oracle.decode(ob.q, ob.k_cache, ob.v_cache, ob.tables, ob.lens, w.scale, w.dtype)
+    got = out.cpu().double().numpy()
+    check_close(got, ref, w.dtype, f"B={B} P={P}")
     for b in np.flatnonzero(ob.lens == 0):
         assert np.array_equal(got[b], np.zeros_like(got[b]))
