@@ -199,13 +199,19 @@ def main():
     # carrying its own start/stop events
     kernel_us = {"decode": None, "reduce": None, "cache_write": None}
     timing_lens = []
+    step_pct = None
     if not args.no_kernel_timer:
         pkv.timer_enable(True)
         base = args.warmup + args.steps
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        marks[0].record(stream)
         for s in range(args.steps):
             step(base + s)
+            marks[s + 1].record(stream)
             timing_lens.append(h_len[(base + s) & 1].numpy().copy())
         torch.cuda.synchronize()
+        per_step = np.sort([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+        step_pct = {f"p{p}": round(float(np.percentile(per_step, p)), 4) for p in (10, 50, 90)}
         for name, entry in (("decode", pkv.PKV_TIMER_DECODE), ("reduce", pkv.PKV_TIMER_REDUCE),
                             ("cache_write", pkv.PKV_TIMER_CACHE_WRITE)):
             ms, n = pkv.timer_read(entry)
@@ -246,11 +252,13 @@ def main():
                    "pool_blocks": nb, "pool_gb_per_layer": round(nb * w.block_bytes_per_layer / 1e9, 3)},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),
+        "step_ms_percentiles": step_pct,
         "decode_kernel_us": kernel_us["decode"],
         "reduce_kernel_us": kernel_us["reduce"],
         "cache_write_kernel_us": kernel_us["cache_write"],
         "kernel_timing": "HIP start/stop events bound to each kernel launch (library timer), "
-                         "averaged over every launch of the timed steps",
+                         "averaged over every launch of the timed steps; step percentiles "
+                         "from events between the steps of that same instrumented pass",
         "cache_state": f"{L} distinct per-layer pools cycled; warm-up {args.warmup} steps excluded",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1) if alg else None,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

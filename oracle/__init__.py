@@ -9,7 +9,8 @@ draws only).
 Contents
   oracle.c       plain C, IEEE binary64: textbook attention over K/V gathered through
                  the block table, per-partition results and their merge, the slot-mapped
-                 cache write.  Built with gcc into liboracle.so by ``build()``.
+                 cache write, the FP8 (OCP e4m3) encoding of a quantised KV cache.  Built
+                 with gcc into liboracle.so by ``build()``.
   allocator.py   Python model of the block pool (FIFO free queue, reference counts).
 
 Parity status: every function here is pinned by tests/test_oracle_*.py against
@@ -28,7 +29,7 @@ from .allocator import PoolError, PoolModel, bytes_per_token  # noqa: F401
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
 
 _lib = None
 
@@ -54,17 +55,24 @@ def lib():
         L.oracle_to_f64.restype = None
         L.oracle_attend.argtypes = [P, P, P, P, P, P, I64, I32, D]
         L.oracle_attend.restype = None
-        L.oracle_gather.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I64, I32]
+        F = ctypes.c_float
+        L.oracle_fp8_quantize.argtypes = [P, P, I64, I32, F]
+        L.oracle_fp8_quantize.restype = None
+        L.oracle_fp8_encode.argtypes = [P, P, I64]
+        L.oracle_fp8_encode.restype = None
+        L.oracle_gather.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I64, I32, D, D]
         L.oracle_gather.restype = ctypes.c_int
         L.oracle_decode.argtypes = [P, P, I32, P, I64, P, P, P, P, I32, I32, I32, I32, I32,
-                                    I64, D, I32, I32]
+                                    I64, D, I32, I32, D, D, I32]
         L.oracle_decode.restype = ctypes.c_int
         L.oracle_decode_partitions.argtypes = [P, P, P, P, I32, P, I64, P, P, P, P, I32, I32,
-                                               I32, I32, I32, I64, D, I32, I32, I32, I32]
+                                               I32, I32, I32, I64, D, I32, I32, D, D, I32, I32,
+                                               I32]
         L.oracle_decode_partitions.restype = ctypes.c_int
         L.oracle_merge.argtypes = [P, P, P, P, P, I32, I32, I32]
         L.oracle_merge.restype = None
-        L.oracle_cache_write.argtypes = [P, P, P, P, P, I32, I32, I32, I64, I64, I64, I32]
+        L.oracle_cache_write.argtypes = [P, P, P, P, P, I32, I32, I32, I64, I64, I64, I32, I32,
+                                         F, F]
         L.oracle_cache_write.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -77,13 +85,15 @@ def _ptr(a: np.ndarray):
 
 def raw(x) -> np.ndarray:
     """torch tensor / numpy array -> numpy array of its raw storage (fp32 as float32,
-    fp16/bf16 as uint16 bit patterns), C-contiguous, on the host."""
+    fp16/bf16 as uint16 bit patterns, fp8 as uint8 codes), C-contiguous, on the host."""
     try:
         import torch
         if isinstance(x, torch.Tensor):
             x = x.detach().cpu().contiguous()
             if x.dtype in (torch.float16, torch.bfloat16):
                 return x.view(torch.int16).numpy().view(np.uint16)
+            if x.dtype == torch.float8_e4m3fn:
+                return x.view(torch.uint8).numpy()
             return x.numpy()
     except ImportError:  # pragma: no cover
         pass
@@ -109,16 +119,34 @@ def attend(q, K, V, scale: float):
     return o, m.value, l.value
 
 
+def fp8_encode(v) -> np.ndarray:
+    """OCP e4m3 codes (uint8) of fp64 values: nearest finite value, ties to the even
+    code, saturating at +-448; NaN -> S.1111.111."""
+    a = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint8)
+    lib().oracle_fp8_encode(_ptr(out), _ptr(a), a.size)
+    return out
+
+
+def fp8_quantize(x, src_dtype: str, scale: float) -> np.ndarray:
+    """Codes of x / scale (division in binary32) for x given in src_dtype."""
+    a = raw(x)
+    out = np.empty(a.shape, dtype=np.uint8)
+    lib().oracle_fp8_quantize(_ptr(out), _ptr(a), a.size, DTYPE_CODE[src_dtype], scale)
+    return out
+
+
 def gather(k_cache, v_cache, table_row, t0: int, t1: int, g: int, num_kv_heads: int,
-           head_dim: int, dtype: str):
-    """Rows [t0, t1) of KV head g gathered through one block-table row -> fp64 (K, V)."""
+           head_dim: int, dtype: str, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Rows [t0, t1) of KV head g gathered through one block-table row -> fp64 (K, V);
+    dtype is the cache's, and an fp8 cache's codes are multiplied by k_scale / v_scale."""
     kc, vc = raw(k_cache), raw(v_cache)
     tr = np.ascontiguousarray(table_row, dtype=np.int32)
     K = np.empty((t1 - t0, head_dim), dtype=np.float64)
     V = np.empty_like(K)
     nb = kc.shape[0]
     rc = lib().oracle_gather(_ptr(K), _ptr(V), _ptr(kc), _ptr(vc), _ptr(tr), t0, t1, g,
-                             num_kv_heads, head_dim, nb, DTYPE_CODE[dtype])
+                             num_kv_heads, head_dim, nb, DTYPE_CODE[dtype], k_scale, v_scale)
     if rc != 0:
         raise ValueError("block table points outside the pool")
     return K, V
@@ -132,10 +160,12 @@ def _rows_arg(rows):
 
 
 def decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype: str,
-           rows=None, nthreads: int = 0) -> np.ndarray:
+           rows=None, nthreads: int = 0, kv_dtype: str | None = None, k_scale: float = 1.0,
+           v_scale: float = 1.0) -> np.ndarray:
     """Single-pass paged decode in fp64.
 
-    q [B][Hq][d]; k_cache/v_cache in the documented block layout; block_tables int32
+    q [B][Hq][d] in dtype; k_cache/v_cache in the documented block layout, in kv_dtype
+    (default dtype; "fp8": codes times k_scale / v_scale); block_tables int32
     [B][max_blocks]; seq_lens int32 [B]. Returns fp64 [B][Hq][d] (rows=None) or
     [len(rows)][d] for the (b, h) pairs in rows."""
     qa, kc, vc = raw(q), raw(k_cache), raw(v_cache)
@@ -147,14 +177,16 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype: str
     out = np.empty((B * Hq if r is None else nr, d), dtype=np.float64)
     rc = lib().oracle_decode(_ptr(out), None if r is None else _ptr(r), nr, _ptr(qa), Hq * d,
                              _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Hq, Hkv, d,
-                             bt.shape[1], kc.shape[0], scale, DTYPE_CODE[dtype], nthreads)
+                             bt.shape[1], kc.shape[0], scale, DTYPE_CODE[dtype],
+                             DTYPE_CODE[kv_dtype or dtype], k_scale, v_scale, nthreads)
     if rc != 0:
         raise ValueError("oracle_decode: bad arguments")
     return out.reshape(B, Hq, d) if r is None else out
 
 
 def decode_partitions(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype: str,
-                      partition_size: int, max_partitions: int, rows=None, nthreads: int = 0):
+                      partition_size: int, max_partitions: int, rows=None, nthreads: int = 0,
+                      kv_dtype: str | None = None, k_scale: float = 1.0, v_scale: float = 1.0):
     """Per-partition fp64 results (o [R][P][d], m [R][P], l [R][P]), R = B*Hq or len(rows)."""
     qa, kc, vc = raw(q), raw(k_cache), raw(v_cache)
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
@@ -169,7 +201,8 @@ def decode_partitions(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
     rc = lib().oracle_decode_partitions(
         _ptr(o), _ptr(m), _ptr(l), None if r is None else _ptr(r), nr, _ptr(qa), Hq * d,
         _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Hq, Hkv, d, bt.shape[1], kc.shape[0], scale,
-        DTYPE_CODE[dtype], partition_size, max_partitions, nthreads)
+        DTYPE_CODE[dtype], DTYPE_CODE[kv_dtype or dtype], k_scale, v_scale, partition_size,
+        max_partitions, nthreads)
     if rc != 0:
         raise ValueError("oracle_decode_partitions: bad arguments")
     return o, m, l
@@ -186,23 +219,26 @@ def merge(o, m, l, n_parts) -> np.ndarray:
 
 
 def cache_write(key, value, k_cache: np.ndarray, v_cache: np.ndarray, slot_mapping,
-                dtype: str) -> None:
-    """In-place slot-mapped bit copy of key/value [T][Hkv][d] into host caches
-    (numpy arrays of raw storage in the documented layout)."""
+                dtype: str, cache_dtype: str | None = None, k_scale: float = 1.0,
+                v_scale: float = 1.0) -> None:
+    """In-place slot-mapped write of key/value [T][Hkv][d] (in dtype) into host caches
+    (numpy arrays of raw storage in the documented layout): a bit copy, or with
+    cache_dtype "fp8" the e4m3 codes of key / k_scale and value / v_scale."""
     ka, va = raw(key), raw(value)
     sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
     T, Hkv, d = ka.shape
     assert k_cache.flags["C_CONTIGUOUS"] and v_cache.flags["C_CONTIGUOUS"]
     rc = lib().oracle_cache_write(_ptr(ka), _ptr(va), _ptr(k_cache), _ptr(v_cache), _ptr(sm),
                                   T, Hkv, d, k_cache.shape[0], Hkv * d, Hkv * d,
-                                  DTYPE_CODE[dtype])
+                                  DTYPE_CODE[dtype], DTYPE_CODE[cache_dtype or dtype], k_scale,
+                                  v_scale)
     if rc != 0:
         raise ValueError("slot outside the pool")
 
 
 def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
     """Shapes of the K and V caches in the documented layout (x = 16 / element bytes)."""
-    x = 16 // (4 if dtype == "f32" else 2)
+    x = 16 // {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[dtype]
     return ((num_blocks, num_kv_heads, head_dim // x, 16, x),
             (num_blocks, num_kv_heads, head_dim, 16))
 
@@ -214,6 +250,9 @@ def empty_caches(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
     if dtype == "f32":
         kc = np.full(ks, np.nan if fill_nan else 0, dtype=np.float32)
         vc = np.full(vs, np.nan if fill_nan else 0, dtype=np.float32)
+    elif dtype == "fp8":
+        kc = np.full(ks, 0x7F if fill_nan else 0, dtype=np.uint8)
+        vc = np.full(vs, 0x7F if fill_nan else 0, dtype=np.uint8)
     else:
         nan_bits = 0x7E00 if dtype == "f16" else 0x7FC0
         kc = np.full(ks, nan_bits if fill_nan else 0, dtype=np.uint16)

@@ -32,8 +32,18 @@
  *   (§03 step 3: a new token goes into the current block, a new block is taken only
  *   when the last one is full).
  *
+ *   FP8 KV cache ("Yerel LLM sistemlerinde backpressure ve ölçekleme", the paragraph
+ *   on KV cache quantisation: storing K/V in FP8 halves the bytes per token, at some
+ *   accuracy cost on long contexts).  The page names neither the format nor a scale;
+ *   our reading is the OCP e4m3 format (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ *   bits, no infinities, NaN = S.1111.111, largest finite 448) with one scale per
+ *   tensor for K and one for V.  A stored code c stands for value(c) * scale.  Writing
+ *   x: v = x / scale in IEEE binary32 (the precision the library decides in), then the
+ *   code of the finite e4m3 value nearest to v, ties to the even code; so |v| > 448
+ *   (infinities included) saturates to +-448.  NaN gives S.1111.111.
+ *
  * Cache layout (the pages leave it open; this is the layout the library documents):
- *   x = 16 / element_bytes (8 for fp16/bf16, 4 for fp32)
+ *   x = 16 / element_bytes (16 for fp8, 8 for fp16/bf16, 4 for fp32)
  *   K: [num_blocks][Hkv][d / x][16][x]   element (blk, g, t, i) at
  *        (((blk * Hkv + g) * (d / x) + i / x) * 16 + t) * x + i % x
  *   V: [num_blocks][Hkv][d][16]          element (blk, g, t, i) at
@@ -51,7 +61,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_FP8 = 3 };
 #define OR_BS 16
 
 /* IEEE 754 binary16 -> binary64, from the format's definition:
@@ -73,13 +83,48 @@ static double bf16_bits_to_f64(uint16_t h) {
     return (double)f;
 }
 
+/* OCP e4m3 -> binary64, from the format's definition: 1 sign bit, 4 exponent bits
+ * (bias 7), 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN
+ * and there is no infinity. */
+static double fp8_bits_to_f64(uint8_t c) {
+    int sign = c >> 7, e = (c >> 3) & 0xf, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);                  /* (m/8) * 2^(1-7) */
+    else v = ldexp((double)(8 | m), e - 10);               /* (1.m) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* binary64 -> OCP e4m3: the code of the nearest finite value, ties to the even code
+ * (round to nearest even on the 3-bit mantissa); larger magnitudes saturate to 448.
+ * Written as a search over the 127 non-negative finite codes so that it follows the
+ * definition of rounding to nearest with no bit tricks. */
+static uint8_t fp8_from_f64(double v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    if (isnan(v)) return sign | 0x7f;
+    double a = fabs(v), best_d = INFINITY;
+    /* 448 is the nearest finite value to any larger magnitude.  Said outright: far out
+     * (1e30, inf) every distance below rounds to the same binary64 value. */
+    if (a >= 448.0) return sign | 0x7e;
+    int best = 0;
+    for (int c = 0; c <= 0x7e; ++c) {
+        double dd = fabs(a - fp8_bits_to_f64((uint8_t)c));
+        if (dd < best_d || (dd == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best_d = dd;
+            best = c;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
 static double elem(const void* base, int64_t idx, int dtype) {
     if (dtype == OR_F32) return (double)((const float*)base)[idx];
+    if (dtype == OR_FP8) return fp8_bits_to_f64(((const uint8_t*)base)[idx]);
     uint16_t h = ((const uint16_t*)base)[idx];
     return dtype == OR_F16 ? half_bits_to_f64(h) : bf16_bits_to_f64(h);
 }
 
-static int elem_bytes(int dtype) { return dtype == OR_F32 ? 4 : 2; }
+static int elem_bytes(int dtype) { return dtype == OR_F32 ? 4 : dtype == OR_FP8 ? 1 : 2; }
 
 static int64_t k_off(int64_t blk, int g, int t, int i, int Hkv, int d, int x) {
     return (((blk * Hkv + g) * (d / x) + i / x) * OR_BS + t) * x + i % x;
@@ -91,6 +136,22 @@ static int64_t v_off(int64_t blk, int g, int t, int i, int Hkv, int d) {
 /* Element-wise widening, exported so tests can pin the conversions. */
 void oracle_to_f64(double* dst, const void* src, int64_t n, int32_t dtype) {
     for (int64_t k = 0; k < n; ++k) dst[k] = elem(src, k, dtype);
+}
+
+/* FP8 quantisation of n elements of src (fp32/fp16/bf16): dst[k] = e4m3 code of the
+ * binary32 quotient src[k] / scale. */
+void oracle_fp8_quantize(uint8_t* dst, const void* src, int64_t n, int32_t src_dtype,
+                         float scale) {
+    for (int64_t k = 0; k < n; ++k) {
+        float v = (float)elem(src, k, src_dtype);   /* exact: fp16/bf16 fit in binary32 */
+        float qv = v / scale;
+        dst[k] = fp8_from_f64((double)qv);
+    }
+}
+
+/* The e4m3 encoder on binary64 inputs, exported for its pins. */
+void oracle_fp8_encode(uint8_t* dst, const double* src, int64_t n) {
+    for (int64_t k = 0; k < n; ++k) dst[k] = fp8_from_f64(src[k]);
 }
 
 /* Textbook attention of one query over n contiguous rows.
@@ -127,19 +188,21 @@ void oracle_attend(double* o, double* m_out, double* l_out, const double* q,
 }
 
 /* Gather rows [t0, t1) of KV head g of one sequence through its block-table row
- * into contiguous fp64 arrays K[t1-t0][d], V[t1-t0][d].  Returns -1 when the
- * table points outside the pool. */
+ * into contiguous fp64 arrays K[t1-t0][d], V[t1-t0][d], each element times its
+ * cache's scale (1 unless the cache is fp8).  Returns -1 when the table points
+ * outside the pool. */
 int oracle_gather(double* K, double* V, const void* k_cache, const void* v_cache,
                   const int32_t* table_row, int64_t t0, int64_t t1, int32_t g,
-                  int32_t Hkv, int32_t d, int64_t num_blocks, int32_t dtype) {
+                  int32_t Hkv, int32_t d, int64_t num_blocks, int32_t dtype,
+                  double k_scale, double v_scale) {
     int x = 16 / elem_bytes(dtype);
     for (int64_t t = t0; t < t1; ++t) {
         int64_t blk = table_row[t / OR_BS];
         int off = (int)(t % OR_BS);
         if (blk < 0 || blk >= num_blocks) return -1;
         for (int i = 0; i < d; ++i) {
-            K[(t - t0) * d + i] = elem(k_cache, k_off(blk, g, off, i, Hkv, d, x), dtype);
-            V[(t - t0) * d + i] = elem(v_cache, v_off(blk, g, off, i, Hkv, d), dtype);
+            K[(t - t0) * d + i] = elem(k_cache, k_off(blk, g, off, i, Hkv, d, x), dtype) * k_scale;
+            V[(t - t0) * d + i] = elem(v_cache, v_off(blk, g, off, i, Hkv, d), dtype) * v_scale;
         }
     }
     return 0;
@@ -153,9 +216,10 @@ static int decode_core(double* o, double* m, double* l, const int32_t* rows, int
                        const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                        const int32_t* tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
                        int32_t Hkv, int32_t d, int32_t max_blocks, int64_t num_blocks,
-                       double scale, int32_t dtype, int32_t part, int32_t max_parts,
-                       int32_t nthreads) {
-    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || (d % (16 / elem_bytes(dtype))) != 0) return -1;
+                       double scale, int32_t q_dtype, int32_t kv_dtype, double k_scale,
+                       double v_scale, int32_t part, int32_t max_parts, int32_t nthreads) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || (d % (16 / elem_bytes(kv_dtype))) != 0) return -1;
+    if (q_dtype == OR_FP8) return -1;
     int G = Hq / Hkv;
     int64_t total = rows ? n_rows : (int64_t)B * Hq;
     int bad = 0;
@@ -175,7 +239,7 @@ static int decode_core(double* o, double* m, double* l, const int32_t* rows, int
         int nslots = part > 0 ? max_parts : 1;
         if (np > nslots) { bad |= 1; continue; }
         double* qq = (double*)malloc(sizeof(double) * d);
-        for (int i = 0; i < d; ++i) qq[i] = elem(q, (int64_t)b * q_stride + (int64_t)h * d + i, dtype);
+        for (int i = 0; i < d; ++i) qq[i] = elem(q, (int64_t)b * q_stride + (int64_t)h * d + i, q_dtype);
         for (int p = 0; p < nslots; ++p) {
             double* op = o + (r * nslots + p) * d;
             double mp = -INFINITY, lp = 0.0;
@@ -184,7 +248,8 @@ static int decode_core(double* o, double* m, double* l, const int32_t* rows, int
                 double* K = (double*)malloc(sizeof(double) * (size_t)((t1 - t0) * d));
                 double* V = (double*)malloc(sizeof(double) * (size_t)((t1 - t0) * d));
                 if (oracle_gather(K, V, k_cache, v_cache, tables + (int64_t)b * max_blocks,
-                                  t0, t1, g, Hkv, d, num_blocks, dtype) != 0) bad |= 1;
+                                  t0, t1, g, Hkv, d, num_blocks, kv_dtype, k_scale,
+                                  v_scale) != 0) bad |= 1;
                 oracle_attend(op, &mp, &lp, qq, K, V, t1 - t0, d, scale);
                 free(K);
                 free(V);
@@ -204,10 +269,11 @@ int oracle_decode(double* out, const int32_t* rows, int32_t n_rows, const void* 
                   int64_t q_stride, const void* k_cache, const void* v_cache,
                   const int32_t* tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
                   int32_t Hkv, int32_t d, int32_t max_blocks, int64_t num_blocks,
-                  double scale, int32_t dtype, int32_t nthreads) {
+                  double scale, int32_t q_dtype, int32_t kv_dtype, double k_scale,
+                  double v_scale, int32_t nthreads) {
     return decode_core(out, NULL, NULL, rows, n_rows, q, q_stride, k_cache, v_cache, tables,
-                       seq_lens, B, Hq, Hkv, d, max_blocks, num_blocks, scale, dtype, 0, 1,
-                       nthreads);
+                       seq_lens, B, Hq, Hkv, d, max_blocks, num_blocks, scale, q_dtype,
+                       kv_dtype, k_scale, v_scale, 0, 1, nthreads);
 }
 
 /* Per-partition results: o[r][max_parts][d], m[r][max_parts], l[r][max_parts];
@@ -217,11 +283,12 @@ int oracle_decode_partitions(double* o, double* m, double* l, const int32_t* row
                              const void* k_cache, const void* v_cache, const int32_t* tables,
                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                              int32_t d, int32_t max_blocks, int64_t num_blocks, double scale,
-                             int32_t dtype, int32_t part, int32_t max_parts, int32_t nthreads) {
+                             int32_t q_dtype, int32_t kv_dtype, double k_scale, double v_scale,
+                             int32_t part, int32_t max_parts, int32_t nthreads) {
     if (part <= 0 || max_parts <= 0) return -1;
     return decode_core(o, m, l, rows, n_rows, q, q_stride, k_cache, v_cache, tables, seq_lens,
-                       B, Hq, Hkv, d, max_blocks, num_blocks, scale, dtype, part, max_parts,
-                       nthreads);
+                       B, Hq, Hkv, d, max_blocks, num_blocks, scale, q_dtype, kv_dtype,
+                       k_scale, v_scale, part, max_parts, nthreads);
 }
 
 /* Merge of per-partition results for n_rows rows, each with n_parts[r] live
@@ -247,13 +314,15 @@ void oracle_merge(double* out, const double* o, const double* m, const double* l
     }
 }
 
-/* Slot-mapped cache write (raw bit copy).  Returns -1 (and writes nothing) if a
- * slot lies outside the pool. */
+/* Slot-mapped cache write.  With cache_dtype == dtype a raw bit copy; with an fp8
+ * cache each element is quantised (k_scale for K, v_scale for V) as described at
+ * the top.  Returns -1 (and writes nothing) if a slot lies outside the pool. */
 int oracle_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                        const int32_t* slot_mapping, int32_t num_tokens, int32_t Hkv, int32_t d,
                        int64_t num_blocks, int64_t key_stride, int64_t value_stride,
-                       int32_t dtype) {
-    int e = elem_bytes(dtype), x = 16 / e;
+                       int32_t dtype, int32_t cache_dtype, float k_scale, float v_scale) {
+    int e = elem_bytes(dtype), ce = elem_bytes(cache_dtype), x = 16 / ce;
+    if (cache_dtype != dtype && (cache_dtype != OR_FP8 || dtype == OR_FP8)) return -1;
     for (int t = 0; t < num_tokens; ++t)
         if ((int64_t)slot_mapping[t] >= num_blocks * OR_BS) return -1;
     for (int t = 0; t < num_tokens; ++t) {
@@ -263,10 +332,17 @@ int oracle_cache_write(const void* key, const void* value, void* k_cache, void* 
         int off = (int)(s % OR_BS);
         for (int g = 0; g < Hkv; ++g)
             for (int i = 0; i < d; ++i) {
-                memcpy((char*)k_cache + k_off(blk, g, off, i, Hkv, d, x) * e,
-                       (const char*)key + (t * key_stride + (int64_t)g * d + i) * e, (size_t)e);
-                memcpy((char*)v_cache + v_off(blk, g, off, i, Hkv, d) * e,
-                       (const char*)value + (t * value_stride + (int64_t)g * d + i) * e, (size_t)e);
+                const char* ksrc = (const char*)key + (t * key_stride + (int64_t)g * d + i) * e;
+                const char* vsrc = (const char*)value + (t * value_stride + (int64_t)g * d + i) * e;
+                char* kdst = (char*)k_cache + k_off(blk, g, off, i, Hkv, d, x) * ce;
+                char* vdst = (char*)v_cache + v_off(blk, g, off, i, Hkv, d) * ce;
+                if (cache_dtype == OR_FP8) {
+                    oracle_fp8_quantize((uint8_t*)kdst, ksrc, 1, dtype, k_scale);
+                    oracle_fp8_quantize((uint8_t*)vdst, vsrc, 1, dtype, v_scale);
+                } else {
+                    memcpy(kdst, ksrc, (size_t)e);
+                    memcpy(vdst, vsrc, (size_t)e);
+                }
             }
     }
     return 0;
