@@ -27,7 +27,7 @@
  *   - The pool object is not thread-safe; use one per thread or lock around it.
  *
  * Cache layout (per layer; the pages do not fix one). x = 16 / element_bytes,
- * i.e. 8 for fp16/bf16 and 4 for fp32:
+ * i.e. 16 for an FP8 cache, 8 for fp16/bf16 and 4 for fp32:
  *   k_cache: [num_blocks][num_kv_heads][head_dim / x][16][x]
  *   v_cache: [num_blocks][num_kv_heads][head_dim][16]
  * Token t of a sequence lives in physical block table[t / 16], row t % 16. One
@@ -58,6 +58,10 @@ extern "C" {
 #define PKV_F32 0
 #define PKV_F16 1
 #define PKV_BF16 2
+/* FP8 KV cache element: OCP e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities, S.1111.111 = NaN, largest finite 448). A cache type only: for
+ * kv_bytes_per_token, kv_pool_create and the *_fp8 entry points below. */
+#define PKV_FP8_E4M3 3
 
 #define PKV_BLOCK_SIZE 16
 
@@ -92,7 +96,8 @@ int pkv_timer_read(int32_t entry, double* total_ms, int64_t* launches);
  * ("Yerel LLM sistemlerinde backpressure ve ölçekleme", section "KV bütçesi": the
  * formula, with 327,680 bytes for an 80-layer, 8-KV-head, head_dim 128 FP16 model;
  * "vLLM Nedir? ...", section "Asıl şişen şey ağırlık değil, KV cache": about 128 KB
- * for 32 layers). Returns -1 for a bad argument. */
+ * for 32 layers). PKV_FP8_E4M3 counts one byte per element, half the FP16 figure
+ * (same page, the paragraph on KV cache quantisation). Returns -1 for a bad argument. */
 int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
                            int32_t dtype);
 
@@ -314,6 +319,67 @@ int paged_attention_reduce(void* out, const float* part_out, const float* part_m
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t max_blocks_per_seq, int32_t partition_size,
                            int32_t max_partitions, int32_t out_dtype, void* stream);
+
+/* ==== FP8 KV cache ================================================================
+ * Storing K and V in FP8 halves the bytes per token, so the same memory holds about
+ * twice the context, at some accuracy cost on long contexts ("Yerel LLM sistemlerinde
+ * backpressure ve ölçekleme", the paragraph on KV cache quantisation). The page names
+ * no format or scaling; here: PKV_FP8_E4M3 codes with one scale per tensor for K
+ * (k_scale) and one for V (v_scale), a code c standing for value(c) * scale. Queries,
+ * new K/V rows and outputs stay fp16/bf16 (or fp32 out); the layout is the one above
+ * with x = 16 (k_cache [num_blocks][Hkv][head_dim/16][16][16] bytes, v_cache
+ * [num_blocks][Hkv][head_dim][16] bytes). The decode kernels widen the codes to the
+ * query type exactly (every e4m3 value is an fp16 and a bf16 value), fold k_scale into
+ * the logit scale and v_scale into the output. */
+
+/* reshape_and_cache_fp8: reshape_and_cache into an FP8 cache. Each element x of
+ * key (value) is stored as the e4m3 code of the binary32 quotient x / k_scale
+ * (x / v_scale), rounded to the nearest finite e4m3 value with ties to the even code:
+ * magnitudes above 448 (and infinities) saturate to +-448, NaN gives S.1111.111.
+ *   key, value: in_dtype (PKV_F16 or PKV_BF16), strides multiples of 8 elements.
+ *   k_scale, v_scale: finite, > 0.
+ *   head_dim: a positive multiple of 16.
+ * Everything else as reshape_and_cache. Errors: EINVAL, ENOTSUP (in_dtype), EHIP. */
+int reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                          int64_t key_stride, int64_t value_stride, int32_t in_dtype,
+                          float k_scale, float v_scale, void* stream);
+
+/* paged_attention_decode_fp8: paged_attention_decode over FP8 caches, i.e. with
+ * K_b[t] = value(code) * k_scale and V_b[t] = value(code) * v_scale. in_dtype (the
+ * query's) is PKV_F16 or PKV_BF16; out_dtype in_dtype or PKV_F32. All three partition
+ * modes; the partial results and paged_attention_reduce are unchanged (they already
+ * include the scales). Errors as paged_attention_decode, plus EINVAL for a scale that
+ * is not finite and positive, ENOTSUP for in_dtype F32. */
+int paged_attention_decode_fp8(void* out, float* part_out, float* part_max, float* part_sum,
+                               const void* q, int64_t q_stride, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                               float k_scale, float v_scale, int32_t partition_size,
+                               int32_t max_partitions, int32_t in_dtype, int32_t out_dtype,
+                               void* stream);
+
+/* paged_attention_decode_append_fp8: paged_attention_decode_append over FP8 caches:
+ * reshape_and_cache_fp8 of one new row per sequence, then paged_attention_decode_fp8.
+ * The new token is attended to as its stored (quantised) value, so the result equals
+ * the two calls under the same condition on slot_mapping as
+ * paged_attention_decode_append. Fused into the decode launch for partition_size >= 0;
+ * a separate cache-write launch with PKV_PARTITION_AUTO. */
+int paged_attention_decode_append_fp8(void* out, float* part_out, float* part_max,
+                                      float* part_sum, const void* q, int64_t q_stride,
+                                      const void* key, const void* value, int64_t key_stride,
+                                      int64_t value_stride, const int32_t* slot_mapping,
+                                      void* k_cache, void* v_cache, const int32_t* block_tables,
+                                      const int32_t* seq_lens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, float scale, float k_scale,
+                                      float v_scale, int32_t partition_size,
+                                      int32_t max_partitions, int32_t in_dtype,
+                                      int32_t out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

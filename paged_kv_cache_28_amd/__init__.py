@@ -8,7 +8,10 @@ device memory and the current HIP stream only. The functions keep the C names:
   kv_bytes_per_token(...)
   reshape_and_cache(...)         slot-mapped write of new tokens' K/V
   paged_attention_decode(...)    GQA decode attention through block tables
+  paged_attention_decode_append(...)  the new token's cache write fused with the decode
   paged_attention_reduce(...)    merge of per-partition results
+  reshape_and_cache_fp8, paged_attention_decode_fp8, paged_attention_decode_append_fp8:
+                                 the same over an FP8 (e4m3) cache with per-tensor K/V scales
 
 There is no fallback: if libpkv.so is missing or fails to load, every call raises.
 """
@@ -22,7 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(HERE, "libpkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOTSUP, PKV_ENOMEM, PKV_ENOENT, PKV_EHIP = 0, -1, -2, -3, -4, -5
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_PARTITION_AUTO = -1
 BLOCK_SIZE = 16
 _CODE_NAMES = {PKV_EINVAL: "EINVAL", PKV_ENOTSUP: "ENOTSUP", PKV_ENOMEM: "ENOMEM",
@@ -81,6 +84,13 @@ def lib():
         "paged_attention_decode_append": ([P, P, P, P, P, I64, P, P, I64, I64, P, P, P, P, P,
                                            I32, I32, I32, I32, I32, I32, I64, F, I32, I32, I32,
                                            I32, P], ctypes.c_int),
+        "reshape_and_cache_fp8": ([P, P, P, P, P, I32, I32, I32, I32, I64, I64, I64, I32, F, F,
+                                   P], ctypes.c_int),
+        "paged_attention_decode_fp8": ([P, P, P, P, P, I64, P, P, P, P, I32, I32, I32, I32, I32,
+                                        I32, I64, F, F, F, I32, I32, I32, I32, P], ctypes.c_int),
+        "paged_attention_decode_append_fp8": ([P, P, P, P, P, I64, P, P, I64, I64, P, P, P, P, P,
+                                               I32, I32, I32, I32, I32, I32, I64, F, F, F, I32,
+                                               I32, I32, I32, P], ctypes.c_int),
         "pkv_timer_enable": ([I32], ctypes.c_int),
         "pkv_timer_read": ([I32, P, P], ctypes.c_int),
     }
@@ -98,7 +108,8 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "kv_pool_free_seq", "kv_pool_seq_len", "kv_pool_seq_blocks", "kv_pool_free_queue",
             "kv_pool_refcount", "kv_pool_build_tables", "kv_pool_stats", "reshape_and_cache",
             "paged_attention_decode", "paged_attention_reduce", "paged_attention_decode_append",
-            "pkv_timer_enable", "pkv_timer_read")
+            "reshape_and_cache_fp8", "paged_attention_decode_fp8",
+            "paged_attention_decode_append_fp8", "pkv_timer_enable", "pkv_timer_read")
 
 
 def _check(rc: int):
@@ -117,9 +128,11 @@ def _torch():
 
 
 def dtype_code(dt) -> int:
+    """PKV_* code of a torch dtype or name; an FP8 cache is held in uint8 tensors."""
     torch = _torch()
     m = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
-         "f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16}
+         torch.uint8: PKV_FP8_E4M3, "f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16,
+         "fp8": PKV_FP8_E4M3}
     if dt not in m:
         raise ValueError(f"unsupported dtype {dt}")
     return m[dt]
@@ -128,7 +141,8 @@ def dtype_code(dt) -> int:
 def torch_dtype(code_or_name):
     torch = _torch()
     return {PKV_F32: torch.float32, PKV_F16: torch.float16, PKV_BF16: torch.bfloat16,
-            "f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[code_or_name]
+            PKV_FP8_E4M3: torch.uint8, "f32": torch.float32, "f16": torch.float16,
+            "bf16": torch.bfloat16, "fp8": torch.uint8}[code_or_name]
 
 
 def _stream(t, stream):
@@ -155,14 +169,15 @@ def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype)
 
 def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype):
     """(k_shape, v_shape) of one layer's caches: [nb][Hkv][d/x][16][x], [nb][Hkv][d][16]."""
-    x = 16 // (4 if dtype_code(dtype) == PKV_F32 else 2)
+    x = 16 // {PKV_F32: 4, PKV_F16: 2, PKV_BF16: 2, PKV_FP8_E4M3: 1}[dtype_code(dtype)]
     return ((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x),
             (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE))
 
 
 def alloc_caches(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda",
                  fill=None):
-    """Allocate one layer's (k_cache, v_cache) through PyTorch (uninitialised, or filled)."""
+    """Allocate one layer's (k_cache, v_cache) through PyTorch (uninitialised, or filled;
+    an FP8 cache is uint8, fill being a code)."""
     torch = _torch()
     ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, dtype)
     td = torch_dtype(dtype) if not isinstance(dtype, torch.dtype) else dtype
@@ -367,6 +382,87 @@ def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_c
         dtype_code(out.dtype), _stream(q, stream)))
 
 
+# ------------------------------------------------------------------ FP8 cache
+def _fp8_cache(k_cache, v_cache):
+    torch = _torch()
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("an FP8 cache is held in uint8 tensors")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+
+
+def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale: float,
+                          v_scale: float, stream=None):
+    """reshape_and_cache into an FP8 cache: the e4m3 codes of key / k_scale and
+    value / v_scale (key/value fp16 or bf16 [T][Hkv][d])."""
+    T, hkv, d = key.shape
+    for t, nm in ((key, "key"), (value, "value")):
+        if t.dim() != 3 or t.shape != key.shape or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{nm} must be [T][Hkv][d] with dense heads/dims")
+    _fp8_cache(k_cache, v_cache)
+    if slot_mapping.numel() < T:
+        raise ValueError("slot_mapping shorter than the token count")
+    _check(lib().reshape_and_cache_fp8(
+        _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, BLOCK_SIZE,
+        k_cache.shape[0], key.stride(0), value.stride(0), dtype_code(key.dtype), float(k_scale),
+        float(v_scale), _stream(key, stream)))
+
+
+def paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                               k_scale: float, v_scale: float, partition_size: int = 0,
+                               part_out=None, part_max=None, part_sum=None,
+                               max_partitions: int = 0, stream=None):
+    """paged_attention_decode over an FP8 cache (codes times k_scale / v_scale)."""
+    B, Hq, d = q.shape
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must have dense heads/dims")
+    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
+    if not (block_tables.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("block_tables and seq_lens must be contiguous")
+    _fp8_cache(k_cache, v_cache)
+    _check(lib().paged_attention_decode_fp8(
+        _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
+        _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
+        B, Hq, k_cache.shape[1], d, BLOCK_SIZE, block_tables.shape[1], k_cache.shape[0],
+        float(scale), float(k_scale), float(v_scale), partition_size, max_partitions,
+        dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
+
+
+def paged_attention_decode_append_fp8(out, q, key, value, slot_mapping, k_cache, v_cache,
+                                      block_tables, seq_lens, scale: float, k_scale: float,
+                                      v_scale: float, partition_size: int = 0, part_out=None,
+                                      part_max=None, part_sum=None, max_partitions: int = 0,
+                                      stream=None):
+    """paged_attention_decode_append over an FP8 cache: the new rows are stored as
+    codes and attended to as their stored values."""
+    B, Hq, d = q.shape
+    hkv = k_cache.shape[1]
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must have dense heads/dims")
+    for t, nm in ((key, "key"), (value, "value")):
+        if tuple(t.shape) != (B, hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{nm} must be [B][Hkv][d] with dense heads/dims")
+    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
+    if not (block_tables.is_contiguous() and seq_lens.is_contiguous() and
+            slot_mapping.is_contiguous()):
+        raise ValueError("block_tables, seq_lens and slot_mapping must be contiguous")
+    _fp8_cache(k_cache, v_cache)
+    if slot_mapping.numel() < B:
+        raise ValueError("slot_mapping shorter than the batch")
+    _check(lib().paged_attention_decode_append_fp8(
+        _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
+        _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(key, "key"),
+        _dev(value, "value"), key.stride(0), value.stride(0), _dev(slot_mapping, "slot_mapping"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, BLOCK_SIZE, block_tables.shape[1],
+        k_cache.shape[0], float(scale), float(k_scale), float(v_scale), partition_size,
+        max_partitions, dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
+
+
 def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partition_size: int,
                            num_kv_heads: int, max_blocks_per_seq: int, stream=None):
     B, Hq, d = out.shape
@@ -409,13 +505,23 @@ def alloc_partials(B: int, Hq: int, d: int, max_partitions: int, device="cuda"):
 
 
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
-           partition_size: int = 0, partials=None, stream=None, append=None):
+           partition_size: int = 0, partials=None, stream=None, append=None, kv_scales=None):
     """Decode + (if partitioned or balanced) reduce: the launches of one layer's attention.
     append=(key, value, slot_mapping) writes one new token per sequence first, fused
-    (paged_attention_decode_append)."""
+    (paged_attention_decode_append). kv_scales=(k_scale, v_scale): the caches are FP8."""
     po, pm, ps = partials if partition_size != 0 else (None, None, None)
     maxp = po.shape[2] if po is not None else 0
-    if append is not None:
+    if kv_scales is not None:
+        ks, vs = kv_scales
+        if append is not None:
+            key, value, slots = append
+            paged_attention_decode_append_fp8(out, q, key, value, slots, k_cache, v_cache,
+                                              block_tables, seq_lens, scale, ks, vs,
+                                              partition_size, po, pm, ps, maxp, stream=stream)
+        else:
+            paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
+                                       ks, vs, partition_size, po, pm, ps, maxp, stream=stream)
+    elif append is not None:
         key, value, slots = append
         paged_attention_decode_append(out, q, key, value, slots, k_cache, v_cache, block_tables,
                                       seq_lens, scale, partition_size, po, pm, ps, maxp,

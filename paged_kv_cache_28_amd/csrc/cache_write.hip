@@ -6,8 +6,11 @@
 // One thread moves one 16-byte group of x = 16 / element_bytes dimensions of one
 // (token, KV head): K keeps the group together (cache layout [blk][g][d/x][16][x]),
 // V spreads it over x rows of its [blk][g][d][16] tile. A pure bit copy.
+// reshape_and_cache_fp8 stores the e4m3 codes of x / scale instead (FP8 KV cache).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 
 #include "device.hpp"
 #include "status.hpp"
@@ -52,7 +55,93 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     }
 }
 
+// FP8 cache: one thread quantises 16 dimensions of one (token, KV head), i.e. one 16-byte
+// K group of the [blk][g][d/16][16][16] layout and 16 bytes of V, one per dimension row
+// of the [blk][g][d][16] tile.
+template <typename T>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens, int32_t hkv,
+    int32_t d, int64_t num_blocks, int64_t key_stride, int64_t value_stride, float k_scale,
+    float v_scale) {
+    const int nchunk = d / 16;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = int64_t(num_tokens) * hkv * nchunk;
+    if (idx >= total) return;
+    const int c = int(idx % nchunk);
+    const int g = int((idx / nchunk) % hkv);
+    const int64_t t = idx / (int64_t(nchunk) * hkv);
+    const uint4* kr = reinterpret_cast<const uint4*>(key + t * key_stride + int64_t(g) * d + c * 16);
+    const uint4* vr = reinterpret_cast<const uint4*>(value + t * value_stride + int64_t(g) * d + c * 16);
+    const uint4 k0 = kr[0], k1 = kr[1], v0 = vr[0], v1 = vr[1];
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_blocks * 16) return;
+    const int64_t tile = (slot >> 4) * hkv + g;
+    const int off = int(slot & 15);
+    *reinterpret_cast<uint4*>(kc + ((tile * nchunk + c) * 16 + off) * 16) =
+        quantize_fp8_x16<T>(k0, k1, k_scale);
+    const uint4 vq = quantize_fp8_x16<T>(v0, v1, v_scale);
+    const uint32_t w[4] = {vq.x, vq.y, vq.z, vq.w};
+    uint8_t* vdst = vc + (tile * d + int64_t(c) * 16) * 16 + off;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) vdst[k * 16] = uint8_t(w[k / 4] >> (8 * (k % 4)));
+}
+
 }  // namespace pkv
+
+extern "C" int reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                     void* v_cache, const int32_t* slot_mapping,
+                                     int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int64_t num_blocks, int64_t key_stride,
+                                     int64_t value_stride, int32_t in_dtype, float k_scale,
+                                     float v_scale, void* stream) {
+    using pkv::fail;
+    if (in_dtype != PKV_F16 && in_dtype != PKV_BF16)
+        return fail(in_dtype == PKV_F32 ? PKV_ENOTSUP : PKV_EINVAL,
+                    "reshape_and_cache_fp8: in_dtype must be F16 or BF16, got %d", in_dtype);
+    if (num_tokens < 0) return fail(PKV_EINVAL, "reshape_and_cache_fp8: negative num_tokens");
+    if (block_size != PKV_BLOCK_SIZE)
+        return fail(PKV_EINVAL, "reshape_and_cache_fp8: block_size must be 16, got %d", block_size);
+    if (num_kv_heads <= 0 || head_dim <= 0 || head_dim % 16 != 0 || num_blocks <= 0)
+        return fail(PKV_EINVAL, "reshape_and_cache_fp8: bad shape (Hkv %d, head_dim %d, "
+                                "blocks %lld)", num_kv_heads, head_dim, (long long)num_blocks);
+    if (key_stride < int64_t(num_kv_heads) * head_dim ||
+        value_stride < int64_t(num_kv_heads) * head_dim || key_stride % 8 || value_stride % 8)
+        return fail(PKV_EINVAL, "reshape_and_cache_fp8: token strides must cover Hkv*head_dim "
+                                "and be multiples of 8 elements");
+    if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+        return fail(PKV_EINVAL, "reshape_and_cache_fp8: k_scale and v_scale must be finite and "
+                                "positive");
+    if (num_tokens == 0) return pkv::ok();
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+        return fail(PKV_EINVAL, "reshape_and_cache_fp8: NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) |
+         reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
+        return fail(PKV_EINVAL, "reshape_and_cache_fp8: buffers must be 16-byte aligned");
+    const int64_t total = int64_t(num_tokens) * num_kv_heads * (head_dim / 16);
+    const int64_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffff) return fail(PKV_EINVAL, "reshape_and_cache_fp8: too many tokens");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* kp = static_cast<const uint16_t*>(key);
+    const uint16_t* vp = static_cast<const uint16_t*>(value);
+    uint8_t* kcp = static_cast<uint8_t*>(k_cache);
+    uint8_t* vcp = static_cast<uint8_t*>(v_cache);
+    const pkv::LaunchEvents ev = pkv::timer_events(PKV_TIMER_CACHE_WRITE);
+    if (in_dtype == PKV_BF16)
+        hipExtLaunchKernelGGL(pkv::reshape_and_cache_fp8_kernel<pkv::bf16_t>, dim3(unsigned(grid)),
+                              dim3(256), 0, s, ev.start, ev.stop, 0, kp, vp, kcp, vcp,
+                              slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
+                              key_stride, value_stride, k_scale, v_scale);
+    else
+        hipExtLaunchKernelGGL(pkv::reshape_and_cache_fp8_kernel<pkv::f16_t>, dim3(unsigned(grid)),
+                              dim3(256), 0, s, ev.start, ev.stop, 0, kp, vp, kcp, vcp,
+                              slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
+                              key_stride, value_stride, k_scale, v_scale);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return fail(PKV_EHIP, "reshape_and_cache_fp8: launch failed: %s", hipGetErrorString(err));
+    return pkv::ok();
+}
 
 extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cache,
                                  void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,

@@ -71,7 +71,9 @@ struct DecodeArgs {
     int32_t max_blocks;    // block-table row length
     int32_t part_blocks;   // blocks per partition
     int32_t max_partitions;
-    float scale_log2;      // scale * log2(e): logits in base-2 units
+    float scale_log2;      // scale * log2(e) (* k_scale for an FP8 cache): base-2 logits
+    float k_scale;         // FP8 cache: per-tensor scales (new rows are quantised with
+    float v_scale;         // them; v_scale multiplies every output); 1 otherwise
     int32_t num_seqs;
     SplitParams split;     // balanced mode only
     int32_t slots;         // balanced mode: result slots per wave
@@ -111,23 +113,35 @@ __device__ void write_zero_rows(const DecodeArgs& a, int b, int g) {
 }
 
 // Fused append: copy the new token's K and V rows of KV head g into its slot (the
-// reshape_and_cache layout), with the threads of the calling workgroup. A slot outside
-// the pool (or negative) is skipped, as reshape_and_cache does.
-template <int D>
+// reshape_and_cache layout; FP8 cache: their codes, as reshape_and_cache_fp8 stores
+// them), with the threads of the calling workgroup. A slot outside the pool (or
+// negative) is skipped, as reshape_and_cache does.
+template <typename T, int D, bool F8>
 __device__ void write_new_token(const DecodeArgs& a, int b, int g, int slot) {
     if (slot < 0 || int64_t(slot) >= a.num_blocks * 16) return;
     const int64_t tile = (int64_t(slot) >> 4) * a.num_kv_heads + g;
     const int off = slot & 15;
     const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride + int64_t(g) * D;
     const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride + int64_t(g) * D;
-    uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k_cache));
-    uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v_cache));
     const int t = threadIdx.x;
-    if (t < D / 8)   // K: [tile][d/8][16][8], one 16-byte group per thread
-        *reinterpret_cast<uint4*>(kc + ((tile * (D / 8) + t) * 16 + off) * 8) =
-            *reinterpret_cast<const uint4*>(krow + 8 * t);
-    for (int d = t; d < D; d += blockDim.x)   // V: [tile][d][16]
-        vc[(tile * D + d) * 16 + off] = vrow[d];
+    if constexpr (F8) {
+        uint8_t* kc = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.k_cache));
+        uint8_t* vc = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.v_cache));
+        if (t < D / 16)   // K: [tile][d/16][16][16] bytes, one 16-byte group per thread
+            *reinterpret_cast<uint4*>(kc + ((tile * (D / 16) + t) * 16 + off) * 16) =
+                quantize_fp8_x16<T>(*reinterpret_cast<const uint4*>(krow + 16 * t),
+                                    *reinterpret_cast<const uint4*>(krow + 16 * t + 8), a.k_scale);
+        for (int d = t; d < D; d += blockDim.x)   // V: [tile][d][16] bytes
+            vc[(tile * D + d) * 16 + off] = uint8_t(quantize_fp8(Bits<T>::to_f32(vrow[d]), a.v_scale));
+    } else {
+        uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k_cache));
+        uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v_cache));
+        if (t < D / 8)   // K: [tile][d/8][16][8], one 16-byte group per thread
+            *reinterpret_cast<uint4*>(kc + ((tile * (D / 8) + t) * 16 + off) * 8) =
+                *reinterpret_cast<const uint4*>(krow + 8 * t);
+        for (int d = t; d < D; d += blockDim.x)   // V: [tile][d][16]
+            vc[(tile * D + d) * 16 + off] = vrow[d];
+    }
 }
 
 // Merge the per-wave states held in LDS and write out or the partition result.
@@ -148,7 +162,7 @@ __device__ void merge_and_store(const DecodeArgs& a, const float* sm_m, const fl
             L += f * sm_l[w * 16 + h];
             O += f * sm_o[(w * G + h) * D + dim];
         }
-        const float o = O / L;
+        const float o = O / L * a.v_scale;
         const int hq = g * G + h;
         if (direct) {
             OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + hq) * D + dim, o);
@@ -164,18 +178,92 @@ __device__ void merge_and_store(const DecodeArgs& a, const float* sm_m, const fl
 }
 
 // ---------------------------------------------------------------- fp16 / bf16
-// K and V of one (block, KV head) tile as this lane holds them for the two products.
-template <int D>
-struct KvTile {
+// K and V of one (block, KV head) tile as this lane holds them for the two products,
+// per cache type, and the operands the matrix instructions take from it.
+//   16-bit cache: k[c] is the A operand of QK step c (dims 32c + 8 quad .. + 7 of token
+//     l%16, 16 bytes at (64c + l) * 16 of the [d/8][16][8] tile); v[c] that of PV step c
+//     (dim 16c + l%16, tokens 4 quad .. + 3).
+//   FP8 cache ([d/16][16][16] bytes): one 16-byte load k[i] at (64i + l) * 16 holds dims
+//     16(4i + quad) .. + 15 of token l%16 and feeds QK steps 2i (its first 8 dims) and
+//     2i + 1 (the last 8); the dimensions of the contraction are taken in another order,
+//     and the Q^T operand follows the same order (q_dim). v[c] holds the four codes of
+//     PV step c. The codes are widened to T when used.
+template <int D, bool F8> struct KvTile;
+template <int D> struct KvTile<D, false> {
     uint4 k[D / 32];
     uint2 v[D / 16];
 };
+template <int D> struct KvTile<D, true> {
+    uint4 k[D / 64];
+    uint32_t v[D / 16];
+};
 
-template <typename T, int D, typename OutT, int W, bool Append>
+// First query dimension of the 8 that lane group `quad` feeds QK step c with.
+template <bool F8>
+__device__ __forceinline__ int q_dim(int c, int quad) {
+    return F8 ? 64 * (c >> 1) + 16 * quad + 8 * (c & 1) : 32 * c + 8 * quad;
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(KvTile<D, false>& t, const char* kt, const char* vt,
+                                          int lane) {
+    const int col = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 16);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        t.v[c] = *reinterpret_cast<const uint2*>(vt + ((16 * c + col) * 16 + 4 * quad) * 2);
+}
+template <int D>
+__device__ __forceinline__ void load_tile(KvTile<D, true>& t, const char* kt, const char* vt,
+                                          int lane) {
+    const int col = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) t.k[i] = *reinterpret_cast<const uint4*>(kt + (64 * i + lane) * 16);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        t.v[c] = *reinterpret_cast<const uint32_t*>(vt + (16 * c + col) * 16 + 4 * quad);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ uint4 k_operand(const KvTile<D, false>& t, int c) { return t.k[c]; }
+template <typename T, int D>
+__device__ __forceinline__ uint4 k_operand(const KvTile<D, true>& t, int c) {
+    const uint4 w = t.k[c >> 1];
+    const uint2 a = Fp8<T>::x4((c & 1) ? w.z : w.x), b = Fp8<T>::x4((c & 1) ? w.w : w.y);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+template <typename T, int D>
+__device__ __forceinline__ uint2 v_operand(const KvTile<D, false>& t, int c) { return t.v[c]; }
+template <typename T, int D>
+__device__ __forceinline__ uint2 v_operand(const KvTile<D, true>& t, int c) { return Fp8<T>::x4(t.v[c]); }
+
+// Zero V rows tok0 + e (e = 0..3) of this lane whose keep[e] is false, so that whatever
+// bytes a partly filled block holds there never reach the sum (0 weight times NaN would).
+template <int D>
+__device__ __forceinline__ void mask_rows(KvTile<D, false>& t, bool k0, bool k1, bool k2, bool k3) {
+    const uint32_t lo = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
+    const uint32_t hi = (k2 ? 0x0000ffffu : 0u) | (k3 ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        t.v[c].x &= lo;
+        t.v[c].y &= hi;
+    }
+}
+template <int D>
+__device__ __forceinline__ void mask_rows(KvTile<D, true>& t, bool k0, bool k1, bool k2, bool k3) {
+    const uint32_t m = (k0 ? 0xffu : 0u) | (k1 ? 0xff00u : 0u) | (k2 ? 0xff0000u : 0u) |
+                       (k3 ? 0xff000000u : 0u);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) t.v[c] &= m;
+}
+
+template <typename T, int D, typename OutT, int W, bool Append, bool F8>
 __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
-    static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
+    static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
     constexpr int NQK = D / 32;   // 16x16x32 steps for S
     constexpr int NPV = D / 16;   // 16x16x16 steps for O
+    constexpr int NKL = F8 ? D / 64 : D / 32;   // 16-byte K loads per tile and lane
     extern __shared__ float lds[];
     float* sm_m = lds;                  // [W][16]
     float* sm_l = lds + W * 16;         // [W][16]
@@ -217,27 +305,40 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     uint4 qf[NQK];
     {
         const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(b) * a.q_stride +
-                               int64_t(g * G + col) * D + 8 * quad;
+                               int64_t(g * G + col) * D;
 #pragma unroll
         for (int c = 0; c < NQK; ++c)
-            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + 32 * c) : make_uint4(0, 0, 0, 0);
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + q_dim<F8>(c, quad))
+                            : make_uint4(0, 0, 0, 0);
     }
-    // Fused append: the new token's rows, every lane its share: K dims 32c + 8 quad .. + 7
-    // (as the A operand holds them), V dim 16c + l%16. Kept in registers: reading them
-    // from LDS inside the tile loop made the compiler move the tiles to scratch.
+    // Fused append: the new token's rows, every lane its share in the tile layout: K as
+    // the lane's 16-byte K loads hold them (16-bit cache: dims 32c + 8 quad .. + 7; FP8
+    // cache: the codes of dims 16(4i + quad) .. + 15), V dim 16c + l%16 (FP8: its code).
+    // Kept in registers: reading them from LDS inside the tile loop made the compiler move
+    // the tiles to scratch.
     int slot = -1;
-    uint4 nk[Append ? NQK : 1];
+    uint4 nk[Append ? NKL : 1];
     uint32_t nv[Append ? NPV : 1];
     if constexpr (Append) {
         slot = a.slot_mapping[b];
         const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
-                               int64_t(g) * D + 8 * quad;
+                               int64_t(g) * D;
         const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
                                int64_t(g) * D + col;
+        if constexpr (F8) {
 #pragma unroll
-        for (int c = 0; c < NQK; ++c) nk[c] = *reinterpret_cast<const uint4*>(krow + 32 * c);
+            for (int i = 0; i < NKL; ++i)
+                nk[i] = quantize_fp8_x16<T>(*reinterpret_cast<const uint4*>(krow + 64 * i + 16 * quad),
+                                            *reinterpret_cast<const uint4*>(krow + 64 * i + 16 * quad + 8),
+                                            a.k_scale);
 #pragma unroll
-        for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c];
+            for (int c = 0; c < NPV; ++c) nv[c] = quantize_fp8(Bits<T>::to_f32(vrow[16 * c]), a.v_scale);
+        } else {
+#pragma unroll
+            for (int c = 0; c < NKL; ++c) nk[c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * quad);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c];
+        }
     }
 
     // This wave takes blocks first, first + W, ... of its partition. The block ids of its
@@ -255,7 +356,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     if (blk_begin >= nblk) {
         if (p == 0) write_zero_rows<OutT, D>(a, b, g);
         if constexpr (Append)
-            if (p == 0 && n == 0) write_new_token<D>(a, b, g, slot);
+            if (p == 0 && n == 0) write_new_token<T, D, F8>(a, b, g, slot);
         return;
     }
     const int blk_end = min(nblk, blk_begin + a.part_blocks);
@@ -281,16 +382,22 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
             if (wave != w_new || slot < 0 || int64_t(slot) >= a.num_blocks * 16) return;
             const int64_t tile = (int64_t(slot) >> 4) * a.num_kv_heads + g;
             const int off = slot & 15;
-            uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k_cache));
-            uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v_cache));
-            if (col == 0) {   // K: group 4c + quad holds dims 32c + 8 quad .. + 7
+            char* kc = const_cast<char*>(static_cast<const char*>(a.k_cache));
+            char* vc = const_cast<char*>(static_cast<const char*>(a.v_cache));
+            // K: 16-byte group 4c + quad of the row is the lane's nk[c]
+            if (col == 0) {
 #pragma unroll
-                for (int c = 0; c < NQK; ++c)
-                    *reinterpret_cast<uint4*>(kc + ((tile * (D / 8) + 4 * c + quad) * 16 + off) * 8) = nk[c];
+                for (int c = 0; c < NKL; ++c)
+                    *reinterpret_cast<uint4*>(kc + ((tile * (NKL * 4) + 4 * c + quad) * 16 + off) * 16) = nk[c];
             }
             if (quad == 0) {  // V: dims 16c + col
 #pragma unroll
-                for (int c = 0; c < NPV; ++c) vc[(tile * D + 16 * c + col) * 16 + off] = uint16_t(nv[c]);
+                for (int c = 0; c < NPV; ++c) {
+                    if constexpr (F8)
+                        reinterpret_cast<uint8_t*>(vc)[(tile * D + 16 * c + col) * 16 + off] = uint8_t(nv[c]);
+                    else
+                        reinterpret_cast<uint16_t*>(vc)[(tile * D + 16 * c + col) * 16 + off] = uint16_t(nv[c]);
+                }
             }
         }
     };
@@ -306,33 +413,27 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr float kSlack = 8.0f;
     float m = -INFINITY, lsum = 0.f;
 
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache);
-    const int64_t tile_elems = int64_t(D) * 16;
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    const int64_t tile_bytes = int64_t(D) * 16 * (F8 ? 1 : 2);
     int tab = 0;   // block ids of the current segment: lane k holds block k
 
     // Issue the loads of block k of the segment; false if its id breaks the
     // precondition (then a safe address is read and the block is skipped).
-    auto load = [&](KvTile<D>& t, int k) -> bool {
+    auto load = [&](KvTile<D, F8>& t, int k) -> bool {
         int64_t phys = __builtin_amdgcn_readlane(tab, k);
         const bool ok = phys >= 0 && phys < a.num_blocks;
         phys = ok ? phys : 0;
         const int64_t tile = phys * a.num_kv_heads + g;
-        const uint16_t* kt = kbase + tile * tile_elems;
-        const uint16_t* vt = vbase + tile * tile_elems;
-#pragma unroll
-        for (int c = 0; c < NQK; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 8);
-#pragma unroll
-        for (int c = 0; c < NPV; ++c)
-            t.v[c] = *reinterpret_cast<const uint2*>(vt + (16 * c + col) * 16 + 4 * quad);
+        load_tile<D>(t, kbase + tile * tile_bytes, vbase + tile * tile_bytes, lane);
         return ok;
     };
 
-    auto compute = [&](KvTile<D>& t, int j, bool ok) {
+    auto compute = [&](KvTile<D, F8>& t, int j, bool ok) {
         if (!ok) return;
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(t.k[c], qf[c], s);
+        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(k_operand<T, D>(t, c), qf[c], s);
 
         const int tok0 = j * 16 + 4 * quad;
         float x[4];
@@ -353,15 +454,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m);
         lsum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
 
-        if (j * 16 + 16 > lim) {   // partly filled block: rows from lim on may hold anything
-            const uint32_t keep_lo = (tok0 + 0 < lim ? 0x0000ffffu : 0u) | (tok0 + 1 < lim ? 0xffff0000u : 0u);
-            const uint32_t keep_hi = (tok0 + 2 < lim ? 0x0000ffffu : 0u) | (tok0 + 3 < lim ? 0xffff0000u : 0u);
-#pragma unroll
-            for (int c = 0; c < NPV; ++c) {
-                t.v[c].x &= keep_lo;
-                t.v[c].y &= keep_hi;
-            }
-        }
+        if (j * 16 + 16 > lim)   // partly filled block: rows from lim on may hold anything
+            mask_rows<D>(t, tok0 + 0 < lim, tok0 + 1 < lim, tok0 + 2 < lim, tok0 + 3 < lim);
         uint16_t hi[4], lo[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
@@ -371,8 +465,9 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                                      uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
 #pragma unroll
         for (int c = 0; c < NPV; ++c) {
-            acc[c] = Mfma<T>::pv(t.v[c], phi, acc[c]);
-            acc[c] = Mfma<T>::pv(t.v[c], plo, acc[c]);
+            const uint2 vv = v_operand<T, D>(t, c);
+            acc[c] = Mfma<T>::pv(vv, phi, acc[c]);
+            acc[c] = Mfma<T>::pv(vv, plo, acc[c]);
         }
     };
 
@@ -391,7 +486,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                 lim = subst ? n - 1 : n;
             }
         }
-        KvTile<D> A, B;
+        KvTile<D, F8> A, B;
         bool okA = load(A, 0), okB;
         if (k0 == 0) store_new_row();
         for (int k = 0; k < cnt; k += 2) {
@@ -407,11 +502,16 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     // valid row is row 0.
     if constexpr (Append) {
         if (wave == w_new && subst) {
-            KvTile<D> t;
+            KvTile<D, F8> t;
 #pragma unroll
-            for (int c = 0; c < NQK; ++c) t.k[c] = col == 0 ? nk[c] : make_uint4(0, 0, 0, 0);
+            for (int c = 0; c < NKL; ++c) t.k[c] = col == 0 ? nk[c] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int c = 0; c < NPV; ++c) t.v[c] = make_uint2(quad == 0 ? nv[c] & 0xffffu : 0u, 0u);
+            for (int c = 0; c < NPV; ++c) {
+                if constexpr (F8)
+                    t.v[c] = quad == 0 ? nv[c] & 0xffu : 0u;
+                else
+                    t.v[c] = make_uint2(quad == 0 ? nv[c] & 0xffffu : 0u, 0u);
+            }
             lim = 1;
             compute(t, 0, true);
         }
@@ -460,7 +560,7 @@ __host__ __device__ constexpr int split_wave_bytes(int G, int D, int slots) {
     return split_q_bytes(G, D) + slots * (split_slot_floats(G, D) * 4 + 16);
 }
 
-template <typename T, int D, typename OutT>
+template <typename T, int D, typename OutT, bool F8>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a) {
     constexpr int NQK = D / 32, NPV = D / 16;
     constexpr int kWaves = kSplitThreads / 64;
@@ -479,9 +579,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     const int t0 = int(t0l);
     const int t1 = min(total, t0 + share);
 
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache);
-    const int64_t tile_elems = int64_t(D) * 16;
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    const int64_t tile_bytes = int64_t(D) * 16 * (F8 ? 1 : 2);
     const int qpiece = G * D;                              // elements per staged query set
     char* my_lds = reinterpret_cast<char*>(s_dyn) + wave * split_wave_bytes(G, D, a.slots);
     uint16_t* my_q = reinterpret_cast<uint16_t*>(my_lds);
@@ -507,10 +607,11 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
         first_j = j;
         cur_bg = bg;
         ++piece_slot;
-        const uint16_t* qs = my_q + piece_slot * qpiece + (col < G ? col : 0) * D + 8 * quad;
+        const uint16_t* qs = my_q + piece_slot * qpiece + (col < G ? col : 0) * D;
 #pragma unroll
         for (int c = 0; c < NQK; ++c)
-            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qs + 32 * c) : make_uint4(0, 0, 0, 0);
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qs + q_dim<F8>(c, quad))
+                            : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int c = 0; c < NPV; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         m = -INFINITY;
@@ -553,7 +654,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
         if (nused == a.slots) flush();
         float* so = slots + nused * slot_floats;
         if (col < G) {
-            const float inv = 1.0f / L;
+            const float inv = a.v_scale / L;
 #pragma unroll
             for (int c = 0; c < NPV; ++c)
                 *reinterpret_cast<float4*>(so + col * D + 16 * c + 4 * quad) =
@@ -573,23 +674,17 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     };
 
     int tphys = 0, tbg = 0, tj = 0;   // per-lane metadata of the current batch
-    auto load = [&](KvTile<D>& t, int k) -> bool {
+    auto load = [&](KvTile<D, F8>& t, int k) -> bool {
         int64_t phys = __builtin_amdgcn_readlane(tphys, k);
         const bool ok = phys >= 0 && phys < a.num_blocks;
         phys = ok ? phys : 0;
         const int g = __builtin_amdgcn_readlane(tbg, k) % hkv;
         const int64_t tile = phys * hkv + g;
-        const uint16_t* kt = kbase + tile * tile_elems;
-        const uint16_t* vt = vbase + tile * tile_elems;
-#pragma unroll
-        for (int c = 0; c < NQK; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 8);
-#pragma unroll
-        for (int c = 0; c < NPV; ++c)
-            t.v[c] = *reinterpret_cast<const uint2*>(vt + (16 * c + col) * 16 + 4 * quad);
+        load_tile<D>(t, kbase + tile * tile_bytes, vbase + tile * tile_bytes, lane);
         return ok;
     };
 
-    auto compute = [&](KvTile<D>& t, int k, bool ok) {   // ok == false: tile masked out
+    auto compute = [&](KvTile<D, F8>& t, int k, bool ok) {   // ok == false: tile masked out
         const int bg = __builtin_amdgcn_readlane(tbg, k);
         const int j = __builtin_amdgcn_readlane(tj, k);
         if (bg != cur_bg) {
@@ -603,7 +698,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
         const int n = ok ? seg_n : 0;
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(t.k[c], qf[c], s);
+        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(k_operand<T, D>(t, c), qf[c], s);
         const int tok0 = j * 16 + 4 * quad;
         float x[4];
 #pragma unroll
@@ -622,15 +717,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
 #pragma unroll
         for (int e = 0; e < 4; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m);
         lsum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-        if (j * 16 + 16 > n) {
-            const uint32_t keep_lo = (tok0 + 0 < n ? 0x0000ffffu : 0u) | (tok0 + 1 < n ? 0xffff0000u : 0u);
-            const uint32_t keep_hi = (tok0 + 2 < n ? 0x0000ffffu : 0u) | (tok0 + 3 < n ? 0xffff0000u : 0u);
-#pragma unroll
-            for (int c = 0; c < NPV; ++c) {
-                t.v[c].x &= keep_lo;
-                t.v[c].y &= keep_hi;
-            }
-        }
+        if (j * 16 + 16 > n) mask_rows<D>(t, tok0 + 0 < n, tok0 + 1 < n, tok0 + 2 < n, tok0 + 3 < n);
         uint16_t hi[4], lo[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
@@ -640,8 +727,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
                                      uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
 #pragma unroll
         for (int c = 0; c < NPV; ++c) {
-            acc[c] = Mfma<T>::pv(t.v[c], phi, acc[c]);
-            acc[c] = Mfma<T>::pv(t.v[c], plo, acc[c]);
+            const uint2 vv = v_operand<T, D>(t, c);
+            acc[c] = Mfma<T>::pv(vv, phi, acc[c]);
+            acc[c] = Mfma<T>::pv(vv, plo, acc[c]);
         }
     };
 
@@ -715,13 +803,13 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
         // computes. Tiles past the end repeat the last one with every token masked:
         // the loop has no data-dependent branch, and each wait covers only the
         // loads it needs.
-        KvTile<D> X[kSplitStage], Y[kSplitStage];
+        KvTile<D, F8> X[kSplitStage], Y[kSplitStage];
         bool okX[kSplitStage], okY[kSplitStage];
-        auto load_stage = [&](KvTile<D>* t, bool* ok, int k) {
+        auto load_stage = [&](KvTile<D, F8>* t, bool* ok, int k) {
 #pragma unroll
             for (int i = 0; i < kSplitStage; ++i) ok[i] = load(t[i], min(k + i, cnt - 1));
         };
-        auto compute_stage = [&](KvTile<D>* t, const bool* ok, int k) {
+        auto compute_stage = [&](KvTile<D, F8>* t, const bool* ok, int k) {
 #pragma unroll
             for (int i = 0; i < kSplitStage; ++i)
                 compute(t[i], min(k + i, cnt - 1), ok[i] && k + i < cnt);
@@ -868,26 +956,26 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 
 constexpr int kWaves = 4;
 
-template <typename T, int D, typename OutT>
+template <typename T, int D, typename OutT, bool F8>
 hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
     const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
     if (a.new_k)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true>), grid, dim3(kWaves * 64),
-                              lds, s, ev.start, ev.stop, 0, a);
+        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true, F8>), grid,
+                              dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
     else
-        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, false>), grid, dim3(kWaves * 64),
-                              lds, s, ev.start, ev.stop, 0, a);
+        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, false, F8>), grid,
+                              dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
-template <typename T, int D, typename OutT>
+template <typename T, int D, typename OutT, bool F8>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
     const int groups = (a.split.units + kSplitThreads / 64 - 1) / (kSplitThreads / 64);
     const size_t lds = size_t(kSplitThreads / 64) * split_wave_bytes(a.group, D, a.slots);
     const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
-    hipExtLaunchKernelGGL((decode_split_kernel<T, D, OutT>), dim3(groups), dim3(kSplitThreads), lds, s,
-                          ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((decode_split_kernel<T, D, OutT, F8>), dim3(groups), dim3(kSplitThreads),
+                          lds, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
 
@@ -898,23 +986,29 @@ hipError_t launch_f32(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid, hipStream_t s,
-                    bool split) {
+template <int D, bool F8>
+hipError_t dispatch_16(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid, hipStream_t s,
+                       bool split) {
     if (split) {
         if (in_dtype == PKV_BF16)
-            return out_dtype == PKV_F32 ? launch_split<bf16_t, D, float>(a, s)
-                                        : launch_split<bf16_t, D, bf16_t>(a, s);
-        return out_dtype == PKV_F32 ? launch_split<f16_t, D, float>(a, s)
-                                    : launch_split<f16_t, D, f16_t>(a, s);
+            return out_dtype == PKV_F32 ? launch_split<bf16_t, D, float, F8>(a, s)
+                                        : launch_split<bf16_t, D, bf16_t, F8>(a, s);
+        return out_dtype == PKV_F32 ? launch_split<f16_t, D, float, F8>(a, s)
+                                    : launch_split<f16_t, D, f16_t, F8>(a, s);
     }
     if (in_dtype == PKV_BF16)
-        return out_dtype == PKV_F32 ? launch_mfma<bf16_t, D, float>(a, grid, s)
-                                    : launch_mfma<bf16_t, D, bf16_t>(a, grid, s);
-    if (in_dtype == PKV_F16)
-        return out_dtype == PKV_F32 ? launch_mfma<f16_t, D, float>(a, grid, s)
-                                    : launch_mfma<f16_t, D, f16_t>(a, grid, s);
-    return launch_f32<D, float>(a, grid, s);
+        return out_dtype == PKV_F32 ? launch_mfma<bf16_t, D, float, F8>(a, grid, s)
+                                    : launch_mfma<bf16_t, D, bf16_t, F8>(a, grid, s);
+    return out_dtype == PKV_F32 ? launch_mfma<f16_t, D, float, F8>(a, grid, s)
+                                : launch_mfma<f16_t, D, f16_t, F8>(a, grid, s);
+}
+
+template <int D>
+hipError_t dispatch(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid, hipStream_t s,
+                    bool split, bool fp8) {
+    if (in_dtype == PKV_F32) return launch_f32<D, float>(a, grid, s);
+    return fp8 ? dispatch_16<D, true>(a, in_dtype, out_dtype, grid, s, split)
+               : dispatch_16<D, false>(a, in_dtype, out_dtype, grid, s, split);
 }
 
 // Waves per compute unit that the balanced split plans for: two workgroups of four
@@ -973,16 +1067,27 @@ struct AppendIn {
     const int32_t* slot_mapping;
 };
 
+// FP8 cache: kv_dtype == PKV_FP8_E4M3 and its two scales; otherwise kv_dtype == in_dtype.
 int decode_impl(const char* who, void* out, float* part_out, float* part_max, float* part_sum,
                 const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                 int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                 int32_t partition_size, int32_t max_partitions, int32_t in_dtype,
-                int32_t out_dtype, const AppendIn& app, void* stream) {
+                int32_t out_dtype, int32_t kv_dtype, float k_scale, float v_scale,
+                const AppendIn& app, void* stream) {
     using pkv::fail;
     const int e = pkv::elem_bytes(in_dtype);
     if (e == 0) return fail(PKV_EINVAL, "%s: unknown in_dtype %d", who, in_dtype);
+    const bool fp8 = kv_dtype == PKV_FP8_E4M3;
+    if (fp8) {
+        if (in_dtype == PKV_F32)
+            return fail(PKV_ENOTSUP, "%s: an FP8 cache needs F16 or BF16 queries", who);
+        if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+            return fail(PKV_EINVAL, "%s: k_scale and v_scale must be finite and positive", who);
+    } else {
+        k_scale = v_scale = 1.0f;
+    }
     if (pkv::elem_bytes(out_dtype) == 0)
         return fail(PKV_EINVAL, "%s: unknown out_dtype %d", who, out_dtype);
     if (out_dtype != in_dtype && out_dtype != PKV_F32)
@@ -1059,10 +1164,16 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
             return fail(PKV_EINVAL, "%s: key and value must be 16-byte aligned", who);
         fused = in_dtype != PKV_F32 && !split;
         if (!fused) {
-            const int rc = reshape_and_cache(app.key, app.value, const_cast<void*>(k_cache),
-                                             const_cast<void*>(v_cache), app.slot_mapping, num_seqs,
-                                             num_kv_heads, head_dim, block_size, num_blocks,
-                                             app.key_stride, app.value_stride, in_dtype, stream);
+            const int rc =
+                fp8 ? reshape_and_cache_fp8(app.key, app.value, const_cast<void*>(k_cache),
+                                            const_cast<void*>(v_cache), app.slot_mapping, num_seqs,
+                                            num_kv_heads, head_dim, block_size, num_blocks,
+                                            app.key_stride, app.value_stride, in_dtype, k_scale,
+                                            v_scale, stream)
+                    : reshape_and_cache(app.key, app.value, const_cast<void*>(k_cache),
+                                        const_cast<void*>(v_cache), app.slot_mapping, num_seqs,
+                                        num_kv_heads, head_dim, block_size, num_blocks,
+                                        app.key_stride, app.value_stride, in_dtype, stream);
             if (rc != PKV_OK) return rc;
         }
     }
@@ -1085,7 +1196,9 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
     a.max_blocks = max_blocks_per_seq;
     a.part_blocks = part_blocks;
     a.max_partitions = partition_size != 0 ? max_partitions : 1;
-    a.scale_log2 = scale * pkv::kLog2e;
+    a.scale_log2 = scale * k_scale * pkv::kLog2e;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     a.num_seqs = num_seqs;
     a.split.units = split ? pkv::split_units() : 0;
     a.split.min_share = split ? (max_blocks_per_seq + max_partitions - 2) / (max_partitions - 1) : 0;
@@ -1107,8 +1220,8 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
                           ? dim3{unsigned(num_kv_heads), unsigned(num_seqs), unsigned(grid_parts)}
                           : dim3{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
     const hipError_t err = head_dim == 128
-                               ? pkv::dispatch<128>(a, in_dtype, out_dtype, grid, s, split)
-                               : pkv::dispatch<64>(a, in_dtype, out_dtype, grid, s, split);
+                               ? pkv::dispatch<128>(a, in_dtype, out_dtype, grid, s, split, fp8)
+                               : pkv::dispatch<64>(a, in_dtype, out_dtype, grid, s, split, fp8);
     if (err != hipSuccess)
         return fail(PKV_EHIP, "%s: launch failed: %s", who, hipGetErrorString(err));
     return pkv::ok();
@@ -1128,8 +1241,8 @@ extern "C" int paged_attention_decode(void* out, float* part_out, float* part_ma
     return decode_impl("paged_attention_decode", out, part_out, part_max, part_sum, q, q_stride,
                        k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                        head_dim, block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
-                       max_partitions, in_dtype, out_dtype, AppendIn{nullptr, nullptr, 0, 0, nullptr},
-                       stream);
+                       max_partitions, in_dtype, out_dtype, in_dtype, 1.0f, 1.0f,
+                       AppendIn{nullptr, nullptr, 0, 0, nullptr}, stream);
 }
 
 extern "C" int paged_attention_decode_append(
@@ -1145,6 +1258,41 @@ extern "C" int paged_attention_decode_append(
     return decode_impl("paged_attention_decode_append", out, part_out, part_max, part_sum, q,
                        q_stride, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
-                       partition_size, max_partitions, in_dtype, out_dtype,
+                       partition_size, max_partitions, in_dtype, out_dtype, in_dtype, 1.0f, 1.0f,
                        AppendIn{key, value, key_stride, value_stride, slot_mapping}, stream);
+}
+
+extern "C" int paged_attention_decode_fp8(void* out, float* part_out, float* part_max,
+                                          float* part_sum, const void* q, int64_t q_stride,
+                                          const void* k_cache, const void* v_cache,
+                                          const int32_t* block_tables, const int32_t* seq_lens,
+                                          int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_blocks_per_seq,
+                                          int64_t num_blocks, float scale, float k_scale,
+                                          float v_scale, int32_t partition_size,
+                                          int32_t max_partitions, int32_t in_dtype,
+                                          int32_t out_dtype, void* stream) {
+    return decode_impl("paged_attention_decode_fp8", out, part_out, part_max, part_sum, q,
+                       q_stride, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       partition_size, max_partitions, in_dtype, out_dtype, PKV_FP8_E4M3, k_scale,
+                       v_scale, AppendIn{nullptr, nullptr, 0, 0, nullptr}, stream);
+}
+
+extern "C" int paged_attention_decode_append_fp8(
+    void* out, float* part_out, float* part_max, float* part_sum, const void* q, int64_t q_stride,
+    const void* key, const void* value, int64_t key_stride, int64_t value_stride,
+    const int32_t* slot_mapping, void* k_cache, void* v_cache, const int32_t* block_tables,
+    const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+    float scale, float k_scale, float v_scale, int32_t partition_size, int32_t max_partitions,
+    int32_t in_dtype, int32_t out_dtype, void* stream) {
+    if (num_seqs > 0 && !key)
+        return pkv::fail(PKV_EINVAL, "paged_attention_decode_append_fp8: NULL key");
+    return decode_impl("paged_attention_decode_append_fp8", out, part_out, part_max, part_sum, q,
+                       q_stride, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       partition_size, max_partitions, in_dtype, out_dtype, PKV_FP8_E4M3, k_scale,
+                       v_scale, AppendIn{key, value, key_stride, value_stride, slot_mapping}, stream);
 }

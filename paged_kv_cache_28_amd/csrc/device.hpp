@@ -111,6 +111,70 @@ template <> struct Mfma<f16_t> {
     }
 };
 
+// 16-bit pattern of the input type -> fp32 (exact).
+template <typename T> struct Bits;
+template <> struct Bits<bf16_t> {
+    __device__ __forceinline__ static float to_f32(uint16_t h) { return bf16_bits_to_f32(h); }
+};
+template <> struct Bits<f16_t> {
+    __device__ __forceinline__ static float to_f32(uint16_t h) { return f16_bits_to_f32(h); }
+};
+
+// ---- FP8 KV cache: OCP e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// S.1111.111 = NaN, largest finite 448).
+//
+// fp8x4_to<T>(w): the four codes in w (lowest byte first) as four 16-bit values of T,
+// two per 32-bit word, lowest first. Exact: every e4m3 value is a bf16 and an fp16
+// value. One gfx950 conversion per pair; its scale operand is 1 (the cache scales are
+// applied to the logits and the output instead).
+template <typename T> struct Fp8;
+template <> struct Fp8<bf16_t> {
+    __device__ __forceinline__ static uint2 x4(uint32_t w) {
+        return make_uint2(
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+    }
+};
+template <> struct Fp8<f16_t> {
+    __device__ __forceinline__ static uint2 x4(uint32_t w) {
+        return make_uint2(
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
+    }
+};
+
+// binary32 -> e4m3 code: the nearest finite value, ties to the even code. Magnitudes
+// beyond 448 (infinities too) saturate: the hardware conversion (round to nearest even)
+// only ever sees the clamped value. NaN gives S.1111.111 with the input's sign.
+__device__ __forceinline__ uint32_t f32_to_fp8(float x) {
+    const float c = fminf(fmaxf(x, -448.0f), 448.0f);
+    const uint32_t code = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false)) & 0xffu;
+    return x != x ? ((__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u) | 0x7fu : code;
+}
+
+// The stored code of input element x under a per-tensor scale: x / scale rounded once
+// to binary32 (an IEEE division), then encoded.
+__device__ __forceinline__ uint32_t quantize_fp8(float x, float scale) {
+    return f32_to_fp8(x / scale);
+}
+
+// Codes of the 16 input elements in a0 (elements 0-7) and a1 (8-15), packed four per
+// word, lowest first: one 16-byte group of the FP8 cache.
+template <typename T>
+__device__ __forceinline__ uint4 quantize_fp8_x16(uint4 a0, uint4 a1, float scale) {
+    const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = w[2 * k], hi = w[2 * k + 1];
+        o[k] = quantize_fp8(Bits<T>::to_f32(uint16_t(lo)), scale) |
+               (quantize_fp8(Bits<T>::to_f32(uint16_t(lo >> 16)), scale) << 8) |
+               (quantize_fp8(Bits<T>::to_f32(uint16_t(hi)), scale) << 16) |
+               (quantize_fp8(Bits<T>::to_f32(uint16_t(hi >> 16)), scale) << 24);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
     return fmaxf(v, __shfl_xor(v, mask, 64));
 }

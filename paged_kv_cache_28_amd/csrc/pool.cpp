@@ -76,7 +76,7 @@ const char* pkv_last_error(void) { return pkv::last_error().c_str(); }
 
 int64_t kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
                            int32_t dtype) {
-    int e = pkv::elem_bytes(dtype);
+    int e = pkv::cache_elem_bytes(dtype);
     if (num_layers <= 0 || num_kv_heads <= 0 || head_dim <= 0 || e == 0) {
         fail(PKV_EINVAL, "kv_bytes_per_token: bad shape or dtype");
         return -1;
@@ -94,11 +94,11 @@ int kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t num_layers,
                     (long long)num_blocks);
     if (block_size != PKV_BLOCK_SIZE)
         return fail(PKV_EINVAL, "kv_pool_create: block_size must be 16, got %d", block_size);
-    if (num_layers <= 0 || num_kv_heads <= 0 || head_dim <= 0 || pkv::elem_bytes(dtype) == 0)
+    if (num_layers <= 0 || num_kv_heads <= 0 || head_dim <= 0 || pkv::cache_elem_bytes(dtype) == 0)
         return fail(PKV_EINVAL, "kv_pool_create: bad model shape or dtype");
-    if (head_dim % (16 / pkv::elem_bytes(dtype)) != 0)
+    if (head_dim % (16 / pkv::cache_elem_bytes(dtype)) != 0)
         return fail(PKV_EINVAL, "kv_pool_create: head_dim must be a multiple of %d",
-                    16 / pkv::elem_bytes(dtype));
+                    16 / pkv::cache_elem_bytes(dtype));
     kv_pool* p = new (std::nothrow) kv_pool();
     if (!p) return fail(PKV_ENOMEM, "kv_pool_create: out of host memory");
     p->num_blocks = num_blocks;
@@ -140,7 +140,7 @@ int64_t kv_pool_bytes_per_token(const kv_pool* pool) {
 
 int kv_pool_cache_shape(const kv_pool* pool, int64_t k_shape[5], int64_t v_shape[4]) {
     if (!pool || !k_shape || !v_shape) return fail(PKV_EINVAL, "kv_pool_cache_shape: NULL");
-    int x = 16 / pkv::elem_bytes(pool->dtype);
+    int x = 16 / pkv::cache_elem_bytes(pool->dtype);
     k_shape[0] = pool->num_blocks;
     k_shape[1] = pool->num_kv_heads;
     k_shape[2] = pool->head_dim / x;

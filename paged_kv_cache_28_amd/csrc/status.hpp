@@ -27,8 +27,12 @@ inline int ok() {
     return PKV_OK;
 }
 
+// Bytes of a query / output / input-row element (0: not such a type).
 inline int elem_bytes(int dtype) {
     return dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2 : 0;
 }
+
+// Bytes of a cache element: the types above plus the FP8 cache type.
+inline int cache_elem_bytes(int dtype) { return dtype == PKV_FP8_E4M3 ? 1 : elem_bytes(dtype); }
 
 }  // namespace pkv

@@ -26,11 +26,24 @@ class GpuBatch:
     lens_d: torch.Tensor
 
 
+def write(w, key, value, kc, vc, slots):
+    """The library's cache write for the workload's cache type."""
+    if w.cache_dtype == "fp8":
+        pkv.reshape_and_cache_fp8(key, value, kc, vc, slots, w.k_scale, w.v_scale)
+    else:
+        pkv.reshape_and_cache(key, value, kc, vc, slots)
+
+
+def kv_scales(w):
+    return (w.k_scale, w.v_scale) if w.cache_dtype == "fp8" else None
+
+
 def build(ob, device="cuda", fill=float("nan"), write_new: bool = True) -> GpuBatch:
-    """write_new=False leaves the new tokens' slots unwritten (for the fused append)."""
+    """write_new=False leaves the new tokens' slots unwritten (for the fused append).
+    An FP8 cache is filled with the NaN code 0x7F where fill is NaN."""
     w = ob.w
     B = len(ob.lens)
-    pool = pkv.kv_pool_create(ob.num_blocks, 1, w.num_kv_heads, w.head_dim, w.dtype,
+    pool = pkv.kv_pool_create(ob.num_blocks, 1, w.num_kv_heads, w.head_dim, w.cache_dtype,
                               free_order=ob.free_order)
     prompt = []
     for b in range(B):
@@ -43,14 +56,15 @@ def build(ob, device="cuda", fill=float("nan"), write_new: bool = True) -> GpuBa
         new[live] = pool.append_batch(live)
     tables, lens = pool.build_tables(list(range(B)), ob.max_blocks)
 
-    kc, vc = pkv.alloc_caches(ob.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, device,
+    if w.cache_dtype == "fp8" and fill is not None and fill != fill:
+        fill = 0x7F
+    kc, vc = pkv.alloc_caches(ob.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, device,
                               fill=fill)
     if len(prompt_slots):
-        pkv.reshape_and_cache(ob.prompt_k.to(device), ob.prompt_v.to(device), kc, vc,
-                              torch.from_numpy(prompt_slots).to(device))
+        write(w, ob.prompt_k.to(device), ob.prompt_v.to(device), kc, vc,
+              torch.from_numpy(prompt_slots).to(device))
     if write_new:
-        pkv.reshape_and_cache(ob.new_k.to(device), ob.new_v.to(device), kc, vc,
-                              torch.from_numpy(new).to(device))
+        write(w, ob.new_k.to(device), ob.new_v.to(device), kc, vc, torch.from_numpy(new).to(device))
     return GpuBatch(pool, prompt_slots, new, tables, lens, kc, vc, ob.q.to(device),
                     torch.from_numpy(tables).to(device), torch.from_numpy(lens).to(device))
 
@@ -66,5 +80,5 @@ def run_decode(gb: GpuBatch, w, partition_size=0, out_dtype=torch.float32, max_p
         maxp = max_partitions or pkv.max_partitions_for(gb.tables.shape[1], partition_size)
         parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, dev))
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale,
-               partition_size, parts)
+               partition_size, parts, kv_scales=kv_scales(w))
     return out, parts

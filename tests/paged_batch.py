@@ -42,11 +42,17 @@ class OracleBatch:
         if n == 0:
             z = np.zeros((0, self.w.num_kv_heads, self.w.head_dim))
             return z, z
-        pk = oracle.to_f64(self.prompt_k[off:off + n - 1], dt)
-        pv = oracle.to_f64(self.prompt_v[off:off + n - 1], dt)
-        nk = oracle.to_f64(self.new_k[b:b + 1], dt)
-        nv = oracle.to_f64(self.new_v[b:b + 1], dt)
+        pk, pv = self._stored(self.prompt_k[off:off + n - 1], self.prompt_v[off:off + n - 1])
+        nk, nv = self._stored(self.new_k[b:b + 1], self.new_v[b:b + 1])
         return np.concatenate([pk, nk]), np.concatenate([pv, nv])
+
+    def _stored(self, k, v):
+        """fp64 values of rows as the cache holds them (FP8: dequantised codes)."""
+        w, dt = self.w, self.w.dtype
+        if w.cache_dtype != "fp8":
+            return oracle.to_f64(k, dt), oracle.to_f64(v, dt)
+        return (oracle.to_f64(oracle.fp8_quantize(k, dt, w.k_scale), "fp8") * w.k_scale,
+                oracle.to_f64(oracle.fp8_quantize(v, dt, w.v_scale), "fp8") * w.v_scale)
 
 
 def build(w: workloads.Workload, lens=None, seed_stream: int = 0, num_blocks: int | None = None,
@@ -80,11 +86,12 @@ def build(w: workloads.Workload, lens=None, seed_stream: int = 0, num_blocks: in
     tables, tl = pool.tables(list(range(B)), max_blocks)
     assert np.array_equal(tl, lens)
 
-    kc, vc = oracle.empty_caches(num_blocks, w.num_kv_heads, w.head_dim, w.dtype)
+    kc, vc = oracle.empty_caches(num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype)
     ps = np.asarray(prompt_slots, dtype=np.int32)
     ns = np.asarray(new_slots, dtype=np.int32)
+    cw = dict(cache_dtype=w.cache_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
     if len(ps):
-        oracle.cache_write(prompt_k, prompt_v, kc, vc, ps, w.dtype)
-    oracle.cache_write(new_k, new_v, kc, vc, ns, w.dtype)
+        oracle.cache_write(prompt_k, prompt_v, kc, vc, ps, w.dtype, **cw)
+    oracle.cache_write(new_k, new_v, kc, vc, ns, w.dtype, **cw)
     return OracleBatch(w, lens.astype(np.int32), free_order, num_blocks, q, prompt_k, prompt_v,
                        new_k, new_v, ps, ns, tables, max_blocks, kc, vc, pool)

@@ -62,10 +62,22 @@ class Workload:
     prefix_tokens: int = 0
     prompt_lo: int = 0
     prompt_hi: int = 0
+    # KV cache element type ("" = dtype; "fp8" = OCP e4m3 codes of x / k_scale, x / v_scale)
+    kv_dtype: str = ""
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def group(self) -> int:
         return self.num_heads // self.num_kv_heads
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def cache_elem_bytes(self) -> int:
+        return 1 if self.cache_dtype == "fp8" else self.elem_bytes
 
     @property
     def elem_bytes(self) -> int:
@@ -78,7 +90,7 @@ class Workload:
     @property
     def block_bytes_per_layer(self) -> int:
         """Bytes of one physical block (K and V, all KV heads) in one layer."""
-        return 2 * self.num_kv_heads * BLOCK_SIZE * self.head_dim * self.elem_bytes
+        return 2 * self.num_kv_heads * BLOCK_SIZE * self.head_dim * self.cache_elem_bytes
 
 
 WORKLOADS = {
@@ -89,6 +101,11 @@ WORKLOADS = {
     "llama8b": Workload("llama8b", layers=32, batch=64, num_heads=32, num_kv_heads=8,
                         head_dim=128, dtype="bf16", seed=28002, len_lo=128, len_hi=2048,
                         partition_size=0),
+    # The same with an FP8 (e4m3) KV cache: per-tensor scales put N(0,1) rows at up to
+    # about 6.7 (K) and 5.6 (V) standard deviations inside e4m3's +-448.
+    "llama8b_fp8": Workload("llama8b_fp8", layers=32, batch=64, num_heads=32, num_kv_heads=8,
+                            head_dim=128, dtype="bf16", seed=28002, len_lo=128, len_hi=2048,
+                            partition_size=0, kv_dtype="fp8", k_scale=0.015, v_scale=0.0125),
     # Llama-3-70B shape: 80 layers, 64q/8kv, d 128, fp16, B 128; 90% short
     # (300 prompt + up to 100 generated), 10% long (30,000 + up to 4,000). The ragged mix
     # runs best in the balanced split.
