@@ -115,7 +115,9 @@ def main():
     else:
         P = pkv.PKV_PARTITION_AUTO if args.partition == "auto" else int(args.partition)
     L, B, Hq, Hkv, d = w.layers, w.batch, w.num_heads, w.num_kv_heads, w.head_dim
-    e = w.elem_bytes
+    e = w.elem_bytes                 # q, out and new-row inputs
+    ekv = w.cache_elem_bytes         # cache elements (1 for an FP8 cache)
+    fp8 = w.cache_dtype == "fp8"
     tdt = pkv.torch_dtype(w.dtype)
 
     # ---------------------------------------------------------------- setup
@@ -135,9 +137,15 @@ def main():
     g.manual_seed(w.seed)
     caches = []
     for _ in range(L):
-        kc, vc = pkv.alloc_caches(nb, Hkv, d, tdt, dev)
-        kc.normal_(generator=g)
-        vc.normal_(generator=g)
+        kc, vc = pkv.alloc_caches(nb, Hkv, d, w.cache_dtype, dev)
+        if fp8:   # codes of N(0,1) draws under the workload's scales
+            for t, sc in ((kc, w.k_scale), (vc, w.v_scale)):
+                x = torch.randn(t.shape, generator=g, device=dev).div_(sc).clamp_(-448, 448)
+                t.copy_(x.to(torch.float8_e4m3fn).view(torch.uint8))
+                del x
+        else:
+            kc.normal_(generator=g)
+            vc.normal_(generator=g)
         caches.append((kc, vc))
     q = [torch.randn((B, Hq, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
     k_new = [torch.randn((B, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
@@ -162,7 +170,7 @@ def main():
         copied[k].synchronize()                       # H2D of two steps ago has finished
         pool.append_batch(ids, out=h_slot[k].numpy())
         pool.build_tables(ids, max_blocks, h_tab[k].numpy(), h_len[k].numpy())
-        kv_bytes_steps.append(int(h_len[k].numpy().astype(np.int64).sum()) * Hkv * d * 2 * e * L)
+        kv_bytes_steps.append(int(h_len[k].numpy().astype(np.int64).sum()) * Hkv * d * 2 * ekv * L)
         d_slot.copy_(h_slot[k], non_blocking=True)
         d_tab.copy_(h_tab[k], non_blocking=True)
         d_len.copy_(h_len[k], non_blocking=True)
@@ -170,7 +178,17 @@ def main():
         po, pm, ps = parts if P != 0 else (None, None, None)
         for layer in range(L):
             kc, vc = caches[layer]
-            if args.unfused:
+            if fp8 and args.unfused:
+                pkv.reshape_and_cache_fp8(k_new[layer], v_new[layer], kc, vc, d_slot, w.k_scale,
+                                          w.v_scale)
+                pkv.paged_attention_decode_fp8(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
+                                               w.k_scale, w.v_scale, P, po, pm, ps, maxp)
+            elif fp8:
+                pkv.paged_attention_decode_append_fp8(out[layer], q[layer], k_new[layer],
+                                                      v_new[layer], d_slot, kc, vc, d_tab, d_len,
+                                                      w.scale, w.k_scale, w.v_scale, P, po, pm,
+                                                      ps, maxp)
+            elif args.unfused:
                 pkv.reshape_and_cache(k_new[layer], v_new[layer], kc, vc, d_slot)
                 pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
                                            P, po, pm, ps, maxp)
@@ -220,11 +238,11 @@ def main():
     dec_avg_s = kernel_us["decode"] / 1e6 if kernel_us["decode"] else float("nan")
     # algorithmic bytes of one decode launch: KV once per (seq, KV head), q, out, table rows;
     # fused, also the new rows read from the inputs and written to the pool
-    new_rows = 0 if args.unfused else 2 * (2 * B * Hkv * d * e) + 4 * B
+    new_rows = 0 if args.unfused else 2 * (B * Hkv * d * (e + ekv)) + 4 * B
     alg = []
     for ln in timing_lens:
         ln = ln.astype(np.int64)
-        alg.append(int(ln.sum()) * Hkv * d * 2 * e + 2 * B * Hq * d * e +
+        alg.append(int(ln.sum()) * Hkv * d * 2 * ekv + 2 * B * Hq * d * e +
                    int((-(-ln // 16)).sum()) * 4 + 4 * B + new_rows)
     alg_per_launch = sum(alg) / len(alg) if alg else float("nan")
     achieved = alg_per_launch / dec_avg_s / 1e9
@@ -244,6 +262,8 @@ def main():
         "data": "synthetic (seeded draws of the workload's shapes and length mix)",
         "config": {"workload": f"{w.name}-decode", "layers": L, "batch": B, "num_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": d, "block_size": 16,
+                   "kv_cache_dtype": ("fp8 e4m3, k_scale %g, v_scale %g" % (w.k_scale, w.v_scale)
+                                      if fp8 else w.dtype),
                    "seq_len_range": [w.len_lo, w.len_hi],
                    "partition_size": "auto" if P == pkv.PKV_PARTITION_AUTO else P,
                    "cache_write": ("separate launch" if args.unfused else
@@ -264,7 +284,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4) if alg else None, "traffic": None,
                      "kernel": ("paged_attention_decode" if args.unfused
-                                else "paged_attention_decode_append (fused cache write + decode)"),
+                                else "paged_attention_decode_append (fused cache write + decode)")
+                               + ("_fp8" if fp8 else ""),
                      "alg_bytes_per_launch": int(alg_per_launch) if alg else None},
         "cpu_baseline": None,
     }
@@ -329,11 +350,13 @@ def cpu_baseline(w, cache0, q0, d_tab, d_len, budget_s: float):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         cores = os.cpu_count() or 1
-    kv_per_pass = int(lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * 2 * w.elem_bytes
+    kv_per_pass = (int(lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * 2 *
+                   w.cache_elem_bytes)
     passes, t = 0, 0.0
     while t < budget_s:
         t0 = time.perf_counter()
-        oracle.decode(q_h, kc_h, vc_h, tab, lens, w.scale, w.dtype, nthreads=cores)
+        oracle.decode(q_h, kc_h, vc_h, tab, lens, w.scale, w.dtype, nthreads=cores,
+                      kv_dtype=w.cache_dtype, k_scale=w.k_scale, v_scale=w.v_scale)
         t += time.perf_counter() - t0
         passes += 1
     return {"value": round(kv_per_pass * passes / t / 1e9, 4), "unit": "GB/s", "cores": cores,

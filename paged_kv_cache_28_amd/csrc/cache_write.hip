@@ -55,36 +55,40 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     }
 }
 
-// FP8 cache: one thread quantises 16 dimensions of one (token, KV head), i.e. one 16-byte
-// K group of the [blk][g][d/16][16][16] layout and 16 bytes of V, one per dimension row
-// of the [blk][g][d][16] tile.
+// FP8 cache: one thread quantises 4 dimensions of one (token, KV head): a quarter of a
+// 16-byte K group of the [blk][g][d/16][16][16] layout (one 4-byte store) and 4 bytes of
+// V, one per dimension row of the [blk][g][d][16] tile. Four dimensions per thread keep
+// the correctly rounded divisions per thread few; sixteen made the kernel latency-bound.
 template <typename T>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, uint8_t* __restrict__ kc,
     uint8_t* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens, int32_t hkv,
     int32_t d, int64_t num_blocks, int64_t key_stride, int64_t value_stride, float k_scale,
     float v_scale) {
-    const int nchunk = d / 16;
+    const int nq = d / 4;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t total = int64_t(num_tokens) * hkv * nchunk;
+    const int64_t total = int64_t(num_tokens) * hkv * nq;
     if (idx >= total) return;
-    const int c = int(idx % nchunk);
-    const int g = int((idx / nchunk) % hkv);
-    const int64_t t = idx / (int64_t(nchunk) * hkv);
-    const uint4* kr = reinterpret_cast<const uint4*>(key + t * key_stride + int64_t(g) * d + c * 16);
-    const uint4* vr = reinterpret_cast<const uint4*>(value + t * value_stride + int64_t(g) * d + c * 16);
-    const uint4 k0 = kr[0], k1 = kr[1], v0 = vr[0], v1 = vr[1];
+    const int c = int(idx % nq);              // dimensions 4c .. 4c + 3
+    const int g = int((idx / nq) % hkv);
+    const int64_t t = idx / (int64_t(nq) * hkv);
+    const uint2 kr = *reinterpret_cast<const uint2*>(key + t * key_stride + int64_t(g) * d + 4 * c);
+    const uint2 vr = *reinterpret_cast<const uint2*>(value + t * value_stride + int64_t(g) * d + 4 * c);
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_blocks * 16) return;
     const int64_t tile = (slot >> 4) * hkv + g;
     const int off = int(slot & 15);
-    *reinterpret_cast<uint4*>(kc + ((tile * nchunk + c) * 16 + off) * 16) =
-        quantize_fp8_x16<T>(k0, k1, k_scale);
-    const uint4 vq = quantize_fp8_x16<T>(v0, v1, v_scale);
-    const uint32_t w[4] = {vq.x, vq.y, vq.z, vq.w};
-    uint8_t* vdst = vc + (tile * d + int64_t(c) * 16) * 16 + off;
+    const uint32_t h[4] = {kr.x & 0xffffu, kr.x >> 16, kr.y & 0xffffu, kr.y >> 16};
+    const uint32_t u[4] = {vr.x & 0xffffu, vr.x >> 16, vr.y & 0xffffu, vr.y >> 16};
+    uint32_t kw = 0;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) vdst[k * 16] = uint8_t(w[k / 4] >> (8 * (k % 4)));
+    for (int k = 0; k < 4; ++k) kw |= quantize_fp8(Bits<T>::to_f32(uint16_t(h[k])), k_scale) << (8 * k);
+    // dims 4c .. 4c + 3 sit in group 4c / 16 at byte (4c) % 16 of the token's 16-byte row
+    *reinterpret_cast<uint32_t*>(kc + ((tile * (d / 16) + (4 * c) / 16) * 16 + off) * 16 + (4 * c) % 16) = kw;
+    uint8_t* vdst = vc + (tile * d + int64_t(4) * c) * 16 + off;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        vdst[k * 16] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(u[k])), v_scale));
 }
 
 }  // namespace pkv
@@ -118,7 +122,7 @@ extern "C" int reshape_and_cache_fp8(const void* key, const void* value, void* k
     if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) |
          reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
         return fail(PKV_EINVAL, "reshape_and_cache_fp8: buffers must be 16-byte aligned");
-    const int64_t total = int64_t(num_tokens) * num_kv_heads * (head_dim / 16);
+    const int64_t total = int64_t(num_tokens) * num_kv_heads * (head_dim / 4);
     const int64_t grid = (total + 255) / 256;
     if (grid > 0x7fffffff) return fail(PKV_EINVAL, "reshape_and_cache_fp8: too many tokens");
     hipStream_t s = static_cast<hipStream_t>(stream);

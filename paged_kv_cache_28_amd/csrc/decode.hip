@@ -313,33 +313,57 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
     // Fused append: the new token's rows, every lane its share in the tile layout: K as
     // the lane's 16-byte K loads hold them (16-bit cache: dims 32c + 8 quad .. + 7; FP8
-    // cache: the codes of dims 16(4i + quad) .. + 15), V dim 16c + l%16 (FP8: its code).
-    // Kept in registers: reading them from LDS inside the tile loop made the compiler move
-    // the tiles to scratch.
+    // cache: dims 16(4i + quad) .. + 15), V dim 16c + l%16. Kept in registers: reading
+    // them from LDS inside the tile loop made the compiler move the tiles to scratch.
+    // FP8: each lane loads D/64 consecutive elements of each raw row (nkr, nvr) and, in
+    // the wave that stores the row, quantises just those (quantize_new, once its first
+    // tiles are on the way); the codes meet in the wave's LDS slice, from which every
+    // lane takes the ones it holds in the tile layout (nk, nv). Quantising whole K groups
+    // per lane instead cost 40 divisions per lane.
+    constexpr int NQ = D / 64;   // elements of each new row one lane quantises
     int slot = -1;
     uint4 nk[Append ? NKL : 1];
     uint32_t nv[Append ? NPV : 1];
+    uint32_t nkr = 0, nvr = 0;   // FP8: NQ raw 16-bit elements each (NQ <= 2)
     if constexpr (Append) {
         slot = a.slot_mapping[b];
         const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
                                int64_t(g) * D;
         const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
-                               int64_t(g) * D + col;
+                               int64_t(g) * D;
         if constexpr (F8) {
-#pragma unroll
-            for (int i = 0; i < NKL; ++i)
-                nk[i] = quantize_fp8_x16<T>(*reinterpret_cast<const uint4*>(krow + 64 * i + 16 * quad),
-                                            *reinterpret_cast<const uint4*>(krow + 64 * i + 16 * quad + 8),
-                                            a.k_scale);
-#pragma unroll
-            for (int c = 0; c < NPV; ++c) nv[c] = quantize_fp8(Bits<T>::to_f32(vrow[16 * c]), a.v_scale);
+            static_assert(NQ == 1 || NQ == 2, "head_dim 64 or 128");
+            if constexpr (NQ == 2) {
+                nkr = *reinterpret_cast<const uint32_t*>(krow + 2 * lane);
+                nvr = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
+            } else {
+                nkr = krow[lane];
+                nvr = vrow[lane];
+            }
         } else {
 #pragma unroll
             for (int c = 0; c < NKL; ++c) nk[c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * quad);
 #pragma unroll
-            for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c];
+            for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c + col];
         }
     }
+    auto quantize_new = [&]() {
+        if constexpr (Append && F8) {
+            // this wave's slice of sm_o (G * D floats >= 2 * D bytes), free until the merge
+            uint8_t* q8 = reinterpret_cast<uint8_t*>(sm_o + wave * G * D);
+#pragma unroll
+            for (int e = 0; e < NQ; ++e) {
+                q8[NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nkr >> (16 * e))), a.k_scale));
+                q8[D + NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nvr >> (16 * e))), a.v_scale));
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < NKL; ++i) nk[i] = *reinterpret_cast<const uint4*>(q8 + 64 * i + 16 * quad);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) nv[c] = q8[D + 16 * c + col];
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
 
     // This wave takes blocks first, first + W, ... of its partition. The block ids of its
     // first 64 are read before the length is known (the table row has max_blocks
@@ -379,7 +403,9 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     // streams (issued at the end of the stream they would lengthen the kernel's tail).
     auto store_new_row = [&]() {
         if constexpr (Append) {
-            if (wave != w_new || slot < 0 || int64_t(slot) >= a.num_blocks * 16) return;
+            if (wave != w_new) return;
+            quantize_new();   // FP8: the codes, also those of the one-row tile at the end
+            if (slot < 0 || int64_t(slot) >= a.num_blocks * 16) return;
             const int64_t tile = (int64_t(slot) >> 4) * a.num_kv_heads + g;
             const int off = slot & 15;
             char* kc = const_cast<char*>(static_cast<const char*>(a.k_cache));
@@ -471,10 +497,12 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
-    // Segments of up to 64 blocks (one block id per lane). Inside a segment two tiles
-    // are in flight: the next block's loads are always issued (the last one re-reads
-    // the final block, which is then in cache) before the current block is used, so
-    // the wait for the current tile never waits for the next.
+    // Segments of up to 64 blocks (one block id per lane). Inside a segment two stages of
+    // S tiles are in flight: the next stage's loads are always issued (past the end they
+    // re-read the final block, which is then in cache) before the current stage is used,
+    // so the wait for the current tile never waits for the next. S = 1 also for the
+    // half-size FP8 tiles: stages of two measured slower.
+    constexpr int S = 1;
     for (int k0 = 0; k0 < nmine; k0 += 64) {
         const int cnt = min(64, nmine - k0);
         tab = k0 == 0 ? tab0 : (lane < cnt ? table[first + (k0 + lane) * W] : 0);
@@ -486,15 +514,23 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                 lim = subst ? n - 1 : n;
             }
         }
-        KvTile<D, F8> A, B;
-        bool okA = load(A, 0), okB;
+        KvTile<D, F8> X[S], Y[S];
+        bool okX[S], okY[S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) okX[i] = load(X[i], min(i, cnt - 1));
         if (k0 == 0) store_new_row();
-        for (int k = 0; k < cnt; k += 2) {
-            okB = load(B, min(k + 1, cnt - 1));
-            compute(A, first + (k0 + k) * W, okA);
-            if (k + 1 >= cnt) break;
-            okA = load(A, min(k + 2, cnt - 1));
-            compute(B, first + (k0 + k + 1) * W, okB);
+        for (int k = 0; k < cnt; k += 2 * S) {
+#pragma unroll
+            for (int i = 0; i < S; ++i) okY[i] = load(Y[i], min(k + S + i, cnt - 1));
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+                if (k + i < cnt) compute(X[i], first + (k0 + k + i) * W, okX[i]);
+            if (k + S >= cnt) break;
+#pragma unroll
+            for (int i = 0; i < S; ++i) okX[i] = load(X[i], min(k + 2 * S + i, cnt - 1));
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+                if (k + S + i < cnt) compute(Y[i], first + (k0 + k + S + i) * W, okY[i]);
         }
     }
 
@@ -803,23 +839,24 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
         // computes. Tiles past the end repeat the last one with every token masked:
         // the loop has no data-dependent branch, and each wait covers only the
         // loads it needs.
-        KvTile<D, F8> X[kSplitStage], Y[kSplitStage];
-        bool okX[kSplitStage], okY[kSplitStage];
+        constexpr int S = kSplitStage;   // also for FP8 tiles: stages of two measured slower
+        KvTile<D, F8> X[S], Y[S];
+        bool okX[S], okY[S];
         auto load_stage = [&](KvTile<D, F8>* t, bool* ok, int k) {
 #pragma unroll
-            for (int i = 0; i < kSplitStage; ++i) ok[i] = load(t[i], min(k + i, cnt - 1));
+            for (int i = 0; i < S; ++i) ok[i] = load(t[i], min(k + i, cnt - 1));
         };
         auto compute_stage = [&](KvTile<D, F8>* t, const bool* ok, int k) {
 #pragma unroll
-            for (int i = 0; i < kSplitStage; ++i)
+            for (int i = 0; i < S; ++i)
                 compute(t[i], min(k + i, cnt - 1), ok[i] && k + i < cnt);
         };
         load_stage(X, okX, 0);
-        for (int k = 0; k < cnt; k += 2 * kSplitStage) {
-            load_stage(Y, okY, k + kSplitStage);
+        for (int k = 0; k < cnt; k += 2 * S) {
+            load_stage(Y, okY, k + S);
             compute_stage(X, okX, k);
-            load_stage(X, okX, k + 2 * kSplitStage);
-            compute_stage(Y, okY, k + kSplitStage);
+            load_stage(X, okX, k + 2 * S);
+            compute_stage(Y, okY, k + S);
         }
         tb += cnt;
     }
