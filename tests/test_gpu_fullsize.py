@@ -3,7 +3,8 @@ bench uses for it and in the balanced split, checked on sampled outputs.
 
 * slots and block tables: every one, bit-exact against the oracle's pool model;
 * cache write: a random sample of tokens read back through the documented layout,
-  bit-exact against the rows that were written;
+  bit-exact against the rows that were written (FP8 cache: against the oracle's codes of
+  those rows);
 * attention: sampled (sequence, head) rows against the oracle's textbook attention over
   the sequence's logical K/V (paged equals contiguous is pinned in the oracle tests),
   max |err| <= 2e-3 on fp32 output (inputs fp16/bf16) and max|err|/max|ref| <= 1e-3.
@@ -40,7 +41,7 @@ class Layer:
         B, Hkv, d = len(lens), w.num_kv_heads, w.head_dim
         nb = workloads.pool_blocks_for(lens)
         order = workloads.draw_free_order(nb, workloads.rng(w.seed, 1, layer))
-        pool = pkv.kv_pool_create(nb, 1, Hkv, d, w.dtype, free_order=order)
+        pool = pkv.kv_pool_create(nb, 1, Hkv, d, w.cache_dtype, free_order=order)
         model = oracle.PoolModel(nb, order)
         prompt = np.maximum(lens - 1, 0)
         ps_p, ps_m = [], []
@@ -64,11 +65,15 @@ class Layer:
         self.nk = workloads.draw_tokens_device(B, w, (2, layer, 2), device)
         self.nv = workloads.draw_tokens_device(B, w, (2, layer, 3), device)
         self.q = workloads.draw_q_device(w, (3, layer), device)
-        self.kc, self.vc = pkv.alloc_caches(nb, Hkv, d, w.dtype, device, fill=float("nan"))
-        pkv.reshape_and_cache(self.pk, self.pv, self.kc, self.vc,
-                              torch.from_numpy(self.prompt_slots).to(device))
-        pkv.reshape_and_cache(self.nk, self.nv, self.kc, self.vc,
-                              torch.from_numpy(self.new_slots).to(device))
+        self.fp8 = w.cache_dtype == "fp8"
+        self.kc, self.vc = pkv.alloc_caches(nb, Hkv, d, w.cache_dtype, device,
+                                            fill=0x7F if self.fp8 else float("nan"))
+        for k, v, sl in ((self.pk, self.pv, self.prompt_slots), (self.nk, self.nv, self.new_slots)):
+            sl = torch.from_numpy(sl).to(device)
+            if self.fp8:
+                pkv.reshape_and_cache_fp8(k, v, self.kc, self.vc, sl, w.k_scale, w.v_scale)
+            else:
+                pkv.reshape_and_cache(k, v, self.kc, self.vc, sl)
         self.tables_d = torch.from_numpy(self.tables).to(device)
         self.lens_d = torch.from_numpy(self.lens).to(device)
         self.num_blocks = nb
@@ -83,7 +88,8 @@ class Layer:
         if P != 0:
             maxp = pkv.max_partitions_for(self.max_blocks, P)
             parts = pkv.alloc_partials(B, w.num_heads, w.head_dim, maxp, dev)
-        pkv.decode(out, self.q, self.kc, self.vc, self.tables_d, self.lens_d, w.scale, P, parts)
+        pkv.decode(out, self.q, self.kc, self.vc, self.tables_d, self.lens_d, w.scale, P, parts,
+                   kv_scales=(w.k_scale, w.v_scale) if self.fp8 else None)
         torch.cuda.synchronize()
         return out
 
@@ -92,12 +98,16 @@ class Layer:
         lo, hi = int(self.offsets[b]), int(self.offsets[b + 1])
         k = torch.cat([self.pk[lo:hi, g], self.nk[b:b + 1, g]]).cpu()
         v = torch.cat([self.pv[lo:hi, g], self.nv[b:b + 1, g]]).cpu()
-        return oracle.to_f64(k, self.w.dtype), oracle.to_f64(v, self.w.dtype)
+        w = self.w
+        if self.fp8:   # the values the cache holds: the oracle's codes, dequantised
+            return (oracle.to_f64(oracle.fp8_quantize(k, w.dtype, w.k_scale), "fp8") * w.k_scale,
+                    oracle.to_f64(oracle.fp8_quantize(v, w.dtype, w.v_scale), "fp8") * w.v_scale)
+        return oracle.to_f64(k, w.dtype), oracle.to_f64(v, w.dtype)
 
     def check_cache_sample(self, n=4096, seed=0):
         """Read a random sample of written tokens back through the documented layout."""
         w = self.w
-        x = 8 if w.elem_bytes == 2 else 4
+        x = 16 // w.cache_elem_bytes if self.fp8 else (8 if w.elem_bytes == 2 else 4)
         gen = np.random.default_rng(seed)
         T = len(self.prompt_slots)
         pick = gen.choice(T, size=min(n, T), replace=False) if T else np.zeros(0, np.int64)
@@ -107,13 +117,21 @@ class Layer:
         got_k = kv[blk, :, :, off, :].reshape(len(pick), w.num_kv_heads, w.head_dim)
         got_v = self.vc[blk, :, :, off]
         idx = torch.from_numpy(pick).to(self.device)
-        assert torch.equal(got_k.view(torch.int16), self.pk[idx].view(torch.int16))
-        assert torch.equal(got_v.view(torch.int16), self.pv[idx].view(torch.int16))
         nslots = torch.from_numpy(self.new_slots.astype(np.int64)).to(self.device)
         got_nk = kv[nslots // 16, :, :, nslots % 16, :].reshape(-1, w.num_kv_heads, w.head_dim)
+        got_nv = self.vc[nslots // 16, :, :, nslots % 16]
+        if self.fp8:
+            def codes(x, sc):
+                return torch.from_numpy(oracle.fp8_quantize(x.cpu(), w.dtype, sc))
+            assert torch.equal(got_k.cpu(), codes(self.pk[idx], w.k_scale))
+            assert torch.equal(got_v.cpu(), codes(self.pv[idx], w.v_scale))
+            assert torch.equal(got_nk.cpu(), codes(self.nk, w.k_scale))
+            assert torch.equal(got_nv.cpu(), codes(self.nv, w.v_scale))
+            return
+        assert torch.equal(got_k.view(torch.int16), self.pk[idx].view(torch.int16))
+        assert torch.equal(got_v.view(torch.int16), self.pv[idx].view(torch.int16))
         assert torch.equal(got_nk.view(torch.int16), self.nk.view(torch.int16))
-        assert torch.equal(self.vc[nslots // 16, :, :, nslots % 16].view(torch.int16),
-                           self.nv.view(torch.int16))
+        assert torch.equal(got_nv.view(torch.int16), self.nv.view(torch.int16))
 
     def sample_rows(self, n_random, seed=1):
         w = self.w
@@ -147,8 +165,8 @@ class Layer:
         return err
 
 
-CASES = [("llama8b", 0, 0), ("llama8b", AUTO, 0), ("llama70b", 512, 96), ("llama70b", AUTO, 96),
-         ("long", 512, 24), ("long", AUTO, 24)]
+CASES = [("llama8b", 0, 0), ("llama8b", AUTO, 0), ("llama8b_fp8", 0, 48), ("llama8b_fp8", AUTO, 48),
+         ("llama70b", 512, 96), ("llama70b", AUTO, 96), ("long", 512, 24), ("long", AUTO, 24)]
 
 
 @pytest.mark.parametrize("name,P,n_random", CASES,
