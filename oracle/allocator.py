@@ -23,8 +23,37 @@ Readings where the pages are silent:
   at the back, in the order of the freed request's table. The initial order is
   given by the caller (a random permutation scatters requests over the pool).
 * slot = physical_block * 16 + offset_in_block.
-* Sharing aliases whole blocks only (the shared token count must be a multiple
-  of 16), so a shared block is always full and is never written again.
+* share_prefix aliases whole blocks only (the shared token count must be a multiple
+  of 16), so a block shared that way is full and is never written again.
+
+Prefix caching and copy-on-write ("vLLM Nedir? ...", section "Prefix caching": every
+full 16-token block is keyed by the previous block's key, its own tokens and, for the
+first block, a cache salt; a request that brings the same chain references the cached
+physical block instead of recomputing it; only full blocks are keyed, so a prefix that
+ends inside a block leaves its last tokens to compute; a salt in the first block keeps
+tenants apart. Same page, step 5: a finished request's blocks go back to the free queue
+unless the prefix cache still holds them. "Yerel LLM ...", section "4. Prefill ve
+decode": the cache lives while memory allows and is evicted when room is needed.
+"vLLM ve Triton ...", §03, paragraph on sharing: a shared block stays a single copy
+until one of its users wants to change it, and is copied then, as copy-on-write.)
+Readings, where the pages leave steps open:
+* The key of block j is the exact content it stands for: (salt, the sequence's tokens
+  0 .. 16(j+1) - 1). A chain of the previous block's key and this block's tokens is
+  that same content. Here the key is held exactly.
+* A block is registered when it becomes full in a sequence whose every token id is
+  known (appended with append_tokens); the first block with a key keeps it (a later
+  block with the same content stays unregistered).
+* Freed blocks always go to the back of the free queue and keep their key: the free
+  queue is the eviction order. A block popped for allocation loses its key. A hit on a
+  block with no references takes it out of the free queue.
+* Lookups stop at the first miss. They cover only blocks that end before the prompt's
+  last token, so at least one prompt token is always left to compute (the step that
+  yields the first output token needs one).
+* fork(parent, child) shares every block of the parent, the partly filled last one
+  included. Appending to a partly filled block that other tables also reference first
+  moves this sequence to a fresh block: the call returns (old, new), and the caller
+  copies the old block's rows into the new one on the device (copy_blocks) before
+  writing the new tokens.
 """
 from __future__ import annotations
 
@@ -55,12 +84,62 @@ class PoolModel:
         self.ref = [0] * num_blocks
         self.seqs: dict[int, list] = {}   # seq_id -> [blocks, length]
         self.alloc_failures = 0
+        # prefix cache: key -> block and block -> key, key = (salt, tuple(prefix tokens));
+        # per sequence: its salt and token ids (None once a token id is unknown)
+        self.cache: dict[tuple, int] = {}
+        self.key_of: dict[int, tuple] = {}
+        self.salt: dict[int, int] = {}
+        self.tokens: dict[int, list | None] = {}
+        self.hits = 0                     # blocks found in the prefix cache so far
 
     # -- sequences ------------------------------------------------------------
-    def add_seq(self, sid: int) -> None:
+    def add_seq(self, sid: int, salt: int = 0) -> None:
         if sid in self.seqs:
             raise PoolError("EINVAL", f"sequence {sid} exists")
         self.seqs[sid] = [[], 0]
+        self.salt[sid] = salt
+        self.tokens[sid] = []
+
+    def _pop_free(self) -> int:
+        """Take the front of the free queue for a new use: it loses its cache key."""
+        blk = self.free.popleft()
+        key = self.key_of.pop(blk, None)
+        if key is not None:
+            del self.cache[key]
+        return blk
+
+    def add_seq_prefix(self, sid: int, prompt, salt: int = 0) -> int:
+        """New sequence whose table starts with the cached blocks of its prompt's prefix.
+        Returns the number of prompt tokens found (a multiple of 16); the caller appends
+        the rest with append_tokens."""
+        self.add_seq(sid, salt)
+        prompt = [int(t) for t in prompt]
+        blocks, n = [], 0
+        while n + BLOCK_SIZE <= len(prompt) - 1:
+            blk = self.cache.get((salt, tuple(prompt[:n + BLOCK_SIZE])))
+            if blk is None:
+                break
+            if self.ref[blk] == 0:
+                self.free.remove(blk)
+            self.ref[blk] += 1
+            blocks.append(blk)
+            n += BLOCK_SIZE
+        self.hits += len(blocks)
+        self.seqs[sid] = [blocks, n]
+        self.tokens[sid] = prompt[:n]
+        return n
+
+    def fork(self, parent: int, child: int) -> None:
+        """child shares every block of parent (partly filled last block included)."""
+        p = self._seq(parent)
+        if child in self.seqs:
+            raise PoolError("EINVAL", f"sequence {child} exists")
+        for blk in p[0]:
+            self.ref[blk] += 1
+        self.seqs[child] = [list(p[0]), p[1]]
+        self.salt[child] = self.salt[parent]
+        toks = self.tokens[parent]
+        self.tokens[child] = None if toks is None else list(toks)
 
     def _seq(self, sid: int):
         if sid not in self.seqs:
@@ -77,35 +156,73 @@ class PoolModel:
             self.ref[blk] += 1
         dst[0] = list(s[0][:nb])
         dst[1] = n_tokens
+        self.tokens[sid] = None            # shared without token ids: never keyed
 
-    def append(self, sid: int, n_tokens: int) -> list[int]:
-        """Reserve slots for n_tokens new tokens; returns their slot ids.
-        Raises ENOMEM (and changes nothing) when the free queue is too short."""
+    def _shared_tail(self, s) -> bool:
+        blocks, length = s
+        return length % BLOCK_SIZE != 0 and self.ref[blocks[-1]] > 1
+
+    def _append(self, sid: int, n_tokens: int, token_ids):
         s = self._seq(sid)
         if n_tokens < 0:
             raise PoolError("EINVAL", "negative token count")
         blocks, length = s
-        need = -(-(length + n_tokens) // BLOCK_SIZE) - len(blocks)
+        cow = n_tokens > 0 and self._shared_tail(s)
+        need = -(-(length + n_tokens) // BLOCK_SIZE) - len(blocks) + int(cow)
         if need > len(self.free):
             self.alloc_failures += 1
             raise PoolError("ENOMEM", f"need {need} blocks, {len(self.free)} free")
-        for _ in range(need):
-            blk = self.free.popleft()
+        pair = None
+        if cow:                      # copy-on-write of the shared, partly filled last block
+            new = self._pop_free()
+            self.ref[new] = 1
+            old = blocks[-1]
+            self.ref[old] -= 1       # others still reference it (ref was > 1)
+            blocks[-1] = new
+            pair = (old, new)
+        while len(blocks) * BLOCK_SIZE < length + n_tokens:
+            blk = self._pop_free()
             self.ref[blk] = 1
             blocks.append(blk)
-        slots = []
-        for pos in range(length, length + n_tokens):
-            slots.append(blocks[pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE)
+        slots = [blocks[pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE
+                 for pos in range(length, length + n_tokens)]
         s[1] = length + n_tokens
-        return slots
+        toks = self.tokens[sid]
+        if token_ids is None or toks is None:
+            self.tokens[sid] = None
+        else:
+            toks.extend(int(t) for t in token_ids)
+            for j in range(length // BLOCK_SIZE, s[1] // BLOCK_SIZE):   # blocks now full
+                key = (self.salt[sid], tuple(toks[:(j + 1) * BLOCK_SIZE]))
+                blk = blocks[j]
+                if key not in self.cache and blk not in self.key_of:
+                    self.cache[key] = blk
+                    self.key_of[blk] = key
+        return slots, pair
+
+    def append(self, sid: int, n_tokens: int) -> list[int]:
+        """Reserve slots for n_tokens new tokens whose ids are not given (the sequence's
+        later blocks are never keyed); returns their slot ids. Raises ENOMEM (and
+        changes nothing) when the free queue is too short. A shared, partly filled last
+        block needs append_tokens (copy-on-write): EINVAL."""
+        if n_tokens > 0 and self._shared_tail(self._seq(sid)):
+            raise PoolError("EINVAL", "shared partly filled block: use append_tokens")
+        return self._append(sid, n_tokens, None)[0]
+
+    def append_tokens(self, sid: int, token_ids):
+        """append for tokens with known ids: returns (slots, copy) where copy is
+        (old_block, new_block) when the shared last block was copied, else None."""
+        token_ids = [int(t) for t in token_ids]
+        return self._append(sid, len(token_ids), token_ids)
 
     def free_seq(self, sid: int) -> None:
         blocks, _ = self._seq(sid)
         for blk in blocks:
             self.ref[blk] -= 1
             if self.ref[blk] == 0:
-                self.free.append(blk)
+                self.free.append(blk)      # keeps its key until popped again
         del self.seqs[sid]
+        del self.salt[sid], self.tokens[sid]
 
     # -- views ------------------------------------------------------------------
     def seq_len(self, sid: int) -> int:
@@ -131,7 +248,8 @@ class PoolModel:
         shared = sum(1 for r in self.ref if r > 1)
         return {"total": self.num_blocks, "free": len(self.free), "used": used,
                 "shared": shared, "alloc_failures": self.alloc_failures,
-                "num_seqs": len(self.seqs)}
+                "num_seqs": len(self.seqs), "cached": len(self.cache),
+                "prefix_hits": self.hits}
 
 
 def bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
