@@ -87,7 +87,8 @@ const char* pkv_version(void);
 #define PKV_TIMER_DECODE 0
 #define PKV_TIMER_REDUCE 1
 #define PKV_TIMER_CACHE_WRITE 2
-#define PKV_TIMER_ENTRIES 3
+#define PKV_TIMER_COPY_BLOCKS 3
+#define PKV_TIMER_ENTRIES 4
 int pkv_timer_enable(int32_t enable);
 int pkv_timer_read(int32_t entry, double* total_ms, int64_t* launches);
 
@@ -112,6 +113,8 @@ typedef struct {
     int64_t shared_blocks;  /* blocks with reference count >= 2              */
     int64_t alloc_failures; /* appends refused with PKV_ENOMEM so far         */
     int64_t num_seqs;       /* live sequences                                 */
+    int64_t cached_blocks;  /* blocks holding a prefix-cache key              */
+    int64_t prefix_hit_blocks; /* blocks found by kv_pool_add_seq_prefix so far */
 } kv_pool_stats_t;
 
 /* Create a pool of num_blocks physical blocks of block_size (must be 16) tokens for
@@ -148,6 +151,57 @@ int kv_pool_add_seq(kv_pool* pool, int64_t seq_id);
  * Errors: ENOENT (unknown id), EINVAL (seq not empty, n_tokens not allowed). */
 int kv_pool_share_prefix(kv_pool* pool, int64_t seq_id, int64_t src_seq_id, int32_t n_tokens);
 
+/* ---- prefix caching and copy-on-write ----------------------------------------------
+ * ("vLLM Nedir? ...", section "Prefix caching"; "vLLM ve Triton ...", §03 on sharing;
+ * "Yerel LLM ...", section "4. Prefill ve decode", on eviction.)
+ * Every full block of a sequence whose token ids are all known (kv_pool_add_seq_prefix,
+ * kv_pool_append_tokens, kv_pool_append_batch_tokens; kv_pool_add_seq counts as an empty
+ * prompt with salt 0) gets a key: a 64-bit hash chain over the salt and the token ids of
+ * the blocks up to it, with the block's own 16 ids and its parent's chain hash kept to
+ * check a hit. Only the first block with a given key holds it. A block freed to the free
+ * queue keeps its key until it is popped for a new use (the free queue is the eviction
+ * order); a hit on a free block takes it out of the queue. kv_pool_append,
+ * kv_pool_append_batch and kv_pool_share_prefix give tokens without ids: that sequence's
+ * later blocks get no key. */
+
+/* Register seq_id with the longest run of cached blocks that starts its prompt: block j
+ * (tokens 16j .. 16j + 15) is looked up while it ends before the prompt's last token, so
+ * at least one prompt token is always left to compute; the walk stops at the first miss.
+ * *n_cached_out = 16 x the blocks found (their reference counts + 1). The caller then
+ * appends prompt[*n_cached_out ..] with kv_pool_append_tokens and writes only their K/V.
+ * salt: blocks are found only under the salt they were stored with (tenant isolation).
+ * Errors: EINVAL (seq_id live, n_prompt < 0, NULLs). */
+int kv_pool_add_seq_prefix(kv_pool* pool, int64_t seq_id, const int32_t* prompt,
+                           int32_t n_prompt, uint64_t salt, int32_t* n_cached_out);
+
+/* child_id (new) shares every block of parent_id, the partly filled last block included
+ * (reference counts + 1): parallel sampling and beam search branches. The first append
+ * to a shared, partly filled block copies it (copy-on-write, see below).
+ * Errors: ENOENT (parent), EINVAL (child live). */
+int kv_pool_fork(kv_pool* pool, int64_t parent_id, int64_t child_id);
+
+/* kv_pool_append for tokens with known ids (tokens[0 .. n_tokens)). If the sequence's
+ * last block is partly filled and referenced by other tables too, the sequence first
+ * moves to a fresh block: copy_out[0] = the old block, copy_out[1] = the new one, and the
+ * caller must copy the old block's rows into the new one in every layer (copy_blocks)
+ * before writing the new tokens' K/V; otherwise copy_out = {-1, -1}. Full blocks are
+ * keyed as described above. ENOMEM (nothing changed) counts the copy's block too.
+ * Errors: ENOENT, EINVAL (NULLs, n_tokens < 0), ENOMEM. */
+int kv_pool_append_tokens(kv_pool* pool, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                          int32_t* slot_mapping_out, int32_t* copy_out);
+
+/* The decode step with token ids: one token (tokens[i]) for each of the n distinct
+ * sequences; slot_mapping_out[i] as kv_pool_append_batch. The copies that copy-on-write
+ * needs are listed in copies_out[0 .. 2 * *n_copies_out) as (old, new) pairs (at most
+ * n). Sequences are served in the order given: when every table that shares a partly
+ * filled block writes to it in this step, the last of them writes in place and only the
+ * others copy it. All or nothing: ENOMEM (exactly when the free queue is shorter than
+ * the blocks the step takes) leaves every sequence unchanged.
+ * Errors: ENOENT, EINVAL (duplicates, NULLs), ENOMEM. */
+int kv_pool_append_batch_tokens(kv_pool* pool, const int64_t* seq_ids, const int32_t* tokens,
+                                int32_t n, int32_t* slot_mapping_out, int32_t* copies_out,
+                                int32_t* n_copies_out);
+
 /* allocate_slots: reserve n_tokens new positions at the end of seq_id and write
  * their slot ids to slot_mapping_out[0..n_tokens). A new physical block is popped
  * from the front of the free queue only when the sequence's last block is full
@@ -159,7 +213,9 @@ int kv_pool_append(kv_pool* pool, int64_t seq_id, int32_t n_tokens, int32_t* slo
 
 /* Decode step: one new position for each of the n distinct sequences in seq_ids;
  * slot_mapping_out[i] is the slot of seq_ids[i]. All or nothing: ENOMEM leaves
- * every sequence unchanged. Errors: ENOENT, EINVAL (duplicate ids, nulls). */
+ * every sequence unchanged. kv_pool_append and this call refuse (EINVAL) a sequence
+ * whose last block is shared and partly filled: the *_tokens calls copy it.
+ * Errors: ENOENT, EINVAL (duplicate ids, nulls). */
 int kv_pool_append_batch(kv_pool* pool, const int64_t* seq_ids, int32_t n,
                          int32_t* slot_mapping_out);
 
@@ -319,6 +375,19 @@ int paged_attention_reduce(void* out, const float* part_out, const float* part_m
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t max_blocks_per_seq, int32_t partition_size,
                            int32_t max_partitions, int32_t out_dtype, void* stream);
+
+/* copy_blocks: the device half of copy-on-write. For each pair p < n_pairs,
+ * (src, dst) = (pairs[2p], pairs[2p + 1]), copy block src onto block dst in the K and
+ * the V cache of every layer: block_bytes bytes each, the whole block (the rows past
+ * the sequence's length are rewritten before they are read). Pairs with an id outside
+ * [0, num_blocks) or src == dst are skipped; two pairs must not share a dst.
+ *   k_caches, v_caches: host arrays of num_layers device pointers (16-byte aligned).
+ *   pairs: device int32 [n_pairs][2] (kv_pool_append_tokens / _batch_tokens output).
+ *   block_bytes: num_kv_heads * 16 * head_dim * element bytes (a multiple of 16).
+ * Errors: EINVAL (NULLs, alignment, num_layers outside 1..256, block_bytes), EHIP. */
+int copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                const int32_t* pairs, int32_t n_pairs, int64_t block_bytes, int64_t num_blocks,
+                void* stream);
 
 /* ==== FP8 KV cache ================================================================
  * Storing K and V in FP8 halves the bytes per token, so the same memory holds about

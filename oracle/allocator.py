@@ -215,6 +215,32 @@ class PoolModel:
         token_ids = [int(t) for t in token_ids]
         return self._append(sid, len(token_ids), token_ids)
 
+    def append_batch_tokens(self, sids, token_ids):
+        """The decode step with token ids: one token per distinct sequence, all or
+        nothing. Returns (slots, copies) with the (old, new) copies in batch order."""
+        sids = [int(x) for x in sids]
+        if len(set(sids)) != len(sids):
+            raise PoolError("EINVAL", "duplicate sequence")
+        ref = list(self.ref)          # a dry run in batch order counts the blocks needed
+        need = 0
+        for sid in sids:
+            blocks, length = self._seq(sid)
+            if length % BLOCK_SIZE == 0:
+                need += 1
+            elif ref[blocks[-1]] > 1:
+                ref[blocks[-1]] -= 1
+                need += 1
+        if need > len(self.free):
+            self.alloc_failures += 1
+            raise PoolError("ENOMEM", f"need {need} blocks, {len(self.free)} free")
+        slots, copies = [], []
+        for sid, t in zip(sids, token_ids):
+            sl, cp = self.append_tokens(sid, [t])
+            slots += sl
+            if cp is not None:
+                copies.append(cp)
+        return slots, copies
+
     def free_seq(self, sid: int) -> None:
         blocks, _ = self._seq(sid)
         for blk in blocks:

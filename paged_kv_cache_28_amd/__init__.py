@@ -43,7 +43,8 @@ class PkvError(RuntimeError):
 
 class _Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("total_blocks", "free_blocks", "used_blocks",
-                                              "shared_blocks", "alloc_failures", "num_seqs")]
+                                              "shared_blocks", "alloc_failures", "num_seqs",
+                                              "cached_blocks", "prefix_hit_blocks")]
 
 
 def lib():
@@ -55,6 +56,7 @@ def lib():
         raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    U64 = ctypes.c_uint64
     PP = ctypes.POINTER(ctypes.c_void_p)
     sig = {
         "pkv_last_error": ([], ctypes.c_char_p),
@@ -75,6 +77,11 @@ def lib():
         "kv_pool_refcount": ([P, I64, P], ctypes.c_int),
         "kv_pool_build_tables": ([P, P, I32, I32, P, P], ctypes.c_int),
         "kv_pool_stats": ([P, P], ctypes.c_int),
+        "kv_pool_add_seq_prefix": ([P, I64, P, I32, U64, P], ctypes.c_int),
+        "kv_pool_fork": ([P, I64, I64], ctypes.c_int),
+        "kv_pool_append_tokens": ([P, I64, P, I32, P, P], ctypes.c_int),
+        "kv_pool_append_batch_tokens": ([P, P, P, I32, P, P, P], ctypes.c_int),
+        "copy_blocks": ([P, P, I32, P, I32, I64, I64, P], ctypes.c_int),
         "reshape_and_cache": ([P, P, P, P, P, I32, I32, I32, I32, I64, I64, I64, I32, P],
                               ctypes.c_int),
         "paged_attention_decode": ([P, P, P, P, P, I64, P, P, P, P, I32, I32, I32, I32, I32, I32,
@@ -109,7 +116,9 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "kv_pool_refcount", "kv_pool_build_tables", "kv_pool_stats", "reshape_and_cache",
             "paged_attention_decode", "paged_attention_reduce", "paged_attention_decode_append",
             "reshape_and_cache_fp8", "paged_attention_decode_fp8",
-            "paged_attention_decode_append_fp8", "pkv_timer_enable", "pkv_timer_read")
+            "paged_attention_decode_append_fp8", "pkv_timer_enable", "pkv_timer_read",
+            "kv_pool_add_seq_prefix", "kv_pool_fork", "kv_pool_append_tokens",
+            "kv_pool_append_batch_tokens", "copy_blocks")
 
 
 def _check(rc: int):
@@ -250,6 +259,47 @@ class KVPool:
                                           len(ids), slots.ctypes.data_as(ctypes.c_void_p)))
         return slots
 
+    def add_seq_prefix(self, seq_id: int, prompt, salt: int = 0) -> int:
+        """Register seq_id starting with the cached blocks of its prompt; returns the
+        number of prompt tokens found (append the rest with append_tokens)."""
+        np = self._np
+        p = np.ascontiguousarray(prompt, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().kv_pool_add_seq_prefix(self._h, seq_id, p.ctypes.data_as(ctypes.c_void_p),
+                                            len(p), ctypes.c_uint64(salt & (2 ** 64 - 1)),
+                                            ctypes.byref(n)))
+        return n.value
+
+    def fork(self, parent_id: int, child_id: int):
+        _check(lib().kv_pool_fork(self._h, parent_id, child_id))
+
+    def append_tokens(self, seq_id: int, tokens):
+        """append for tokens with known ids: (int32 slots, (old, new) block copy or None)."""
+        np = self._np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(len(t), dtype=np.int32)
+        cp = np.empty(2, dtype=np.int32)
+        _check(lib().kv_pool_append_tokens(self._h, seq_id, t.ctypes.data_as(ctypes.c_void_p),
+                                           len(t), slots.ctypes.data_as(ctypes.c_void_p),
+                                           cp.ctypes.data_as(ctypes.c_void_p)))
+        return slots, (None if cp[0] < 0 else (int(cp[0]), int(cp[1])))
+
+    def append_batch_tokens(self, seq_ids, tokens, out=None):
+        """Decode step with token ids: (int32 slots, int32 [k][2] block copies)."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        if t.shape != ids.shape:
+            raise ValueError("one token per sequence")
+        slots = np.empty(len(ids), dtype=np.int32) if out is None else out
+        copies = np.empty((max(len(ids), 1), 2), dtype=np.int32)
+        nc = ctypes.c_int32()
+        _check(lib().kv_pool_append_batch_tokens(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), t.ctypes.data_as(ctypes.c_void_p),
+            len(ids), slots.ctypes.data_as(ctypes.c_void_p),
+            copies.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nc)))
+        return slots, copies[:nc.value]
+
     def free_seq(self, seq_id: int):
         _check(lib().kv_pool_free_seq(self._h, seq_id))
 
@@ -297,7 +347,8 @@ class KVPool:
         _check(lib().kv_pool_stats(self._h, ctypes.byref(s)))
         return {"total": s.total_blocks, "free": s.free_blocks, "used": s.used_blocks,
                 "shared": s.shared_blocks, "alloc_failures": s.alloc_failures,
-                "num_seqs": s.num_seqs}
+                "num_seqs": s.num_seqs, "cached": s.cached_blocks,
+                "prefix_hits": s.prefix_hit_blocks}
 
 
 def kv_pool_create(num_blocks, num_layers, num_kv_heads, head_dim, dtype, free_order=None,
@@ -463,6 +514,24 @@ def paged_attention_decode_append_fp8(out, q, key, value, slot_mapping, k_cache,
         max_partitions, dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
 
 
+def copy_blocks(k_caches, v_caches, pairs, stream=None):
+    """Copy-on-write on the device: for each (src, dst) row of pairs (device int32
+    [n][2]), block src onto block dst in every layer's K and V cache (lists of tensors)."""
+    L = len(k_caches)
+    if L != len(v_caches) or L == 0:
+        raise ValueError("one K and one V cache per layer")
+    for t in list(k_caches) + list(v_caches):
+        if not t.is_contiguous() or t.shape[0] != k_caches[0].shape[0]:
+            raise ValueError("caches must be contiguous with the same number of blocks")
+    if pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+        raise ValueError("pairs must be a contiguous [n][2] int32 tensor")
+    kp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in k_caches])
+    vp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in v_caches])
+    block_bytes = k_caches[0][0].numel() * k_caches[0].element_size()
+    _check(lib().copy_blocks(kp, vp, L, _dev(pairs, "pairs"), pairs.shape[0], block_bytes,
+                             k_caches[0].shape[0], _stream(pairs, stream)))
+
+
 def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partition_size: int,
                            num_kv_heads: int, max_blocks_per_seq: int, stream=None):
     B, Hq, d = out.shape
@@ -474,7 +543,7 @@ def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partitio
 
 
 # ------------------------------------------------------------------ kernel timer
-PKV_TIMER_DECODE, PKV_TIMER_REDUCE, PKV_TIMER_CACHE_WRITE = 0, 1, 2
+PKV_TIMER_DECODE, PKV_TIMER_REDUCE, PKV_TIMER_CACHE_WRITE, PKV_TIMER_COPY_BLOCKS = 0, 1, 2, 3
 
 
 def timer_enable(on: bool = True):

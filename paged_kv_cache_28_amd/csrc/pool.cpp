@@ -9,9 +9,19 @@
 // to the free queue; a request is dropped and its blocks returned when the pool is
 // short, so a refused allocation must change nothing).
 //
-// The free queue is a ring buffer over num_blocks entries (a block is either queued
-// or referenced, never both, so the ring never overflows). Sequences live in a hash
-// map keyed by the caller's 64-bit id.
+// Prefix caching and copy-on-write ("vLLM Nedir? ...", section "Prefix caching": full
+// 16-token blocks are keyed by a chain of the previous block's key, the block's tokens
+// and, for the first block, a salt; a request bringing the same chain references the
+// cached block; "vLLM ve Triton ...", §03 on sharing: a shared block is copied when one
+// of its users writes to it). Keys here: a 64-bit hash chain h_j = mix(h_{j-1}, tokens of
+// block j) from h_{-1} = root(salt). A hit is checked against the block's own 16 token
+// ids and its parent's chain hash, so a false hit needs two different prefixes with one
+// 64-bit chain hash. A block is keyed when it fills in a sequence whose token ids are all
+// known; freed blocks keep their key in the free queue, which is the eviction order, and
+// lose it when popped for a new use.
+//
+// The free queue is a doubly linked list over the block ids (a prefix hit takes a block
+// out of its middle). Sequences live in a hash map keyed by the caller's 64-bit id.
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -32,31 +42,100 @@ std::string& last_error() {
 using pkv::fail;
 using pkv::ok;
 
+namespace {
+// splitmix64's output function (Steele, Lea, Flood, "Fast splittable pseudorandom number
+// generators", 2014): a bijection of 64-bit words with full avalanche.
+inline uint64_t mix64(uint64_t x) {
+    x ^= x >> 30;
+    x *= 0xbf58476d1ce4e5b9ull;
+    x ^= x >> 27;
+    x *= 0x94d049bb133111ebull;
+    return x ^ (x >> 31);
+}
+inline uint64_t chain_root(uint64_t salt) { return mix64(salt ^ 0x9e3779b97f4a7c15ull); }
+inline uint64_t chain_next(uint64_t parent, const int32_t* tok) {
+    uint64_t h = parent;
+    for (int k = 0; k < PKV_BLOCK_SIZE; ++k) h = mix64(h ^ uint64_t(uint32_t(tok[k])));
+    return h;
+}
+}  // namespace
+
 struct kv_pool {
     int64_t num_blocks = 0;
     int32_t num_layers = 0, num_kv_heads = 0, head_dim = 0, dtype = 0;
-    // FIFO free queue as a ring: entries [head, head + count) mod num_blocks
-    std::vector<int32_t> ring;
-    int64_t head = 0, count = 0;
+    // FIFO free queue as a doubly linked list over block ids (-1 ends)
+    std::vector<int32_t> nxt, prv;
+    std::vector<char> queued;
+    int32_t fhead = -1, ftail = -1;
+    int64_t count = 0;
     std::vector<int32_t> ref;
+    // prefix cache: chain hash -> block; per block its key, parent hash and 16 token ids
+    std::unordered_map<uint64_t, int32_t> cache;
+    std::vector<char> keyed;
+    std::vector<uint64_t> key, key_parent;
+    std::vector<int32_t> key_tokens;   // [num_blocks][16]
+    int64_t prefix_hits = 0;
     struct Seq {
         std::vector<int32_t> blocks;
         int64_t len = 0;
+        uint64_t salt = 0;
+        bool hashable = true;           // every token id known: full blocks get keys
+        std::vector<uint64_t> chain;    // chain hash of each full block (hashable only)
+        std::vector<int32_t> tail;      // token ids of the partly filled last block
     };
     std::unordered_map<int64_t, Seq> seqs;
     int64_t alloc_failures = 0;
 
-    int32_t pop_front() {
-        int32_t b = ring[head];
-        head = head + 1 == num_blocks ? 0 : head + 1;
+    void unlink(int32_t b) {
+        const int32_t p = prv[b], n = nxt[b];
+        (p >= 0 ? nxt[p] : fhead) = n;
+        (n >= 0 ? prv[n] : ftail) = p;
+        prv[b] = nxt[b] = -1;
+        queued[b] = 0;
         --count;
+    }
+    // a block for a new use: the front of the free queue, which loses its cache key
+    int32_t pop_front() {
+        const int32_t b = fhead;
+        unlink(b);
+        if (keyed[b]) {
+            cache.erase(key[b]);
+            keyed[b] = 0;
+        }
         return b;
     }
     void push_back(int32_t b) {
-        int64_t tail = head + count;
-        if (tail >= num_blocks) tail -= num_blocks;
-        ring[tail] = b;
+        prv[b] = ftail;
+        nxt[b] = -1;
+        (ftail >= 0 ? nxt[ftail] : fhead) = b;
+        ftail = b;
+        queued[b] = 1;
         ++count;
+    }
+    // key block b (now full in s, as its block j) unless the key is taken already
+    void register_full(Seq& s, int64_t j, const int32_t* tok) {
+        const uint64_t parent = j == 0 ? chain_root(s.salt) : s.chain[size_t(j - 1)];
+        const uint64_t h = chain_next(parent, tok);
+        s.chain.push_back(h);
+        const int32_t b = s.blocks[size_t(j)];
+        if (keyed[b] || cache.count(h)) return;
+        cache.emplace(h, b);
+        keyed[b] = 1;
+        key[b] = h;
+        key_parent[b] = parent;
+        std::memcpy(&key_tokens[size_t(b) * PKV_BLOCK_SIZE], tok, sizeof(int32_t) * PKV_BLOCK_SIZE);
+    }
+    // the cached block for (parent hash, 16 tokens), or -1
+    int32_t lookup(uint64_t parent, const int32_t* tok, uint64_t* h_out) const {
+        const uint64_t h = chain_next(parent, tok);
+        auto it = cache.find(h);
+        if (it == cache.end()) return -1;
+        const int32_t b = it->second;
+        if (key_parent[b] != parent ||
+            std::memcmp(&key_tokens[size_t(b) * PKV_BLOCK_SIZE], tok, sizeof(int32_t) * PKV_BLOCK_SIZE))
+            return -1;
+        *h_out = h;
+        return b;
     }
     Seq* find(int64_t id) {
         auto it = seqs.find(id);
@@ -106,8 +185,14 @@ int kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t num_layers,
     p->num_kv_heads = num_kv_heads;
     p->head_dim = head_dim;
     p->dtype = dtype;
-    p->ring.resize(num_blocks);
+    p->nxt.assign(num_blocks, -1);
+    p->prv.assign(num_blocks, -1);
+    p->queued.assign(num_blocks, 0);
     p->ref.assign(num_blocks, 0);
+    p->keyed.assign(num_blocks, 0);
+    p->key.assign(num_blocks, 0);
+    p->key_parent.assign(num_blocks, 0);
+    p->key_tokens.assign(size_t(num_blocks) * PKV_BLOCK_SIZE, 0);
     if (free_order) {
         std::vector<char> seen(num_blocks, 0);
         for (int64_t i = 0; i < num_blocks; ++i) {
@@ -117,13 +202,11 @@ int kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t num_layers,
                 return fail(PKV_EINVAL, "kv_pool_create: free_order is not a permutation");
             }
             seen[b] = 1;
-            p->ring[i] = b;
         }
+        for (int64_t i = 0; i < num_blocks; ++i) p->push_back(free_order[i]);
     } else {
-        for (int64_t i = 0; i < num_blocks; ++i) p->ring[i] = int32_t(i);
+        for (int64_t i = 0; i < num_blocks; ++i) p->push_back(int32_t(i));
     }
-    p->head = 0;
-    p->count = num_blocks;
     *out = p;
     return ok();
 }
@@ -176,18 +259,77 @@ int kv_pool_share_prefix(kv_pool* pool, int64_t seq_id, int64_t src_seq_id, int3
     dst->blocks.assign(src->blocks.begin(), src->blocks.begin() + nb);
     for (int32_t b : dst->blocks) ++pool->ref[b];
     dst->len = n_tokens;
+    dst->hashable = false;   // shared without token ids: its blocks get no keys
     return ok();
 }
 
-static int append_one_seq(kv_pool* pool, kv_pool::Seq* s, int32_t n_tokens, int32_t* slots) {
-    int64_t need = kv_pool::blocks_for(s->len + n_tokens) - int64_t(s->blocks.size());
-    if (need > pool->count) {
-        ++pool->alloc_failures;
-        return fail(PKV_ENOMEM, "kv_pool_append: need %lld blocks, %lld free", (long long)need,
-                    (long long)pool->count);
+int kv_pool_add_seq_prefix(kv_pool* pool, int64_t seq_id, const int32_t* prompt,
+                           int32_t n_prompt, uint64_t salt, int32_t* n_cached_out) {
+    if (!pool || !n_cached_out) return fail(PKV_EINVAL, "kv_pool_add_seq_prefix: NULL");
+    if (n_prompt < 0 || (n_prompt > 0 && !prompt))
+        return fail(PKV_EINVAL, "kv_pool_add_seq_prefix: bad prompt");
+    if (pool->find(seq_id))
+        return fail(PKV_EINVAL, "kv_pool_add_seq_prefix: sequence %lld exists", (long long)seq_id);
+    kv_pool::Seq s;
+    s.salt = salt;
+    uint64_t h = chain_root(salt);
+    int64_t n = 0;
+    while (n + PKV_BLOCK_SIZE <= int64_t(n_prompt) - 1) {
+        uint64_t hn = 0;
+        const int32_t b = pool->lookup(h, prompt + n, &hn);
+        if (b < 0) break;
+        if (pool->queued[b]) pool->unlink(b);
+        ++pool->ref[b];
+        s.blocks.push_back(b);
+        s.chain.push_back(hn);
+        h = hn;
+        n += PKV_BLOCK_SIZE;
     }
-    for (int64_t k = 0; k < need; ++k) {
-        int32_t b = pool->pop_front();
+    pool->prefix_hits += int64_t(s.blocks.size());
+    s.len = n;
+    pool->seqs.emplace(seq_id, std::move(s));
+    *n_cached_out = int32_t(n);
+    return ok();
+}
+
+int kv_pool_fork(kv_pool* pool, int64_t parent_id, int64_t child_id) {
+    if (!pool) return fail(PKV_EINVAL, "kv_pool_fork: pool is NULL");
+    const kv_pool::Seq* p = pool->find(parent_id);
+    if (!p) return fail(PKV_ENOENT, "kv_pool_fork: unknown sequence %lld", (long long)parent_id);
+    if (pool->find(child_id))
+        return fail(PKV_EINVAL, "kv_pool_fork: sequence %lld exists", (long long)child_id);
+    kv_pool::Seq c = *p;
+    for (int32_t b : c.blocks) ++pool->ref[b];
+    pool->seqs.emplace(child_id, std::move(c));
+    return ok();
+}
+
+// Does appending to s first need a copy of its last block (partly filled and shared)?
+static bool needs_copy(const kv_pool* pool, const kv_pool::Seq* s) {
+    return s->len % PKV_BLOCK_SIZE != 0 && pool->ref[s->blocks.back()] > 1;
+}
+
+static int64_t blocks_needed(const kv_pool* pool, const kv_pool::Seq* s, int64_t n_tokens) {
+    return kv_pool::blocks_for(s->len + n_tokens) - int64_t(s->blocks.size()) +
+           (n_tokens > 0 && needs_copy(pool, s) ? 1 : 0);
+}
+
+// Append n_tokens (token ids in `tokens`, or NULL when unknown) after the caller checked
+// that the free queue holds blocks_needed(). copy[0..1] gets (old, new) when the shared
+// last block was copied, else (-1, -1).
+static void append_one_seq(kv_pool* pool, kv_pool::Seq* s, int32_t n_tokens,
+                           const int32_t* tokens, int32_t* slots, int32_t* copy) {
+    copy[0] = copy[1] = -1;
+    if (n_tokens > 0 && needs_copy(pool, s)) {
+        const int32_t nb = pool->pop_front();
+        pool->ref[nb] = 1;
+        copy[0] = s->blocks.back();
+        copy[1] = nb;
+        --pool->ref[copy[0]];   // still referenced by the others
+        s->blocks.back() = nb;
+    }
+    while (int64_t(s->blocks.size()) * PKV_BLOCK_SIZE < s->len + n_tokens) {
+        const int32_t b = pool->pop_front();
         pool->ref[b] = 1;
         s->blocks.push_back(b);
     }
@@ -195,7 +337,34 @@ static int append_one_seq(kv_pool* pool, kv_pool::Seq* s, int32_t n_tokens, int3
         int64_t pos = s->len + k;
         slots[k] = s->blocks[pos / PKV_BLOCK_SIZE] * PKV_BLOCK_SIZE + int32_t(pos % PKV_BLOCK_SIZE);
     }
+    if (!tokens) {
+        s->hashable = false;
+        s->tail.clear();
+    } else if (s->hashable) {
+        for (int32_t k = 0; k < n_tokens; ++k) {
+            s->tail.push_back(tokens[k]);
+            if (s->tail.size() == PKV_BLOCK_SIZE) {   // block (len + k) / 16 is now full
+                pool->register_full(*s, (s->len + k) / PKV_BLOCK_SIZE, s->tail.data());
+                s->tail.clear();
+            }
+        }
+    }
     s->len += n_tokens;
+}
+
+static int append_checked(kv_pool* pool, const char* who, kv_pool::Seq* s, int32_t n_tokens,
+                          const int32_t* tokens, int32_t* slots, int32_t* copy) {
+    if (!tokens && n_tokens > 0 && needs_copy(pool, s))
+        return fail(PKV_EINVAL, "%s: the last block is shared and partly filled; "
+                                "kv_pool_append_tokens copies it", who);
+    int64_t need = blocks_needed(pool, s, n_tokens);
+    if (need > pool->count) {
+        ++pool->alloc_failures;
+        return fail(PKV_ENOMEM, "%s: need %lld blocks, %lld free", who, (long long)need,
+                    (long long)pool->count);
+    }
+    int32_t unused[2];
+    append_one_seq(pool, s, n_tokens, tokens, slots, copy ? copy : unused);
     return PKV_OK;
 }
 
@@ -210,7 +379,25 @@ int kv_pool_append(kv_pool* pool, int64_t seq_id, int32_t n_tokens, int32_t* slo
         ++pool->alloc_failures;
         return fail(PKV_ENOMEM, "kv_pool_append: sequence longer than the whole pool");
     }
-    int rc = append_one_seq(pool, s, n_tokens, slot_mapping_out);
+    int rc = append_checked(pool, "kv_pool_append", s, n_tokens, nullptr, slot_mapping_out, nullptr);
+    return rc == PKV_OK ? ok() : rc;
+}
+
+int kv_pool_append_tokens(kv_pool* pool, int64_t seq_id, const int32_t* tokens, int32_t n_tokens,
+                          int32_t* slot_mapping_out, int32_t* copy_out) {
+    if (!pool) return fail(PKV_EINVAL, "kv_pool_append_tokens: pool is NULL");
+    if (n_tokens < 0) return fail(PKV_EINVAL, "kv_pool_append_tokens: negative n_tokens");
+    if (!copy_out || (n_tokens > 0 && (!slot_mapping_out || !tokens)))
+        return fail(PKV_EINVAL, "kv_pool_append_tokens: NULL argument");
+    kv_pool::Seq* s = pool->find(seq_id);
+    if (!s) return fail(PKV_ENOENT, "kv_pool_append_tokens: unknown sequence %lld",
+                        (long long)seq_id);
+    if (s->len + n_tokens > int64_t(pool->num_blocks) * PKV_BLOCK_SIZE) {
+        ++pool->alloc_failures;
+        return fail(PKV_ENOMEM, "kv_pool_append_tokens: sequence longer than the whole pool");
+    }
+    int rc = append_checked(pool, "kv_pool_append_tokens", s, n_tokens, tokens, slot_mapping_out,
+                            copy_out);
     return rc == PKV_OK ? ok() : rc;
 }
 
@@ -231,14 +418,75 @@ int kv_pool_append_batch(kv_pool* pool, const int64_t* seq_ids, int32_t n,
         if (!seen.insert(seq_ids[i]).second)
             return fail(PKV_EINVAL, "kv_pool_append_batch: duplicate sequence %lld",
                         (long long)seq_ids[i]);
-        need += kv_pool::blocks_for(seqs[i]->len + 1) - int64_t(seqs[i]->blocks.size());
+        if (needs_copy(pool, seqs[i]))
+            return fail(PKV_EINVAL, "kv_pool_append_batch: sequence %lld shares its partly "
+                                    "filled last block; kv_pool_append_batch_tokens copies it",
+                        (long long)seq_ids[i]);
+        need += blocks_needed(pool, seqs[i], 1);
     }
     if (need > pool->count) {
         ++pool->alloc_failures;
         return fail(PKV_ENOMEM, "kv_pool_append_batch: need %lld blocks, %lld free",
                     (long long)need, (long long)pool->count);
     }
-    for (int32_t i = 0; i < n; ++i) append_one_seq(pool, seqs[i], 1, slot_mapping_out + i);
+    int32_t unused[2];
+    for (int32_t i = 0; i < n; ++i)
+        append_one_seq(pool, seqs[i], 1, nullptr, slot_mapping_out + i, unused);
+    return ok();
+}
+
+int kv_pool_append_batch_tokens(kv_pool* pool, const int64_t* seq_ids, const int32_t* tokens,
+                                int32_t n, int32_t* slot_mapping_out, int32_t* copies_out,
+                                int32_t* n_copies_out) {
+    if (!pool) return fail(PKV_EINVAL, "kv_pool_append_batch_tokens: pool is NULL");
+    if (n < 0 || !n_copies_out) return fail(PKV_EINVAL, "kv_pool_append_batch_tokens: bad n");
+    *n_copies_out = 0;
+    if (n == 0) return ok();
+    if (!seq_ids || !tokens || !slot_mapping_out || !copies_out)
+        return fail(PKV_EINVAL, "kv_pool_append_batch_tokens: NULL");
+    std::vector<kv_pool::Seq*> seqs(n);
+    std::unordered_set<int64_t> seen;
+    seen.reserve(size_t(n) * 2);
+    // Blocks the step needs, counted in batch order: when every table sharing a partly
+    // filled block writes to it in this step, the last of them finds it unshared and
+    // writes in place, so only the others copy it.
+    std::unordered_map<int32_t, int32_t> copied;   // shared tail block -> copies so far
+    int64_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        seqs[i] = pool->find(seq_ids[i]);
+        if (!seqs[i]) return fail(PKV_ENOENT, "kv_pool_append_batch_tokens: unknown sequence %lld",
+                                  (long long)seq_ids[i]);
+        if (!seen.insert(seq_ids[i]).second)
+            return fail(PKV_EINVAL, "kv_pool_append_batch_tokens: duplicate sequence %lld",
+                        (long long)seq_ids[i]);
+        const kv_pool::Seq* sq = seqs[i];
+        if (sq->len % PKV_BLOCK_SIZE == 0) {
+            ++need;                                  // a fresh block for the token
+        } else {
+            const int32_t tb = sq->blocks.back();
+            int32_t& c = copied[tb];
+            if (pool->ref[tb] - c > 1) {             // still shared when its turn comes
+                ++c;
+                ++need;
+            }
+        }
+    }
+    if (need > pool->count) {
+        ++pool->alloc_failures;
+        return fail(PKV_ENOMEM, "kv_pool_append_batch_tokens: need %lld blocks, %lld free",
+                    (long long)need, (long long)pool->count);
+    }
+    int32_t nc = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t copy[2];
+        append_one_seq(pool, seqs[i], 1, tokens + i, slot_mapping_out + i, copy);
+        if (copy[0] >= 0) {
+            copies_out[2 * nc] = copy[0];
+            copies_out[2 * nc + 1] = copy[1];
+            ++nc;
+        }
+    }
+    *n_copies_out = nc;
     return ok();
 }
 
@@ -282,11 +530,8 @@ int kv_pool_free_queue(const kv_pool* pool, int32_t* blocks_out, int64_t capacit
     *n_out = pool->count;
     if (pool->count > capacity || (pool->count > 0 && !blocks_out))
         return fail(PKV_EINVAL, "kv_pool_free_queue: capacity too small");
-    for (int64_t k = 0; k < pool->count; ++k) {
-        int64_t idx = pool->head + k;
-        if (idx >= pool->num_blocks) idx -= pool->num_blocks;
-        blocks_out[k] = pool->ring[idx];
-    }
+    int64_t k = 0;
+    for (int32_t b = pool->fhead; b >= 0; b = pool->nxt[b]) blocks_out[k++] = b;
     return ok();
 }
 
@@ -334,6 +579,8 @@ int kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out) {
     out->shared_blocks = shared;
     out->alloc_failures = pool->alloc_failures;
     out->num_seqs = int64_t(pool->seqs.size());
+    out->cached_blocks = int64_t(pool->cache.size());
+    out->prefix_hit_blocks = pool->prefix_hits;
     return ok();
 }
 

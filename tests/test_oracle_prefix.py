@@ -129,6 +129,23 @@ def test_a_refused_copy_on_write_changes_nothing():
     assert e.value.code == "EINVAL"
 
 
+def test_a_step_where_all_sharers_write_copies_for_all_but_the_last():
+    m = PoolModel(3)
+    m.add_seq(1)
+    m.append_tokens(1, _prompt(20))                    # blocks 0 and 1 in use, one free
+    m.fork(1, 2)
+    slots, copies = m.append_batch_tokens([1, 2], [5, 6])
+    b0, b1 = m.seq_blocks(2)
+    assert len(copies) == 1 and copies[0][0] == b1     # seq 1 copies, seq 2 keeps b1
+    new = copies[0][1]
+    assert m.seq_blocks(1) == [b0, new] and slots == [new * BS + 4, b1 * BS + 4]
+    assert m.ref[b1] == 1 and m.ref[new] == 1 and len(m.free) == 0
+    m.fork(2, 3)
+    with pytest.raises(PoolError) as e:                # one copy needed, no free block
+        m.append_batch_tokens([2, 3], [7, 8])
+    assert e.value.code == "ENOMEM"
+
+
 def _check_invariants(m, written):
     refs = [0] * m.num_blocks
     for sid, (blocks, n) in m.seqs.items():
