@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-kernel-timer", action="store_true",
                     help="skip the kernel-timing pass (no roofline figure)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
+                    help="only time copy_blocks (copy-on-write of N forked sequences' partly "
+                         "filled blocks, every layer of the workload) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer 8 times (a plain copy of known size, to "
                          "scale the HBM byte counters) and exit")
@@ -89,10 +92,51 @@ def calibrate_copy():
                                          "copies": 8}}), flush=True)
 
 
+def bench_copy_blocks(args):
+    """copy_blocks on the workload's layer pools: N (src, dst) pairs with distinct blocks,
+    K and V of every layer, timed with the library's kernel timer."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_28_amd as pkv
+    import workloads
+    w = workloads.WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    lens = workloads.draw_seq_lens(w)
+    nb = workloads.pool_blocks_for(lens)
+    n = args.copy_blocks
+    caches = [pkv.alloc_caches(nb, w.num_kv_heads, w.head_dim, w.cache_dtype, dev, fill=1)
+              for _ in range(w.layers)]
+    pick = np.random.default_rng(w.seed).permutation(nb)[:2 * n].astype(np.int32)
+    pairs = torch.from_numpy(pick.reshape(2, n).T.copy()).to(dev)
+    ks, vs = [c[0] for c in caches], [c[1] for c in caches]
+    for _ in range(args.warmup):
+        pkv.copy_blocks(ks, vs, pairs)
+    torch.cuda.synchronize()
+    pkv.timer_enable(True)
+    for _ in range(args.steps):
+        pkv.copy_blocks(ks, vs, pairs)
+    torch.cuda.synchronize()
+    ms, launches = pkv.timer_read(pkv.PKV_TIMER_COPY_BLOCKS)
+    pkv.timer_enable(False)
+    block_bytes = ks[0][0].numel() * ks[0].element_size()
+    moved = 2 * 2 * w.layers * n * block_bytes          # K and V, read and written
+    per_call_us = ms * 1e3 / args.steps
+    print(json.dumps({"copy_blocks": {
+        "workload": w.name, "pairs": n, "layers": w.layers, "block_bytes": block_bytes,
+        "launches_per_call": launches // args.steps, "us_per_call": round(per_call_us, 3),
+        "bytes_per_call": moved, "GB/s": round(moved / (per_call_us * 1e-6) / 1e9, 1),
+        "frac_of_peak": round(moved / (per_call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.copy_blocks:
+        bench_copy_blocks(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged decode path has no multi-GPU "
