@@ -9,8 +9,9 @@ draws only).
 Contents
   oracle.c       plain C, IEEE binary64: textbook attention over K/V gathered through
                  the block table, per-partition results and their merge, the slot-mapped
-                 cache write, the FP8 (OCP e4m3) encoding of a quantised KV cache.  Built
-                 with gcc into liboracle.so by ``build()``.
+                 cache write, the FP8 (OCP e4m3) encoding of a quantised KV cache, and
+                 causal multi-query (chunked prefill) attention.  Built with gcc into
+                 liboracle.so by ``build()``.
   allocator.py   Python model of the block pool (FIFO free queue, reference counts).
 
 Parity status: every function here is pinned by tests/test_oracle_*.py against
@@ -69,6 +70,9 @@ def lib():
                                                I32, I32, I32, I64, D, I32, I32, D, D, I32, I32,
                                                I32]
         L.oracle_decode_partitions.restype = ctypes.c_int
+        L.oracle_prefill.argtypes = [P, P, I32, P, I64, P, P, P, P, P, I32, I32, I32, I32, I32,
+                                     I64, D, I32, I32, D, D, I32]
+        L.oracle_prefill.restype = ctypes.c_int
         L.oracle_merge.argtypes = [P, P, P, P, P, I32, I32, I32]
         L.oracle_merge.restype = None
         L.oracle_cache_write.argtypes = [P, P, P, P, P, I32, I32, I32, I64, I64, I64, I32, I32,
@@ -206,6 +210,32 @@ def decode_partitions(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
     if rc != 0:
         raise ValueError("oracle_decode_partitions: bad arguments")
     return o, m, l
+
+
+def prefill(q, q_start, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype: str,
+            rows=None, nthreads: int = 0, kv_dtype: str | None = None, k_scale: float = 1.0,
+            v_scale: float = 1.0) -> np.ndarray:
+    """Multi-query (chunked prefill) paged attention in fp64: q [T][Hq][d] holds the
+    queries of every sequence back to back (sequence b: rows q_start[b] .. q_start[b+1]-1,
+    the last positions of its seq_lens[b]); each attends causally to its sequence's
+    positions up to its own. Returns [T][Hq][d], or [len(rows)][d] for (row, head) pairs."""
+    qa, kc, vc = raw(q), raw(k_cache), raw(v_cache)
+    qs = np.ascontiguousarray(q_start, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    T, Hq, d = qa.shape
+    B = len(sl)
+    assert qs.shape == (B + 1,) and qs[0] == 0 and qs[-1] == T
+    Hkv = kc.shape[1]
+    r, nr = _rows_arg(rows)
+    out = np.empty((T * Hq if r is None else nr, d), dtype=np.float64)
+    rc = lib().oracle_prefill(_ptr(out), None if r is None else _ptr(r), nr, _ptr(qa), Hq * d,
+                              _ptr(qs), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Hq, Hkv, d,
+                              bt.shape[1], kc.shape[0], scale, DTYPE_CODE[dtype],
+                              DTYPE_CODE[kv_dtype or dtype], k_scale, v_scale, nthreads)
+    if rc != 0:
+        raise ValueError("oracle_prefill: bad arguments")
+    return out.reshape(T, Hq, d) if r is None else out
 
 
 def merge(o, m, l, n_parts) -> np.ndarray:

@@ -291,6 +291,59 @@ int oracle_decode_partitions(double* o, double* m, double* l, const int32_t* row
                        k_scale, v_scale, part, max_parts, nthreads);
 }
 
+/* Multi-query (chunked prefill) attention ("vLLM Nedir? ...", section "Chunked prefill";
+ * "Yerel LLM ...", section "4. Prefill ve decode": a long prompt is processed in chunks
+ * over several steps, each chunk's K/V joining the cache before the next).  Sequence b's
+ * queries are rows q_start[b] .. q_start[b+1]-1 of q: the last L = q_start[b+1] -
+ * q_start[b] of its n = seq_lens[b] positions, so query i sits at position n - L + i and
+ * attends to positions 0 .. n - L + i (causal; the chunk's own K/V is already in the
+ * cache).  A query whose position would be negative (L > n) gets a zero row.
+ * out[r][h][d] for every query row r and head h (rows == NULL), or out[k][d] for the
+ * (row, head) pairs rows[2k], rows[2k+1]. */
+int oracle_prefill(double* out, const int32_t* rows, int32_t n_rows, const void* q,
+                   int64_t q_stride, const int32_t* q_start, const void* k_cache,
+                   const void* v_cache, const int32_t* tables, const int32_t* seq_lens,
+                   int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t max_blocks,
+                   int64_t num_blocks, double scale, int32_t q_dtype, int32_t kv_dtype,
+                   double k_scale, double v_scale, int32_t nthreads) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || q_dtype == OR_FP8) return -1;
+    int G = Hq / Hkv;
+    int64_t total_q = q_start[B];
+    int64_t total = rows ? n_rows : total_q * Hq;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#endif
+    for (int64_t k = 0; k < total; ++k) {
+        int64_t r = rows ? rows[2 * k] : k / Hq;
+        int h = rows ? rows[2 * k + 1] : (int)(k % Hq);
+        double* o = out + k * d;
+        if (r < 0 || r >= total_q || h < 0 || h >= Hq) { bad |= 1; continue; }
+        int b = 0;
+        while (b < B && q_start[b + 1] <= r) ++b;           /* the sequence of row r */
+        int64_t L = q_start[b + 1] - q_start[b], n = seq_lens[b];
+        int64_t pos = n - L + (r - q_start[b]);
+        if (n > (int64_t)max_blocks * OR_BS) { bad |= 1; continue; }
+        if (pos < 0) {
+            for (int i = 0; i < d; ++i) o[i] = 0.0;
+            continue;
+        }
+        double* qq = (double*)malloc(sizeof(double) * d);
+        double* K = (double*)malloc(sizeof(double) * (size_t)((pos + 1) * d));
+        double* V = (double*)malloc(sizeof(double) * (size_t)((pos + 1) * d));
+        for (int i = 0; i < d; ++i) qq[i] = elem(q, r * q_stride + (int64_t)h * d + i, q_dtype);
+        if (oracle_gather(K, V, k_cache, v_cache, tables + (int64_t)b * max_blocks, 0, pos + 1,
+                          h / G, Hkv, d, num_blocks, kv_dtype, k_scale, v_scale) != 0)
+            bad |= 1;
+        oracle_attend(o, NULL, NULL, qq, K, V, pos + 1, d, scale);
+        free(qq);
+        free(K);
+        free(V);
+    }
+    return bad ? -1 : 0;
+}
+
 /* Merge of per-partition results for n_rows rows, each with n_parts[r] live
  * partitions: out = sum_p w_p o_p / sum_p w_p, w_p = exp(m_p - M) l_p, M = max m_p.
  * A row with no live partition gets o = 0. */
