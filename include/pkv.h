@@ -88,7 +88,8 @@ const char* pkv_version(void);
 #define PKV_TIMER_REDUCE 1
 #define PKV_TIMER_CACHE_WRITE 2
 #define PKV_TIMER_COPY_BLOCKS 3
-#define PKV_TIMER_ENTRIES 4
+#define PKV_TIMER_PREFILL 4
+#define PKV_TIMER_ENTRIES 5
 int pkv_timer_enable(int32_t enable);
 int pkv_timer_read(int32_t entry, double* total_ms, int64_t* launches);
 
@@ -375,6 +376,32 @@ int paged_attention_reduce(void* out, const float* part_out, const float* part_m
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t max_blocks_per_seq, int32_t partition_size,
                            int32_t max_partitions, int32_t out_dtype, void* stream);
+
+/* paged_attention_prefill: causal multi-query attention over the paged cache, for
+ * chunked prefill: a long prompt is processed in chunks over several steps, each chunk's
+ * K/V written to the cache (reshape_and_cache) before its queries attend ("vLLM Nedir?
+ * ...", section "Chunked prefill"; "Yerel LLM ...", section "4. Prefill ve decode").
+ * Sequence b's queries are rows q_start[b] .. q_start[b+1] - 1 of q: the last
+ * L_b = q_start[b+1] - q_start[b] of its n = seq_lens[b] positions. Query i (position
+ * p = n - L_b + i) of query head h attends to positions 0 .. p of KV head
+ * h / (num_heads / num_kv_heads):
+ *     out[r][h] = sum_{t <= p} softmax_t(scale * q[r][h] . K_b[t]) V_b[t]
+ * A query with p < 0 (L_b > n) gets a zero row. Single-query rows (L_b = 1) are the
+ * decode step; paged_attention_decode is the faster call for those.
+ *   q:       device, in_dtype (F16 or BF16), row r at q + r * q_stride elements
+ *            (q_stride >= num_heads * head_dim, a multiple of 8), heads dense in a row.
+ *   q_start: device int32 [num_seqs + 1], q_start[0] = 0, non-decreasing;
+ *            L_b <= max_q_len (rows past max_q_len are not computed).
+ *   out:     device [q_start[num_seqs]][num_heads][head_dim], out_dtype (in_dtype or F32).
+ *   caches, block_tables, seq_lens as paged_attention_decode (16-bit caches).
+ * Supported: head_dim 64 or 128, num_heads / num_kv_heads <= 16.
+ * Errors: EINVAL, ENOTSUP (dtypes, head_dim, group size), EHIP. */
+int paged_attention_prefill(void* out, const void* q, int64_t q_stride, const int32_t* q_start,
+                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t max_q_len,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            float scale, int32_t in_dtype, int32_t out_dtype, void* stream);
 
 /* copy_blocks: the device half of copy-on-write. For each pair p < n_pairs,
  * (src, dst) = (pairs[2p], pairs[2p + 1]), copy block src onto block dst in the K and

@@ -82,6 +82,8 @@ def lib():
         "kv_pool_append_tokens": ([P, I64, P, I32, P, P], ctypes.c_int),
         "kv_pool_append_batch_tokens": ([P, P, P, I32, P, P, P], ctypes.c_int),
         "copy_blocks": ([P, P, I32, P, I32, I64, I64, P], ctypes.c_int),
+        "paged_attention_prefill": ([P, P, I64, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                     I64, F, I32, I32, P], ctypes.c_int),
         "reshape_and_cache": ([P, P, P, P, P, I32, I32, I32, I32, I64, I64, I64, I32, P],
                               ctypes.c_int),
         "paged_attention_decode": ([P, P, P, P, P, I64, P, P, P, P, I32, I32, I32, I32, I32, I32,
@@ -118,7 +120,7 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "reshape_and_cache_fp8", "paged_attention_decode_fp8",
             "paged_attention_decode_append_fp8", "pkv_timer_enable", "pkv_timer_read",
             "kv_pool_add_seq_prefix", "kv_pool_fork", "kv_pool_append_tokens",
-            "kv_pool_append_batch_tokens", "copy_blocks")
+            "kv_pool_append_batch_tokens", "copy_blocks", "paged_attention_prefill")
 
 
 def _check(rc: int):
@@ -514,6 +516,31 @@ def paged_attention_decode_append_fp8(out, q, key, value, slot_mapping, k_cache,
         max_partitions, dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
 
 
+def paged_attention_prefill(out, q, q_start, k_cache, v_cache, block_tables, seq_lens,
+                            scale: float, max_q_len: int, stream=None):
+    """Causal multi-query attention (chunked prefill): q/out [T][Hq][d] hold every
+    sequence's chunk back to back, sequence b in rows q_start[b] .. q_start[b+1]-1 (device
+    int32 [B+1]); the chunk is the last positions of seq_lens[b] and its K/V is already in
+    the cache. max_q_len bounds the chunk lengths (host value)."""
+    T, Hq, d = q.shape
+    if q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must have dense heads/dims")
+    if tuple(out.shape) != (T, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T][Hq][d] tensor")
+    B = seq_lens.numel()
+    if q_start.numel() != B + 1 or not q_start.is_contiguous():
+        raise ValueError("q_start must hold num_seqs + 1 offsets")
+    if not (block_tables.is_contiguous() and seq_lens.is_contiguous() and
+            k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("block_tables, seq_lens and the caches must be contiguous")
+    _check(lib().paged_attention_prefill(
+        _dev(out, "out"), _dev(q, "q"), q.stride(0), _dev(q_start, "q_start"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(seq_lens, "seq_lens"), B, int(max_q_len), Hq, k_cache.shape[1], d, BLOCK_SIZE,
+        block_tables.shape[1], k_cache.shape[0], float(scale), dtype_code(q.dtype),
+        dtype_code(out.dtype), _stream(q, stream)))
+
+
 def copy_blocks(k_caches, v_caches, pairs, stream=None):
     """Copy-on-write on the device: for each (src, dst) row of pairs (device int32
     [n][2]), block src onto block dst in every layer's K and V cache (lists of tensors)."""
@@ -544,6 +571,7 @@ def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partitio
 
 # ------------------------------------------------------------------ kernel timer
 PKV_TIMER_DECODE, PKV_TIMER_REDUCE, PKV_TIMER_CACHE_WRITE, PKV_TIMER_COPY_BLOCKS = 0, 1, 2, 3
+PKV_TIMER_PREFILL = 4
 
 
 def timer_enable(on: bool = True):

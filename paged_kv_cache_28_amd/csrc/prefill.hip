@@ -1,0 +1,325 @@
+// paged_attention_prefill: causal multi-query attention over the paged cache, for chunked
+// prefill. A long prompt is processed in chunks over several steps; each chunk's K/V joins
+// the cache (reshape_and_cache) and then its queries attend to every earlier position of
+// the sequence and to the chunk up to themselves ("vLLM Nedir? PagedAttention ile
+// Production LLM Serving", section "Chunked prefill"; "Yerel LLM sistemlerinde backpressure
+// ve ölçekleme", section "4. Prefill ve decode"). With many queries per sequence the work
+// is a dense contraction, so it runs on the matrix cores.
+//
+// Work decomposition: one workgroup of 4 waves per (query tile, KV head, sequence). The
+// 16 columns of the matrix products are (query token, head of the GQA group) pairs; a wave
+// holds NC column tiles (16 * NC columns = 16 * NC / G query tokens), so every K/V tile it
+// loads into registers feeds NC x 16 columns. The 4 waves take the key blocks round-robin,
+// each with its own online softmax per column, and merge through LDS one column tile at a
+// time. Causal mask: each lane masks with its own column's limit (keys at positions up to
+// the query's), and a column tile whose queries see none of a block skips it.
+//
+// Per tile and column tile the products are those of the decode kernel:
+//   S^T[16 keys][16 cols] = K_tile x Q^T   (16x16x32, d/32 steps)
+//   O^T[d][16 cols]      += V^T x P^T       (16x16x16, d/16 steps, P split in two parts)
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "device.hpp"
+#include "status.hpp"
+#include "tile.hpp"
+#include "timer.hpp"
+
+namespace pkv {
+
+struct PrefillArgs {
+    void* out;                 // [T][Hq][D]
+    const void* q;             // row r at q + r * q_stride
+    const int32_t* q_start;    // [num_seqs + 1]
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int64_t q_stride;
+    int64_t num_blocks;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t group;
+    int32_t max_blocks;
+    float scale_log2;
+};
+
+constexpr int kPrefillWaves = 4;
+
+template <int D>
+__host__ __device__ constexpr size_t prefill_lds_bytes() {
+    return sizeof(float) * (2 * kPrefillWaves * 16 + size_t(kPrefillWaves) * 16 * D);
+}
+
+template <typename T, int D, typename OutT, int NC>
+__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs a) {
+    constexpr int W = kPrefillWaves;
+    constexpr int NQK = D / 32, NPV = D / 16;
+    extern __shared__ float lds[];
+    float* sm_m = lds;                  // [W][16]
+    float* sm_l = lds + W * 16;         // [W][16]
+    float* sm_o = lds + 2 * W * 16;     // [W][16][D]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, quad = lane >> 4;
+    const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int G = a.group;
+    const int QT = 16 * NC / G;         // query tokens of this workgroup
+    const int q0 = a.q_start[b];
+    const int L = a.q_start[b + 1] - q0;
+    const int t0 = qt * QT;
+    if (t0 >= L) return;
+    const int tcount = min(QT, L - t0);
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > a.max_blocks * 16 ? a.max_blocks * 16 : n);
+
+    // This lane's column in each column tile: query token, head, causal limit (keys
+    // below it are visible), and its Q^T operand.
+    int lim[NC];
+    int tile_lim[NC];   // largest limit of the column tile (wave-uniform)
+    uint4 qf[NC][NQK];
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+        const int c = 16 * ct + col;
+        const int tok = c / G, hg = c - tok * G;
+        const bool valid = tok < tcount;
+        const int pos = n - L + t0 + tok;          // the query's position in its sequence
+        lim[ct] = valid ? max(0, min(pos + 1, n)) : 0;
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                               int64_t(q0 + t0 + (valid ? tok : 0)) * a.q_stride +
+                               int64_t(g * G + hg) * D;
+#pragma unroll
+        for (int s = 0; s < NQK; ++s)
+            qf[ct][s] = valid ? *reinterpret_cast<const uint4*>(qrow + q_dim<false>(s, quad))
+                              : make_uint4(0, 0, 0, 0);
+        int m = lim[ct];
+#pragma unroll
+        for (int k = 1; k < 16; k <<= 1) m = max(m, __shfl_xor(m, k, 64));
+        tile_lim[ct] = __builtin_amdgcn_readfirstlane(m);
+    }
+    int key_end = 0;   // keys any column of the workgroup sees
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) key_end = max(key_end, tile_lim[ct]);
+    const int nblk = (key_end + 15) >> 4;
+
+    f32x4 acc[NC][NPV];
+    float m[NC], lsum[NC];
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) acc[ct][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[ct] = -INFINITY;
+        lsum[ct] = 0.f;
+    }
+    constexpr float kSlack = 8.0f;   // lazy reference point, as in the decode kernel
+
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    const int64_t tile_bytes = int64_t(D) * 16 * 2;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    int tab = 0;
+
+    auto load = [&](KvTile<D, false>& t, int k) -> bool {
+        int64_t phys = __builtin_amdgcn_readlane(tab, k);
+        const bool ok = phys >= 0 && phys < a.num_blocks;
+        phys = ok ? phys : 0;
+        const int64_t tile = phys * a.num_kv_heads + g;
+        load_tile<D>(t, kbase + tile * tile_bytes, vbase + tile * tile_bytes, lane);
+        return ok;
+    };
+
+    auto compute = [&](KvTile<D, false>& t, int j, bool ok) {
+        if (!ok) return;
+        const int tok0 = j * 16 + 4 * quad;
+        if (j * 16 + 16 > n)   // rows past the sequence may hold anything
+            mask_rows<D>(t, tok0 + 0 < n, tok0 + 1 < n, tok0 + 2 < n, tok0 + 3 < n);
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+            if (j * 16 >= tile_lim[ct]) continue;   // no query of this column tile sees it
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(k_operand<T, D>(t, c), qf[ct][c], s);
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = tok0 + e < lim[ct] ? s[e] * a.scale_log2 : -INFINITY;
+            const float bm = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+            const bool move = bm > m[ct] + kSlack;
+            if (__builtin_amdgcn_ballot_w64(move)) {
+                const float mn = move ? bm : m[ct];
+                const float alpha = exp2_fast(m[ct] - mn);
+                lsum[ct] *= alpha;
+#pragma unroll
+                for (int c = 0; c < NPV; ++c) acc[ct][c] *= alpha;
+                m[ct] = mn;
+            }
+            float pe[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m[ct]);
+            lsum[ct] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+            uint16_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
+            const uint2 phi = make_uint2(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                                         uint32_t(hi[2]) | (uint32_t(hi[3]) << 16));
+            const uint2 plo = make_uint2(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                                         uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) {
+                const uint2 vv = v_operand<T, D>(t, c);
+                acc[ct][c] = Mfma<T>::pv(vv, phi, acc[ct][c]);
+                acc[ct][c] = Mfma<T>::pv(vv, plo, acc[ct][c]);
+            }
+        }
+    };
+
+    // This wave's blocks: wave, wave + W, ...; segments of 64 block ids (one per lane),
+    // two tiles in flight as in the decode kernel.
+    const int nmine = wave < nblk ? (nblk - wave + W - 1) / W : 0;
+    for (int k0 = 0; k0 < nmine; k0 += 64) {
+        const int cnt = min(64, nmine - k0);
+        tab = lane < cnt ? table[wave + (k0 + lane) * W] : 0;
+        KvTile<D, false> A, B;
+        bool okA = load(A, 0), okB;
+        for (int k = 0; k < cnt; k += 2) {
+            okB = load(B, min(k + 1, cnt - 1));
+            compute(A, wave + (k0 + k) * W, okA);
+            if (k + 1 >= cnt) break;
+            okA = load(A, min(k + 2, cnt - 1));
+            compute(B, wave + (k0 + k + 1) * W, okB);
+        }
+    }
+
+    // Merge the waves' states column tile by column tile and write the rows.
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+        float ls = lsum[ct];
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        if (lane < 16) {
+            sm_m[wave * 16 + lane] = m[ct];
+            sm_l[wave * 16 + lane] = ls;
+        }
+#pragma unroll
+        for (int c = 0; c < NPV; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm_o[(wave * 16 + col) * D + 16 * c + 4 * quad + e] = acc[ct][c][e];
+        __syncthreads();
+        for (int i = threadIdx.x; i < 16 * D; i += W * 64) {
+            const int c = i / D, dim = i - c * D;
+            const int cc = 16 * ct + c;
+            const int tok = cc / G, hg = cc - tok * G;
+            if (tok >= tcount) continue;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * 16 + c]);
+            float o = 0.f;
+            if (M != -INFINITY) {   // a query before position 0 sees no key: zero row
+                float Lw = 0.f, O = 0.f;
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    const float f = exp2_fast(sm_m[w * 16 + c] - M);
+                    Lw += f * sm_l[w * 16 + c];
+                    O += f * sm_o[(w * 16 + c) * D + dim];
+                }
+                o = O / Lw;
+            }
+            const int64_t row = int64_t(q0 + t0 + tok) * a.num_heads + g * G + hg;
+            OutStore<OutT>::st(a.out, row * D + dim, o);
+        }
+        __syncthreads();
+    }
+}
+
+template <typename T, int D, typename OutT>
+hipError_t launch_prefill(const PrefillArgs& a, int max_q_len, int num_kv_heads, int num_seqs,
+                          hipStream_t s) {
+    constexpr int NC = 4;
+    const int qt_tokens = 16 * NC / a.group;
+    const dim3 grid(unsigned((max_q_len + qt_tokens - 1) / qt_tokens), unsigned(num_kv_heads),
+                    unsigned(num_seqs));
+    const LaunchEvents ev = timer_events(PKV_TIMER_PREFILL);
+    hipExtLaunchKernelGGL((prefill_kernel<T, D, OutT, NC>), grid, dim3(kPrefillWaves * 64),
+                          prefill_lds_bytes<D>(), s, ev.start, ev.stop, 0, a);
+    return hipGetLastError();
+}
+
+}  // namespace pkv
+
+extern "C" int paged_attention_prefill(void* out, const void* q, int64_t q_stride,
+                                       const int32_t* q_start, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* seq_lens, int32_t num_seqs,
+                                       int32_t max_q_len, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                       int32_t in_dtype, int32_t out_dtype, void* stream) {
+    using pkv::fail;
+    const char* who = "paged_attention_prefill";
+    if (in_dtype != PKV_F16 && in_dtype != PKV_BF16)
+        return fail(in_dtype == PKV_F32 ? PKV_ENOTSUP : PKV_EINVAL,
+                    "%s: in_dtype must be F16 or BF16", who);
+    if (out_dtype != in_dtype && out_dtype != PKV_F32)
+        return fail(PKV_ENOTSUP, "%s: out_dtype must be in_dtype or F32", who);
+    if (num_seqs < 0 || max_q_len < 0) return fail(PKV_EINVAL, "%s: negative sizes", who);
+    if (block_size != PKV_BLOCK_SIZE)
+        return fail(PKV_EINVAL, "%s: block_size must be 16, got %d", who, block_size);
+    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+        return fail(PKV_EINVAL, "%s: num_heads %d not a multiple of num_kv_heads %d", who,
+                    num_heads, num_kv_heads);
+    if (num_seqs > 65535 || num_kv_heads > 65535)
+        return fail(PKV_EINVAL, "%s: num_seqs / num_kv_heads above 65535", who);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PKV_ENOTSUP, "%s: head_dim %d (built: 64, 128)", who, head_dim);
+    const int G = num_heads / num_kv_heads;
+    if (G > 16) return fail(PKV_ENOTSUP, "%s: group size %d too large", who, G);
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return fail(PKV_EINVAL, "%s: bad max_blocks_per_seq / num_blocks", who);
+    if (q_stride < int64_t(num_heads) * head_dim || q_stride % 8)
+        return fail(PKV_EINVAL, "%s: q_stride must cover num_heads*head_dim and be a multiple "
+                                "of 8", who);
+    if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale not finite", who);
+    if (num_seqs == 0 || max_q_len == 0) return pkv::ok();
+    if (!out || !q || !q_start || !k_cache || !v_cache || !block_tables || !seq_lens)
+        return fail(PKV_EINVAL, "%s: NULL pointer", who);
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+         reinterpret_cast<uintptr_t>(v_cache)) & 15)
+        return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned", who);
+    const int qt_tokens = 16 * 4 / G;
+    if ((int64_t(max_q_len) + qt_tokens - 1) / qt_tokens > 0x7fffffff)
+        return fail(PKV_EINVAL, "%s: max_q_len too large", who);
+    pkv::PrefillArgs a;
+    a.out = out;
+    a.q = q;
+    a.q_start = q_start;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.q_stride = q_stride;
+    a.num_blocks = num_blocks;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = G;
+    a.max_blocks = max_blocks_per_seq;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (head_dim == 128)
+        err = in_dtype == PKV_BF16
+                  ? (out_dtype == PKV_F32 ? pkv::launch_prefill<pkv::bf16_t, 128, float>(a, max_q_len, num_kv_heads, num_seqs, s)
+                                          : pkv::launch_prefill<pkv::bf16_t, 128, pkv::bf16_t>(a, max_q_len, num_kv_heads, num_seqs, s))
+                  : (out_dtype == PKV_F32 ? pkv::launch_prefill<pkv::f16_t, 128, float>(a, max_q_len, num_kv_heads, num_seqs, s)
+                                          : pkv::launch_prefill<pkv::f16_t, 128, pkv::f16_t>(a, max_q_len, num_kv_heads, num_seqs, s));
+    else
+        err = in_dtype == PKV_BF16
+                  ? (out_dtype == PKV_F32 ? pkv::launch_prefill<pkv::bf16_t, 64, float>(a, max_q_len, num_kv_heads, num_seqs, s)
+                                          : pkv::launch_prefill<pkv::bf16_t, 64, pkv::bf16_t>(a, max_q_len, num_kv_heads, num_seqs, s))
+                  : (out_dtype == PKV_F32 ? pkv::launch_prefill<pkv::f16_t, 64, float>(a, max_q_len, num_kv_heads, num_seqs, s)
+                                          : pkv::launch_prefill<pkv::f16_t, 64, pkv::f16_t>(a, max_q_len, num_kv_heads, num_seqs, s));
+    if (err != hipSuccess)
+        return fail(PKV_EHIP, "%s: launch failed: %s", who, hipGetErrorString(err));
+    return pkv::ok();
+}

@@ -1,0 +1,94 @@
+// One (block, KV head) tile of K and V as a lane holds it for the two matrix products of
+// the attention kernels (decode and prefill), the operands taken from it, and row masking.
+// The 16 columns of both products are whatever the kernel puts there (query heads of a
+// GQA group in decode; (query token, head) pairs in prefill).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace pkv {
+
+// K and V of one (block, KV head) tile as this lane holds them for the two products,
+// per cache type, and the operands the matrix instructions take from it.
+//   16-bit cache: k[c] is the A operand of QK step c (dims 32c + 8 quad .. + 7 of token
+//     l%16, 16 bytes at (64c + l) * 16 of the [d/8][16][8] tile); v[c] that of PV step c
+//     (dim 16c + l%16, tokens 4 quad .. + 3).
+//   FP8 cache ([d/16][16][16] bytes): one 16-byte load k[i] at (64i + l) * 16 holds dims
+//     16(4i + quad) .. + 15 of token l%16 and feeds QK steps 2i (its first 8 dims) and
+//     2i + 1 (the last 8); the dimensions of the contraction are taken in another order,
+//     and the Q^T operand follows the same order (q_dim). v[c] holds the four codes of
+//     PV step c. The codes are widened to T when used.
+template <int D, bool F8> struct KvTile;
+template <int D> struct KvTile<D, false> {
+    uint4 k[D / 32];
+    uint2 v[D / 16];
+};
+template <int D> struct KvTile<D, true> {
+    uint4 k[D / 64];
+    uint32_t v[D / 16];
+};
+
+// First query dimension of the 8 that lane group `quad` feeds QK step c with.
+template <bool F8>
+__device__ __forceinline__ int q_dim(int c, int quad) {
+    return F8 ? 64 * (c >> 1) + 16 * quad + 8 * (c & 1) : 32 * c + 8 * quad;
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(KvTile<D, false>& t, const char* kt, const char* vt,
+                                          int lane) {
+    const int col = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 16);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        t.v[c] = *reinterpret_cast<const uint2*>(vt + ((16 * c + col) * 16 + 4 * quad) * 2);
+}
+template <int D>
+__device__ __forceinline__ void load_tile(KvTile<D, true>& t, const char* kt, const char* vt,
+                                          int lane) {
+    const int col = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) t.k[i] = *reinterpret_cast<const uint4*>(kt + (64 * i + lane) * 16);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        t.v[c] = *reinterpret_cast<const uint32_t*>(vt + (16 * c + col) * 16 + 4 * quad);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ uint4 k_operand(const KvTile<D, false>& t, int c) { return t.k[c]; }
+template <typename T, int D>
+__device__ __forceinline__ uint4 k_operand(const KvTile<D, true>& t, int c) {
+    const uint4 w = t.k[c >> 1];
+    const uint2 a = Fp8<T>::x4((c & 1) ? w.z : w.x), b = Fp8<T>::x4((c & 1) ? w.w : w.y);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+template <typename T, int D>
+__device__ __forceinline__ uint2 v_operand(const KvTile<D, false>& t, int c) { return t.v[c]; }
+template <typename T, int D>
+__device__ __forceinline__ uint2 v_operand(const KvTile<D, true>& t, int c) { return Fp8<T>::x4(t.v[c]); }
+
+// Zero V rows tok0 + e (e = 0..3) of this lane whose keep[e] is false, so that whatever
+// bytes a partly filled block holds there never reach the sum (0 weight times NaN would).
+template <int D>
+__device__ __forceinline__ void mask_rows(KvTile<D, false>& t, bool k0, bool k1, bool k2, bool k3) {
+    const uint32_t lo = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
+    const uint32_t hi = (k2 ? 0x0000ffffu : 0u) | (k3 ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        t.v[c].x &= lo;
+        t.v[c].y &= hi;
+    }
+}
+template <int D>
+__device__ __forceinline__ void mask_rows(KvTile<D, true>& t, bool k0, bool k1, bool k2, bool k3) {
+    const uint32_t m = (k0 ? 0xffu : 0u) | (k1 ? 0xff00u : 0u) | (k2 ? 0xff0000u : 0u) |
+                       (k3 ? 0xff000000u : 0u);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) t.v[c] &= m;
+}
+
+}  // namespace pkv

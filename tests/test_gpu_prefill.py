@@ -1,0 +1,126 @@
+"""GPU parity of paged_attention_prefill (causal multi-query attention for chunked
+prefill) against the oracle on the same seeded inputs.
+
+Bars as for decode: fp32 output max |err| <= 2e-3 and max|err| / max|ref| <= 1e-3 for
+16-bit inputs; 16-bit output equal to the RNE cast of the kernel's fp32 result and within
+the fp32 bar plus half an output ulp of the oracle. Cases: whole prompts, chunks that end
+longer contexts, single-query rows mixed with chunks, chunks longer than their sequence
+(zero rows), several shapes of GQA group and head size, and a prompt processed in chunks
+over several calls against one call over the whole prompt ("vLLM Nedir? PagedAttention ile
+Production LLM Serving", section "Chunked prefill").
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_batch
+import oracle
+import paged_batch
+import paged_kv_cache_28_amd as pkv
+import workloads
+from test_gpu_parity import TOL, _ulp, check_close
+
+pytestmark = pytest.mark.gpu
+B8 = workloads.WORKLOADS["llama8b"]
+SHAPES = {
+    "bf16-d128-g4": dataclasses.replace(B8, num_blocks=0),
+    "f16-d64-g8": dataclasses.replace(B8, dtype="f16", num_heads=16, num_kv_heads=2, head_dim=64,
+                                      num_blocks=0),
+    "bf16-d128-g16": dataclasses.replace(B8, num_heads=32, num_kv_heads=2, num_blocks=0),
+    "bf16-d64-g1": dataclasses.replace(B8, num_heads=4, num_kv_heads=4, head_dim=64, num_blocks=0),
+}
+# (context length, chunk length) per sequence
+CASES = {
+    "whole": [(1, 1), (16, 16), (23, 23), (70, 70), (129, 129)],
+    "chunks": [(40, 7), (97, 33), (300, 64), (513, 100), (1000, 17)],
+    "mixed": [(700, 1), (64, 64), (250, 1), (431, 150), (33, 1), (2, 2)],
+    "short": [(5, 8), (12, 12), (3, 30)],
+}
+
+
+@pytest.fixture(scope="module")
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _run(w, spec, device, out_dtype=torch.float32, seed=0):
+    lens = [n for n, _ in spec]
+    chunk = [L for _, L in spec]
+    ob = paged_batch.build(w, lens=lens, seed_stream=seed)
+    gb = gpu_batch.build(ob, device)
+    q = workloads.draw_q(w, workloads.rng(w.seed, 60, seed), batch=int(sum(chunk)))
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    out = torch.full(tuple(q.shape), float("nan"), dtype=out_dtype, device=device)
+    pkv.paged_attention_prefill(out, q.to(device), torch.from_numpy(qs).to(device), gb.k_cache,
+                                gb.v_cache, gb.tables_d, gb.lens_d, w.scale, max(chunk))
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q, qs, ob.k_cache, ob.v_cache, ob.tables, ob.lens, w.scale, w.dtype)
+    return out, ref
+
+
+@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_prefill_matches_oracle(name, case, device):
+    out, ref = _run(SHAPES[name], CASES[case], device)
+    check_close(out.cpu().double().numpy(), ref, SHAPES[name].dtype, f"{name} {case}")
+
+
+@pytest.mark.parametrize("name", ["bf16-d128-g4", "f16-d64-g8"])
+def test_prefill_16bit_output(name, device):
+    w = SHAPES[name]
+    tdt = pkv.torch_dtype(w.dtype)
+    out_lp, ref = _run(w, CASES["mixed"], device, out_dtype=tdt)
+    out_32, _ = _run(w, CASES["mixed"], device)
+    assert torch.equal(out_lp, out_32.to(tdt))
+    got = out_lp.cpu().double().numpy()
+    assert np.all(np.abs(got - ref) <= TOL[w.dtype] + 0.5 * _ulp(got, w.dtype))
+
+
+def test_a_prompt_in_chunks_equals_one_pass(device):
+    """The same 300-token prompt: written and attended in 64-token chunks over five calls,
+    and in one call; every row within the bar of the oracle, and the two GPU results within
+    fp32 summation-order differences of each other."""
+    w = SHAPES["bf16-d128-g4"]
+    n = 300
+    ob = paged_batch.build(w, lens=[n])
+    gb = gpu_batch.build(ob, device)
+    q = workloads.draw_q(w, workloads.rng(w.seed, 61), batch=n).to(device)
+    ref = oracle.prefill(q.cpu(), np.array([0, n], np.int32), ob.k_cache, ob.v_cache, ob.tables,
+                         ob.lens, w.scale, w.dtype)
+    one = torch.empty(q.shape, dtype=torch.float32, device=device)
+    pkv.paged_attention_prefill(one, q, torch.tensor([0, n], dtype=torch.int32, device=device),
+                                gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale, n)
+    parts = torch.empty_like(one)
+    for c0 in range(0, n, 64):
+        c1 = min(n, c0 + 64)
+        qs = torch.tensor([0, c1 - c0], dtype=torch.int32, device=device)
+        lens = torch.tensor([c1], dtype=torch.int32, device=device)   # the context so far
+        pkv.paged_attention_prefill(parts[c0:c1], q[c0:c1], qs, gb.k_cache, gb.v_cache,
+                                    gb.tables_d, lens, w.scale, c1 - c0)
+    torch.cuda.synchronize()
+    for got in (one, parts):
+        check_close(got.cpu().double().numpy(), ref, w.dtype, "chunked prompt")
+    assert ((one - parts).abs() <= 2e-5 + 1e-5 * one.abs()).all()
+
+
+def test_prefill_rejects_bad_arguments(device):
+    w = SHAPES["bf16-d128-g4"]
+    kc, vc = pkv.alloc_caches(4, w.num_kv_heads, w.head_dim, w.dtype, device, fill=0.0)
+    q = torch.zeros((3, w.num_heads, w.head_dim), dtype=torch.float32, device=device)
+    qs = torch.tensor([0, 3], dtype=torch.int32, device=device)
+    tab = torch.zeros((1, 1), dtype=torch.int32, device=device)
+    ln = torch.tensor([3], dtype=torch.int32, device=device)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attention_prefill(q.clone(), q, qs, kc, vc, tab, ln, 0.1, 3)
+    assert e.value.code == pkv.PKV_ENOTSUP                 # fp32 queries
+    qb = q.bfloat16()
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attention_prefill(qb.half(), qb, qs, kc, vc, tab, ln, 0.1, 3)
+    assert e.value.code == pkv.PKV_ENOTSUP                 # out type neither bf16 nor f32
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attention_prefill(q, qb, qs, kc, vc, tab, ln, float("nan"), 3)
+    assert e.value.code == pkv.PKV_EINVAL
