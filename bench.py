@@ -130,6 +130,112 @@ def bench_copy_blocks(args):
           flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+
+
+def bench_prefill(args):
+    """Chunked prefill (workloads with prefill_tokens): per step, one chunk of the long
+    prompt (its K/V written, then paged_attention_prefill) and one fused decode token for
+    each user, in every layer. A pass is all chunks of the prompt; one untimed pass, one
+    timed pass, one pass with the library's kernel timer, each on a fresh pool."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_28_amd as pkv
+    import workloads
+    w = workloads.WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    L, U, Hq, Hkv, d = w.layers, w.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    tdt = pkv.torch_dtype(w.dtype)
+    C = -(-w.prefill_tokens // w.prefill_chunks)
+    chunks = [(c0, min(w.prefill_tokens, c0 + C)) for c0 in range(0, w.prefill_tokens, C)]
+    ulens = workloads.draw_seq_lens(w)
+    nsteps = len(chunks)
+    nb = workloads.pool_blocks_for(list(ulens) + [w.prefill_tokens], growth_tokens=nsteps)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    caches = []
+    for _ in range(L):
+        kc, vc = pkv.alloc_caches(nb, Hkv, d, tdt, dev)
+        kc.normal_(generator=g)
+        vc.normal_(generator=g)
+        caches.append((kc, vc))
+    qp = [torch.randn((C, Hq, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    kp = [torch.randn((C, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    vp = [torch.randn((C, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    qu = [torch.randn((U, Hq, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    ku = [torch.randn((U, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    vu = [torch.randn((U, Hkv, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    outp = torch.empty((C, Hq, d), device=dev, dtype=tdt)
+    outu = torch.empty((U, Hq, d), device=dev, dtype=tdt)
+    mbp = -(-w.prefill_tokens // 16)
+    mbu = int(-(-(int(ulens.max()) + nsteps) // 16))
+    order = workloads.draw_free_order(nb, workloads.rng(w.seed, 1))
+
+    def run_pass():
+        pool = pkv.kv_pool_create(nb, L, Hkv, d, w.dtype, free_order=order)
+        uid = np.arange(1, U + 1, dtype=np.int64)
+        for u in range(U):
+            pool.add_seq(int(uid[u]))
+            pool.append(int(uid[u]), int(ulens[u]) - 1)
+        pool.add_seq(0)
+        for c0, c1 in chunks:
+            ps = torch.from_numpy(pool.append(0, c1 - c0)).to(dev)
+            tp, lp = pool.build_tables([0], mbp)
+            us = torch.from_numpy(pool.append_batch(uid)).to(dev)
+            tu, lu = pool.build_tables(uid, mbu)
+            tp, lp, tu, lu = (torch.from_numpy(x).to(dev) for x in (tp, lp, tu, lu))
+            qs = torch.tensor([0, c1 - c0], dtype=torch.int32, device=dev)
+            for l in range(L):
+                kc, vc = caches[l]
+                pkv.reshape_and_cache(kp[l][:c1 - c0], vp[l][:c1 - c0], kc, vc, ps)
+                pkv.paged_attention_prefill(outp[:c1 - c0], qp[l][:c1 - c0], qs, kc, vc, tp, lp,
+                                            w.scale, c1 - c0)
+                pkv.paged_attention_decode_append(outu, qu[l], ku[l], vu[l], us, kc, vc, tu, lu,
+                                                  w.scale)
+        pool.close()
+
+    run_pass()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_pass()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    pkv.timer_enable(True)
+    run_pass()
+    torch.cuda.synchronize()
+    pre_ms, pre_n = pkv.timer_read(pkv.PKV_TIMER_PREFILL)
+    dec_ms, dec_n = pkv.timer_read(pkv.PKV_TIMER_DECODE)
+    cw_ms, cw_n = pkv.timer_read(pkv.PKV_TIMER_CACHE_WRITE)
+    pkv.timer_enable(False)
+    # causal attention of the whole prompt: query at position p attends to p + 1 keys;
+    # 2 flops per multiply-add in Q K^T and in P V, every query head, every layer
+    pairs = sum((c1 * (c1 + 1) - c0 * (c0 + 1)) // 2 for c0, c1 in chunks)
+    flops = 4 * d * Hq * pairs * L
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    result = {
+        "metric": "chunked prefill: paged_attention_prefill MFMA TFLOP/s (causal attention of "
+                  "the prompt) + step time with the users' decode",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": nsteps,
+        "warmup": 1, "ms_per_step": round(elapsed / nsteps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded draws)",
+        "config": {"workload": w.name, "layers": L, "prompt_tokens": w.prefill_tokens,
+                   "chunks": nsteps, "chunk_tokens": C, "decode_users": U,
+                   "user_seq_len_range": [w.len_lo, w.len_hi], "num_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": d, "block_size": 16},
+        "prefill_kernel_us_avg": round(pre_ms * 1e3 / pre_n, 2),
+        "prefill_tokens_per_s_per_layer": round(w.prefill_tokens / (pre_ms * 1e-3 / L), 1),
+        "decode_kernel_us_avg": round(dec_ms * 1e3 / dec_n, 3) if dec_n else None,
+        "cache_write_kernel_us_avg": round(cw_ms * 1e3 / cw_n, 3) if cw_n else None,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "paged_attention_prefill",
+                     "alg_flops_per_pass": flops},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -137,6 +243,13 @@ def main():
         return
     if args.copy_blocks:
         bench_copy_blocks(args)
+        return
+    import workloads as _wl
+    if _wl.WORKLOADS[args.config].prefill_tokens:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_prefill(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the paged decode path has no multi-GPU "

@@ -9,14 +9,27 @@
 // Work decomposition: one workgroup of 4 waves per (query tile, KV head, sequence). The
 // 16 columns of the matrix products are (query token, head of the GQA group) pairs; a wave
 // holds NC column tiles (16 * NC columns = 16 * NC / G query tokens), so every K/V tile it
-// loads into registers feeds NC x 16 columns. The 4 waves take the key blocks round-robin,
-// each with its own online softmax per column, and merge through LDS one column tile at a
-// time. Causal mask: each lane masks with its own column's limit (keys at positions up to
-// the query's), and a column tile whose queries see none of a block skips it.
+// loads into registers feeds NC x 16 columns. The 4 waves take the key blocks round-robin
+// with no barrier in the loop, each with its own online softmax per column, and merge
+// through LDS one column tile at a time at the end. Causal mask: each lane masks with its
+// own column's limit (keys at positions up to the query's), and a column tile whose queries
+// see none of a block pair skips it. (Staging the tiles in LDS for all four waves measured
+// slower: the barrier per block kept the waves in lockstep.)
 //
-// Per tile and column tile the products are those of the decode kernel:
-//   S^T[16 keys][16 cols] = K_tile x Q^T   (16x16x32, d/32 steps)
-//   O^T[d][16 cols]      += V^T x P^T       (16x16x16, d/16 steps, P split in two parts)
+// A wave takes its blocks in pairs (A, B). Per pair and column tile:
+//   S_A^T, S_B^T[16 keys][16 cols] = K_tile x Q^T          (16x16x32, d/32 steps each)
+//   O^T[d][16 cols] += V^T[d][32 keys] x P^T[32 keys][16 cols]   (16x16x32, d/16 steps)
+// The 32 keys of one PV step are the lane's 4 rows of A and its 4 rows of B (the 8 k-slots
+// of lane l are tokens 4 (l/16) .. + 3 of A, then of B, in both operands), so P and V stay
+// in the lanes that produced them. On gfx950 the 16x16x32 instruction issues at the rate of
+// the 16x16x16 one with twice the work, so pairs halve the PV issue time. P is split in a
+// high and a low bf16/fp16 part as in decode.
+//
+// Each pair is loaded and then used (no second pair in flight): with NC = 2 that keeps the
+// wave at two per SIMD, and the other wave's math covers a pair's load. Measured on the
+// 30,000-token chunked prefill: this form 500 TFLOP/s; double-buffered pairs (one wave per
+// SIMD) 354; single blocks with the 16x16x16 product 460; NC = 1 (three waves per SIMD) 348;
+// NC = 4 361; tiles staged in LDS for the workgroup 290.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
     int tab = 0;
 
-    auto load = [&](KvTile<D, false>& t, int k) -> bool {
+    auto load = [&](KvTile<D, false>& t, int k) __attribute__((always_inline)) -> bool {
         int64_t phys = __builtin_amdgcn_readlane(tab, k);
         const bool ok = phys >= 0 && phys < a.num_blocks;
         phys = ok ? phys : 0;
@@ -131,46 +144,65 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
         return ok;
     };
 
-    auto compute = [&](KvTile<D, false>& t, int j, bool ok) {
-        if (!ok) return;
-        const int tok0 = j * 16 + 4 * quad;
-        if (j * 16 + 16 > n)   // rows past the sequence may hold anything
-            mask_rows<D>(t, tok0 + 0 < n, tok0 + 1 < n, tok0 + 2 < n, tok0 + 3 < n);
+    // Blocks jA and jB (ok: a valid block id) as one 32-key step; okB false for the odd last
+    // block of a wave, whose B then contributes nothing.
+    auto compute_pair = [&](const KvTile<D, false>& A, const KvTile<D, false>& B, int jA, int jB,
+                            bool okA, bool okB) __attribute__((always_inline)) {
+        const int tA = jA * 16 + 4 * quad, tB = jB * 16 + 4 * quad;
+        // V rows past the sequence may hold anything: zeroed as the operands are built
+        // (the tiles stay read-only, which keeps them in registers)
+        auto keep = [&](int t) { return (t < n ? 0x0000ffffu : 0u) | (t + 1 < n ? 0xffff0000u : 0u); };
+        const uint32_t ka0 = keep(tA), ka1 = keep(tA + 2), kb0 = keep(tB), kb1 = keep(tB + 2);
+        const int jmin = okB ? min(jA, jB) : jA;
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            if (j * 16 >= tile_lim[ct]) continue;   // no query of this column tile sees it
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            if (jmin * 16 >= tile_lim[ct]) continue;   // no query of this tile sees the pair
+            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(k_operand<T, D>(t, c), qf[ct][c], s);
-            float x[4];
+            for (int c = 0; c < NQK; ++c) {
+                sa = Mfma<T>::qk(k_operand<T, D>(A, c), qf[ct][c], sa);
+                sb = Mfma<T>::qk(k_operand<T, D>(B, c), qf[ct][c], sb);
+            }
+            float x[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = tok0 + e < lim[ct] ? s[e] * a.scale_log2 : -INFINITY;
-            const float bm = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+            for (int e = 0; e < 4; ++e) {
+                x[e] = okA && tA + e < lim[ct] ? sa[e] * a.scale_log2 : -INFINITY;
+                x[4 + e] = okB && tB + e < lim[ct] ? sb[e] * a.scale_log2 : -INFINITY;
+            }
+            const float bm = max_over_rows(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
             const bool move = bm > m[ct] + kSlack;
             if (__builtin_amdgcn_ballot_w64(move)) {
+                // a lane that keeps its reference keeps factor 1 (also one whose column has
+                // seen no key yet, where m - m would be -inf - -inf)
                 const float mn = move ? bm : m[ct];
-                const float alpha = exp2_fast(m[ct] - mn);
+                const float alpha = move ? exp2_fast(m[ct] - mn) : 1.0f;
                 lsum[ct] *= alpha;
 #pragma unroll
                 for (int c = 0; c < NPV; ++c) acc[ct][c] *= alpha;
                 m[ct] = mn;
             }
-            float pe[4];
+            float pe[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m[ct]);
-            lsum[ct] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-            uint16_t hi[4], lo[4];
+            for (int e = 0; e < 8; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m[ct]);
+            lsum[ct] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+            uint16_t hi[8], lo[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
-            const uint2 phi = make_uint2(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
-                                         uint32_t(hi[2]) | (uint32_t(hi[3]) << 16));
-            const uint2 plo = make_uint2(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
-                                         uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
+            for (int e = 0; e < 8; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
+            const uint4 phi = make_uint4(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                                         uint32_t(hi[2]) | (uint32_t(hi[3]) << 16),
+                                         uint32_t(hi[4]) | (uint32_t(hi[5]) << 16),
+                                         uint32_t(hi[6]) | (uint32_t(hi[7]) << 16));
+            const uint4 plo = make_uint4(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                                         uint32_t(lo[2]) | (uint32_t(lo[3]) << 16),
+                                         uint32_t(lo[4]) | (uint32_t(lo[5]) << 16),
+                                         uint32_t(lo[6]) | (uint32_t(lo[7]) << 16));
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
-                const uint2 vv = v_operand<T, D>(t, c);
-                acc[ct][c] = Mfma<T>::pv(vv, phi, acc[ct][c]);
-                acc[ct][c] = Mfma<T>::pv(vv, plo, acc[ct][c]);
+                const uint2 va = v_operand<T, D>(A, c), vb = v_operand<T, D>(B, c);
+                const uint4 vv = make_uint4(va.x & ka0, va.y & ka1, vb.x & kb0, vb.y & kb1);
+                acc[ct][c] = Mfma<T>::qk(vv, phi, acc[ct][c]);
+                acc[ct][c] = Mfma<T>::qk(vv, plo, acc[ct][c]);
             }
         }
     };
@@ -181,14 +213,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
     for (int k0 = 0; k0 < nmine; k0 += 64) {
         const int cnt = min(64, nmine - k0);
         tab = lane < cnt ? table[wave + (k0 + lane) * W] : 0;
-        KvTile<D, false> A, B;
-        bool okA = load(A, 0), okB;
+        // pairs (k, k + 1) of this segment, each loaded and then used; an odd last block
+        // pairs with itself, its second copy masked out
         for (int k = 0; k < cnt; k += 2) {
-            okB = load(B, min(k + 1, cnt - 1));
-            compute(A, wave + (k0 + k) * W, okA);
-            if (k + 1 >= cnt) break;
-            okA = load(A, min(k + 2, cnt - 1));
-            compute(B, wave + (k0 + k + 1) * W, okB);
+            KvTile<D, false> X0, X1;
+            const bool ox0 = load(X0, k), ox1 = load(X1, min(k + 1, cnt - 1));
+            compute_pair(X0, X1, wave + (k0 + k) * W, wave + (k0 + k + 1) * W, ox0,
+                         ox1 && k + 1 < cnt);
         }
     }
 
@@ -236,7 +267,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
 template <typename T, int D, typename OutT>
 hipError_t launch_prefill(const PrefillArgs& a, int max_q_len, int num_kv_heads, int num_seqs,
                           hipStream_t s) {
-    constexpr int NC = 4;
+    constexpr int NC = 2;
     const int qt_tokens = 16 * NC / a.group;
     const dim3 grid(unsigned((max_q_len + qt_tokens - 1) / qt_tokens), unsigned(num_kv_heads),
                     unsigned(num_seqs));
@@ -287,7 +318,7 @@ extern "C" int paged_attention_prefill(void* out, const void* q, int64_t q_strid
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
          reinterpret_cast<uintptr_t>(v_cache)) & 15)
         return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned", who);
-    const int qt_tokens = 16 * 4 / G;
+    const int qt_tokens = 16 * 2 / G;
     if ((int64_t(max_q_len) + qt_tokens - 1) / qt_tokens > 0x7fffffff)
         return fail(PKV_EINVAL, "%s: max_q_len too large", who);
     pkv::PrefillArgs a;

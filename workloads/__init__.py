@@ -62,6 +62,10 @@ class Workload:
     prefix_tokens: int = 0
     prompt_lo: int = 0
     prompt_hi: int = 0
+    # chunked prefill: a prefill_tokens-token prompt in prefill_chunks chunks, each step also
+    # decoding one token for each of `batch` users
+    prefill_tokens: int = 0
+    prefill_chunks: int = 0
     # KV cache element type ("" = dtype; "fp8" = OCP e4m3 codes of x / k_scale, x / v_scale)
     kv_dtype: str = ""
     k_scale: float = 1.0
@@ -117,6 +121,13 @@ WORKLOADS = {
     "long": Workload("long", layers=1, batch=4, num_heads=32, num_kv_heads=8, head_dim=128,
                      dtype="bf16", seed=28004, kv_std=0.5, len_lo=131072, len_hi=262144,
                      partition_size=512),
+    # Chunked prefill ("Yerel LLM ...", section "4. Prefill ve decode": a 30,000-token
+    # document summary arriving among 20 streaming users; chunked, each step computes one
+    # prefill chunk and one decode token per user, 1/8 of the prompt per step in the
+    # page's diagram), on the 8B shape; the users' contexts as in the 8B workload.
+    "prefill_30k": Workload("prefill_30k", layers=32, batch=20, num_heads=32, num_kv_heads=8,
+                            head_dim=128, dtype="bf16", seed=28006, len_lo=128, len_hi=2048,
+                            prefill_tokens=30000, prefill_chunks=8),
     # Continuous-batching churn on the 8B shape with a ~200 GB pool.
     "churn": Workload("churn", layers=32, batch=256, num_heads=32, num_kv_heads=8,
                       head_dim=128, dtype="bf16", seed=28005, pool_bytes=200e9,
