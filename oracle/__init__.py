@@ -61,22 +61,22 @@ def lib():
         L.oracle_fp8_quantize.restype = None
         L.oracle_fp8_encode.argtypes = [P, P, I64]
         L.oracle_fp8_encode.restype = None
-        L.oracle_gather.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I64, I32, D, D]
+        L.oracle_gather.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I64, I32, D, D, I32]
         L.oracle_gather.restype = ctypes.c_int
         L.oracle_decode.argtypes = [P, P, I32, P, I64, P, P, P, P, I32, I32, I32, I32, I32,
-                                    I64, D, I32, I32, D, D, I32]
+                                    I64, D, I32, I32, D, D, I32, I32]
         L.oracle_decode.restype = ctypes.c_int
         L.oracle_decode_partitions.argtypes = [P, P, P, P, I32, P, I64, P, P, P, P, I32, I32,
                                                I32, I32, I32, I64, D, I32, I32, D, D, I32, I32,
-                                               I32]
+                                               I32, I32]
         L.oracle_decode_partitions.restype = ctypes.c_int
         L.oracle_prefill.argtypes = [P, P, I32, P, I64, P, P, P, P, P, I32, I32, I32, I32, I32,
-                                     I64, D, I32, I32, D, D, I32]
+                                     I64, D, I32, I32, D, D, I32, I32]
         L.oracle_prefill.restype = ctypes.c_int
         L.oracle_merge.argtypes = [P, P, P, P, P, I32, I32, I32]
         L.oracle_merge.restype = None
         L.oracle_cache_write.argtypes = [P, P, P, P, P, I32, I32, I32, I64, I64, I64, I32, I32,
-                                         F, F]
+                                         F, F, I32]
         L.oracle_cache_write.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -85,6 +85,11 @@ def lib():
 def _ptr(a: np.ndarray):
     assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def block_size_of(v_cache) -> int:
+    """Tokens per block of a cache in the documented layout: V is [nb][Hkv][d][BS]."""
+    return int(v_cache.shape[3])
 
 
 def raw(x) -> np.ndarray:
@@ -150,7 +155,8 @@ def gather(k_cache, v_cache, table_row, t0: int, t1: int, g: int, num_kv_heads: 
     V = np.empty_like(K)
     nb = kc.shape[0]
     rc = lib().oracle_gather(_ptr(K), _ptr(V), _ptr(kc), _ptr(vc), _ptr(tr), t0, t1, g,
-                             num_kv_heads, head_dim, nb, DTYPE_CODE[dtype], k_scale, v_scale)
+                             num_kv_heads, head_dim, nb, DTYPE_CODE[dtype], k_scale, v_scale,
+                             block_size_of(vc))
     if rc != 0:
         raise ValueError("block table points outside the pool")
     return K, V
@@ -182,7 +188,8 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype: str
     rc = lib().oracle_decode(_ptr(out), None if r is None else _ptr(r), nr, _ptr(qa), Hq * d,
                              _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Hq, Hkv, d,
                              bt.shape[1], kc.shape[0], scale, DTYPE_CODE[dtype],
-                             DTYPE_CODE[kv_dtype or dtype], k_scale, v_scale, nthreads)
+                             DTYPE_CODE[kv_dtype or dtype], k_scale, v_scale, nthreads,
+                             block_size_of(vc))
     if rc != 0:
         raise ValueError("oracle_decode: bad arguments")
     return out.reshape(B, Hq, d) if r is None else out
@@ -206,7 +213,7 @@ def decode_partitions(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
         _ptr(o), _ptr(m), _ptr(l), None if r is None else _ptr(r), nr, _ptr(qa), Hq * d,
         _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Hq, Hkv, d, bt.shape[1], kc.shape[0], scale,
         DTYPE_CODE[dtype], DTYPE_CODE[kv_dtype or dtype], k_scale, v_scale, partition_size,
-        max_partitions, nthreads)
+        max_partitions, nthreads, block_size_of(vc))
     if rc != 0:
         raise ValueError("oracle_decode_partitions: bad arguments")
     return o, m, l
@@ -232,7 +239,8 @@ def prefill(q, q_start, k_cache, v_cache, block_tables, seq_lens, scale: float, 
     rc = lib().oracle_prefill(_ptr(out), None if r is None else _ptr(r), nr, _ptr(qa), Hq * d,
                               _ptr(qs), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Hq, Hkv, d,
                               bt.shape[1], kc.shape[0], scale, DTYPE_CODE[dtype],
-                              DTYPE_CODE[kv_dtype or dtype], k_scale, v_scale, nthreads)
+                              DTYPE_CODE[kv_dtype or dtype], k_scale, v_scale, nthreads,
+                              block_size_of(vc))
     if rc != 0:
         raise ValueError("oracle_prefill: bad arguments")
     return out.reshape(T, Hq, d) if r is None else out
@@ -261,22 +269,23 @@ def cache_write(key, value, k_cache: np.ndarray, v_cache: np.ndarray, slot_mappi
     rc = lib().oracle_cache_write(_ptr(ka), _ptr(va), _ptr(k_cache), _ptr(v_cache), _ptr(sm),
                                   T, Hkv, d, k_cache.shape[0], Hkv * d, Hkv * d,
                                   DTYPE_CODE[dtype], DTYPE_CODE[cache_dtype or dtype], k_scale,
-                                  v_scale)
+                                  v_scale, block_size_of(v_cache))
     if rc != 0:
         raise ValueError("slot outside the pool")
 
 
-def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
+def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
+                 block_size: int = 16):
     """Shapes of the K and V caches in the documented layout (x = 16 / element bytes)."""
     x = 16 // {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[dtype]
-    return ((num_blocks, num_kv_heads, head_dim // x, 16, x),
-            (num_blocks, num_kv_heads, head_dim, 16))
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+            (num_blocks, num_kv_heads, head_dim, block_size))
 
 
 def empty_caches(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
-                 fill_nan: bool = True):
+                 fill_nan: bool = True, block_size: int = 16):
     """Host caches of raw storage, every element NaN (so unwritten slots poison reads)."""
-    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, dtype)
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, dtype, block_size)
     if dtype == "f32":
         kc = np.full(ks, np.nan if fill_nan else 0, dtype=np.float32)
         vc = np.full(vs, np.nan if fill_nan else 0, dtype=np.float32)

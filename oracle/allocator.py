@@ -73,13 +73,14 @@ class PoolError(Exception):
 
 
 class PoolModel:
-    def __init__(self, num_blocks: int, free_order=None):
-        if num_blocks <= 0:
-            raise PoolError("EINVAL", "num_blocks must be positive")
+    def __init__(self, num_blocks: int, free_order=None, block_size: int = BLOCK_SIZE):
+        if num_blocks <= 0 or block_size <= 0:
+            raise PoolError("EINVAL", "num_blocks and block_size must be positive")
         order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
         if sorted(order) != list(range(num_blocks)):
             raise PoolError("EINVAL", "free_order must be a permutation of 0..num_blocks-1")
         self.num_blocks = num_blocks
+        self.bs = block_size
         self.free = deque(order)
         self.ref = [0] * num_blocks
         self.seqs: dict[int, list] = {}   # seq_id -> [blocks, length]
@@ -115,15 +116,15 @@ class PoolModel:
         self.add_seq(sid, salt)
         prompt = [int(t) for t in prompt]
         blocks, n = [], 0
-        while n + BLOCK_SIZE <= len(prompt) - 1:
-            blk = self.cache.get((salt, tuple(prompt[:n + BLOCK_SIZE])))
+        while n + self.bs <= len(prompt) - 1:
+            blk = self.cache.get((salt, tuple(prompt[:n + self.bs])))
             if blk is None:
                 break
             if self.ref[blk] == 0:
                 self.free.remove(blk)
             self.ref[blk] += 1
             blocks.append(blk)
-            n += BLOCK_SIZE
+            n += self.bs
         self.hits += len(blocks)
         self.seqs[sid] = [blocks, n]
         self.tokens[sid] = prompt[:n]
@@ -149,9 +150,9 @@ class PoolModel:
     def share_prefix(self, sid: int, src: int, n_tokens: int) -> None:
         """Alias the first n_tokens (a multiple of 16) of src's table into empty sid."""
         dst, s = self._seq(sid), self._seq(src)
-        if dst[1] != 0 or n_tokens < 0 or n_tokens % BLOCK_SIZE or n_tokens > s[1]:
+        if dst[1] != 0 or n_tokens < 0 or n_tokens % self.bs or n_tokens > s[1]:
             raise PoolError("EINVAL", "bad prefix share")
-        nb = n_tokens // BLOCK_SIZE
+        nb = n_tokens // self.bs
         for blk in s[0][:nb]:
             self.ref[blk] += 1
         dst[0] = list(s[0][:nb])
@@ -160,7 +161,7 @@ class PoolModel:
 
     def _shared_tail(self, s) -> bool:
         blocks, length = s
-        return length % BLOCK_SIZE != 0 and self.ref[blocks[-1]] > 1
+        return length % self.bs != 0 and self.ref[blocks[-1]] > 1
 
     def _append(self, sid: int, n_tokens: int, token_ids):
         s = self._seq(sid)
@@ -168,7 +169,7 @@ class PoolModel:
             raise PoolError("EINVAL", "negative token count")
         blocks, length = s
         cow = n_tokens > 0 and self._shared_tail(s)
-        need = -(-(length + n_tokens) // BLOCK_SIZE) - len(blocks) + int(cow)
+        need = -(-(length + n_tokens) // self.bs) - len(blocks) + int(cow)
         if need > len(self.free):
             self.alloc_failures += 1
             raise PoolError("ENOMEM", f"need {need} blocks, {len(self.free)} free")
@@ -180,11 +181,11 @@ class PoolModel:
             self.ref[old] -= 1       # others still reference it (ref was > 1)
             blocks[-1] = new
             pair = (old, new)
-        while len(blocks) * BLOCK_SIZE < length + n_tokens:
+        while len(blocks) * self.bs < length + n_tokens:
             blk = self._pop_free()
             self.ref[blk] = 1
             blocks.append(blk)
-        slots = [blocks[pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE
+        slots = [blocks[pos // self.bs] * self.bs + pos % self.bs
                  for pos in range(length, length + n_tokens)]
         s[1] = length + n_tokens
         toks = self.tokens[sid]
@@ -192,8 +193,8 @@ class PoolModel:
             self.tokens[sid] = None
         else:
             toks.extend(int(t) for t in token_ids)
-            for j in range(length // BLOCK_SIZE, s[1] // BLOCK_SIZE):   # blocks now full
-                key = (self.salt[sid], tuple(toks[:(j + 1) * BLOCK_SIZE]))
+            for j in range(length // self.bs, s[1] // self.bs):   # blocks now full
+                key = (self.salt[sid], tuple(toks[:(j + 1) * self.bs]))
                 blk = blocks[j]
                 if key not in self.cache and blk not in self.key_of:
                     self.cache[key] = blk
@@ -225,7 +226,7 @@ class PoolModel:
         need = 0
         for sid in sids:
             blocks, length = self._seq(sid)
-            if length % BLOCK_SIZE == 0:
+            if length % self.bs == 0:
                 need += 1
             elif ref[blocks[-1]] > 1:
                 ref[blocks[-1]] -= 1

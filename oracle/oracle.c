@@ -42,12 +42,15 @@
  *   code of the finite e4m3 value nearest to v, ties to the even code; so |v| > 448
  *   (infinities included) saturates to +-448.  NaN gives S.1111.111.
  *
- * Cache layout (the pages leave it open; this is the layout the library documents):
+ * Cache layout (the pages leave it open; this is the layout the library documents), for
+ * blocks of BS tokens (16 by default; 8 and 32 as the block-size variants: "vLLM ve
+ * Triton ...", the paragraph calling block size a tuning knob):
  *   x = 16 / element_bytes (16 for fp8, 8 for fp16/bf16, 4 for fp32)
- *   K: [num_blocks][Hkv][d / x][16][x]   element (blk, g, t, i) at
- *        (((blk * Hkv + g) * (d / x) + i / x) * 16 + t) * x + i % x
- *   V: [num_blocks][Hkv][d][16]          element (blk, g, t, i) at
- *        ((blk * Hkv + g) * d + i) * 16 + t
+ *   K: [num_blocks][Hkv][d / x][BS][x]   element (blk, g, t, i) at
+ *        (((blk * Hkv + g) * (d / x) + i / x) * BS + t) * x + i % x
+ *   V: [num_blocks][Hkv][d][BS]          element (blk, g, t, i) at
+ *        ((blk * Hkv + g) * d + i) * BS + t
+ *   Token t of a sequence lives in block table[t / BS], row t % BS.
  *   key/value rows: element (t, g, i) at t * row_stride + g * d + i
  *   q:              element (b, h, i) at b * q_stride + h * d + i
  *
@@ -62,7 +65,6 @@
 #endif
 
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_FP8 = 3 };
-#define OR_BS 16
 
 /* IEEE 754 binary16 -> binary64, from the format's definition:
  * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
@@ -126,11 +128,11 @@ static double elem(const void* base, int64_t idx, int dtype) {
 
 static int elem_bytes(int dtype) { return dtype == OR_F32 ? 4 : dtype == OR_FP8 ? 1 : 2; }
 
-static int64_t k_off(int64_t blk, int g, int t, int i, int Hkv, int d, int x) {
-    return (((blk * Hkv + g) * (d / x) + i / x) * OR_BS + t) * x + i % x;
+static int64_t k_off(int64_t blk, int g, int t, int i, int Hkv, int d, int x, int bs) {
+    return (((blk * Hkv + g) * (d / x) + i / x) * bs + t) * x + i % x;
 }
-static int64_t v_off(int64_t blk, int g, int t, int i, int Hkv, int d) {
-    return ((blk * Hkv + g) * d + i) * OR_BS + t;
+static int64_t v_off(int64_t blk, int g, int t, int i, int Hkv, int d, int bs) {
+    return ((blk * Hkv + g) * d + i) * bs + t;
 }
 
 /* Element-wise widening, exported so tests can pin the conversions. */
@@ -194,15 +196,15 @@ void oracle_attend(double* o, double* m_out, double* l_out, const double* q,
 int oracle_gather(double* K, double* V, const void* k_cache, const void* v_cache,
                   const int32_t* table_row, int64_t t0, int64_t t1, int32_t g,
                   int32_t Hkv, int32_t d, int64_t num_blocks, int32_t dtype,
-                  double k_scale, double v_scale) {
+                  double k_scale, double v_scale, int32_t bs) {
     int x = 16 / elem_bytes(dtype);
     for (int64_t t = t0; t < t1; ++t) {
-        int64_t blk = table_row[t / OR_BS];
-        int off = (int)(t % OR_BS);
+        int64_t blk = table_row[t / bs];
+        int off = (int)(t % bs);
         if (blk < 0 || blk >= num_blocks) return -1;
         for (int i = 0; i < d; ++i) {
-            K[(t - t0) * d + i] = elem(k_cache, k_off(blk, g, off, i, Hkv, d, x), dtype) * k_scale;
-            V[(t - t0) * d + i] = elem(v_cache, v_off(blk, g, off, i, Hkv, d), dtype) * v_scale;
+            K[(t - t0) * d + i] = elem(k_cache, k_off(blk, g, off, i, Hkv, d, x, bs), dtype) * k_scale;
+            V[(t - t0) * d + i] = elem(v_cache, v_off(blk, g, off, i, Hkv, d, bs), dtype) * v_scale;
         }
     }
     return 0;
@@ -217,7 +219,8 @@ static int decode_core(double* o, double* m, double* l, const int32_t* rows, int
                        const int32_t* tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
                        int32_t Hkv, int32_t d, int32_t max_blocks, int64_t num_blocks,
                        double scale, int32_t q_dtype, int32_t kv_dtype, double k_scale,
-                       double v_scale, int32_t part, int32_t max_parts, int32_t nthreads) {
+                       double v_scale, int32_t part, int32_t max_parts, int32_t nthreads,
+                       int32_t bs) {
     if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || (d % (16 / elem_bytes(kv_dtype))) != 0) return -1;
     if (q_dtype == OR_FP8) return -1;
     int G = Hq / Hkv;
@@ -233,7 +236,7 @@ static int decode_core(double* o, double* m, double* l, const int32_t* rows, int
         if (b < 0 || b >= B || h < 0 || h >= Hq) { bad |= 1; continue; }
         int g = h / G;
         int64_t n = seq_lens[b];
-        if (n > (int64_t)max_blocks * OR_BS) { bad |= 1; continue; }
+        if (n > (int64_t)max_blocks * bs) { bad |= 1; continue; }
         int64_t P = part > 0 ? part : (n > 0 ? n : 1);
         int64_t np = n > 0 ? (n + P - 1) / P : 0;
         int nslots = part > 0 ? max_parts : 1;
@@ -249,7 +252,7 @@ static int decode_core(double* o, double* m, double* l, const int32_t* rows, int
                 double* V = (double*)malloc(sizeof(double) * (size_t)((t1 - t0) * d));
                 if (oracle_gather(K, V, k_cache, v_cache, tables + (int64_t)b * max_blocks,
                                   t0, t1, g, Hkv, d, num_blocks, kv_dtype, k_scale,
-                                  v_scale) != 0) bad |= 1;
+                                  v_scale, bs) != 0) bad |= 1;
                 oracle_attend(op, &mp, &lp, qq, K, V, t1 - t0, d, scale);
                 free(K);
                 free(V);
@@ -270,10 +273,10 @@ int oracle_decode(double* out, const int32_t* rows, int32_t n_rows, const void* 
                   const int32_t* tables, const int32_t* seq_lens, int32_t B, int32_t Hq,
                   int32_t Hkv, int32_t d, int32_t max_blocks, int64_t num_blocks,
                   double scale, int32_t q_dtype, int32_t kv_dtype, double k_scale,
-                  double v_scale, int32_t nthreads) {
+                  double v_scale, int32_t nthreads, int32_t bs) {
     return decode_core(out, NULL, NULL, rows, n_rows, q, q_stride, k_cache, v_cache, tables,
                        seq_lens, B, Hq, Hkv, d, max_blocks, num_blocks, scale, q_dtype,
-                       kv_dtype, k_scale, v_scale, 0, 1, nthreads);
+                       kv_dtype, k_scale, v_scale, 0, 1, nthreads, bs);
 }
 
 /* Per-partition results: o[r][max_parts][d], m[r][max_parts], l[r][max_parts];
@@ -284,11 +287,11 @@ int oracle_decode_partitions(double* o, double* m, double* l, const int32_t* row
                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                              int32_t d, int32_t max_blocks, int64_t num_blocks, double scale,
                              int32_t q_dtype, int32_t kv_dtype, double k_scale, double v_scale,
-                             int32_t part, int32_t max_parts, int32_t nthreads) {
+                             int32_t part, int32_t max_parts, int32_t nthreads, int32_t bs) {
     if (part <= 0 || max_parts <= 0) return -1;
     return decode_core(o, m, l, rows, n_rows, q, q_stride, k_cache, v_cache, tables, seq_lens,
                        B, Hq, Hkv, d, max_blocks, num_blocks, scale, q_dtype, kv_dtype,
-                       k_scale, v_scale, part, max_parts, nthreads);
+                       k_scale, v_scale, part, max_parts, nthreads, bs);
 }
 
 /* Multi-query (chunked prefill) attention ("vLLM Nedir? ...", section "Chunked prefill";
@@ -305,8 +308,8 @@ int oracle_prefill(double* out, const int32_t* rows, int32_t n_rows, const void*
                    const void* v_cache, const int32_t* tables, const int32_t* seq_lens,
                    int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t max_blocks,
                    int64_t num_blocks, double scale, int32_t q_dtype, int32_t kv_dtype,
-                   double k_scale, double v_scale, int32_t nthreads) {
-    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || q_dtype == OR_FP8) return -1;
+                   double k_scale, double v_scale, int32_t nthreads, int32_t bs) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || q_dtype == OR_FP8 || bs <= 0) return -1;
     int G = Hq / Hkv;
     int64_t total_q = q_start[B];
     int64_t total = rows ? n_rows : total_q * Hq;
@@ -324,7 +327,7 @@ int oracle_prefill(double* out, const int32_t* rows, int32_t n_rows, const void*
         while (b < B && q_start[b + 1] <= r) ++b;           /* the sequence of row r */
         int64_t L = q_start[b + 1] - q_start[b], n = seq_lens[b];
         int64_t pos = n - L + (r - q_start[b]);
-        if (n > (int64_t)max_blocks * OR_BS) { bad |= 1; continue; }
+        if (n > (int64_t)max_blocks * bs) { bad |= 1; continue; }
         if (pos < 0) {
             for (int i = 0; i < d; ++i) o[i] = 0.0;
             continue;
@@ -334,7 +337,7 @@ int oracle_prefill(double* out, const int32_t* rows, int32_t n_rows, const void*
         double* V = (double*)malloc(sizeof(double) * (size_t)((pos + 1) * d));
         for (int i = 0; i < d; ++i) qq[i] = elem(q, r * q_stride + (int64_t)h * d + i, q_dtype);
         if (oracle_gather(K, V, k_cache, v_cache, tables + (int64_t)b * max_blocks, 0, pos + 1,
-                          h / G, Hkv, d, num_blocks, kv_dtype, k_scale, v_scale) != 0)
+                          h / G, Hkv, d, num_blocks, kv_dtype, k_scale, v_scale, bs) != 0)
             bad |= 1;
         oracle_attend(o, NULL, NULL, qq, K, V, pos + 1, d, scale);
         free(qq);
@@ -373,22 +376,24 @@ void oracle_merge(double* out, const double* o, const double* m, const double* l
 int oracle_cache_write(const void* key, const void* value, void* k_cache, void* v_cache,
                        const int32_t* slot_mapping, int32_t num_tokens, int32_t Hkv, int32_t d,
                        int64_t num_blocks, int64_t key_stride, int64_t value_stride,
-                       int32_t dtype, int32_t cache_dtype, float k_scale, float v_scale) {
+                       int32_t dtype, int32_t cache_dtype, float k_scale, float v_scale,
+                       int32_t bs) {
     int e = elem_bytes(dtype), ce = elem_bytes(cache_dtype), x = 16 / ce;
     if (cache_dtype != dtype && (cache_dtype != OR_FP8 || dtype == OR_FP8)) return -1;
+    if (bs <= 0) return -1;
     for (int t = 0; t < num_tokens; ++t)
-        if ((int64_t)slot_mapping[t] >= num_blocks * OR_BS) return -1;
+        if ((int64_t)slot_mapping[t] >= num_blocks * bs) return -1;
     for (int t = 0; t < num_tokens; ++t) {
         int64_t s = slot_mapping[t];
         if (s < 0) continue;
-        int64_t blk = s / OR_BS;
-        int off = (int)(s % OR_BS);
+        int64_t blk = s / bs;
+        int off = (int)(s % bs);
         for (int g = 0; g < Hkv; ++g)
             for (int i = 0; i < d; ++i) {
                 const char* ksrc = (const char*)key + (t * key_stride + (int64_t)g * d + i) * e;
                 const char* vsrc = (const char*)value + (t * value_stride + (int64_t)g * d + i) * e;
-                char* kdst = (char*)k_cache + k_off(blk, g, off, i, Hkv, d, x) * ce;
-                char* vdst = (char*)v_cache + v_off(blk, g, off, i, Hkv, d) * ce;
+                char* kdst = (char*)k_cache + k_off(blk, g, off, i, Hkv, d, x, bs) * ce;
+                char* vdst = (char*)v_cache + v_off(blk, g, off, i, Hkv, d, bs) * ce;
                 if (cache_dtype == OR_FP8) {
                     oracle_fp8_quantize((uint8_t*)kdst, ksrc, 1, dtype, k_scale);
                     oracle_fp8_quantize((uint8_t*)vdst, vsrc, 1, dtype, v_scale);

@@ -61,8 +61,9 @@ def build(w: workloads.Workload, lens=None, seed_stream: int = 0, num_blocks: in
     lens = (workloads.draw_seq_lens(w, workloads.rng(w.seed, 0, seed_stream))
             if lens is None else np.asarray(lens, dtype=np.int64))
     B = len(lens)
+    bs = w.block_size
     if num_blocks is None:
-        num_blocks = w.num_blocks or workloads.pool_blocks_for(lens)
+        num_blocks = w.num_blocks or workloads.pool_blocks_for(lens, block_size=bs)
     free_order = workloads.draw_free_order(num_blocks, gen)
     n_prompt = np.maximum(lens - 1, 0)
     prompt_k = workloads.draw_tokens(int(n_prompt.sum()), w, gen)
@@ -71,7 +72,7 @@ def build(w: workloads.Workload, lens=None, seed_stream: int = 0, num_blocks: in
     new_v = workloads.draw_tokens(B, w, gen)
     q = workloads.draw_q(w, gen, batch=B)
 
-    pool = oracle.PoolModel(num_blocks, free_order)
+    pool = oracle.PoolModel(num_blocks, free_order, block_size=bs)
     prompt_slots, new_slots = [], []
     for b in range(B):
         pool.add_seq(b)
@@ -82,11 +83,12 @@ def build(w: workloads.Workload, lens=None, seed_stream: int = 0, num_blocks: in
         else:
             new_slots.append(-1)       # an empty sequence writes nothing
     if max_blocks is None:
-        max_blocks = max(1, int(max(-(-int(n) // 16) for n in lens)))
+        max_blocks = max(1, int(max(-(-int(n) // bs) for n in lens)))
     tables, tl = pool.tables(list(range(B)), max_blocks)
     assert np.array_equal(tl, lens)
 
-    kc, vc = oracle.empty_caches(num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype)
+    kc, vc = oracle.empty_caches(num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype,
+                                 block_size=bs)
     ps = np.asarray(prompt_slots, dtype=np.int32)
     ns = np.asarray(new_slots, dtype=np.int32)
     cw = dict(cache_dtype=w.cache_dtype, k_scale=w.k_scale, v_scale=w.v_scale)

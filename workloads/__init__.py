@@ -66,6 +66,8 @@ class Workload:
     # decoding one token for each of `batch` users
     prefill_tokens: int = 0
     prefill_chunks: int = 0
+    # tokens per KV block (16; 8 and 32 are the block-size variants)
+    block_size: int = 16
     # KV cache element type ("" = dtype; "fp8" = OCP e4m3 codes of x / k_scale, x / v_scale)
     kv_dtype: str = ""
     k_scale: float = 1.0
@@ -94,7 +96,7 @@ class Workload:
     @property
     def block_bytes_per_layer(self) -> int:
         """Bytes of one physical block (K and V, all KV heads) in one layer."""
-        return 2 * self.num_kv_heads * BLOCK_SIZE * self.head_dim * self.cache_elem_bytes
+        return 2 * self.num_kv_heads * self.block_size * self.head_dim * self.cache_elem_bytes
 
 
 WORKLOADS = {
@@ -218,10 +220,11 @@ def draw_q_device(w: Workload, stream, device, batch: int | None = None):
     return x.to({"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype])
 
 
-def pool_blocks_for(lens, growth_tokens: int = 0, slack: float = 0.10) -> int:
+def pool_blocks_for(lens, growth_tokens: int = 0, slack: float = 0.10,
+                    block_size: int = BLOCK_SIZE) -> int:
     """Pool size (blocks) that holds every sequence plus growth_tokens more each,
     plus a slack fraction of unused blocks."""
-    need = sum(-(-(int(n) + growth_tokens) // BLOCK_SIZE) for n in lens)
+    need = sum(-(-(int(n) + growth_tokens) // block_size) for n in lens)
     return int(need * (1.0 + slack)) + 1
 
 
