@@ -2,7 +2,8 @@
  * pkv.h - C ABI of the paged KV cache decode library (libpkv.so) for AMD MI355X (gfx950).
  *
  * The library implements the decode hot path of PagedAttention:
- *   - a host-side block pool: fixed 16-token KV blocks, a per-sequence block table,
+ *   - a host-side block pool: fixed-size KV blocks (8, 16 or 32 tokens), a per-sequence
+ *     block table,
  *     on-demand allocation, a free queue and reference-counted sharing
  *     ("vLLM ve Triton ile maliyet optimizasyonu", §03 Yöntem, steps 1-3 and the
  *     paragraph on sharing; "vLLM Nedir? PagedAttention ile Production LLM Serving",
@@ -26,16 +27,20 @@
  *     break a precondition are unspecified.
  *   - The pool object is not thread-safe; use one per thread or lock around it.
  *
- * Cache layout (per layer; the pages do not fix one). x = 16 / element_bytes,
- * i.e. 16 for an FP8 cache, 8 for fp16/bf16 and 4 for fp32:
- *   k_cache: [num_blocks][num_kv_heads][head_dim / x][16][x]
- *   v_cache: [num_blocks][num_kv_heads][head_dim][16]
- * Token t of a sequence lives in physical block table[t / 16], row t % 16. One
- * (block, KV head) tile of K or V is one contiguous run of 16 * head_dim elements;
- * K keeps 16-byte groups of x dimensions per token together, V keeps the 16 tokens
+ * Cache layout (per layer; the pages do not fix one). BS = block_size, the tokens per
+ * block: 16 (the pages' figure, "vLLM ve Triton ile maliyet optimizasyonu", §03 Yöntem,
+ * step 1), 8 or 32. x = 16 / element_bytes, i.e. 16 for an FP8 cache, 8 for fp16/bf16
+ * and 4 for fp32:
+ *   k_cache: [num_blocks][num_kv_heads][head_dim / x][BS][x]
+ *   v_cache: [num_blocks][num_kv_heads][head_dim][BS]
+ * Token t of a sequence lives in physical block table[t / BS], row t % BS. One
+ * (block, KV head) tile of K or V is one contiguous run of BS * head_dim elements;
+ * K keeps 16-byte groups of x dimensions per token together, V keeps the BS tokens
  * of each dimension together. Both match the operand layout of the gfx950 matrix
- * instructions, so the decode kernel loads tiles straight into registers.
- * A slot is physical_block * 16 + row.
+ * instructions, so the kernels load tiles straight into registers; they walk the
+ * context in 16-token tiles, one block, half a block (BS = 32) or two blocks (BS = 8).
+ * A slot is physical_block * BS + row. Every call that takes block_size accepts 8, 16
+ * or 32 (EINVAL otherwise); the caches, tables and slots passed must use that size.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -63,6 +68,7 @@ extern "C" {
  * kv_bytes_per_token, kv_pool_create and the *_fp8 entry points below. */
 #define PKV_FP8_E4M3 3
 
+/* the default block size (tokens per block) */
 #define PKV_BLOCK_SIZE 16
 
 /* partition_size value asking paged_attention_decode for the balanced split */
@@ -118,7 +124,7 @@ typedef struct {
     int64_t prefix_hit_blocks; /* blocks found by kv_pool_add_seq_prefix so far */
 } kv_pool_stats_t;
 
-/* Create a pool of num_blocks physical blocks of block_size (must be 16) tokens for
+/* Create a pool of num_blocks physical blocks of block_size (8, 16 or 32) tokens for
  * a model with num_layers layers, num_kv_heads KV heads of head_dim elements of
  * type dtype. One block id addresses the same block in every layer's cache.
  *   free_order: NULL for 0, 1, ..., num_blocks-1, else a permutation of those ids
@@ -126,7 +132,8 @@ typedef struct {
  * The pool holds no device memory: the caller reserves the caches up front (for
  * each layer one K and one V buffer of kv_pool_cache_shape() elements), which is
  * the one-time reservation of "Yerel LLM ...", section "3. VRAM fragmantasyonu".
- * Errors: EINVAL (sizes, block_size != 16, dtype, not a permutation). */
+ * Errors: EINVAL (sizes, block_size, num_blocks * block_size above INT32_MAX, dtype,
+ * not a permutation). */
 int kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t num_layers,
                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                    const int32_t* free_order, kv_pool** out);
@@ -147,7 +154,7 @@ int kv_pool_add_seq(kv_pool* pool, int64_t seq_id);
  * pointing its table at the same physical blocks (reference count + 1 each), as for
  * a shared system prompt or parallel samples ("vLLM Nedir? ...", section
  * "PagedAttention", on block sharing; §03 on sharing). n_tokens must be a multiple
- * of 16 and at most src's length, so a shared block is full and never written again
+ * of the block size and at most src's length, so a shared block is full and never written again
  * (copy-on-write of partly filled shared blocks is not provided).
  * Errors: ENOENT (unknown id), EINVAL (seq not empty, n_tokens not allowed). */
 int kv_pool_share_prefix(kv_pool* pool, int64_t seq_id, int64_t src_seq_id, int32_t n_tokens);
@@ -158,7 +165,7 @@ int kv_pool_share_prefix(kv_pool* pool, int64_t seq_id, int64_t src_seq_id, int3
  * Every full block of a sequence whose token ids are all known (kv_pool_add_seq_prefix,
  * kv_pool_append_tokens, kv_pool_append_batch_tokens; kv_pool_add_seq counts as an empty
  * prompt with salt 0) gets a key: a 64-bit hash chain over the salt and the token ids of
- * the blocks up to it, with the block's own 16 ids and its parent's chain hash kept to
+ * the blocks up to it, with the block's own token ids and its parent's chain hash kept to
  * check a hit. Only the first block with a given key holds it. A block freed to the free
  * queue keeps its key until it is popped for a new use (the free queue is the eviction
  * order); a hit on a free block takes it out of the queue. kv_pool_append,
@@ -166,9 +173,9 @@ int kv_pool_share_prefix(kv_pool* pool, int64_t seq_id, int64_t src_seq_id, int3
  * later blocks get no key. */
 
 /* Register seq_id with the longest run of cached blocks that starts its prompt: block j
- * (tokens 16j .. 16j + 15) is looked up while it ends before the prompt's last token, so
- * at least one prompt token is always left to compute; the walk stops at the first miss.
- * *n_cached_out = 16 x the blocks found (their reference counts + 1). The caller then
+ * (tokens BS j .. BS j + BS - 1) is looked up while it ends before the prompt's last
+ * token, so at least one prompt token is always left to compute; the walk stops at the
+ * first miss. *n_cached_out = BS x the blocks found (their reference counts + 1). The caller then
  * appends prompt[*n_cached_out ..] with kv_pool_append_tokens and writes only their K/V.
  * salt: blocks are found only under the salt they were stored with (tenant isolation).
  * Errors: EINVAL (seq_id live, n_prompt < 0, NULLs). */
@@ -254,17 +261,17 @@ int kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
 /* ==== device kernels ========================================================== */
 
 /* reshape_and_cache: for every token t in [0, num_tokens) with s = slot_mapping[t]
- * in [0, num_blocks * 16), copy the raw bits of key[t][g][:] and value[t][g][:] for
- * every KV head g into row s % 16 of block s / 16 of k_cache / v_cache (layout
+ * in [0, num_blocks * BS), copy the raw bits of key[t][g][:] and value[t][g][:] for
+ * every KV head g into row s % BS of block s / BS of k_cache / v_cache (layout
  * above). Tokens with a negative slot are skipped. Nothing else is written. This is
  * how a new token's K/V enter the block that on-demand allocation gave it (§03
  * step 3). Duplicate slots in one call are a caller error (which write wins is
- * unspecified); slots at or past num_blocks * 16 are ignored.
+ * unspecified); slots at or past num_blocks * BS are ignored.
  *   key, value:   device, dtype, element (t, g, i) at t * key_stride + g * head_dim + i
  *                 (resp. value_stride); 16-byte aligned, strides multiples of x.
  *   slot_mapping: device int32 [num_tokens].
  *   dtype: PKV_F32, PKV_F16 or PKV_BF16 (a bit copy: the type only sets the size).
- * Errors: EINVAL (nulls, alignment, block_size != 16, head_dim not a positive
+ * Errors: EINVAL (nulls, alignment, block_size, head_dim not a positive
  * multiple of x, sizes), EHIP. num_tokens == 0 is a no-op. */
 int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                       const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
@@ -284,7 +291,7 @@ int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v
  *                 q_stride elements (>= num_heads * head_dim, multiple of x).
  *   k_cache/v_cache: device, layout above, num_blocks blocks, in_dtype.
  *   block_tables: device int32 [num_seqs][max_blocks_per_seq]; entries past
- *                 ceil(n / 16) are not read. seq_lens: device int32 [num_seqs].
+ *                 ceil(n / BS) are not read. seq_lens: device int32 [num_seqs].
  *   out:          device [num_seqs][num_heads][head_dim], out_dtype (in_dtype or
  *                 PKV_F32), written with round-to-nearest-even.
  *   partition_size == 0: one pass over the whole context; part_* may be NULL.
@@ -299,23 +306,26 @@ int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v
  *                   part_sum[b][h][p]    = sum of exp(s_t - m_p) over the partition,
  *                 so that part_max + log(part_sum) is the partition's log-sum-exp;
  *   partition_size == PKV_PARTITION_AUTO (fp16/bf16, num_seqs <= 1024): balanced
- *                 split. All (sequence, KV head, block) tiles form one list that is cut
- *                 into equal runs, one per wave of the launch, so ragged lengths do
- *                 not leave the device idle. A (sequence, KV head) whose blocks all fall
+ *                 split. All (sequence, KV head, 16-token tile) triples form one list
+ *                 that is cut into equal runs, one per wave of the launch, so ragged
+ *                 lengths do not leave the device idle. A (sequence, KV head) whose tiles
+ *                 all fall
  *                 in one run writes out; otherwise each run's share ("piece" k) writes
  *                 part_out/part_max/part_sum at index k as above. Pieces per (b, h) stay
  *                 <= max_partitions (>= 2 required): each run spans at least
- *                 ceil(max_blocks_per_seq / (max_partitions - 1)) tiles.
+ *                 ceil(T / (max_partitions - 1)) tiles of 16 tokens, T = ceil(
+ *                 max_blocks_per_seq * BS / 16).
  *                 paged_attention_reduce must follow, with the same arguments: it
  *                 merges the split rows and writes the zero rows of empty sequences.
  *                 out and part_out must be 16-byte aligned in this mode.
  *   For partition_size > 0, part_* must be non-null with max_partitions >=
- *   ceil(max_blocks_per_seq * 16 / partition_size), and paged_attention_reduce()
+ *   ceil(max_blocks_per_seq * BS / partition_size), and paged_attention_reduce()
  *   produces out for the rows with more than one partition.
  * Supported: head_dim in {64, 128}; in_dtype F16/BF16 with num_heads/num_kv_heads
- * <= 16; in_dtype F32 with num_heads/num_kv_heads <= 8.
- * Errors: EINVAL (nulls, alignment, num_heads % num_kv_heads, block_size != 16,
- * partition arguments, sizes), ENOTSUP (head_dim, group size, dtype pair), EHIP.
+ * <= 16; in_dtype F32 with num_heads/num_kv_heads <= 8 and 16-token blocks.
+ * Errors: EINVAL (nulls, alignment, num_heads % num_kv_heads, block_size,
+ * partition arguments, sizes), ENOTSUP (head_dim, group size, dtype pair, F32 with
+ * block_size != 16), EHIP.
  * num_seqs == 0 is a no-op. */
 int paged_attention_decode(void* out, float* part_out, float* part_max, float* part_sum,
                            const void* q, int64_t q_stride, const void* k_cache,
@@ -367,15 +377,16 @@ int paged_attention_decode_append(void* out, float* part_out, float* part_max, f
  *     M = max_p part_max,  w_p = exp(part_max[p] - M) * part_sum[p],
  *     out[b][h] = sum_p w_p part_out[p] / sum_p w_p        (p < np only)
  * Rows with np <= 1 are not touched (the decode kernel wrote them). Buffers and
- * num_kv_heads, max_blocks_per_seq, partition_size, max_partitions are those of the
- * paged_attention_decode call; out_dtype in {F32, F16, BF16}; out and part_out must be
+ * num_kv_heads, block_size, max_blocks_per_seq, partition_size, max_partitions are those
+ * of the paged_attention_decode call; out_dtype in {F32, F16, BF16}; out and part_out must be
  * 16-byte aligned. Each row is merged in 32-dimension slices, one workgroup per
  * (slice, head, sequence), reading every record once. Errors: EINVAL, ENOTSUP, EHIP. */
 int paged_attention_reduce(void* out, const float* part_out, const float* part_max,
                            const float* part_sum, const int32_t* seq_lens, int32_t num_seqs,
                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t max_blocks_per_seq, int32_t partition_size,
-                           int32_t max_partitions, int32_t out_dtype, void* stream);
+                           int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t partition_size, int32_t max_partitions, int32_t out_dtype,
+                           void* stream);
 
 /* paged_attention_prefill: causal multi-query attention over the paged cache, for
  * chunked prefill: a long prompt is processed in chunks over several steps, each chunk's
@@ -410,7 +421,7 @@ int paged_attention_prefill(void* out, const void* q, int64_t q_stride, const in
  * [0, num_blocks) or src == dst are skipped; two pairs must not share a dst.
  *   k_caches, v_caches: host arrays of num_layers device pointers (16-byte aligned).
  *   pairs: device int32 [n_pairs][2] (kv_pool_append_tokens / _batch_tokens output).
- *   block_bytes: num_kv_heads * 16 * head_dim * element bytes (a multiple of 16).
+ *   block_bytes: num_kv_heads * BS * head_dim * element bytes (a multiple of 16).
  * Errors: EINVAL (NULLs, alignment, num_layers outside 1..256, block_bytes), EHIP. */
 int copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                 const int32_t* pairs, int32_t n_pairs, int64_t block_bytes, int64_t num_blocks,
@@ -423,8 +434,8 @@ int copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers
  * no format or scaling; here: PKV_FP8_E4M3 codes with one scale per tensor for K
  * (k_scale) and one for V (v_scale), a code c standing for value(c) * scale. Queries,
  * new K/V rows and outputs stay fp16/bf16 (or fp32 out); the layout is the one above
- * with x = 16 (k_cache [num_blocks][Hkv][head_dim/16][16][16] bytes, v_cache
- * [num_blocks][Hkv][head_dim][16] bytes). The decode kernels widen the codes to the
+ * with x = 16 (k_cache [num_blocks][Hkv][head_dim/16][BS][16] bytes, v_cache
+ * [num_blocks][Hkv][head_dim][BS] bytes). The decode kernels widen the codes to the
  * query type exactly (every e4m3 value is an fp16 and a bf16 value), fold k_scale into
  * the logit scale and v_scale into the output. */
 

@@ -27,7 +27,7 @@ LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(HERE, "libpkv.so")
 PKV_OK, PKV_EINVAL, PKV_ENOTSUP, PKV_ENOMEM, PKV_ENOENT, PKV_EHIP = 0, -1, -2, -3, -4, -5
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_PARTITION_AUTO = -1
-BLOCK_SIZE = 16
+BLOCK_SIZE = 16          # default tokens per block; 8 and 32 are the other sizes built
 _CODE_NAMES = {PKV_EINVAL: "EINVAL", PKV_ENOTSUP: "ENOTSUP", PKV_ENOMEM: "ENOMEM",
                PKV_ENOENT: "ENOENT", PKV_EHIP: "EHIP"}
 
@@ -88,7 +88,8 @@ def lib():
                               ctypes.c_int),
         "paged_attention_decode": ([P, P, P, P, P, I64, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                     I64, F, I32, I32, I32, I32, P], ctypes.c_int),
-        "paged_attention_reduce": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P],
+        "paged_attention_reduce": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
+                                    P],
                                    ctypes.c_int),
         "paged_attention_decode_append": ([P, P, P, P, P, I64, P, P, I64, I64, P, P, P, P, P,
                                            I32, I32, I32, I32, I32, I32, I64, F, I32, I32, I32,
@@ -178,19 +179,27 @@ def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype)
     return v
 
 
-def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype):
-    """(k_shape, v_shape) of one layer's caches: [nb][Hkv][d/x][16][x], [nb][Hkv][d][16]."""
+def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype,
+                 block_size: int = BLOCK_SIZE):
+    """(k_shape, v_shape) of one layer's caches: [nb][Hkv][d/x][BS][x], [nb][Hkv][d][BS]."""
     x = 16 // {PKV_F32: 4, PKV_F16: 2, PKV_BF16: 2, PKV_FP8_E4M3: 1}[dtype_code(dtype)]
-    return ((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x),
-            (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE))
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+            (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def block_size_of(v_cache) -> int:
+    """Tokens per block of a cache pair, read from the V cache's shape [nb][Hkv][d][BS]."""
+    if v_cache.dim() != 4:
+        raise ValueError("v_cache must be [num_blocks][Hkv][d][block_size]")
+    return int(v_cache.shape[3])
 
 
 def alloc_caches(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda",
-                 fill=None):
+                 fill=None, block_size: int = BLOCK_SIZE):
     """Allocate one layer's (k_cache, v_cache) through PyTorch (uninitialised, or filled;
     an FP8 cache is uint8, fill being a code)."""
     torch = _torch()
-    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, dtype)
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, dtype, block_size)
     td = torch_dtype(dtype) if not isinstance(dtype, torch.dtype) else dtype
     kc = torch.empty(ks, dtype=td, device=device)
     vc = torch.empty(vs, dtype=td, device=device)
@@ -372,7 +381,7 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
         raise ValueError("slot_mapping shorter than the token count")
     _check(lib().reshape_and_cache(
         _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
-        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, BLOCK_SIZE,
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, block_size_of(v_cache),
         k_cache.shape[0], key.stride(0), value.stride(0), dtype_code(key.dtype),
         _stream(key, stream)))
 
@@ -398,7 +407,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
-        B, Hq, hkv, d, BLOCK_SIZE, block_tables.shape[1], k_cache.shape[0], float(scale),
+        B, Hq, hkv, d, block_size_of(v_cache), block_tables.shape[1], k_cache.shape[0], float(scale),
         partition_size, max_partitions, dtype_code(q.dtype), dtype_code(out.dtype),
         _stream(q, stream)))
 
@@ -430,7 +439,7 @@ def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_c
         _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(key, "key"),
         _dev(value, "value"), key.stride(0), value.stride(0), _dev(slot_mapping, "slot_mapping"),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
-        _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, BLOCK_SIZE, block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, block_size_of(v_cache), block_tables.shape[1],
         k_cache.shape[0], float(scale), partition_size, max_partitions, dtype_code(q.dtype),
         dtype_code(out.dtype), _stream(q, stream)))
 
@@ -457,7 +466,7 @@ def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale: f
         raise ValueError("slot_mapping shorter than the token count")
     _check(lib().reshape_and_cache_fp8(
         _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
-        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, BLOCK_SIZE,
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, block_size_of(v_cache),
         k_cache.shape[0], key.stride(0), value.stride(0), dtype_code(key.dtype), float(k_scale),
         float(v_scale), _stream(key, stream)))
 
@@ -479,7 +488,7 @@ def paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, seq_lens,
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
-        B, Hq, k_cache.shape[1], d, BLOCK_SIZE, block_tables.shape[1], k_cache.shape[0],
+        B, Hq, k_cache.shape[1], d, block_size_of(v_cache), block_tables.shape[1], k_cache.shape[0],
         float(scale), float(k_scale), float(v_scale), partition_size, max_partitions,
         dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
 
@@ -511,7 +520,7 @@ def paged_attention_decode_append_fp8(out, q, key, value, slot_mapping, k_cache,
         _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(key, "key"),
         _dev(value, "value"), key.stride(0), value.stride(0), _dev(slot_mapping, "slot_mapping"),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
-        _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, BLOCK_SIZE, block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, block_size_of(v_cache), block_tables.shape[1],
         k_cache.shape[0], float(scale), float(k_scale), float(v_scale), partition_size,
         max_partitions, dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
 
@@ -536,7 +545,7 @@ def paged_attention_prefill(out, q, q_start, k_cache, v_cache, block_tables, seq
     _check(lib().paged_attention_prefill(
         _dev(out, "out"), _dev(q, "q"), q.stride(0), _dev(q_start, "q_start"),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
-        _dev(seq_lens, "seq_lens"), B, int(max_q_len), Hq, k_cache.shape[1], d, BLOCK_SIZE,
+        _dev(seq_lens, "seq_lens"), B, int(max_q_len), Hq, k_cache.shape[1], d, block_size_of(v_cache),
         block_tables.shape[1], k_cache.shape[0], float(scale), dtype_code(q.dtype),
         dtype_code(out.dtype), _stream(q, stream)))
 
@@ -560,13 +569,15 @@ def copy_blocks(k_caches, v_caches, pairs, stream=None):
 
 
 def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partition_size: int,
-                           num_kv_heads: int, max_blocks_per_seq: int, stream=None):
+                           num_kv_heads: int, max_blocks_per_seq: int,
+                           block_size: int = BLOCK_SIZE, stream=None):
     B, Hq, d = out.shape
     P = part_out.shape[2]
     _check(lib().paged_attention_reduce(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(seq_lens, "seq_lens"), B, Hq, num_kv_heads, d,
-        max_blocks_per_seq, partition_size, P, dtype_code(out.dtype), _stream(out, stream)))
+        block_size, max_blocks_per_seq, partition_size, P, dtype_code(out.dtype),
+        _stream(out, stream)))
 
 
 # ------------------------------------------------------------------ kernel timer
@@ -586,12 +597,13 @@ def timer_read(entry: int):
     return ms.value, n.value
 
 
-def max_partitions_for(max_blocks: int, partition_size: int) -> int:
-    """Partial slots per (b, h): ceil(max_blocks*16 / P) for fixed partitions; for the
-    balanced split a bound that keeps every piece at least 4 blocks long."""
+def max_partitions_for(max_blocks: int, partition_size: int, block_size: int = BLOCK_SIZE) -> int:
+    """Partial slots per (b, h): ceil(max_blocks*BS / P) for fixed partitions; for the
+    balanced split a bound that keeps every piece at least four 16-token tiles long."""
     if partition_size == PKV_PARTITION_AUTO:
-        return max(2, -(-max_blocks // 4) + 1)
-    return -(-max_blocks * BLOCK_SIZE // partition_size)
+        tiles = -(-max_blocks * block_size // 16)
+        return max(2, -(-tiles // 4) + 1)
+    return -(-max_blocks * block_size // partition_size)
 
 
 def alloc_partials(B: int, Hq: int, d: int, max_partitions: int, device="cuda"):
@@ -628,4 +640,4 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
                                partition_size, po, pm, ps, maxp, stream=stream)
     if partition_size != 0:
         paged_attention_reduce(out, po, pm, ps, seq_lens, partition_size, k_cache.shape[1],
-                               block_tables.shape[1], stream=stream)
+                               block_tables.shape[1], block_size_of(v_cache), stream=stream)

@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["pool.cpp", "timer.cpp", "cache_write.hip", "decode.hip", "reduce.hip", "copy_blocks.hip", "prefill.hip"]
+SOURCES = ["pool.cpp", "timer.cpp", "cache_write.hip", "decode.hip", "decode_bs8.hip", "decode_bs32.hip",
+           "reduce.hip", "copy_blocks.hip", "prefill.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -4,8 +4,10 @@
 // §03 Yöntem, step 3); this kernel is the device half of that step.
 //
 // One thread moves one 16-byte group of x = 16 / element_bytes dimensions of one
-// (token, KV head): K keeps the group together (cache layout [blk][g][d/x][16][x]),
-// V spreads it over x rows of its [blk][g][d][16] tile. A pure bit copy.
+// (token, KV head): K keeps the group together (cache layout [blk][g][d/x][BS][x]),
+// V spreads it over x rows of its [blk][g][d][BS] tile. A pure bit copy. The block size
+// BS = 2^lbs (8, 16 or 32 tokens) is a run-time argument: slot s is row s % BS of
+// block s / BS.
 // reshape_and_cache_fp8 stores the e4m3 codes of x / scale instead (FP8 KV cache).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -22,8 +24,9 @@ template <int E>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const char* __restrict__ key, const char* __restrict__ value, char* __restrict__ kc,
     char* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens, int32_t hkv,
-    int32_t d, int64_t num_blocks, int64_t key_stride_b, int64_t value_stride_b) {
+    int32_t d, int64_t num_blocks, int64_t key_stride_b, int64_t value_stride_b, int32_t lbs) {
     constexpr int X = 16 / E;
+    const int bs = 1 << lbs;
     const int nchunk = d / X;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t total = int64_t(num_tokens) * hkv * nchunk;
@@ -37,34 +40,35 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint4 kv = *reinterpret_cast<const uint4*>(key + src_k);
     const uint4 vv = *reinterpret_cast<const uint4*>(value + src_v);
     const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_blocks * 16) return;
-    const int64_t blk = slot >> 4;
-    const int off = int(slot & 15);
+    if (slot < 0 || slot >= (num_blocks << lbs)) return;
+    const int64_t blk = slot >> lbs;
+    const int off = int(slot & (bs - 1));
     const int64_t tile = blk * hkv + g;
-    *reinterpret_cast<uint4*>(kc + ((tile * nchunk + c) * 16 + off) * 16) = kv;
+    *reinterpret_cast<uint4*>(kc + ((tile * nchunk + c) * bs + off) * 16) = kv;
     // V: element k of the group is dimension c*X + k, row `off` of that dimension
-    char* vdst = vc + ((tile * d + int64_t(c) * X) * 16 + off) * E;
+    char* vdst = vc + ((tile * d + int64_t(c) * X) * bs + off) * E;
     if constexpr (E == 2) {
         const uint16_t* h = reinterpret_cast<const uint16_t*>(&vv);
 #pragma unroll
-        for (int k = 0; k < X; ++k) reinterpret_cast<uint16_t*>(vdst + k * 16 * E)[0] = h[k];
+        for (int k = 0; k < X; ++k) reinterpret_cast<uint16_t*>(vdst + k * bs * E)[0] = h[k];
     } else {
         const uint32_t* w = reinterpret_cast<const uint32_t*>(&vv);
 #pragma unroll
-        for (int k = 0; k < X; ++k) reinterpret_cast<uint32_t*>(vdst + k * 16 * E)[0] = w[k];
+        for (int k = 0; k < X; ++k) reinterpret_cast<uint32_t*>(vdst + k * bs * E)[0] = w[k];
     }
 }
 
 // FP8 cache: one thread quantises 4 dimensions of one (token, KV head): a quarter of a
-// 16-byte K group of the [blk][g][d/16][16][16] layout (one 4-byte store) and 4 bytes of
-// V, one per dimension row of the [blk][g][d][16] tile. Four dimensions per thread keep
+// 16-byte K group of the [blk][g][d/16][BS][16] layout (one 4-byte store) and 4 bytes of
+// V, one per dimension row of the [blk][g][d][BS] tile. Four dimensions per thread keep
 // the correctly rounded divisions per thread few; sixteen made the kernel latency-bound.
 template <typename T>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, uint8_t* __restrict__ kc,
     uint8_t* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens, int32_t hkv,
     int32_t d, int64_t num_blocks, int64_t key_stride, int64_t value_stride, float k_scale,
-    float v_scale) {
+    float v_scale, int32_t lbs) {
+    const int bs = 1 << lbs;
     const int nq = d / 4;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t total = int64_t(num_tokens) * hkv * nq;
@@ -75,20 +79,20 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint2 kr = *reinterpret_cast<const uint2*>(key + t * key_stride + int64_t(g) * d + 4 * c);
     const uint2 vr = *reinterpret_cast<const uint2*>(value + t * value_stride + int64_t(g) * d + 4 * c);
     const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_blocks * 16) return;
-    const int64_t tile = (slot >> 4) * hkv + g;
-    const int off = int(slot & 15);
+    if (slot < 0 || slot >= (num_blocks << lbs)) return;
+    const int64_t tile = (slot >> lbs) * hkv + g;
+    const int off = int(slot & (bs - 1));
     const uint32_t h[4] = {kr.x & 0xffffu, kr.x >> 16, kr.y & 0xffffu, kr.y >> 16};
     const uint32_t u[4] = {vr.x & 0xffffu, vr.x >> 16, vr.y & 0xffffu, vr.y >> 16};
     uint32_t kw = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) kw |= quantize_fp8(Bits<T>::to_f32(uint16_t(h[k])), k_scale) << (8 * k);
     // dims 4c .. 4c + 3 sit in group 4c / 16 at byte (4c) % 16 of the token's 16-byte row
-    *reinterpret_cast<uint32_t*>(kc + ((tile * (d / 16) + (4 * c) / 16) * 16 + off) * 16 + (4 * c) % 16) = kw;
-    uint8_t* vdst = vc + (tile * d + int64_t(4) * c) * 16 + off;
+    *reinterpret_cast<uint32_t*>(kc + ((tile * (d / 16) + (4 * c) / 16) * bs + off) * 16 + (4 * c) % 16) = kw;
+    uint8_t* vdst = vc + (tile * d + int64_t(4) * c) * bs + off;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        vdst[k * 16] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(u[k])), v_scale));
+        vdst[k * bs] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(u[k])), v_scale));
 }
 
 }  // namespace pkv
@@ -104,8 +108,10 @@ extern "C" int reshape_and_cache_fp8(const void* key, const void* value, void* k
         return fail(in_dtype == PKV_F32 ? PKV_ENOTSUP : PKV_EINVAL,
                     "reshape_and_cache_fp8: in_dtype must be F16 or BF16, got %d", in_dtype);
     if (num_tokens < 0) return fail(PKV_EINVAL, "reshape_and_cache_fp8: negative num_tokens");
-    if (block_size != PKV_BLOCK_SIZE)
-        return fail(PKV_EINVAL, "reshape_and_cache_fp8: block_size must be 16, got %d", block_size);
+    if (block_size != 8 && block_size != 16 && block_size != 32)
+        return fail(PKV_EINVAL, "reshape_and_cache_fp8: block_size must be 8, 16 or 32, got %d",
+                    block_size);
+    const int lbs = block_size == 8 ? 3 : block_size == 16 ? 4 : 5;
     if (num_kv_heads <= 0 || head_dim <= 0 || head_dim % 16 != 0 || num_blocks <= 0)
         return fail(PKV_EINVAL, "reshape_and_cache_fp8: bad shape (Hkv %d, head_dim %d, "
                                 "blocks %lld)", num_kv_heads, head_dim, (long long)num_blocks);
@@ -135,12 +141,12 @@ extern "C" int reshape_and_cache_fp8(const void* key, const void* value, void* k
         hipExtLaunchKernelGGL(pkv::reshape_and_cache_fp8_kernel<pkv::bf16_t>, dim3(unsigned(grid)),
                               dim3(256), 0, s, ev.start, ev.stop, 0, kp, vp, kcp, vcp,
                               slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
-                              key_stride, value_stride, k_scale, v_scale);
+                              key_stride, value_stride, k_scale, v_scale, lbs);
     else
         hipExtLaunchKernelGGL(pkv::reshape_and_cache_fp8_kernel<pkv::f16_t>, dim3(unsigned(grid)),
                               dim3(256), 0, s, ev.start, ev.stop, 0, kp, vp, kcp, vcp,
                               slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
-                              key_stride, value_stride, k_scale, v_scale);
+                              key_stride, value_stride, k_scale, v_scale, lbs);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return fail(PKV_EHIP, "reshape_and_cache_fp8: launch failed: %s", hipGetErrorString(err));
@@ -156,8 +162,10 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
     const int e = pkv::elem_bytes(dtype);
     if (e == 0) return fail(PKV_EINVAL, "reshape_and_cache: unknown dtype %d", dtype);
     if (num_tokens < 0) return fail(PKV_EINVAL, "reshape_and_cache: negative num_tokens");
-    if (block_size != PKV_BLOCK_SIZE)
-        return fail(PKV_EINVAL, "reshape_and_cache: block_size must be 16, got %d", block_size);
+    if (block_size != 8 && block_size != 16 && block_size != 32)
+        return fail(PKV_EINVAL, "reshape_and_cache: block_size must be 8, 16 or 32, got %d",
+                    block_size);
+    const int lbs = block_size == 8 ? 3 : block_size == 16 ? 4 : 5;
     const int x = 16 / e;
     if (num_kv_heads <= 0 || head_dim <= 0 || head_dim % x != 0 || num_blocks <= 0)
         return fail(PKV_EINVAL, "reshape_and_cache: bad shape (Hkv %d, head_dim %d, blocks %lld)",
@@ -184,11 +192,13 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
     if (e == 2)
         hipExtLaunchKernelGGL(pkv::reshape_and_cache_kernel<2>, dim3(unsigned(grid)), dim3(256), 0,
                               s, ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
-                              num_kv_heads, head_dim, num_blocks, key_stride * 2, value_stride * 2);
+                              num_kv_heads, head_dim, num_blocks, key_stride * 2, value_stride * 2,
+                              lbs);
     else
         hipExtLaunchKernelGGL(pkv::reshape_and_cache_kernel<4>, dim3(unsigned(grid)), dim3(256), 0,
                               s, ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
-                              num_kv_heads, head_dim, num_blocks, key_stride * 4, value_stride * 4);
+                              num_kv_heads, head_dim, num_blocks, key_stride * 4, value_stride * 4,
+                              lbs);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return fail(PKV_EHIP, "reshape_and_cache: launch failed: %s", hipGetErrorString(err));

@@ -1,0 +1,6 @@
+// Decode kernels for blocks of 8 tokens (decode_kernels.hpp).
+#include "decode_kernels.hpp"
+
+namespace pkv {
+template hipError_t dispatch_bs<8>(const DecodeArgs&, int, int, int, dim3, hipStream_t, bool, bool);
+}  // namespace pkv

@@ -1,0 +1,1035 @@
+// Kernels of paged_attention_decode: single-query attention for a batch of sequences
+// whose K/V live in scattered blocks of BS tokens (8, 16 or 32) reached through
+// per-sequence block tables. Each block size is instantiated in a translation unit of its
+// own (decode.hip: 16, decode_bs8.hip, decode_bs32.hip) through dispatch_bs.
+//
+// The attention math is ordinary scaled dot-product attention; paging only changes
+// where K and V are read from ("vLLM ve Triton ile maliyet optimizasyonu", §03 Yöntem,
+// closing paragraphs; the block table is step 2 there). Grouped-query attention lets
+// the query heads of a group share one KV head ("Yerel LLM sistemlerinde backpressure
+// ve ölçekleme", section "KV bütçesi"), so every KV tile is loaded once and used for
+// all G = Hq / Hkv query heads of its group.
+//
+// Work decomposition, three launch modes:
+//   single pass / fixed partitions (decode_mfma_kernel): one workgroup per (context
+//     partition, KV head, sequence); its W waves take the partition's blocks
+//     round-robin, each keeping its own online softmax state, and merge through LDS at
+//     the end. A sequence with one partition writes its output; otherwise the partition
+//     writes (o_p, m_p, l_p) for the reduce.
+//   balanced split (decode_split_kernel): all tiles of the batch cut into equal runs,
+//     one per wave (split.hpp); pieces that do not cover their (sequence, KV head) leave
+//     records for the reduce.
+//   fp32 inputs (decode_f32_kernel): plain vector arithmetic, the correctness path.
+// The fused append (paged_attention_decode_append) also stores each sequence's new K/V
+// row and, in the first two modes, attends to it from the key/value inputs.
+//
+// fp16/bf16 path, one wave per tile of 16 tokens (matrix instructions, wave64); the
+// layout offsets below are those of BS = 16 (tile.hpp gives the others):
+//   S^T[16 tokens][16 cols] = K_tile[16][d] x Q^T[d][16 cols]   (16x16x32, d/32 steps)
+//      A = K tile: lane l holds token l%16, dims 32c + 8(l/16) .. +7. In the cache
+//          layout [d/8][16][8] that is the 16 bytes at (64c + l) * 16: each step
+//          reads 1 KiB contiguous.
+//      B = Q^T: lane l holds query head l%16 of the group (zero past G), same dims.
+//      C: lane l holds head l%16 for tokens 4(l/16) + e, e = 0..3.
+//   online softmax on those 4 values (cross-lane max over lanes l^16, l^32, which
+//   hold the other tokens of the same head);
+//   O^T[d][16 cols] += V^T[d][16 tokens] x P^T[16 tokens][16 cols]  (16x16x16, d/16)
+//      A = V^T: lane l holds dim 16c + l%16, tokens 4(l/16) + e: 8 bytes at
+//          (16c + l%16) * 32 + 8 (l/16) in the [d][16] layout (512 B per step).
+//      B = P^T: exactly the C layout of the first product, so no data movement.
+//      P is split into a high and a low part in the input type (two products), so
+//      the weights keep ~16 significant bits instead of 8 (bf16) or 11 (fp16).
+//   C: lane l holds head l%16, dims 16c + 4(l/16) + e: its rescale factor is the
+//      lane's own running max, so the online softmax needs no transposes.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+
+#include "device.hpp"
+#include "split.hpp"
+#include "tile.hpp"
+#include "status.hpp"
+#include "timer.hpp"
+
+namespace pkv {
+
+struct DecodeArgs {
+    void* out;
+    float* part_out;
+    float* part_max;
+    float* part_sum;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int64_t q_stride;      // elements between sequences in q
+    int64_t num_blocks;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t group;         // G = num_heads / num_kv_heads
+    int32_t max_blocks;    // block-table row length
+    int32_t max_len;       // max_blocks * block size: longest context the table holds
+    int32_t max_tiles;     // ceil(max_len / 16): 16-token tiles of the longest context
+    int32_t part_tiles;    // 16-token tiles per partition
+    int32_t max_partitions;
+    float scale_log2;      // scale * log2(e) (* k_scale for an FP8 cache): base-2 logits
+    float k_scale;         // FP8 cache: per-tensor scales (new rows are quantised with
+    float v_scale;         // them; v_scale multiplies every output); 1 otherwise
+    int32_t num_seqs;
+    SplitParams split;     // balanced mode only
+    int32_t slots;         // balanced mode: result slots per wave
+    // Grid order of the single-pass / partitioned kernels. Consecutive workgroups go to
+    // different XCDs. With fewer than 8 partitions per sequence, partition-fastest order
+    // would put every partition 0 on the same few XCDs, so the grid is (KV head, sequence,
+    // partition); with 8 or more it is (partition, KV head, sequence), which measured
+    // faster on long contexts.
+    int32_t heads_fastest;
+    // Single pass with at most kLptMaxSeqs sequences: workgroups are dispatched one CU
+    // after the other, one round of lpt_round sequences (x KV heads) per sweep over the
+    // CUs, and a CU keeps the workgroups of all rounds. The sequences are handed out by
+    // length in serpentine order (round 0 takes ranks 0 .. R-1, round 1 ranks 2R-1 .. R,
+    // ...), so a CU that holds one of the longest also holds one of the shortest and the
+    // CUs finish together. 0: sequences in index order.
+    int32_t lpt_round;
+    // fused append (paged_attention_decode_append): the new token of sequence b has
+    // rows new_k/new_v + b * new_*_stride ([Hkv][D]) and goes to slot_mapping[b]
+    const void* new_k;
+    const void* new_v;
+    const int32_t* slot_mapping;
+    int64_t new_k_stride;
+    int64_t new_v_stride;
+};
+
+constexpr int kLptMaxSeqs = 256;
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Write the zero row of an empty sequence (n == 0) for the G heads of group g.
+template <typename OutT, int D>
+__device__ void write_zero_rows(const DecodeArgs& a, int b, int g) {
+    for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) {
+        const int h = g * a.group + i / D;
+        OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + h) * D + i % D, 0.0f);
+    }
+}
+
+// Fused append: copy the new token's K and V rows of KV head g into its slot (the
+// reshape_and_cache layout; FP8 cache: their codes, as reshape_and_cache_fp8 stores
+// them), with the threads of the calling workgroup. A slot outside the pool (or
+// negative) is skipped, as reshape_and_cache does.
+template <typename T, int D, bool F8, int BS>
+__device__ void write_new_token(const DecodeArgs& a, int b, int g, int slot) {
+    if (slot < 0 || int64_t(slot) >= a.num_blocks * BS) return;
+    const int64_t tile = int64_t(slot / BS) * a.num_kv_heads + g;
+    const int off = slot % BS;
+    const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride + int64_t(g) * D;
+    const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride + int64_t(g) * D;
+    const int t = threadIdx.x;
+    if constexpr (F8) {
+        uint8_t* kc = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.k_cache));
+        uint8_t* vc = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.v_cache));
+        if (t < D / 16)   // K: [tile][d/16][BS][16] bytes, one 16-byte group per thread
+            *reinterpret_cast<uint4*>(kc + ((tile * (D / 16) + t) * BS + off) * 16) =
+                quantize_fp8_x16<T>(*reinterpret_cast<const uint4*>(krow + 16 * t),
+                                    *reinterpret_cast<const uint4*>(krow + 16 * t + 8), a.k_scale);
+        for (int d = t; d < D; d += blockDim.x)   // V: [tile][d][BS] bytes
+            vc[(tile * D + d) * BS + off] = uint8_t(quantize_fp8(Bits<T>::to_f32(vrow[d]), a.v_scale));
+    } else {
+        uint16_t* kc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k_cache));
+        uint16_t* vc = const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v_cache));
+        if (t < D / 8)   // K: [tile][d/8][BS][8], one 16-byte group per thread
+            *reinterpret_cast<uint4*>(kc + ((tile * (D / 8) + t) * BS + off) * 8) =
+                *reinterpret_cast<const uint4*>(krow + 8 * t);
+        for (int d = t; d < D; d += blockDim.x)   // V: [tile][d][BS]
+            vc[(tile * D + d) * BS + off] = vrow[d];
+    }
+}
+
+// Merge the per-wave states held in LDS and write out or the partition result.
+// sm_m / sm_l: [W][16], sm_o: [W][G][D] (unnormalised accumulators).
+template <typename OutT, int D, int W>
+__device__ void merge_and_store(const DecodeArgs& a, const float* sm_m, const float* sm_l,
+                                const float* sm_o, int b, int g, int p, bool direct) {
+    const int G = a.group;
+    for (int i = threadIdx.x; i < G * D; i += W * 64) {
+        const int h = i / D, dim = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * 16 + h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float f = exp2_fast(sm_m[w * 16 + h] - M);  // 0 for a wave with no block
+            L += f * sm_l[w * 16 + h];
+            O += f * sm_o[(w * G + h) * D + dim];
+        }
+        const float o = O / L * a.v_scale;
+        const int hq = g * G + h;
+        if (direct) {
+            OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + hq) * D + dim, o);
+        } else {
+            const int64_t row = (int64_t(b) * a.num_heads + hq) * a.max_partitions + p;
+            a.part_out[row * D + dim] = o;
+            if (dim == 0) {
+                a.part_max[row] = M * kLn2;   // back to natural-log units
+                a.part_sum[row] = L;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- fp16 / bf16
+
+template <typename T, int D, typename OutT, int W, bool Append, bool F8, int BS>
+__global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
+    static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
+    constexpr int NQK = D / 32;   // 16x16x32 steps for S
+    constexpr int NPV = D / 16;   // 16x16x16 steps for O
+    constexpr int NKL = F8 ? D / 64 : D / 32;   // 16-byte K loads per tile and lane
+    extern __shared__ float lds[];
+    float* sm_m = lds;                  // [W][16]
+    float* sm_l = lds + W * 16;         // [W][16]
+    float* sm_o = lds + 2 * W * 16;     // [W][G][D]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
+    int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
+    const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
+    if (a.lpt_round > 0) {   // rank the lengths (ties by index); slot b takes a serpentine rank
+        __shared__ int s_n[kLptMaxSeqs];
+        __shared__ int s_pick;
+        const int t = threadIdx.x;
+        const int max_len = a.max_len;
+        for (int i = t; i < a.num_seqs; i += W * 64) {
+            const int v = a.seq_lens[i];
+            s_n[i] = v < 0 ? 0 : (v > max_len ? max_len : v);
+        }
+        __syncthreads();
+        for (int i = t; i < a.num_seqs; i += W * 64) {
+            const int mine = s_n[i];
+            int rank = 0;
+            for (int k = 0; k < a.num_seqs; ++k) {
+                const int o = s_n[k];
+                rank += (o > mine) || (o == mine && k < i);
+            }
+            const int R = a.lpt_round, r = b / R, pos = b - r * R;
+            const int hi = min(R, a.num_seqs - r * R);   // sequences in this round
+            if (rank == r * R + ((r & 1) ? hi - 1 - pos : pos)) s_pick = i;
+        }
+        __syncthreads();
+        b = s_pick;
+    }
+    const int G = a.group;
+    const int col = lane & 15, quad = lane >> 4;
+
+    // Q^T operand (B of the first product): head l%16 of the group, 8 dims per step.
+    // Issued first so its latency overlaps the sequence-length read.
+    uint4 qf[NQK];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(b) * a.q_stride +
+                               int64_t(g * G + col) * D;
+#pragma unroll
+        for (int c = 0; c < NQK; ++c)
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + q_dim<F8>(c, quad))
+                            : make_uint4(0, 0, 0, 0);
+    }
+    // Fused append: the new token's rows, every lane its share in the tile layout: K as
+    // the lane's 16-byte K loads hold them (16-bit cache: dims 32c + 8 quad .. + 7; FP8
+    // cache: dims 16(4i + quad) .. + 15), V dim 16c + l%16. Kept in registers: reading
+    // them from LDS inside the tile loop made the compiler move the tiles to scratch.
+    // FP8: each lane loads D/64 consecutive elements of each raw row (nkr, nvr) and, in
+    // the wave that stores the row, quantises just those (quantize_new, once its first
+    // tiles are on the way); the codes meet in the wave's LDS slice, from which every
+    // lane takes the ones it holds in the tile layout (nk, nv). Quantising whole K groups
+    // per lane instead cost 40 divisions per lane.
+    constexpr int NQ = D / 64;   // elements of each new row one lane quantises
+    int slot = -1;
+    uint4 nk[Append ? NKL : 1];
+    uint32_t nv[Append ? NPV : 1];
+    uint32_t nkr = 0, nvr = 0;   // FP8: NQ raw 16-bit elements each (NQ <= 2)
+    if constexpr (Append) {
+        slot = a.slot_mapping[b];
+        const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
+                               int64_t(g) * D;
+        const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
+                               int64_t(g) * D;
+        if constexpr (F8) {
+            static_assert(NQ == 1 || NQ == 2, "head_dim 64 or 128");
+            if constexpr (NQ == 2) {
+                nkr = *reinterpret_cast<const uint32_t*>(krow + 2 * lane);
+                nvr = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
+            } else {
+                nkr = krow[lane];
+                nvr = vrow[lane];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NKL; ++c) nk[c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * quad);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c + col];
+        }
+    }
+    auto quantize_new = [&]() {
+        if constexpr (Append && F8) {
+            // this wave's slice of sm_o (G * D floats >= 2 * D bytes), free until the merge
+            uint8_t* q8 = reinterpret_cast<uint8_t*>(sm_o + wave * G * D);
+#pragma unroll
+            for (int e = 0; e < NQ; ++e) {
+                q8[NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nkr >> (16 * e))), a.k_scale));
+                q8[D + NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nvr >> (16 * e))), a.v_scale));
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < NKL; ++i) nk[i] = *reinterpret_cast<const uint4*>(q8 + 64 * i + 16 * quad);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) nv[c] = q8[D + 16 * c + col];
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
+
+    // The context is walked in 16-token tiles (tile j: positions 16j .. 16j + 15), which
+    // are blocks for BS = 16, halves of blocks for BS = 32 and pairs of blocks for BS = 8
+    // (tile_ids, load_tile_bs). This wave takes tiles first, first + W, ... of its
+    // partition. The block ids of its first 64 are read before the length is known (the
+    // table row has max_blocks entries): the id load does not wait for the length load.
+    const int blk_begin = p * a.part_tiles;
+    const int first = blk_begin + wave;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    int tab0, tab0b;
+    tile_ids<BS>(table, a.max_blocks, first + lane * W, tab0, tab0b);
+
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    const int nblk = (n + 15) >> 4;
+    const int jl = n > 0 ? (n - 1) >> 4 : -1;     // tile of the newest token
+    if (blk_begin >= nblk) {
+        if (p == 0) write_zero_rows<OutT, D>(a, b, g);
+        if constexpr (Append)
+            if (p == 0 && n == 0) write_new_token<T, D, F8, BS>(a, b, g, slot);
+        return;
+    }
+    const int blk_end = min(nblk, blk_begin + a.part_tiles);
+    const bool direct = nblk <= a.part_tiles;
+
+    const int nmine = first < blk_end ? (blk_end - first + W - 1) / W : 0;
+    // The wave that holds tile jl (w_new) stores the new rows into the slot. When the
+    // slot is the newest position's (what the block pool hands out), the tiles stop one
+    // row short (row n-1 is masked like a row past the end, so it does not matter whether
+    // the store has landed when tile jl is read) and w_new adds the new token after its
+    // last tile as a one-row tile from the key/value inputs. Otherwise the cache is read
+    // as it is. lim: rows below it are valid.
+    bool subst = false;   // set by w_new when it reaches the table segment holding jl
+    int lim = n;
+    const bool own_new = jl >= blk_begin && jl < blk_end;   // this workgroup holds tile jl
+    const int w_new = own_new ? (jl - blk_begin) % W : -1;
+    const int k_new = own_new ? (jl - first) / W : -1;      // jl's index in w_new's list
+    // The row stores, issued right after w_new's first tile loads: those loads are older,
+    // so their wait does not include the stores, and the stores complete while the wave
+    // streams (issued at the end of the stream they would lengthen the kernel's tail).
+    auto store_new_row = [&]() {
+        if constexpr (Append) {
+            if (wave != w_new) return;
+            quantize_new();   // FP8: the codes, also those of the one-row tile at the end
+            if (slot < 0 || int64_t(slot) >= a.num_blocks * BS) return;
+            const int64_t tile = int64_t(slot / BS) * a.num_kv_heads + g;
+            const int off = slot % BS;
+            char* kc = const_cast<char*>(static_cast<const char*>(a.k_cache));
+            char* vc = const_cast<char*>(static_cast<const char*>(a.v_cache));
+            // K ([d/x][BS][x] per block and head): 16-byte group 4c + quad of the row is
+            // the lane's nk[c]
+            if (col == 0) {
+#pragma unroll
+                for (int c = 0; c < NKL; ++c)
+                    *reinterpret_cast<uint4*>(kc + ((tile * (NKL * 4) + 4 * c + quad) * BS + off) * 16) = nk[c];
+            }
+            if (quad == 0) {  // V ([d][BS]): dims 16c + col
+#pragma unroll
+                for (int c = 0; c < NPV; ++c) {
+                    if constexpr (F8)
+                        reinterpret_cast<uint8_t*>(vc)[(tile * D + 16 * c + col) * BS + off] = uint8_t(nv[c]);
+                    else
+                        reinterpret_cast<uint16_t*>(vc)[(tile * D + 16 * c + col) * BS + off] = uint16_t(nv[c]);
+                }
+            }
+        }
+    };
+
+    f32x4 acc[NPV];
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Softmax state per head (lane l: head l%16), in base-2 logit units: m is the
+    // reference point of the exponentials, lsum = sum of 2^(x - m) over this lane's
+    // tokens. m is the running maximum, except that it is only moved when a block's
+    // maximum exceeds it by more than kSlack, so the rescale of acc is rare; every
+    // 2^(x - m) stays below 2^kSlack, far from overflow.
+    constexpr float kSlack = 8.0f;
+    float m = -INFINITY, lsum = 0.f;
+
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    const int64_t tile_bytes = int64_t(D) * BS * (F8 ? 1 : 2);   // one block of one KV head
+    int tab = 0, tabb = 0;   // block ids of the current segment: lane k holds tile k's
+
+    // Issue the loads of tile k of the segment (tile j of the sequence). Returns bit 0
+    // set if the id of its (first) block is valid, bit 1 if that of its second block is
+    // (BS = 8; always set otherwise). An invalid id breaks the precondition: a safe
+    // address is read instead; the tile is skipped (bit 0) or its rows 8-15 masked (bit 1).
+    auto load = [&](KvTile<D, F8>& t, int k, int j) -> int {
+        int64_t pa = __builtin_amdgcn_readlane(tab, k);
+        const bool oka = pa >= 0 && pa < a.num_blocks;
+        pa = oka ? pa : 0;
+        int64_t pb = pa;
+        bool okb = true;
+        if constexpr (BS == 8) {
+            pb = __builtin_amdgcn_readlane(tabb, k);
+            okb = pb >= 0 && pb < a.num_blocks;
+            pb = okb ? pb : 0;
+        }
+        const int64_t ta = pa * a.num_kv_heads + g, tb = pb * a.num_kv_heads + g;
+        load_tile_bs<D, BS>(t, kbase + ta * tile_bytes, vbase + ta * tile_bytes,
+                            kbase + tb * tile_bytes, vbase + tb * tile_bytes, 16 * (j & 1), lane);
+        return int(oka) | (int(okb) << 1);
+    };
+
+    auto compute = [&](KvTile<D, F8>& t, int j, int ok) {
+        if (!(ok & 1)) return;
+        const int lim_t = (ok & 2) ? lim : min(lim, j * 16 + 8);   // rows below it are valid
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(k_operand<T, D>(t, c), qf[c], s);
+
+        const int tok0 = j * 16 + 4 * quad;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = tok0 + e < lim_t ? s[e] * a.scale_log2 : -INFINITY;
+        const float bm = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const bool move = bm > m + kSlack;          // true on the first block (m = -inf)
+        if (__builtin_amdgcn_ballot_w64(move)) {    // wave-uniform, rare after the first block
+            const float mn = move ? bm : m;
+            const float alpha = exp2_fast(m - mn);   // 1 where m stays, 0 from -inf
+            lsum *= alpha;
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) acc[c] *= alpha;
+            m = mn;
+        }
+        float pe[4];   // a masked row gives 0, also while m is still -inf
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m);
+        lsum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+
+        if (j * 16 + 16 > lim_t)   // partly filled tile: rows from lim_t on may hold anything
+            mask_rows<D>(t, tok0 + 0 < lim_t, tok0 + 1 < lim_t, tok0 + 2 < lim_t, tok0 + 3 < lim_t);
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
+        const uint2 phi = make_uint2(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                                     uint32_t(hi[2]) | (uint32_t(hi[3]) << 16));
+        const uint2 plo = make_uint2(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                                     uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) {
+            const uint2 vv = v_operand<T, D>(t, c);
+            acc[c] = Mfma<T>::pv(vv, phi, acc[c]);
+            acc[c] = Mfma<T>::pv(vv, plo, acc[c]);
+        }
+    };
+
+    // Segments of up to 64 blocks (one block id per lane). Inside a segment two stages of
+    // S tiles are in flight: the next stage's loads are always issued (past the end they
+    // re-read the final block, which is then in cache) before the current stage is used,
+    // so the wait for the current tile never waits for the next. S = 1 also for the
+    // half-size FP8 tiles: stages of two measured slower.
+    constexpr int S = 1;
+    for (int k0 = 0; k0 < nmine; k0 += 64) {
+        const int cnt = min(64, nmine - k0);
+        if (k0 == 0) {
+            tab = tab0;
+            tabb = tab0b;
+        } else {
+            tile_ids<BS>(table, a.max_blocks, lane < cnt ? first + (k0 + lane) * W : a.max_tiles,
+                         tab, tabb);
+        }
+        if constexpr (Append) {
+            if (wave == w_new && k_new >= k0 && k_new < k0 + 64) {   // wave-uniform
+                // the block holding position n - 1: tile jl's, or for BS = 8 its first or
+                // second block
+                const int half = BS == 8 && ((n - 1) & 15) >= 8;
+                const int64_t phys_l = __builtin_amdgcn_readlane(half ? tabb : tab, k_new - k0);
+                subst = slot >= 0 && phys_l >= 0 && phys_l < a.num_blocks &&
+                        int64_t(slot) == phys_l * BS + (n - 1) % BS;
+                lim = subst ? n - 1 : n;
+            }
+        }
+        KvTile<D, F8> X[S], Y[S];
+        int okX[S], okY[S];
+        auto tile_of = [&](int k) { return first + (k0 + k) * W; };
+#pragma unroll
+        for (int i = 0; i < S; ++i) okX[i] = load(X[i], min(i, cnt - 1), tile_of(min(i, cnt - 1)));
+        if (k0 == 0) store_new_row();
+        for (int k = 0; k < cnt; k += 2 * S) {
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                const int kk = min(k + S + i, cnt - 1);
+                okY[i] = load(Y[i], kk, tile_of(kk));
+            }
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+                if (k + i < cnt) compute(X[i], tile_of(k + i), okX[i]);
+            if (k + S >= cnt) break;
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                const int kk = min(k + 2 * S + i, cnt - 1);
+                okX[i] = load(X[i], kk, tile_of(kk));
+            }
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+                if (k + S + i < cnt) compute(Y[i], tile_of(k + S + i), okY[i]);
+        }
+    }
+
+    // Fused append, in w_new after its last tile: the new token as a tile whose only
+    // valid row is row 0.
+    if constexpr (Append) {
+        if (wave == w_new && subst) {
+            KvTile<D, F8> t;
+#pragma unroll
+            for (int c = 0; c < NKL; ++c) t.k[c] = col == 0 ? nk[c] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) {
+                if constexpr (F8)
+                    t.v[c] = quad == 0 ? nv[c] & 0xffu : 0u;
+                else
+                    t.v[c] = make_uint2(quad == 0 ? nv[c] & 0xffffu : 0u, 0u);
+            }
+            lim = 1;
+            compute(t, 0, 3);
+        }
+    }
+
+    // lanes l, l^16, l^32, l^48 hold the same head: total its running sum
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+
+    if (lane < 16) {
+        sm_m[wave * 16 + lane] = m;
+        sm_l[wave * 16 + lane] = lsum;
+    }
+    if (col < G) {
+#pragma unroll
+        for (int c = 0; c < NPV; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm_o[(wave * G + col) * D + 16 * c + 4 * quad + e] = acc[c][e];
+    }
+    __syncthreads();
+    merge_and_store<OutT, D, W>(a, sm_m, sm_l, sm_o, b, g, p, direct);
+}
+
+// ------------------------------------------------------- fp16 / bf16, balanced split
+// Same per-tile arithmetic as decode_mfma_kernel; the work is cut as described in
+// split.hpp. Each wave is independent: it reads the block ids of up to 64 of its tiles
+// with one vector load (lane k: tile k), then streams the tiles, switching (sequence,
+// KV head) at piece boundaries. A piece covering all of its (b, g) is written to out;
+// any other piece becomes an (o, m, l) record at piece index u - floor(start / s).
+//
+// Finished pieces are parked in LDS result slots of the wave and written to HBM only
+// after its last tile (or when the slots are full). On gfx950 one counter tracks both
+// outstanding loads and outstanding stores, so a store issued between tile loads makes
+// every later tile wait for the store's completion as well; parking the results keeps
+// the stream of tile loads free of stores.
+constexpr int kSplitPiecesPerBatch = 4;   // queries staged in LDS per wave and batch
+constexpr int kSplitStage = 1;            // tiles per pipeline stage (two stages per wave)
+constexpr int kSplitMaxSlots = 8;         // result slots per wave (upper bound)
+constexpr int kSplitWaveLds = 17920;      // LDS bytes per wave: staged queries + slots
+
+// Per-wave LDS of the balanced split: staged queries, then `slots` result slots of
+// (G*D outputs, G reference points, G sums) floats, then 4 ints of metadata per slot.
+__host__ __device__ constexpr int split_q_bytes(int G, int D) { return kSplitPiecesPerBatch * G * D * 2; }
+__host__ __device__ constexpr int split_slot_floats(int G, int D) { return (G * D + 2 * G + 3) & ~3; }
+__host__ __device__ constexpr int split_wave_bytes(int G, int D, int slots) {
+    return split_q_bytes(G, D) + slots * (split_slot_floats(G, D) * 4 + 16);
+}
+
+template <typename T, int D, typename OutT, bool F8, int BS>
+__global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs a) {
+    constexpr int NQK = D / 32, NPV = D / 16;
+    constexpr int kWaves = kSplitThreads / 64;
+    __shared__ int32_t s_end[kSplitMaxSeqs];
+    __shared__ int32_t s_len[kSplitMaxSeqs];
+    __shared__ int32_t s_wave[kWaves];
+    extern __shared__ uint4 s_dyn[];    // per wave: see split_wave_bytes
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, quad = lane >> 4;
+    const int G = a.group, hkv = a.num_kv_heads;
+    const int total = split_scan(a.seq_lens, a.num_seqs, hkv, a.max_len, s_end, s_len, s_wave);
+    const int share = split_share(total, a.split);
+    const int u = blockIdx.x * kWaves + wave;
+    const int64_t t0l = int64_t(u) * share;
+    if (t0l >= total) return;
+    const int t0 = int(t0l);
+    const int t1 = min(total, t0 + share);
+
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    const int64_t tile_bytes = int64_t(D) * BS * (F8 ? 1 : 2);   // one block of one KV head
+    const int qpiece = G * D;                              // elements per staged query set
+    char* my_lds = reinterpret_cast<char*>(s_dyn) + wave * split_wave_bytes(G, D, a.slots);
+    uint16_t* my_q = reinterpret_cast<uint16_t*>(my_lds);
+    const int slot_floats = split_slot_floats(G, D);
+    float* slots = reinterpret_cast<float*>(my_lds + split_q_bytes(G, D));
+    int32_t* slot_meta = reinterpret_cast<int32_t*>(slots + a.slots * slot_floats);
+    int nused = 0;   // result slots in use (wave-uniform)
+    constexpr float kSlack = 8.0f;
+
+    // state of the current piece
+    uint4 qf[NQK];
+    f32x4 acc[NPV];
+    float m = -INFINITY, lsum = 0.f;
+    int cur_bg = -1, seg_b = 0, seg_g = 0, seg_n = 0, seg_nblk = 0, seg_start = 0;
+    int first_j = 0, last_j = 0, piece_slot = -1;
+
+    auto begin_piece = [&](int bg, int j) {
+        seg_b = bg / hkv;
+        seg_g = bg - seg_b * hkv;
+        seg_n = s_len[seg_b];
+        seg_nblk = (seg_n + 15) >> 4;
+        seg_start = (seg_b ? s_end[seg_b - 1] : 0) + seg_g * seg_nblk;
+        first_j = j;
+        cur_bg = bg;
+        ++piece_slot;
+        const uint16_t* qs = my_q + piece_slot * qpiece + (col < G ? col : 0) * D;
+#pragma unroll
+        for (int c = 0; c < NQK; ++c)
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qs + q_dim<F8>(c, quad))
+                            : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        lsum = 0.f;
+    };
+
+    // Write the parked results: G*D outputs per slot, four consecutive ones per lane
+    // and store (the G heads of a group are consecutive rows of out).
+    auto flush = [&]() {
+        __builtin_amdgcn_wave_barrier();
+        for (int sl = 0; sl < nused; ++sl) {
+            const float* so = slots + sl * slot_floats;
+            const int b = slot_meta[4 * sl], g = slot_meta[4 * sl + 1], piece = slot_meta[4 * sl + 2];
+            const int64_t head0 = int64_t(b) * a.num_heads + g * G;
+            for (int i = 4 * lane; i < G * D; i += 256) {
+                const float4 v = *reinterpret_cast<const float4*>(so + i);
+                if (piece < 0) {
+                    OutStore<OutT>::st4(a.out, head0 * D + i, v);
+                } else {
+                    const int64_t row = (head0 + i / D) * a.max_partitions + piece;
+                    *reinterpret_cast<float4*>(a.part_out + row * D + i % D) = v;
+                }
+            }
+            if (piece >= 0 && lane < G) {
+                const int64_t row = (head0 + lane) * a.max_partitions + piece;
+                a.part_max[row] = so[G * D + lane];
+                a.part_sum[row] = so[G * D + G + lane];
+            }
+        }
+        nused = 0;
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // Park the finished piece in the next result slot (normalised outputs; the
+    // reference point in natural-log units and the sum for the reduce).
+    auto end_piece = [&]() {
+        float L = lsum;
+        L += __shfl_xor(L, 16, 64);
+        L += __shfl_xor(L, 32, 64);
+        if (nused == a.slots) flush();
+        float* so = slots + nused * slot_floats;
+        if (col < G) {
+            const float inv = a.v_scale / L;
+#pragma unroll
+            for (int c = 0; c < NPV; ++c)
+                *reinterpret_cast<float4*>(so + col * D + 16 * c + 4 * quad) =
+                    make_float4(acc[c][0] * inv, acc[c][1] * inv, acc[c][2] * inv, acc[c][3] * inv);
+            if (quad == 0) {
+                so[G * D + col] = m * kLn2;
+                so[G * D + G + col] = L;
+            }
+        }
+        if (lane == 0) {
+            const bool whole = first_j == 0 && last_j == seg_nblk - 1;
+            slot_meta[4 * nused] = seg_b;
+            slot_meta[4 * nused + 1] = seg_g;
+            slot_meta[4 * nused + 2] = whole ? -1 : u - seg_start / share;
+        }
+        ++nused;
+    };
+
+    // per-lane metadata of the current batch: tile k's block ids (tphys; tphysb the
+    // second block for BS = 8), (b, g) and tile index j
+    int tphys = 0, tphysb = 0, tbg = 0, tj = 0;
+    // bit 0: the (first) block id is valid; bit 1: the second one (BS = 8) is
+    auto load = [&](KvTile<D, F8>& t, int k) -> int {
+        int64_t pa = __builtin_amdgcn_readlane(tphys, k);
+        const bool oka = pa >= 0 && pa < a.num_blocks;
+        pa = oka ? pa : 0;
+        int64_t pb = pa;
+        bool okb = true;
+        if constexpr (BS == 8) {
+            pb = __builtin_amdgcn_readlane(tphysb, k);
+            okb = pb >= 0 && pb < a.num_blocks;
+            pb = okb ? pb : 0;
+        }
+        const int g = __builtin_amdgcn_readlane(tbg, k) % hkv;
+        const int j = __builtin_amdgcn_readlane(tj, k);
+        const int64_t ta = pa * hkv + g, tb = pb * hkv + g;
+        load_tile_bs<D, BS>(t, kbase + ta * tile_bytes, vbase + ta * tile_bytes,
+                            kbase + tb * tile_bytes, vbase + tb * tile_bytes, 16 * (j & 1), lane);
+        return int(oka) | (int(okb) << 1);
+    };
+
+    auto compute = [&](KvTile<D, F8>& t, int k, int ok) {   // ok & 1 == 0: tile masked out
+        const int bg = __builtin_amdgcn_readlane(tbg, k);
+        const int j = __builtin_amdgcn_readlane(tj, k);
+        if (bg != cur_bg) {
+            if (cur_bg >= 0) end_piece();
+            begin_piece(bg, j);
+        }
+        last_j = j;
+        // A tile whose block id broke the precondition is read from block 0 and then
+        // masked out entirely (arithmetic, not a branch, so every loaded register is
+        // consumed and the waits stay per tile); an invalid second block (BS = 8) masks
+        // rows 8-15.
+        const int n = (ok & 1) ? ((ok & 2) ? seg_n : min(seg_n, j * 16 + 8)) : 0;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(k_operand<T, D>(t, c), qf[c], s);
+        const int tok0 = j * 16 + 4 * quad;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = tok0 + e < n ? s[e] * a.scale_log2 : -INFINITY;
+        const float bm = max_over_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const bool move = bm > m + kSlack;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float mn = move ? bm : m;
+            const float alpha = exp2_fast(m - mn);
+            lsum *= alpha;
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) acc[c] *= alpha;
+            m = mn;
+        }
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m);
+        lsum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+        if (j * 16 + 16 > n) mask_rows<D>(t, tok0 + 0 < n, tok0 + 1 < n, tok0 + 2 < n, tok0 + 3 < n);
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
+        const uint2 phi = make_uint2(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                                     uint32_t(hi[2]) | (uint32_t(hi[3]) << 16));
+        const uint2 plo = make_uint2(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                                     uint32_t(lo[2]) | (uint32_t(lo[3]) << 16));
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) {
+            const uint2 vv = v_operand<T, D>(t, c);
+            acc[c] = Mfma<T>::pv(vv, phi, acc[c]);
+            acc[c] = Mfma<T>::pv(vv, plo, acc[c]);
+        }
+    };
+
+    // Batches of up to 64 tiles spanning up to kSplitPiecesPerBatch (b, g) pieces.
+    // Per batch: lane k finds tile k's (b, g, j) by binary search, then the block ids
+    // and the pieces' queries are fetched together (one wait), the queries staged in
+    // this wave's LDS slots; the tiles then stream two deep with no other load.
+    for (int tb = t0; tb < t1;) {
+        int cnt = min(64, t1 - tb);
+        int lb = 0, lg = 0, lj = 0;
+        if (lane < cnt) {
+            const int t = tb + lane;
+            int lo = 0, hi = a.num_seqs - 1;   // first b with s_end[b] > t
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_end[mid] > t) hi = mid; else lo = mid + 1;
+            }
+            const int nb = (s_len[lo] + 15) >> 4;
+            const int r = t - (lo ? s_end[lo - 1] : 0);
+            lb = lo;
+            lg = r / nb;
+            lj = r - lg * nb;
+        }
+        const int lbg = lb * hkv + lg;
+        // lanes that open a new piece; cut the batch before the fifth one
+        const int prev = __shfl_up(lbg, 1, 64);
+        const bool opens = lane < cnt && (lane == 0 || prev != lbg);
+        uint64_t opens_mask = __builtin_amdgcn_ballot_w64(opens);
+        for (int c = 0; c < kSplitPiecesPerBatch && opens_mask; ++c) opens_mask &= opens_mask - 1;
+        if (opens_mask) cnt = __builtin_ctzll(opens_mask);
+        tbg = lbg;
+        tj = lj;
+        // One round trip for all metadata: the block ids of the batch and the queries
+        // of its pieces (piece p opens at the p-th set bit of pm) are loaded together,
+        // then the queries are staged in this wave's LDS slots.
+        tile_ids<BS>(a.block_tables + int64_t(lb) * a.max_blocks, a.max_blocks,
+                     lane < cnt ? lj : a.max_tiles, tphys, tphysb);
+        const uint64_t pm = __builtin_amdgcn_ballot_w64(opens && lane < cnt);
+        constexpr int kQChunks = (16 * D * 2 + 1023) / 1024;   // 1 KiB per lane-chunk, G <= 16
+        uint4 qv[kSplitPiecesPerBatch][kQChunks];
+        {
+            uint64_t mm = pm;
+#pragma unroll
+            for (int p = 0; p < kSplitPiecesPerBatch; ++p) {
+                const int src = mm ? __builtin_ctzll(mm) : 0;
+                mm &= mm ? mm - 1 : 0;
+                const int pbg = __builtin_amdgcn_readlane(lbg, src);
+                const int pb = pbg / hkv, pg = pbg - pb * hkv;
+                const uint16_t* qg = static_cast<const uint16_t*>(a.q) + int64_t(pb) * a.q_stride +
+                                     int64_t(pg) * G * D;
+#pragma unroll
+                for (int c = 0; c < kQChunks; ++c) {
+                    const int i = (c * 64 + lane) * 8;
+                    qv[p][c] = i < qpiece ? *reinterpret_cast<const uint4*>(qg + i) : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < kSplitPiecesPerBatch; ++p)
+#pragma unroll
+            for (int c = 0; c < kQChunks; ++c) {
+                const int i = (c * 64 + lane) * 8;
+                if (i < qpiece) *reinterpret_cast<uint4*>(my_q + p * qpiece + i) = qv[p][c];
+            }
+        piece_slot = -1;
+        if (cur_bg >= 0 && __builtin_amdgcn_readlane(tbg, 0) == cur_bg) {
+            // the batch continues the previous piece: keep its state, re-point the slot
+            piece_slot = 0;
+        }
+        // Two stages of kSplitStage tiles: the loads of the next stage are issued
+        // before the current one is used, so a wave keeps tiles in flight while it
+        // computes. Tiles past the end repeat the last one with every token masked:
+        // the loop has no data-dependent branch, and each wait covers only the
+        // loads it needs.
+        constexpr int S = kSplitStage;   // also for FP8 tiles: stages of two measured slower
+        KvTile<D, F8> X[S], Y[S];
+        int okX[S], okY[S];
+        auto load_stage = [&](KvTile<D, F8>* t, int* ok, int k) {
+#pragma unroll
+            for (int i = 0; i < S; ++i) ok[i] = load(t[i], min(k + i, cnt - 1));
+        };
+        auto compute_stage = [&](KvTile<D, F8>* t, const int* ok, int k) {
+#pragma unroll
+            for (int i = 0; i < S; ++i)
+                compute(t[i], min(k + i, cnt - 1), k + i < cnt ? ok[i] : 0);
+        };
+        load_stage(X, okX, 0);
+        for (int k = 0; k < cnt; k += 2 * S) {
+            load_stage(Y, okY, k + S);
+            compute_stage(X, okX, k);
+            load_stage(X, okX, k + 2 * S);
+            compute_stage(Y, okY, k + S);
+        }
+        tb += cnt;
+    }
+    if (cur_bg >= 0) end_piece();
+    flush();
+}
+
+// ---------------------------------------------------------------------- fp32
+// 16-token blocks only. One wave per (partition, KV head, sequence). Lane l scores token l%16 for query
+// heads l/16 and l/16 + 4 of the group; for the weighted sum it owns dimensions
+// l and l + 64 of every head.
+template <int D, typename OutT>
+__global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
+    constexpr int GMAX = 8;
+    constexpr int ND = (D + 63) / 64;
+    __shared__ float sq[GMAX][D];
+    __shared__ float sp[GMAX][16];
+    __shared__ float salpha[GMAX];
+    __shared__ float sm[1][16], sl[1][16];
+
+    const int lane = threadIdx.x;
+    const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
+    const int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
+    const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
+    const int G = a.group;
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    const int nblk = (n + 15) >> 4;
+    const int blk_begin = p * a.part_tiles;
+    if (blk_begin >= nblk) {
+        if (p == 0) write_zero_rows<OutT, D>(a, b, g);
+        return;
+    }
+    const int blk_end = min(nblk, blk_begin + a.part_tiles);
+    const bool direct = nblk <= a.part_tiles;
+
+    const float* qrow = static_cast<const float*>(a.q) + int64_t(b) * a.q_stride + int64_t(g) * G * D;
+    for (int i = lane; i < G * D; i += 64) sq[i / D][i % D] = qrow[i];
+    __syncthreads();
+
+    const int t = lane & 15, hs = lane >> 4;
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    float acc[GMAX][ND];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+        for (int k = 0; k < ND; ++k) acc[h][k] = 0.f;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    const float* kbase = static_cast<const float*>(a.k_cache);
+    const float* vbase = static_cast<const float*>(a.v_cache);
+    for (int j = blk_begin; j < blk_end; ++j) {
+        const int64_t phys = table[j];
+        if (phys < 0 || phys >= a.num_blocks) continue;
+        const int64_t tile = (phys * a.num_kv_heads + g) * int64_t(D) * 16;
+        const float* kt = kbase + tile;   // [D/4][16][4]
+        const float* vt = vbase + tile;   // [D][16]
+        const bool valid = j * 16 + t < n;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int h = hs + 4 * r;
+            float x = -INFINITY;
+            if (h < G && valid) {
+                float dot = 0.f;
+                for (int i = 0; i < D; ++i) dot += sq[h][i] * kt[((i >> 2) * 16 + t) * 4 + (i & 3)];
+                x = dot * a.scale_log2;
+            }
+            float bm = x;
+#pragma unroll
+            for (int s = 1; s < 16; s <<= 1) bm = wave_max_xor(bm, s);
+            const float mn = fmaxf(m[r], bm);
+            // a head with no valid token yet keeps -inf; guard the 0 * inf case
+            const float alpha = mn == -INFINITY ? 1.f : exp2_fast(m[r] - mn);
+            const float pv = x == -INFINITY ? 0.f : exp2_fast(x - mn);
+            float ps = pv;
+#pragma unroll
+            for (int s = 1; s < 16; s <<= 1) ps += __shfl_xor(ps, s, 64);
+            l[r] = l[r] * alpha + ps;
+            m[r] = mn;
+            if (h < G) {
+                sp[h][t] = pv;
+                if (t == 0) salpha[h] = alpha;
+            }
+        }
+        __syncthreads();
+        const int nvalid = min(16, n - j * 16);
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h >= G) break;
+            const float al = salpha[h];
+#pragma unroll
+            for (int k = 0; k < ND; ++k) {
+                const int dim = lane + 64 * k;
+                if (dim >= D) continue;
+                float s = acc[h][k] * al;
+                for (int tt = 0; tt < nvalid; ++tt) s += sp[h][tt] * vt[dim * 16 + tt];
+                acc[h][k] = s;
+            }
+        }
+        __syncthreads();
+    }
+    // publish each head's (m, l)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int h = hs + 4 * r;
+        if (h < G && t == 0) {
+            sm[0][h] = m[r];
+            sl[0][h] = l[r];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+        if (h >= G) break;
+        const float M = sm[0][h], L = sl[0][h];
+        const int hq = g * G + h;
+#pragma unroll
+        for (int k = 0; k < ND; ++k) {
+            const int dim = lane + 64 * k;
+            if (dim >= D) continue;
+            const float o = acc[h][k] / L;
+            if (direct) {
+                OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + hq) * D + dim, o);
+            } else {
+                const int64_t row = (int64_t(b) * a.num_heads + hq) * a.max_partitions + p;
+                a.part_out[row * D + dim] = o;
+                if (dim == 0) {
+                    a.part_max[row] = M * kLn2;
+                    a.part_sum[row] = L;
+                }
+            }
+        }
+    }
+}
+
+constexpr int kWaves = 4;
+
+template <typename T, int D, typename OutT, bool F8, int BS>
+hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+    const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
+    const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
+    if (a.new_k)
+        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true, F8, BS>), grid,
+                              dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
+    else
+        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, false, F8, BS>), grid,
+                              dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D, typename OutT, bool F8, int BS>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
+    const int groups = (a.split.units + kSplitThreads / 64 - 1) / (kSplitThreads / 64);
+    const size_t lds = size_t(kSplitThreads / 64) * split_wave_bytes(a.group, D, a.slots);
+    const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
+    hipExtLaunchKernelGGL((decode_split_kernel<T, D, OutT, F8, BS>), dim3(groups),
+                          dim3(kSplitThreads), lds, s, ev.start, ev.stop, 0, a);
+    return hipGetLastError();
+}
+
+template <int D, typename OutT>
+hipError_t launch_f32(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+    const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
+    hipExtLaunchKernelGGL((decode_f32_kernel<D, OutT>), grid, dim3(64), 0, s, ev.start, ev.stop, 0, a);
+    return hipGetLastError();
+}
+
+template <int D, bool F8, int BS>
+hipError_t dispatch_16(const DecodeArgs& a, int in_dtype, int out_dtype, dim3 grid, hipStream_t s,
+                       bool split) {
+    if (split) {
+        if (in_dtype == PKV_BF16)
+            return out_dtype == PKV_F32 ? launch_split<bf16_t, D, float, F8, BS>(a, s)
+                                        : launch_split<bf16_t, D, bf16_t, F8, BS>(a, s);
+        return out_dtype == PKV_F32 ? launch_split<f16_t, D, float, F8, BS>(a, s)
+                                    : launch_split<f16_t, D, f16_t, F8, BS>(a, s);
+    }
+    if (in_dtype == PKV_BF16)
+        return out_dtype == PKV_F32 ? launch_mfma<bf16_t, D, float, F8, BS>(a, grid, s)
+                                    : launch_mfma<bf16_t, D, bf16_t, F8, BS>(a, grid, s);
+    return out_dtype == PKV_F32 ? launch_mfma<f16_t, D, float, F8, BS>(a, grid, s)
+                                : launch_mfma<f16_t, D, f16_t, F8, BS>(a, grid, s);
+}
+
+// Launch the decode kernel for blocks of BS tokens (the fp32 kernel: BS = 16 only; the
+// caller checks).
+template <int BS>
+hipError_t dispatch_bs(const DecodeArgs& a, int head_dim, int in_dtype, int out_dtype, dim3 grid,
+                       hipStream_t s, bool split, bool fp8) {
+    if (in_dtype == PKV_F32) {
+        if constexpr (BS == 16)
+            return head_dim == 128 ? launch_f32<128, float>(a, grid, s) : launch_f32<64, float>(a, grid, s);
+        return hipErrorInvalidValue;
+    }
+    if (head_dim == 128)
+        return fp8 ? dispatch_16<128, true, BS>(a, in_dtype, out_dtype, grid, s, split)
+                   : dispatch_16<128, false, BS>(a, in_dtype, out_dtype, grid, s, split);
+    return fp8 ? dispatch_16<64, true, BS>(a, in_dtype, out_dtype, grid, s, split)
+               : dispatch_16<64, false, BS>(a, in_dtype, out_dtype, grid, s, split);
+}
+
+int device_cus();
+
+}  // namespace pkv

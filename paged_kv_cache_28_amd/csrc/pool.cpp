@@ -1,5 +1,6 @@
-// Host block pool: fixed 16-token KV blocks handed out on demand from a FIFO free
-// queue, per-sequence block tables, reference-counted sharing.
+// Host block pool: fixed-size KV blocks (8, 16 or 32 tokens, chosen when the pool is
+// created) handed out on demand from a FIFO free queue, per-sequence block tables,
+// reference-counted sharing.
 //
 // What it follows: "vLLM ve Triton ile maliyet optimizasyonu", §03 Yöntem, steps 1-3
 // (blocks, block table, a new block only when the last one is full) and the paragraph
@@ -10,11 +11,11 @@
 // short, so a refused allocation must change nothing).
 //
 // Prefix caching and copy-on-write ("vLLM Nedir? ...", section "Prefix caching": full
-// 16-token blocks are keyed by a chain of the previous block's key, the block's tokens
+// blocks are keyed by a chain of the previous block's key, the block's tokens
 // and, for the first block, a salt; a request bringing the same chain references the
 // cached block; "vLLM ve Triton ...", §03 on sharing: a shared block is copied when one
 // of its users writes to it). Keys here: a 64-bit hash chain h_j = mix(h_{j-1}, tokens of
-// block j) from h_{-1} = root(salt). A hit is checked against the block's own 16 token
+// block j) from h_{-1} = root(salt). A hit is checked against the block's own token
 // ids and its parent's chain hash, so a false hit needs two different prefixes with one
 // 64-bit chain hash. A block is keyed when it fills in a sequence whose token ids are all
 // known; freed blocks keep their key in the free queue, which is the eviction order, and
@@ -53,15 +54,16 @@ inline uint64_t mix64(uint64_t x) {
     return x ^ (x >> 31);
 }
 inline uint64_t chain_root(uint64_t salt) { return mix64(salt ^ 0x9e3779b97f4a7c15ull); }
-inline uint64_t chain_next(uint64_t parent, const int32_t* tok) {
+inline uint64_t chain_next(uint64_t parent, const int32_t* tok, int bs) {
     uint64_t h = parent;
-    for (int k = 0; k < PKV_BLOCK_SIZE; ++k) h = mix64(h ^ uint64_t(uint32_t(tok[k])));
+    for (int k = 0; k < bs; ++k) h = mix64(h ^ uint64_t(uint32_t(tok[k])));
     return h;
 }
 }  // namespace
 
 struct kv_pool {
     int64_t num_blocks = 0;
+    int32_t bs = 16;                    // tokens per block: 8, 16 or 32
     int32_t num_layers = 0, num_kv_heads = 0, head_dim = 0, dtype = 0;
     // FIFO free queue as a doubly linked list over block ids (-1 ends)
     std::vector<int32_t> nxt, prv;
@@ -69,11 +71,11 @@ struct kv_pool {
     int32_t fhead = -1, ftail = -1;
     int64_t count = 0;
     std::vector<int32_t> ref;
-    // prefix cache: chain hash -> block; per block its key, parent hash and 16 token ids
+    // prefix cache: chain hash -> block; per block its key, parent hash and bs token ids
     std::unordered_map<uint64_t, int32_t> cache;
     std::vector<char> keyed;
     std::vector<uint64_t> key, key_parent;
-    std::vector<int32_t> key_tokens;   // [num_blocks][16]
+    std::vector<int32_t> key_tokens;   // [num_blocks][bs]
     int64_t prefix_hits = 0;
     struct Seq {
         std::vector<int32_t> blocks;
@@ -115,7 +117,7 @@ struct kv_pool {
     // key block b (now full in s, as its block j) unless the key is taken already
     void register_full(Seq& s, int64_t j, const int32_t* tok) {
         const uint64_t parent = j == 0 ? chain_root(s.salt) : s.chain[size_t(j - 1)];
-        const uint64_t h = chain_next(parent, tok);
+        const uint64_t h = chain_next(parent, tok, bs);
         s.chain.push_back(h);
         const int32_t b = s.blocks[size_t(j)];
         if (keyed[b] || cache.count(h)) return;
@@ -123,16 +125,16 @@ struct kv_pool {
         keyed[b] = 1;
         key[b] = h;
         key_parent[b] = parent;
-        std::memcpy(&key_tokens[size_t(b) * PKV_BLOCK_SIZE], tok, sizeof(int32_t) * PKV_BLOCK_SIZE);
+        std::memcpy(&key_tokens[size_t(b) * bs], tok, sizeof(int32_t) * bs);
     }
-    // the cached block for (parent hash, 16 tokens), or -1
+    // the cached block for (parent hash, bs tokens), or -1
     int32_t lookup(uint64_t parent, const int32_t* tok, uint64_t* h_out) const {
-        const uint64_t h = chain_next(parent, tok);
+        const uint64_t h = chain_next(parent, tok, bs);
         auto it = cache.find(h);
         if (it == cache.end()) return -1;
         const int32_t b = it->second;
         if (key_parent[b] != parent ||
-            std::memcmp(&key_tokens[size_t(b) * PKV_BLOCK_SIZE], tok, sizeof(int32_t) * PKV_BLOCK_SIZE))
+            std::memcmp(&key_tokens[size_t(b) * bs], tok, sizeof(int32_t) * bs))
             return -1;
         *h_out = h;
         return b;
@@ -146,7 +148,7 @@ struct kv_pool {
         return it == seqs.end() ? nullptr : &it->second;
     }
     // blocks a sequence of length len needs
-    static int64_t blocks_for(int64_t len) { return (len + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE; }
+    int64_t blocks_for(int64_t len) const { return (len + bs - 1) / bs; }
 };
 
 extern "C" {
@@ -171,8 +173,12 @@ int kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t num_layers,
     if (num_blocks <= 0 || num_blocks > INT32_MAX)
         return fail(PKV_EINVAL, "kv_pool_create: num_blocks %lld out of range",
                     (long long)num_blocks);
-    if (block_size != PKV_BLOCK_SIZE)
-        return fail(PKV_EINVAL, "kv_pool_create: block_size must be 16, got %d", block_size);
+    if (block_size != 8 && block_size != 16 && block_size != 32)
+        return fail(PKV_EINVAL, "kv_pool_create: block_size must be 8, 16 or 32, got %d",
+                    block_size);
+    if (num_blocks * block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "kv_pool_create: %lld blocks of %d tokens overflow int32 slot ids",
+                    (long long)num_blocks, block_size);
     if (num_layers <= 0 || num_kv_heads <= 0 || head_dim <= 0 || pkv::cache_elem_bytes(dtype) == 0)
         return fail(PKV_EINVAL, "kv_pool_create: bad model shape or dtype");
     if (head_dim % (16 / pkv::cache_elem_bytes(dtype)) != 0)
@@ -181,6 +187,7 @@ int kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t num_layers,
     kv_pool* p = new (std::nothrow) kv_pool();
     if (!p) return fail(PKV_ENOMEM, "kv_pool_create: out of host memory");
     p->num_blocks = num_blocks;
+    p->bs = block_size;
     p->num_layers = num_layers;
     p->num_kv_heads = num_kv_heads;
     p->head_dim = head_dim;
@@ -192,7 +199,7 @@ int kv_pool_create(int64_t num_blocks, int32_t block_size, int32_t num_layers,
     p->keyed.assign(num_blocks, 0);
     p->key.assign(num_blocks, 0);
     p->key_parent.assign(num_blocks, 0);
-    p->key_tokens.assign(size_t(num_blocks) * PKV_BLOCK_SIZE, 0);
+    p->key_tokens.assign(size_t(num_blocks) * block_size, 0);
     if (free_order) {
         std::vector<char> seen(num_blocks, 0);
         for (int64_t i = 0; i < num_blocks; ++i) {
@@ -227,12 +234,12 @@ int kv_pool_cache_shape(const kv_pool* pool, int64_t k_shape[5], int64_t v_shape
     k_shape[0] = pool->num_blocks;
     k_shape[1] = pool->num_kv_heads;
     k_shape[2] = pool->head_dim / x;
-    k_shape[3] = PKV_BLOCK_SIZE;
+    k_shape[3] = pool->bs;
     k_shape[4] = x;
     v_shape[0] = pool->num_blocks;
     v_shape[1] = pool->num_kv_heads;
     v_shape[2] = pool->head_dim;
-    v_shape[3] = PKV_BLOCK_SIZE;
+    v_shape[3] = pool->bs;
     return ok();
 }
 
@@ -251,11 +258,11 @@ int kv_pool_share_prefix(kv_pool* pool, int64_t seq_id, int64_t src_seq_id, int3
     if (!dst || !src) return fail(PKV_ENOENT, "kv_pool_share_prefix: unknown sequence");
     if (dst->len != 0 || !dst->blocks.empty())
         return fail(PKV_EINVAL, "kv_pool_share_prefix: target sequence is not empty");
-    if (n_tokens < 0 || n_tokens % PKV_BLOCK_SIZE != 0 || n_tokens > src->len)
-        return fail(PKV_EINVAL,
-                    "kv_pool_share_prefix: n_tokens must be a multiple of 16 within the source");
+    if (n_tokens < 0 || n_tokens % pool->bs != 0 || n_tokens > src->len)
+        return fail(PKV_EINVAL, "kv_pool_share_prefix: n_tokens must be a multiple of the "
+                                "block size (%d) within the source", pool->bs);
     if (seq_id == src_seq_id) return fail(PKV_EINVAL, "kv_pool_share_prefix: same sequence");
-    int64_t nb = n_tokens / PKV_BLOCK_SIZE;
+    int64_t nb = n_tokens / pool->bs;
     dst->blocks.assign(src->blocks.begin(), src->blocks.begin() + nb);
     for (int32_t b : dst->blocks) ++pool->ref[b];
     dst->len = n_tokens;
@@ -274,7 +281,7 @@ int kv_pool_add_seq_prefix(kv_pool* pool, int64_t seq_id, const int32_t* prompt,
     s.salt = salt;
     uint64_t h = chain_root(salt);
     int64_t n = 0;
-    while (n + PKV_BLOCK_SIZE <= int64_t(n_prompt) - 1) {
+    while (n + pool->bs <= int64_t(n_prompt) - 1) {
         uint64_t hn = 0;
         const int32_t b = pool->lookup(h, prompt + n, &hn);
         if (b < 0) break;
@@ -283,7 +290,7 @@ int kv_pool_add_seq_prefix(kv_pool* pool, int64_t seq_id, const int32_t* prompt,
         s.blocks.push_back(b);
         s.chain.push_back(hn);
         h = hn;
-        n += PKV_BLOCK_SIZE;
+        n += pool->bs;
     }
     pool->prefix_hits += int64_t(s.blocks.size());
     s.len = n;
@@ -306,11 +313,11 @@ int kv_pool_fork(kv_pool* pool, int64_t parent_id, int64_t child_id) {
 
 // Does appending to s first need a copy of its last block (partly filled and shared)?
 static bool needs_copy(const kv_pool* pool, const kv_pool::Seq* s) {
-    return s->len % PKV_BLOCK_SIZE != 0 && pool->ref[s->blocks.back()] > 1;
+    return s->len % pool->bs != 0 && pool->ref[s->blocks.back()] > 1;
 }
 
 static int64_t blocks_needed(const kv_pool* pool, const kv_pool::Seq* s, int64_t n_tokens) {
-    return kv_pool::blocks_for(s->len + n_tokens) - int64_t(s->blocks.size()) +
+    return pool->blocks_for(s->len + n_tokens) - int64_t(s->blocks.size()) +
            (n_tokens > 0 && needs_copy(pool, s) ? 1 : 0);
 }
 
@@ -328,14 +335,15 @@ static void append_one_seq(kv_pool* pool, kv_pool::Seq* s, int32_t n_tokens,
         --pool->ref[copy[0]];   // still referenced by the others
         s->blocks.back() = nb;
     }
-    while (int64_t(s->blocks.size()) * PKV_BLOCK_SIZE < s->len + n_tokens) {
+    const int32_t bs = pool->bs;
+    while (int64_t(s->blocks.size()) * bs < s->len + n_tokens) {
         const int32_t b = pool->pop_front();
         pool->ref[b] = 1;
         s->blocks.push_back(b);
     }
     for (int32_t k = 0; k < n_tokens; ++k) {
         int64_t pos = s->len + k;
-        slots[k] = s->blocks[pos / PKV_BLOCK_SIZE] * PKV_BLOCK_SIZE + int32_t(pos % PKV_BLOCK_SIZE);
+        slots[k] = s->blocks[pos / bs] * bs + int32_t(pos % bs);
     }
     if (!tokens) {
         s->hashable = false;
@@ -343,8 +351,8 @@ static void append_one_seq(kv_pool* pool, kv_pool::Seq* s, int32_t n_tokens,
     } else if (s->hashable) {
         for (int32_t k = 0; k < n_tokens; ++k) {
             s->tail.push_back(tokens[k]);
-            if (s->tail.size() == PKV_BLOCK_SIZE) {   // block (len + k) / 16 is now full
-                pool->register_full(*s, (s->len + k) / PKV_BLOCK_SIZE, s->tail.data());
+            if (int32_t(s->tail.size()) == bs) {   // block (len + k) / bs is now full
+                pool->register_full(*s, (s->len + k) / bs, s->tail.data());
                 s->tail.clear();
             }
         }
@@ -374,7 +382,7 @@ int kv_pool_append(kv_pool* pool, int64_t seq_id, int32_t n_tokens, int32_t* slo
     if (n_tokens > 0 && !slot_mapping_out) return fail(PKV_EINVAL, "kv_pool_append: NULL output");
     kv_pool::Seq* s = pool->find(seq_id);
     if (!s) return fail(PKV_ENOENT, "kv_pool_append: unknown sequence %lld", (long long)seq_id);
-    int64_t max_len = int64_t(pool->num_blocks) * PKV_BLOCK_SIZE;
+    int64_t max_len = int64_t(pool->num_blocks) * pool->bs;
     if (s->len + n_tokens > max_len) {
         ++pool->alloc_failures;
         return fail(PKV_ENOMEM, "kv_pool_append: sequence longer than the whole pool");
@@ -392,7 +400,7 @@ int kv_pool_append_tokens(kv_pool* pool, int64_t seq_id, const int32_t* tokens, 
     kv_pool::Seq* s = pool->find(seq_id);
     if (!s) return fail(PKV_ENOENT, "kv_pool_append_tokens: unknown sequence %lld",
                         (long long)seq_id);
-    if (s->len + n_tokens > int64_t(pool->num_blocks) * PKV_BLOCK_SIZE) {
+    if (s->len + n_tokens > int64_t(pool->num_blocks) * pool->bs) {
         ++pool->alloc_failures;
         return fail(PKV_ENOMEM, "kv_pool_append_tokens: sequence longer than the whole pool");
     }
@@ -460,7 +468,7 @@ int kv_pool_append_batch_tokens(kv_pool* pool, const int64_t* seq_ids, const int
             return fail(PKV_EINVAL, "kv_pool_append_batch_tokens: duplicate sequence %lld",
                         (long long)seq_ids[i]);
         const kv_pool::Seq* sq = seqs[i];
-        if (sq->len % PKV_BLOCK_SIZE == 0) {
+        if (sq->len % pool->bs == 0) {
             ++need;                                  // a fresh block for the token
         } else {
             const int32_t tb = sq->blocks.back();

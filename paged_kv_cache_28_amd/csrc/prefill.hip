@@ -16,7 +16,9 @@
 // see none of a block pair skips it. (Staging the tiles in LDS for all four waves measured
 // slower: the barrier per block kept the waves in lockstep.)
 //
-// A wave takes its blocks in pairs (A, B). Per pair and column tile:
+// Keys are walked in 16-token tiles whatever the block size BS (8, 16 or 32; a template
+// parameter): a tile is a block, half a block or two blocks (tile.hpp). A wave takes its
+// tiles in pairs (A, B). Per pair and column tile:
 //   S_A^T, S_B^T[16 keys][16 cols] = K_tile x Q^T          (16x16x32, d/32 steps each)
 //   O^T[d][16 cols] += V^T[d][32 keys] x P^T[32 keys][16 cols]   (16x16x32, d/16 steps)
 // The 32 keys of one PV step are the lane's 4 rows of A and its 4 rows of B (the 8 k-slots
@@ -57,6 +59,8 @@ struct PrefillArgs {
     int32_t num_kv_heads;
     int32_t group;
     int32_t max_blocks;
+    int32_t max_len;           // max_blocks * block size
+    int32_t max_tiles;         // ceil(max_len / 16)
     float scale_log2;
 };
 
@@ -67,7 +71,7 @@ __host__ __device__ constexpr size_t prefill_lds_bytes() {
     return sizeof(float) * (2 * kPrefillWaves * 16 + size_t(kPrefillWaves) * 16 * D);
 }
 
-template <typename T, int D, typename OutT, int NC>
+template <typename T, int D, typename OutT, int NC, int BS>
 __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs a) {
     constexpr int W = kPrefillWaves;
     constexpr int NQK = D / 32, NPV = D / 16;
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
     if (t0 >= L) return;
     const int tcount = min(QT, L - t0);
     int n = a.seq_lens[b];
-    n = n < 0 ? 0 : (n > a.max_blocks * 16 ? a.max_blocks * 16 : n);
+    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
 
     // This lane's column in each column tile: query token, head, causal limit (keys
     // below it are visible), and its Q^T operand.
@@ -131,32 +135,51 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
 
     const char* kbase = static_cast<const char*>(a.k_cache);
     const char* vbase = static_cast<const char*>(a.v_cache);
-    const int64_t tile_bytes = int64_t(D) * 16 * 2;
+    const int64_t tile_bytes = int64_t(D) * BS * 2;   // one block of one KV head
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
-    int tab = 0;
+    int tab = 0, tabb = 0;   // lane k: tile k's block id (and its second block's, BS = 8)
 
-    auto load = [&](KvTile<D, false>& t, int k) __attribute__((always_inline)) -> bool {
-        int64_t phys = __builtin_amdgcn_readlane(tab, k);
-        const bool ok = phys >= 0 && phys < a.num_blocks;
-        phys = ok ? phys : 0;
-        const int64_t tile = phys * a.num_kv_heads + g;
-        load_tile<D>(t, kbase + tile * tile_bytes, vbase + tile * tile_bytes, lane);
-        return ok;
+    // Issue tile j's loads (segment index k). Bit 0 of the result: its (first) block id is
+    // valid; bit 1: its second block's (BS = 8; always set otherwise). An invalid id is
+    // replaced by a safe address and its rows count as past the end.
+    auto load = [&](KvTile<D, false>& t, int k, int j) __attribute__((always_inline)) -> int {
+        int64_t pa = __builtin_amdgcn_readlane(tab, k);
+        const bool oka = pa >= 0 && pa < a.num_blocks;
+        pa = oka ? pa : 0;
+        int64_t pb = pa;
+        bool okb = true;
+        if constexpr (BS == 8) {
+            pb = __builtin_amdgcn_readlane(tabb, k);
+            okb = pb >= 0 && pb < a.num_blocks;
+            pb = okb ? pb : 0;
+        }
+        const int64_t ta = pa * a.num_kv_heads + g, tb = pb * a.num_kv_heads + g;
+        load_tile_bs<D, BS>(t, kbase + ta * tile_bytes, vbase + ta * tile_bytes,
+                            kbase + tb * tile_bytes, vbase + tb * tile_bytes, 16 * (j & 1), lane);
+        return int(oka) | (int(okb) << 1);
     };
 
-    // Blocks jA and jB (ok: a valid block id) as one 32-key step; okB false for the odd last
-    // block of a wave, whose B then contributes nothing.
+    // Tiles jA and jB (ok bits as load returns them) as one 32-key step; okB is 0 for the
+    // odd last tile of a wave, whose B then contributes nothing.
     auto compute_pair = [&](const KvTile<D, false>& A, const KvTile<D, false>& B, int jA, int jB,
-                            bool okA, bool okB) __attribute__((always_inline)) {
+                            int okA, int okB) __attribute__((always_inline)) {
         const int tA = jA * 16 + 4 * quad, tB = jB * 16 + 4 * quad;
-        // V rows past the sequence may hold anything: zeroed as the operands are built
+        // keys of each tile below nA / nB are real: past the sequence, or behind an invalid
+        // block id, they are not
+        const int nA = (okA & 1) ? ((okA & 2) ? n : min(n, jA * 16 + 8)) : 0;
+        const int nB = (okB & 1) ? ((okB & 2) ? n : min(n, jB * 16 + 8)) : 0;
+        // V rows that are not real may hold anything: zeroed as the operands are built
         // (the tiles stay read-only, which keeps them in registers)
-        auto keep = [&](int t) { return (t < n ? 0x0000ffffu : 0u) | (t + 1 < n ? 0xffff0000u : 0u); };
-        const uint32_t ka0 = keep(tA), ka1 = keep(tA + 2), kb0 = keep(tB), kb1 = keep(tB + 2);
-        const int jmin = okB ? min(jA, jB) : jA;
+        auto keep = [&](int t, int nt) {
+            return (t < nt ? 0x0000ffffu : 0u) | (t + 1 < nt ? 0xffff0000u : 0u);
+        };
+        const uint32_t ka0 = keep(tA, nA), ka1 = keep(tA + 2, nA), kb0 = keep(tB, nB),
+                       kb1 = keep(tB + 2, nB);
+        const int jmin = (okB & 1) ? min(jA, jB) : jA;
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
             if (jmin * 16 >= tile_lim[ct]) continue;   // no query of this tile sees the pair
+            const int la = min(lim[ct], nA), lb = min(lim[ct], nB);
             f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NQK; ++c) {
@@ -166,8 +189,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
             float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = okA && tA + e < lim[ct] ? sa[e] * a.scale_log2 : -INFINITY;
-                x[4 + e] = okB && tB + e < lim[ct] ? sb[e] * a.scale_log2 : -INFINITY;
+                x[e] = tA + e < la ? sa[e] * a.scale_log2 : -INFINITY;
+                x[4 + e] = tB + e < lb ? sb[e] * a.scale_log2 : -INFINITY;
             }
             const float bm = max_over_rows(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                                                  fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
@@ -207,19 +230,22 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
         }
     };
 
-    // This wave's blocks: wave, wave + W, ...; segments of 64 block ids (one per lane),
-    // two tiles in flight as in the decode kernel.
+    // This wave's tiles: wave, wave + W, ...; segments of 64 tiles (block ids one per
+    // lane).
     const int nmine = wave < nblk ? (nblk - wave + W - 1) / W : 0;
     for (int k0 = 0; k0 < nmine; k0 += 64) {
         const int cnt = min(64, nmine - k0);
-        tab = lane < cnt ? table[wave + (k0 + lane) * W] : 0;
-        // pairs (k, k + 1) of this segment, each loaded and then used; an odd last block
+        tile_ids<BS>(table, a.max_blocks, lane < cnt ? wave + (k0 + lane) * W : a.max_tiles, tab,
+                     tabb);
+        // pairs (k, k + 1) of this segment, each loaded and then used; an odd last tile
         // pairs with itself, its second copy masked out
         for (int k = 0; k < cnt; k += 2) {
             KvTile<D, false> X0, X1;
-            const bool ox0 = load(X0, k), ox1 = load(X1, min(k + 1, cnt - 1));
+            const int k1 = min(k + 1, cnt - 1);
+            const int ox0 = load(X0, k, wave + (k0 + k) * W);
+            const int ox1 = load(X1, k1, wave + (k0 + k1) * W);
             compute_pair(X0, X1, wave + (k0 + k) * W, wave + (k0 + k + 1) * W, ox0,
-                         ox1 && k + 1 < cnt);
+                         k + 1 < cnt ? ox1 : 0);
         }
     }
 
@@ -264,7 +290,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
     }
 }
 
-template <typename T, int D, typename OutT>
+template <typename T, int D, typename OutT, int BS>
 hipError_t launch_prefill(const PrefillArgs& a, int max_q_len, int num_kv_heads, int num_seqs,
                           hipStream_t s) {
     constexpr int NC = 2;
@@ -272,9 +298,27 @@ hipError_t launch_prefill(const PrefillArgs& a, int max_q_len, int num_kv_heads,
     const dim3 grid(unsigned((max_q_len + qt_tokens - 1) / qt_tokens), unsigned(num_kv_heads),
                     unsigned(num_seqs));
     const LaunchEvents ev = timer_events(PKV_TIMER_PREFILL);
-    hipExtLaunchKernelGGL((prefill_kernel<T, D, OutT, NC>), grid, dim3(kPrefillWaves * 64),
+    hipExtLaunchKernelGGL((prefill_kernel<T, D, OutT, NC, BS>), grid, dim3(kPrefillWaves * 64),
                           prefill_lds_bytes<D>(), s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
+}
+
+template <int BS>
+hipError_t dispatch_prefill(const PrefillArgs& a, int head_dim, int in_dtype, int out_dtype,
+                            int max_q_len, int num_kv_heads, int num_seqs, hipStream_t s) {
+    const bool f32 = out_dtype == PKV_F32;
+    if (head_dim == 128) {
+        if (in_dtype == PKV_BF16)
+            return f32 ? launch_prefill<bf16_t, 128, float, BS>(a, max_q_len, num_kv_heads, num_seqs, s)
+                       : launch_prefill<bf16_t, 128, bf16_t, BS>(a, max_q_len, num_kv_heads, num_seqs, s);
+        return f32 ? launch_prefill<f16_t, 128, float, BS>(a, max_q_len, num_kv_heads, num_seqs, s)
+                   : launch_prefill<f16_t, 128, f16_t, BS>(a, max_q_len, num_kv_heads, num_seqs, s);
+    }
+    if (in_dtype == PKV_BF16)
+        return f32 ? launch_prefill<bf16_t, 64, float, BS>(a, max_q_len, num_kv_heads, num_seqs, s)
+                   : launch_prefill<bf16_t, 64, bf16_t, BS>(a, max_q_len, num_kv_heads, num_seqs, s);
+    return f32 ? launch_prefill<f16_t, 64, float, BS>(a, max_q_len, num_kv_heads, num_seqs, s)
+               : launch_prefill<f16_t, 64, f16_t, BS>(a, max_q_len, num_kv_heads, num_seqs, s);
 }
 
 }  // namespace pkv
@@ -295,8 +339,8 @@ extern "C" int paged_attention_prefill(void* out, const void* q, int64_t q_strid
     if (out_dtype != in_dtype && out_dtype != PKV_F32)
         return fail(PKV_ENOTSUP, "%s: out_dtype must be in_dtype or F32", who);
     if (num_seqs < 0 || max_q_len < 0) return fail(PKV_EINVAL, "%s: negative sizes", who);
-    if (block_size != PKV_BLOCK_SIZE)
-        return fail(PKV_EINVAL, "%s: block_size must be 16, got %d", who, block_size);
+    if (block_size != 8 && block_size != 16 && block_size != 32)
+        return fail(PKV_EINVAL, "%s: block_size must be 8, 16 or 32, got %d", who, block_size);
     if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
         return fail(PKV_EINVAL, "%s: num_heads %d not a multiple of num_kv_heads %d", who,
                     num_heads, num_kv_heads);
@@ -306,7 +350,8 @@ extern "C" int paged_attention_prefill(void* out, const void* q, int64_t q_strid
         return fail(PKV_ENOTSUP, "%s: head_dim %d (built: 64, 128)", who, head_dim);
     const int G = num_heads / num_kv_heads;
     if (G > 16) return fail(PKV_ENOTSUP, "%s: group size %d too large", who, G);
-    if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+        int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
         return fail(PKV_EINVAL, "%s: bad max_blocks_per_seq / num_blocks", who);
     if (q_stride < int64_t(num_heads) * head_dim || q_stride % 8)
         return fail(PKV_EINVAL, "%s: q_stride must cover num_heads*head_dim and be a multiple "
@@ -335,21 +380,16 @@ extern "C" int paged_attention_prefill(void* out, const void* q, int64_t q_strid
     a.num_kv_heads = num_kv_heads;
     a.group = G;
     a.max_blocks = max_blocks_per_seq;
+    a.max_len = max_blocks_per_seq * block_size;
+    a.max_tiles = (a.max_len + 15) / 16;
     a.scale_log2 = scale * 1.44269504088896340736f;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err;
-    if (head_dim == 128)
-        err = in_dtype == PKV_BF16
-                  ? (out_dtype == PKV_F32 ? pkv::launch_prefill<pkv::bf16_t, 128, float>(a, max_q_len, num_kv_heads, num_seqs, s)
-                                          : pkv::launch_prefill<pkv::bf16_t, 128, pkv::bf16_t>(a, max_q_len, num_kv_heads, num_seqs, s))
-                  : (out_dtype == PKV_F32 ? pkv::launch_prefill<pkv::f16_t, 128, float>(a, max_q_len, num_kv_heads, num_seqs, s)
-                                          : pkv::launch_prefill<pkv::f16_t, 128, pkv::f16_t>(a, max_q_len, num_kv_heads, num_seqs, s));
-    else
-        err = in_dtype == PKV_BF16
-                  ? (out_dtype == PKV_F32 ? pkv::launch_prefill<pkv::bf16_t, 64, float>(a, max_q_len, num_kv_heads, num_seqs, s)
-                                          : pkv::launch_prefill<pkv::bf16_t, 64, pkv::bf16_t>(a, max_q_len, num_kv_heads, num_seqs, s))
-                  : (out_dtype == PKV_F32 ? pkv::launch_prefill<pkv::f16_t, 64, float>(a, max_q_len, num_kv_heads, num_seqs, s)
-                                          : pkv::launch_prefill<pkv::f16_t, 64, pkv::f16_t>(a, max_q_len, num_kv_heads, num_seqs, s));
+    const hipError_t err =
+        block_size == 16
+            ? pkv::dispatch_prefill<16>(a, head_dim, in_dtype, out_dtype, max_q_len, num_kv_heads, num_seqs, s)
+        : block_size == 8
+            ? pkv::dispatch_prefill<8>(a, head_dim, in_dtype, out_dtype, max_q_len, num_kv_heads, num_seqs, s)
+            : pkv::dispatch_prefill<32>(a, head_dim, in_dtype, out_dtype, max_q_len, num_kv_heads, num_seqs, s);
     if (err != hipSuccess)
         return fail(PKV_EHIP, "%s: launch failed: %s", who, hipGetErrorString(err));
     return pkv::ok();

@@ -29,7 +29,7 @@ struct ReduceArgs {
     int32_t num_seqs;
     int32_t num_heads;
     int32_t num_kv_heads;
-    int32_t max_blocks;
+    int32_t max_len;        // max_blocks_per_seq * block_size
     int32_t part_tokens;
     int32_t max_partitions;
     SplitParams split;
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(ReduceArgs a) {
     const int b = blockIdx.z;
     const int dim0 = slice * S + 4 * dl;
     const int hkv = a.num_kv_heads, G = a.num_heads / hkv, g = h / G;
-    const int max_len = a.max_blocks * 16;
+    const int max_len = a.max_len;
     const int64_t out_at = (int64_t(b) * a.num_heads + h) * D + dim0;
 
     int n = a.seq_lens[b];
@@ -187,24 +187,31 @@ hipError_t dispatch_reduce(const ReduceArgs& a, int out_dtype, bool split, hipSt
 extern "C" int paged_attention_reduce(void* out, const float* part_out, const float* part_max,
                                       const float* part_sum, const int32_t* seq_lens,
                                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, int32_t max_blocks_per_seq,
-                                      int32_t partition_size, int32_t max_partitions,
-                                      int32_t out_dtype, void* stream) {
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int32_t partition_size,
+                                      int32_t max_partitions, int32_t out_dtype, void* stream) {
     using pkv::fail;
     if (pkv::elem_bytes(out_dtype) == 0)
         return fail(PKV_EINVAL, "paged_attention_reduce: unknown out_dtype %d", out_dtype);
     if (num_seqs < 0 || num_seqs > 65535 || num_heads <= 0 || num_heads > 65535 || num_kv_heads <= 0 ||
         num_heads % num_kv_heads || max_blocks_per_seq <= 0)
         return fail(PKV_EINVAL, "paged_attention_reduce: bad num_seqs / heads / max_blocks");
+    if (block_size != 8 && block_size != 16 && block_size != 32)
+        return fail(PKV_EINVAL, "paged_attention_reduce: block_size must be 8, 16 or 32, got %d",
+                    block_size);
+    if (int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "paged_attention_reduce: max_blocks_per_seq too large");
+    const int32_t max_len = max_blocks_per_seq * block_size;
+    const int32_t max_tiles = (max_len + 15) / 16;   // 16-token tiles, as the decode plans
     if (head_dim != 64 && head_dim != 128)
         return fail(PKV_ENOTSUP, "paged_attention_reduce: head_dim %d (built: 64, 128)", head_dim);
     const bool split = partition_size == PKV_PARTITION_AUTO;
     if (split) {
         if (num_seqs > pkv::kSplitMaxSeqs || max_partitions < 2 ||
-            int64_t(num_seqs) * num_kv_heads * max_blocks_per_seq >= (int64_t(1) << 31))
+            int64_t(num_seqs) * num_kv_heads * max_tiles >= (int64_t(1) << 31))
             return fail(PKV_EINVAL, "paged_attention_reduce: arguments do not match a "
                                     "PKV_PARTITION_AUTO decode");
-    } else if (partition_size <= 0 || partition_size % PKV_BLOCK_SIZE || max_partitions <= 0) {
+    } else if (partition_size <= 0 || partition_size % 16 || max_partitions <= 0) {
         return fail(PKV_EINVAL, "paged_attention_reduce: bad partition_size / max_partitions");
     }
     if (num_seqs == 0) return pkv::ok();
@@ -221,11 +228,11 @@ extern "C" int paged_attention_reduce(void* out, const float* part_out, const fl
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
-    a.max_blocks = max_blocks_per_seq;
+    a.max_len = max_len;
     a.part_tokens = partition_size;
     a.max_partitions = max_partitions;
     a.split.units = split ? pkv::split_units() : 0;
-    a.split.min_share = split ? (max_blocks_per_seq + max_partitions - 2) / (max_partitions - 1) : 0;
+    a.split.min_share = split ? (max_tiles + max_partitions - 2) / (max_partitions - 1) : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = head_dim == 128 ? pkv::dispatch_reduce<128>(a, out_dtype, split, s)
                                            : pkv::dispatch_reduce<64>(a, out_dtype, split, s);

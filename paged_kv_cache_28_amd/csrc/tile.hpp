@@ -58,6 +58,80 @@ __device__ __forceinline__ void load_tile(KvTile<D, true>& t, const char* kt, co
         t.v[c] = *reinterpret_cast<const uint32_t*>(vt + (16 * c + col) * 16 + 4 * quad);
 }
 
+// Blocks of BS tokens (8, 16 or 32) hold 16-token tiles as follows: BS = 16, a tile is a
+// block; BS = 32, a tile is rows 16h .. 16h + 15 (h = 0, 1) of a block; BS = 8, a tile is
+// two blocks, rows 0-7 from block A and 8-15 from block B. The per-(block, KV head) layout
+// is K [d/x][BS][x], V [d][BS], so the lane's rows sit at these offsets (16-bit cache:
+// x = 8; FP8 cache: x = 16; ka/va: block A's head tile, kb/vb: block B's, row0 = 16h).
+template <int D, int BS>
+__device__ __forceinline__ void load_tile_bs(KvTile<D, false>& t, const char* ka, const char* va,
+                                             const char* kb, const char* vb, int row0, int lane) {
+    static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+    if constexpr (BS == 16) {
+        load_tile<D>(t, ka, va, lane);
+    } else {
+        const int col = lane & 15, quad = lane >> 4;
+        const char* kt = ka;
+        int krow = row0 + col;
+        const char* vt = va;
+        int vrow = row0 + 4 * quad;
+        if constexpr (BS == 8) {
+            kt = col < 8 ? ka : kb;
+            krow = col & 7;
+            vt = quad < 2 ? va : vb;
+            vrow = 4 * (quad & 1);
+        }
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+            t.k[c] = *reinterpret_cast<const uint4*>(kt + ((4 * c + quad) * BS + krow) * 16);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            t.v[c] = *reinterpret_cast<const uint2*>(vt + ((16 * c + col) * BS + vrow) * 2);
+    }
+}
+template <int D, int BS>
+__device__ __forceinline__ void load_tile_bs(KvTile<D, true>& t, const char* ka, const char* va,
+                                             const char* kb, const char* vb, int row0, int lane) {
+    static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+    if constexpr (BS == 16) {
+        load_tile<D>(t, ka, va, lane);
+    } else {
+        const int col = lane & 15, quad = lane >> 4;
+        const char* kt = ka;
+        int krow = row0 + col;
+        const char* vt = va;
+        int vrow = row0 + 4 * quad;
+        if constexpr (BS == 8) {
+            kt = col < 8 ? ka : kb;
+            krow = col & 7;
+            vt = quad < 2 ? va : vb;
+            vrow = 4 * (quad & 1);
+        }
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i)
+            t.k[i] = *reinterpret_cast<const uint4*>(kt + ((4 * i + quad) * BS + krow) * 16);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            t.v[c] = *reinterpret_cast<const uint32_t*>(vt + (16 * c + col) * BS + vrow);
+    }
+}
+
+// Block ids behind 16-token tile t of a block-table row with max_blocks entries: ida is
+// the block holding the tile's rows 0-7 (all 16 when BS >= 16), idb the one holding rows
+// 8-15 when BS = 8 (else -1); an index past the row gives -1.
+template <int BS>
+__device__ __forceinline__ void tile_ids(const int32_t* row, int max_blocks, int t, int& ida,
+                                         int& idb) {
+    if constexpr (BS == 8) {
+        ida = 2 * t < max_blocks ? row[2 * t] : -1;
+        idb = 2 * t + 1 < max_blocks ? row[2 * t + 1] : -1;
+    } else {
+        const int i = BS == 32 ? t >> 1 : t;
+        ida = i < max_blocks ? row[i] : -1;
+        idb = -1;
+    }
+}
+
 template <typename T, int D>
 __device__ __forceinline__ uint4 k_operand(const KvTile<D, false>& t, int c) { return t.k[c]; }
 template <typename T, int D>

@@ -44,7 +44,7 @@ def build(ob, device="cuda", fill=float("nan"), write_new: bool = True) -> GpuBa
     w = ob.w
     B = len(ob.lens)
     pool = pkv.kv_pool_create(ob.num_blocks, 1, w.num_kv_heads, w.head_dim, w.cache_dtype,
-                              free_order=ob.free_order)
+                              free_order=ob.free_order, block_size=w.block_size)
     prompt = []
     for b in range(B):
         pool.add_seq(b)
@@ -59,7 +59,7 @@ def build(ob, device="cuda", fill=float("nan"), write_new: bool = True) -> GpuBa
     if w.cache_dtype == "fp8" and fill is not None and fill != fill:
         fill = 0x7F
     kc, vc = pkv.alloc_caches(ob.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, device,
-                              fill=fill)
+                              fill=fill, block_size=w.block_size)
     if len(prompt_slots):
         write(w, ob.prompt_k.to(device), ob.prompt_v.to(device), kc, vc,
               torch.from_numpy(prompt_slots).to(device))
@@ -77,7 +77,8 @@ def run_decode(gb: GpuBatch, w, partition_size=0, out_dtype=torch.float32, max_p
     out = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=dev)
     parts = None
     if partition_size != 0:
-        maxp = max_partitions or pkv.max_partitions_for(gb.tables.shape[1], partition_size)
+        maxp = max_partitions or pkv.max_partitions_for(gb.tables.shape[1], partition_size,
+                                                        w.block_size)
         parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, dev))
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale,
                partition_size, parts, kv_scales=kv_scales(w))

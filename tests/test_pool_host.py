@@ -65,6 +65,20 @@ def test_seventeen_tokens_take_two_blocks():
     assert slots.tolist() == [63 * 16 + i for i in range(16)] + [62 * 16]
 
 
+@pytest.mark.parametrize("bs,blocks", [(8, [63, 62, 61]), (32, [63])])
+def test_seventeen_tokens_at_other_block_sizes(bs, blocks):
+    """The same 17 tokens: three 8-token blocks, or one 32-token block; the cache shapes
+    carry the block size."""
+    pool = pkv.kv_pool_create(64, 1, 8, 128, "bf16", free_order=np.arange(63, -1, -1),
+                              block_size=bs)
+    pool.add_seq(11)
+    slots = pool.append(11, 17)
+    assert pool.seq_blocks(11) == blocks
+    assert slots.tolist() == [blocks[t // bs] * bs + t % bs for t in range(17)]
+    assert pool.cache_shape() == ((64, 8, 16, bs, 8), (64, 8, 128, bs))
+    assert pkv.cache_shapes(64, 8, 128, "bf16", bs) == pool.cache_shape()
+
+
 def _same_state(pool, model, ids):
     assert pool.free_queue() == list(model.free)
     st_ = pool.stats()
@@ -84,12 +98,12 @@ def _same_state(pool, model, ids):
 @settings(max_examples=80, deadline=None)
 @given(st.lists(st.tuples(st.sampled_from(["add", "append", "batch", "free", "share"]),
                           st.integers(0, 9), st.integers(0, 90)), max_size=120),
-       st.integers(0, 2 ** 31 - 1))
-def test_pool_matches_oracle_model(ops, seed):
+       st.integers(0, 2 ** 31 - 1), st.sampled_from([8, 16, 32]))
+def test_pool_matches_oracle_model(ops, seed, bs):
     nb = 48
     order = np.random.default_rng(seed).permutation(nb)
-    pool = pkv.kv_pool_create(nb, 2, 2, 64, "bf16", free_order=order)
-    model = oracle.PoolModel(nb, order)
+    pool = pkv.kv_pool_create(nb, 2, 2, 64, "bf16", free_order=order, block_size=bs)
+    model = oracle.PoolModel(nb, order, block_size=bs)
     ids = list(range(10))
     codes = {"EINVAL": pkv.PKV_EINVAL, "ENOMEM": pkv.PKV_ENOMEM, "ENOENT": pkv.PKV_ENOENT}
     for op, sid, n in ops:
@@ -105,7 +119,7 @@ def test_pool_matches_oracle_model(ops, seed):
                 for i in sel:
                     if i not in model.seqs:
                         raise oracle.PoolError("ENOENT")
-                need = sum(1 for i in sel if model.seq_len(i) % 16 == 0)
+                need = sum(1 for i in sel if model.seq_len(i) % bs == 0)
                 if need > len(model.free):
                     model.alloc_failures += 1
                     raise oracle.PoolError("ENOMEM")
@@ -115,7 +129,7 @@ def test_pool_matches_oracle_model(ops, seed):
             fn_p, fn_m = (lambda: pool.free_seq(sid)), (lambda: model.free_seq(sid))
         else:
             src = (sid + 3) % 10
-            k = (n // 16) * 16
+            k = (n // bs) * bs
             fn_p, fn_m = (lambda: pool.share_prefix(sid, src, k)), \
                 (lambda: model.share_prefix(sid, src, k))
         try:
@@ -158,8 +172,11 @@ def test_exhaustion_is_atomic_and_counted():
 
 
 def test_invalid_pool_arguments():
-    with pytest.raises(pkv.PkvError):
-        pkv.kv_pool_create(16, 1, 8, 128, "bf16", block_size=32)
+    for bs in (0, 12, 24, 64):
+        with pytest.raises(pkv.PkvError):
+            pkv.kv_pool_create(16, 1, 8, 128, "bf16", block_size=bs)
+    with pytest.raises(pkv.PkvError):                   # slot ids would overflow int32
+        pkv.kv_pool_create(2 ** 27, 1, 8, 128, "bf16", block_size=32)
     with pytest.raises(pkv.PkvError):
         pkv.kv_pool_create(4, 1, 8, 128, "bf16", free_order=[0, 1, 1, 2])
     with pytest.raises(pkv.PkvError):
@@ -182,7 +199,10 @@ def _decode_rc(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(Hq=30), pkv.PKV_EINVAL),                      # not a multiple of Hkv
-    (dict(bs=32), pkv.PKV_EINVAL),
+    (dict(bs=24), pkv.PKV_EINVAL),
+    (dict(bs=64), pkv.PKV_EINVAL),
+    (dict(bs=8, ind=pkv.PKV_F32), pkv.PKV_ENOTSUP),      # fp32 inputs: 16-token blocks only
+    (dict(bs=32, mb=2 ** 26), pkv.PKV_EINVAL),          # max_blocks * block_size overflows
     (dict(d=96), pkv.PKV_ENOTSUP),
     (dict(Hq=8 * 17), pkv.PKV_ENOTSUP),                 # group of 17
     (dict(ind=pkv.PKV_F32, Hq=8 * 9, q_stride=9 * 8 * 128), pkv.PKV_ENOTSUP),
@@ -216,7 +236,7 @@ def test_cache_write_and_reduce_reject_bad_arguments():
     L = pkv.lib()
     good = dict(k=V(1 << 20), v=V(1 << 20), kc=V(1 << 20), vc=V(1 << 20), s=V(1 << 20))
     assert L.reshape_and_cache(good["k"], good["v"], good["kc"], good["vc"], good["s"], 4, 8,
-                               128, 8, 64, 1024, 1024, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+                               128, 12, 64, 1024, 1024, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
     assert L.reshape_and_cache(good["k"], good["v"], good["kc"], good["vc"], good["s"], 4, 8,
                                100, 16, 64, 1024, 1024, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
     assert L.reshape_and_cache(good["k"], good["v"], good["kc"], good["vc"], good["s"], 4, 8,
@@ -227,8 +247,9 @@ def test_cache_write_and_reduce_reject_bad_arguments():
                                pkv.PKV_BF16, None) == pkv.PKV_OK
     r = lambda *a: L.paged_attention_reduce(good["k"], good["k"], good["k"], good["k"],
                                             good["s"], *a, None)
-    assert r(4, 32, 8, 96, 64, 512, 8, pkv.PKV_F32) == pkv.PKV_ENOTSUP       # head_dim
-    assert r(4, 32, 8, 128, 64, 500, 8, pkv.PKV_F32) == pkv.PKV_EINVAL       # P % 16
-    assert r(4, 30, 8, 128, 64, 512, 8, pkv.PKV_F32) == pkv.PKV_EINVAL       # Hq % Hkv
-    assert r(4, 32, 8, 128, 64, pkv.PKV_PARTITION_AUTO, 1, pkv.PKV_F32) == pkv.PKV_EINVAL
-    assert r(2000, 32, 8, 128, 64, pkv.PKV_PARTITION_AUTO, 8, pkv.PKV_F32) == pkv.PKV_EINVAL
+    assert r(4, 32, 8, 96, 16, 64, 512, 8, pkv.PKV_F32) == pkv.PKV_ENOTSUP       # head_dim
+    assert r(4, 32, 8, 128, 16, 64, 500, 8, pkv.PKV_F32) == pkv.PKV_EINVAL       # P % 16
+    assert r(4, 30, 8, 128, 16, 64, 512, 8, pkv.PKV_F32) == pkv.PKV_EINVAL       # Hq % Hkv
+    assert r(4, 32, 8, 128, 12, 64, 512, 8, pkv.PKV_F32) == pkv.PKV_EINVAL       # block size
+    assert r(4, 32, 8, 128, 16, 64, pkv.PKV_PARTITION_AUTO, 1, pkv.PKV_F32) == pkv.PKV_EINVAL
+    assert r(2000, 32, 8, 128, 16, 64, pkv.PKV_PARTITION_AUTO, 8, pkv.PKV_F32) == pkv.PKV_EINVAL

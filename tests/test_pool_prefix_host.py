@@ -32,13 +32,14 @@ def _both(fn_pool, fn_model):
     return fn_pool(), rm
 
 
+@pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("seed", range(8))
-def test_prefix_cache_fork_and_copy_on_write_match_the_model(seed):
+def test_prefix_cache_fork_and_copy_on_write_match_the_model(seed, bs):
     gen = np.random.default_rng(100 + seed)
-    nb = int(gen.integers(24, 64))
+    nb = int(gen.integers(24, 64)) * 16 // bs
     order = gen.permutation(nb).astype(np.int32)
-    pool = pkv.kv_pool_create(nb, 2, 2, 64, "bf16", free_order=order)
-    model = oracle.PoolModel(nb, order)
+    pool = pkv.kv_pool_create(nb, 2, 2, 64, "bf16", free_order=order, block_size=bs)
+    model = oracle.PoolModel(nb, order, block_size=bs)
     prompts = [list(gen.integers(0, 3, size=int(gen.integers(1, 80)))) for _ in range(8)]
     live, nxt = [], 0
     for _ in range(300):
