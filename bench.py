@@ -34,6 +34,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# the sources that define the decode kernels: HBM counters taken for other sources are stale
+DECODE_SOURCES = ("decode.hip", "decode_kernels.hpp", "tile.hpp", "device.hpp")
 
 
 def parse():
@@ -51,6 +53,8 @@ def parse():
     ap.add_argument("--no-kernel-timer", action="store_true",
                     help="skip the kernel-timing pass (no roofline figure)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--block-size", type=int, default=None, choices=(8, 16, 32),
+                    help="tokens per KV block (default: the workload's, 16)")
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
                     help="only time copy_blocks (copy-on-write of N forked sequences' partly "
                          "filled blocks, every layer of the workload) and exit")
@@ -60,20 +64,24 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(workload: str, partition_size: int, fused: bool):
+def decode_source_sha256() -> str:
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_cache_28_amd", "csrc")
+    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                   for f in DECODE_SOURCES)).hexdigest()
+
+
+def measured_traffic(workload: str, partition_size: int, fused: bool, block_size: int):
     """HBM bytes per decode launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE runs recorded in
     profiles/ (scaled by the copy calibration), or None if those counters were taken for
-    another workload/mode or for kernel sources other than the ones built now."""
-    import hashlib
+    another workload/mode/block size or for kernel sources other than the ones built now."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
     if partition_size != 0 or not fused or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("mode") != "single pass, fused append":
+    if rec.get("mode") != "single pass, fused append" or rec.get("block_size") != block_size:
         return None
-    csrc = os.path.join(ROOT, "paged_kv_cache_28_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("decode.hip", "device.hpp"))
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+    if decode_source_sha256() != rec.get("source_sha256"):
         return None
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
@@ -272,6 +280,7 @@ def main():
     else:
         P = pkv.PKV_PARTITION_AUTO if args.partition == "auto" else int(args.partition)
     L, B, Hq, Hkv, d = w.layers, w.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    bs = args.block_size or w.block_size
     e = w.elem_bytes                 # q, out and new-row inputs
     ekv = w.cache_elem_bytes         # cache elements (1 for an FP8 cache)
     fp8 = w.cache_dtype == "fp8"
@@ -280,21 +289,21 @@ def main():
     # ---------------------------------------------------------------- setup
     lens0 = workloads.draw_seq_lens(w)                 # context at the first step
     total_steps = args.warmup + 2 * args.steps        # timed steps + kernel-timing pass
-    nb = workloads.pool_blocks_for(lens0, growth_tokens=total_steps)
+    nb = workloads.pool_blocks_for(lens0, growth_tokens=total_steps, block_size=bs)
     order = workloads.draw_free_order(nb, workloads.rng(w.seed, 1))
-    pool = pkv.kv_pool_create(nb, L, Hkv, d, w.dtype, free_order=order)
+    pool = pkv.kv_pool_create(nb, L, Hkv, d, w.cache_dtype, free_order=order, block_size=bs)
     ids = np.arange(B, dtype=np.int64)
     for b in range(B):
         pool.add_seq(int(b))
         pool.append(int(b), int(lens0[b]) - 1)        # the cached prompt
-    max_blocks = int(-(-(int(lens0.max()) + total_steps) // 16))
-    maxp = pkv.max_partitions_for(max_blocks, P) if P != 0 else 0
+    max_blocks = int(-(-(int(lens0.max()) + total_steps) // bs))
+    maxp = pkv.max_partitions_for(max_blocks, P, bs) if P != 0 else 0
 
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
     caches = []
     for _ in range(L):
-        kc, vc = pkv.alloc_caches(nb, Hkv, d, w.cache_dtype, dev)
+        kc, vc = pkv.alloc_caches(nb, Hkv, d, w.cache_dtype, dev, block_size=bs)
         if fp8:   # codes of N(0,1) draws under the workload's scales
             for t, sc in ((kc, w.k_scale), (vc, w.v_scale)):
                 x = torch.randn(t.shape, generator=g, device=dev).div_(sc).clamp_(-448, 448)
@@ -354,7 +363,7 @@ def main():
                                                   v_new[layer], d_slot, kc, vc, d_tab, d_len,
                                                   w.scale, P, po, pm, ps, maxp)
             if P != 0:
-                pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P, Hkv, max_blocks)
+                pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P, Hkv, max_blocks, bs)
 
     for s in range(args.warmup):
         step(s)
@@ -400,7 +409,7 @@ def main():
     for ln in timing_lens:
         ln = ln.astype(np.int64)
         alg.append(int(ln.sum()) * Hkv * d * 2 * ekv + 2 * B * Hq * d * e +
-                   int((-(-ln // 16)).sum()) * 4 + 4 * B + new_rows)
+                   int((-(-ln // bs)).sum()) * 4 + 4 * B + new_rows)
     alg_per_launch = sum(alg) / len(alg) if alg else float("nan")
     achieved = alg_per_launch / dec_avg_s / 1e9
     value = kv_total / elapsed / 1e9
@@ -418,7 +427,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded draws of the workload's shapes and length mix)",
         "config": {"workload": f"{w.name}-decode", "layers": L, "batch": B, "num_heads": Hq,
-                   "num_kv_heads": Hkv, "head_dim": d, "block_size": 16,
+                   "num_kv_heads": Hkv, "head_dim": d, "block_size": bs,
                    "kv_cache_dtype": ("fp8 e4m3, k_scale %g, v_scale %g" % (w.k_scale, w.v_scale)
                                       if fp8 else w.dtype),
                    "seq_len_range": [w.len_lo, w.len_hi],
@@ -426,7 +435,9 @@ def main():
                    "cache_write": ("separate launch" if args.unfused else
                                    "paged_attention_decode_append: separate launch in the balanced split"
                                    if P == pkv.PKV_PARTITION_AUTO else "fused into the decode launch"),
-                   "pool_blocks": nb, "pool_gb_per_layer": round(nb * w.block_bytes_per_layer / 1e9, 3)},
+                   "pool_blocks": nb,
+                   "pool_gb_per_layer": round(nb * w.block_bytes_per_layer * bs / w.block_size / 1e9, 3),
+                   "block_table_bytes": B * max_blocks * 4},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),
         "step_ms_percentiles": step_pct,
@@ -446,7 +457,7 @@ def main():
                      "alg_bytes_per_launch": int(alg_per_launch) if alg else None},
         "cpu_baseline": None,
     }
-    result["roofline"]["traffic"] = measured_traffic(w.name, P, not args.unfused)
+    result["roofline"]["traffic"] = measured_traffic(w.name, P, not args.unfused, bs)
     ceiling = stream_ceiling()
     result["stream_ceiling"] = ceiling
     if alg:
