@@ -1,8 +1,10 @@
 """Benchmark: one decode step of a Llama-3-8B-shaped batch through the paged KV path.
 
 A step is the whole hot path for one new token of every sequence:
-  host:   allocate_slots for each sequence (kv_pool_append_batch) and the dense block
-          tables (kv_pool_build_tables) into pinned buffers, then their copy to HBM;
+  host:   allocate_slots for each sequence (kv_pool_append_batch), the dense block
+          tables (kv_pool_build_tables) into pinned buffers, then their copy to HBM, and
+          the step's decode order from the host lengths (paged_attention_decode_plan, used
+          by every layer's single-pass launch; --no-plan: the kernel ranks the lengths);
   device: for each of the 32 layers, the new tokens' K/V written into that layer's pool
           and paged_attention_decode over the whole context, in one fused launch
           (paged_attention_decode_append; --unfused: reshape_and_cache then
@@ -10,6 +12,9 @@ A step is the whole hot path for one new token of every sequence:
 Every layer has its own K/V pool (about 313 MB, more than the 256 MB Infinity Cache),
 so each layer's context streams from HBM. Inputs are synthetic (seeded draws of the
 8B-shaped workload) and resident in HBM before timing starts.
+
+Python's garbage collector is frozen and disabled from the warm-up to the end of the
+kernel-timing pass (a full collection takes about 40 ms and would otherwise land in one step).
 
 Printed: one JSON line. `value` is KV GB/s over the whole step (algorithmic KV bytes
 read by the decode kernels / step time), timed with no per-launch instrumentation;
@@ -53,6 +58,9 @@ def parse():
     ap.add_argument("--no-kernel-timer", action="store_true",
                     help="skip the kernel-timing pass (no roofline figure)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-plan", action="store_true",
+                    help="no host-side decode plan: the single-pass kernel ranks the lengths "
+                         "itself at every launch")
     ap.add_argument("--block-size", type=int, default=None, choices=(8, 16, 32),
                     help="tokens per KV block (default: the workload's, 16)")
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
@@ -336,6 +344,8 @@ def main():
         copied[k].synchronize()                       # H2D of two steps ago has finished
         pool.append_batch(ids, out=h_slot[k].numpy())
         pool.build_tables(ids, max_blocks, h_tab[k].numpy(), h_len[k].numpy())
+        # the step's schedule, once for all layers (the single pass uses it)
+        order = None if args.no_plan else pkv.paged_attention_decode_plan(h_len[k].numpy(), Hkv)
         kv_bytes_steps.append(int(h_len[k].numpy().astype(np.int64).sum()) * Hkv * d * 2 * ekv * L)
         d_slot.copy_(h_slot[k], non_blocking=True)
         d_tab.copy_(h_tab[k], non_blocking=True)
@@ -348,23 +358,31 @@ def main():
                 pkv.reshape_and_cache_fp8(k_new[layer], v_new[layer], kc, vc, d_slot, w.k_scale,
                                           w.v_scale)
                 pkv.paged_attention_decode_fp8(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
-                                               w.k_scale, w.v_scale, P, po, pm, ps, maxp)
+                                               w.k_scale, w.v_scale, P, po, pm, ps, maxp,
+                                               seq_order=order)
             elif fp8:
                 pkv.paged_attention_decode_append_fp8(out[layer], q[layer], k_new[layer],
                                                       v_new[layer], d_slot, kc, vc, d_tab, d_len,
                                                       w.scale, w.k_scale, w.v_scale, P, po, pm,
-                                                      ps, maxp)
+                                                      ps, maxp, seq_order=order)
             elif args.unfused:
                 pkv.reshape_and_cache(k_new[layer], v_new[layer], kc, vc, d_slot)
                 pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
-                                           P, po, pm, ps, maxp)
+                                           P, po, pm, ps, maxp, seq_order=order)
             else:
                 pkv.paged_attention_decode_append(out[layer], q[layer], k_new[layer],
                                                   v_new[layer], d_slot, kc, vc, d_tab, d_len,
-                                                  w.scale, P, po, pm, ps, maxp)
+                                                  w.scale, P, po, pm, ps, maxp, seq_order=order)
             if P != 0:
                 pkv.paged_attention_reduce(out[layer], po, pm, ps, d_len, P, Hkv, max_blocks, bs)
 
+    # Python's cyclic collector stays off from the warm-up to the end of the kernel-timing
+    # pass: a full collection of the interpreter's heap (torch's objects) takes about 40 ms
+    # and would land in whichever step crosses its allocation threshold.
+    import gc
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -401,6 +419,7 @@ def main():
             ms, n = pkv.timer_read(entry)
             kernel_us[name] = round(ms / n * 1e3, 3) if n else None
         pkv.timer_enable(False)
+    gc.enable()
     dec_avg_s = kernel_us["decode"] / 1e6 if kernel_us["decode"] else float("nan")
     # algorithmic bytes of one decode launch: KV once per (seq, KV head), q, out, table rows;
     # fused, also the new rows read from the inputs and written to the pool
@@ -435,6 +454,8 @@ def main():
                    "cache_write": ("separate launch" if args.unfused else
                                    "paged_attention_decode_append: separate launch in the balanced split"
                                    if P == pkv.PKV_PARTITION_AUTO else "fused into the decode launch"),
+                   "decode_plan": ("in-kernel ranking" if args.no_plan or P != 0 else
+                                   "host plan once per step (paged_attention_decode_plan)"),
                    "pool_blocks": nb,
                    "pool_gb_per_layer": round(nb * w.block_bytes_per_layer * bs / w.block_size / 1e9, 3),
                    "block_table_bytes": B * max_blocks * 4},

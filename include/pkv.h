@@ -321,11 +321,18 @@ int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v
  *   For partition_size > 0, part_* must be non-null with max_partitions >=
  *   ceil(max_blocks_per_seq * BS / partition_size), and paged_attention_reduce()
  *   produces out for the rows with more than one partition.
+ *   seq_order:    NULL, or a host array of num_seqs ints, a permutation of 0 .. num_seqs-1
+ *                 (paged_attention_decode_plan's output): the order in which the single
+ *                 pass hands the sequences to its workgroups (copied into the launch; the
+ *                 caller may reuse or free it on return). It only schedules: the results
+ *                 are bit-identical with any order or with NULL, where the kernel ranks the
+ *                 lengths itself (one extra dependent load and a ranking at every launch).
+ *                 Used by the fp16/bf16 single pass with num_seqs <= 256; ignored otherwise.
  * Supported: head_dim in {64, 128}; in_dtype F16/BF16 with num_heads/num_kv_heads
  * <= 16; in_dtype F32 with num_heads/num_kv_heads <= 8 and 16-token blocks.
  * Errors: EINVAL (nulls, alignment, num_heads % num_kv_heads, block_size,
- * partition arguments, sizes), ENOTSUP (head_dim, group size, dtype pair, F32 with
- * block_size != 16), EHIP.
+ * partition arguments, seq_order not a permutation, sizes), ENOTSUP (head_dim, group size,
+ * dtype pair, F32 with block_size != 16), EHIP.
  * num_seqs == 0 is a no-op. */
 int paged_attention_decode(void* out, float* part_out, float* part_max, float* part_sum,
                            const void* q, int64_t q_stride, const void* k_cache,
@@ -334,7 +341,20 @@ int paged_attention_decode(void* out, float* part_out, float* part_max, float* p
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                            int32_t partition_size, int32_t max_partitions, int32_t in_dtype,
-                           int32_t out_dtype, void* stream);
+                           int32_t out_dtype, const int32_t* seq_order, void* stream);
+
+/* paged_attention_decode_plan: the host half of a decode step's scheduling, computed once
+ * per step and passed to every layer's decode call as seq_order. From a host copy of the
+ * batch's lengths (negative counts as 0): rank the sequences by length, longest first
+ * (ties by index), and deal them in serpentine rounds of R = max(1, CUs / num_kv_heads)
+ * sequences, CUs of the current HIP device: slot b of round r = b / R, position
+ * pos = b - R r, takes rank R r + pos in even rounds and R r + (n_r - 1 - pos) in odd
+ * ones (n_r = sequences in that round). Workgroups are dispatched one compute unit after
+ * the other, so a unit that holds one of the longest sequences also holds one of the
+ * shortest, and the units finish together. order_out: host int32 [num_seqs].
+ * Errors: EINVAL (NULLs, num_seqs < 0, num_kv_heads <= 0). */
+int paged_attention_decode_plan(const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t* order_out);
 
 /* paged_attention_decode_append: the decode step of one new token per sequence in one
  * call: reshape_and_cache of key/value rows b (one token each, num_tokens = num_seqs)
@@ -368,7 +388,7 @@ int paged_attention_decode_append(void* out, float* part_out, float* part_max, f
                                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                   int64_t num_blocks, float scale, int32_t partition_size,
                                   int32_t max_partitions, int32_t in_dtype, int32_t out_dtype,
-                                  void* stream);
+                                  const int32_t* seq_order, void* stream);
 
 /* paged_attention_reduce: for every (b, h) whose sequence has more than one
  * partition (np = ceil(seq_lens[b] / partition_size) > 1; with PKV_PARTITION_AUTO, np
@@ -467,7 +487,7 @@ int paged_attention_decode_fp8(void* out, float* part_out, float* part_max, floa
                                int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                                float k_scale, float v_scale, int32_t partition_size,
                                int32_t max_partitions, int32_t in_dtype, int32_t out_dtype,
-                               void* stream);
+                               const int32_t* seq_order, void* stream);
 
 /* paged_attention_decode_append_fp8: paged_attention_decode_append over FP8 caches:
  * reshape_and_cache_fp8 of one new row per sequence, then paged_attention_decode_fp8.
@@ -486,7 +506,7 @@ int paged_attention_decode_append_fp8(void* out, float* part_out, float* part_ma
                                       int64_t num_blocks, float scale, float k_scale,
                                       float v_scale, int32_t partition_size,
                                       int32_t max_partitions, int32_t in_dtype,
-                                      int32_t out_dtype, void* stream);
+                                      int32_t out_dtype, const int32_t* seq_order, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,7 @@ device memory and the current HIP stream only. The functions keep the C names:
   paged_attention_decode(...)    GQA decode attention through block tables
   paged_attention_decode_append(...)  the new token's cache write fused with the decode
   paged_attention_reduce(...)    merge of per-partition results
+  paged_attention_decode_plan(...)  host-side order of a step's single-pass decodes
   reshape_and_cache_fp8, paged_attention_decode_fp8, paged_attention_decode_append_fp8:
                                  the same over an FP8 (e4m3) cache with per-tensor K/V scales
 
@@ -87,20 +88,21 @@ def lib():
         "reshape_and_cache": ([P, P, P, P, P, I32, I32, I32, I32, I64, I64, I64, I32, P],
                               ctypes.c_int),
         "paged_attention_decode": ([P, P, P, P, P, I64, P, P, P, P, I32, I32, I32, I32, I32, I32,
-                                    I64, F, I32, I32, I32, I32, P], ctypes.c_int),
+                                    I64, F, I32, I32, I32, I32, P, P], ctypes.c_int),
+        "paged_attention_decode_plan": ([P, I32, I32, P], ctypes.c_int),
         "paged_attention_reduce": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
                                     P],
                                    ctypes.c_int),
         "paged_attention_decode_append": ([P, P, P, P, P, I64, P, P, I64, I64, P, P, P, P, P,
                                            I32, I32, I32, I32, I32, I32, I64, F, I32, I32, I32,
-                                           I32, P], ctypes.c_int),
+                                           I32, P, P], ctypes.c_int),
         "reshape_and_cache_fp8": ([P, P, P, P, P, I32, I32, I32, I32, I64, I64, I64, I32, F, F,
                                    P], ctypes.c_int),
         "paged_attention_decode_fp8": ([P, P, P, P, P, I64, P, P, P, P, I32, I32, I32, I32, I32,
-                                        I32, I64, F, F, F, I32, I32, I32, I32, P], ctypes.c_int),
+                                        I32, I64, F, F, F, I32, I32, I32, I32, P, P], ctypes.c_int),
         "paged_attention_decode_append_fp8": ([P, P, P, P, P, I64, P, P, I64, I64, P, P, P, P, P,
                                                I32, I32, I32, I32, I32, I32, I64, F, F, F, I32,
-                                               I32, I32, I32, P], ctypes.c_int),
+                                               I32, I32, I32, P, P], ctypes.c_int),
         "pkv_timer_enable": ([I32], ctypes.c_int),
         "pkv_timer_read": ([I32, P, P], ctypes.c_int),
     }
@@ -121,7 +123,8 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "reshape_and_cache_fp8", "paged_attention_decode_fp8",
             "paged_attention_decode_append_fp8", "pkv_timer_enable", "pkv_timer_read",
             "kv_pool_add_seq_prefix", "kv_pool_fork", "kv_pool_append_tokens",
-            "kv_pool_append_batch_tokens", "copy_blocks", "paged_attention_prefill")
+            "kv_pool_append_batch_tokens", "copy_blocks", "paged_attention_prefill",
+            "paged_attention_decode_plan")
 
 
 def _check(rc: int):
@@ -368,6 +371,28 @@ def kv_pool_create(num_blocks, num_layers, num_kv_heads, head_dim, dtype, free_o
 
 
 # ------------------------------------------------------------------------ kernels
+def _order(seq_order, B: int):
+    """seq_order (None or a host sequence of B ints) as (pointer, keep-alive array)."""
+    if seq_order is None:
+        return None, None
+    import numpy as np
+    a = np.ascontiguousarray(seq_order, dtype=np.int32)
+    if a.shape != (B,):
+        raise ValueError("seq_order must hold one entry per sequence")
+    return a.ctypes.data_as(ctypes.c_void_p), a
+
+
+def paged_attention_decode_plan(seq_lens, num_kv_heads: int):
+    """The single-pass decode order for a step (host int32 [B]) from a host copy of the
+    lengths; pass it as seq_order to every layer's decode call of that step."""
+    import numpy as np
+    ln = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    order = np.empty(ln.shape[0], dtype=np.int32)
+    _check(lib().paged_attention_decode_plan(ln.ctypes.data_as(ctypes.c_void_p), ln.shape[0],
+                                             num_kv_heads, order.ctypes.data_as(ctypes.c_void_p)))
+    return order
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     """key/value: device [T][Hkv][d] (token stride free, head/dim dense); caches in the
     documented layout; slot_mapping: device int32 [T]."""
@@ -389,12 +414,13 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
                            partition_size: int = 0, part_out=None, part_max=None, part_sum=None,
                            max_partitions: int = 0, num_kv_heads: int | None = None,
-                           stream=None):
+                           stream=None, seq_order=None):
     """out/q: device [B][Hq][d] (q's sequence stride is free); block_tables int32
     [B][max_blocks]; seq_lens int32 [B]. partition_size: 0 (single pass), a multiple
     of 16 (fixed partitions) or PKV_PARTITION_AUTO (balanced split); the last two
     need fp32 partial buffers part_out [B][Hq][P][d], part_max/part_sum [B][Hq][P]
-    and a paged_attention_reduce call with the same arguments."""
+    and a paged_attention_reduce call with the same arguments. seq_order: the step's
+    paged_attention_decode_plan (host), or None."""
     B, Hq, d = q.shape
     if q.stride(2) != 1 or q.stride(1) != d:
         raise ValueError("q must have dense heads/dims")
@@ -403,19 +429,20 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
     if not (block_tables.is_contiguous() and seq_lens.is_contiguous()):
         raise ValueError("block_tables and seq_lens must be contiguous")
     hkv = k_cache.shape[1] if num_kv_heads is None else num_kv_heads
+    op, _keep = _order(seq_order, B)
     _check(lib().paged_attention_decode(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
         B, Hq, hkv, d, block_size_of(v_cache), block_tables.shape[1], k_cache.shape[0], float(scale),
-        partition_size, max_partitions, dtype_code(q.dtype), dtype_code(out.dtype),
+        partition_size, max_partitions, dtype_code(q.dtype), dtype_code(out.dtype), op,
         _stream(q, stream)))
 
 
 def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_cache,
                                   block_tables, seq_lens, scale: float, partition_size: int = 0,
                                   part_out=None, part_max=None, part_sum=None,
-                                  max_partitions: int = 0, stream=None):
+                                  max_partitions: int = 0, stream=None, seq_order=None):
     """reshape_and_cache of one new token per sequence (key/value [B][Hkv][d], their
     slots in slot_mapping int32 [B]) fused with paged_attention_decode over seq_lens,
     which count the new token. Same outputs and follow-up reduce as
@@ -434,6 +461,7 @@ def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_c
         raise ValueError("block_tables, seq_lens, slot_mapping and the caches must be contiguous")
     if slot_mapping.numel() < B:
         raise ValueError("slot_mapping shorter than the batch")
+    op, _keep = _order(seq_order, B)
     _check(lib().paged_attention_decode_append(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(key, "key"),
@@ -441,7 +469,7 @@ def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_c
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
         _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, block_size_of(v_cache), block_tables.shape[1],
         k_cache.shape[0], float(scale), partition_size, max_partitions, dtype_code(q.dtype),
-        dtype_code(out.dtype), _stream(q, stream)))
+        dtype_code(out.dtype), op, _stream(q, stream)))
 
 
 # ------------------------------------------------------------------ FP8 cache
@@ -474,7 +502,7 @@ def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale: f
 def paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
                                k_scale: float, v_scale: float, partition_size: int = 0,
                                part_out=None, part_max=None, part_sum=None,
-                               max_partitions: int = 0, stream=None):
+                               max_partitions: int = 0, stream=None, seq_order=None):
     """paged_attention_decode over an FP8 cache (codes times k_scale / v_scale)."""
     B, Hq, d = q.shape
     if q.stride(2) != 1 or q.stride(1) != d:
@@ -484,20 +512,21 @@ def paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, seq_lens,
     if not (block_tables.is_contiguous() and seq_lens.is_contiguous()):
         raise ValueError("block_tables and seq_lens must be contiguous")
     _fp8_cache(k_cache, v_cache)
+    op, _keep = _order(seq_order, B)
     _check(lib().paged_attention_decode_fp8(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
         B, Hq, k_cache.shape[1], d, block_size_of(v_cache), block_tables.shape[1], k_cache.shape[0],
         float(scale), float(k_scale), float(v_scale), partition_size, max_partitions,
-        dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
+        dtype_code(q.dtype), dtype_code(out.dtype), op, _stream(q, stream)))
 
 
 def paged_attention_decode_append_fp8(out, q, key, value, slot_mapping, k_cache, v_cache,
                                       block_tables, seq_lens, scale: float, k_scale: float,
                                       v_scale: float, partition_size: int = 0, part_out=None,
                                       part_max=None, part_sum=None, max_partitions: int = 0,
-                                      stream=None):
+                                      stream=None, seq_order=None):
     """paged_attention_decode_append over an FP8 cache: the new rows are stored as
     codes and attended to as their stored values."""
     B, Hq, d = q.shape
@@ -515,6 +544,7 @@ def paged_attention_decode_append_fp8(out, q, key, value, slot_mapping, k_cache,
     _fp8_cache(k_cache, v_cache)
     if slot_mapping.numel() < B:
         raise ValueError("slot_mapping shorter than the batch")
+    op, _keep = _order(seq_order, B)
     _check(lib().paged_attention_decode_append_fp8(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(q, "q"), q.stride(0), _dev(key, "key"),
@@ -522,7 +552,7 @@ def paged_attention_decode_append_fp8(out, q, key, value, slot_mapping, k_cache,
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
         _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, block_size_of(v_cache), block_tables.shape[1],
         k_cache.shape[0], float(scale), float(k_scale), float(v_scale), partition_size,
-        max_partitions, dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
+        max_partitions, dtype_code(q.dtype), dtype_code(out.dtype), op, _stream(q, stream)))
 
 
 def paged_attention_prefill(out, q, q_start, k_cache, v_cache, block_tables, seq_lens,
@@ -614,10 +644,12 @@ def alloc_partials(B: int, Hq: int, d: int, max_partitions: int, device="cuda"):
 
 
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
-           partition_size: int = 0, partials=None, stream=None, append=None, kv_scales=None):
+           partition_size: int = 0, partials=None, stream=None, append=None, kv_scales=None,
+           seq_order=None):
     """Decode + (if partitioned or balanced) reduce: the launches of one layer's attention.
     append=(key, value, slot_mapping) writes one new token per sequence first, fused
-    (paged_attention_decode_append). kv_scales=(k_scale, v_scale): the caches are FP8."""
+    (paged_attention_decode_append). kv_scales=(k_scale, v_scale): the caches are FP8.
+    seq_order: the step's paged_attention_decode_plan (host), or None."""
     po, pm, ps = partials if partition_size != 0 else (None, None, None)
     maxp = po.shape[2] if po is not None else 0
     if kv_scales is not None:
@@ -626,18 +658,21 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
             key, value, slots = append
             paged_attention_decode_append_fp8(out, q, key, value, slots, k_cache, v_cache,
                                               block_tables, seq_lens, scale, ks, vs,
-                                              partition_size, po, pm, ps, maxp, stream=stream)
+                                              partition_size, po, pm, ps, maxp, stream=stream,
+                                              seq_order=seq_order)
         else:
             paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
-                                       ks, vs, partition_size, po, pm, ps, maxp, stream=stream)
+                                       ks, vs, partition_size, po, pm, ps, maxp, stream=stream,
+                                       seq_order=seq_order)
     elif append is not None:
         key, value, slots = append
         paged_attention_decode_append(out, q, key, value, slots, k_cache, v_cache, block_tables,
                                       seq_lens, scale, partition_size, po, pm, ps, maxp,
-                                      stream=stream)
+                                      stream=stream, seq_order=seq_order)
     else:
         paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale,
-                               partition_size, po, pm, ps, maxp, stream=stream)
+                               partition_size, po, pm, ps, maxp, stream=stream,
+                               seq_order=seq_order)
     if partition_size != 0:
         paged_attention_reduce(out, po, pm, ps, seq_lens, partition_size, k_cache.shape[1],
                                block_tables.shape[1], block_size_of(v_cache), stream=stream)

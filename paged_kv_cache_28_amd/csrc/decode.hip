@@ -7,6 +7,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <mutex>
+#include <numeric>
+#include <vector>
 
 #include "decode_kernels.hpp"
 
@@ -80,7 +82,7 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
                 int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                 int32_t partition_size, int32_t max_partitions, int32_t in_dtype,
                 int32_t out_dtype, int32_t kv_dtype, float k_scale, float v_scale,
-                const AppendIn& app, void* stream) {
+                const AppendIn& app, const int32_t* seq_order, void* stream) {
     using pkv::fail;
     const int e = pkv::elem_bytes(in_dtype);
     if (e == 0) return fail(PKV_EINVAL, "%s: unknown in_dtype %d", who, in_dtype);
@@ -151,6 +153,15 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
     if (num_seqs == 0) return pkv::ok();
     if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
         return fail(PKV_EINVAL, "%s: NULL pointer", who);
+    if (seq_order) {   // host memory: a permutation of the batch
+        std::vector<char> seen(size_t(num_seqs), 0);
+        for (int32_t i = 0; i < num_seqs; ++i) {
+            const int32_t v = seq_order[i];
+            if (v < 0 || v >= num_seqs || seen[size_t(v)])
+                return fail(PKV_EINVAL, "%s: seq_order is not a permutation of the batch", who);
+            seen[size_t(v)] = 1;
+        }
+    }
     if (grid_parts > 1 && (!part_out || !part_max || !part_sum))
         return fail(PKV_EINVAL, "%s: partitioned mode needs part_* buffers", who);
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
@@ -227,8 +238,15 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
     a.new_v_stride = app.value_stride;
     a.heads_fastest = grid_parts < 8;
     a.lpt_round = 0;
-    if (!split && grid_parts == 1 && num_seqs <= pkv::kLptMaxSeqs && in_dtype != PKV_F32)
-        a.lpt_round = std::max(1, pkv::device_cus() / num_kv_heads);
+    a.use_order = 0;
+    if (!split && grid_parts == 1 && num_seqs <= pkv::kLptMaxSeqs && in_dtype != PKV_F32) {
+        if (seq_order) {
+            a.use_order = 1;
+            for (int32_t i = 0; i < num_seqs; ++i) a.order[i] = uint16_t(seq_order[i]);
+        } else {
+            a.lpt_round = std::max(1, pkv::device_cus() / num_kv_heads);
+        }
+    }
     const dim3 grid = a.heads_fastest
                           ? dim3{unsigned(num_kv_heads), unsigned(num_seqs), unsigned(grid_parts)}
                           : dim3{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
@@ -251,12 +269,13 @@ extern "C" int paged_attention_decode(void* out, float* part_out, float* part_ma
                                       int32_t head_dim, int32_t block_size,
                                       int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                                       int32_t partition_size, int32_t max_partitions,
-                                      int32_t in_dtype, int32_t out_dtype, void* stream) {
+                                      int32_t in_dtype, int32_t out_dtype,
+                                      const int32_t* seq_order, void* stream) {
     return decode_impl("paged_attention_decode", out, part_out, part_max, part_sum, q, q_stride,
                        k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                        head_dim, block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
                        max_partitions, in_dtype, out_dtype, in_dtype, 1.0f, 1.0f,
-                       AppendIn{nullptr, nullptr, 0, 0, nullptr}, stream);
+                       AppendIn{nullptr, nullptr, 0, 0, nullptr}, seq_order, stream);
 }
 
 extern "C" int paged_attention_decode_append(
@@ -266,14 +285,15 @@ extern "C" int paged_attention_decode_append(
     const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
     float scale, int32_t partition_size, int32_t max_partitions, int32_t in_dtype,
-    int32_t out_dtype, void* stream) {
+    int32_t out_dtype, const int32_t* seq_order, void* stream) {
     if (num_seqs > 0 && !key)
         return pkv::fail(PKV_EINVAL, "paged_attention_decode_append: NULL key");
     return decode_impl("paged_attention_decode_append", out, part_out, part_max, part_sum, q,
                        q_stride, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        partition_size, max_partitions, in_dtype, out_dtype, in_dtype, 1.0f, 1.0f,
-                       AppendIn{key, value, key_stride, value_stride, slot_mapping}, stream);
+                       AppendIn{key, value, key_stride, value_stride, slot_mapping}, seq_order,
+                       stream);
 }
 
 extern "C" int paged_attention_decode_fp8(void* out, float* part_out, float* part_max,
@@ -286,12 +306,13 @@ extern "C" int paged_attention_decode_fp8(void* out, float* part_out, float* par
                                           int64_t num_blocks, float scale, float k_scale,
                                           float v_scale, int32_t partition_size,
                                           int32_t max_partitions, int32_t in_dtype,
-                                          int32_t out_dtype, void* stream) {
+                                          int32_t out_dtype, const int32_t* seq_order,
+                                          void* stream) {
     return decode_impl("paged_attention_decode_fp8", out, part_out, part_max, part_sum, q,
                        q_stride, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        partition_size, max_partitions, in_dtype, out_dtype, PKV_FP8_E4M3, k_scale,
-                       v_scale, AppendIn{nullptr, nullptr, 0, 0, nullptr}, stream);
+                       v_scale, AppendIn{nullptr, nullptr, 0, 0, nullptr}, seq_order, stream);
 }
 
 extern "C" int paged_attention_decode_append_fp8(
@@ -301,12 +322,35 @@ extern "C" int paged_attention_decode_append_fp8(
     const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
     float scale, float k_scale, float v_scale, int32_t partition_size, int32_t max_partitions,
-    int32_t in_dtype, int32_t out_dtype, void* stream) {
+    int32_t in_dtype, int32_t out_dtype, const int32_t* seq_order, void* stream) {
     if (num_seqs > 0 && !key)
         return pkv::fail(PKV_EINVAL, "paged_attention_decode_append_fp8: NULL key");
     return decode_impl("paged_attention_decode_append_fp8", out, part_out, part_max, part_sum, q,
                        q_stride, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        partition_size, max_partitions, in_dtype, out_dtype, PKV_FP8_E4M3, k_scale,
-                       v_scale, AppendIn{key, value, key_stride, value_stride, slot_mapping}, stream);
+                       v_scale, AppendIn{key, value, key_stride, value_stride, slot_mapping},
+                       seq_order, stream);
+}
+
+extern "C" int paged_attention_decode_plan(const int32_t* seq_lens, int32_t num_seqs,
+                                           int32_t num_kv_heads, int32_t* order_out) {
+    using pkv::fail;
+    if (num_seqs < 0 || num_kv_heads <= 0)
+        return fail(PKV_EINVAL, "paged_attention_decode_plan: bad num_seqs / num_kv_heads");
+    if (num_seqs == 0) return pkv::ok();
+    if (!seq_lens || !order_out) return fail(PKV_EINVAL, "paged_attention_decode_plan: NULL");
+    // rank r = the r-th longest (ties by index); slot b of round r = b / R takes rank
+    // R r + pos, or R r + (hi - 1 - pos) in odd rounds
+    std::vector<int32_t> by_rank(static_cast<size_t>(num_seqs));
+    std::iota(by_rank.begin(), by_rank.end(), 0);
+    auto len = [&](int32_t i) { return seq_lens[i] < 0 ? 0 : seq_lens[i]; };
+    std::stable_sort(by_rank.begin(), by_rank.end(),
+                     [&](int32_t x, int32_t y) { return len(x) > len(y); });
+    const int32_t R = std::max(1, pkv::device_cus() / num_kv_heads);
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        const int32_t r = b / R, pos = b - r * R, hi = std::min(R, num_seqs - r * R);
+        order_out[b] = by_rank[size_t(r * R + ((r & 1) ? hi - 1 - pos : pos))];
+    }
+    return pkv::ok();
 }

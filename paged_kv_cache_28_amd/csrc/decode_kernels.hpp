@@ -58,6 +58,8 @@
 
 namespace pkv {
 
+constexpr int kLptMaxSeqs = 256;
+
 struct DecodeArgs {
     void* out;
     float* part_out;
@@ -95,8 +97,14 @@ struct DecodeArgs {
     // CUs, and a CU keeps the workgroups of all rounds. The sequences are handed out by
     // length in serpentine order (round 0 takes ranks 0 .. R-1, round 1 ranks 2R-1 .. R,
     // ...), so a CU that holds one of the longest also holds one of the shortest and the
-    // CUs finish together. 0: sequences in index order.
+    // CUs finish together. 0: sequences in index order (or in the host plan's order).
     int32_t lpt_round;
+    // The same serpentine order computed on the host from a host copy of the lengths
+    // (paged_attention_decode_plan, once per step for every layer): slot b of the grid takes
+    // sequence order[b], so the kernel starts with its queries and block ids instead of a
+    // length load and the ranking. Only used with lpt_round == 0.
+    int32_t use_order;
+    uint16_t order[kLptMaxSeqs];
     // fused append (paged_attention_decode_append): the new token of sequence b has
     // rows new_k/new_v + b * new_*_stride ([Hkv][D]) and goes to slot_mapping[b]
     const void* new_k;
@@ -106,7 +114,6 @@ struct DecodeArgs {
     int64_t new_v_stride;
 };
 
-constexpr int kLptMaxSeqs = 256;
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -201,7 +208,9 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
     int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
     const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
-    if (a.lpt_round > 0) {   // rank the lengths (ties by index); slot b takes a serpentine rank
+    if (a.use_order) {
+        b = a.order[b];
+    } else if (a.lpt_round > 0) {   // rank the lengths (ties by index); slot b takes a serpentine rank
         __shared__ int s_n[kLptMaxSeqs];
         __shared__ int s_pick;
         const int t = threadIdx.x;

@@ -130,7 +130,7 @@ def test_append_validation(device):
             nv.data_ptr(), nk.stride(0), nv.stride(0), slots.data_ptr(), gb.k_cache.data_ptr(),
             gb.v_cache.data_ptr(), gb.tables_d.data_ptr(), gb.lens_d.data_ptr(), 2, w.num_heads,
             w.num_kv_heads, w.head_dim, 16, gb.tables.shape[1], gb.k_cache.shape[0], w.scale, 0,
-            0, pkv.PKV_BF16, pkv.PKV_F32, None]
+            0, pkv.PKV_BF16, pkv.PKV_F32, None, None]
     bad = list(args); bad[10] = None                      # no slot_mapping
     assert L.paged_attention_decode_append(*bad) == pkv.PKV_EINVAL
     bad = list(args); bad[8] = w.num_kv_heads * w.head_dim - 8   # key stride too short

@@ -188,13 +188,15 @@ def _decode_rc(**kw):
     import ctypes
     a = dict(out=1 << 20, po=None, pm=None, ps=None, q=1 << 20, q_stride=4096, kc=1 << 20,
              vc=1 << 20, bt=1 << 20, sl=1 << 20, B=4, Hq=32, Hkv=8, d=128, bs=16, mb=8, nb=64,
-             scale=0.1, P=0, maxp=0, ind=pkv.PKV_BF16, outd=pkv.PKV_F32)
+             scale=0.1, P=0, maxp=0, ind=pkv.PKV_BF16, outd=pkv.PKV_F32, order=None)
     a.update(kw)
     V = ctypes.c_void_p
+    order = None if a["order"] is None else (ctypes.c_int32 * len(a["order"]))(*a["order"])
     return pkv.lib().paged_attention_decode(
         V(a["out"]), V(a["po"]), V(a["pm"]), V(a["ps"]), V(a["q"]), a["q_stride"], V(a["kc"]),
         V(a["vc"]), V(a["bt"]), V(a["sl"]), a["B"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["mb"],
-        a["nb"], a["scale"], a["P"], a["maxp"], a["ind"], a["outd"], None)
+        a["nb"], a["scale"], a["P"], a["maxp"], a["ind"], a["outd"],
+        ctypes.cast(order, V) if order is not None else None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -220,6 +222,8 @@ def _decode_rc(**kw):
     (dict(P=pkv.PKV_PARTITION_AUTO, maxp=1, po=1 << 20, pm=1 << 20, ps=1 << 20), pkv.PKV_EINVAL),
     (dict(P=pkv.PKV_PARTITION_AUTO, maxp=8, B=1025), pkv.PKV_ENOTSUP),
     (dict(P=pkv.PKV_PARTITION_AUTO, maxp=8, ind=pkv.PKV_F32, q_stride=8192), pkv.PKV_ENOTSUP),
+    (dict(order=[0, 1, 1, 2]), pkv.PKV_EINVAL),         # seq_order not a permutation
+    (dict(order=[0, 1, 2, 4]), pkv.PKV_EINVAL),
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, code):
     assert _decode_rc(**kw) == code
@@ -253,3 +257,20 @@ def test_cache_write_and_reduce_reject_bad_arguments():
     assert r(4, 32, 8, 128, 12, 64, 512, 8, pkv.PKV_F32) == pkv.PKV_EINVAL       # block size
     assert r(4, 32, 8, 128, 16, 64, pkv.PKV_PARTITION_AUTO, 1, pkv.PKV_F32) == pkv.PKV_EINVAL
     assert r(2000, 32, 8, 128, 16, 64, pkv.PKV_PARTITION_AUTO, 8, pkv.PKV_F32) == pkv.PKV_EINVAL
+
+
+# --------------------------------------------------- host-side decode plan (ordering only)
+def test_decode_plan_is_a_length_ranked_permutation():
+    gen = np.random.default_rng(5)
+    for B in (1, 7, 64, 256):
+        lens = gen.integers(-3, 3000, size=B).astype(np.int32)
+        lens[::9] = lens[0]                       # ties
+        for hkv in (1, 8, 64, 1024):
+            order = pkv.paged_attention_decode_plan(lens, hkv)
+            assert sorted(order.tolist()) == list(range(B))
+        # one sequence per round (R = 1 once num_kv_heads >= the CU count): longest first,
+        # ties by index
+        ranked = sorted(range(B), key=lambda i: (-max(int(lens[i]), 0), i))
+        assert pkv.paged_attention_decode_plan(lens, 1 << 20).tolist() == ranked
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_attention_decode_plan(np.array([1, 2], np.int32), 0)
