@@ -1,5 +1,6 @@
 """Full-size parity: one layer of each workload at its real size, in the launch mode the
-bench uses for it and in the balanced split, checked on sampled outputs.
+bench uses for it (the 8B single pass with the step's host plan) and in the balanced split,
+and the 8B workload at 8 and 32 tokens per block, checked on sampled outputs.
 
 * slots and block tables: every one, bit-exact against the oracle's pool model;
 * cache write: a random sample of tokens read back through the documented layout,
@@ -35,14 +36,15 @@ def device():
 class Layer:
     """One layer of a workload through the library, with its oracle-side twin state."""
 
-    def __init__(self, w, device, layer=0):
+    def __init__(self, w, device, layer=0, block_size=16):
         self.w = w
+        self.bs = bs = block_size
         lens = workloads.draw_seq_lens(w).astype(np.int64)
         B, Hkv, d = len(lens), w.num_kv_heads, w.head_dim
-        nb = workloads.pool_blocks_for(lens)
+        nb = workloads.pool_blocks_for(lens, block_size=bs)
         order = workloads.draw_free_order(nb, workloads.rng(w.seed, 1, layer))
-        pool = pkv.kv_pool_create(nb, 1, Hkv, d, w.cache_dtype, free_order=order)
-        model = oracle.PoolModel(nb, order)
+        pool = pkv.kv_pool_create(nb, 1, Hkv, d, w.cache_dtype, free_order=order, block_size=bs)
+        model = oracle.PoolModel(nb, order, block_size=bs)
         prompt = np.maximum(lens - 1, 0)
         ps_p, ps_m = [], []
         for b in range(B):
@@ -54,7 +56,7 @@ class Layer:
         assert np.array_equal(self.prompt_slots, np.asarray(ps_m, np.int32)), "prompt slots"
         self.new_slots = pool.append_batch(list(range(B)))
         assert self.new_slots.tolist() == [model.append(b, 1)[0] for b in range(B)], "new slots"
-        self.max_blocks = int(-(-lens.max() // 16))
+        self.max_blocks = int(-(-lens.max() // bs))
         self.tables, self.lens = pool.build_tables(list(range(B)), self.max_blocks)
         mt, ml = model.tables(list(range(B)), self.max_blocks)
         assert np.array_equal(self.tables, mt) and np.array_equal(self.lens, ml), "tables"
@@ -67,7 +69,8 @@ class Layer:
         self.q = workloads.draw_q_device(w, (3, layer), device)
         self.fp8 = w.cache_dtype == "fp8"
         self.kc, self.vc = pkv.alloc_caches(nb, Hkv, d, w.cache_dtype, device,
-                                            fill=0x7F if self.fp8 else float("nan"))
+                                            fill=0x7F if self.fp8 else float("nan"),
+                                            block_size=bs)
         for k, v, sl in ((self.pk, self.pv, self.prompt_slots), (self.nk, self.nv, self.new_slots)):
             sl = torch.from_numpy(sl).to(device)
             if self.fp8:
@@ -79,17 +82,18 @@ class Layer:
         self.num_blocks = nb
         self.device = device
 
-    def decode(self, P):
+    def decode(self, P, plan=False):
         w, dev = self.w, self.device
         B = len(self.lens)
         out = torch.full((B, w.num_heads, w.head_dim), float("nan"), dtype=torch.float32,
                          device=dev)
         parts = None
         if P != 0:
-            maxp = pkv.max_partitions_for(self.max_blocks, P)
+            maxp = pkv.max_partitions_for(self.max_blocks, P, self.bs)
             parts = pkv.alloc_partials(B, w.num_heads, w.head_dim, maxp, dev)
+        order = pkv.paged_attention_decode_plan(self.lens, w.num_kv_heads) if plan else None
         pkv.decode(out, self.q, self.kc, self.vc, self.tables_d, self.lens_d, w.scale, P, parts,
-                   kv_scales=(w.k_scale, w.v_scale) if self.fp8 else None)
+                   kv_scales=(w.k_scale, w.v_scale) if self.fp8 else None, seq_order=order)
         torch.cuda.synchronize()
         return out
 
@@ -111,15 +115,16 @@ class Layer:
         gen = np.random.default_rng(seed)
         T = len(self.prompt_slots)
         pick = gen.choice(T, size=min(n, T), replace=False) if T else np.zeros(0, np.int64)
+        bs = self.bs
         slots = torch.from_numpy(self.prompt_slots[pick].astype(np.int64)).to(self.device)
-        blk, off = slots // 16, slots % 16
-        kv = self.kc.view(self.num_blocks, w.num_kv_heads, w.head_dim // x, 16, x)
+        blk, off = slots // bs, slots % bs
+        kv = self.kc.view(self.num_blocks, w.num_kv_heads, w.head_dim // x, bs, x)
         got_k = kv[blk, :, :, off, :].reshape(len(pick), w.num_kv_heads, w.head_dim)
         got_v = self.vc[blk, :, :, off]
         idx = torch.from_numpy(pick).to(self.device)
         nslots = torch.from_numpy(self.new_slots.astype(np.int64)).to(self.device)
-        got_nk = kv[nslots // 16, :, :, nslots % 16, :].reshape(-1, w.num_kv_heads, w.head_dim)
-        got_nv = self.vc[nslots // 16, :, :, nslots % 16]
+        got_nk = kv[nslots // bs, :, :, nslots % bs, :].reshape(-1, w.num_kv_heads, w.head_dim)
+        got_nv = self.vc[nslots // bs, :, :, nslots % bs]
         if self.fp8:
             def codes(x, sc):
                 return torch.from_numpy(oracle.fp8_quantize(x.cpu(), w.dtype, sc))
@@ -165,17 +170,23 @@ class Layer:
         return err
 
 
-CASES = [("llama8b", 0, 0), ("llama8b", AUTO, 0), ("llama8b_fp8", 0, 48), ("llama8b_fp8", AUTO, 48),
-         ("llama70b", 512, 96), ("llama70b", AUTO, 96), ("long", 512, 24), ("long", AUTO, 24)]
+# (workload, partition size, random rows, block size, host plan)
+CASES = [("llama8b", 0, 0, 16, True), ("llama8b", 0, 0, 16, False), ("llama8b", AUTO, 0, 16, False),
+         ("llama8b_fp8", 0, 48, 16, True), ("llama8b_fp8", AUTO, 48, 16, False),
+         ("llama8b", 0, 0, 8, True), ("llama8b", AUTO, 0, 32, False),
+         ("llama8b_fp8", 0, 48, 32, True),
+         ("llama70b", 512, 96, 16, False), ("llama70b", AUTO, 96, 16, False),
+         ("long", 512, 24, 16, False), ("long", AUTO, 24, 16, False)]
 
 
-@pytest.mark.parametrize("name,P,n_random", CASES,
-                         ids=[f"{n}-{'auto' if p == AUTO else p}" for n, p, _ in CASES])
-def test_full_size_layer(name, P, n_random, device):
+@pytest.mark.parametrize("name,P,n_random,bs,plan", CASES,
+                         ids=[f"{n}-{'auto' if p == AUTO else p}-bs{bs}{'-plan' if pl else ''}"
+                              for n, p, _, bs, pl in CASES])
+def test_full_size_layer(name, P, n_random, bs, plan, device):
     w = W[name]
-    layer = Layer(w, device)
+    layer = Layer(w, device, block_size=bs)
     layer.check_cache_sample()
-    out = layer.decode(P)
+    out = layer.decode(P, plan)
     if name == "llama8b":
         rows = [(b, h) for b in range(w.batch) for h in range(w.num_heads)]
     else:
