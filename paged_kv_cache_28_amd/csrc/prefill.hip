@@ -82,7 +82,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, quad = lane >> 4;
-    const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // query tiles in reverse: under the causal mask a later tile sees more keys, so the
+    // longest workgroups are dispatched first and the short ones fill the tail
+    const int qt = int(gridDim.x) - 1 - int(blockIdx.x), g = blockIdx.y, b = blockIdx.z;
     const int G = a.group;
     const int QT = 16 * NC / G;         // query tokens of this workgroup
     const int q0 = a.q_start[b];
