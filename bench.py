@@ -252,6 +252,181 @@ def bench_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_churn(args):
+    """Continuous-batching churn: the 8B shape on a ~200 GB pool, 256 live sequences with log-uniform prompts in [16, 32768], 20% of them
+    aliasing a 1,024-token system prompt written once. A step retires 5% of the live
+    sequences (their blocks back to the free queue), admits as many (pool allocation of
+    their prompts, and in every layer the prompts' K/V written with reshape_and_cache),
+    appends one token to every live sequence and decodes it in every layer (balanced split:
+    the new rows' cache write, the decode and the reduce). Timed: K steps after W warm-up
+    steps with no instrumentation, then K more steps under the library's kernel timer."""
+    import gc
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_28_amd as pkv
+    import workloads
+    w = workloads.WORKLOADS["churn"]
+    dev = torch.device("cuda:0")
+    L, B, Hq, Hkv, d = w.layers, w.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    e = w.elem_bytes
+    tdt = pkv.torch_dtype(w.dtype)
+    P = pkv.PKV_PARTITION_AUTO
+    nb = workloads.churn_pool_blocks(w)
+    order = workloads.draw_free_order(nb, workloads.rng(w.seed, 1))
+    pool = pkv.kv_pool_create(nb, L, Hkv, d, w.dtype, free_order=order)
+    total_steps = args.warmup + 2 * args.steps
+    max_blocks = -(-(w.prefix_tokens + w.prompt_hi + total_steps + 1) // 16)
+    maxp = pkv.max_partitions_for(max_blocks, P)
+    caches = [pkv.alloc_caches(nb, Hkv, d, w.dtype, dev) for _ in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    SRC = 1 << 17   # prompt rows are slices of one random buffer (values do not set the time)
+    src_k = torch.randn((SRC, Hkv, d), generator=g, device=dev, dtype=tdt)
+    src_v = torch.randn((SRC, Hkv, d), generator=g, device=dev, dtype=tdt)
+    q = [torch.randn((B, Hq, d), generator=g, device=dev, dtype=tdt) for _ in range(L)]
+    k_new = torch.randn((B, Hkv, d), generator=g, device=dev, dtype=tdt)
+    v_new = torch.randn((B, Hkv, d), generator=g, device=dev, dtype=tdt)
+    out = torch.empty((B, Hq, d), device=dev, dtype=tdt)
+    parts = pkv.alloc_partials(B, Hq, d, maxp, dev)
+
+    def write_prompts(slots, timed_cw=None):
+        """The prompt rows of every layer; slots: int32 host array."""
+        if len(slots) == 0:
+            return
+        for c0 in range(0, len(slots), SRC):
+            sl = torch.from_numpy(np.ascontiguousarray(slots[c0:c0 + SRC])).to(dev)
+            n = sl.numel()
+            for layer in range(L):
+                kc, vc = caches[layer]
+                if timed_cw is not None:
+                    timed_cw[1] += pkv.timer_read(pkv.PKV_TIMER_CACHE_WRITE)[0]
+                pkv.reshape_and_cache(src_k[:n], src_v[:n], kc, vc, sl)
+                if timed_cw is not None:
+                    timed_cw[0] += pkv.timer_read(pkv.PKV_TIMER_CACHE_WRITE)[0]
+
+    # the shared system prompt (sequence -1) and the initial batch
+    PREFIX = -1
+    pool.add_seq(PREFIX)
+    init_slots = [pool.append(PREFIX, w.prefix_tokens)]
+    live, sharer, next_id = [], {}, 0
+    for is_sharer, n in workloads.draw_churn_initial(w, workloads.rng(w.seed, 5, 0)):
+        pool.add_seq(next_id)
+        if is_sharer:
+            pool.share_prefix(next_id, PREFIX, w.prefix_tokens)
+        init_slots.append(pool.append(next_id, n))
+        live.append(next_id)
+        sharer[next_id] = is_sharer
+        next_id += 1
+    write_prompts(np.concatenate(init_slots))
+    torch.cuda.synchronize()
+    print(f"churn: pool of {nb} blocks, {len(live)} sequences written", file=sys.stderr, flush=True)
+
+    h_tab = torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True)
+    h_len = torch.empty(B, dtype=torch.int32, pin_memory=True)
+    stats = {"prompt_tokens": 0, "kv_logical": 0, "kv_unique": 0}
+    prefix_bytes = w.prefix_tokens * Hkv * d * 2 * e
+
+    def step(s, timed_cw=None):
+        nonlocal next_id
+        retire, admits = workloads.draw_churn_step(w, workloads.rng(w.seed, 6, 0, s), live)
+        for pos in sorted(retire, reverse=True):
+            sid = live.pop(pos)
+            pool.free_seq(sid)
+            sharer.pop(sid)
+        pslots = []
+        for is_sharer, n in admits:
+            pool.add_seq(next_id)
+            if is_sharer:
+                pool.share_prefix(next_id, PREFIX, w.prefix_tokens)
+            pslots.append(pool.append(next_id, n))
+            live.append(next_id)
+            sharer[next_id] = is_sharer
+            next_id += 1
+        pslots = np.concatenate(pslots) if pslots else np.zeros(0, np.int32)
+        stats["prompt_tokens"] += len(pslots)
+        dslots = torch.from_numpy(pool.append_batch(live)).to(dev)
+        pool.build_tables(live, max_blocks, h_tab.numpy(), h_len.numpy())
+        lens = h_len.numpy().astype(np.int64)
+        n_share = sum(1 for sid in live if sharer[sid])
+        kv = int(lens.sum()) * Hkv * d * 2 * e
+        stats["kv_logical"] += kv * L
+        stats["kv_unique"] += (kv - max(0, n_share - 1) * prefix_bytes) * L
+        d_tab = h_tab.to(dev, non_blocking=True)
+        d_len = h_len.to(dev, non_blocking=True)
+        write_prompts(pslots, timed_cw)
+        for layer in range(L):
+            kc, vc = caches[layer]
+            if timed_cw is not None:
+                timed_cw[1] += pkv.timer_read(pkv.PKV_TIMER_CACHE_WRITE)[0]
+            pkv.decode(out, q[layer], kc, vc, d_tab, d_len, w.scale, P, parts,
+                       append=(k_new, v_new, dslots))
+        torch.cuda.synchronize()   # the pinned table buffer is reused by the next step
+
+    gc.collect()
+    gc.freeze()
+    gc.disable()
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    print("churn: warm-up done", file=sys.stderr, flush=True)
+    stats = {k: 0 for k in stats}
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timed = dict(stats)
+    print("churn: timed steps done", file=sys.stderr, flush=True)
+    # kernel-timing pass: prompt writes timed alone (cw[0]), the new rows' writes (cw[1])
+    stats = {k: 0 for k in stats}
+    cw = [0.0, 0.0]
+    pkv.timer_enable(True)
+    for s in range(args.steps):
+        step(args.warmup + args.steps + s, cw)
+    torch.cuda.synchronize()
+    cw[1] += pkv.timer_read(pkv.PKV_TIMER_CACHE_WRITE)[0]
+    dec_ms, dec_n = pkv.timer_read(pkv.PKV_TIMER_DECODE)
+    red_ms, red_n = pkv.timer_read(pkv.PKV_TIMER_REDUCE)
+    pkv.timer_enable(False)
+    gc.enable()
+    attn_s = (dec_ms + red_ms) * 1e-3
+    pt = stats["prompt_tokens"]
+    prompt_bytes = pt * Hkv * d * 2 * e * L          # written (the rows are read as much)
+    result = {
+        "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + decode tokens/s/layer",
+        "value": round(timed["kv_logical"] / elapsed / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded churn events, prompt lengths and prefix sharing)",
+        "config": {"workload": "churn", "layers": L, "batch": B, "num_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": d, "block_size": 16,
+                   "pool_blocks": nb, "pool_gb": round(nb * w.block_bytes_per_layer * L / 1e9, 1),
+                   "prefix_tokens": w.prefix_tokens, "share_frac": w.share_frac,
+                   "retire_frac": w.retire_frac, "prompt_range": [w.prompt_lo, w.prompt_hi],
+                   "partition_size": "auto"},
+        "step_kv_gb_s_note": "value = logical KV bytes read by the decode over whole steps "
+                             "(retire + admit + prompt writes + 32 layers of decode) / step time",
+        "attention_kv_logical_gb_s": round(stats["kv_logical"] / attn_s / 1e9, 1),
+        "attention_kv_unique_gb_s": round(stats["kv_unique"] / attn_s / 1e9, 1),
+        "attention_pct_of_peak": round(100 * stats["kv_logical"] / attn_s / 1e9 / HBM_PEAK_GBS, 2),
+        "decode_kernel_us": round(dec_ms * 1e3 / dec_n, 2) if dec_n else None,
+        "reduce_kernel_us": round(red_ms * 1e3 / red_n, 2) if red_n else None,
+        "new_rows_cache_write_us": round(cw[1] * 1e3 / dec_n, 2) if dec_n else None,
+        "prompt_tokens_per_step": round(pt / args.steps, 1),
+        "prompt_write_us_per_layer": round(cw[0] * 1e3 / (args.steps * L), 2),
+        "prompt_write_gb_s": round(2 * prompt_bytes / (cw[0] * 1e-3) / 1e9, 1) if cw[0] else None,
+        "decode_tok_s_per_layer": round(B * args.steps * L / (attn_s + cw[1] * 1e-3), 1),
+        "kernel_timing": "library timer (HIP events bound to each launch) in a second pass of "
+                         "K steps; the prompt writes are read back one by one",
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    pool.close()
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -261,6 +436,12 @@ def main():
         bench_copy_blocks(args)
         return
     import workloads as _wl
+    if args.config == "churn":
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_churn(args)
+        return
     if _wl.WORKLOADS[args.config].prefill_tokens:
         if args.gpus != 1:
             print("bench.py measures one GPU only", file=sys.stderr)

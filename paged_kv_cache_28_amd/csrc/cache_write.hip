@@ -3,11 +3,16 @@
 // taken only when the last one is full ("vLLM ve Triton ile maliyet optimizasyonu",
 // §03 Yöntem, step 3); this kernel is the device half of that step.
 //
-// One thread moves one 16-byte group of x = 16 / element_bytes dimensions of one
-// (token, KV head): K keeps the group together (cache layout [blk][g][d/x][BS][x]),
-// V spreads it over x rows of its [blk][g][d][BS] tile. A pure bit copy. The block size
-// BS = 2^lbs (8, 16 or 32 tokens) is a run-time argument: slot s is row s % BS of
-// block s / BS.
+// A pure bit copy into K's [blk][g][d/x][BS][x] layout (x = 16 / element_bytes, one
+// 16-byte group per row) and V's [blk][g][d][BS] tile. The block size BS = 2^lbs (8, 16
+// or 32 tokens) is a run-time argument: slot s is row s % BS of block s / BS. Two forms:
+// - flat: one thread per 16-byte group of one (token, KV head). Every wave is busy even
+//   for a decode step's few scattered tokens, but a lane's K write lands BS * 16 bytes
+//   from its neighbour's and its V elements BS * element_bytes apart;
+// - rows (bulk writes: a prompt, a prefill chunk): one wave per 16 consecutive tokens of
+//   one KV head, which turns the rows around in LDS so that consecutive lanes write
+//   consecutive tokens, i.e. contiguous bytes where the slots are consecutive.
+// The launcher takes the rows form when it still gives every compute unit a wave.
 // reshape_and_cache_fp8 stores the e4m3 codes of x / scale instead (FP8 KV cache).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -55,6 +60,58 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
         const uint32_t* w = reinterpret_cast<const uint32_t*>(&vv);
 #pragma unroll
         for (int k = 0; k < X; ++k) reinterpret_cast<uint32_t*>(vdst + k * bs * E)[0] = w[k];
+    }
+}
+
+// Rows form: one wave per (16 consecutive tokens, KV head). The rows are read coalesced
+// (consecutive lanes take consecutive 16-byte groups of one token), turned around in LDS,
+// and written with consecutive lanes on consecutive tokens: for K the same 16-byte group
+// of 16 tokens, for V the same dimension of 16 tokens. Tokens with consecutive slots in
+// one block (a prompt, a chunk) then write contiguous bytes whatever the block alignment;
+// any other slot mapping is still written element by element correctly.
+template <int E>
+__global__ __launch_bounds__(64) void reshape_and_cache_rows_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, char* __restrict__ kc,
+    char* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens, int32_t hkv,
+    int32_t d, int64_t num_blocks, int64_t key_stride_b, int64_t value_stride_b, int32_t lbs) {
+    constexpr int X = 16 / E;               // elements per 16-byte group
+    extern __shared__ uint4 s_rows[];
+    const int nchunk = d / X;               // 16-byte groups per row
+    const int per = 16 * nchunk;            // groups of the 16 tokens
+    const int vpad = nchunk + 1;            // LDS row pitch of V (uint4), padded
+    uint4* Kl = s_rows;                     // group c of token r at c * 17 + r
+    uint4* Vl = s_rows + nchunk * 17;       // token r's V row at r * vpad
+    const int g = blockIdx.y;
+    const int64_t t0 = int64_t(blockIdx.x) * 16;
+    const int lane = threadIdx.x;
+    const int bs = 1 << lbs;
+    // this lane's token for the writes (r = lane % 16) and its slot
+    const int rw = lane & 15;
+    int64_t slot = t0 + rw < num_tokens ? int64_t(slots[t0 + rw]) : -1;
+    if (slot >= (num_blocks << lbs)) slot = -1;
+    for (int q = lane; q < per; q += 64) {
+        const int r = q / nchunk, c = q - r * nchunk;
+        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+        if (t0 + r < num_tokens) {
+            kv = *reinterpret_cast<const uint4*>(key + (t0 + r) * key_stride_b + (int64_t(g) * d + c * X) * E);
+            vv = *reinterpret_cast<const uint4*>(value + (t0 + r) * value_stride_b + (int64_t(g) * d + c * X) * E);
+        }
+        Kl[c * 17 + r] = kv;
+        Vl[r * vpad + c] = vv;
+    }
+    __syncthreads();
+    if (slot < 0) return;   // no barrier follows
+    const int64_t tile = (slot >> lbs) * hkv + g;
+    const int off = int(slot & (bs - 1));
+    for (int c = lane >> 4; c < nchunk; c += 4)   // K: group c of token rw
+        *reinterpret_cast<uint4*>(kc + ((tile * nchunk + c) * bs + off) * 16) = Kl[c * 17 + rw];
+    const char* vrow = reinterpret_cast<const char*>(Vl + rw * vpad);
+    for (int i = lane >> 4; i < d; i += 4) {      // V: dimension i of token rw
+        char* dst = vc + ((tile * d + i) * bs + off) * E;
+        if constexpr (E == 2)
+            *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(vrow + i * E);
+        else
+            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(vrow + i * E);
     }
 }
 
@@ -189,16 +246,32 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
     char* kcp = static_cast<char*>(k_cache);
     char* vcp = static_cast<char*>(v_cache);
     const pkv::LaunchEvents ev = pkv::timer_events(PKV_TIMER_CACHE_WRITE);
-    if (e == 2)
+    // rows form: waves = token tiles x KV heads; LDS = K groups (pitch 17) + V rows
+    // (pitch d/x + 1)
+    const int64_t rtiles = (int64_t(num_tokens) + 15) / 16;
+    const size_t rlds = sizeof(uint4) * size_t(head_dim / x) * (17 + 16) + sizeof(uint4) * 16;
+    const bool rows = rtiles * num_kv_heads >= pkv::device_cus() && rtiles <= 0x7fffffff &&
+                      num_kv_heads <= 65535 && rlds <= 65536;
+    const int64_t kst = key_stride * e, vst = value_stride * e;
+    if (rows) {
+        const dim3 rgrid{unsigned(rtiles), unsigned(num_kv_heads), 1u};
+        if (e == 2)
+            hipExtLaunchKernelGGL(pkv::reshape_and_cache_rows_kernel<2>, rgrid, dim3(64), rlds, s,
+                                  ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
+                                  num_kv_heads, head_dim, num_blocks, kst, vst, lbs);
+        else
+            hipExtLaunchKernelGGL(pkv::reshape_and_cache_rows_kernel<4>, rgrid, dim3(64), rlds, s,
+                                  ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
+                                  num_kv_heads, head_dim, num_blocks, kst, vst, lbs);
+    } else if (e == 2) {
         hipExtLaunchKernelGGL(pkv::reshape_and_cache_kernel<2>, dim3(unsigned(grid)), dim3(256), 0,
                               s, ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
-                              num_kv_heads, head_dim, num_blocks, key_stride * 2, value_stride * 2,
-                              lbs);
-    else
+                              num_kv_heads, head_dim, num_blocks, kst, vst, lbs);
+    } else {
         hipExtLaunchKernelGGL(pkv::reshape_and_cache_kernel<4>, dim3(unsigned(grid)), dim3(256), 0,
                               s, ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
-                              num_kv_heads, head_dim, num_blocks, key_stride * 4, value_stride * 4,
-                              lbs);
+                              num_kv_heads, head_dim, num_blocks, kst, vst, lbs);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return fail(PKV_EHIP, "reshape_and_cache: launch failed: %s", hipGetErrorString(err));

@@ -18,12 +18,6 @@ template hipError_t dispatch_bs<16>(const DecodeArgs&, int, int, int, dim3, hipS
 extern template hipError_t dispatch_bs<8>(const DecodeArgs&, int, int, int, dim3, hipStream_t, bool, bool);
 extern template hipError_t dispatch_bs<32>(const DecodeArgs&, int, int, int, dim3, hipStream_t, bool, bool);
 
-// Waves per compute unit that the balanced split plans for: two workgroups of four
-// waves (two waves per SIMD) on every unit. With two tiles in flight per wave this keeps
-// enough reads queued to saturate HBM; deeper queues measured slower (the extra reads
-// only add queueing delay and spread the finishing times of the waves).
-// PKV_SPLIT_WAVES_PER_CU overrides the count (a tuning knob; it must not change between
-// a decode and its reduce).
 int device_cus() {
     static std::mutex mu;
     static int cache[64] = {0};
@@ -40,6 +34,12 @@ int device_cus() {
     return cache[dev];
 }
 
+// Waves per compute unit that the balanced split plans for: two workgroups of four
+// waves (two waves per SIMD) on every unit. With two tiles in flight per wave this keeps
+// enough reads queued to saturate HBM; deeper queues measured slower (the extra reads
+// only add queueing delay and spread the finishing times of the waves).
+// PKV_SPLIT_WAVES_PER_CU overrides the count (a tuning knob; it must not change between
+// a decode and its reduce).
 int split_units() {
     static std::mutex mu;
     static int cache[64] = {0};
@@ -47,16 +47,12 @@ int split_units() {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     std::lock_guard<std::mutex> lock(mu);
     if (cache[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
         int per = 8;
         if (const char* env = std::getenv("PKV_SPLIT_WAVES_PER_CU")) {
             const int v = std::atoi(env);
             if (v > 0 && v <= 64) per = v;
         }
-        cache[dev] = cus * per;
+        cache[dev] = device_cus() * per;
     }
     return cache[dev];
 }

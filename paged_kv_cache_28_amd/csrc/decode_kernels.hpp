@@ -1039,6 +1039,4 @@ hipError_t dispatch_bs(const DecodeArgs& a, int head_dim, int in_dtype, int out_
                : dispatch_16<64, false, BS>(a, in_dtype, out_dtype, grid, s, split);
 }
 
-int device_cus();
-
 }  // namespace pkv

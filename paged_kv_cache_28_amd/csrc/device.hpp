@@ -194,4 +194,8 @@ __device__ __forceinline__ float max_over_rows(float x) {
                  __builtin_bit_cast(float, (unsigned)r32[1]));
 }
 
+// Host side: compute units of the current device (cached per device; 256 when the
+// query fails). Launchers size grids and plans by it.
+int device_cus();
+
 }  // namespace pkv

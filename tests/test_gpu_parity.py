@@ -109,6 +109,52 @@ def test_cache_write_with_token_stride_and_skipped_slots(device):
     assert np.array_equal(oracle.raw(kc), okc) and np.array_equal(oracle.raw(vc), ovc)
 
 
+# The library picks between two kernels by size: a flat one (a thread per 16-byte group,
+# decode steps) and a rows one (a wave per 16 tokens of a KV head, prompts and chunks)
+# once ceil(T / 16) * Hkv reaches the device's compute units (256 on MI355X). The cases
+# below sit on either side of that line for each element size and block size.
+CW_CASES = [
+    ("bf16", 16, 128, 8, 519),    # rows: 33 tiles x 8 heads
+    ("f16", 8, 64, 8, 517),
+    ("bf16", 32, 128, 8, 530),
+    ("f32", 16, 128, 2, 2055),    # rows with 4-byte elements: 129 tiles x 2 heads
+    ("f32", 32, 64, 4, 1030),
+    ("f32", 8, 128, 1, 40),       # flat
+    ("bf16", 16, 128, 8, 40),     # flat
+]
+
+
+@pytest.mark.parametrize("dtype,bs,d,hkv,T", CW_CASES)
+@pytest.mark.parametrize("pattern", ["consecutive", "scattered"])
+def test_cache_write_forms_are_bit_exact(dtype, bs, d, hkv, T, pattern, device):
+    """Consecutive slots from a start inside a block (a prompt), or a random permutation;
+    key/value are strided slices of a fused buffer; some slots are negative and one lies
+    past the pool (both write nothing)."""
+    import paged_kv_cache_28_amd as pkv
+    w = dataclasses.replace(W["llama8b"], num_kv_heads=3 * hkv, head_dim=d, dtype=dtype,
+                            block_size=bs)
+    fused = workloads.draw_tokens(T, w, workloads.rng(92, T, bs))
+    key, value = fused[:, :hkv], fused[:, hkv:2 * hkv]
+    if pattern == "consecutive":
+        start = 3 * bs + 5
+        nb = (start + T) // bs + 2
+        slots = (start + np.arange(T)).astype(np.int32)
+    else:
+        nb = 2 * T // bs + 2
+        slots = np.random.default_rng(T + bs).permutation(nb * bs)[:T].astype(np.int32)
+    slots[::37] = -1
+    slots[min(11, T - 1)] = nb * bs + 3
+    kc, vc = pkv.alloc_caches(nb, hkv, d, dtype, device, fill=0.0, block_size=bs)
+    fd = fused.to(device)
+    pkv.reshape_and_cache(fd[:, :hkv], fd[:, hkv:2 * hkv], kc, vc,
+                          torch.from_numpy(slots).to(device))
+    okc, ovc = oracle.empty_caches(nb, hkv, d, dtype, fill_nan=False, block_size=bs)
+    oracle.cache_write(key.contiguous(), value.contiguous(), okc, ovc,
+                       np.where(slots >= nb * bs, -1, slots), dtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(oracle.raw(kc), okc) and np.array_equal(oracle.raw(vc), ovc)
+
+
 # ------------------------------------------------------------------- decode
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_single_pass_decode_matches_oracle(name, device):
