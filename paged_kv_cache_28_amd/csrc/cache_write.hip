@@ -13,7 +13,8 @@
 //   one KV head, which turns the rows around in LDS so that consecutive lanes write
 //   consecutive tokens, i.e. contiguous bytes where the slots are consecutive.
 // The launcher takes the rows form when it still gives every compute unit a wave.
-// reshape_and_cache_fp8 stores the e4m3 codes of x / scale instead (FP8 KV cache).
+// reshape_and_cache_fp8 stores the e4m3 codes of x / scale instead (FP8 KV cache), with
+// the same two forms (its rows form: a 256-thread workgroup per tile).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -152,6 +153,70 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
         vdst[k * bs] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(u[k])), v_scale));
 }
 
+// Rows form of the FP8 write (bulk writes), as for the 16-bit caches but with a workgroup
+// of 256 threads per 16 consecutive tokens of one KV head: each thread quantises one
+// 16-byte chunk (8 dimensions) of K and of V (d = 128), so the correctly rounded divisions
+// are spread over four times the threads of a one-wave tile (a wave per tile left the
+// launch latency-bound up to a few thousand tokens). Consecutive threads read consecutive
+// chunks of a token; the codes are turned around in LDS (K groups at a pitch of 17 x 16
+// bytes, V rows at d + 8 bytes: 8-byte aligned, and the 16 rows of one byte column fall in
+// 16 different banks) and written one token per thread (thread % 16): 16-byte K groups,
+// then single V bytes, so that consecutive slots give contiguous stores.
+template <typename T>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_rows_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, const int32_t* __restrict__ slots, int32_t num_tokens, int32_t hkv,
+    int32_t d, int64_t num_blocks, int64_t key_stride, int64_t value_stride, float k_scale,
+    float v_scale, int32_t lbs) {
+    extern __shared__ uint4 s_codes[];
+    const int n8 = d / 8;                    // 16-byte input chunks per row
+    const int n16 = d / 16;                  // 16-byte K groups per row
+    const int vpitch = d + 8;                // bytes per V row in LDS
+    uint8_t* Kl = reinterpret_cast<uint8_t*>(s_codes);              // group c of token r at (c * 17 + r) * 16
+    uint8_t* Vl = Kl + n16 * 17 * 16;                                 // token r's codes at r * vpitch
+    const int g = blockIdx.y;
+    const int64_t t0 = int64_t(blockIdx.x) * 16;
+    const int tid = threadIdx.x;
+    const int bs = 1 << lbs;
+    const int rw = tid & 15;   // the token this thread writes
+    int64_t slot = t0 + rw < num_tokens ? int64_t(slots[t0 + rw]) : -1;
+    if (slot >= (num_blocks << lbs)) slot = -1;
+    const int nt = blockDim.x;
+    auto codes8 = [](uint4 a, float scale) {
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        uint32_t o[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint32_t lo = w[2 * k], hi = w[2 * k + 1];
+            o[k] = quantize_fp8(Bits<T>::to_f32(uint16_t(lo)), scale) |
+                   (quantize_fp8(Bits<T>::to_f32(uint16_t(lo >> 16)), scale) << 8) |
+                   (quantize_fp8(Bits<T>::to_f32(uint16_t(hi)), scale) << 16) |
+                   (quantize_fp8(Bits<T>::to_f32(uint16_t(hi >> 16)), scale) << 24);
+        }
+        return make_uint2(o[0], o[1]);
+    };
+    for (int q = tid; q < 16 * n8; q += nt) {
+        const int r = q / n8, c = q - r * n8;
+        uint2 kq = make_uint2(0, 0), vq = make_uint2(0, 0);
+        if (t0 + r < num_tokens) {
+            const int64_t col = int64_t(g) * d + 8 * c;
+            kq = codes8(*reinterpret_cast<const uint4*>(key + (t0 + r) * key_stride + col), k_scale);
+            vq = codes8(*reinterpret_cast<const uint4*>(value + (t0 + r) * value_stride + col), v_scale);
+        }
+        *reinterpret_cast<uint2*>(Kl + ((c >> 1) * 17 + r) * 16 + 8 * (c & 1)) = kq;
+        *reinterpret_cast<uint2*>(Vl + r * vpitch + 8 * c) = vq;
+    }
+    __syncthreads();
+    if (slot < 0) return;   // no barrier follows
+    const int64_t tile = (slot >> lbs) * hkv + g;
+    const int off = int(slot & (bs - 1));
+    for (int c = tid >> 4; c < n16; c += nt / 16)   // K: group c of token rw
+        *reinterpret_cast<uint4*>(kc + ((tile * n16 + c) * bs + off) * 16) =
+            *reinterpret_cast<const uint4*>(Kl + (c * 17 + rw) * 16);
+    for (int i = tid >> 4; i < d; i += nt / 16)    // V: dimension i of token rw
+        vc[(tile * d + i) * bs + off] = Vl[rw * vpitch + i];
+}
+
 }  // namespace pkv
 
 extern "C" int reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
@@ -194,7 +259,23 @@ extern "C" int reshape_and_cache_fp8(const void* key, const void* value, void* k
     uint8_t* kcp = static_cast<uint8_t*>(k_cache);
     uint8_t* vcp = static_cast<uint8_t*>(v_cache);
     const pkv::LaunchEvents ev = pkv::timer_events(PKV_TIMER_CACHE_WRITE);
-    if (in_dtype == PKV_BF16)
+    // rows form when it gives every compute unit a workgroup
+    const int64_t rtiles = (int64_t(num_tokens) + 15) / 16;
+    const size_t rlds = size_t(head_dim / 16) * 17 * 16 + size_t(16) * (head_dim + 8);
+    if (rtiles * num_kv_heads >= pkv::device_cus() && rtiles <= 0x7fffffff &&
+        num_kv_heads <= 65535 && rlds <= 65536) {
+        const dim3 rgrid{unsigned(rtiles), unsigned(num_kv_heads), 1u};
+        if (in_dtype == PKV_BF16)
+            hipExtLaunchKernelGGL(pkv::reshape_and_cache_fp8_rows_kernel<pkv::bf16_t>, rgrid,
+                                  dim3(256), rlds, s, ev.start, ev.stop, 0, kp, vp, kcp, vcp,
+                                  slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
+                                  key_stride, value_stride, k_scale, v_scale, lbs);
+        else
+            hipExtLaunchKernelGGL(pkv::reshape_and_cache_fp8_rows_kernel<pkv::f16_t>, rgrid,
+                                  dim3(256), rlds, s, ev.start, ev.stop, 0, kp, vp, kcp, vcp,
+                                  slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,
+                                  key_stride, value_stride, k_scale, v_scale, lbs);
+    } else if (in_dtype == PKV_BF16)
         hipExtLaunchKernelGGL(pkv::reshape_and_cache_fp8_kernel<pkv::bf16_t>, dim3(unsigned(grid)),
                               dim3(256), 0, s, ev.start, ev.stop, 0, kp, vp, kcp, vcp,
                               slot_mapping, num_tokens, num_kv_heads, head_dim, num_blocks,

@@ -95,6 +95,54 @@ def test_fp8_cache_write_is_bit_exact(dtype, scale, device):
     assert np.array_equal(oracle.raw(kc), okc) and np.array_equal(oracle.raw(vc), ovc)
 
 
+# Both forms of the FP8 write (flat: a thread per 4 dimensions; rows: a wave per 16 tokens
+# of a KV head, taken once ceil(T / 16) * Hkv reaches the compute units, 256 on MI355X).
+FP8_CW_CASES = [
+    ("bf16", 16, 128, 8, 519),    # rows
+    ("f16", 8, 64, 8, 517),       # rows
+    ("bf16", 32, 128, 4, 1030),   # rows
+    ("bf16", 16, 128, 8, 40),     # flat
+]
+
+
+@pytest.mark.parametrize("dtype,bs,d,hkv,T", FP8_CW_CASES)
+@pytest.mark.parametrize("pattern", ["consecutive", "scattered"])
+def test_fp8_cache_write_forms_are_bit_exact(dtype, bs, d, hkv, T, pattern, device):
+    """Consecutive slots from a start inside a block, or a random permutation; the special
+    rows (ties, range limits, NaN, zeros) at both ends; strided inputs; negative slots and
+    one past the pool write nothing."""
+    w = dataclasses.replace(W8, dtype=dtype, num_kv_heads=hkv, head_dim=d, block_size=bs)
+    gen = workloads.rng(78, T, bs)
+    key = workloads.draw_tokens(T, w, gen, std=2.5)
+    value = workloads.draw_tokens(T, w, gen, std=2.5)
+    ks, vs = 0.0173, 0.026
+    sk = _special_rows(ks, dtype, hkv, d)
+    key[:sk.shape[0]] = sk
+    sv = _special_rows(vs, dtype, hkv, d)
+    value[T - sv.shape[0]:] = sv
+    fused = torch.zeros((T, 3 * hkv, d), dtype=key.dtype)
+    fused[:, :hkv], fused[:, 2 * hkv:] = key, value
+    if pattern == "consecutive":
+        start = 3 * bs + 5
+        nb = (start + T) // bs + 2
+        slots = (start + np.arange(T)).astype(np.int32)
+    else:
+        nb = 2 * T // bs + 2
+        slots = np.random.default_rng(T + bs).permutation(nb * bs)[:T].astype(np.int32)
+    slots[::37] = -1
+    slots[min(11, T - 1)] = nb * bs + 3
+    kc, vc = pkv.alloc_caches(nb, hkv, d, "fp8", device, fill=0x5A, block_size=bs)
+    fd = fused.to(device)
+    pkv.reshape_and_cache_fp8(fd[:, :hkv], fd[:, 2 * hkv:], kc, vc,
+                              torch.from_numpy(slots).to(device), ks, vs)
+    okc, ovc = oracle.empty_caches(nb, hkv, d, "fp8", fill_nan=False, block_size=bs)
+    okc[:], ovc[:] = 0x5A, 0x5A
+    oracle.cache_write(key, value, okc, ovc, np.where(slots >= nb * bs, -1, slots), dtype,
+                       cache_dtype="fp8", k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(oracle.raw(kc), okc) and np.array_equal(oracle.raw(vc), ovc)
+
+
 def test_fp8_pool_slots_tables_and_caches_are_bit_exact(device):
     w = SHAPES["8b-bf16-fp8"]
     ob = paged_batch.build(w, lens=RAGGED)
