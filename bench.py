@@ -25,6 +25,7 @@ is the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--config llama8b]
                        [--partition P] [--no-cpu-baseline]
+       python bench.py --config churn   (continuous batching; 50 timed steps after 10)
 """
 from __future__ import annotations
 
@@ -46,8 +47,10 @@ DECODE_SOURCES = ("decode.hip", "decode_kernels.hpp", "tile.hpp", "device.hpp")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; churn: 50)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default 5; churn: 10)")
     ap.add_argument("--config", default="llama8b")
     ap.add_argument("--partition", default=None,
                     help="auto (balanced split), 0 (single pass) or a multiple of 16; "
@@ -69,7 +72,13 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer 8 times (a plain copy of known size, to "
                          "scale the HBM byte counters) and exit")
-    return ap.parse_args()
+    args = ap.parse_args()
+    churn = args.config == "churn"
+    if args.steps is None:
+        args.steps = 50 if churn else 20
+    if args.warmup is None:
+        args.warmup = 10 if churn else 5
+    return args
 
 
 def decode_source_sha256() -> str:
