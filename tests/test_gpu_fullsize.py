@@ -1,6 +1,7 @@
 """Full-size parity: one layer of each workload at its real size, in the launch mode the
 bench uses for it (the 8B single pass with the step's host plan) and in the balanced split,
-and the 8B workload at 8 and 32 tokens per block, checked on sampled outputs.
+and the 8B workload at 8 and 32 tokens per block, checked on sampled outputs; for the 8B
+and 70B workloads also layers 1, the last and two seeded random ones in the bench's mode.
 
 * slots and block tables: every one, bit-exact against the oracle's pool model;
 * cache write: a random sample of tokens read back through the documented layout,
@@ -192,3 +193,31 @@ def test_full_size_layer(name, P, n_random, bs, plan, device):
     else:
         rows = layer.sample_rows(n_random)
     layer.check_rows(out, rows)
+
+
+def _other_layers(name):
+    """Layer 1, the last layer and two seeded random layers in between (layer 0 is above)."""
+    L = W[name].layers
+    extra = np.random.default_rng(28).choice(np.arange(2, L - 1), size=2, replace=False)
+    return [1, L - 1] + sorted(int(x) for x in extra)
+
+
+# the bench's launch mode of each multi-layer workload: 8B single pass with the host plan,
+# 70B balanced split
+LAYER_CASES = ([("llama8b", 0, 0, True, layer) for layer in _other_layers("llama8b")] +
+               [("llama70b", AUTO, 48, False, layer) for layer in _other_layers("llama70b")])
+
+
+@pytest.mark.parametrize("name,P,n_random,plan,layer", LAYER_CASES,
+                         ids=[f"{n}-layer{layer}" for n, _, _, _, layer in LAYER_CASES])
+def test_full_size_other_layers(name, P, n_random, plan, layer, device):
+    """Each layer has its own pool order and its own K/V and query draws."""
+    w = W[name]
+    lay = Layer(w, device, layer=layer)
+    lay.check_cache_sample(seed=layer)
+    out = lay.decode(P, plan)
+    if name == "llama8b":
+        rows = [(b, h) for b in range(w.batch) for h in range(w.num_heads)]
+    else:
+        rows = lay.sample_rows(n_random, seed=layer)
+    lay.check_rows(out, rows)
