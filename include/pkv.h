@@ -3,16 +3,19 @@
  *
  * The library implements the decode hot path of PagedAttention:
  *   - a host-side block pool: fixed-size KV blocks (8, 16 or 32 tokens), a per-sequence
- *     block table,
- *     on-demand allocation, a free queue and reference-counted sharing
+ *     block table, on-demand allocation, a free queue and reference-counted sharing
  *     ("vLLM ve Triton ile maliyet optimizasyonu", §03 Yöntem, steps 1-3 and the
  *     paragraph on sharing; "vLLM Nedir? PagedAttention ile Production LLM Serving",
- *     sections "PagedAttention" and "Bir istek motorun içinde");
+ *     sections "PagedAttention" and "Bir istek motorun içinde"), with prefix caching
+ *     and copy-on-write (kv_pool_add_seq_prefix, kv_pool_fork, copy_blocks);
  *   - reshape_and_cache: the slot-mapped write of each new token's K/V;
  *   - paged_attention_decode: single-query attention of a batch of sequences whose
- *     K/V are gathered through their block tables, with grouped-query attention;
+ *     K/V are gathered through their block tables, with grouped-query attention, and
+ *     paged_attention_decode_plan, its host-side schedule for a step;
  *   - paged_attention_reduce: the merge of per-partition results when the context
- *     is split into partitions.
+ *     is split into partitions;
+ *   - paged_attention_prefill: causal multi-query attention for chunked prefill;
+ *   - the same write and decode calls over an FP8 (e4m3) cache (*_fp8).
  *
  * General rules
  *   - Every function returns PKV_OK (0) or a negative PKV_E* code; pkv_last_error()
@@ -154,8 +157,9 @@ int kv_pool_add_seq(kv_pool* pool, int64_t seq_id);
  * pointing its table at the same physical blocks (reference count + 1 each), as for
  * a shared system prompt or parallel samples ("vLLM Nedir? ...", section
  * "PagedAttention", on block sharing; §03 on sharing). n_tokens must be a multiple
- * of the block size and at most src's length, so a shared block is full and never written again
- * (copy-on-write of partly filled shared blocks is not provided).
+ * of the block size and at most src's length, so a shared block is full and never
+ * written again (to share a partly filled block use kv_pool_fork, whose first append
+ * copies it).
  * Errors: ENOENT (unknown id), EINVAL (seq not empty, n_tokens not allowed). */
 int kv_pool_share_prefix(kv_pool* pool, int64_t seq_id, int64_t src_seq_id, int32_t n_tokens);
 
@@ -272,7 +276,12 @@ int kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
  *   slot_mapping: device int32 [num_tokens].
  *   dtype: PKV_F32, PKV_F16 or PKV_BF16 (a bit copy: the type only sets the size).
  * Errors: EINVAL (nulls, alignment, block_size, head_dim not a positive
- * multiple of x, sizes), EHIP. num_tokens == 0 is a no-op. */
+ * multiple of x, sizes), EHIP. num_tokens == 0 is a no-op.
+ * Performance: write a prompt's (or a prefill chunk's) tokens in one call. Once
+ * ceil(num_tokens / 16) * num_kv_heads reaches the device's compute units, each group
+ * of 16 consecutive tokens is turned around on chip, so that consecutive slots are
+ * written as contiguous bytes; a decode step's few scattered tokens take a
+ * thread-per-16-bytes form instead. Both write the same bytes. */
 int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                       const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
@@ -308,10 +317,10 @@ int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v
  *   partition_size == PKV_PARTITION_AUTO (fp16/bf16, num_seqs <= 1024): balanced
  *                 split. All (sequence, KV head, 16-token tile) triples form one list
  *                 that is cut into equal runs, one per wave of the launch, so ragged
- *                 lengths do not leave the device idle. A (sequence, KV head) whose tiles
- *                 all fall
- *                 in one run writes out; otherwise each run's share ("piece" k) writes
- *                 part_out/part_max/part_sum at index k as above. Pieces per (b, h) stay
+ *                 lengths do not leave the device idle. A (sequence, KV head) whose
+ *                 tiles all fall in one run writes out; otherwise each run's share
+ *                 ("piece" k) writes part_out/part_max/part_sum at index k as above.
+ *                 Pieces per (b, h) stay
  *                 <= max_partitions (>= 2 required): each run spans at least
  *                 ceil(T / (max_partitions - 1)) tiles of 16 tokens, T = ceil(
  *                 max_blocks_per_seq * BS / 16).
@@ -466,7 +475,8 @@ int copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers
  *   key, value: in_dtype (PKV_F16 or PKV_BF16), strides multiples of 8 elements.
  *   k_scale, v_scale: finite, > 0.
  *   head_dim: a positive multiple of 16.
- * Everything else as reshape_and_cache. Errors: EINVAL, ENOTSUP (in_dtype), EHIP. */
+ * Everything else as reshape_and_cache (its two forms included).
+ * Errors: EINVAL, ENOTSUP (in_dtype), EHIP. */
 int reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
