@@ -8,30 +8,35 @@
 //
 // Work decomposition: one workgroup of 4 waves per (query tile, KV head, sequence). The
 // 16 columns of the matrix products are (query token, head of the GQA group) pairs; a wave
-// holds NC column tiles (16 * NC columns = 16 * NC / G query tokens), so every K/V tile it
-// loads into registers feeds NC x 16 columns. The 4 waves take the key blocks round-robin
+// holds NC column tiles (16 * NC columns = 16 * NC / G query tokens), so every K/V pair it
+// loads into registers feeds NC x 16 columns. The 4 waves take the key pairs round-robin
 // with no barrier in the loop, each with its own online softmax per column, and merge
 // through LDS one column tile at a time at the end. Causal mask: each lane masks with its
 // own column's limit (keys at positions up to the query's), and a column tile whose queries
-// see none of a block pair skips it. (Staging the tiles in LDS for all four waves measured
+// see none of a pair skips it. (Staging the tiles in LDS for all four waves measured
 // slower: the barrier per block kept the waves in lockstep.)
 //
-// Keys are walked in 16-token tiles whatever the block size BS (8, 16 or 32; a template
-// parameter): a tile is a block, half a block or two blocks (tile.hpp). A wave takes its
-// tiles in pairs (A, B). Per pair and column tile:
-//   S_A^T, S_B^T[16 keys][16 cols] = K_tile x Q^T          (16x16x32, d/32 steps each)
+// Keys are walked in pairs of 32 consecutive positions, whatever the block size BS (8, 16
+// or 32; a template parameter): a pair is four blocks, two blocks or one block. Per pair
+// and column tile:
+//   S_A^T, S_B^T[16 keys][16 cols] = K_rows x Q^T          (16x16x32, d/32 steps each)
 //   O^T[d][16 cols] += V^T[d][32 keys] x P^T[32 keys][16 cols]   (16x16x32, d/16 steps)
-// The 32 keys of one PV step are the lane's 4 rows of A and its 4 rows of B (the 8 k-slots
-// of lane l are tokens 4 (l/16) .. + 3 of A, then of B, in both operands), so P and V stay
-// in the lanes that produced them. On gfx950 the 16x16x32 instruction issues at the rate of
-// the 16x16x16 one with twice the work, so pairs halve the PV issue time. P is split in a
-// high and a low bf16/fp16 part as in decode.
+// The two QK products read their K rows in a permuted order (row r of A: position
+// 8 (r / 4) + r % 4 of the pair; of B: that + 4), so that lane l holds the logits of the
+// 8 consecutive positions 8 (l/16) .. + 7, which are its 8 k-slots of the PV step in both
+// operands: P stays in the lanes that produced it, and the lane's V operand is one 16-byte
+// load of those positions of one dimension row. On gfx950 the 16x16x32 instruction issues
+// at the rate of the 16x16x16 one with twice the work, so pairs halve the PV issue time. P
+// is split in a high and a low bf16/fp16 part as in decode.
 //
 // Each pair is loaded and then used (no second pair in flight): with NC = 2 that keeps the
 // wave at two per SIMD, and the other wave's math covers a pair's load. Measured on the
-// 30,000-token chunked prefill: this form 500 TFLOP/s; double-buffered pairs (one wave per
-// SIMD) 354; single blocks with the 16x16x16 product 460; NC = 1 (three waves per SIMD) 348;
-// NC = 4 361; tiles staged in LDS for the workgroup 290.
+// 30,000-token chunked prefill: this form 532-552 TFLOP/s; the same with two 16-token tiles
+// W tiles apart and 8-byte V loads per tile (24 loads per pair instead of 16) 1.5-3% less;
+// the next pair's K and V loads issued into the same registers once the QK (resp. PV)
+// products are done, no gain; double-buffered pairs (one wave per SIMD) 354; single blocks
+// with the 16x16x16 product 460; NC = 1 (three waves per SIMD) 348; NC = 4 361; tiles
+// staged in LDS for the workgroup 290.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -122,15 +127,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
     int key_end = 0;   // keys any column of the workgroup sees
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) key_end = max(key_end, tile_lim[ct]);
-    const int nblk = (key_end + 15) >> 4;
 
     f32x4 acc[NC][NPV];
-    float m[NC], lsum[NC];
+    float m_ref[NC], lsum[NC];
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
 #pragma unroll
         for (int c = 0; c < NPV; ++c) acc[ct][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m[ct] = -INFINITY;
+        m_ref[ct] = -INFINITY;
         lsum[ct] = 0.f;
     }
     constexpr float kSlack = 8.0f;   // lazy reference point, as in the decode kernel
@@ -139,77 +143,106 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
     const char* vbase = static_cast<const char*>(a.v_cache);
     const int64_t tile_bytes = int64_t(D) * BS * 2;   // one block of one KV head
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
-    int tab = 0, tabb = 0;   // lane k: tile k's block id (and its second block's, BS = 8)
 
-    // Issue tile j's loads (segment index k). Bit 0 of the result: its (first) block id is
-    // valid; bit 1: its second block's (BS = 8; always set otherwise). An invalid id is
-    // replaced by a safe address and its rows count as past the end.
-    auto load = [&](KvTile<D, false>& t, int k, int j) __attribute__((always_inline)) -> int {
-        int64_t pa = __builtin_amdgcn_readlane(tab, k);
-        const bool oka = pa >= 0 && pa < a.num_blocks;
-        pa = oka ? pa : 0;
-        int64_t pb = pa;
-        bool okb = true;
-        if constexpr (BS == 8) {
-            pb = __builtin_amdgcn_readlane(tabb, k);
-            okb = pb >= 0 && pb < a.num_blocks;
-            pb = okb ? pb : 0;
-        }
-        const int64_t ta = pa * a.num_kv_heads + g, tb = pb * a.num_kv_heads + g;
-        load_tile_bs<D, BS>(t, kbase + ta * tile_bytes, vbase + ta * tile_bytes,
-                            kbase + tb * tile_bytes, vbase + tb * tile_bytes, 16 * (j & 1), lane);
-        return int(oka) | (int(okb) << 1);
+    // Keys are walked in pairs of 32 consecutive positions (pair m: 32m .. 32m + 31, the
+    // 16-token tiles 2m and 2m + 1), each a 16x16x32 PV step. The QK products read their
+    // K rows in a permuted order so that each lane ends up holding the logits of 8
+    // consecutive positions: MFMA row r of product A reads position 8 (r / 4) + r % 4 of
+    // the pair, product B that position + 4, so lane (quad, col) gets positions
+    // 8 quad .. 8 quad + 3 from A and 8 quad + 4 .. + 7 from B. Its V operand is then one
+    // 16-byte load of those 8 positions of one dimension row, half the V loads of two
+    // 16-token tiles. 8 consecutive positions never cross a block (BS >= 8).
+    constexpr int NB = 32 / BS;                         // blocks per pair (4, 2, 1)
+    const int ra = 8 * (col >> 2) + (col & 3), rb = ra + 4, rv = 8 * quad;
+    auto blk_of = [](int t) { return t / BS; };
+    auto row_of = [](int t) { return t % BS; };
+    int ids[NB];   // block ids of this segment: lane k holds pair k's
+
+    struct Pair {
+        uint4 ka[NQK];   // K rows of product A, QK steps 0 .. NQK - 1
+        uint4 kb[NQK];   // product B
+        uint4 v[NPV];    // positions 8 quad .. + 7 of dimension 16 c + col
     };
 
-    // Tiles jA and jB (ok bits as load returns them) as one 32-key step; okB is 0 for the
-    // odd last tile of a wave, whose B then contributes nothing.
-    auto compute_pair = [&](const KvTile<D, false>& A, const KvTile<D, false>& B, int jA, int jB,
-                            int okA, int okB) __attribute__((always_inline)) {
-        const int tA = jA * 16 + 4 * quad, tB = jB * 16 + 4 * quad;
-        // keys of each tile below nA / nB are real: past the sequence, or behind an invalid
-        // block id, they are not
-        const int nA = (okA & 1) ? ((okA & 2) ? n : min(n, jA * 16 + 8)) : 0;
-        const int nB = (okB & 1) ? ((okB & 2) ? n : min(n, jB * 16 + 8)) : 0;
-        // V rows that are not real may hold anything: zeroed as the operands are built
-        // (the tiles stay read-only, which keeps them in registers)
-        auto keep = [&](int t, int nt) {
-            return (t < nt ? 0x0000ffffu : 0u) | (t + 1 < nt ? 0xffff0000u : 0u);
+    // Issue the loads of segment pair k. Returns bit i set if the pair's block i has a
+    // valid id; an invalid id is replaced by a safe address and its rows masked.
+    auto load_pair = [&](Pair& t, int k) __attribute__((always_inline)) -> int {
+        int okm = 0;
+        auto id = [&](int i) -> int32_t {   // block i's id, or 0 (safe) if invalid
+            const int32_t p = __builtin_amdgcn_readlane(ids[i], k);
+            const bool ok = p >= 0 && int64_t(p) < a.num_blocks;
+            okm |= int(ok) << i;
+            return ok ? p : 0;
         };
-        const uint32_t ka0 = keep(tA, nA), ka1 = keep(tA + 2, nA), kb0 = keep(tB, nB),
-                       kb1 = keep(tB + 2, nB);
-        const int jmin = (okB & 1) ? min(jA, jB) : jA;
+        // separate variables, not an array: the compiler turns selects among array
+        // elements into an indexed scratch access
+        const int32_t p0 = id(0);
+        const int32_t p1 = NB > 1 ? id(1) : 0;
+        const int32_t p2 = NB > 2 ? id(2) : 0;
+        const int32_t p3 = NB > 2 ? id(3) : 0;
+        auto pick = [&](int bi) {   // the id of pair block bi (lane-varying)
+            const int32_t lo = (bi & 1) ? p1 : p0;
+            const int32_t hi = (bi & 1) ? p3 : p2;
+            const int32_t p = NB == 1 ? p0 : NB == 2 ? lo : ((bi & 2) ? hi : lo);
+            return (int64_t(p) * a.num_kv_heads + g) * tile_bytes;
+        };
+        const char* kA = kbase + pick(blk_of(ra));
+        const char* kB = kbase + pick(blk_of(rb));
+        const char* vt = vbase + pick(blk_of(rv));
+        const int rowa = row_of(ra), rowb = row_of(rb), rowv = row_of(rv);
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) {
+            t.ka[c] = *reinterpret_cast<const uint4*>(kA + ((4 * c + quad) * BS + rowa) * 16);
+            t.kb[c] = *reinterpret_cast<const uint4*>(kB + ((4 * c + quad) * BS + rowb) * 16);
+        }
+#pragma unroll
+        for (int c = 0; c < NPV; ++c)
+            t.v[c] = *reinterpret_cast<const uint4*>(vt + ((16 * c + col) * BS + rowv) * 2);
+        return okm;
+    };
+
+    auto compute_pair = [&](const Pair& t, int m, int okm) __attribute__((always_inline)) {
+        const int p0 = 32 * m + 8 * quad;   // first of this lane's 8 positions
+        // positions below nv are real: past the sequence, or in a block whose id is
+        // invalid, they are not
+        const int nv = ((okm >> blk_of(rv)) & 1) ? n : 0;
+        // V rows that are not real may hold anything: zeroed as the operand is built
+        auto keep = [&](int t) {
+            return (t < nv ? 0x0000ffffu : 0u) | (t + 1 < nv ? 0xffff0000u : 0u);
+        };
+        const uint32_t k0 = keep(p0), k1 = keep(p0 + 2), k2 = keep(p0 + 4), k3 = keep(p0 + 6);
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            if (jmin * 16 >= tile_lim[ct]) continue;   // no query of this tile sees the pair
-            const int la = min(lim[ct], nA), lb = min(lim[ct], nB);
+            if (32 * m >= tile_lim[ct]) continue;   // no query of this tile sees the pair
+            const int lv = min(lim[ct], nv);
             f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NQK; ++c) {
-                sa = Mfma<T>::qk(k_operand<T, D>(A, c), qf[ct][c], sa);
-                sb = Mfma<T>::qk(k_operand<T, D>(B, c), qf[ct][c], sb);
+                sa = Mfma<T>::qk(t.ka[c], qf[ct][c], sa);
+                sb = Mfma<T>::qk(t.kb[c], qf[ct][c], sb);
             }
             float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = tA + e < la ? sa[e] * a.scale_log2 : -INFINITY;
-                x[4 + e] = tB + e < lb ? sb[e] * a.scale_log2 : -INFINITY;
+                x[e] = p0 + e < lv ? sa[e] * a.scale_log2 : -INFINITY;
+                x[4 + e] = p0 + 4 + e < lv ? sb[e] * a.scale_log2 : -INFINITY;
             }
             const float bm = max_over_rows(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                                                  fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
-            const bool move = bm > m[ct] + kSlack;
+            const bool move = bm > m_ref[ct] + kSlack;
             if (__builtin_amdgcn_ballot_w64(move)) {
                 // a lane that keeps its reference keeps factor 1 (also one whose column has
                 // seen no key yet, where m - m would be -inf - -inf)
-                const float mn = move ? bm : m[ct];
-                const float alpha = move ? exp2_fast(m[ct] - mn) : 1.0f;
+                const float mn = move ? bm : m_ref[ct];
+                const float alpha = move ? exp2_fast(m_ref[ct] - mn) : 1.0f;
                 lsum[ct] *= alpha;
 #pragma unroll
                 for (int c = 0; c < NPV; ++c) acc[ct][c] *= alpha;
-                m[ct] = mn;
+                m_ref[ct] = mn;
             }
             float pe[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m[ct]);
+            for (int e = 0; e < 8; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m_ref[ct]);
             lsum[ct] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
             uint16_t hi[8], lo[8];
 #pragma unroll
@@ -224,30 +257,30 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
                                          uint32_t(lo[6]) | (uint32_t(lo[7]) << 16));
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
-                const uint2 va = v_operand<T, D>(A, c), vb = v_operand<T, D>(B, c);
-                const uint4 vv = make_uint4(va.x & ka0, va.y & ka1, vb.x & kb0, vb.y & kb1);
+                const uint4 vv = make_uint4(t.v[c].x & k0, t.v[c].y & k1, t.v[c].z & k2,
+                                            t.v[c].w & k3);
                 acc[ct][c] = Mfma<T>::qk(vv, phi, acc[ct][c]);
                 acc[ct][c] = Mfma<T>::qk(vv, plo, acc[ct][c]);
             }
         }
     };
 
-    // This wave's tiles: wave, wave + W, ...; segments of 64 tiles (block ids one per
-    // lane).
-    const int nmine = wave < nblk ? (nblk - wave + W - 1) / W : 0;
+    // This wave's pairs: wave, wave + W, ...; segments of 64 pairs (block ids one pair per
+    // lane), each pair loaded and then used.
+    const int npairs = (key_end + 31) >> 5;
+    const int nmine = wave < npairs ? (npairs - wave + W - 1) / W : 0;
     for (int k0 = 0; k0 < nmine; k0 += 64) {
         const int cnt = min(64, nmine - k0);
-        tile_ids<BS>(table, a.max_blocks, lane < cnt ? wave + (k0 + lane) * W : a.max_tiles, tab,
-                     tabb);
-        // pairs (k, k + 1) of this segment, each loaded and then used; an odd last tile
-        // pairs with itself, its second copy masked out
-        for (int k = 0; k < cnt; k += 2) {
-            KvTile<D, false> X0, X1;
-            const int k1 = min(k + 1, cnt - 1);
-            const int ox0 = load(X0, k, wave + (k0 + k) * W);
-            const int ox1 = load(X1, k1, wave + (k0 + k1) * W);
-            compute_pair(X0, X1, wave + (k0 + k) * W, wave + (k0 + k + 1) * W, ox0,
-                         k + 1 < cnt ? ox1 : 0);
+        const int mp = wave + (k0 + lane) * W;   // this lane's pair
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int bi = NB * mp + i;
+            ids[i] = lane < cnt && bi < a.max_blocks ? table[bi] : -1;
+        }
+        for (int k = 0; k < cnt; ++k) {
+            Pair t;
+            const int okm = load_pair(t, k);
+            compute_pair(t, wave + (k0 + k) * W, okm);
         }
     }
 
@@ -258,7 +291,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
         ls += __shfl_xor(ls, 16, 64);
         ls += __shfl_xor(ls, 32, 64);
         if (lane < 16) {
-            sm_m[wave * 16 + lane] = m[ct];
+            sm_m[wave * 16 + lane] = m_ref[ct];
             sm_l[wave * 16 + lane] = ls;
         }
 #pragma unroll

@@ -1,7 +1,7 @@
 // One (block, KV head) tile of K and V as a lane holds it for the two matrix products of
-// the attention kernels (decode and prefill), the operands taken from it, and row masking.
-// The 16 columns of both products are whatever the kernel puts there (query heads of a
-// GQA group in decode; (query token, head) pairs in prefill).
+// the decode kernels, the operands taken from it, and row masking. The 16 columns of both
+// products are the query heads of a GQA group. The prefill kernel walks keys in 32-position
+// pairs of its own layout and takes only q_dim from here (its Q^T operand order).
 #pragma once
 
 #include <hip/hip_runtime.h>
