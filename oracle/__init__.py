@@ -46,11 +46,16 @@ def build() -> str:
 
 
 def lib():
+    """The compiled oracle. ORACLE_LIBRARY names another build of oracle.c instead (the
+    mutation tests load deliberately broken copies through it); build() never writes it."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            build()
-        L = ctypes.CDLL(LIB_PATH)
+        path = os.environ.get("ORACLE_LIBRARY")
+        if not path:
+            path = LIB_PATH
+            if not os.path.exists(path):
+                build()
+        L = ctypes.CDLL(path)
         P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         L.oracle_to_f64.argtypes = [P, P, I64, I32]
         L.oracle_to_f64.restype = None
