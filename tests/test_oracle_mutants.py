@@ -73,3 +73,65 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
     r = _run_pins(src.replace(old, new), tmp_path)
     assert r.returncode == 1, (f"no pin caught '{name}' (pytest exit {r.returncode}):\n"
                                + r.stdout[-2000:])
+
+
+# The pool model (oracle/allocator.py), Python: each mutant runs in a copy of the tree's
+# oracle, workloads and tests, so the real file is never touched. Its pins are the
+# oracle's own tests (worked examples, invariants), not the comparisons with the C++ pool.
+ALLOC_PINS = ["tests/test_oracle_allocator.py", "tests/test_oracle_prefix.py",
+              "tests/test_oracle_blocksize.py"]
+ALLOC_MUTANTS = [
+    ("free queue taken from the back", "blk = self.free.popleft()", "blk = self.free.pop()"),
+    ("freed blocks pushed to the front",
+     "self.free.append(blk)      # keeps its key until popped again",
+     "self.free.appendleft(blk)"),
+    ("a new block one token early", "while len(blocks) * self.bs < length + n_tokens:",
+     "while len(blocks) * self.bs <= length + n_tokens:"),
+    ("slot offset counted from the block's end",
+     "slots = [blocks[pos // self.bs] * self.bs + pos % self.bs",
+     "slots = [blocks[pos // self.bs] * self.bs + (self.bs - 1 - pos % self.bs)"),
+    ("shared blocks freed with their first owner",
+     "            self.ref[blk] -= 1\n            if self.ref[blk] == 0:",
+     "            self.ref[blk] -= 1\n            if self.ref[blk] <= 1:"),
+    ("bytes per token without K and V", "return 2 * num_layers * num_kv_heads * head_dim * elem_bytes",
+     "return num_layers * num_kv_heads * head_dim * elem_bytes"),
+    ("copy-on-write block not counted", "need = -(-(length + n_tokens) // self.bs) - len(blocks) + int(cow)",
+     "need = -(-(length + n_tokens) // self.bs) - len(blocks)"),
+    ("prefix key of the block alone, not the chain",
+     "key = (self.salt[sid], tuple(toks[:(j + 1) * self.bs]))",
+     "key = (self.salt[sid], tuple(toks[j * self.bs:(j + 1) * self.bs]))"),
+]
+
+
+def _copy_tree(dst):
+    import shutil
+    for d in ("oracle", "workloads", "tests"):
+        shutil.copytree(os.path.join(ROOT, d), os.path.join(dst, d),
+                        ignore=shutil.ignore_patterns("__pycache__", "*.tmp"))
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), dst)
+
+
+def _run_alloc_pins(old, new, tmp_path):
+    dst = tmp_path / "tree"
+    _copy_tree(str(dst))
+    f = dst / "oracle" / "allocator.py"
+    if old is not None:
+        src = f.read_text()
+        assert src.count(old) == 1, f"mutation anchor not found once: {old!r}"
+        f.write_text(src.replace(old, new))
+    env = {k: v for k, v in os.environ.items() if k != "ORACLE_LIBRARY"}
+    return subprocess.run([sys.executable, "-m", "pytest", *ALLOC_PINS, "-x", "-q", "-m",
+                           "not gpu", "-p", "no:cacheprovider"], cwd=str(dst), env=env,
+                          capture_output=True, text=True, timeout=600)
+
+
+def test_unmodified_pool_model_copy_passes_the_pins(tmp_path):
+    r = _run_alloc_pins(None, None, tmp_path)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name,old,new", ALLOC_MUTANTS, ids=[m[0] for m in ALLOC_MUTANTS])
+def test_pins_catch_planted_pool_model_mistake(name, old, new, tmp_path):
+    r = _run_alloc_pins(old, new, tmp_path)
+    assert r.returncode == 1, (f"no pin caught '{name}' (pytest exit {r.returncode}):\n"
+                               + r.stdout[-2000:])
