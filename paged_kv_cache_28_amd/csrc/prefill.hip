@@ -30,13 +30,17 @@
 // is split in a high and a low bf16/fp16 part as in decode.
 //
 // Each pair is loaded and then used (no second pair in flight): with NC = 2 that keeps the
-// wave at two per SIMD, and the other wave's math covers a pair's load. Measured on the
-// 30,000-token chunked prefill: this form 532-552 TFLOP/s; the same with two 16-token tiles
-// W tiles apart and 8-byte V loads per tile (24 loads per pair instead of 16) 1.5-3% less;
-// the next pair's K and V loads issued into the same registers once the QK (resp. PV)
-// products are done, no gain; double-buffered pairs (one wave per SIMD) 354; single blocks
-// with the 16x16x16 product 460; NC = 1 (three waves per SIMD) 348; NC = 4 361; tiles
-// staged in LDS for the workgroup 290.
+// wave at two per SIMD, and the other wave's math covers a pair's load. The vector-ALU work
+// per pair bounds the kernel as much as anything (64 more multiplies per pair cost 7%), so
+// the V rows past the real ones are zeroed once per pair and only in a pair that has any,
+// and the softmax weights need no per-element select. Measured on the 30,000-token chunked
+// prefill (TFLOP/s): this form 578-585; the masking per column tile and per element
+// 544-547; two 16-token tiles W tiles apart with 8-byte V loads (24 loads per pair instead
+// of 16) a further 1.5-3% less; the next pair's K and V loads issued into the same
+// registers once the QK (resp. PV) products are done, no gain; double-buffered pairs (one
+// wave per SIMD) 354; single blocks with the 16x16x16 product 460; NC = 1 (three waves per
+// SIMD) 348; NC = 4 with Q^T in registers 361, in LDS 531 (against 540); tiles staged in
+// LDS for the workgroup 290.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -201,16 +205,26 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
         return okm;
     };
 
-    auto compute_pair = [&](const Pair& t, int m, int okm) __attribute__((always_inline)) {
+    auto compute_pair = [&](Pair& t, int m, int okm) __attribute__((always_inline)) {
         const int p0 = 32 * m + 8 * quad;   // first of this lane's 8 positions
         // positions below nv are real: past the sequence, or in a block whose id is
         // invalid, they are not
         const int nv = ((okm >> blk_of(rv)) & 1) ? n : 0;
-        // V rows that are not real may hold anything: zeroed as the operand is built
-        auto keep = [&](int t) {
-            return (t < nv ? 0x0000ffffu : 0u) | (t + 1 < nv ? 0xffff0000u : 0u);
-        };
-        const uint32_t k0 = keep(p0), k1 = keep(p0 + 2), k2 = keep(p0 + 4), k3 = keep(p0 + 6);
+        // V rows that are not real may hold anything: zeroed once per pair, and only in a
+        // pair that has such rows (the last pair of a sequence or an invalid block)
+        if (__builtin_amdgcn_ballot_w64(p0 + 8 > nv)) {
+            auto keep = [&](int q) {
+                return (q < nv ? 0x0000ffffu : 0u) | (q + 1 < nv ? 0xffff0000u : 0u);
+            };
+            const uint32_t k0 = keep(p0), k1 = keep(p0 + 2), k2 = keep(p0 + 4), k3 = keep(p0 + 6);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) {
+                t.v[c].x &= k0;
+                t.v[c].y &= k1;
+                t.v[c].z &= k2;
+                t.v[c].w &= k3;
+            }
+        }
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
             if (32 * m >= tile_lim[ct]) continue;   // no query of this tile sees the pair
@@ -240,9 +254,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
                 for (int c = 0; c < NPV; ++c) acc[ct][c] *= alpha;
                 m_ref[ct] = mn;
             }
+            // exp2(-inf - m) is 0 for a finite m; m is -inf only while the column has seen
+            // no real key, and then every x is -inf too, so one select per lane (not per
+            // element) keeps those weights 0 instead of exp2(-inf + inf)
+            const float mref = m_ref[ct] == -INFINITY ? 0.f : m_ref[ct];
             float pe[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pe[e] = x[e] == -INFINITY ? 0.f : exp2_fast(x[e] - m_ref[ct]);
+            for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(x[e] - mref);
             lsum[ct] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
             uint16_t hi[8], lo[8];
 #pragma unroll
@@ -257,10 +275,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
                                          uint32_t(lo[6]) | (uint32_t(lo[7]) << 16));
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
-                const uint4 vv = make_uint4(t.v[c].x & k0, t.v[c].y & k1, t.v[c].z & k2,
-                                            t.v[c].w & k3);
-                acc[ct][c] = Mfma<T>::qk(vv, phi, acc[ct][c]);
-                acc[ct][c] = Mfma<T>::qk(vv, plo, acc[ct][c]);
+                acc[ct][c] = Mfma<T>::qk(t.v[c], phi, acc[ct][c]);
+                acc[ct][c] = Mfma<T>::qk(t.v[c], plo, acc[ct][c]);
             }
         }
     };
