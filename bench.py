@@ -438,6 +438,10 @@ def bench_churn(args):
 
 def main():
     args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only (run with --gpus 1): every path here is timed "
+              "on one GPU's share of the work", file=sys.stderr)
+        sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
         return
@@ -446,22 +450,11 @@ def main():
         return
     import workloads as _wl
     if args.config == "churn":
-        if args.gpus != 1:
-            print("bench.py measures one GPU only", file=sys.stderr)
-            sys.exit(2)
         bench_churn(args)
         return
     if _wl.WORKLOADS[args.config].prefill_tokens:
-        if args.gpus != 1:
-            print("bench.py measures one GPU only", file=sys.stderr)
-            sys.exit(2)
         bench_prefill(args)
         return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the paged decode path has no multi-GPU "
-              "component in this build (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
     import numpy as np
     import torch
 
