@@ -539,6 +539,327 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     merge_and_store<OutT, D, W>(a, sm_m, sm_l, sm_o, b, g, p, direct);
 }
 
+// ------------------------------------------------ FP8 cache, 32-token blocks, whole blocks
+// FP8 caches at 32 tokens per block, single pass or partitions of whole blocks. The 16-token
+// tiles of decode_mfma_kernel read half of every 32-byte V row there, so each V load
+// instruction touches twice the sectors of the 16-token case. Here a wave takes whole
+// blocks: the two QK products of a block read their K rows in a permuted order (MFMA row r
+// of product A: position 8 (r / 4) + r % 4 of the block, of product B that + 4), so lane l
+// holds the logits of positions 8 (l/16) .. + 7, which are its 8 k-slots of one 16x16x32
+// PV product in both operands. Its V operand is then one 8-byte load of those 8 positions
+// of a dimension row: the block's V rows are read whole, with half the load instructions.
+// Softmax, reference points, merging and the fused append are those of decode_mfma_kernel.
+template <int D> struct KvBlock32 {
+    uint4 ka[D / 64];   // K rows of product A: 16 codes (dims 16 (4 i + quad) ..) each
+    uint4 kb[D / 64];   // product B
+    uint2 v[D / 16];    // positions 8 quad .. + 7 of dimension 16 c + col
+};
+
+template <typename T, int D, typename OutT, int W, bool Append>
+__global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) {
+    static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
+    constexpr int BS = 32;
+    constexpr int NQK = D / 32;   // 16x16x32 steps for S
+    constexpr int NPV = D / 16;   // 16x16x32 steps for O (32 positions each)
+    constexpr int NKL = D / 64;   // 16-byte K loads per product and lane
+    extern __shared__ float lds[];
+    float* sm_m = lds;                  // [W][16]
+    float* sm_l = lds + W * 16;         // [W][16]
+    float* sm_o = lds + 2 * W * 16;     // [W][G][D]
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
+    int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
+    const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
+    if (a.use_order) {
+        b = a.order[b];
+    } else if (a.lpt_round > 0) {   // rank the lengths as decode_mfma_kernel does
+        __shared__ int s_n[kLptMaxSeqs];
+        __shared__ int s_pick;
+        const int t = threadIdx.x;
+        const int max_len = a.max_len;
+        for (int i = t; i < a.num_seqs; i += W * 64) {
+            const int v = a.seq_lens[i];
+            s_n[i] = v < 0 ? 0 : (v > max_len ? max_len : v);
+        }
+        __syncthreads();
+        for (int i = t; i < a.num_seqs; i += W * 64) {
+            const int mine = s_n[i];
+            int rank = 0;
+            for (int k = 0; k < a.num_seqs; ++k) {
+                const int o = s_n[k];
+                rank += (o > mine) || (o == mine && k < i);
+            }
+            const int R = a.lpt_round, r = b / R, pos = b - r * R;
+            const int hi = min(R, a.num_seqs - r * R);
+            if (rank == r * R + ((r & 1) ? hi - 1 - pos : pos)) s_pick = i;
+        }
+        __syncthreads();
+        b = s_pick;
+    }
+    const int G = a.group;
+    const int col = lane & 15, quad = lane >> 4;
+    const int ra = 8 * (col >> 2) + (col & 3), rb = ra + 4;   // this lane's K rows of A, B
+
+    uint4 qf[NQK];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(b) * a.q_stride +
+                               int64_t(g * G + col) * D;
+#pragma unroll
+        for (int c = 0; c < NQK; ++c)
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + q_dim<true>(c, quad))
+                            : make_uint4(0, 0, 0, 0);
+    }
+    // fused append: the new row's codes as this lane holds them (nk: the K groups of a
+    // lane with col == 0, i.e. MFMA row 0 = position 0 of product A; nv: byte 0 of the
+    // lanes with quad == 0, position 0 of each dimension)
+    constexpr int NQ = D / 64;
+    int slot = -1;
+    uint4 nk[Append ? NKL : 1];
+    uint32_t nv[Append ? NPV : 1];
+    uint32_t nkr = 0, nvr = 0;
+    if constexpr (Append) {
+        slot = a.slot_mapping[b];
+        const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
+                               int64_t(g) * D;
+        const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
+                               int64_t(g) * D;
+        static_assert(NQ == 1 || NQ == 2, "head_dim 64 or 128");
+        if constexpr (NQ == 2) {
+            nkr = *reinterpret_cast<const uint32_t*>(krow + 2 * lane);
+            nvr = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
+        } else {
+            nkr = krow[lane];
+            nvr = vrow[lane];
+        }
+    }
+    auto quantize_new = [&]() {
+        if constexpr (Append) {
+            uint8_t* q8 = reinterpret_cast<uint8_t*>(sm_o + wave * G * D);
+#pragma unroll
+            for (int e = 0; e < NQ; ++e) {
+                q8[NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nkr >> (16 * e))), a.k_scale));
+                q8[D + NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nvr >> (16 * e))), a.v_scale));
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < NKL; ++i) nk[i] = *reinterpret_cast<const uint4*>(q8 + 64 * i + 16 * quad);
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) nv[c] = q8[D + 16 * c + col];
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
+
+    // whole blocks: this wave takes blocks first, first + W, ... of its partition
+    const int part_blocks = a.part_tiles >> 1;
+    const int blk_begin = p * part_blocks;
+    const int first = blk_begin + wave;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    const int tab0 = first + lane * W < a.max_blocks ? table[first + lane * W] : -1;
+
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    const int nblk = (n + BS - 1) / BS;
+    const int jl = n > 0 ? (n - 1) / BS : -1;    // block of the newest token
+    if (blk_begin >= nblk) {
+        if (p == 0) write_zero_rows<OutT, D>(a, b, g);
+        if constexpr (Append)
+            if (p == 0 && n == 0) write_new_token<T, D, true, BS>(a, b, g, slot);
+        return;
+    }
+    const int blk_end = min(nblk, blk_begin + part_blocks);
+    const bool direct = nblk <= part_blocks;
+    const int nmine = first < blk_end ? (blk_end - first + W - 1) / W : 0;
+    bool subst = false;
+    int lim = n;
+    const bool own_new = jl >= blk_begin && jl < blk_end;
+    const int w_new = own_new ? (jl - blk_begin) % W : -1;
+    const int k_new = own_new ? (jl - first) / W : -1;
+    auto store_new_row = [&]() {
+        if constexpr (Append) {
+            if (wave != w_new) return;
+            quantize_new();
+            if (slot < 0 || int64_t(slot) >= a.num_blocks * BS) return;
+            const int64_t tile = int64_t(slot / BS) * a.num_kv_heads + g;
+            const int off = slot % BS;
+            char* kc = const_cast<char*>(static_cast<const char*>(a.k_cache));
+            char* vc = const_cast<char*>(static_cast<const char*>(a.v_cache));
+            if (col == 0) {
+#pragma unroll
+                for (int c = 0; c < NKL; ++c)
+                    *reinterpret_cast<uint4*>(kc + ((tile * (NKL * 4) + 4 * c + quad) * BS + off) * 16) = nk[c];
+            }
+            if (quad == 0) {
+#pragma unroll
+                for (int c = 0; c < NPV; ++c)
+                    reinterpret_cast<uint8_t*>(vc)[(tile * D + 16 * c + col) * BS + off] = uint8_t(nv[c]);
+            }
+        }
+    };
+
+    f32x4 acc[NPV];
+#pragma unroll
+    for (int c = 0; c < NPV; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr float kSlack = 8.0f;
+    float m = -INFINITY, lsum = 0.f;
+
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    constexpr int64_t tile_bytes = int64_t(D) * BS;   // one block of one KV head (codes)
+    int tab = 0;
+
+    // Issue the loads of segment block k; false if its id is invalid (a safe address is
+    // read and the block is skipped).
+    auto load = [&](KvBlock32<D>& t, int k) -> bool {
+        int64_t pa = __builtin_amdgcn_readlane(tab, k);
+        const bool ok = pa >= 0 && pa < a.num_blocks;
+        pa = ok ? pa : 0;
+        const char* kt = kbase + (pa * a.num_kv_heads + g) * tile_bytes;
+        const char* vt = vbase + (pa * a.num_kv_heads + g) * tile_bytes;
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) {
+            t.ka[i] = *reinterpret_cast<const uint4*>(kt + ((4 * i + quad) * BS + ra) * 16);
+            t.kb[i] = *reinterpret_cast<const uint4*>(kt + ((4 * i + quad) * BS + rb) * 16);
+        }
+#pragma unroll
+        for (int c = 0; c < NPV; ++c)
+            t.v[c] = *reinterpret_cast<const uint2*>(vt + (16 * c + col) * BS + 8 * quad);
+        return ok;
+    };
+    auto kop = [](const uint4& w, int c) {   // 8 codes of QK step c, widened
+        const uint2 lo = Fp8<T>::x4((c & 1) ? w.z : w.x), hi = Fp8<T>::x4((c & 1) ? w.w : w.y);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+
+    // block jb (positions 32 jb .. + 31); positions below lim are valid
+    auto compute = [&](KvBlock32<D>& t, int jb, bool ok) {
+        if (!ok) return;
+        const int p0 = jb * BS + 8 * quad;   // this lane's 8 positions
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NQK; ++c) {
+            sa = Mfma<T>::qk(kop(t.ka[c >> 1], c), qf[c], sa);
+            sb = Mfma<T>::qk(kop(t.kb[c >> 1], c), qf[c], sb);
+        }
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = p0 + e < lim ? sa[e] * a.scale_log2 : -INFINITY;
+            x[4 + e] = p0 + 4 + e < lim ? sb[e] * a.scale_log2 : -INFINITY;
+        }
+        const float bm = max_over_rows(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+        const bool move = bm > m + kSlack;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float mn = move ? bm : m;
+            const float alpha = exp2_fast(m - mn);
+            lsum *= alpha;
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) acc[c] *= alpha;
+            m = mn;
+        }
+        const float mref = m == -INFINITY ? 0.f : m;
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(x[e] - mref);
+        lsum += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        if (jb * BS + BS > lim) {   // partly valid block: rows from lim on may hold anything
+            uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                m0 |= (p0 + e < lim ? 0xffu : 0u) << (8 * e);
+                m1 |= (p0 + 4 + e < lim ? 0xffu : 0u) << (8 * e);
+            }
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) {
+                t.v[c].x &= m0;
+                t.v[c].y &= m1;
+            }
+        }
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
+        const uint4 phi = make_uint4(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                                     uint32_t(hi[2]) | (uint32_t(hi[3]) << 16),
+                                     uint32_t(hi[4]) | (uint32_t(hi[5]) << 16),
+                                     uint32_t(hi[6]) | (uint32_t(hi[7]) << 16));
+        const uint4 plo = make_uint4(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                                     uint32_t(lo[2]) | (uint32_t(lo[3]) << 16),
+                                     uint32_t(lo[4]) | (uint32_t(lo[5]) << 16),
+                                     uint32_t(lo[6]) | (uint32_t(lo[7]) << 16));
+#pragma unroll
+        for (int c = 0; c < NPV; ++c) {
+            const uint2 w0 = Fp8<T>::x4(t.v[c].x), w1 = Fp8<T>::x4(t.v[c].y);
+            const uint4 vv = make_uint4(w0.x, w0.y, w1.x, w1.y);
+            acc[c] = Mfma<T>::qk(vv, phi, acc[c]);
+            acc[c] = Mfma<T>::qk(vv, plo, acc[c]);
+        }
+    };
+
+    // segments of up to 64 blocks (one block id per lane), two blocks in flight
+    for (int k0 = 0; k0 < nmine; k0 += 64) {
+        const int cnt = min(64, nmine - k0);
+        if (k0 == 0) {
+            tab = tab0;
+        } else {
+            const int jb = first + (k0 + lane) * W;
+            tab = lane < cnt && jb < a.max_blocks ? table[jb] : -1;
+        }
+        if constexpr (Append) {
+            if (wave == w_new && k_new >= k0 && k_new < k0 + 64) {   // wave-uniform
+                const int64_t phys_l = __builtin_amdgcn_readlane(tab, k_new - k0);
+                subst = slot >= 0 && phys_l >= 0 && phys_l < a.num_blocks &&
+                        int64_t(slot) == phys_l * BS + (n - 1) % BS;
+                lim = subst ? n - 1 : n;
+            }
+        }
+        KvBlock32<D> X, Y;
+        auto blk_of = [&](int k) { return first + (k0 + k) * W; };
+        bool okX = load(X, 0), okY = false;
+        if (k0 == 0) store_new_row();
+        for (int k = 0; k < cnt; k += 2) {
+            const int k1 = min(k + 1, cnt - 1);
+            okY = load(Y, k1);
+            compute(X, blk_of(k), okX);
+            if (k + 1 >= cnt) break;
+            const int k2 = min(k + 2, cnt - 1);
+            okX = load(X, k2);
+            compute(Y, blk_of(k + 1), okY);
+        }
+    }
+
+    // the new token as a block whose only valid position is 0 (row 0 of product A)
+    if constexpr (Append) {
+        if (wave == w_new && subst) {
+            KvBlock32<D> t;
+#pragma unroll
+            for (int c = 0; c < NKL; ++c) {
+                t.ka[c] = col == 0 ? nk[c] : make_uint4(0, 0, 0, 0);
+                t.kb[c] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) t.v[c] = make_uint2(quad == 0 ? nv[c] & 0xffu : 0u, 0u);
+            lim = 1;
+            compute(t, 0, true);
+        }
+    }
+
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (lane < 16) {
+        sm_m[wave * 16 + lane] = m;
+        sm_l[wave * 16 + lane] = lsum;
+    }
+    if (col < G) {
+#pragma unroll
+        for (int c = 0; c < NPV; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm_o[(wave * G + col) * D + 16 * c + 4 * quad + e] = acc[c][e];
+    }
+    __syncthreads();
+    merge_and_store<OutT, D, W>(a, sm_m, sm_l, sm_o, b, g, p, direct);
+}
+
 // ------------------------------------------------------- fp16 / bf16, balanced split
 // Same per-tile arithmetic as decode_mfma_kernel; the work is cut as described in
 // split.hpp. Each wave is independent: it reads the block ids of up to 64 of its tiles
@@ -979,6 +1300,17 @@ template <typename T, int D, typename OutT, bool F8, int BS>
 hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
     const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
+    if constexpr (F8 && BS == 32) {
+        if (a.part_tiles % 2 == 0) {   // partitions of whole blocks: the whole-block kernel
+            if (a.new_k)
+                hipExtLaunchKernelGGL((decode_fp8_blk32_kernel<T, D, OutT, kWaves, true>), grid,
+                                      dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
+            else
+                hipExtLaunchKernelGGL((decode_fp8_blk32_kernel<T, D, OutT, kWaves, false>), grid,
+                                      dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
+            return hipGetLastError();
+        }
+    }
     if (a.new_k)
         hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true, F8, BS>), grid,
                               dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
