@@ -158,6 +158,73 @@ __device__ void write_new_token(const DecodeArgs& a, int b, int g, int slot) {
     }
 }
 
+// FP8 fused append, in two halves. load_new_row_fp8: this lane's D/64 consecutive raw
+// elements of the new K and V rows. quantize_new_row_fp8: their codes, met in the wave's
+// LDS slice q8 (2 D bytes), from which every lane takes the ones it holds in the tile
+// layout: nk[i] the 16 codes of K group 4 i + quad, nv[c] the code of dimension 16 c + col.
+// Quantising whole K groups per lane instead cost 40 divisions per lane.
+template <int D>
+__device__ __forceinline__ void load_new_row_fp8(const uint16_t* krow, const uint16_t* vrow,
+                                                 int lane, uint32_t& nkr, uint32_t& nvr) {
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    if constexpr (D == 128) {
+        nkr = *reinterpret_cast<const uint32_t*>(krow + 2 * lane);
+        nvr = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
+    } else {
+        nkr = krow[lane];
+        nvr = vrow[lane];
+    }
+}
+template <typename T, int D>
+__device__ __forceinline__ void quantize_new_row_fp8(const DecodeArgs& a, uint8_t* q8, int lane,
+                                                     uint32_t nkr, uint32_t nvr, uint4* nk,
+                                                     uint32_t* nv) {
+    constexpr int NQ = D / 64;
+    const int col = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) {
+        q8[NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nkr >> (16 * e))), a.k_scale));
+        q8[D + NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nvr >> (16 * e))), a.v_scale));
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) nk[i] = *reinterpret_cast<const uint4*>(q8 + 64 * i + 16 * quad);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) nv[c] = q8[D + 16 * c + col];
+    __builtin_amdgcn_wave_barrier();
+}
+
+// The sequence that grid slot b takes when the kernel ranks the lengths itself (no host
+// plan): the lengths are ranked longest first (ties by index) and slot b of round
+// r = b / R, position pos, takes rank R r + pos in even rounds and R r + (n_r - 1 - pos)
+// in odd ones (R = lpt_round, n_r = sequences in that round). Every thread of the
+// workgroup calls it; it synchronises the workgroup twice.
+template <int W>
+__device__ int lpt_pick(const DecodeArgs& a, int b) {
+    __shared__ int s_n[kLptMaxSeqs];
+    __shared__ int s_pick;
+    const int t = threadIdx.x;
+    const int max_len = a.max_len;
+    for (int i = t; i < a.num_seqs; i += W * 64) {
+        const int v = a.seq_lens[i];
+        s_n[i] = v < 0 ? 0 : (v > max_len ? max_len : v);
+    }
+    __syncthreads();
+    for (int i = t; i < a.num_seqs; i += W * 64) {
+        const int mine = s_n[i];
+        int rank = 0;
+        for (int k = 0; k < a.num_seqs; ++k) {
+            const int o = s_n[k];
+            rank += (o > mine) || (o == mine && k < i);
+        }
+        const int R = a.lpt_round, r = b / R, pos = b - r * R;
+        const int hi = min(R, a.num_seqs - r * R);   // sequences in this round
+        if (rank == r * R + ((r & 1) ? hi - 1 - pos : pos)) s_pick = i;
+    }
+    __syncthreads();
+    return s_pick;
+}
+
 // Merge the per-wave states held in LDS and write out or the partition result.
 // sm_m / sm_l: [W][16], sm_o: [W][G][D] (unnormalised accumulators).
 template <typename OutT, int D, int W>
@@ -208,32 +275,10 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
     int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
     const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
-    if (a.use_order) {
+    if (a.use_order)
         b = a.order[b];
-    } else if (a.lpt_round > 0) {   // rank the lengths (ties by index); slot b takes a serpentine rank
-        __shared__ int s_n[kLptMaxSeqs];
-        __shared__ int s_pick;
-        const int t = threadIdx.x;
-        const int max_len = a.max_len;
-        for (int i = t; i < a.num_seqs; i += W * 64) {
-            const int v = a.seq_lens[i];
-            s_n[i] = v < 0 ? 0 : (v > max_len ? max_len : v);
-        }
-        __syncthreads();
-        for (int i = t; i < a.num_seqs; i += W * 64) {
-            const int mine = s_n[i];
-            int rank = 0;
-            for (int k = 0; k < a.num_seqs; ++k) {
-                const int o = s_n[k];
-                rank += (o > mine) || (o == mine && k < i);
-            }
-            const int R = a.lpt_round, r = b / R, pos = b - r * R;
-            const int hi = min(R, a.num_seqs - r * R);   // sequences in this round
-            if (rank == r * R + ((r & 1) ? hi - 1 - pos : pos)) s_pick = i;
-        }
-        __syncthreads();
-        b = s_pick;
-    }
+    else if (a.lpt_round > 0)
+        b = lpt_pick<W>(a, b);
     const int G = a.group;
     const int col = lane & 15, quad = lane >> 4;
 
@@ -257,11 +302,10 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     // tiles are on the way); the codes meet in the wave's LDS slice, from which every
     // lane takes the ones it holds in the tile layout (nk, nv). Quantising whole K groups
     // per lane instead cost 40 divisions per lane.
-    constexpr int NQ = D / 64;   // elements of each new row one lane quantises
     int slot = -1;
     uint4 nk[Append ? NKL : 1];
     uint32_t nv[Append ? NPV : 1];
-    uint32_t nkr = 0, nvr = 0;   // FP8: NQ raw 16-bit elements each (NQ <= 2)
+    uint32_t nkr = 0, nvr = 0;   // FP8: D/64 raw 16-bit elements each
     if constexpr (Append) {
         slot = a.slot_mapping[b];
         const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
@@ -269,14 +313,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
                                int64_t(g) * D;
         if constexpr (F8) {
-            static_assert(NQ == 1 || NQ == 2, "head_dim 64 or 128");
-            if constexpr (NQ == 2) {
-                nkr = *reinterpret_cast<const uint32_t*>(krow + 2 * lane);
-                nvr = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
-            } else {
-                nkr = krow[lane];
-                nvr = vrow[lane];
-            }
+            load_new_row_fp8<D>(krow, vrow, lane, nkr, nvr);
         } else {
 #pragma unroll
             for (int c = 0; c < NKL; ++c) nk[c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * quad);
@@ -285,21 +322,9 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         }
     }
     auto quantize_new = [&]() {
-        if constexpr (Append && F8) {
-            // this wave's slice of sm_o (G * D floats >= 2 * D bytes), free until the merge
-            uint8_t* q8 = reinterpret_cast<uint8_t*>(sm_o + wave * G * D);
-#pragma unroll
-            for (int e = 0; e < NQ; ++e) {
-                q8[NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nkr >> (16 * e))), a.k_scale));
-                q8[D + NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nvr >> (16 * e))), a.v_scale));
-            }
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int i = 0; i < NKL; ++i) nk[i] = *reinterpret_cast<const uint4*>(q8 + 64 * i + 16 * quad);
-#pragma unroll
-            for (int c = 0; c < NPV; ++c) nv[c] = q8[D + 16 * c + col];
-            __builtin_amdgcn_wave_barrier();
-        }
+        if constexpr (Append && F8)   // in this wave's slice of sm_o, free until the merge
+            quantize_new_row_fp8<T, D>(a, reinterpret_cast<uint8_t*>(sm_o + wave * G * D), lane,
+                                       nkr, nvr, nk, nv);
     };
 
     // The context is walked in 16-token tiles (tile j: positions 16j .. 16j + 15), which
@@ -571,32 +596,10 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
     const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
     int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
     const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
-    if (a.use_order) {
+    if (a.use_order)
         b = a.order[b];
-    } else if (a.lpt_round > 0) {   // rank the lengths as decode_mfma_kernel does
-        __shared__ int s_n[kLptMaxSeqs];
-        __shared__ int s_pick;
-        const int t = threadIdx.x;
-        const int max_len = a.max_len;
-        for (int i = t; i < a.num_seqs; i += W * 64) {
-            const int v = a.seq_lens[i];
-            s_n[i] = v < 0 ? 0 : (v > max_len ? max_len : v);
-        }
-        __syncthreads();
-        for (int i = t; i < a.num_seqs; i += W * 64) {
-            const int mine = s_n[i];
-            int rank = 0;
-            for (int k = 0; k < a.num_seqs; ++k) {
-                const int o = s_n[k];
-                rank += (o > mine) || (o == mine && k < i);
-            }
-            const int R = a.lpt_round, r = b / R, pos = b - r * R;
-            const int hi = min(R, a.num_seqs - r * R);
-            if (rank == r * R + ((r & 1) ? hi - 1 - pos : pos)) s_pick = i;
-        }
-        __syncthreads();
-        b = s_pick;
-    }
+    else if (a.lpt_round > 0)
+        b = lpt_pick<W>(a, b);
     const int G = a.group;
     const int col = lane & 15, quad = lane >> 4;
     const int ra = 8 * (col >> 2) + (col & 3), rb = ra + 4;   // this lane's K rows of A, B
@@ -613,7 +616,6 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
     // fused append: the new row's codes as this lane holds them (nk: the K groups of a
     // lane with col == 0, i.e. MFMA row 0 = position 0 of product A; nv: byte 0 of the
     // lanes with quad == 0, position 0 of each dimension)
-    constexpr int NQ = D / 64;
     int slot = -1;
     uint4 nk[Append ? NKL : 1];
     uint32_t nv[Append ? NPV : 1];
@@ -624,30 +626,12 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
                                int64_t(g) * D;
         const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
                                int64_t(g) * D;
-        static_assert(NQ == 1 || NQ == 2, "head_dim 64 or 128");
-        if constexpr (NQ == 2) {
-            nkr = *reinterpret_cast<const uint32_t*>(krow + 2 * lane);
-            nvr = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
-        } else {
-            nkr = krow[lane];
-            nvr = vrow[lane];
-        }
+        load_new_row_fp8<D>(krow, vrow, lane, nkr, nvr);
     }
     auto quantize_new = [&]() {
-        if constexpr (Append) {
-            uint8_t* q8 = reinterpret_cast<uint8_t*>(sm_o + wave * G * D);
-#pragma unroll
-            for (int e = 0; e < NQ; ++e) {
-                q8[NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nkr >> (16 * e))), a.k_scale));
-                q8[D + NQ * lane + e] = uint8_t(quantize_fp8(Bits<T>::to_f32(uint16_t(nvr >> (16 * e))), a.v_scale));
-            }
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int i = 0; i < NKL; ++i) nk[i] = *reinterpret_cast<const uint4*>(q8 + 64 * i + 16 * quad);
-#pragma unroll
-            for (int c = 0; c < NPV; ++c) nv[c] = q8[D + 16 * c + col];
-            __builtin_amdgcn_wave_barrier();
-        }
+        if constexpr (Append)
+            quantize_new_row_fp8<T, D>(a, reinterpret_cast<uint8_t*>(sm_o + wave * G * D), lane,
+                                       nkr, nvr, nk, nv);
     };
 
     // whole blocks: this wave takes blocks first, first + W, ... of its partition
