@@ -89,7 +89,9 @@ def test_decode_matches_oracle(bs, name, P, device):
                     f"bs {bs} {name} P {P} lens {lens[:3]}")
 
 
-@pytest.mark.parametrize("P", [0, 32, AUTO], ids=["single", "p32", "auto"])
+# at 32 tokens per block, FP8 caches walk whole blocks (single pass, partitions of whole
+# blocks) or 16-token tiles (partitions of 16 tokens): both paths are covered
+@pytest.mark.parametrize("P", [0, 16, 32, AUTO], ids=["single", "p16", "p32", "auto"])
 @pytest.mark.parametrize("bs", [8, 32])
 def test_fp8_decode_matches_oracle(bs, P, device):
     w = _fp8(_w("bf16-d128-g4", bs))
@@ -101,7 +103,7 @@ def test_fp8_decode_matches_oracle(bs, P, device):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-@pytest.mark.parametrize("P", [0, 32, AUTO], ids=["single", "p32", "auto"])
+@pytest.mark.parametrize("P", [0, 16, 32, AUTO], ids=["single", "p16", "p32", "auto"])
 @pytest.mark.parametrize("bs", [8, 32])
 def test_fused_append_matches_oracle(bs, P, kv, device):
     """The decode step in one call: the new rows land bit-exactly where the oracle's cache
