@@ -33,6 +33,7 @@ SHAPES = {
     "f16-d64-g8": dataclasses.replace(B8, dtype="f16", num_heads=16, num_kv_heads=2, head_dim=64,
                                       num_blocks=0),
     "bf16-d64-g1": dataclasses.replace(B8, num_heads=4, num_kv_heads=4, head_dim=64, num_blocks=0),
+    "bf16-d128-g16": dataclasses.replace(B8, num_heads=32, num_kv_heads=2, num_blocks=0),
 }
 LENS = [0, 1, 2, 7, 8, 9, 15, 16, 17, 24, 31, 32, 33, 63, 100, 255, 257, 700]
 SHORT = [1, 9, 17]          # at 8 tokens per block: a 3-entry table row
@@ -127,6 +128,27 @@ def test_fused_append_matches_oracle(bs, P, kv, device):
     assert np.array_equal(oracle.raw(gb.v_cache).view(np.uint8), ob.v_cache.view(np.uint8))
     check_close(out.cpu().double().numpy(), _oracle_decode(ob, w), w.dtype,
                 f"append {kv} bs {bs} P {P}")
+
+
+@pytest.mark.parametrize("append", [False, True], ids=["decode", "append"])
+@pytest.mark.parametrize("name", ["bf16-d128-g16", "bf16-d64-g1"])
+def test_fp8_whole_blocks_at_group_size_extremes(name, append, device):
+    """The whole-block kernel (FP8 at 32 tokens per block, single pass) with the largest
+    and the smallest GQA group, plain and with the fused append."""
+    w = _fp8(_w(name, 32))
+    ob = paged_batch.build(w, lens=LENS)
+    gb = gpu_batch.build(ob, device, write_new=not append)
+    B, Hq, d = gb.q.shape
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=device)
+    app = None
+    if append:
+        app = (ob.new_k.to(device), ob.new_v.to(device), torch.from_numpy(gb.new_slots).to(device))
+    pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale, 0, None,
+               append=app, kv_scales=gpu_batch.kv_scales(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(oracle.raw(gb.k_cache).view(np.uint8), ob.k_cache.view(np.uint8))
+    assert np.array_equal(oracle.raw(gb.v_cache).view(np.uint8), ob.v_cache.view(np.uint8))
+    check_close(out.cpu().double().numpy(), _oracle_decode(ob, w), w.dtype, f"{name} {append}")
 
 
 # (context length, chunk length) per sequence
