@@ -175,6 +175,128 @@ def _dev(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+# ------------------------------------------------------------ argument validation
+# The C ABI sees raw pointers and sizes only, so a tensor of the wrong type or shape would
+# be read with the wrong element size or extent. Every device wrapper below checks what it
+# hands over (types, shapes, contiguity, one device) and raises ValueError before any call.
+def _index(t, name, numel_min=None, shape=None):
+    """An int32, contiguous index tensor (slots, lengths, tables, offsets)."""
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel_min is not None and t.numel() < numel_min:
+        raise ValueError(f"{name} must hold at least {numel_min} entries, got {t.numel()}")
+
+
+def _same_device(ref, named):
+    for t, nm in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{nm} is on {t.device}, expected {ref.device} (where q is)")
+
+
+def _float_type(t, name):
+    torch = _torch()
+    if t.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise ValueError(f"{name} must be float32, float16 or bfloat16, got {t.dtype}")
+
+
+def _caches(k_cache, v_cache, elem_dtype, hkv=None, head_dim=None):
+    """k_cache [nb][Hkv][d/x][BS][x] and v_cache [nb][Hkv][d][BS] of elem_dtype, contiguous;
+    returns (num_blocks, Hkv, head_dim, BS)."""
+    torch = _torch()
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != elem_dtype:
+            raise ValueError(f"{nm} must be {elem_dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [nb][Hkv][d/x][BS][x] and v_cache [nb][Hkv][d][BS]")
+    nb, h, d, bs = (int(x) for x in v_cache.shape)
+    x = 16 // k_cache.element_size()
+    if tuple(k_cache.shape) != (nb, h, d // x, bs, x) or d % x:
+        raise ValueError(f"k_cache shape {tuple(k_cache.shape)} does not match v_cache "
+                         f"{tuple(v_cache.shape)} in the documented layout (x = {x})")
+    if hkv is not None and h != hkv:
+        raise ValueError(f"the caches hold {h} KV heads, expected {hkv}")
+    if head_dim is not None and d != head_dim:
+        raise ValueError(f"the caches hold head_dim {d}, expected {head_dim}")
+    return nb, h, d, bs
+
+
+def _rows(t, name, B, H, d, dtype=None):
+    """[B][H][d] with dense heads and dimensions (the first stride is free)."""
+    if tuple(t.shape) != (B, H, d) or t.stride(2) != 1 or t.stride(1) != d:
+        raise ValueError(f"{name} must be [{B}][{H}][{d}] with dense heads/dims, got "
+                         f"{tuple(t.shape)} strides {tuple(t.stride())}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _partials(part_out, part_max, part_sum, B, Hq, d, partition_size, max_partitions):
+    """The fp32 partial buffers of a partitioned decode: part_out [B][Hq][P][d],
+    part_max / part_sum [B][Hq][P], contiguous. The reduce indexes them with
+    P = part_out.shape[2], so max_partitions must be P (0: take it from part_out).
+    Returns max_partitions."""
+    torch = _torch()
+    if partition_size == 0:
+        return max_partitions
+    if part_out is None or part_max is None or part_sum is None:
+        raise ValueError("a partitioned decode needs part_out, part_max and part_sum")
+    if part_out.dim() != 4 or tuple(part_out.shape[:2]) != (B, Hq) or part_out.shape[3] != d:
+        raise ValueError(f"part_out must be [{B}][{Hq}][P][{d}], got {tuple(part_out.shape)}")
+    P = int(part_out.shape[2])
+    for t, nm in ((part_out, "part_out"), (part_max, "part_max"), (part_sum, "part_sum")):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous float32 tensor")
+    for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
+        if tuple(t.shape) != (B, Hq, P):
+            raise ValueError(f"{nm} must be [{B}][{Hq}][{P}], got {tuple(t.shape)}")
+    if max_partitions == 0:
+        return P
+    if max_partitions != P:
+        raise ValueError(f"max_partitions {max_partitions} differs from part_out's {P}")
+    return P
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, partition_size, part_out,
+                 part_max, part_sum, max_partitions, fp8, append=None):
+    """Checks shared by the decode wrappers; returns (B, Hq, d, Hkv, BS, max_partitions)."""
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][d]")
+    B, Hq, d = (int(x) for x in q.shape)
+    _float_type(q, "q")
+    _rows(q, "q", B, Hq, d)
+    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
+    _float_type(out, "out")
+    _, hkv, _, bs = _caches(k_cache, v_cache, torch.uint8 if fp8 else q.dtype, head_dim=d)
+    if Hq % hkv:
+        raise ValueError(f"num_heads {Hq} is not a multiple of the caches' {hkv} KV heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables must be [{B}][max_blocks], got {tuple(block_tables.shape)}")
+    _index(block_tables, "block_tables")
+    _index(seq_lens, "seq_lens", shape=(B,))
+    maxp = _partials(part_out, part_max, part_sum, B, Hq, d, partition_size, max_partitions)
+    named = [(out, "out"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+             (block_tables, "block_tables"), (seq_lens, "seq_lens"), (part_out, "part_out"),
+             (part_max, "part_max"), (part_sum, "part_sum")]
+    if append is not None:
+        key, value, slot_mapping = append
+        _rows(key, "key", B, hkv, d, q.dtype)
+        _rows(value, "value", B, hkv, d, q.dtype)
+        _index(slot_mapping, "slot_mapping", numel_min=B)
+        named += [(key, "key"), (value, "value"), (slot_mapping, "slot_mapping")]
+    _same_device(q, named)
+    return B, Hq, d, hkv, bs, maxp
+
+
 def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, dtype) -> int:
     v = lib().kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype_code(dtype))
     if v < 0:
@@ -396,14 +518,16 @@ def paged_attention_decode_plan(seq_lens, num_kv_heads: int):
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     """key/value: device [T][Hkv][d] (token stride free, head/dim dense); caches in the
     documented layout; slot_mapping: device int32 [T]."""
-    T, hkv, d = key.shape
-    for t, nm in ((key, "key"), (value, "value")):
-        if t.dim() != 3 or t.shape != key.shape or t.stride(2) != 1 or t.stride(1) != d:
-            raise ValueError(f"{nm} must be [T][Hkv][d] with dense heads/dims")
-    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
-        raise ValueError("caches must be contiguous")
-    if slot_mapping.numel() < T:
-        raise ValueError("slot_mapping shorter than the token count")
+    if key.dim() != 3:
+        raise ValueError("key must be [T][Hkv][d]")
+    T, hkv, d = (int(x) for x in key.shape)
+    _float_type(key, "key")
+    _rows(key, "key", T, hkv, d)
+    _rows(value, "value", T, hkv, d, key.dtype)
+    _caches(k_cache, v_cache, key.dtype, hkv, d)
+    _index(slot_mapping, "slot_mapping", numel_min=T)
+    _same_device(key, [(value, "value"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                       (slot_mapping, "slot_mapping")])
     _check(lib().reshape_and_cache(
         _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, block_size_of(v_cache),
@@ -421,14 +545,11 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
     need fp32 partial buffers part_out [B][Hq][P][d], part_max/part_sum [B][Hq][P]
     and a paged_attention_reduce call with the same arguments. seq_order: the step's
     paged_attention_decode_plan (host), or None."""
-    B, Hq, d = q.shape
-    if q.stride(2) != 1 or q.stride(1) != d:
-        raise ValueError("q must have dense heads/dims")
-    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
-    if not (block_tables.is_contiguous() and seq_lens.is_contiguous()):
-        raise ValueError("block_tables and seq_lens must be contiguous")
-    hkv = k_cache.shape[1] if num_kv_heads is None else num_kv_heads
+    B, Hq, d, hkv, _, max_partitions = _decode_args(
+        out, q, k_cache, v_cache, block_tables, seq_lens, partition_size, part_out, part_max,
+        part_sum, max_partitions, fp8=False)
+    if num_kv_heads is not None and num_kv_heads != hkv:
+        raise ValueError(f"num_kv_heads {num_kv_heads} differs from the caches' {hkv}")
     op, _keep = _order(seq_order, B)
     _check(lib().paged_attention_decode(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
@@ -447,20 +568,9 @@ def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_c
     slots in slot_mapping int32 [B]) fused with paged_attention_decode over seq_lens,
     which count the new token. Same outputs and follow-up reduce as
     paged_attention_decode."""
-    B, Hq, d = q.shape
-    hkv = k_cache.shape[1]
-    if q.stride(2) != 1 or q.stride(1) != d:
-        raise ValueError("q must have dense heads/dims")
-    for t, nm in ((key, "key"), (value, "value")):
-        if tuple(t.shape) != (B, hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
-            raise ValueError(f"{nm} must be [B][Hkv][d] with dense heads/dims")
-    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
-    if not (block_tables.is_contiguous() and seq_lens.is_contiguous() and
-            slot_mapping.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()):
-        raise ValueError("block_tables, seq_lens, slot_mapping and the caches must be contiguous")
-    if slot_mapping.numel() < B:
-        raise ValueError("slot_mapping shorter than the batch")
+    B, Hq, d, hkv, _, max_partitions = _decode_args(
+        out, q, k_cache, v_cache, block_tables, seq_lens, partition_size, part_out, part_max,
+        part_sum, max_partitions, fp8=False, append=(key, value, slot_mapping))
     op, _keep = _order(seq_order, B)
     _check(lib().paged_attention_decode_append(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
@@ -473,25 +583,21 @@ def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_c
 
 
 # ------------------------------------------------------------------ FP8 cache
-def _fp8_cache(k_cache, v_cache):
-    torch = _torch()
-    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
-        raise ValueError("an FP8 cache is held in uint8 tensors")
-    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
-        raise ValueError("caches must be contiguous")
-
-
 def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale: float,
                           v_scale: float, stream=None):
     """reshape_and_cache into an FP8 cache: the e4m3 codes of key / k_scale and
     value / v_scale (key/value fp16 or bf16 [T][Hkv][d])."""
-    T, hkv, d = key.shape
-    for t, nm in ((key, "key"), (value, "value")):
-        if t.dim() != 3 or t.shape != key.shape or t.stride(2) != 1 or t.stride(1) != d:
-            raise ValueError(f"{nm} must be [T][Hkv][d] with dense heads/dims")
-    _fp8_cache(k_cache, v_cache)
-    if slot_mapping.numel() < T:
-        raise ValueError("slot_mapping shorter than the token count")
+    torch = _torch()
+    if key.dim() != 3:
+        raise ValueError("key must be [T][Hkv][d]")
+    T, hkv, d = (int(x) for x in key.shape)
+    _float_type(key, "key")
+    _rows(key, "key", T, hkv, d)
+    _rows(value, "value", T, hkv, d, key.dtype)
+    _caches(k_cache, v_cache, torch.uint8, hkv, d)
+    _index(slot_mapping, "slot_mapping", numel_min=T)
+    _same_device(key, [(value, "value"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                       (slot_mapping, "slot_mapping")])
     _check(lib().reshape_and_cache_fp8(
         _dev(key, "key"), _dev(value, "value"), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, block_size_of(v_cache),
@@ -504,14 +610,9 @@ def paged_attention_decode_fp8(out, q, k_cache, v_cache, block_tables, seq_lens,
                                part_out=None, part_max=None, part_sum=None,
                                max_partitions: int = 0, stream=None, seq_order=None):
     """paged_attention_decode over an FP8 cache (codes times k_scale / v_scale)."""
-    B, Hq, d = q.shape
-    if q.stride(2) != 1 or q.stride(1) != d:
-        raise ValueError("q must have dense heads/dims")
-    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
-    if not (block_tables.is_contiguous() and seq_lens.is_contiguous()):
-        raise ValueError("block_tables and seq_lens must be contiguous")
-    _fp8_cache(k_cache, v_cache)
+    B, Hq, d, hkv, _, max_partitions = _decode_args(
+        out, q, k_cache, v_cache, block_tables, seq_lens, partition_size, part_out, part_max,
+        part_sum, max_partitions, fp8=True)
     op, _keep = _order(seq_order, B)
     _check(lib().paged_attention_decode_fp8(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
@@ -529,21 +630,9 @@ def paged_attention_decode_append_fp8(out, q, key, value, slot_mapping, k_cache,
                                       stream=None, seq_order=None):
     """paged_attention_decode_append over an FP8 cache: the new rows are stored as
     codes and attended to as their stored values."""
-    B, Hq, d = q.shape
-    hkv = k_cache.shape[1]
-    if q.stride(2) != 1 or q.stride(1) != d:
-        raise ValueError("q must have dense heads/dims")
-    for t, nm in ((key, "key"), (value, "value")):
-        if tuple(t.shape) != (B, hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
-            raise ValueError(f"{nm} must be [B][Hkv][d] with dense heads/dims")
-    if tuple(out.shape) != (B, Hq, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
-    if not (block_tables.is_contiguous() and seq_lens.is_contiguous() and
-            slot_mapping.is_contiguous()):
-        raise ValueError("block_tables, seq_lens and slot_mapping must be contiguous")
-    _fp8_cache(k_cache, v_cache)
-    if slot_mapping.numel() < B:
-        raise ValueError("slot_mapping shorter than the batch")
+    B, Hq, d, hkv, _, max_partitions = _decode_args(
+        out, q, k_cache, v_cache, block_tables, seq_lens, partition_size, part_out, part_max,
+        part_sum, max_partitions, fp8=True, append=(key, value, slot_mapping))
     op, _keep = _order(seq_order, B)
     _check(lib().paged_attention_decode_append_fp8(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
@@ -561,17 +650,25 @@ def paged_attention_prefill(out, q, q_start, k_cache, v_cache, block_tables, seq
     sequence's chunk back to back, sequence b in rows q_start[b] .. q_start[b+1]-1 (device
     int32 [B+1]); the chunk is the last positions of seq_lens[b] and its K/V is already in
     the cache. max_q_len bounds the chunk lengths (host value)."""
-    T, Hq, d = q.shape
-    if q.stride(2) != 1 or q.stride(1) != d:
-        raise ValueError("q must have dense heads/dims")
+    if q.dim() != 3:
+        raise ValueError("q must be [T][Hq][d]")
+    T, Hq, d = (int(x) for x in q.shape)
+    _float_type(q, "q")
+    _rows(q, "q", T, Hq, d)
     if tuple(out.shape) != (T, Hq, d) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [T][Hq][d] tensor")
+    _float_type(out, "out")
+    _, hkv, _, _ = _caches(k_cache, v_cache, q.dtype, head_dim=d)
+    if Hq % hkv:
+        raise ValueError(f"num_heads {Hq} is not a multiple of the caches' {hkv} KV heads")
     B = seq_lens.numel()
-    if q_start.numel() != B + 1 or not q_start.is_contiguous():
-        raise ValueError("q_start must hold num_seqs + 1 offsets")
-    if not (block_tables.is_contiguous() and seq_lens.is_contiguous() and
-            k_cache.is_contiguous() and v_cache.is_contiguous()):
-        raise ValueError("block_tables, seq_lens and the caches must be contiguous")
+    _index(seq_lens, "seq_lens", shape=(B,))
+    _index(q_start, "q_start", shape=(B + 1,))
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables must be [{B}][max_blocks], got {tuple(block_tables.shape)}")
+    _index(block_tables, "block_tables")
+    _same_device(q, [(out, "out"), (q_start, "q_start"), (k_cache, "k_cache"),
+                     (v_cache, "v_cache"), (block_tables, "block_tables"), (seq_lens, "seq_lens")])
     _check(lib().paged_attention_prefill(
         _dev(out, "out"), _dev(q, "q"), q.stride(0), _dev(q_start, "q_start"),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
@@ -589,8 +686,14 @@ def copy_blocks(k_caches, v_caches, pairs, stream=None):
     for t in list(k_caches) + list(v_caches):
         if not t.is_contiguous() or t.shape[0] != k_caches[0].shape[0]:
             raise ValueError("caches must be contiguous with the same number of blocks")
-    if pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be a contiguous [n][2] int32 tensor")
+    _index(pairs, "pairs")
+    for group in (k_caches, v_caches):
+        for t in group:
+            if t.dtype != k_caches[0].dtype or tuple(t.shape) != tuple(group[0].shape):
+                raise ValueError("every layer's caches must have the same type and shape")
+    _same_device(pairs, [(t, "cache") for t in list(k_caches) + list(v_caches)])
     kp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in k_caches])
     vp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in v_caches])
     block_bytes = k_caches[0][0].numel() * k_caches[0].element_size()
@@ -601,8 +704,16 @@ def copy_blocks(k_caches, v_caches, pairs, stream=None):
 def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partition_size: int,
                            num_kv_heads: int, max_blocks_per_seq: int,
                            block_size: int = BLOCK_SIZE, stream=None):
-    B, Hq, d = out.shape
-    P = part_out.shape[2]
+    if out.dim() != 3 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][Hq][d] tensor")
+    B, Hq, d = (int(x) for x in out.shape)
+    _float_type(out, "out")
+    if partition_size == 0:
+        raise ValueError("paged_attention_reduce follows a partitioned decode (partition_size != 0)")
+    P = _partials(part_out, part_max, part_sum, B, Hq, d, partition_size, 0)
+    _index(seq_lens, "seq_lens", shape=(B,))
+    _same_device(out, [(part_out, "part_out"), (part_max, "part_max"), (part_sum, "part_sum"),
+                       (seq_lens, "seq_lens")])
     _check(lib().paged_attention_reduce(
         _dev(out, "out"), _dev(part_out, "part_out"), _dev(part_max, "part_max"),
         _dev(part_sum, "part_sum"), _dev(seq_lens, "seq_lens"), B, Hq, num_kv_heads, d,

@@ -13,7 +13,7 @@ import gpu_batch
 import oracle
 import paged_batch
 import paged_kv_cache_28_amd as pkv
-from test_gpu_parity import RAGGED, SHAPES, check_close
+from test_gpu_parity import RAGGED, SHAPES, TOL, _ulp, check_close
 
 pytestmark = pytest.mark.gpu
 AUTO = pkv.PKV_PARTITION_AUTO
@@ -44,7 +44,7 @@ def _same_output(a, b):
         assert ((x - y).abs() <= eps * torch.maximum(x.abs(), y.abs()) + 1e-6).all()
 
 
-def _run(gb, w, P, out_dtype, append):
+def _run(gb, w, P, out_dtype, append, plan=False):
     B, Hq, d = gb.q.shape
     dev = gb.q.device
     out = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=dev)
@@ -52,15 +52,17 @@ def _run(gb, w, P, out_dtype, append):
     if P != 0:
         maxp = pkv.max_partitions_for(gb.tables.shape[1], P)
         parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, dev))
+    order = pkv.paged_attention_decode_plan(gb.lens, w.num_kv_heads) if plan else None
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale, P, parts,
-               append=append)
+               append=append, seq_order=order)
     torch.cuda.synchronize()
     return out
 
 
-def _pair(ob, w, P, device, out_dtype=torch.float32, pre_written=()):
+def _pair(ob, w, P, device, out_dtype=torch.float32, pre_written=(), plan=False):
     """(two-call result, fused result): outputs and both caches of each path.
-    Sequences in pre_written already hold their new row and pass slot -1."""
+    Sequences in pre_written already hold their new row and pass slot -1. plan: both
+    paths take the step's host plan (paged_attention_decode_plan) as seq_order."""
     res = []
     for fused in (False, True):
         gb = gpu_batch.build(ob, device, write_new=False)
@@ -73,10 +75,10 @@ def _pair(ob, w, P, device, out_dtype=torch.float32, pre_written=()):
             slots[idx] = -1
         slots_d = torch.from_numpy(slots).to(device)
         if fused:
-            out = _run(gb, w, P, out_dtype, (nk, nv, slots_d))
+            out = _run(gb, w, P, out_dtype, (nk, nv, slots_d), plan)
         else:
             pkv.reshape_and_cache(nk, nv, gb.k_cache, gb.v_cache, slots_d)
-            out = _run(gb, w, P, out_dtype, None)
+            out = _run(gb, w, P, out_dtype, None, plan)
         res.append((out, gb.k_cache, gb.v_cache))
     return res
 
@@ -109,13 +111,27 @@ def test_append_with_cached_rows_and_bf16_out(P, out_dtype, device):
     _same_output(oa, ob_)
 
 
-def test_append_full_size_8b(device):
-    """The 8B workload at full size in the bench's launch mode."""
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_append_full_size_8b(out_dtype, device):
+    """The 8B workload at full size in the bench's launch mode: the fused append with the
+    step's host plan. Caches bit-exact against the oracle's cache write and the two-call
+    path; every one of the 2,048 output rows against the fp64 oracle (fp32 output: the
+    2e-3 and 1e-3 bars; bf16 output, what the bench writes: the fp32 bar plus half an
+    output ulp)."""
     w = SHAPES["8b-bf16"]
     ob = paged_batch.build(w)
-    (oa, ka, va), (ob_, kb, vb) = _pair(ob, w, w.partition_size, device, torch.bfloat16)
+    (oa, ka, va), (ob_, kb, vb) = _pair(ob, w, w.partition_size, device, out_dtype, plan=True)
     assert torch.equal(_bits(ka), _bits(kb)) and torch.equal(_bits(va), _bits(vb))
+    assert np.array_equal(oracle.raw(kb), ob.k_cache) and np.array_equal(oracle.raw(vb), ob.v_cache)
     _same_output(oa, ob_)
+    ref = oracle.decode(ob.q, ob.k_cache, ob.v_cache, ob.tables, ob.lens, w.scale, w.dtype)
+    got = ob_.cpu().double().numpy()
+    assert got.shape[0] * got.shape[1] == 2048
+    if out_dtype == torch.float32:
+        check_close(got, ref, w.dtype, "8B fused + plan")
+    else:
+        assert np.all(np.isfinite(got))
+        assert np.all(np.abs(got - ref) <= TOL["bf16"] + 0.5 * _ulp(got, "bf16"))
 
 
 def test_append_validation(device):

@@ -114,9 +114,12 @@ def test_prefill_rejects_bad_arguments(device):
     qs = torch.tensor([0, 3], dtype=torch.int32, device=device)
     tab = torch.zeros((1, 1), dtype=torch.int32, device=device)
     ln = torch.tensor([3], dtype=torch.int32, device=device)
+    kc32, vc32 = pkv.alloc_caches(4, w.num_kv_heads, w.head_dim, "f32", device, fill=0.0)
     with pytest.raises(pkv.PkvError) as e:
-        pkv.paged_attention_prefill(q.clone(), q, qs, kc, vc, tab, ln, 0.1, 3)
-    assert e.value.code == pkv.PKV_ENOTSUP                 # fp32 queries
+        pkv.paged_attention_prefill(q.clone(), q, qs, kc32, vc32, tab, ln, 0.1, 3)
+    assert e.value.code == pkv.PKV_ENOTSUP                 # fp32 queries and caches
+    with pytest.raises(ValueError, match="k_cache must be"):
+        pkv.paged_attention_prefill(q.clone(), q, qs, kc, vc, tab, ln, 0.1, 3)   # f32 over bf16
     qb = q.bfloat16()
     with pytest.raises(pkv.PkvError) as e:
         pkv.paged_attention_prefill(qb.half(), qb, qs, kc, vc, tab, ln, 0.1, 3)
