@@ -48,6 +48,7 @@
 #ifndef PKV_H
 #define PKV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -416,6 +417,35 @@ int paged_attention_reduce(void* out, const float* part_out, const float* part_m
                            int32_t block_size, int32_t max_blocks_per_seq,
                            int32_t partition_size, int32_t max_partitions, int32_t out_dtype,
                            void* stream);
+
+/* paged_attention_decode_noalloc: for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It is
+ * paged_attention_decode with partition_size > 0 or PKV_PARTITION_AUTO followed by
+ * paged_attention_reduce, with the partition records (part_out, part_max, part_sum) kept
+ * in a static device workspace of paged_attention_decode_noalloc_workspace() bytes
+ * (64 MiB) instead of caller buffers. The workspace belongs to the library: the runtime
+ * reserves it on each device when the library's code is first used there, and it stays
+ * reserved until the process ends; the call itself allocates and frees nothing.
+ *   Every call on one device shares that device's workspace, so calls that may overlap on
+ *   one device (other streams, other threads) race and must be serialised by the caller;
+ *   calls on one stream are ordered and safe. Nothing in the workspace needs clearing.
+ *   partition_size == 0 is the single pass and uses no workspace.
+ *   Records: num_seqs * num_heads rows of P records of (head_dim + 2) floats, with
+ *   P = ceil(max_blocks_per_seq * block_size / partition_size) for fixed partitions, and for
+ *   PKV_PARTITION_AUTO P = max(2, ceil(T / 4) + 1) (T = ceil(max_blocks_per_seq *
+ *   block_size / 16)) lowered to what the workspace holds (longer pieces, same result to
+ *   fp32 rounding).
+ *   out must be 16-byte aligned. Other arguments, outputs and errors as
+ *   paged_attention_decode; EINVAL (nothing enqueued) when the records do not fit, with a
+ *   message giving the bytes needed. */
+size_t paged_attention_decode_noalloc_workspace(void);
+int paged_attention_decode_noalloc(void* out, const void* q, int64_t q_stride, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                   int32_t partition_size, int32_t in_dtype, int32_t out_dtype,
+                                   void* stream);
 
 /* paged_attention_prefill: causal multi-query attention over the paged cache, for
  * chunked prefill: a long prompt is processed in chunks over several steps, each chunk's

@@ -103,6 +103,9 @@ def lib():
         "paged_attention_decode_append_fp8": ([P, P, P, P, P, I64, P, P, I64, I64, P, P, P, P, P,
                                                I32, I32, I32, I32, I32, I32, I64, F, F, F, I32,
                                                I32, I32, I32, P, P], ctypes.c_int),
+        "paged_attention_decode_noalloc": ([P, P, I64, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                            I64, F, I32, I32, I32, P], ctypes.c_int),
+        "paged_attention_decode_noalloc_workspace": ([], ctypes.c_size_t),
         "pkv_timer_enable": ([I32], ctypes.c_int),
         "pkv_timer_read": ([I32, P, P], ctypes.c_int),
     }
@@ -124,7 +127,8 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "paged_attention_decode_append_fp8", "pkv_timer_enable", "pkv_timer_read",
             "kv_pool_add_seq_prefix", "kv_pool_fork", "kv_pool_append_tokens",
             "kv_pool_append_batch_tokens", "copy_blocks", "paged_attention_prefill",
-            "paged_attention_decode_plan")
+            "paged_attention_decode_plan", "paged_attention_decode_noalloc",
+            "paged_attention_decode_noalloc_workspace")
 
 
 def _check(rc: int):
@@ -580,6 +584,27 @@ def paged_attention_decode_append(out, q, key, value, slot_mapping, k_cache, v_c
         _dev(seq_lens, "seq_lens"), B, Hq, hkv, d, block_size_of(v_cache), block_tables.shape[1],
         k_cache.shape[0], float(scale), partition_size, max_partitions, dtype_code(q.dtype),
         dtype_code(out.dtype), op, _stream(q, stream)))
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens,
+                                   scale: float, partition_size: int = PKV_PARTITION_AUTO,
+                                   stream=None):
+    """A partitioned decode and its reduce in one call with no device allocation: the
+    partition records live in the library's static per-device workspace (calls that
+    overlap on one device race on it). partition_size: a multiple of 16 or
+    PKV_PARTITION_AUTO (0: the single pass)."""
+    B, Hq, d, hkv, bs, _ = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, 0,
+                                        None, None, None, 0, fp8=False)
+    _check(lib().paged_attention_decode_noalloc(
+        _dev(out, "out"), _dev(q, "q"), q.stride(0), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
+        B, Hq, hkv, d, bs, block_tables.shape[1], k_cache.shape[0], float(scale), partition_size,
+        dtype_code(q.dtype), dtype_code(out.dtype), _stream(q, stream)))
+
+
+def noalloc_workspace_bytes() -> int:
+    """Bytes of the static per-device workspace of paged_attention_decode_noalloc."""
+    return int(lib().paged_attention_decode_noalloc_workspace())
 
 
 # ------------------------------------------------------------------ FP8 cache

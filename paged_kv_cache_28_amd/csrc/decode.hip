@@ -350,3 +350,123 @@ extern "C" int paged_attention_decode_plan(const int32_t* seq_lens, int32_t num_
     }
     return pkv::ok();
 }
+
+// ---- decode without allocation -----------------------------------------------------
+// paged_attention_decode_noalloc: a partitioned decode and its reduce in one call, for
+// callers that cannot allocate device memory. The partition records (part_out, part_max,
+// part_sum) live in `scratch`, a file-scope device array that the runtime reserves on each
+// device when this code object is first used there and keeps until the process ends. Every
+// call on a device shares that device's array: calls that overlap on one device (two
+// streams, two threads) race on it. Nothing in it has to start at zero: the decode writes
+// every record the reduce reads, so the contents a previous call left do not matter.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;   // 64 MiB per device
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up on the first call made
+// with that device current and kept. In host code the name `scratch` stands for a
+// host-side shadow, not device memory: only this address may reach a kernel.
+int scratch_address(const char* who, char** out) {
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return pkv::fail(PKV_EHIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return pkv::fail(PKV_ENOTSUP, "%s: device ordinal %d", who, dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return pkv::fail(PKV_EHIP, "%s: hipGetSymbolAddress(scratch): %s", who,
+                             hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = static_cast<char*>(addr[dev]);
+    return PKV_OK;
+}
+
+size_t round_up_256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" size_t paged_attention_decode_noalloc_workspace(void) { return kScratchBytes; }
+
+extern "C" int paged_attention_decode_noalloc(void* out, const void* q, int64_t q_stride,
+                                              const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, const int32_t* seq_lens,
+                                              int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t block_size, int32_t max_blocks_per_seq,
+                                              int64_t num_blocks, float scale,
+                                              int32_t partition_size, int32_t in_dtype,
+                                              int32_t out_dtype, void* stream) {
+    using pkv::fail;
+    const char* who = "paged_attention_decode_noalloc";
+    const AppendIn none{nullptr, nullptr, 0, 0, nullptr};
+    if (partition_size == 0)   // the single pass keeps no records
+        return decode_impl(who, out, nullptr, nullptr, nullptr, q, q_stride, k_cache, v_cache,
+                           block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                           block_size, max_blocks_per_seq, num_blocks, scale, 0, 0, in_dtype,
+                           out_dtype, in_dtype, 1.0f, 1.0f, none, nullptr, stream);
+    // Sizes of the records, from arguments decode_impl checks again below.
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+        (block_size != 8 && block_size != 16 && block_size != 32) ||
+        int64_t(max_blocks_per_seq) * block_size > INT32_MAX)
+        return fail(PKV_EINVAL, "%s: bad num_seqs / num_heads / head_dim / block_size / "
+                                "max_blocks_per_seq", who);
+    if (partition_size != PKV_PARTITION_AUTO && (partition_size < 0 || partition_size % 16))
+        return fail(PKV_EINVAL, "%s: partition_size must be 0, PKV_PARTITION_AUTO or a "
+                                "positive multiple of 16", who);
+    const int64_t max_tiles = (int64_t(max_blocks_per_seq) * block_size + 15) / 16;
+    const int64_t rows = int64_t(num_seqs) * num_heads;   // (b, h) rows of records
+    const int64_t rec_bytes = (int64_t(head_dim) + 2) * 4;  // o, m and l of one record
+    int64_t maxp;
+    if (partition_size == PKV_PARTITION_AUTO) {
+        // The bound paged_attention_decode's callers use (pieces of at least four tiles),
+        // lowered to what the workspace holds: fewer records per row only make the pieces
+        // longer (the split stays balanced up to that length).
+        maxp = std::max<int64_t>(2, (max_tiles + 3) / 4 + 1);
+        const int64_t fit = rows > 0 ? int64_t(kScratchBytes - 512) / (rows * rec_bytes) : maxp;
+        maxp = std::min(maxp, fit);
+        if (maxp < 2)
+            return fail(PKV_EINVAL, "%s: %lld (sequence, head) rows need %lld bytes of workspace "
+                                    "for two records each, above the %zu-byte static workspace",
+                        who, (long long)rows, (long long)(2 * rows * rec_bytes), kScratchBytes);
+    } else {
+        maxp = (max_tiles + partition_size / 16 - 1) / (partition_size / 16);
+        if (rows * maxp * rec_bytes + 512 > int64_t(kScratchBytes))
+            return fail(PKV_EINVAL, "%s: %lld rows x %lld partitions need %lld bytes of workspace, "
+                                    "above the %zu-byte static workspace (use larger partitions or "
+                                    "paged_attention_decode with caller-owned buffers)",
+                        who, (long long)rows, (long long)maxp,
+                        (long long)(rows * maxp * rec_bytes), kScratchBytes);
+    }
+    if (maxp > INT32_MAX) return fail(PKV_EINVAL, "%s: too many partitions", who);
+    if (num_seqs > 0 && (!out || (reinterpret_cast<uintptr_t>(out) & 15)))
+        return fail(PKV_EINVAL, "%s: out must be non-NULL and 16-byte aligned", who);
+    char* ws = nullptr;
+    if (num_seqs > 0) {
+        const int rc = scratch_address(who, &ws);
+        if (rc != PKV_OK) return rc;
+    }
+    // part_out [rows][maxp][d], then part_max and part_sum [rows][maxp], 256-byte aligned
+    const size_t o_bytes = round_up_256(size_t(rows * maxp * head_dim) * 4);
+    const size_t m_bytes = round_up_256(size_t(rows * maxp) * 4);
+    float* part_out = reinterpret_cast<float*>(ws);
+    float* part_max = reinterpret_cast<float*>(ws + o_bytes);
+    float* part_sum = reinterpret_cast<float*>(ws + o_bytes + m_bytes);
+    int rc = decode_impl(who, out, part_out, part_max, part_sum, q, q_stride, k_cache, v_cache,
+                         block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                         block_size, max_blocks_per_seq, num_blocks, scale, partition_size,
+                         int32_t(maxp), in_dtype, out_dtype, in_dtype, 1.0f, 1.0f, none, nullptr,
+                         stream);
+    if (rc != PKV_OK || num_seqs == 0) return rc;
+    return paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, num_seqs, num_heads,
+                                  num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                  partition_size, int32_t(maxp), out_dtype, stream);
+}
