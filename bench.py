@@ -69,6 +69,18 @@ def parse():
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
                     help="only time copy_blocks (copy-on-write of N forked sequences' partly "
                          "filled blocks, every layer of the workload) and exit")
+    ap.add_argument("--no-70b", action="store_true",
+                    help="llama8b: skip the second object (the 70B batch, balanced split)")
+    ap.add_argument("--print-launch-bytes", action="store_true",
+                    help="add the algorithmic bytes of every decode launch to the line (for "
+                         "pairing with HBM counters of the same run)")
+    ap.add_argument("--traffic-summary", nargs=5, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "BENCH_LOG"),
+                    help="only pair rocprofv3 HBM counters with the launches' algorithmic "
+                         "bytes and write profiles/decode_<workload>_traffic.json")
+    ap.add_argument("--cache-write-sweep", action="store_true",
+                    help="only time reshape_and_cache / reshape_and_cache_fp8 over token counts "
+                         "and slot patterns (8B shape) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer 8 times (a plain copy of known size, to "
                          "scale the HBM byte counters) and exit")
@@ -88,19 +100,98 @@ def decode_source_sha256() -> str:
                                    for f in DECODE_SOURCES)).hexdigest()
 
 
-def measured_traffic(workload: str, partition_size: int, fused: bool, block_size: int):
-    """HBM bytes per decode launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE runs recorded in
-    profiles/ (scaled by the copy calibration), or None if those counters were taken for
-    another workload/mode/block size or for kernel sources other than the ones built now."""
+def measured_traffic(workload: str, partition_size: int, fused: bool, block_size: int, args,
+                     alg_per_launch):
+    """HBM bytes per decode launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+    profiles/decode_<workload>_traffic.json (copy-calibrated, averaged over the kernel-timing
+    pass's dispatches of a run of this same command), or None unless that record was taken
+    for the kernel sources built now, in this launch mode, with this many steps, and over
+    launches whose algorithmic bytes equal this run's (the same dispatches)."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
-    if partition_size != 0 or not fused or not os.path.exists(path):
+    if partition_size != 0 or not fused or not os.path.exists(path) or alg_per_launch is None:
         return None
     rec = json.load(open(path))
     if rec.get("mode") != "single pass, fused append" or rec.get("block_size") != block_size:
         return None
     if decode_source_sha256() != rec.get("source_sha256"):
         return None
-    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+    tp = rec.get("timing_pass") or {}
+    if (rec.get("steps"), rec.get("warmup")) != (args.steps, args.warmup) or \
+            tp.get("alg_bytes_per_launch") != alg_per_launch:
+        return None
+    return {"bytes_per_launch": int(tp["fetch_bytes_per_launch"] + tp["write_bytes_per_launch"]),
+            "record": {"file": os.path.relpath(path, ROOT),
+                       "fetch_bytes_per_launch": tp["fetch_bytes_per_launch"],
+                       "write_bytes_per_launch": tp["write_bytes_per_launch"],
+                       "fetch_over_alg": round(tp["fetch_bytes_per_launch"] / alg_per_launch, 4),
+                       "dispatches": tp["dispatches"]}}
+
+
+def _counter_rows(d: str):
+    """(dispatch id, kernel name, counter, value) rows of a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
+                             float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def traffic_summary(spec):
+    """Pair the HBM counters of a decode run with the algorithmic bytes of the same
+    dispatches. spec: FETCH_DIR WRITE_DIR CAL_FETCH_DIR CAL_WRITE_DIR BENCH_LOG: the
+    rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE directories of `bench.py ... --no-cpu-baseline
+    --no-70b --print-launch-bytes`, those of `bench.py --calibrate-copy`, and the bench's
+    JSON line from the FETCH_SIZE run. Writes profiles/decode_<workload>_traffic.json and
+    prints the figures."""
+    import numpy as np
+    fetch_d, write_d, cal_f, cal_w, log = spec
+    line = [ln for ln in open(log) if ln.startswith("{") and '"launch_alg_bytes"' in ln][-1]
+    bench = json.loads(line)
+    alg = np.asarray(bench["launch_alg_bytes"], dtype=np.float64)
+
+    def per_dispatch(d, counter, match):
+        vals = {}
+        for did, name, cn, v in _counter_rows(d):
+            if cn == counter and match(name):
+                vals[did] = vals.get(did, 0.0) + v
+        return np.asarray([vals[k] for k in sorted(vals)])
+
+    def scale(d, counter):   # bytes per KiB of the counter, from 1 GiB copies
+        v = per_dispatch(d, counter, lambda n: "copyBuffer" in n)
+        big = v[v > 0.9 * v.max()]
+        return (1 << 30) / (float(np.median(big)) * 1024)
+
+    is_decode = lambda n: "pkv::decode_" in n   # noqa: E731
+    fs, ws = scale(cal_f, "FETCH_SIZE"), scale(cal_w, "WRITE_SIZE")
+    f = per_dispatch(fetch_d, "FETCH_SIZE", is_decode) * 1024 * fs
+    wr = per_dispatch(write_d, "WRITE_SIZE", is_decode) * 1024 * ws
+    if not (len(f) == len(wr) == len(alg)):
+        raise SystemExit(f"dispatch counts differ: fetch {len(f)}, write {len(wr)}, "
+                         f"launches {len(alg)}")
+    cfg = bench["config"]
+    n_t = bench["steps"] * cfg["layers"]
+    sl = slice(len(alg) - n_t, len(alg))
+    rec = {
+        "kernel": bench["roofline"]["kernel"], "mode": "single pass, fused append",
+        "workload": cfg["workload"].replace("-decode", ""), "block_size": cfg["block_size"],
+        "source_sha256": decode_source_sha256(), "steps": bench["steps"],
+        "warmup": bench["warmup"], "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+        "timing_pass": {"dispatches": n_t,
+                        "fetch_bytes_per_launch": int(f[sl].mean()),
+                        "write_bytes_per_launch": int(wr[sl].mean()),
+                        "alg_bytes_per_launch": int(alg[sl].mean())},
+        "all_dispatches": {"dispatches": len(alg), "fetch_over_alg": round(float(f.sum() / alg.sum()), 4),
+                           "write_bytes_per_launch": int(wr.mean())},
+    }
+    out = os.path.join(ROOT, "profiles", f"decode_{rec['workload']}_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def calibrate_copy():
@@ -153,6 +244,57 @@ def bench_copy_blocks(args):
         "bytes_per_call": moved, "GB/s": round(moved / (per_call_us * 1e-6) / 1e9, 1),
         "frac_of_peak": round(moved / (per_call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}),
           flush=True)
+
+
+def bench_cache_write_sweep(args):
+    """reshape_and_cache (and its FP8 form) on the 8B shape (8 KV heads, d 128, bf16 rows) for
+    prompt-sized and decode-sized token counts, with consecutive slots (a prompt or chunk) and
+    scattered ones (one token each of many sequences), timed with the library's kernel timer
+    (median of 20 launches over a pool larger than the Infinity Cache)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_28_amd as pkv
+    dev = torch.device("cuda:0")
+    Hkv, d = 8, 128
+    nb = 40000                                        # 655 MB per cache pair in bf16
+    rows = {}
+    for cache in ("bf16", "fp8"):
+        kc, vc = pkv.alloc_caches(nb, Hkv, d, cache, dev, fill=0)
+        for T in (64, 256, 1024, 4096, 16384):
+            src = torch.randn((T, Hkv, d), device=dev).to(torch.bfloat16)
+            gen = np.random.default_rng(T)
+            for pattern in ("consecutive", "scattered"):
+                if pattern == "consecutive":
+                    start = int(gen.integers(0, nb * 16 - T))
+                    slots = np.arange(start, start + T, dtype=np.int32)
+                else:
+                    slots = (gen.permutation(nb)[:T] * 16 + gen.integers(0, 16, T)).astype(np.int32)
+                sl = torch.from_numpy(slots).to(dev)
+
+                def call():
+                    if cache == "fp8":
+                        pkv.reshape_and_cache_fp8(src, src, kc, vc, sl, 0.015, 0.0125)
+                    else:
+                        pkv.reshape_and_cache(src, src, kc, vc, sl)
+                call()
+                torch.cuda.synchronize()
+                pkv.timer_enable(True)
+                times = []
+                for _ in range(20):
+                    call()
+                    ms, n = pkv.timer_read(pkv.PKV_TIMER_CACHE_WRITE)
+                    times.append(ms * 1e3 / max(n, 1))
+                pkv.timer_enable(False)
+                us = float(np.median(times))
+                moved = T * Hkv * d * (2 + (1 if cache == "fp8" else 2)) * 2   # read + write
+                rows[f"{cache}/{pattern}/{T}"] = {"us": round(us, 2),
+                                                  "GB/s": round(moved / (us * 1e-6) / 1e9, 1)}
+        del kc, vc
+        torch.cuda.empty_cache()
+    print(json.dumps({"cache_write_sweep": rows, "shape": "8 KV heads, head_dim 128, bf16 rows",
+                      "timing": "library kernel timer, median of 20 launches",
+                      "bytes": "rows read + cache bytes written"}), flush=True)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
@@ -442,8 +584,14 @@ def main():
         print("bench.py measures one GPU only (run with --gpus 1): every path here is timed "
               "on one GPU's share of the work", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary)
+        return
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.cache_write_sweep:
+        bench_cache_write_sweep(args)
         return
     if args.copy_blocks:
         bench_copy_blocks(args)
@@ -455,27 +603,46 @@ def main():
     if _wl.WORKLOADS[args.config].prefill_tokens:
         bench_prefill(args)
         return
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = _wl.WORKLOADS[args.config]
+    result, ceiling = bench_decode(args, w, primary=True)
+    # The other decode configuration the target names: the 70B batch in its own launch mode
+    # (balanced split, its own 80 layer pools), timed the same way in the same run.
+    if (args.config == "llama8b" and not args.no_70b and args.partition is None and
+            args.block_size is None and not args.unfused and not args.no_plan):
+        r70, _ = bench_decode(args, _wl.WORKLOADS["llama70b"], primary=False, ceiling=ceiling)
+        result["llama70b"] = r70
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args, w, primary: bool, ceiling=None):
+    """The decode step of workload w: K timed steps after W warm-up steps with no
+    instrumentation, then K more under the library's kernel timer. Returns the bench line
+    (primary) or its compact form for a second configuration, and the measured ceilings."""
+    import gc
+
     import numpy as np
     import torch
 
     import paged_kv_cache_28_amd as pkv
     import workloads
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
     dev = torch.device("cuda:0")
-    w = workloads.WORKLOADS[args.config]
-    if args.partition is None:
+    if args.partition is None or not primary:
         P = w.partition_size
     else:
         P = pkv.PKV_PARTITION_AUTO if args.partition == "auto" else int(args.partition)
     L, B, Hq, Hkv, d = w.layers, w.batch, w.num_heads, w.num_kv_heads, w.head_dim
-    bs = args.block_size or w.block_size
+    bs = (args.block_size if primary else None) or w.block_size
     e = w.elem_bytes                 # q, out and new-row inputs
     ekv = w.cache_elem_bytes         # cache elements (1 for an FP8 cache)
     fp8 = w.cache_dtype == "fp8"
     tdt = pkv.torch_dtype(w.dtype)
+    unfused = args.unfused and primary
+    no_plan = args.no_plan and primary
 
     # ---------------------------------------------------------------- setup
     lens0 = workloads.draw_seq_lens(w)                 # context at the first step
@@ -521,6 +688,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     kv_bytes_steps = []
+    step_lens = []      # every step's lengths, in launch order (for per-launch bytes)
 
     def step(s: int):
         k = s & 1
@@ -528,8 +696,9 @@ def main():
         pool.append_batch(ids, out=h_slot[k].numpy())
         pool.build_tables(ids, max_blocks, h_tab[k].numpy(), h_len[k].numpy())
         # the step's schedule, once for all layers (the single pass uses it)
-        order = None if args.no_plan else pkv.paged_attention_decode_plan(h_len[k].numpy(), Hkv)
+        order = None if no_plan else pkv.paged_attention_decode_plan(h_len[k].numpy(), Hkv)
         kv_bytes_steps.append(int(h_len[k].numpy().astype(np.int64).sum()) * Hkv * d * 2 * ekv * L)
+        step_lens.append(h_len[k].numpy().copy())
         d_slot.copy_(h_slot[k], non_blocking=True)
         d_tab.copy_(h_tab[k], non_blocking=True)
         d_len.copy_(h_len[k], non_blocking=True)
@@ -537,7 +706,7 @@ def main():
         po, pm, ps = parts if P != 0 else (None, None, None)
         for layer in range(L):
             kc, vc = caches[layer]
-            if fp8 and args.unfused:
+            if fp8 and unfused:
                 pkv.reshape_and_cache_fp8(k_new[layer], v_new[layer], kc, vc, d_slot, w.k_scale,
                                           w.v_scale)
                 pkv.paged_attention_decode_fp8(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
@@ -548,7 +717,7 @@ def main():
                                                       v_new[layer], d_slot, kc, vc, d_tab, d_len,
                                                       w.scale, w.k_scale, w.v_scale, P, po, pm,
                                                       ps, maxp, seq_order=order)
-            elif args.unfused:
+            elif unfused:
                 pkv.reshape_and_cache(k_new[layer], v_new[layer], kc, vc, d_slot)
                 pkv.paged_attention_decode(out[layer], q[layer], kc, vc, d_tab, d_len, w.scale,
                                            P, po, pm, ps, maxp, seq_order=order)
@@ -562,7 +731,6 @@ def main():
     # Python's cyclic collector stays off from the warm-up to the end of the kernel-timing
     # pass: a full collection of the interpreter's heap (torch's objects) takes about 40 ms
     # and would land in whichever step crosses its allocation threshold.
-    import gc
     gc.collect()
     gc.freeze()
     gc.disable()
@@ -570,11 +738,9 @@ def main():
         step(s)
     torch.cuda.synchronize()
     kv_bytes_steps.clear()
-    lens_steps = []
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(args.warmup + s)
-        lens_steps.append(h_len[(args.warmup + s) & 1].numpy().copy())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -604,17 +770,80 @@ def main():
         pkv.timer_enable(False)
     gc.enable()
     dec_avg_s = kernel_us["decode"] / 1e6 if kernel_us["decode"] else float("nan")
+    attn_s = dec_avg_s + (kernel_us["reduce"] or 0.0) / 1e6
+
     # algorithmic bytes of one decode launch: KV once per (seq, KV head), q, out, table rows;
     # fused, also the new rows read from the inputs and written to the pool
-    new_rows = 0 if args.unfused else 2 * (B * Hkv * d * (e + ekv)) + 4 * B
-    alg = []
-    for ln in timing_lens:
+    fused_write = not unfused and P != pkv.PKV_PARTITION_AUTO
+    new_rows = 2 * (B * Hkv * d * (e + ekv)) + 4 * B if fused_write else 0
+
+    def alg_bytes(ln):
         ln = ln.astype(np.int64)
-        alg.append(int(ln.sum()) * Hkv * d * 2 * ekv + 2 * B * Hq * d * e +
-                   int((-(-ln // bs)).sum()) * 4 + 4 * B + new_rows)
+        return (int(ln.sum()) * Hkv * d * 2 * ekv + 2 * B * Hq * d * e +
+                int((-(-ln // bs)).sum()) * 4 + 4 * B + new_rows)
+
+    alg = [alg_bytes(ln) for ln in timing_lens]
     alg_per_launch = sum(alg) / len(alg) if alg else float("nan")
+    kv_per_launch = (sum(int(ln.astype(np.int64).sum()) for ln in timing_lens) * Hkv * d * 2 * ekv
+                     / len(timing_lens)) if timing_lens else float("nan")
     achieved = alg_per_launch / dec_avg_s / 1e9
     value = kv_total / elapsed / 1e9
+
+    # ceilings: a contiguous read, and the same tile set gathered through the tables of the
+    # kernel-timing pass's last step (no arithmetic), each from HIP kernels of the library
+    if ceiling is None:
+        ceiling = read_ceiling(dev, int(alg_per_launch) if alg else 1 << 28)
+    gather = gather_ceiling(caches, d_tab, d_len, timing_lens[-1] if timing_lens else None,
+                            Hkv, P, no_plan, alg_bytes, kv_bytes=lambda ln: int(
+                                ln.astype(np.int64).sum()) * Hkv * d * 2 * ekv)
+
+    cfg = {"workload": f"{w.name}-decode", "layers": L, "batch": B, "num_heads": Hq,
+           "num_kv_heads": Hkv, "head_dim": d, "block_size": bs,
+           "kv_cache_dtype": ("fp8 e4m3, k_scale %g, v_scale %g" % (w.k_scale, w.v_scale)
+                              if fp8 else w.dtype),
+           "seq_len_range": ([w.len_lo, w.len_hi] if not w.long_frac else
+                             {"short": [w.len_lo, w.len_hi], "long": [w.long_lo, w.long_hi],
+                              "long_frac": w.long_frac}),
+           "partition_size": "auto" if P == pkv.PKV_PARTITION_AUTO else P,
+           "cache_write": ("separate launch" if unfused else
+                           "paged_attention_decode_append: separate launch in the balanced split"
+                           if P == pkv.PKV_PARTITION_AUTO else "fused into the decode launch"),
+           "decode_plan": ("in-kernel ranking" if no_plan or P != 0 else
+                           "host plan once per step (paged_attention_decode_plan)"),
+           "pool_blocks": nb,
+           "pool_gb_per_layer": round(nb * w.block_bytes_per_layer * bs / w.block_size / 1e9, 3),
+           "block_table_bytes": B * max_blocks * 4}
+    kernel_name = (("paged_attention_decode" if unfused or P == pkv.PKV_PARTITION_AUTO
+                    else "paged_attention_decode_append (fused cache write + decode)")
+                   + ("_fp8" if fp8 else "")
+                   + (" (balanced split)" if P == pkv.PKV_PARTITION_AUTO else ""))
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1) if alg else None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4) if alg else None, "traffic": None,
+                "kernel": kernel_name,
+                "alg_bytes_per_launch": int(alg_per_launch) if alg else None}
+    if alg:
+        # against the read of one launch's bytes (8B); a 1.9 GB launch against the 1 GiB read
+        read_rate = ceiling["GB/s"] if primary else ceiling["GB/s_1GiB"]
+        roofline["frac_of_read_ceiling"] = round(achieved / read_rate, 4)
+        if gather:
+            roofline["frac_of_gather_ceiling"] = round(
+                (kv_per_launch / dec_avg_s / 1e9) / gather["GB/s"], 4)
+    if not primary:
+        res = {"workload": cfg["workload"], "config": cfg,
+               "decode_kernel_us": kernel_us["decode"], "reduce_kernel_us": kernel_us["reduce"],
+               "cache_write_kernel_us": kernel_us["cache_write"],
+               "kv_bytes_per_layer": int(kv_per_launch),
+               "attention_kv_gb_s": round(kv_per_launch / attn_s / 1e9, 1),
+               "attention_pct_of_peak": round(100 * kv_per_launch / attn_s / 1e9 / HBM_PEAK_GBS, 2),
+               "step_kv_gb_s": round(value, 1), "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+               "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),
+               "roofline": roofline, "gather_ceiling": gather}
+        del caches, q, k_new, v_new, out, parts
+        pool.close()
+        torch.cuda.empty_cache()
+        return res, ceiling
+
     result = {
         "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + decode tokens/s/layer",
         "value": round(value, 1),
@@ -628,20 +857,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded draws of the workload's shapes and length mix)",
-        "config": {"workload": f"{w.name}-decode", "layers": L, "batch": B, "num_heads": Hq,
-                   "num_kv_heads": Hkv, "head_dim": d, "block_size": bs,
-                   "kv_cache_dtype": ("fp8 e4m3, k_scale %g, v_scale %g" % (w.k_scale, w.v_scale)
-                                      if fp8 else w.dtype),
-                   "seq_len_range": [w.len_lo, w.len_hi],
-                   "partition_size": "auto" if P == pkv.PKV_PARTITION_AUTO else P,
-                   "cache_write": ("separate launch" if args.unfused else
-                                   "paged_attention_decode_append: separate launch in the balanced split"
-                                   if P == pkv.PKV_PARTITION_AUTO else "fused into the decode launch"),
-                   "decode_plan": ("in-kernel ranking" if args.no_plan or P != 0 else
-                                   "host plan once per step (paged_attention_decode_plan)"),
-                   "pool_blocks": nb,
-                   "pool_gb_per_layer": round(nb * w.block_bytes_per_layer * bs / w.block_size / 1e9, 3),
-                   "block_table_bytes": B * max_blocks * 4},
+        "config": cfg,
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_s_per_layer": round(B * L * args.steps / elapsed, 1),
         "step_ms_percentiles": step_pct,
@@ -652,57 +868,174 @@ def main():
                          "averaged over every launch of the timed steps; step percentiles "
                          "from events between the steps of that same instrumented pass",
         "cache_state": f"{L} distinct per-layer pools cycled; warm-up {args.warmup} steps excluded",
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1) if alg else None,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4) if alg else None, "traffic": None,
-                     "kernel": ("paged_attention_decode" if args.unfused
-                                else "paged_attention_decode_append (fused cache write + decode)")
-                               + ("_fp8" if fp8 else ""),
-                     "alg_bytes_per_launch": int(alg_per_launch) if alg else None},
+        "roofline": roofline,
+        "read_ceiling": ceiling,
+        "gather_ceiling": gather,
         "cpu_baseline": None,
     }
-    result["roofline"]["traffic"] = measured_traffic(w.name, P, not args.unfused, bs)
-    ceiling = stream_ceiling()
-    result["stream_ceiling"] = ceiling
-    if alg:
-        result["roofline"]["frac_of_ceiling"] = round(achieved / ceiling["GB/s"], 4)
+    # HBM counters of the same launches: the rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
+    # same command, recorded with the algorithmic bytes of the dispatches they averaged
+    tr = measured_traffic(w.name, P, not unfused, bs, args, int(alg_per_launch) if alg else None)
+    if tr:
+        roofline["traffic"] = tr["bytes_per_launch"]
+        roofline["traffic_record"] = tr["record"]
+    if args.print_launch_bytes:
+        # algorithmic bytes of every decode launch of this run, in launch order (warm-up,
+        # timed, kernel-timing pass): what the traffic summary pairs the counters with
+        result["launch_alg_bytes"] = [alg_bytes(ln) for ln in step_lens for _ in range(L)]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, caches[0], q[0], d_tab, d_len, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    del caches, q, k_new, v_new, out, parts
+    if fp8:
+        result["fp8_accuracy"] = fp8_accuracy(w, dev)
+    pool.close()
+    torch.cuda.empty_cache()
+    return result, ceiling
 
 
-def stream_ceiling():
-    """What this GPU streams in practice, measured beside the roofline's spec peak: a plain
-    device-to-device copy of 1 GiB (read + write bytes) and a read-only pass (fp32 sum of
-    1 GiB), each the median of 10 runs bracketed by events, rotating over buffers so no
-    run finds its input in cache. The decode kernel is read-dominated, so its fraction is
-    taken against the higher of the two."""
+def fp8_accuracy(w, dev):
+    """What the FP8 cache costs in accuracy at several context lengths: one sequence of N(0, 1)
+    K/V (the workload's scales), written to a bf16 cache and to an FP8 cache and decoded from
+    each; the FP8 output's max |difference| from the bf16 output, absolute and over the
+    largest output. The bf16 path itself is within about 4e-6 of the fp64 oracle over these
+    outputs (relative), so the difference is the quantisation's error."""
+    import numpy as np
     import torch
+
+    import paged_kv_cache_28_amd as pkv
+    Hq, Hkv, d = w.num_heads, w.num_kv_heads, w.head_dim
+    tdt = pkv.torch_dtype(w.dtype)
+    rows = []
+    for n in (128, 2048, 32768):
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed + n)
+        k = torch.randn((n, Hkv, d), generator=g, device=dev).to(tdt)
+        v = torch.randn((n, Hkv, d), generator=g, device=dev).to(tdt)
+        q = torch.randn((1, Hq, d), generator=g, device=dev).to(tdt)
+        nb = -(-n // 16)
+        perm = torch.randperm(nb, generator=g, device=dev).to(torch.int32)
+        slots = (perm.repeat_interleave(16)[:n] * 16 +
+                 torch.arange(n, device=dev, dtype=torch.int32) % 16).to(torch.int32)
+        tab, lens = perm[None, :].contiguous(), torch.tensor([n], dtype=torch.int32, device=dev)
+        outs = {}
+        for cache in ("bf16", "fp8"):
+            kc, vc = pkv.alloc_caches(nb, Hkv, d, cache if cache == "fp8" else w.dtype, dev, fill=0)
+            o = torch.empty((1, Hq, d), dtype=torch.float32, device=dev)
+            if cache == "fp8":
+                pkv.reshape_and_cache_fp8(k, v, kc, vc, slots, w.k_scale, w.v_scale)
+                pkv.decode(o, q, kc, vc, tab, lens, w.scale, 0, kv_scales=(w.k_scale, w.v_scale))
+            else:
+                pkv.reshape_and_cache(k, v, kc, vc, slots)
+                pkv.decode(o, q, kc, vc, tab, lens, w.scale, 0)
+            outs[cache] = o.double()
+        err = float((outs["fp8"] - outs["bf16"]).abs().max())
+        top = float(outs["bf16"].abs().max())
+        rows.append({"context": n, "max_abs_err": round(err, 6), "max_abs_out": round(top, 6),
+                     "norm_err": round(err / top, 5)})
+    return {"vs": "the bf16-cache decode of the same K/V", "kv": "N(0, 1)",
+            "k_scale": w.k_scale, "v_scale": w.v_scale, "by_context": rows}
+
+
+def _median_us(pkv, fn, runs: int):
+    """Median kernel time (us) of fn() over `runs` launches under the library timer."""
+    import numpy as np
+    times = []
+    pkv.timer_enable(True)
+    for i in range(runs):
+        fn(i)
+        ms, n = pkv.timer_read(pkv.PKV_TIMER_MEASURE)
+        times.append(ms * 1e3 / max(n, 1))
+    pkv.timer_enable(False)
+    return float(np.median(times))
+
+
+def read_ceiling(dev, launch_bytes: int):
+    """What this GPU streams with no indirection, from the library's contiguous-read kernel
+    with non-temporal loads (as the decode's tile loads): 1 GiB at several launch shapes
+    (the best median of 10 runs), and, at the best shape, a read of exactly one decode
+    launch's bytes (the same ramp-up and tail per launch as the decode pays), beside the
+    same two reads with plain loads. Buffers rotate so that no run finds its input in the
+    256 MB Infinity Cache."""
+    import torch
+
+    import paged_kv_cache_28_amd as pkv
     n = 1 << 30
-    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(4)]
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(2)]
     for t in bufs:
         t.fill_(1)
-
-    def median(fn):
-        times = []
-        for i in range(12):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn(i)
-            b.record()
-            b.synchronize()
-            if i >= 2:
-                times.append(a.elapsed_time(b) / 1e3)
-        return sorted(times)[len(times) // 2]
-
-    t_copy = median(lambda i: bufs[(2 * i + 1) % 4].copy_(bufs[(2 * i) % 4]))
-    t_read = median(lambda i: bufs[i % 4].view(torch.float32).sum())
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    shapes = {}
+    for wpc in (8, 16):
+        for lif in (4, 8, 16):
+            pkv.measure_read(bufs[0], sink, wpc, lif)            # warm
+            us = _median_us(pkv, lambda i: pkv.measure_read(bufs[i % 2], sink, wpc, lif), 10)
+            shapes[f"{wpc}w_{lif}l"] = round(n / (us * 1e-6) / 1e9, 1)
+    best = max(shapes, key=shapes.get)
+    wpc, lif = (int(x[:-1]) for x in best.split("_"))
+    us = _median_us(pkv, lambda i: pkv.measure_read(bufs[i % 2], sink, wpc, lif, False), 10)
+    plain_1g = round(n / (us * 1e-6) / 1e9, 1)
     del bufs
+    m = (launch_bytes + 15) // 16 * 16
+    small = [torch.ones(m, dtype=torch.uint8, device=dev) for _ in range(4)]
+    same = {}
+    for nt in (True, False):
+        us = _median_us(pkv, lambda i: pkv.measure_read(small[i % 4], sink, wpc, lif, nt), 24)
+        same[nt] = (round(us, 2), round(m / (us * 1e-6) / 1e9, 1))
+    del small
     torch.cuda.empty_cache()
-    copy_gbs, read_gbs = 2 * n / t_copy / 1e9, n / t_read / 1e9
-    best = max(copy_gbs, read_gbs)
-    return {"copy_1GiB_GB/s": round(copy_gbs, 1), "read_1GiB_GB/s": round(read_gbs, 1),
-            "GB/s": round(best, 1), "frac_of_peak": round(best / HBM_PEAK_GBS, 4)}
+    return {"GB/s": same[True][1], "frac_of_peak": round(same[True][1] / HBM_PEAK_GBS, 4),
+            "bytes": m, "us": same[True][0], "plain_loads_GB/s": same[False][1],
+            "GB/s_1GiB": shapes[best], "plain_loads_GB/s_1GiB": plain_1g, "best_shape": best,
+            "by_shape_GB/s_1GiB": shapes,
+            "kernel": "pkv_measure_read: contiguous 16-byte non-temporal loads, no arithmetic; "
+                      "GB/s is a read of one decode launch's bytes, GB/s_1GiB a 1 GiB read"}
+
+
+def gather_ceiling(caches, d_tab, d_len, lens, Hkv, P, no_plan, alg_bytes, kv_bytes):
+    """The same K/V tiles a decode launch of the last step reads, gathered through its
+    block tables with no arithmetic (library kernels), cycling over the layers' pools as
+    the decode does: in the single pass's decomposition (one workgroup per (sequence, KV
+    head), the step's host plan) and perfectly balanced (equal runs of tiles per wave).
+    The balanced rate over the read ceiling is the cost of the indirection itself."""
+    import torch
+
+    import paged_kv_cache_28_amd as pkv
+    if lens is None:
+        return None
+    dev = d_tab.device
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    L = len(caches)
+    order = None if no_plan else pkv.paged_attention_decode_plan(lens, Hkv)
+    kvb = kv_bytes(lens)
+    res = {"kv_bytes": kvb, "kernel": "pkv_measure_gather: K and V tiles through the block "
+                                      "tables, two in flight per wave, no arithmetic, "
+                                      "non-temporal loads (and plain ones for comparison)"}
+    bs = int(caches[0][1].shape[3])
+    modes = [("per_seq", False)] + ([("balanced", True)] if bs == 16 else [])
+    for name, bal in modes:
+        for nt, tag in ((True, ""), (False, "_plain_loads")):
+            pkv.measure_gather(*caches[0], d_tab, d_len, sink, order, bal, nt)   # warm
+            us = _median_us(pkv, lambda i: pkv.measure_gather(*caches[i % L], d_tab, d_len, sink,
+                                                              order, bal, nt), 2 * L)
+            res[f"{name}{tag}_us"] = round(us, 2)
+            res[f"{name}{tag}_GB/s"] = round(kvb / (us * 1e-6) / 1e9, 1)
+    best = max(res.get("per_seq_GB/s", 0), res.get("balanced_GB/s", 0))
+    res["GB/s"] = best
+    res["frac_of_peak"] = round(best / HBM_PEAK_GBS, 4)
+    return res
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), so the baseline states where it ran."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(w, cache0, q0, d_tab, d_len, budget_s: float):
@@ -732,7 +1065,8 @@ def cpu_baseline(w, cache0, q0, d_tab, d_len, budget_s: float):
         t += time.perf_counter() - t0
         passes += 1
     return {"value": round(kv_per_pass * passes / t / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "tok_s_per_layer": round(len(lens) * passes / t, 2),
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "tok_s_per_layer": round(len(lens) * passes / t, 2),
             "seconds": round(t, 2),
             "sample": f"layer 0 of the step, all {len(lens)} sequences "
                       f"({int(lens.sum())} context tokens), decoded {passes}x by the fp64 "

@@ -99,9 +99,39 @@ const char* pkv_version(void);
 #define PKV_TIMER_CACHE_WRITE 2
 #define PKV_TIMER_COPY_BLOCKS 3
 #define PKV_TIMER_PREFILL 4
-#define PKV_TIMER_ENTRIES 5
+#define PKV_TIMER_MEASURE 5
+#define PKV_TIMER_ENTRIES 6
 int pkv_timer_enable(int32_t enable);
 int pkv_timer_read(int32_t entry, double* total_ms, int64_t* launches);
+
+/* ---- streaming ceilings -----------------------------------------------------------
+ * Not part of the method: measuring aids, timed under PKV_TIMER_MEASURE. They read and
+ * fold their input into a running XOR (stored to sink[i % sink_len], a device uint32
+ * buffer; nothing else is written), so the decode kernels' rates can be set against what
+ * the same GPU streams with no arithmetic, and the gather against the contiguous read is
+ * the cost of reading through a block table ("vLLM ve Triton ile maliyet optimizasyonu",
+ * §05 Sınırlar, on the indirection cost of paged reads).
+ * pkv_measure_read: bytes (a multiple of 16) of buf, 16-byte aligned, read once in order by
+ *   device CUs x waves_per_cu (4 .. 32, a multiple of 4) waves, each with loads_in_flight
+ *   (2, 4, 8 or 16) 16-byte loads per lane in flight.
+ * pkv_measure_gather: the K and V tiles that paged_attention_decode reads for the batch
+ *   (every (block, KV head) tile of every sequence's first ceil(n / block_size) table
+ *   entries; head_dim * block_size * element bytes of 1, 2, 4 or 8 KiB). balanced == 0:
+ *   the single pass's decomposition, one workgroup of 4 waves per (KV head, sequence) in
+ *   its grid order (seq_order as for paged_attention_decode, or NULL), the waves taking
+ *   blocks round-robin two in flight. balanced != 0 (16-token blocks): all tiles of the
+ *   batch in one list cut into equal runs, one per wave, 8 waves per CU.
+ * nontemporal != 0: the loads carry the non-temporal hint, as the decode kernels' tile loads
+ *   do (the caches do not keep the lines); 0: plain loads.
+ * Errors: EINVAL, ENOTSUP (sizes not built), EHIP. */
+int pkv_measure_read(const void* buf, int64_t bytes, int32_t waves_per_cu, int32_t loads_in_flight,
+                     int32_t nontemporal, uint32_t* sink, int32_t sink_len, void* stream);
+int pkv_measure_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t cache_dtype,
+                       int32_t max_blocks_per_seq, int64_t num_blocks, const int32_t* seq_order,
+                       int32_t balanced, int32_t nontemporal, uint32_t* sink, int32_t sink_len,
+                       void* stream);
 
 /* ---- KV bytes per token ------------------------------------------------------------
  * 2 (K and V) x layers x KV heads x head_dim x bytes per element
@@ -151,7 +181,9 @@ int64_t kv_pool_bytes_per_token(const kv_pool* pool);
 /* Shapes (in elements) of one layer's K and V cache in the layout above. */
 int kv_pool_cache_shape(const kv_pool* pool, int64_t k_shape[5], int64_t v_shape[4]);
 
-/* Register a new, empty sequence. EINVAL if seq_id is already live. */
+/* Register a new, empty sequence: a request entering the engine, before the scheduling
+ * step allocates its slots ("vLLM Nedir? ...", section "Bir istek motorun içinde", steps 1
+ * and 2). EINVAL if seq_id is already live. */
 int kv_pool_add_seq(kv_pool* pool, int64_t seq_id);
 
 /* Make empty sequence seq_id start with the first n_tokens tokens of src_seq_id by
@@ -253,14 +285,19 @@ int kv_pool_free_queue(const kv_pool* pool, int32_t* blocks_out, int64_t capacit
 /* Reference count of block blk (0 for a free block). Errors: EINVAL. */
 int kv_pool_refcount(const kv_pool* pool, int64_t blk, int32_t* ref_out);
 
-/* Dense block tables for the n sequences in seq_ids: tables_out is int32
- * [n][max_blocks], row i holding seq_ids[i]'s physical blocks then -1 padding;
- * seq_lens_out[i] is its length. Host memory (pinned or not).
+/* Dense block tables for the n sequences in seq_ids: the per-request table that maps
+ * logical blocks to physical ones and that the attention kernel follows ("vLLM ve Triton
+ * ...", §03 Yöntem, step 2). tables_out is int32 [n][max_blocks], row i holding
+ * seq_ids[i]'s physical blocks then -1 padding; seq_lens_out[i] is its length. Host memory
+ * (pinned or not).
  * Errors: ENOENT, EINVAL (a table longer than max_blocks, nulls). */
 int kv_pool_build_tables(const kv_pool* pool, const int64_t* seq_ids, int32_t n,
                          int32_t max_blocks, int32_t* tables_out, int32_t* seq_lens_out);
 
-/* Counters of the pool. */
+/* Counters of the pool: every block is either free or used, so free + used = total
+ * (equal-sized blocks leave no external fragmentation, "vLLM ve Triton ...", §03 Yöntem,
+ * step 3); alloc_failures counts the refused allocations after which the scheduler drops
+ * a request ("vLLM Nedir? ...", section "Bir istek motorun içinde", step 2). */
 int kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
 
 /* ==== device kernels ========================================================== */
@@ -354,7 +391,11 @@ int paged_attention_decode(void* out, float* part_out, float* part_max, float* p
                            int32_t out_dtype, const int32_t* seq_order, void* stream);
 
 /* paged_attention_decode_plan: the host half of a decode step's scheduling, computed once
- * per step and passed to every layer's decode call as seq_order. From a host copy of the
+ * per step and passed to every layer's decode call as seq_order. Decode rereads each
+ * sequence's whole context every step and is bound by memory bandwidth ("Yerel LLM
+ * sistemlerinde backpressure ve ölçekleme", section "4. Prefill ve decode"), and a batch
+ * mixes very different context lengths (same page, section "Her istek eşit değildir"), so
+ * the work is dealt so that every compute unit streams about as many bytes. From a host copy of the
  * batch's lengths (negative counts as 0): rank the sequences by length, longest first
  * (ties by index), and deal them in serpentine rounds of R = max(1, CUs / num_kv_heads)
  * sequences, CUs of the current HIP device: slot b of round r = b / R, position
@@ -400,7 +441,11 @@ int paged_attention_decode_append(void* out, float* part_out, float* part_max, f
                                   int32_t max_partitions, int32_t in_dtype, int32_t out_dtype,
                                   const int32_t* seq_order, void* stream);
 
-/* paged_attention_reduce: for every (b, h) whose sequence has more than one
+/* paged_attention_reduce: the merge that makes a context split into partitions give the
+ * same softmax-weighted sum as one pass over it (the attention math is unchanged by where
+ * K and V are read from, "vLLM ve Triton ...", §03 Yöntem, closing paragraphs; long
+ * contexts beside short ones, "Yerel LLM ...", section "Her istek eşit değildir", are split
+ * so that one sequence does not serialise on one workgroup). For every (b, h) whose sequence has more than one
  * partition (np = ceil(seq_lens[b] / partition_size) > 1; with PKV_PARTITION_AUTO, np
  * is the number of pieces of the balanced split, and rows of empty sequences are
  * written as zeros):

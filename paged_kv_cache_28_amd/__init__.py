@@ -106,11 +106,18 @@ def lib():
         "paged_attention_decode_noalloc": ([P, P, I64, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                             I64, F, I32, I32, I32, P], ctypes.c_int),
         "paged_attention_decode_noalloc_workspace": ([], ctypes.c_size_t),
+        "pkv_measure_read": ([P, I64, I32, I32, I32, P, I32, P], ctypes.c_int),
+        "pkv_measure_gather": ([P, P, P, P, I32, I32, I32, I32, I32, I32, I64, P, I32, I32, P, I32,
+                                P], ctypes.c_int),
         "pkv_timer_enable": ([I32], ctypes.c_int),
         "pkv_timer_read": ([I32, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
-        fn = getattr(L, name)
+        # A host-only build of the pool (PKV_LIBRARY, e.g. the sanitised one the CPU tests
+        # build) has no kernel entry points: those stay unbound and fail when called.
+        fn = getattr(L, name, None)
+        if fn is None:
+            continue
         fn.argtypes = args
         fn.restype = res
     _lib = L
@@ -128,7 +135,7 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "kv_pool_add_seq_prefix", "kv_pool_fork", "kv_pool_append_tokens",
             "kv_pool_append_batch_tokens", "copy_blocks", "paged_attention_prefill",
             "paged_attention_decode_plan", "paged_attention_decode_noalloc",
-            "paged_attention_decode_noalloc_workspace")
+            "paged_attention_decode_noalloc_workspace", "pkv_measure_read", "pkv_measure_gather")
 
 
 def _check(rc: int):
@@ -749,6 +756,44 @@ def paged_attention_reduce(out, part_out, part_max, part_sum, seq_lens, partitio
 # ------------------------------------------------------------------ kernel timer
 PKV_TIMER_DECODE, PKV_TIMER_REDUCE, PKV_TIMER_CACHE_WRITE, PKV_TIMER_COPY_BLOCKS = 0, 1, 2, 3
 PKV_TIMER_PREFILL = 4
+PKV_TIMER_MEASURE = 5
+
+
+def measure_read(buf, sink, waves_per_cu: int = 8, loads_in_flight: int = 8,
+                 nontemporal: bool = True, stream=None):
+    """Streaming ceiling (a measuring aid): read every byte of the device tensor buf once,
+    contiguously, with no arithmetic (timed under PKV_TIMER_MEASURE)."""
+    _index(sink, "sink")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    _check(lib().pkv_measure_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                  waves_per_cu, loads_in_flight, 1 if nontemporal else 0,
+                                  _dev(sink, "sink"), sink.numel(),
+                                  _stream(buf, stream)))
+
+
+def measure_gather(k_cache, v_cache, block_tables, seq_lens, sink, seq_order=None,
+                   balanced: bool = False, nontemporal: bool = True, stream=None):
+    """Gather ceiling (a measuring aid): read the K/V tiles a decode of this batch reads,
+    through the block tables, with no arithmetic (timed under PKV_TIMER_MEASURE)."""
+    torch = _torch()
+    nb, hkv, d, bs = _caches(k_cache, v_cache, k_cache.dtype)
+    B = seq_lens.numel()
+    _index(seq_lens, "seq_lens", shape=(B,))
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B][max_blocks]")
+    _index(block_tables, "block_tables")
+    _index(sink, "sink")
+    _same_device(k_cache, [(v_cache, "v_cache"), (block_tables, "block_tables"),
+                           (seq_lens, "seq_lens"), (sink, "sink")])
+    op, _keep = _order(seq_order, B)
+    code = PKV_FP8_E4M3 if k_cache.dtype == torch.uint8 else dtype_code(k_cache.dtype)
+    _check(lib().pkv_measure_gather(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                    _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
+                                    B, hkv, d, bs, code, block_tables.shape[1], nb, op,
+                                    1 if balanced else 0, 1 if nontemporal else 0,
+                                    _dev(sink, "sink"), sink.numel(),
+                                    _stream(k_cache, stream)))
 
 
 def timer_enable(on: bool = True):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["pool.cpp", "timer.cpp", "cache_write.hip", "decode.hip", "decode_bs8.hip", "decode_bs32.hip",
-           "reduce.hip", "copy_blocks.hip", "prefill.hip"]
+           "reduce.hip", "copy_blocks.hip", "prefill.hip", "measure.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 

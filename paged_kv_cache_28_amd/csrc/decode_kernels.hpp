@@ -60,6 +60,12 @@ namespace pkv {
 
 constexpr int kLptMaxSeqs = 256;
 
+// K/V tiles in flight per wave in the single-pass / partitioned kernel (1, 2 or 3).
+#ifndef PKV_DECODE_BUFFERS
+#define PKV_DECODE_BUFFERS 2
+#endif
+constexpr int kDecodeBuffers = PKV_DECODE_BUFFERS;
+
 struct DecodeArgs {
     void* out;
     float* part_out;
@@ -474,12 +480,14 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
-    // Segments of up to 64 blocks (one block id per lane). Inside a segment two stages of
-    // S tiles are in flight: the next stage's loads are always issued (past the end they
-    // re-read the final block, which is then in cache) before the current stage is used,
-    // so the wait for the current tile never waits for the next. S = 1 also for the
-    // half-size FP8 tiles: stages of two measured slower.
-    constexpr int S = 1;
+    // Segments of up to 64 blocks (one block id per lane). Inside a segment a wave keeps NB
+    // tiles in flight: the loads of tile k + NB - 1 are issued before tile k is used, so
+    // NB - 1 loads stay outstanding while a tile is computed and the wait for the current
+    // tile never waits for a later one. Past the end of the segment the loads repeat its
+    // last tile (no data-dependent branch around them). Tiles of one stage each, also for
+    // the half-size FP8 tiles (stages of two measured slower).
+    constexpr int NB = kDecodeBuffers;
+    static_assert(NB >= 1 && NB <= 3, "one to three tiles in flight");
     for (int k0 = 0; k0 < nmine; k0 += 64) {
         const int cnt = min(64, nmine - k0);
         if (k0 == 0) {
@@ -500,30 +508,40 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                 lim = subst ? n - 1 : n;
             }
         }
-        KvTile<D, F8> X[S], Y[S];
-        int okX[S], okY[S];
+        KvTile<D, F8> X, Y, Z;
+        int okX = 0, okY = 0, okZ = 0;
         auto tile_of = [&](int k) { return first + (k0 + k) * W; };
-#pragma unroll
-        for (int i = 0; i < S; ++i) okX[i] = load(X[i], min(i, cnt - 1), tile_of(min(i, cnt - 1)));
+        auto ld = [&](KvTile<D, F8>& t, int k) {
+            const int kk = min(k, cnt - 1);
+            return load(t, kk, tile_of(kk));
+        };
+        okX = ld(X, 0);
+        if constexpr (NB == 3) okY = ld(Y, 1);
         if (k0 == 0) store_new_row();
-        for (int k = 0; k < cnt; k += 2 * S) {
-#pragma unroll
-            for (int i = 0; i < S; ++i) {
-                const int kk = min(k + S + i, cnt - 1);
-                okY[i] = load(Y[i], kk, tile_of(kk));
+        if constexpr (NB == 1) {
+            for (int k = 0; k < cnt; ++k) {
+                if (k > 0) okX = ld(X, k);
+                compute(X, tile_of(k), okX);
             }
-#pragma unroll
-            for (int i = 0; i < S; ++i)
-                if (k + i < cnt) compute(X[i], tile_of(k + i), okX[i]);
-            if (k + S >= cnt) break;
-#pragma unroll
-            for (int i = 0; i < S; ++i) {
-                const int kk = min(k + 2 * S + i, cnt - 1);
-                okX[i] = load(X[i], kk, tile_of(kk));
+        } else if constexpr (NB == 2) {
+            for (int k = 0; k < cnt; k += 2) {
+                okY = ld(Y, k + 1);
+                compute(X, tile_of(k), okX);
+                if (k + 1 >= cnt) break;
+                okX = ld(X, k + 2);
+                compute(Y, tile_of(k + 1), okY);
             }
-#pragma unroll
-            for (int i = 0; i < S; ++i)
-                if (k + S + i < cnt) compute(Y[i], tile_of(k + S + i), okY[i]);
+        } else {
+            for (int k = 0; k < cnt; k += 3) {
+                okZ = ld(Z, k + 2);
+                compute(X, tile_of(k), okX);
+                if (k + 1 >= cnt) break;
+                okX = ld(X, k + 3);
+                compute(Y, tile_of(k + 1), okY);
+                if (k + 2 >= cnt) break;
+                okY = ld(Y, k + 4);
+                compute(Z, tile_of(k + 2), okZ);
+            }
         }
     }
 
@@ -702,12 +720,11 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
         const char* vt = vbase + (pa * a.num_kv_heads + g) * tile_bytes;
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
-            t.ka[i] = *reinterpret_cast<const uint4*>(kt + ((4 * i + quad) * BS + ra) * 16);
-            t.kb[i] = *reinterpret_cast<const uint4*>(kt + ((4 * i + quad) * BS + rb) * 16);
+            t.ka[i] = ld_once16(kt + ((4 * i + quad) * BS + ra) * 16);
+            t.kb[i] = ld_once16(kt + ((4 * i + quad) * BS + rb) * 16);
         }
 #pragma unroll
-        for (int c = 0; c < NPV; ++c)
-            t.v[c] = *reinterpret_cast<const uint2*>(vt + (16 * c + col) * BS + 8 * quad);
+        for (int c = 0; c < NPV; ++c) t.v[c] = ld_once8(vt + (16 * c + col) * BS + 8 * quad);
         return ok;
     };
     auto kop = [](const uint4& w, int c) {   // 8 codes of QK step c, widened

@@ -42,20 +42,18 @@ __device__ __forceinline__ void load_tile(KvTile<D, false>& t, const char* kt, c
                                           int lane) {
     const int col = lane & 15, quad = lane >> 4;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kt + (64 * c + lane) * 16);
+    for (int c = 0; c < D / 32; ++c) t.k[c] = ld_once16(kt + (64 * c + lane) * 16);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-        t.v[c] = *reinterpret_cast<const uint2*>(vt + ((16 * c + col) * 16 + 4 * quad) * 2);
+    for (int c = 0; c < D / 16; ++c) t.v[c] = ld_once8(vt + ((16 * c + col) * 16 + 4 * quad) * 2);
 }
 template <int D>
 __device__ __forceinline__ void load_tile(KvTile<D, true>& t, const char* kt, const char* vt,
                                           int lane) {
     const int col = lane & 15, quad = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) t.k[i] = *reinterpret_cast<const uint4*>(kt + (64 * i + lane) * 16);
+    for (int i = 0; i < D / 64; ++i) t.k[i] = ld_once16(kt + (64 * i + lane) * 16);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-        t.v[c] = *reinterpret_cast<const uint32_t*>(vt + (16 * c + col) * 16 + 4 * quad);
+    for (int c = 0; c < D / 16; ++c) t.v[c] = ld_once4(vt + (16 * c + col) * 16 + 4 * quad);
 }
 
 // Blocks of BS tokens (8, 16 or 32) hold 16-token tiles as follows: BS = 16, a tile is a
@@ -82,11 +80,9 @@ __device__ __forceinline__ void load_tile_bs(KvTile<D, false>& t, const char* ka
             vrow = 4 * (quad & 1);
         }
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-            t.k[c] = *reinterpret_cast<const uint4*>(kt + ((4 * c + quad) * BS + krow) * 16);
+        for (int c = 0; c < D / 32; ++c) t.k[c] = ld_once16(kt + ((4 * c + quad) * BS + krow) * 16);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-            t.v[c] = *reinterpret_cast<const uint2*>(vt + ((16 * c + col) * BS + vrow) * 2);
+        for (int c = 0; c < D / 16; ++c) t.v[c] = ld_once8(vt + ((16 * c + col) * BS + vrow) * 2);
     }
 }
 template <int D, int BS>
@@ -108,11 +104,9 @@ __device__ __forceinline__ void load_tile_bs(KvTile<D, true>& t, const char* ka,
             vrow = 4 * (quad & 1);
         }
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i)
-            t.k[i] = *reinterpret_cast<const uint4*>(kt + ((4 * i + quad) * BS + krow) * 16);
+        for (int i = 0; i < D / 64; ++i) t.k[i] = ld_once16(kt + ((4 * i + quad) * BS + krow) * 16);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-            t.v[c] = *reinterpret_cast<const uint32_t*>(vt + (16 * c + col) * BS + vrow);
+        for (int c = 0; c < D / 16; ++c) t.v[c] = ld_once4(vt + (16 * c + col) * BS + vrow);
     }
 }
 
