@@ -5,6 +5,7 @@ compared by the tests."""
 from __future__ import annotations
 
 import dataclasses
+import weakref
 
 import numpy as np
 import torch
@@ -24,6 +25,61 @@ class GpuBatch:
     q: torch.Tensor
     tables_d: torch.Tensor
     lens_d: torch.Tensor
+
+
+# ------------------------------------------------------------------ guard bands
+# Output, partial and cache buffers are views into allocations with a guard band of 0xA5
+# bytes after them; check_guards() asserts after a call that no kernel wrote past the end
+# of what it was given. Buffers are tracked by weak reference, so a buffer the test has
+# dropped is neither kept alive nor checked.
+GUARD_BYTES = 16384
+_GUARDED = []
+
+
+def _guarded_view(shape, dtype, device, extra_bytes=GUARD_BYTES):
+    esize = torch.empty(0, dtype=dtype).element_size()
+    nbytes = int(np.prod(shape)) * esize
+    raw = torch.empty(nbytes + extra_bytes, dtype=torch.uint8, device=device)
+    raw[nbytes:].fill_(0xA5)
+    view = raw[:nbytes].view(dtype).view(*shape)
+    _GUARDED.append((weakref.ref(view), nbytes))
+    return view
+
+
+def guarded_full(shape, fill, dtype, device):
+    """A tensor of `shape` filled with `fill`, followed in memory by a guard band."""
+    t = _guarded_view(shape, dtype, device)
+    t.fill_(fill)
+    return t
+
+
+def check_guards():
+    """Every guard band behind a live guarded buffer is intact."""
+    torch.cuda.synchronize()
+    try:
+        for ref, nbytes in _GUARDED:
+            v = ref()
+            if v is None:
+                continue
+            full = torch.empty(0, dtype=torch.uint8, device=v.device).set_(v.untyped_storage())
+            assert bool((full[nbytes:] == 0xA5).all()), \
+                f"a kernel wrote past the end of a {v.dtype} buffer of shape {tuple(v.shape)}"
+    finally:
+        _GUARDED[:] = [(r, n) for r, n in _GUARDED if r() is not None]
+
+
+def guarded_caches(num_blocks, hkv, d, dtype, device, fill, block_size):
+    """One layer's caches, each followed by a guard band one block long."""
+    ks, vs = pkv.cache_shapes(num_blocks, hkv, d, dtype, block_size)
+    td = pkv.torch_dtype(dtype)
+    out = []
+    for shape in (ks, vs):
+        block = int(np.prod(shape[1:])) * torch.empty(0, dtype=td).element_size()
+        t = _guarded_view(shape, td, device, extra_bytes=block)
+        if fill is not None:
+            t.fill_(fill)
+        out.append(t)
+    return tuple(out)
 
 
 def write(w, key, value, kc, vc, slots):
@@ -58,8 +114,8 @@ def build(ob, device="cuda", fill=float("nan"), write_new: bool = True) -> GpuBa
 
     if w.cache_dtype == "fp8" and fill is not None and fill != fill:
         fill = 0x7F
-    kc, vc = pkv.alloc_caches(ob.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, device,
-                              fill=fill, block_size=w.block_size)
+    kc, vc = guarded_caches(ob.num_blocks, w.num_kv_heads, w.head_dim, w.cache_dtype, device,
+                            fill, w.block_size)
     if len(prompt_slots):
         write(w, ob.prompt_k.to(device), ob.prompt_v.to(device), kc, vc,
               torch.from_numpy(prompt_slots).to(device))
@@ -74,12 +130,20 @@ def run_decode(gb: GpuBatch, w, partition_size=0, out_dtype=torch.float32, max_p
     partitioned, the partial buffers."""
     B, Hq, d = gb.q.shape
     dev = gb.q.device
-    out = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=dev)
+    out = guarded_full((B, Hq, d), float("nan"), out_dtype, dev)
     parts = None
     if partition_size != 0:
         maxp = max_partitions or pkv.max_partitions_for(gb.tables.shape[1], partition_size,
                                                         w.block_size)
-        parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, dev))
+        parts = guarded_partials(B, Hq, d, maxp, dev)
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale,
                partition_size, parts, kv_scales=kv_scales(w))
+    check_guards()
     return out, parts
+
+
+def guarded_partials(B, Hq, d, maxp, device):
+    """NaN-filled partial buffers (part_out, part_max, part_sum), each guarded."""
+    return (guarded_full((B, Hq, maxp, d), float("nan"), torch.float32, device),
+            guarded_full((B, Hq, maxp), float("nan"), torch.float32, device),
+            guarded_full((B, Hq, maxp), float("nan"), torch.float32, device))

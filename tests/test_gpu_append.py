@@ -47,15 +47,15 @@ def _same_output(a, b):
 def _run(gb, w, P, out_dtype, append, plan=False):
     B, Hq, d = gb.q.shape
     dev = gb.q.device
-    out = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=dev)
+    out = gpu_batch.guarded_full((B, Hq, d), float("nan"), out_dtype, dev)
     parts = None
     if P != 0:
         maxp = pkv.max_partitions_for(gb.tables.shape[1], P)
-        parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, dev))
+        parts = gpu_batch.guarded_partials(B, Hq, d, maxp, dev)
     order = pkv.paged_attention_decode_plan(gb.lens, w.num_kv_heads) if plan else None
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale, P, parts,
                append=append, seq_order=order)
-    torch.cuda.synchronize()
+    gpu_batch.check_guards()   # outputs, partials and both caches: nothing written past them
     return out
 
 

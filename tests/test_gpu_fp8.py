@@ -228,14 +228,14 @@ def test_fp8_decode_of_every_finite_code(P, device):
 def _run(gb, w, P, out_dtype, append):
     B, Hq, d = gb.q.shape
     dev = gb.q.device
-    out = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=dev)
+    out = gpu_batch.guarded_full((B, Hq, d), float("nan"), out_dtype, dev)
     parts = None
     if P != 0:
-        parts = tuple(t.fill_(float("nan")) for t in
-                      pkv.alloc_partials(B, Hq, d, pkv.max_partitions_for(gb.tables.shape[1], P), dev))
+        parts = gpu_batch.guarded_partials(B, Hq, d, pkv.max_partitions_for(gb.tables.shape[1], P),
+                                           dev)
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale, P, parts,
                append=append, kv_scales=(w.k_scale, w.v_scale))
-    torch.cuda.synchronize()
+    gpu_batch.check_guards()
     return out
 
 

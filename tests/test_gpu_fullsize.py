@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 import torch
 
+import gpu_batch
 import oracle
 import paged_kv_cache_28_amd as pkv
 import workloads
@@ -69,9 +70,8 @@ class Layer:
         self.nv = workloads.draw_tokens_device(B, w, (2, layer, 3), device)
         self.q = workloads.draw_q_device(w, (3, layer), device)
         self.fp8 = w.cache_dtype == "fp8"
-        self.kc, self.vc = pkv.alloc_caches(nb, Hkv, d, w.cache_dtype, device,
-                                            fill=0x7F if self.fp8 else float("nan"),
-                                            block_size=bs)
+        self.kc, self.vc = gpu_batch.guarded_caches(nb, Hkv, d, w.cache_dtype, device,
+                                                    0x7F if self.fp8 else float("nan"), bs)
         for k, v, sl in ((self.pk, self.pv, self.prompt_slots), (self.nk, self.nv, self.new_slots)):
             sl = torch.from_numpy(sl).to(device)
             if self.fp8:
@@ -86,16 +86,16 @@ class Layer:
     def decode(self, P, plan=False):
         w, dev = self.w, self.device
         B = len(self.lens)
-        out = torch.full((B, w.num_heads, w.head_dim), float("nan"), dtype=torch.float32,
-                         device=dev)
+        out = gpu_batch.guarded_full((B, w.num_heads, w.head_dim), float("nan"), torch.float32,
+                                     dev)
         parts = None
         if P != 0:
             maxp = pkv.max_partitions_for(self.max_blocks, P, self.bs)
-            parts = pkv.alloc_partials(B, w.num_heads, w.head_dim, maxp, dev)
+            parts = gpu_batch.guarded_partials(B, w.num_heads, w.head_dim, maxp, dev)
         order = pkv.paged_attention_decode_plan(self.lens, w.num_kv_heads) if plan else None
         pkv.decode(out, self.q, self.kc, self.vc, self.tables_d, self.lens_d, w.scale, P, parts,
                    kv_scales=(w.k_scale, w.v_scale) if self.fp8 else None, seq_order=order)
-        torch.cuda.synchronize()
+        gpu_batch.check_guards()
         return out
 
     def logical_kv(self, b, g):

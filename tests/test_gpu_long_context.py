@@ -64,15 +64,15 @@ def _oracle_decode(ob, w):
 def _decode(gb, w, P, append=None, plan=False):
     B, Hq, d = gb.q.shape
     dev = gb.q.device
-    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=dev)
+    out = gpu_batch.guarded_full((B, Hq, d), float("nan"), torch.float32, dev)
     parts = None
     if P != 0:
         maxp = pkv.max_partitions_for(gb.tables.shape[1], P, w.block_size)
-        parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, dev))
+        parts = gpu_batch.guarded_partials(B, Hq, d, maxp, dev)
     order = pkv.paged_attention_decode_plan(gb.lens, w.num_kv_heads) if plan else None
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale, P, parts,
                append=append, kv_scales=gpu_batch.kv_scales(w), seq_order=order)
-    torch.cuda.synchronize()
+    gpu_batch.check_guards()   # outputs, partials and both caches: nothing written past them
     return out
 
 
@@ -163,10 +163,10 @@ def test_long_prefill_matches_oracle(n, L, device):
     gb = gpu_batch.build(ob, device)
     q = workloads.draw_q(w, workloads.rng(w.seed, 62, n), batch=L)
     qs = np.array([0, L], np.int32)
-    out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32, device=device)
+    out = gpu_batch.guarded_full(tuple(q.shape), float("nan"), torch.float32, device)
     pkv.paged_attention_prefill(out, q.to(device), torch.from_numpy(qs).to(device), gb.k_cache,
                                 gb.v_cache, gb.tables_d, gb.lens_d, w.scale, L)
-    torch.cuda.synchronize()
+    gpu_batch.check_guards()
     got = out.cpu().double().numpy()
     assert np.all(np.isfinite(got)), "non-finite output"
     if L * w.num_heads <= 2048:   # every row

@@ -60,16 +60,16 @@ def test_noalloc_equals_caller_buffers(P, out_dtype, device):
         gb = gpu_batch.build(ob, device)
         B, Hq, d = gb.q.shape
         print(f"noalloc P={P} call {i}: B={B} max_len={max(lens)}", flush=True)
-        got = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=device)
+        got = gpu_batch.guarded_full((B, Hq, d), float("nan"), out_dtype, device)
         assert _noalloc(gb, w, P, got) == pkv.PKV_OK, pkv.lib().pkv_last_error()
         # the existing entry points with torch-allocated partials of the same count (the
         # natural bound fits the workspace at these sizes)
-        ref_out = torch.full((B, Hq, d), float("nan"), dtype=out_dtype, device=device)
+        ref_out = gpu_batch.guarded_full((B, Hq, d), float("nan"), out_dtype, device)
         maxp = pkv.max_partitions_for(gb.tables.shape[1], P)
-        parts = tuple(t.fill_(float("nan")) for t in pkv.alloc_partials(B, Hq, d, maxp, device))
+        parts = gpu_batch.guarded_partials(B, Hq, d, maxp, device)
         pkv.decode(ref_out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale, P,
                    parts)
-        torch.cuda.synchronize()
+        gpu_batch.check_guards()
         assert torch.equal(got.view(torch.uint8), ref_out.view(torch.uint8)), \
             (got.double() - ref_out.double()).abs().max().item()
         if out_dtype == torch.float32:
