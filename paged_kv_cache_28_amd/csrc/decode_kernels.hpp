@@ -277,7 +277,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     float* sm_l = lds + W * 16;         // [W][16]
     float* sm_o = lds + 2 * W * 16;     // [W][G][D]
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
     int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
     const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
@@ -288,8 +288,22 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int G = a.group;
     const int col = lane & 15, quad = lane >> 4;
 
+    // The block ids of this wave's first 64 tiles and the length are read first: memory
+    // waits complete in issue order, so loads issued ahead of them (queries, new rows)
+    // would hold up the first tile. The context is walked in 16-token tiles (tile j:
+    // positions 16j .. 16j + 15), which are blocks for BS = 16, halves of blocks for
+    // BS = 32 and pairs of blocks for BS = 8 (tile_ids, load_tile_bs). This wave takes
+    // tiles first, first + W, ... of its partition; the table row has max_blocks entries,
+    // so the ids are read before the length is known.
+    const int blk_begin = p * a.part_tiles;
+    const int first = blk_begin + wave;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    int tab0, tab0b;
+    tile_ids<BS>(table, a.max_blocks, first + lane * W, tab0, tab0b);
+    const int n_raw = a.seq_lens[b];
+    __builtin_amdgcn_sched_barrier(0);
+
     // Q^T operand (B of the first product): head l%16 of the group, 8 dims per step.
-    // Issued first so its latency overlaps the sequence-length read.
     uint4 qf[NQK];
     {
         const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(b) * a.q_stride +
@@ -333,19 +347,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                                        nkr, nvr, nk, nv);
     };
 
-    // The context is walked in 16-token tiles (tile j: positions 16j .. 16j + 15), which
-    // are blocks for BS = 16, halves of blocks for BS = 32 and pairs of blocks for BS = 8
-    // (tile_ids, load_tile_bs). This wave takes tiles first, first + W, ... of its
-    // partition. The block ids of its first 64 are read before the length is known (the
-    // table row has max_blocks entries): the id load does not wait for the length load.
-    const int blk_begin = p * a.part_tiles;
-    const int first = blk_begin + wave;
-    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
-    int tab0, tab0b;
-    tile_ids<BS>(table, a.max_blocks, first + lane * W, tab0, tab0b);
-
-    int n = a.seq_lens[b];
-    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    int n = n_raw < 0 ? 0 : (n_raw > a.max_len ? a.max_len : n_raw);
     const int nblk = (n + 15) >> 4;
     const int jl = n > 0 ? (n - 1) >> 4 : -1;     // tile of the newest token
     if (blk_begin >= nblk) {
@@ -420,16 +422,17 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     // set if the id of its (first) block is valid, bit 1 if that of its second block is
     // (BS = 8; always set otherwise). An invalid id breaks the precondition: a safe
     // address is read instead; the tile is skipped (bit 0) or its rows 8-15 masked (bit 1).
+    const uint32_t nb_lim = block_limit(a.num_blocks);
     auto load = [&](KvTile<D, F8>& t, int k, int j) -> int {
-        int64_t pa = __builtin_amdgcn_readlane(tab, k);
-        const bool oka = pa >= 0 && pa < a.num_blocks;
-        pa = oka ? pa : 0;
+        const int ida = __builtin_amdgcn_readlane(tab, k);
+        const bool oka = uint32_t(ida) < nb_lim;
+        const int64_t pa = oka ? ida : 0;
         int64_t pb = pa;
         bool okb = true;
         if constexpr (BS == 8) {
-            pb = __builtin_amdgcn_readlane(tabb, k);
-            okb = pb >= 0 && pb < a.num_blocks;
-            pb = okb ? pb : 0;
+            const int idb = __builtin_amdgcn_readlane(tabb, k);
+            okb = uint32_t(idb) < nb_lim;
+            pb = okb ? idb : 0;
         }
         const int64_t ta = pa * a.num_kv_heads + g, tb = pb * a.num_kv_heads + g;
         load_tile_bs<D, BS>(t, kbase + ta * tile_bytes, vbase + ta * tile_bytes,
@@ -437,9 +440,13 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         return int(oka) | (int(okb) << 1);
     };
 
+    // A tile whose block id broke the precondition (ok bit 0 clear) was read from block 0
+    // and is masked out entirely by arithmetic, not skipped by a branch: every loaded
+    // register is then consumed on every path, so the compiler's memory waits stay per
+    // tile (a path that skips a tile's registers makes it drain all outstanding loads at
+    // the loop head). An invalid second block (BS = 8) masks rows 8-15.
     auto compute = [&](KvTile<D, F8>& t, int j, int ok) {
-        if (!(ok & 1)) return;
-        const int lim_t = (ok & 2) ? lim : min(lim, j * 16 + 8);   // rows below it are valid
+        const int lim_t = !(ok & 1) ? j * 16 : (ok & 2) ? lim : min(lim, j * 16 + 8);
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NQK; ++c) s = Mfma<T>::qk(k_operand<T, D>(t, c), qf[c], s);
@@ -511,9 +518,14 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         KvTile<D, F8> X, Y, Z;
         int okX = 0, okY = 0, okZ = 0;
         auto tile_of = [&](int k) { return first + (k0 + k) * W; };
+        // The scheduling barrier keeps each tile's loads issued before the previous tile's
+        // arithmetic: left free, the compiler hoists that arithmetic (and its wait) above
+        // them, so the next tile is requested only after the current one has arrived.
         auto ld = [&](KvTile<D, F8>& t, int k) {
             const int kk = min(k, cnt - 1);
-            return load(t, kk, tile_of(kk));
+            const int ok = load(t, kk, tile_of(kk));
+            __builtin_amdgcn_sched_barrier(0);
+            return ok;
         };
         okX = ld(X, 0);
         if constexpr (NB == 3) okY = ld(Y, 1);
@@ -610,7 +622,7 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
     float* sm_l = lds + W * 16;         // [W][16]
     float* sm_o = lds + 2 * W * 16;     // [W][G][D]
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
     int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
     const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
@@ -621,6 +633,16 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
     const int G = a.group;
     const int col = lane & 15, quad = lane >> 4;
     const int ra = 8 * (col >> 2) + (col & 3), rb = ra + 4;   // this lane's K rows of A, B
+
+    // block ids and length first (see decode_mfma_kernel); this wave takes blocks first,
+    // first + W, ... of its partition
+    const int part_blocks = a.part_tiles >> 1;
+    const int blk_begin = p * part_blocks;
+    const int first = blk_begin + wave;
+    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
+    const int tab0 = first + lane * W < a.max_blocks ? table[first + lane * W] : -1;
+    const int n_raw = a.seq_lens[b];
+    __builtin_amdgcn_sched_barrier(0);
 
     uint4 qf[NQK];
     {
@@ -652,15 +674,7 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
                                        nkr, nvr, nk, nv);
     };
 
-    // whole blocks: this wave takes blocks first, first + W, ... of its partition
-    const int part_blocks = a.part_tiles >> 1;
-    const int blk_begin = p * part_blocks;
-    const int first = blk_begin + wave;
-    const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
-    const int tab0 = first + lane * W < a.max_blocks ? table[first + lane * W] : -1;
-
-    int n = a.seq_lens[b];
-    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    int n = n_raw < 0 ? 0 : (n_raw > a.max_len ? a.max_len : n_raw);
     const int nblk = (n + BS - 1) / BS;
     const int jl = n > 0 ? (n - 1) / BS : -1;    // block of the newest token
     if (blk_begin >= nblk) {
@@ -712,19 +726,20 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
 
     // Issue the loads of segment block k; false if its id is invalid (a safe address is
     // read and the block is skipped).
+    const uint32_t nb_lim = block_limit(a.num_blocks);
     auto load = [&](KvBlock32<D>& t, int k) -> bool {
-        int64_t pa = __builtin_amdgcn_readlane(tab, k);
-        const bool ok = pa >= 0 && pa < a.num_blocks;
-        pa = ok ? pa : 0;
-        const char* kt = kbase + (pa * a.num_kv_heads + g) * tile_bytes;
-        const char* vt = vbase + (pa * a.num_kv_heads + g) * tile_bytes;
+        const int id = __builtin_amdgcn_readlane(tab, k);
+        const bool ok = uint32_t(id) < nb_lim;
+        const int64_t pa = ok ? id : 0;
+        const buf_rsrc_t kr = tile_rsrc(kbase + (pa * a.num_kv_heads + g) * tile_bytes, int(tile_bytes));
+        const buf_rsrc_t vr = tile_rsrc(vbase + (pa * a.num_kv_heads + g) * tile_bytes, int(tile_bytes));
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
-            t.ka[i] = ld_once16(kt + ((4 * i + quad) * BS + ra) * 16);
-            t.kb[i] = ld_once16(kt + ((4 * i + quad) * BS + rb) * 16);
+            t.ka[i] = bld16(kr, ((4 * i + quad) * BS + ra) * 16);
+            t.kb[i] = bld16(kr, ((4 * i + quad) * BS + rb) * 16);
         }
 #pragma unroll
-        for (int c = 0; c < NPV; ++c) t.v[c] = ld_once8(vt + (16 * c + col) * BS + 8 * quad);
+        for (int c = 0; c < NPV; ++c) t.v[c] = bld8(vr, (16 * c + col) * BS + 8 * quad);
         return ok;
     };
     auto kop = [](const uint4& w, int c) {   // 8 codes of QK step c, widened
@@ -732,9 +747,10 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
 
-    // block jb (positions 32 jb .. + 31); positions below lim are valid
+    // block jb (positions 32 jb .. + 31); positions below lim are valid. An invalid block
+    // id (read from block 0) is masked out by arithmetic, not skipped (see decode_mfma_kernel).
     auto compute = [&](KvBlock32<D>& t, int jb, bool ok) {
-        if (!ok) return;
+        const int lim_b = ok ? lim : jb * BS;
         const int p0 = jb * BS + 8 * quad;   // this lane's 8 positions
         f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -745,8 +761,8 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
         float x[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[e] = p0 + e < lim ? sa[e] * a.scale_log2 : -INFINITY;
-            x[4 + e] = p0 + 4 + e < lim ? sb[e] * a.scale_log2 : -INFINITY;
+            x[e] = p0 + e < lim_b ? sa[e] * a.scale_log2 : -INFINITY;
+            x[4 + e] = p0 + 4 + e < lim_b ? sb[e] * a.scale_log2 : -INFINITY;
         }
         const float bm = max_over_rows(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                                              fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
@@ -764,12 +780,12 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
 #pragma unroll
         for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(x[e] - mref);
         lsum += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-        if (jb * BS + BS > lim) {   // partly valid block: rows from lim on may hold anything
+        if (jb * BS + BS > lim_b) {   // partly valid block: rows from lim_b on may hold anything
             uint32_t m0 = 0, m1 = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                m0 |= (p0 + e < lim ? 0xffu : 0u) << (8 * e);
-                m1 |= (p0 + 4 + e < lim ? 0xffu : 0u) << (8 * e);
+                m0 |= (p0 + e < lim_b ? 0xffu : 0u) << (8 * e);
+                m1 |= (p0 + 4 + e < lim_b ? 0xffu : 0u) << (8 * e);
             }
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
@@ -894,7 +910,7 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     __shared__ int32_t s_len[kSplitMaxSeqs];
     __shared__ int32_t s_wave[kWaves];
     extern __shared__ uint4 s_dyn[];    // per wave: see split_wave_bytes
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = lane & 15, quad = lane >> 4;
     const int G = a.group, hkv = a.num_kv_heads;
     const int total = split_scan(a.seq_lens, a.num_seqs, hkv, a.max_len, s_end, s_len, s_wave);
@@ -1002,17 +1018,18 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     // per-lane metadata of the current batch: tile k's block ids (tphys; tphysb the
     // second block for BS = 8), (b, g) and tile index j
     int tphys = 0, tphysb = 0, tbg = 0, tj = 0;
+    const uint32_t nb_lim = block_limit(a.num_blocks);
     // bit 0: the (first) block id is valid; bit 1: the second one (BS = 8) is
     auto load = [&](KvTile<D, F8>& t, int k) -> int {
-        int64_t pa = __builtin_amdgcn_readlane(tphys, k);
-        const bool oka = pa >= 0 && pa < a.num_blocks;
-        pa = oka ? pa : 0;
+        const int ida = __builtin_amdgcn_readlane(tphys, k);
+        const bool oka = uint32_t(ida) < nb_lim;
+        const int64_t pa = oka ? ida : 0;
         int64_t pb = pa;
         bool okb = true;
         if constexpr (BS == 8) {
-            pb = __builtin_amdgcn_readlane(tphysb, k);
-            okb = pb >= 0 && pb < a.num_blocks;
-            pb = okb ? pb : 0;
+            const int idb = __builtin_amdgcn_readlane(tphysb, k);
+            okb = uint32_t(idb) < nb_lim;
+            pb = okb ? idb : 0;
         }
         const int g = __builtin_amdgcn_readlane(tbg, k) % hkv;
         const int j = __builtin_amdgcn_readlane(tj, k);
@@ -1295,7 +1312,12 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     }
 }
 
-constexpr int kWaves = 4;
+// Waves per workgroup of the single-pass / partitioned kernels (4 or 8).
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+constexpr int kWaves = PKV_DECODE_WAVES;
+static_assert(kWaves == 4 || kWaves == 8, "four or eight waves per workgroup");
 
 template <typename T, int D, typename OutT, bool F8, int BS>
 hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {

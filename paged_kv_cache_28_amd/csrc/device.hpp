@@ -19,6 +19,12 @@ struct f16_t {};
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The index of the calling wave in its workgroup, as a value the compiler knows to be the
+// same in every lane (loops bounded by it compile to scalar loops).
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+}
+
 // Loads of K/V tile data that a decode launch reads exactly once: non-temporal
 // (global_load ... nt), so the L2 and the Infinity Cache do not keep lines that will not be
 // read again. On MI355X this streamed the 8B batch's tile set 6-10% faster than plain loads
@@ -35,6 +41,39 @@ __device__ __forceinline__ uint2 ld_once8(const void* p) {
 }
 __device__ __forceinline__ uint32_t ld_once4(const void* p) {
     return __builtin_nontemporal_load(static_cast<const unsigned int*>(p));
+}
+
+// Block ids are valid in [0, num_blocks). As a 32-bit unsigned limit (negative ids wrap past
+// it) the per-tile test is one scalar compare; a 64-bit signed compare has no scalar form
+// here and went through vector registers that loads in flight were still filling, which
+// made the compiler wait for them before the next tile's loads.
+__device__ __forceinline__ uint32_t block_limit(int64_t num_blocks) {
+    return num_blocks <= 0 ? 0u : (num_blocks > int64_t(0x7fffffff) ? 0x80000000u : uint32_t(num_blocks));
+}
+
+// The same non-temporal tile loads through a buffer resource: a scalar descriptor over one
+// (block, KV head) tile of `bytes` bytes, against which each lane takes a fixed byte offset.
+// Moving to the next tile then rewrites scalar registers only. With 64-bit per-lane
+// addresses the compiler recomputed the address registers at the head of the tile loop and,
+// sharing them with registers that loads were still filling, waited for every outstanding
+// load there: the next tile was requested only once the current one had arrived, which
+// left one tile in flight while the matrix products ran. Offsets past `bytes` would read
+// zero; none is formed. Descriptor word 3 is the raw-dword format of this GPU family.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+constexpr int kBufNT = 2;   // cache policy of the load: non-temporal
+__device__ __forceinline__ buf_rsrc_t tile_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(buf_rsrc_t r, int off, int soff = 0) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kBufNT);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 bld8(buf_rsrc_t r, int off, int soff = 0) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kBufNT);
+    return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint32_t bld4(buf_rsrc_t r, int off, int soff = 0) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kBufNT);
 }
 
 // fp32 -> 16-bit patterns, round to nearest even (NaN stays NaN).

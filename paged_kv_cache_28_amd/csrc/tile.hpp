@@ -37,76 +37,55 @@ __device__ __forceinline__ int q_dim(int c, int quad) {
     return F8 ? 64 * (c >> 1) + 16 * quad + 8 * (c & 1) : 32 * c + 8 * quad;
 }
 
-template <int D>
-__device__ __forceinline__ void load_tile(KvTile<D, false>& t, const char* kt, const char* vt,
-                                          int lane) {
-    const int col = lane & 15, quad = lane >> 4;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) t.k[c] = ld_once16(kt + (64 * c + lane) * 16);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) t.v[c] = ld_once8(vt + ((16 * c + col) * 16 + 4 * quad) * 2);
-}
-template <int D>
-__device__ __forceinline__ void load_tile(KvTile<D, true>& t, const char* kt, const char* vt,
-                                          int lane) {
-    const int col = lane & 15, quad = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) t.k[i] = ld_once16(kt + (64 * i + lane) * 16);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) t.v[c] = ld_once4(vt + (16 * c + col) * 16 + 4 * quad);
-}
-
-// Blocks of BS tokens (8, 16 or 32) hold 16-token tiles as follows: BS = 16, a tile is a
-// block; BS = 32, a tile is rows 16h .. 16h + 15 (h = 0, 1) of a block; BS = 8, a tile is
-// two blocks, rows 0-7 from block A and 8-15 from block B. The per-(block, KV head) layout
-// is K [d/x][BS][x], V [d][BS], so the lane's rows sit at these offsets (16-bit cache:
-// x = 8; FP8 cache: x = 16; ka/va: block A's head tile, kb/vb: block B's, row0 = 16h).
+// Loads of one 16-token tile, through buffer resources over the (block, KV head) tiles
+// (tile_rsrc): ka/va cover the tile of block A; for BS = 32, row0 (0 or 16) picks the
+// half, added as a scalar offset (BS = 16 ignores it: the tile is the block). BS = 8 takes
+// rows 0-7 from block A and 8-15 from block B, a choice that differs between lanes, so it
+// reads through per-lane addresses instead.
 template <int D, int BS>
 __device__ __forceinline__ void load_tile_bs(KvTile<D, false>& t, const char* ka, const char* va,
                                              const char* kb, const char* vb, int row0, int lane) {
     static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
-    if constexpr (BS == 16) {
-        load_tile<D>(t, ka, va, lane);
-    } else {
-        const int col = lane & 15, quad = lane >> 4;
-        const char* kt = ka;
-        int krow = row0 + col;
-        const char* vt = va;
-        int vrow = row0 + 4 * quad;
-        if constexpr (BS == 8) {
-            kt = col < 8 ? ka : kb;
-            krow = col & 7;
-            vt = quad < 2 ? va : vb;
-            vrow = 4 * (quad & 1);
-        }
+    const int col = lane & 15, quad = lane >> 4;
+    if constexpr (BS == 8) {
+        const char* kt = col < 8 ? ka : kb;
+        const int krow = col & 7;
+        const char* vt = quad < 2 ? va : vb;
+        const int vrow = 4 * (quad & 1);
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) t.k[c] = ld_once16(kt + ((4 * c + quad) * BS + krow) * 16);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) t.v[c] = ld_once8(vt + ((16 * c + col) * BS + vrow) * 2);
+    } else {
+        const int r0 = BS == 32 ? row0 : 0;
+        const buf_rsrc_t kr = tile_rsrc(ka, D * BS * 2), vr = tile_rsrc(va, D * BS * 2);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) t.k[c] = bld16(kr, ((4 * c + quad) * BS + col) * 16, r0 * 16);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) t.v[c] = bld8(vr, ((16 * c + col) * BS + 4 * quad) * 2, r0 * 2);
     }
 }
 template <int D, int BS>
 __device__ __forceinline__ void load_tile_bs(KvTile<D, true>& t, const char* ka, const char* va,
                                              const char* kb, const char* vb, int row0, int lane) {
     static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
-    if constexpr (BS == 16) {
-        load_tile<D>(t, ka, va, lane);
-    } else {
-        const int col = lane & 15, quad = lane >> 4;
-        const char* kt = ka;
-        int krow = row0 + col;
-        const char* vt = va;
-        int vrow = row0 + 4 * quad;
-        if constexpr (BS == 8) {
-            kt = col < 8 ? ka : kb;
-            krow = col & 7;
-            vt = quad < 2 ? va : vb;
-            vrow = 4 * (quad & 1);
-        }
+    const int col = lane & 15, quad = lane >> 4;
+    if constexpr (BS == 8) {
+        const char* kt = col < 8 ? ka : kb;
+        const int krow = col & 7;
+        const char* vt = quad < 2 ? va : vb;
+        const int vrow = 4 * (quad & 1);
 #pragma unroll
         for (int i = 0; i < D / 64; ++i) t.k[i] = ld_once16(kt + ((4 * i + quad) * BS + krow) * 16);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) t.v[c] = ld_once4(vt + (16 * c + col) * BS + vrow);
+    } else {
+        const int r0 = BS == 32 ? row0 : 0;
+        const buf_rsrc_t kr = tile_rsrc(ka, D * BS), vr = tile_rsrc(va, D * BS);
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) t.k[i] = bld16(kr, ((4 * i + quad) * BS + col) * 16, r0 * 16);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) t.v[c] = bld4(vr, (16 * c + col) * BS + 4 * quad, r0);
     }
 }
 
