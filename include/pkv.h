@@ -106,8 +106,10 @@ int pkv_timer_read(int32_t entry, double* total_ms, int64_t* launches);
 
 /* ---- streaming ceilings -----------------------------------------------------------
  * Not part of the method: measuring aids, timed under PKV_TIMER_MEASURE. They read and
- * fold their input into a running XOR (stored to sink[i % sink_len], a device uint32
- * buffer; nothing else is written), so the decode kernels' rates can be set against what
+ * fold their input into a running XOR per wave, stored to sink[w % sink_len] for wave w
+ * (a device uint32 buffer; nothing else is written: with sink_len at least the number of
+ * waves and a zeroed sink, the XOR over the sink is that of every 32-bit word read, an
+ * invalid block id reading block 0), so the decode kernels' rates can be set against what
  * the same GPU streams with no arithmetic, and the gather against the contiguous read is
  * the cost of reading through a block table ("vLLM ve Triton ile maliyet optimizasyonu",
  * §05 Sınırlar, on the indirection cost of paged reads).

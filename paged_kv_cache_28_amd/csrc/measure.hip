@@ -5,8 +5,10 @@
 // Triton ile maliyet optimizasyonu", §05 Sınırlar, on the kernel complexity and
 // indirection cost of paged reads).
 //
-// Every loaded 16-byte group is folded into a running XOR that each workgroup stores to
-// `sink`, so no load can be dropped; nothing else is written. Each kernel runs with plain or
+// Every loaded 16-byte group is folded into a running XOR that each wave stores to its own
+// slot of `sink` (wave index modulo sink_len), so no load can be dropped and, with a sink of
+// at least one slot per wave that starts at zero, the XOR over the sink is the XOR of
+// every 32-bit word read; nothing else is written. Each kernel runs with plain or
 // non-temporal loads (the decode kernels use the latter for their tiles).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
         for (int u = 0; u < U; ++u) acc ^= fold(v[u]);
     }
     for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
-    if (threadIdx.x == 0) sink[blockIdx.x % sink_len] = acc;
+    if (lane == 0) sink[(int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6)) % sink_len] = acc;
 }
 
 struct GatherArgs {
@@ -79,17 +81,21 @@ template <int NL>
 struct Tile {
     uint4 k[NL], v[NL];
 };
+// As the decode kernels read their tiles: through a buffer resource per tile, each lane at
+// a fixed offset (see tile_rsrc), so the loop's address registers do not change.
 template <bool NT, int NL>
-__device__ __forceinline__ void load_tile(Tile<NL>& t, const GatherArgs& a, int64_t blk, int g,
+__device__ __forceinline__ void load_tile(Tile<NL>& t, const GatherArgs& a, int blk, int g,
                                           int lane) {
-    const bool ok = blk >= 0 && blk < a.num_blocks;   // an invalid id reads block 0
-    const int64_t off = ((ok ? blk : 0) * a.num_kv_heads + g) * a.tile_bytes;
-    const uint4* kt = reinterpret_cast<const uint4*>(a.k_cache + off);
-    const uint4* vt = reinterpret_cast<const uint4*>(a.v_cache + off);
+    const bool ok = uint32_t(blk) < block_limit(a.num_blocks);   // an invalid id reads block 0
+    const int64_t off = (int64_t(ok ? blk : 0) * a.num_kv_heads + g) * a.tile_bytes;
+    const buf_rsrc_t kr = tile_rsrc(a.k_cache + off, int(a.tile_bytes));
+    const buf_rsrc_t vr = tile_rsrc(a.v_cache + off, int(a.tile_bytes));
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-        t.k[i] = ld16<NT>(kt + 64 * i + lane);
-        t.v[i] = ld16<NT>(vt + 64 * i + lane);
+        const u32x4_t k = __builtin_amdgcn_raw_buffer_load_b128(kr, (64 * i + lane) * 16, 0, NT ? kBufNT : 0);
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(vr, (64 * i + lane) * 16, 0, NT ? kBufNT : 0);
+        t.k[i] = make_uint4(k[0], k[1], k[2], k[3]);
+        t.v[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 }
 template <int NL>
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(256) void gather_seq_kernel(GatherArgs a) {
         }
     }
     for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
-    if (lane == 0) a.sink[(int64_t(blockIdx.y) * gridDim.x + blockIdx.x) % a.sink_len] = acc;
+    if (lane == 0) a.sink[((int64_t(blockIdx.y) * gridDim.x + blockIdx.x) * W + wave) % a.sink_len] = acc;
 }
 
 // Perfect balance: every (sequence, KV head, block) tile of the batch in one list (order

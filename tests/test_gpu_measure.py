@@ -1,0 +1,98 @@
+"""The measuring kernels behind the bench's ceilings read exactly the bytes they claim: the
+contiguous read every 32-bit word of its buffer once, the gather every (block, KV head) K
+and V tile of every sequence's first ceil(n / block_size) table entries once (an invalid
+id reads block 0). Each wave leaves the XOR of what it read in its own sink slot, so the
+XOR over a zeroed sink with a slot per wave must equal the XOR of those words computed
+here on the host."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_28_amd as pkv
+
+pytestmark = pytest.mark.gpu
+SINK = 16384   # more slots than waves in any launch below (at most 256 CUs x 32 waves)
+
+
+@pytest.fixture(scope="module")
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _xor_words(a: np.ndarray, axis=None):
+    return np.bitwise_xor.reduce(np.ascontiguousarray(a).view(np.uint32), axis=axis)
+
+
+def _sink_xor(sink):
+    return int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+
+
+@pytest.mark.parametrize("nbytes", [16, 1 << 20, (1 << 20) + 48, 3 * (1 << 20) + 1024])
+@pytest.mark.parametrize("nt", [True, False])
+@pytest.mark.parametrize("waves,inflight", [(8, 8), (4, 2), (32, 16)])
+def test_read_covers_every_word(nbytes, nt, waves, inflight, device):
+    g = torch.Generator().manual_seed(nbytes + waves)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    buf = host.to(device)
+    sink = torch.zeros(SINK, dtype=torch.int32, device=device)
+    pkv.measure_read(buf, sink, waves_per_cu=waves, loads_in_flight=inflight, nontemporal=nt)
+    torch.cuda.synchronize()
+    assert _sink_xor(sink) == int(_xor_words(host.numpy()))
+
+
+# lengths: empty, one token, a ragged block, and one long enough that every wave of the
+# per-sequence gather reaches its second 64-entry block-id segment (> 4 x 64 blocks)
+LENS = [0, 1, 17, 300, 4200]
+
+
+def _batch(device, dtype, bs, seed, invalid=False):
+    rng = np.random.default_rng(seed)
+    hkv, d = 2, 128
+    x = 16 if dtype == torch.uint8 else 8
+    nblk = [-(-n // bs) for n in LENS]
+    nb = sum(nblk) + 7
+    maxb = max(nblk)
+    ebytes = 1 if dtype == torch.uint8 else 2
+    kbits = rng.integers(0, 256, size=(nb, hkv, d // x, bs, x * ebytes), dtype=np.uint8)
+    vbits = rng.integers(0, 256, size=(nb, hkv, d, bs * ebytes), dtype=np.uint8)
+    ids = rng.permutation(nb)
+    table = np.full((len(LENS), maxb), -1, np.int32)
+    pos = 0
+    for b, m in enumerate(nblk):
+        table[b, :m] = ids[pos:pos + m]
+        pos += m
+    if invalid:   # ids outside [0, nb) inside the lengths: read as block 0
+        table[3, 5] = -3
+        table[4, 100] = nb + 11
+    kc = torch.from_numpy(kbits).view(dtype).reshape(nb, hkv, d // x, bs, x).to(device)
+    vc = torch.from_numpy(vbits).view(dtype).reshape(nb, hkv, d, bs).to(device)
+    # expected: XOR over the tiles read, each (block, KV head) tile's K and V words
+    tile_x = _xor_words(kbits.reshape(nb, hkv, -1), axis=2) ^ _xor_words(vbits.reshape(nb, hkv, -1), axis=2)
+    want = np.uint32(0)
+    for b, m in enumerate(nblk):
+        for j in range(m):
+            blk = table[b, j]
+            blk = blk if 0 <= blk < nb else 0
+            want ^= np.bitwise_xor.reduce(tile_x[blk])
+    lens = torch.tensor(LENS, dtype=torch.int32, device=device)
+    return kc, vc, torch.from_numpy(table).to(device), lens, int(want)
+
+
+@pytest.mark.parametrize("dtype,bs", [(torch.bfloat16, 16), (torch.uint8, 16),
+                                      (torch.float16, 8), (torch.bfloat16, 32)])
+@pytest.mark.parametrize("mode", ["per_seq", "per_seq_plan", "balanced"])
+@pytest.mark.parametrize("nt", [True, False])
+@pytest.mark.parametrize("invalid", [False, True])
+def test_gather_reads_the_decode_tiles(dtype, bs, mode, nt, invalid, device):
+    if mode == "balanced" and bs != 16:
+        pytest.skip("the balanced gather takes 16-token blocks")
+    kc, vc, tables, lens, want = _batch(device, dtype, bs, seed=bs * 7 + int(invalid), invalid=invalid)
+    order = (pkv.paged_attention_decode_plan(np.array(LENS, np.int32), kc.shape[1])
+             if mode == "per_seq_plan" else None)
+    sink = torch.zeros(SINK, dtype=torch.int32, device=device)
+    pkv.measure_gather(kc, vc, tables, lens, sink, seq_order=order,
+                       balanced=(mode == "balanced"), nontemporal=nt)
+    torch.cuda.synchronize()
+    assert _sink_xor(sink) == want
