@@ -170,6 +170,9 @@ def traffic_summary(spec):
     fs, ws = scale(cal_f, "FETCH_SIZE"), scale(cal_w, "WRITE_SIZE")
     f = per_dispatch(fetch_d, "FETCH_SIZE", is_decode) * 1024 * fs
     wr = per_dispatch(write_d, "WRITE_SIZE", is_decode) * 1024 * ws
+    if "fp8_accuracy" in bench and len(f) == len(wr) > len(alg):
+        # the FP8 run's accuracy check decodes after the timed passes: not in the record
+        f, wr = f[:len(alg)], wr[:len(alg)]
     if not (len(f) == len(wr) == len(alg)):
         raise SystemExit(f"dispatch counts differ: fetch {len(f)}, write {len(wr)}, "
                          f"launches {len(alg)}")
