@@ -64,16 +64,21 @@ constexpr int kBufNT = 2;   // cache policy of the load: non-temporal
 __device__ __forceinline__ buf_rsrc_t tile_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), bytes, 0x00020000);
 }
+// POL: the cache policy (kBufNT; 0 for plain loads, where another wave reads the rest of
+// the same lines, as the two halves of a 32-token block are).
+template <int POL = kBufNT>
 __device__ __forceinline__ uint4 bld16(buf_rsrc_t r, int off, int soff = 0) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kBufNT);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, POL);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
+template <int POL = kBufNT>
 __device__ __forceinline__ uint2 bld8(buf_rsrc_t r, int off, int soff = 0) {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kBufNT);
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, POL);
     return make_uint2(v[0], v[1]);
 }
+template <int POL = kBufNT>
 __device__ __forceinline__ uint32_t bld4(buf_rsrc_t r, int off, int soff = 0) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, kBufNT);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, POL);
 }
 
 // fp32 -> 16-bit patterns, round to nearest even (NaN stays NaN).

@@ -37,6 +37,13 @@ __device__ __forceinline__ int q_dim(int c, int quad) {
     return F8 ? 64 * (c >> 1) + 16 * quad + 8 * (c & 1) : 32 * c + 8 * quad;
 }
 
+// Cache policy of the tile loads: non-temporal, except for the half-block tiles of 32-token
+// blocks, whose K and V lines hold rows of both halves, which two waves read at about the
+// same time (non-temporal loads there made the 8B batch at 32 tokens per block 11% slower
+// in the single pass and 17% in the balanced split).
+template <int BS>
+constexpr int kTilePol = BS == 32 ? 0 : kBufNT;
+
 // Loads of one 16-token tile, through buffer resources over the (block, KV head) tiles
 // (tile_rsrc): ka/va cover the tile of block A; for BS = 32, row0 (0 or 16) picks the
 // half, added as a scalar offset (BS = 16 ignores it: the tile is the block). BS = 8 takes
@@ -60,9 +67,9 @@ __device__ __forceinline__ void load_tile_bs(KvTile<D, false>& t, const char* ka
         const int r0 = BS == 32 ? row0 : 0;
         const buf_rsrc_t kr = tile_rsrc(ka, D * BS * 2), vr = tile_rsrc(va, D * BS * 2);
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) t.k[c] = bld16(kr, ((4 * c + quad) * BS + col) * 16, r0 * 16);
+        for (int c = 0; c < D / 32; ++c) t.k[c] = bld16<kTilePol<BS>>(kr, ((4 * c + quad) * BS + col) * 16, r0 * 16);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) t.v[c] = bld8(vr, ((16 * c + col) * BS + 4 * quad) * 2, r0 * 2);
+        for (int c = 0; c < D / 16; ++c) t.v[c] = bld8<kTilePol<BS>>(vr, ((16 * c + col) * BS + 4 * quad) * 2, r0 * 2);
     }
 }
 template <int D, int BS>
@@ -83,9 +90,9 @@ __device__ __forceinline__ void load_tile_bs(KvTile<D, true>& t, const char* ka,
         const int r0 = BS == 32 ? row0 : 0;
         const buf_rsrc_t kr = tile_rsrc(ka, D * BS), vr = tile_rsrc(va, D * BS);
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) t.k[i] = bld16(kr, ((4 * i + quad) * BS + col) * 16, r0 * 16);
+        for (int i = 0; i < D / 64; ++i) t.k[i] = bld16<kTilePol<BS>>(kr, ((4 * i + quad) * BS + col) * 16, r0 * 16);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) t.v[c] = bld4(vr, (16 * c + col) * BS + 4 * quad, r0);
+        for (int c = 0; c < D / 16; ++c) t.v[c] = bld4<kTilePol<BS>>(vr, (16 * c + col) * BS + 4 * quad, r0);
     }
 }
 
