@@ -341,7 +341,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
             for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c + col];
         }
     }
-    auto quantize_new = [&]() {
+    auto quantize_new = [&]() __attribute__((always_inline)) {
         if constexpr (Append && F8)   // in this wave's slice of sm_o, free until the merge
             quantize_new_row_fp8<T, D>(a, reinterpret_cast<uint8_t*>(sm_o + wave * G * D), lane,
                                        nkr, nvr, nk, nv);
@@ -361,20 +361,21 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
 
     const int nmine = first < blk_end ? (blk_end - first + W - 1) / W : 0;
     // The wave that holds tile jl (w_new) stores the new rows into the slot. When the
-    // slot is the newest position's (what the block pool hands out), the tiles stop one
-    // row short (row n-1 is masked like a row past the end, so it does not matter whether
-    // the store has landed when tile jl is read) and w_new adds the new token after its
-    // last tile as a one-row tile from the key/value inputs. Otherwise the cache is read
-    // as it is. lim: rows below it are valid.
+    // slot is the newest position's (what the block pool hands out), w_new overwrites row
+    // n-1 of tile jl in its registers with the new token from the key/value inputs once
+    // the tile has arrived, so it does not matter whether the store had landed when the
+    // tile was read. Otherwise the cache is read as it is. lim: rows below it are valid.
+    // (Adding the new token after the last tile as a one-row tile instead cost a whole
+    // tile's products on the wave that finishes last.)
     bool subst = false;   // set by w_new when it reaches the table segment holding jl
-    int lim = n;
+    const int lim = n;
     const bool own_new = jl >= blk_begin && jl < blk_end;   // this workgroup holds tile jl
     const int w_new = own_new ? (jl - blk_begin) % W : -1;
     const int k_new = own_new ? (jl - first) / W : -1;      // jl's index in w_new's list
     // The row stores, issued right after w_new's first tile loads: those loads are older,
     // so their wait does not include the stores, and the stores complete while the wave
     // streams (issued at the end of the stream they would lengthen the kernel's tail).
-    auto store_new_row = [&]() {
+    auto store_new_row = [&]() __attribute__((always_inline)) {
         if constexpr (Append) {
             if (wave != w_new) return;
             quantize_new();   // FP8: the codes, also those of the one-row tile at the end
@@ -445,7 +446,39 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     // register is then consumed on every path, so the compiler's memory waits stay per
     // tile (a path that skips a tile's registers makes it drain all outstanding loads at
     // the loop head). An invalid second block (BS = 8) masks rows 8-15.
-    auto compute = [&](KvTile<D, F8>& t, int j, int ok) {
+    auto compute = [&](KvTile<D, F8>& t, int j, int ok) __attribute__((always_inline)) {
+        if constexpr (Append) {
+            if (subst && j == jl) {   // wave-uniform: row n-1 of tile jl is the new token
+                // bit masks, not selects between the arrays: a select of two loads would
+                // put the tile and the row in scratch memory to load through a pointer
+                const int off = (n - 1) & 15;
+                const bool vl = quad == (off >> 2);
+                const uint32_t km = col == off ? 0xffffffffu : 0u;
+#pragma unroll
+                for (int c = 0; c < NKL; ++c) {
+                    t.k[c].x = (t.k[c].x & ~km) | (nk[c].x & km);
+                    t.k[c].y = (t.k[c].y & ~km) | (nk[c].y & km);
+                    t.k[c].z = (t.k[c].z & ~km) | (nk[c].z & km);
+                    t.k[c].w = (t.k[c].w & ~km) | (nk[c].w & km);
+                }
+                const int e = off & 3;   // the row's element in the lane's V word(s)
+                if constexpr (F8) {
+                    const uint32_t sh = 8u * uint32_t(e), mk = vl ? 0xffu << sh : 0u;
+#pragma unroll
+                    for (int c = 0; c < NPV; ++c) t.v[c] = (t.v[c] & ~mk) | (((nv[c] & 0xffu) << sh) & mk);
+                } else {
+                    const uint32_t sh = 16u * uint32_t(e & 1);
+                    const uint32_t mx = vl && e < 2 ? 0xffffu << sh : 0u;
+                    const uint32_t my = vl && e >= 2 ? 0xffffu << sh : 0u;
+#pragma unroll
+                    for (int c = 0; c < NPV; ++c) {
+                        const uint32_t r = (nv[c] & 0xffffu) << sh;
+                        t.v[c].x = (t.v[c].x & ~mx) | (r & mx);
+                        t.v[c].y = (t.v[c].y & ~my) | (r & my);
+                    }
+                }
+            }
+        }
         const int lim_t = !(ok & 1) ? j * 16 : (ok & 2) ? lim : min(lim, j * 16 + 8);
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -512,7 +545,6 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                 const int64_t phys_l = __builtin_amdgcn_readlane(half ? tabb : tab, k_new - k0);
                 subst = slot >= 0 && phys_l >= 0 && phys_l < a.num_blocks &&
                         int64_t(slot) == phys_l * BS + (n - 1) % BS;
-                lim = subst ? n - 1 : n;
             }
         }
         KvTile<D, F8> X, Y, Z;
@@ -554,25 +586,6 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
                 okY = ld(Y, k + 4);
                 compute(Z, tile_of(k + 2), okZ);
             }
-        }
-    }
-
-    // Fused append, in w_new after its last tile: the new token as a tile whose only
-    // valid row is row 0.
-    if constexpr (Append) {
-        if (wave == w_new && subst) {
-            KvTile<D, F8> t;
-#pragma unroll
-            for (int c = 0; c < NKL; ++c) t.k[c] = col == 0 ? nk[c] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int c = 0; c < NPV; ++c) {
-                if constexpr (F8)
-                    t.v[c] = quad == 0 ? nv[c] & 0xffu : 0u;
-                else
-                    t.v[c] = make_uint2(quad == 0 ? nv[c] & 0xffffu : 0u, 0u);
-            }
-            lim = 1;
-            compute(t, 0, 3);
         }
     }
 
@@ -668,7 +681,7 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
                                int64_t(g) * D;
         load_new_row_fp8<D>(krow, vrow, lane, nkr, nvr);
     }
-    auto quantize_new = [&]() {
+    auto quantize_new = [&]() __attribute__((always_inline)) {
         if constexpr (Append)
             quantize_new_row_fp8<T, D>(a, reinterpret_cast<uint8_t*>(sm_o + wave * G * D), lane,
                                        nkr, nvr, nk, nv);
@@ -691,7 +704,7 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
     const bool own_new = jl >= blk_begin && jl < blk_end;
     const int w_new = own_new ? (jl - blk_begin) % W : -1;
     const int k_new = own_new ? (jl - first) / W : -1;
-    auto store_new_row = [&]() {
+    auto store_new_row = [&]() __attribute__((always_inline)) {
         if constexpr (Append) {
             if (wave != w_new) return;
             quantize_new();
