@@ -232,7 +232,15 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
     a.slot_mapping = fused ? app.slot_mapping : nullptr;
     a.new_k_stride = app.key_stride;
     a.new_v_stride = app.value_stride;
-    a.heads_fastest = grid_parts < 8;
+    // Fixed partitions in the matrix-core kernel: one partition per wave where the table
+    // holds at least 2 kWaves partitions. Measured on MI355X at 512-token partitions: the
+    // 70B batch 397.5 -> 337.8 us, the 131K-262K-token batch 602-610 -> 573-580 us; the 8B
+    // batch (at most 4 partitions per sequence, most sequences in one or two) 63.0 -> 64.4
+    // us, so short tables keep the W waves per partition.
+    a.per_wave = !split && grid_parts >= 2 * pkv::kWaves && in_dtype != PKV_F32 &&
+                 !(fp8 && block_size == 32 && part_tiles % 2 == 0);
+    const int grid_slots = a.per_wave ? (grid_parts + pkv::kWaves - 1) / pkv::kWaves : grid_parts;
+    a.heads_fastest = grid_slots < 8;
     a.lpt_round = 0;
     a.use_order = 0;
     if (!split && grid_parts == 1 && num_seqs <= pkv::kLptMaxSeqs && in_dtype != PKV_F32) {
@@ -244,8 +252,8 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
         }
     }
     const dim3 grid = a.heads_fastest
-                          ? dim3{unsigned(num_kv_heads), unsigned(num_seqs), unsigned(grid_parts)}
-                          : dim3{unsigned(grid_parts), unsigned(num_kv_heads), unsigned(num_seqs)};
+                          ? dim3{unsigned(num_kv_heads), unsigned(num_seqs), unsigned(grid_slots)}
+                          : dim3{unsigned(grid_slots), unsigned(num_kv_heads), unsigned(num_seqs)};
     const hipError_t err =
         block_size == 16 ? pkv::dispatch_bs<16>(a, head_dim, in_dtype, out_dtype, grid, s, split, fp8)
         : block_size == 8 ? pkv::dispatch_bs<8>(a, head_dim, in_dtype, out_dtype, grid, s, split, fp8)

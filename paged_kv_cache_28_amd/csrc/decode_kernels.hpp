@@ -98,6 +98,11 @@ struct DecodeArgs {
     // partition); with 8 or more it is (partition, KV head, sequence), which measured
     // faster on long contexts.
     int32_t heads_fastest;
+    // Fixed partitions: each wave takes a partition of its own (kWaves partitions per
+    // workgroup, grid slot pg holding partitions pg kWaves ..) and writes its record, so a
+    // workgroup's fixed costs (queries, block ids, the first tiles' latency, the merge) are
+    // paid once per kWaves partitions rather than once per partition.
+    int32_t per_wave;
     // Single pass with at most kLptMaxSeqs sequences: workgroups are dispatched one CU
     // after the other, one round of lpt_round sequences (x KV heads) per sweep over the
     // CUs, and a CU keeps the workgroups of all rounds. The sequences are handed out by
@@ -266,7 +271,7 @@ __device__ void merge_and_store(const DecodeArgs& a, const float* sm_m, const fl
 
 // ---------------------------------------------------------------- fp16 / bf16
 
-template <typename T, int D, typename OutT, int W, bool Append, bool F8, int BS>
+template <typename T, int D, typename OutT, int W, bool Append, bool F8, int BS, bool PW>
 __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
     constexpr int NQK = D / 32;   // 16x16x32 steps for S
@@ -280,7 +285,11 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = a.heads_fastest ? blockIdx.x : blockIdx.y;
     int b = a.heads_fastest ? blockIdx.y : blockIdx.z;
-    const int p = a.heads_fastest ? blockIdx.z : blockIdx.x;
+    // PW (fixed partitions): each wave takes a partition of its own, partitions pg W ..
+    // pg W + W - 1 of grid slot pg, and writes its record itself. Otherwise the W waves
+    // share partition pg and merge through LDS.
+    const int pg = a.heads_fastest ? blockIdx.z : blockIdx.x;
+    const int p = PW ? pg * W + wave : pg;
     if (a.use_order)
         b = a.order[b];
     else if (a.lpt_round > 0)
@@ -296,10 +305,11 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     // tiles first, first + W, ... of its partition; the table row has max_blocks entries,
     // so the ids are read before the length is known.
     const int blk_begin = p * a.part_tiles;
-    const int first = blk_begin + wave;
+    constexpr int STEP = PW ? 1 : W;   // tile stride of a wave's list
+    const int first = blk_begin + (PW ? 0 : wave);
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
     int tab0, tab0b;
-    tile_ids<BS>(table, a.max_blocks, first + lane * W, tab0, tab0b);
+    tile_ids<BS>(table, a.max_blocks, first + lane * STEP, tab0, tab0b);
     const int n_raw = a.seq_lens[b];
     __builtin_amdgcn_sched_barrier(0);
 
@@ -350,16 +360,17 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     int n = n_raw < 0 ? 0 : (n_raw > a.max_len ? a.max_len : n_raw);
     const int nblk = (n + 15) >> 4;
     const int jl = n > 0 ? (n - 1) >> 4 : -1;     // tile of the newest token
-    if (blk_begin >= nblk) {
-        if (p == 0) write_zero_rows<OutT, D>(a, b, g);
+    if ((PW ? pg * W * a.part_tiles : blk_begin) >= nblk) {   // the whole workgroup
+        if (pg == 0) write_zero_rows<OutT, D>(a, b, g);
         if constexpr (Append)
-            if (p == 0 && n == 0) write_new_token<T, D, F8, BS>(a, b, g, slot);
+            if (pg == 0 && n == 0) write_new_token<T, D, F8, BS>(a, b, g, slot);
         return;
     }
+    if (PW && blk_begin >= nblk) return;   // this wave's partition lies past the end
     const int blk_end = min(nblk, blk_begin + a.part_tiles);
     const bool direct = nblk <= a.part_tiles;
 
-    const int nmine = first < blk_end ? (blk_end - first + W - 1) / W : 0;
+    const int nmine = first < blk_end ? (blk_end - first + STEP - 1) / STEP : 0;
     // The wave that holds tile jl (w_new) stores the new rows into the slot. When the
     // slot is the newest position's (what the block pool hands out), w_new overwrites row
     // n-1 of tile jl in its registers with the new token from the key/value inputs once
@@ -370,8 +381,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     bool subst = false;   // set by w_new when it reaches the table segment holding jl
     const int lim = n;
     const bool own_new = jl >= blk_begin && jl < blk_end;   // this workgroup holds tile jl
-    const int w_new = own_new ? (jl - blk_begin) % W : -1;
-    const int k_new = own_new ? (jl - first) / W : -1;      // jl's index in w_new's list
+    const int w_new = own_new ? (PW ? wave : (jl - blk_begin) % W) : -1;
+    const int k_new = own_new ? (jl - first) / STEP : -1;   // jl's index in w_new's list
     // The row stores, issued right after w_new's first tile loads: those loads are older,
     // so their wait does not include the stores, and the stores complete while the wave
     // streams (issued at the end of the stream they would lengthen the kernel's tail).
@@ -534,7 +545,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
             tab = tab0;
             tabb = tab0b;
         } else {
-            tile_ids<BS>(table, a.max_blocks, lane < cnt ? first + (k0 + lane) * W : a.max_tiles,
+            tile_ids<BS>(table, a.max_blocks, lane < cnt ? first + (k0 + lane) * STEP : a.max_tiles,
                          tab, tabb);
         }
         if constexpr (Append) {
@@ -549,7 +560,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         }
         KvTile<D, F8> X, Y, Z;
         int okX = 0, okY = 0, okZ = 0;
-        auto tile_of = [&](int k) { return first + (k0 + k) * W; };
+        auto tile_of = [&](int k) { return first + (k0 + k) * STEP; };
         // The scheduling barrier keeps each tile's loads issued before the previous tile's
         // arithmetic: left free, the compiler hoists that arithmetic (and its wait) above
         // them, so the next tile is requested only after the current one has arrived.
@@ -593,6 +604,31 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
 
+    if constexpr (PW) {   // this wave's partition alone: its result as merge_and_store forms it
+        if (col < G) {
+            const int hq = g * G + col;
+            if (direct) {
+#pragma unroll
+                for (int c = 0; c < NPV; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        OutStore<OutT>::st(a.out, (int64_t(b) * a.num_heads + hq) * D + 16 * c + 4 * quad + e,
+                                           acc[c][e] / lsum * a.v_scale);
+            } else {
+                const int64_t row = (int64_t(b) * a.num_heads + hq) * a.max_partitions + p;
+#pragma unroll
+                for (int c = 0; c < NPV; ++c)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        a.part_out[row * D + 16 * c + 4 * quad + e] = acc[c][e] / lsum * a.v_scale;
+                if (quad == 0) {
+                    a.part_max[row] = m * kLn2;   // back to natural-log units
+                    a.part_sum[row] = lsum;
+                }
+            }
+        }
+        return;
+    }
     if (lane < 16) {
         sm_m[wave * 16 + lane] = m;
         sm_l[wave * 16 + lane] = lsum;
@@ -1347,12 +1383,20 @@ hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
             return hipGetLastError();
         }
     }
-    if (a.new_k)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true, F8, BS>), grid,
+    if (a.per_wave) {
+        if (a.new_k)
+            hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true, F8, BS, true>), grid,
+                                  dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
+        else
+            hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, false, F8, BS, true>), grid,
+                                  dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
+    } else if (a.new_k) {
+        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, true, F8, BS, false>), grid,
                               dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
-    else
-        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, false, F8, BS>), grid,
+    } else {
+        hipExtLaunchKernelGGL((decode_mfma_kernel<T, D, OutT, kWaves, false, F8, BS, false>), grid,
                               dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
+    }
     return hipGetLastError();
 }
 

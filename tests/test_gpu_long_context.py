@@ -45,6 +45,7 @@ LONG_FP8_BS32 = [8193, 9001, 34000, 8192, 700, 1]
 SHAPE_8B = dataclasses.replace(W["llama8b"], num_blocks=0)
 SHAPE_70B = dataclasses.replace(W["llama70b"], num_blocks=0)
 SHAPE_FP8_BS32 = dataclasses.replace(W["llama8b_fp8"], num_blocks=0, block_size=32)
+SHAPE_FP8 = dataclasses.replace(W["llama8b_fp8"], num_blocks=0)
 
 
 @pytest.fixture(scope="module")
@@ -78,13 +79,16 @@ def _decode(gb, w, P, append=None, plan=False):
 
 # (shape, lengths, partition size, host plan): the single pass with and without the plan,
 # fixed partitions of 8,192 and 16,384 tokens (two and four segments per wave inside one
-# partition; the FP8 whole-block kernel takes 16,384 for two), the balanced split, and the
-# 70B shape (G = 8, fp16)
+# partition; the FP8 whole-block kernel takes 16,384 for two), fixed partitions of 512 and
+# 1,024 tokens, where the table holds enough partitions (67 and 34 at 34,000 tokens) for
+# one partition per wave (also over an FP8 cache), the balanced split, and the 70B shape
+# (G = 8, fp16)
 DECODE_CASES = [("8b", LONG, 0, True), ("8b", LONG, 0, False), ("8b", LONG, 8192, False),
-                ("8b", LONG, 16384, False), ("8b", LONG, AUTO, False),
-                ("70b", LONG, 0, True), ("70b", LONG, 8192, False),
+                ("8b", LONG, 16384, False), ("8b", LONG, 512, False), ("8b", LONG, AUTO, False),
+                ("70b", LONG, 0, True), ("70b", LONG, 8192, False), ("70b", LONG, 1024, False),
+                ("fp8", LONG, 512, False),
                 ("fp8-bs32", LONG_FP8_BS32, 0, True), ("fp8-bs32", LONG_FP8_BS32, 16384, False)]
-SHAPES = {"8b": SHAPE_8B, "70b": SHAPE_70B, "fp8-bs32": SHAPE_FP8_BS32}
+SHAPES = {"8b": SHAPE_8B, "70b": SHAPE_70B, "fp8": SHAPE_FP8, "fp8-bs32": SHAPE_FP8_BS32}
 
 
 def _ids(cases):
@@ -115,7 +119,7 @@ def test_long_decode_matches_oracle(shape, lens, P, plan, device, batches):
     check_close(out.cpu().double().numpy(), ref, w.dtype, f"{shape} P={P} plan={plan}")
 
 
-APPEND_CASES = [("8b", LONG, 0, True), ("8b", LONG, 0, False), ("8b", LONG, 8192, False),
+APPEND_CASES = [("8b", LONG, 0, True), ("8b", LONG, 0, False), ("8b", LONG, 8192, False), ("8b", LONG, 512, False),
                 ("70b", LONG, 0, True), ("fp8-bs32", LONG_FP8_BS32, 0, True),
                 ("fp8-bs32", LONG_FP8_BS32, 16384, False)]
 
