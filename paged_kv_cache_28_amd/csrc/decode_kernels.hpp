@@ -389,7 +389,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     auto store_new_row = [&]() __attribute__((always_inline)) {
         if constexpr (Append) {
             if (wave != w_new) return;
-            quantize_new();   // FP8: the codes, also those of the one-row tile at the end
+            quantize_new();   // FP8: the codes, also those put into tile jl's registers
             if (slot < 0 || int64_t(slot) >= a.num_blocks * BS) return;
             const int64_t tile = int64_t(slot / BS) * a.num_kv_heads + g;
             const int off = slot % BS;

@@ -10,8 +10,8 @@ per token. Bars:
     the codes exactly, so quantisation itself is not part of the error;
   * 16-bit output: the fp32 result rounded once (torch's cast of it, bit for bit), within
     the fp32 bar plus half an output ulp of the oracle;
-  * the fused append: caches bit-exact against the two calls it stands for, outputs
-    within fp32 summation-order differences of them.
+  * the fused append: caches and outputs bit-exact against the two calls it stands for
+    (16-token blocks: the new row's codes go into the newest tile's registers).
 """
 import dataclasses
 
@@ -258,9 +258,10 @@ def test_fp8_fused_append_equals_two_calls_and_oracle(name, P, device):
     (o2, k2, v2), (of, kf, vf) = res
     assert torch.equal(kf, k2) and torch.equal(vf, v2)
     assert np.array_equal(oracle.raw(kf), ob.k_cache) and np.array_equal(oracle.raw(vf), ob.v_cache)
-    x, y = of.double(), o2.double()
-    assert torch.isfinite(x).all()
-    assert ((x - y).abs() <= 2e-5 + 1e-5 * y.abs()).all(), (x - y).abs().max().item()
+    # the fused kernel quantises the new row to the same codes and puts them into the
+    # newest tile's registers, so it sums what the two-call path reads back, in its order
+    assert torch.isfinite(of).all()
+    assert torch.equal(of.view(torch.int32), o2.view(torch.int32)), (of.double() - o2.double()).abs().max().item()
     check_close(of.cpu().double().numpy(), _oracle_decode(ob, w), w.dtype, f"{name} fused P={P}")
 
 
