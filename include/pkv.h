@@ -427,9 +427,7 @@ int paged_attention_decode_plan(const int32_t* seq_lens, int32_t num_seqs, int32
  * For fp16/bf16 with partition_size >= 0 the write is fused into the decode launch:
  * the wave holding the newest position stores the row into the caches and takes it for
  * the attention from key/value instead of reading it back, placing it where the cache
- * row would be, so the result equals the two calls' bit for bit (an FP8 cache at 32
- * tokens per block in whole-block steps adds it as a separate one-row step, whose fp32
- * sums run in another order). With fp32 inputs
+ * row would be, so the result equals the two calls' bit for bit. With fp32 inputs
  * or PKV_PARTITION_AUTO the write is a separate launch ahead of the decode on the same
  * stream. The other arguments, the outputs and the errors are those of
  * paged_attention_decode (and of reshape_and_cache for the new rows); with

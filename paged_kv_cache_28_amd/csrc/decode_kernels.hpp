@@ -702,9 +702,8 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
             qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + q_dim<true>(c, quad))
                             : make_uint4(0, 0, 0, 0);
     }
-    // fused append: the new row's codes as this lane holds them (nk: the K groups of a
-    // lane with col == 0, i.e. MFMA row 0 = position 0 of product A; nv: byte 0 of the
-    // lanes with quad == 0, position 0 of each dimension)
+    // fused append: the new row's codes as this lane holds them for any row (nk: the K
+    // groups 4c + quad of the row; nv: the code of dimension 16c + col)
     int slot = -1;
     uint4 nk[Append ? NKL : 1];
     uint32_t nv[Append ? NPV : 1];
@@ -735,8 +734,10 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
     const int blk_end = min(nblk, blk_begin + part_blocks);
     const bool direct = nblk <= part_blocks;
     const int nmine = first < blk_end ? (blk_end - first + W - 1) / W : 0;
+    // w_new puts the new token into row n-1 of block jl in its registers (as
+    // decode_mfma_kernel does for its tiles)
     bool subst = false;
-    int lim = n;
+    const int lim = n;
     const bool own_new = jl >= blk_begin && jl < blk_end;
     const int w_new = own_new ? (jl - blk_begin) % W : -1;
     const int k_new = own_new ? (jl - first) / W : -1;
@@ -798,7 +799,40 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
 
     // block jb (positions 32 jb .. + 31); positions below lim are valid. An invalid block
     // id (read from block 0) is masked out by arithmetic, not skipped (see decode_mfma_kernel).
-    auto compute = [&](KvBlock32<D>& t, int jb, bool ok) {
+    auto compute = [&](KvBlock32<D>& t, int jb, bool ok) __attribute__((always_inline)) {
+        if constexpr (Append) {
+            if (subst && jb == jl) {   // wave-uniform: position off of block jl is the new token
+                // MFMA row r of product A holds position 8 (r / 4) + r % 4, of product B that
+                // + 4; V word h of the lanes with quad == off / 8 holds positions 8 quad + 4 h
+                // .. + 3. Bit masks, not selects between arrays (see decode_mfma_kernel).
+                const int off = (n - 1) % BS;
+                const int r = 4 * (off >> 3) + (off & 3);
+                const bool inb = (off & 7) >= 4;
+                const uint32_t ma = col == r && !inb ? 0xffffffffu : 0u;
+                const uint32_t mb = col == r && inb ? 0xffffffffu : 0u;
+#pragma unroll
+                for (int c = 0; c < NKL; ++c) {
+                    t.ka[c].x = (t.ka[c].x & ~ma) | (nk[c].x & ma);
+                    t.ka[c].y = (t.ka[c].y & ~ma) | (nk[c].y & ma);
+                    t.ka[c].z = (t.ka[c].z & ~ma) | (nk[c].z & ma);
+                    t.ka[c].w = (t.ka[c].w & ~ma) | (nk[c].w & ma);
+                    t.kb[c].x = (t.kb[c].x & ~mb) | (nk[c].x & mb);
+                    t.kb[c].y = (t.kb[c].y & ~mb) | (nk[c].y & mb);
+                    t.kb[c].z = (t.kb[c].z & ~mb) | (nk[c].z & mb);
+                    t.kb[c].w = (t.kb[c].w & ~mb) | (nk[c].w & mb);
+                }
+                const uint32_t sh = 8u * uint32_t(off & 3);
+                const bool vq = quad == (off >> 3);
+                const uint32_t mx = vq && !inb ? 0xffu << sh : 0u;
+                const uint32_t my = vq && inb ? 0xffu << sh : 0u;
+#pragma unroll
+                for (int c = 0; c < NPV; ++c) {
+                    const uint32_t code = (nv[c] & 0xffu) << sh;
+                    t.v[c].x = (t.v[c].x & ~mx) | (code & mx);
+                    t.v[c].y = (t.v[c].y & ~my) | (code & my);
+                }
+            }
+        }
         const int lim_b = ok ? lim : jb * BS;
         const int p0 = jb * BS + 8 * quad;   // this lane's 8 positions
         f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -876,7 +910,6 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
                 const int64_t phys_l = __builtin_amdgcn_readlane(tab, k_new - k0);
                 subst = slot >= 0 && phys_l >= 0 && phys_l < a.num_blocks &&
                         int64_t(slot) == phys_l * BS + (n - 1) % BS;
-                lim = subst ? n - 1 : n;
             }
         }
         KvBlock32<D> X, Y;
@@ -891,22 +924,6 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
             const int k2 = min(k + 2, cnt - 1);
             okX = load(X, k2);
             compute(Y, blk_of(k + 1), okY);
-        }
-    }
-
-    // the new token as a block whose only valid position is 0 (row 0 of product A)
-    if constexpr (Append) {
-        if (wave == w_new && subst) {
-            KvBlock32<D> t;
-#pragma unroll
-            for (int c = 0; c < NKL; ++c) {
-                t.ka[c] = col == 0 ? nk[c] : make_uint4(0, 0, 0, 0);
-                t.kb[c] = make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int c = 0; c < NPV; ++c) t.v[c] = make_uint2(quad == 0 ? nv[c] & 0xffu : 0u, 0u);
-            lim = 1;
-            compute(t, 0, true);
         }
     }
 

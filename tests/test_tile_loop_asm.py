@@ -143,13 +143,16 @@ def test_tile_loop_keeps_loads_in_flight(asm16, pattern):
             assert ld.endswith(" nt"), (nm, ld)   # the non-temporal hint
 
 
-def test_decode_kernels_keep_tiles_in_registers(asm16):
+@pytest.mark.parametrize("src", ["decode.hip", "decode_bs8.hip", "decode_bs32.hip"])
+def test_decode_kernels_keep_tiles_in_registers(src, asm16):
     """No decode kernel uses scratch memory: tiles, queries and the new token's rows stay in
     registers (a select between two such arrays, for one, would make the compiler keep
-    both in scratch and load through a pointer, with a wait for every tile)."""
-    names = re.findall(r"^(_ZN3pkv\w*decode\w+):", asm16, re.M)
+    both in scratch and load through a pointer, with a wait for every tile). Every block
+    size's translation unit, the FP8 whole-block kernel included."""
+    asm = asm16 if src == "decode.hip" else _asm(src)
+    names = re.findall(r"^(_ZN3pkv\w*decode\w+):", asm, re.M)
     assert names
     for nm in names:
-        i = asm16.index(nm + ":")
-        m = re.search(r"ScratchSize: (\d+)", asm16[i:])
+        i = asm.index(nm + ":")
+        m = re.search(r"ScratchSize: (\d+)", asm[i:])
         assert m and m.group(1) == "0", (nm, m.group(1) if m else None)
