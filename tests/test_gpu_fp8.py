@@ -32,6 +32,8 @@ W8 = workloads.WORKLOADS["llama8b_fp8"]
 
 SHAPES = {
     "8b-bf16-fp8": dataclasses.replace(W8, num_blocks=0),
+    # 32-token blocks: the whole-block kernel in the single pass and partitions of 64 tokens
+    "8b-bf16-fp8-bs32": dataclasses.replace(W8, num_blocks=0, block_size=32),
     "f16-d64-g8-fp8": dataclasses.replace(W8, dtype="f16", num_heads=16, num_kv_heads=2,
                                           head_dim=64, k_scale=0.031, v_scale=0.0097),
     "bf16-d128-g16-fp8": dataclasses.replace(W8, num_heads=32, num_kv_heads=2, k_scale=0.02,
@@ -231,8 +233,8 @@ def _run(gb, w, P, out_dtype, append):
     out = gpu_batch.guarded_full((B, Hq, d), float("nan"), out_dtype, dev)
     parts = None
     if P != 0:
-        parts = gpu_batch.guarded_partials(B, Hq, d, pkv.max_partitions_for(gb.tables.shape[1], P),
-                                           dev)
+        parts = gpu_batch.guarded_partials(B, Hq, d, pkv.max_partitions_for(gb.tables.shape[1], P,
+                                                                            w.block_size), dev)
     pkv.decode(out, gb.q, gb.k_cache, gb.v_cache, gb.tables_d, gb.lens_d, w.scale, P, parts,
                append=append, kv_scales=(w.k_scale, w.v_scale))
     gpu_batch.check_guards()
@@ -240,7 +242,7 @@ def _run(gb, w, P, out_dtype, append):
 
 
 @pytest.mark.parametrize("P", [0, 64, AUTO], ids=["single", "p64", "auto"])
-@pytest.mark.parametrize("name", ["8b-bf16-fp8", "f16-d64-g8-fp8"])
+@pytest.mark.parametrize("name", ["8b-bf16-fp8", "f16-d64-g8-fp8", "8b-bf16-fp8-bs32"])
 def test_fp8_fused_append_equals_two_calls_and_oracle(name, P, device):
     w = SHAPES[name]
     ob = paged_batch.build(w, lens=RAGGED)
