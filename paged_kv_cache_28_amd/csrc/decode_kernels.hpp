@@ -331,26 +331,33 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     // the wave that stores the row, quantises just those (quantize_new, once its first
     // tiles are on the way); the codes meet in the wave's LDS slice, from which every
     // lane takes the ones it holds in the tile layout (nk, nv). Quantising whole K groups
-    // per lane instead cost 40 divisions per lane.
+    // per lane instead cost 40 divisions per lane. Only the wave that stores the row loads
+    // it (load_new_rows, once the length has named that wave).
     int slot = -1;
     uint4 nk[Append ? NKL : 1];
     uint32_t nv[Append ? NPV : 1];
     uint32_t nkr = 0, nvr = 0;   // FP8: D/64 raw 16-bit elements each
-    if constexpr (Append) {
-        slot = a.slot_mapping[b];
-        const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
-                               int64_t(g) * D;
-        const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
-                               int64_t(g) * D;
-        if constexpr (F8) {
-            load_new_row_fp8<D>(krow, vrow, lane, nkr, nvr);
-        } else {
 #pragma unroll
-            for (int c = 0; c < NKL; ++c) nk[c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * quad);
+    for (int c = 0; c < (Append ? NKL : 1); ++c) nk[c] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c + col];
+    for (int c = 0; c < (Append ? NPV : 1); ++c) nv[c] = 0;
+    if constexpr (Append) slot = a.slot_mapping[b];
+    auto load_new_rows = [&]() __attribute__((always_inline)) {
+        if constexpr (Append) {
+            const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
+                                   int64_t(g) * D;
+            const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + int64_t(b) * a.new_v_stride +
+                                   int64_t(g) * D;
+            if constexpr (F8) {
+                load_new_row_fp8<D>(krow, vrow, lane, nkr, nvr);
+            } else {
+#pragma unroll
+                for (int c = 0; c < NKL; ++c) nk[c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * quad);
+#pragma unroll
+                for (int c = 0; c < NPV; ++c) nv[c] = vrow[16 * c + col];
+            }
         }
-    }
+    };
     auto quantize_new = [&]() __attribute__((always_inline)) {
         if constexpr (Append && F8)   // in this wave's slice of sm_o, free until the merge
             quantize_new_row_fp8<T, D>(a, reinterpret_cast<uint8_t*>(sm_o + wave * G * D), lane,
@@ -383,13 +390,16 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     const bool own_new = jl >= blk_begin && jl < blk_end;   // this workgroup holds tile jl
     const int w_new = own_new ? (PW ? wave : (jl - blk_begin) % W) : -1;
     const int k_new = own_new ? (jl - first) / STEP : -1;   // jl's index in w_new's list
-    // The row stores, issued right after w_new's first tile loads: those loads are older,
-    // so their wait does not include the stores, and the stores complete while the wave
-    // streams (issued at the end of the stream they would lengthen the kernel's tail).
+    if (wave == w_new) load_new_rows();   // wave-uniform
+    // The row stores, issued by w_new after its last tile. Stores and loads share one
+    // completion counter on this GPU, counted in issue order, so every later tile's wait
+    // would include stores issued ahead of its loads; scattered over 128 V rows (one
+    // element each) they take microseconds to complete. Issued right after the first tile
+    // loads they held up the rest of the wave's stream (8B batch on MI355X: 55.8 us; after
+    // the last tile: 53.2 us; with no stores at all: 51.3 us).
     auto store_new_row = [&]() __attribute__((always_inline)) {
         if constexpr (Append) {
             if (wave != w_new) return;
-            quantize_new();   // FP8: the codes, also those put into tile jl's registers
             if (slot < 0 || int64_t(slot) >= a.num_blocks * BS) return;
             const int64_t tile = int64_t(slot / BS) * a.num_kv_heads + g;
             const int off = slot % BS;
@@ -572,7 +582,7 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
         };
         okX = ld(X, 0);
         if constexpr (NB == 3) okY = ld(Y, 1);
-        if (k0 == 0) store_new_row();
+        if (k0 == 0 && wave == w_new) quantize_new();   // FP8: the codes, for tile jl too
         if constexpr (NB == 1) {
             for (int k = 0; k < cnt; ++k) {
                 if (k > 0) okX = ld(X, k);
@@ -599,6 +609,8 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
             }
         }
     }
+
+    store_new_row();
 
     // lanes l, l^16, l^32, l^48 hold the same head: total its running sum
     lsum += __shfl_xor(lsum, 16, 64);
@@ -741,10 +753,10 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
     const bool own_new = jl >= blk_begin && jl < blk_end;
     const int w_new = own_new ? (jl - blk_begin) % W : -1;
     const int k_new = own_new ? (jl - first) / W : -1;
+    // the row stores, by w_new after its last block (see decode_mfma_kernel)
     auto store_new_row = [&]() __attribute__((always_inline)) {
         if constexpr (Append) {
             if (wave != w_new) return;
-            quantize_new();
             if (slot < 0 || int64_t(slot) >= a.num_blocks * BS) return;
             const int64_t tile = int64_t(slot / BS) * a.num_kv_heads + g;
             const int off = slot % BS;
@@ -915,7 +927,7 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
         KvBlock32<D> X, Y;
         auto blk_of = [&](int k) { return first + (k0 + k) * W; };
         bool okX = load(X, 0), okY = false;
-        if (k0 == 0) store_new_row();
+        if (k0 == 0 && wave == w_new) quantize_new();   // the codes, for block jl too
         for (int k = 0; k < cnt; k += 2) {
             const int k1 = min(k + 1, cnt - 1);
             okY = load(Y, k1);
@@ -926,6 +938,8 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
             compute(Y, blk_of(k + 1), okY);
         }
     }
+
+    store_new_row();
 
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
