@@ -509,9 +509,11 @@ int paged_attention_decode_noalloc(void* out, const void* q, int64_t q_stride, c
  *            (q_stride >= num_heads * head_dim, a multiple of 8), heads dense in a row.
  *   q_start: device int32 [num_seqs + 1], q_start[0] = 0, non-decreasing;
  *            L_b <= max_q_len (rows past max_q_len are not computed).
- *   out:     device [q_start[num_seqs]][num_heads][head_dim], out_dtype (in_dtype or F32).
+ *   out:     device [q_start[num_seqs]][num_heads][head_dim], out_dtype (in_dtype or F32),
+ *            16-byte aligned.
  *   caches, block_tables, seq_lens as paged_attention_decode (16-bit caches).
- * Supported: head_dim 64 or 128, num_heads / num_kv_heads <= 16.
+ * Supported: head_dim 64 or 128, num_heads / num_kv_heads <= 16. The launch stages 64 KiB
+ * (head_dim 128) or 32 KiB (64) of LDS per workgroup.
  * Errors: EINVAL, ENOTSUP (dtypes, head_dim, group size), EHIP. */
 int paged_attention_prefill(void* out, const void* q, int64_t q_stride, const int32_t* q_start,
                             const void* k_cache, const void* v_cache, const int32_t* block_tables,

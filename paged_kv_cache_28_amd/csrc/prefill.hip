@@ -7,40 +7,29 @@
 // is a dense contraction, so it runs on the matrix cores.
 //
 // Work decomposition: one workgroup of 4 waves per (query tile, KV head, sequence). The
-// 16 columns of the matrix products are (query token, head of the GQA group) pairs; a wave
-// holds NC column tiles (16 * NC columns = 16 * NC / G query tokens), so every K/V pair it
-// loads into registers feeds NC x 16 columns. The 4 waves take the key pairs round-robin
-// with no barrier in the loop, each with its own online softmax per column, and merge
-// through LDS one column tile at a time at the end. Causal mask: each lane masks with its
-// own column's limit (keys at positions up to the query's), and a column tile whose queries
-// see none of a pair skips it. (Staging the tiles in LDS for all four waves measured
-// slower: the barrier per block kept the waves in lockstep.)
+// 16 columns of the matrix products are (query token, head of the GQA group) pairs; each
+// wave owns NC column tiles of its own (16 * NC columns, 16 * NC / G query tokens), so a
+// workgroup covers 4 * 16 * NC columns. The context is walked in stages of 64 keys that
+// the workgroup stages in LDS once and all four waves read: each K/V byte fetched from L2
+// feeds 4 * 16 * NC columns. (A design in which the 4 waves shared one set of columns and
+// split the keys fed each fetched byte to 16 * NC columns only; it needed about the whole
+// L2 bandwidth to reach 23% of the matrix-core peak.) A stage is loaded into registers by
+// all 256 threads while the previous one is computed, and written to the other of two LDS
+// buffers after it: one barrier per stage. Each wave keeps its own online softmax per
+// column and writes its rows itself.
 //
-// Keys are walked in pairs of 32 consecutive positions, whatever the block size BS (8, 16
-// or 32; a template parameter): a pair is four blocks, two blocks or one block. Per pair
-// and column tile:
+// Per pair of 32 keys of a stage and column tile:
 //   S_A^T, S_B^T[16 keys][16 cols] = K_rows x Q^T          (16x16x32, d/32 steps each)
 //   O^T[d][16 cols] += V^T[d][32 keys] x P^T[32 keys][16 cols]   (16x16x32, d/16 steps)
 // The two QK products read their K rows in a permuted order (row r of A: position
 // 8 (r / 4) + r % 4 of the pair; of B: that + 4), so that lane l holds the logits of the
 // 8 consecutive positions 8 (l/16) .. + 7, which are its 8 k-slots of the PV step in both
-// operands: P stays in the lanes that produced it, and the lane's V operand is one 16-byte
-// load of those positions of one dimension row. On gfx950 the 16x16x32 instruction issues
-// at the rate of the 16x16x16 one with twice the work, so pairs halve the PV issue time. P
-// is split in a high and a low bf16/fp16 part as in decode.
-//
-// Each pair is loaded and then used (no second pair in flight): with NC = 2 that keeps the
-// wave at two per SIMD, and the other wave's math covers a pair's load. The vector-ALU work
-// per pair bounds the kernel as much as anything (64 more multiplies per pair cost 7%), so
-// the V rows past the real ones are zeroed once per pair and only in a pair that has any,
-// and the softmax weights need no per-element select. Measured on the 30,000-token chunked
-// prefill (TFLOP/s): this form 578-585; the masking per column tile and per element
-// 544-547; two 16-token tiles W tiles apart with 8-byte V loads (24 loads per pair instead
-// of 16) a further 1.5-3% less; the next pair's K and V loads issued into the same
-// registers once the QK (resp. PV) products are done, no gain; double-buffered pairs (one
-// wave per SIMD) 354; single blocks with the 16x16x16 product 460; NC = 1 (three waves per
-// SIMD) 348; NC = 4 with Q^T in registers 361, in LDS 531 (against 540); tiles staged in
-// LDS for the workgroup 290.
+// operands: P stays in the lanes that produced it, and the lane's V operand is 8
+// consecutive positions of one dimension row. P is split in a high and a low bf16/fp16
+// part as in decode. The LDS layout is that of the operands, whatever the block size:
+// K as [pair][product][16-byte dim group][MFMA row], V as [pair][8-key group][dim], so
+// every operand read covers 128 contiguous bytes per 8 lanes, and the arithmetic (so the
+// result) is the same for 8, 16 and 32 tokens per block.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -69,68 +58,105 @@ struct PrefillArgs {
     int32_t group;
     int32_t max_blocks;
     int32_t max_len;           // max_blocks * block size
-    int32_t max_tiles;         // ceil(max_len / 16)
-    float scale_log2;
+    float scale_log2;          // |scale| log2(e), at least the smallest normal float
+    uint32_t q_sign;           // 0x80008000 when scale < 0: the queries' signs are flipped
 };
 
 constexpr int kPrefillWaves = 4;
+constexpr int kPrefillNC = 2;       // column tiles per wave
+constexpr int kStageKeys = 64;      // keys per LDS stage (two pairs)
 
+// One LDS stage: K and V of 64 keys, D dims, 16-bit elements; two stages in flight.
+template <int D>
+__host__ __device__ constexpr size_t prefill_stage_bytes() {
+    return size_t(2) * kStageKeys * D * 2;
+}
 template <int D>
 __host__ __device__ constexpr size_t prefill_lds_bytes() {
-    return sizeof(float) * (2 * kPrefillWaves * 16 + size_t(kPrefillWaves) * 16 * D);
+    return 2 * prefill_stage_bytes<D>();
 }
 
-template <typename T, int D, typename OutT, int NC, int BS>
-__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs a) {
-    constexpr int W = kPrefillWaves;
-    constexpr int NQK = D / 32, NPV = D / 16;
-    extern __shared__ float lds[];
-    float* sm_m = lds;                  // [W][16]
-    float* sm_l = lds + W * 16;         // [W][16]
-    float* sm_o = lds + 2 * W * 16;     // [W][16][D]
+// Query tokens per wave: the 16 * NC columns hold whole tokens' G heads.
+__host__ __device__ constexpr int prefill_wave_tokens(int G) { return 16 * kPrefillNC / G; }
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// max of two logits, which are never NaN here (masked keys are -inf): the median of
+// (a, b, +inf) is their maximum, and unlike fmaxf it needs no quieting of its inputs
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+// the maximum over the four lanes l % 16 + 16 k (the rows of one column)
+__device__ __forceinline__ float rows_max(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = vmax(__builtin_bit_cast(float, (unsigned)r16[0]), __builtin_bit_cast(float, (unsigned)r16[1]));
+    const unsigned w = __builtin_bit_cast(unsigned, y);
+    auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return vmax(__builtin_bit_cast(float, (unsigned)r32[0]), __builtin_bit_cast(float, (unsigned)r32[1]));
+}
+
+template <typename T, int D, typename OutT, int BS>
+__global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
+    constexpr int W = kPrefillWaves, NC = kPrefillNC;
+    constexpr int NQK = D / 32, NPV = D / 16;
+    constexpr int NG = D / 8;                           // 16-byte K dim groups
+    constexpr int NLD = kStageKeys * D * 2 / 16 / (W * 64);   // 16-byte loads per thread, K and V each
+    constexpr int KCH = kStageKeys * NG;                // K chunks per stage
+    constexpr int STAGE_CH = 2 * KCH;                   // K + V chunks per stage
+    static_assert(NLD >= 1 && (NG * BS) % 64 == 0, "a load instruction stays in one block");
+    extern __shared__ uint4 lds4[];                     // [2][STAGE_CH] 16-byte chunks
+
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = lane & 15, quad = lane >> 4;
     // query tiles in reverse: under the causal mask a later tile sees more keys, so the
     // longest workgroups are dispatched first and the short ones fill the tail
     const int qt = int(gridDim.x) - 1 - int(blockIdx.x), g = blockIdx.y, b = blockIdx.z;
     const int G = a.group;
-    const int QT = 16 * NC / G;         // query tokens of this workgroup
+    const int TW = prefill_wave_tokens(G);              // query tokens per wave
+    const int QT = W * TW;                              // per workgroup
     const int q0 = a.q_start[b];
     const int L = a.q_start[b + 1] - q0;
     const int t0 = qt * QT;
     if (t0 >= L) return;
-    const int tcount = min(QT, L - t0);
     int n = a.seq_lens[b];
     n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    const int tw0 = t0 + wave * TW;                     // this wave's first token
+    // keys any query of the workgroup sees: up to the last valid token's position
+    const int wg_last = min(QT, L - t0) - 1;
+    const int key_end = max(0, min(n, n - L + t0 + wg_last + 1));
 
     // This lane's column in each column tile: query token, head, causal limit (keys
     // below it are visible), and its Q^T operand.
-    int lim[NC];
-    int tile_lim[NC];   // largest limit of the column tile (wave-uniform)
+    int lim[NC], tile_lim[NC], tile_min[NC];
     uint4 qf[NC][NQK];
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
         const int c = 16 * ct + col;
         const int tok = c / G, hg = c - tok * G;
-        const bool valid = tok < tcount;
-        const int pos = n - L + t0 + tok;          // the query's position in its sequence
+        const bool valid = tok < TW && tw0 + tok < L;
+        const int pos = n - L + tw0 + tok;               // the query's position in its sequence
         lim[ct] = valid ? max(0, min(pos + 1, n)) : 0;
         const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                               int64_t(q0 + t0 + (valid ? tok : 0)) * a.q_stride +
+                               int64_t(q0 + (valid ? tw0 + tok : 0)) * a.q_stride +
                                int64_t(g * G + hg) * D;
 #pragma unroll
-        for (int s = 0; s < NQK; ++s)
+        for (int s = 0; s < NQK; ++s) {
             qf[ct][s] = valid ? *reinterpret_cast<const uint4*>(qrow + q_dim<false>(s, quad))
                               : make_uint4(0, 0, 0, 0);
-        int m = lim[ct];
+            qf[ct][s].x ^= a.q_sign;
+            qf[ct][s].y ^= a.q_sign;
+            qf[ct][s].z ^= a.q_sign;
+            qf[ct][s].w ^= a.q_sign;
+        }
+        int hi = lim[ct], lo = valid ? lim[ct] : 0x7fffffff;
 #pragma unroll
-        for (int k = 1; k < 16; k <<= 1) m = max(m, __shfl_xor(m, k, 64));
-        tile_lim[ct] = __builtin_amdgcn_readfirstlane(m);
+        for (int k = 1; k < 16; k <<= 1) {
+            hi = max(hi, __shfl_xor(hi, k, 64));
+            lo = min(lo, __shfl_xor(lo, k, 64));
+        }
+        tile_lim[ct] = __builtin_amdgcn_readfirstlane(hi);   // largest limit of the tile
+        tile_min[ct] = __builtin_amdgcn_readfirstlane(lo);   // smallest (valid columns)
     }
-    int key_end = 0;   // keys any column of the workgroup sees
+    int wave_end = 0;   // keys any column of this wave sees
 #pragma unroll
-    for (int ct = 0; ct < NC; ++ct) key_end = max(key_end, tile_lim[ct]);
+    for (int ct = 0; ct < NC; ++ct) wave_end = max(wave_end, tile_lim[ct]);
 
     f32x4 acc[NC][NPV];
     float m_ref[NC], lsum[NC];
@@ -143,124 +169,149 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
     }
     constexpr float kSlack = 8.0f;   // lazy reference point, as in the decode kernel
 
+    // ---- stage loads: thread t issues load i of K and of V at linear chunk t + 256 i of
+    // the stage, in the cache's own order (a block's K tile [NG][BS][16 B], then its V tile
+    // [D][BS] as 16-byte runs of 8 positions), so consecutive lanes read consecutive
+    // bytes; each instruction stays inside one block (a wave-uniform id). The chunk goes
+    // to its place in the operand layout.
     const char* kbase = static_cast<const char*>(a.k_cache);
     const char* vbase = static_cast<const char*>(a.v_cache);
-    const int64_t tile_bytes = int64_t(D) * BS * 2;   // one block of one KV head
+    const int64_t tile_bytes = int64_t(D) * BS * 2;     // one block of one KV head
     const int32_t* table = a.block_tables + int64_t(b) * a.max_blocks;
-
-    // Keys are walked in pairs of 32 consecutive positions (pair m: 32m .. 32m + 31, the
-    // 16-token tiles 2m and 2m + 1), each a 16x16x32 PV step. The QK products read their
-    // K rows in a permuted order so that each lane ends up holding the logits of 8
-    // consecutive positions: MFMA row r of product A reads position 8 (r / 4) + r % 4 of
-    // the pair, product B that position + 4, so lane (quad, col) gets positions
-    // 8 quad .. 8 quad + 3 from A and 8 quad + 4 .. + 7 from B. Its V operand is then one
-    // 16-byte load of those 8 positions of one dimension row, half the V loads of two
-    // 16-token tiles. 8 consecutive positions never cross a block (BS >= 8).
-    constexpr int NB = 32 / BS;                         // blocks per pair (4, 2, 1)
-    const int ra = 8 * (col >> 2) + (col & 3), rb = ra + 4, rv = 8 * quad;
-    auto blk_of = [](int t) { return t / BS; };
-    auto row_of = [](int t) { return t % BS; };
-    int ids[NB];   // block ids of this segment: lane k holds pair k's
-
-    struct Pair {
-        uint4 ka[NQK];   // K rows of product A, QK steps 0 .. NQK - 1
-        uint4 kb[NQK];   // product B
-        uint4 v[NPV];    // positions 8 quad .. + 7 of dimension 16 c + col
+    const uint32_t nb_lim = block_limit(a.num_blocks);
+    constexpr int SB = kStageKeys / BS;                 // blocks per stage
+    const int tid = int(threadIdx.x);
+    // ids of stage s's blocks: lane k < SB holds block k's (0 for an invalid or absent id:
+    // a safe address; such rows break the precondition)
+    auto stage_ids = [&](int s) {
+        const int e = s * SB + lane;
+        const int id = lane < SB && e < a.max_blocks ? table[e] : 0;
+        return uint32_t(id) < nb_lim ? id : 0;
+    };
+    // native vectors, not uint4: copying the struct type between global, private and LDS
+    // memory compiles to copies that keep the staging registers in scratch memory
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 kr[NLD], vr[NLD];
+    auto issue = [&](int ids) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int lin = tid + W * 64 * i;
+            const int bl = __builtin_amdgcn_readfirstlane(lin / (NG * BS));   // block in the stage
+            const int within = lin - (lin / (NG * BS)) * (NG * BS);
+            const int id = __builtin_amdgcn_readlane(ids, bl);
+            const int64_t tb = (int64_t(id) * a.num_kv_heads + g) * tile_bytes;
+            kr[i] = *reinterpret_cast<const u32x4*>(kbase + tb + int64_t(within) * 16);
+            vr[i] = *reinterpret_cast<const u32x4*>(vbase + tb + int64_t(within) * 16);
+        }
+    };
+    auto store = [&](uint4* dst) __attribute__((always_inline)) {
+        u32x4* buf = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int lin = tid + W * 64 * i;
+            const int bl = lin / (NG * BS), within = lin - bl * (NG * BS);
+            {   // K chunk: group gi, row -> key kl of the stage
+                const int gi = within / BS, row = within - gi * BS;
+                const int kl = bl * BS + row, m = kl >> 5, k32 = kl & 31;
+                const int ab = (k32 >> 2) & 1, r = ((k32 >> 3) << 2) | (k32 & 3);
+                buf[((m * 2 + ab) * NG + gi) * 16 + r] = kr[i];
+            }
+            {   // V chunk: dim d, 8 positions from row 8h -> 8-key group of the stage
+                const int d = within / (BS / 8), h = within - d * (BS / 8);
+                const int kl = bl * BS + 8 * h, m = kl >> 5, o = (kl & 31) >> 3;
+                buf[KCH + (m * 4 + o) * D + d] = vr[i];
+            }
+        }
     };
 
-    // Issue the loads of segment pair k. Returns bit i set if the pair's block i has a
-    // valid id; an invalid id is replaced by a safe address and its rows masked.
-    auto load_pair = [&](Pair& t, int k) __attribute__((always_inline)) -> int {
-        int okm = 0;
-        auto id = [&](int i) -> int32_t {   // block i's id, or 0 (safe) if invalid
-            const int32_t p = __builtin_amdgcn_readlane(ids[i], k);
-            const bool ok = p >= 0 && int64_t(p) < a.num_blocks;
-            okm |= int(ok) << i;
-            return ok ? p : 0;
-        };
-        // separate variables, not an array: the compiler turns selects among array
-        // elements into an indexed scratch access
-        const int32_t p0 = id(0);
-        const int32_t p1 = NB > 1 ? id(1) : 0;
-        const int32_t p2 = NB > 2 ? id(2) : 0;
-        const int32_t p3 = NB > 2 ? id(3) : 0;
-        auto pick = [&](int bi) {   // the id of pair block bi (lane-varying)
-            const int32_t lo = (bi & 1) ? p1 : p0;
-            const int32_t hi = (bi & 1) ? p3 : p2;
-            const int32_t p = NB == 1 ? p0 : NB == 2 ? lo : ((bi & 2) ? hi : lo);
-            return (int64_t(p) * a.num_kv_heads + g) * tile_bytes;
-        };
-        const char* kA = kbase + pick(blk_of(ra));
-        const char* kB = kbase + pick(blk_of(rb));
-        const char* vt = vbase + pick(blk_of(rv));
-        const int rowa = row_of(ra), rowb = row_of(rb), rowv = row_of(rv);
+    // ---- one pair of 32 keys (pair m of the stage in buf), both column tiles of the wave
+    // in one block of straight-line code (one masking decision and one rescale branch per
+    // pair), so that the scheduler can interleave one tile's softmax with the other's
+    // matrix products. A tile whose queries see none of the pair goes through the masked
+    // form, which gives it zero weights.
+    auto compute_pair = [&](const uint4* buf, int kp, int m) __attribute__((always_inline)) {
+        uint4 ka[NQK], kb[NQK], v[NPV];
 #pragma unroll
         for (int c = 0; c < NQK; ++c) {
-            t.ka[c] = *reinterpret_cast<const uint4*>(kA + ((4 * c + quad) * BS + rowa) * 16);
-            t.kb[c] = *reinterpret_cast<const uint4*>(kB + ((4 * c + quad) * BS + rowb) * 16);
+            ka[c] = buf[((m * 2 + 0) * NG + 4 * c + quad) * 16 + col];
+            kb[c] = buf[((m * 2 + 1) * NG + 4 * c + quad) * 16 + col];
         }
 #pragma unroll
-        for (int c = 0; c < NPV; ++c)
-            t.v[c] = *reinterpret_cast<const uint4*>(vt + ((16 * c + col) * BS + rowv) * 2);
-        return okm;
-    };
-
-    auto compute_pair = [&](Pair& t, int m, int okm) __attribute__((always_inline)) {
-        const int p0 = 32 * m + 8 * quad;   // first of this lane's 8 positions
-        // positions below nv are real: past the sequence, or in a block whose id is
-        // invalid, they are not
-        const int nv = ((okm >> blk_of(rv)) & 1) ? n : 0;
-        // V rows that are not real may hold anything: zeroed once per pair, and only in a
-        // pair that has such rows (the last pair of a sequence or an invalid block)
-        if (__builtin_amdgcn_ballot_w64(p0 + 8 > nv)) {
+        for (int c = 0; c < NPV; ++c) v[c] = buf[KCH + (m * 4 + quad) * D + 16 * c + col];
+        const int p0 = kp + 8 * quad;   // first of this lane's 8 positions
+        // V rows past the sequence may hold anything: zeroed, only in a pair that has such
+        // rows, so that their zero weights give zero products
+        if (kp + 32 > n) {
             auto keep = [&](int q) {
-                return (q < nv ? 0x0000ffffu : 0u) | (q + 1 < nv ? 0xffff0000u : 0u);
+                return (q < n ? 0x0000ffffu : 0u) | (q + 1 < n ? 0xffff0000u : 0u);
             };
             const uint32_t k0 = keep(p0), k1 = keep(p0 + 2), k2 = keep(p0 + 4), k3 = keep(p0 + 6);
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
-                t.v[c].x &= k0;
-                t.v[c].y &= k1;
-                t.v[c].z &= k2;
-                t.v[c].w &= k3;
+                v[c].x &= k0;
+                v[c].y &= k1;
+                v[c].z &= k2;
+                v[c].w &= k3;
             }
         }
+        f32x4 sa[NC], sb[NC];
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            if (32 * m >= tile_lim[ct]) continue;   // no query of this tile sees the pair
-            const int lv = min(lim[ct], nv);
-            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+            sa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NQK; ++c) {
-                sa = Mfma<T>::qk(t.ka[c], qf[ct][c], sa);
-                sb = Mfma<T>::qk(t.kb[c], qf[ct][c], sb);
+                sa[ct] = Mfma<T>::qk(ka[c], qf[ct][c], sa[ct]);
+                sb[ct] = Mfma<T>::qk(kb[c], qf[ct][c], sb[ct]);
             }
-            float x[8];
+        }
+        // raw logits (scale applied below): the causal diagonal, the sequence end and tiles
+        // that see none of the pair take -inf per key
+        bool masked = false;
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) masked |= kp + 32 > tile_min[ct] || kp >= tile_lim[ct];
+        float x[NC][8], bm[NC];
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[e] = p0 + e < lv ? sa[e] * a.scale_log2 : -INFINITY;
-                x[4 + e] = p0 + 4 + e < lv ? sb[e] * a.scale_log2 : -INFINITY;
+                x[ct][e] = sa[ct][e];
+                x[ct][4 + e] = sb[ct][e];
             }
-            const float bm = max_over_rows(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
-            const bool move = bm > m_ref[ct] + kSlack;
-            if (__builtin_amdgcn_ballot_w64(move)) {
+            if (masked) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[ct][e] = p0 + e < lim[ct] ? x[ct][e] : -INFINITY;
+            }
+            bm[ct] = rows_max(vmax(vmax(vmax(x[ct][0], x[ct][1]), vmax(x[ct][2], x[ct][3])),
+                                   vmax(vmax(x[ct][4], x[ct][5]), vmax(x[ct][6], x[ct][7])))) *
+                     a.scale_log2;
+        }
+        bool any_move = false;
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) any_move |= bm[ct] > m_ref[ct] + kSlack;
+        if (__builtin_amdgcn_ballot_w64(any_move)) {
+#pragma unroll
+            for (int ct = 0; ct < NC; ++ct) {
                 // a lane that keeps its reference keeps factor 1 (also one whose column has
                 // seen no key yet, where m - m would be -inf - -inf)
-                const float mn = move ? bm : m_ref[ct];
+                const bool move = bm[ct] > m_ref[ct] + kSlack;
+                const float mn = move ? bm[ct] : m_ref[ct];
                 const float alpha = move ? exp2_fast(m_ref[ct] - mn) : 1.0f;
                 lsum[ct] *= alpha;
 #pragma unroll
                 for (int c = 0; c < NPV; ++c) acc[ct][c] *= alpha;
                 m_ref[ct] = mn;
             }
-            // exp2(-inf - m) is 0 for a finite m; m is -inf only while the column has seen
-            // no real key, and then every x is -inf too, so one select per lane (not per
-            // element) keeps those weights 0 instead of exp2(-inf + inf)
-            const float mref = m_ref[ct] == -INFINITY ? 0.f : m_ref[ct];
+        }
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+            // 2^(x scale - m): 0 for x = -inf and a finite m; m is -inf only while the
+            // column has seen no real key, and then every x is -inf too, so one select per
+            // lane (not per element) keeps those weights 0 instead of exp2(-inf + inf)
+            const float nm = m_ref[ct] == -INFINITY ? 0.f : -m_ref[ct];
             float pe[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(x[e] - mref);
+            for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(__builtin_fmaf(x[ct][e], a.scale_log2, nm));
             lsum[ct] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
             uint16_t hi[8], lo[8];
 #pragma unroll
@@ -275,81 +326,66 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
                                          uint32_t(lo[6]) | (uint32_t(lo[7]) << 16));
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
-                acc[ct][c] = Mfma<T>::qk(t.v[c], phi, acc[ct][c]);
-                acc[ct][c] = Mfma<T>::qk(t.v[c], plo, acc[ct][c]);
+                acc[ct][c] = Mfma<T>::qk(v[c], phi, acc[ct][c]);
+                acc[ct][c] = Mfma<T>::qk(v[c], plo, acc[ct][c]);
             }
         }
     };
 
-    // This wave's pairs: wave, wave + W, ...; segments of 64 pairs (block ids one pair per
-    // lane), each pair loaded and then used.
-    const int npairs = (key_end + 31) >> 5;
-    const int nmine = wave < npairs ? (npairs - wave + W - 1) / W : 0;
-    for (int k0 = 0; k0 < nmine; k0 += 64) {
-        const int cnt = min(64, nmine - k0);
-        const int mp = wave + (k0 + lane) * W;   // this lane's pair
+    // ---- the stages: stage s + 1 is in flight in registers while stage s is computed from
+    // LDS, then written to the other buffer; one barrier per stage. The last stage loads
+    // itself again into the unused buffer: with no condition around the loads and the
+    // stores, the compiler keeps the staging registers in registers.
+    const int S = (key_end + kStageKeys - 1) / kStageKeys;
+    if (S > 0) {
+        int ids = stage_ids(0);
+        issue(ids);
+        ids = stage_ids(min(1, S - 1));
+        store(lds4);
+        __syncthreads();
+        for (int s = 0; s < S; ++s) {
+            const uint4* cur = lds4 + (s & 1) * STAGE_CH;
+            issue(ids);                                 // stage min(s + 1, S - 1)
+            ids = stage_ids(min(s + 2, S - 1));
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int bi = NB * mp + i;
-            ids[i] = lane < cnt && bi < a.max_blocks ? table[bi] : -1;
-        }
-        for (int k = 0; k < cnt; ++k) {
-            Pair t;
-            const int okm = load_pair(t, k);
-            compute_pair(t, wave + (k0 + k) * W, okm);
+            for (int m = 0; m < 2; ++m) {
+                const int kp = s * kStageKeys + 32 * m;
+                if (kp < wave_end) compute_pair(cur, kp, m);
+            }
+            store(lds4 + ((s + 1) & 1) * STAGE_CH);
+            __syncthreads();
         }
     }
 
-    // Merge the waves' states column tile by column tile and write the rows.
+    // ---- this wave's rows: lanes l, l^16, l^32, l^48 hold parts of the same column
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
         float ls = lsum[ct];
         ls += __shfl_xor(ls, 16, 64);
         ls += __shfl_xor(ls, 32, 64);
-        if (lane < 16) {
-            sm_m[wave * 16 + lane] = m_ref[ct];
-            sm_l[wave * 16 + lane] = ls;
+        const int c = 16 * ct + col;
+        const int tok = c / G, hg = c - tok * G;
+        if (tok >= TW || tw0 + tok >= L) continue;
+        const int64_t row = int64_t(q0 + tw0 + tok) * a.num_heads + g * G + hg;
+#pragma unroll
+        for (int c2 = 0; c2 < NPV; ++c2) {
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);   // a query before position 0 sees no key
+            if (ls > 0.f)
+                o = make_float4(acc[ct][c2][0] / ls, acc[ct][c2][1] / ls, acc[ct][c2][2] / ls,
+                                acc[ct][c2][3] / ls);
+            OutStore<OutT>::st4(a.out, row * D + 16 * c2 + 4 * quad, o);
         }
-#pragma unroll
-        for (int c = 0; c < NPV; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm_o[(wave * 16 + col) * D + 16 * c + 4 * quad + e] = acc[ct][c][e];
-        __syncthreads();
-        for (int i = threadIdx.x; i < 16 * D; i += W * 64) {
-            const int c = i / D, dim = i - c * D;
-            const int cc = 16 * ct + c;
-            const int tok = cc / G, hg = cc - tok * G;
-            if (tok >= tcount) continue;
-            float M = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * 16 + c]);
-            float o = 0.f;
-            if (M != -INFINITY) {   // a query before position 0 sees no key: zero row
-                float Lw = 0.f, O = 0.f;
-#pragma unroll
-                for (int w = 0; w < W; ++w) {
-                    const float f = exp2_fast(sm_m[w * 16 + c] - M);
-                    Lw += f * sm_l[w * 16 + c];
-                    O += f * sm_o[(w * 16 + c) * D + dim];
-                }
-                o = O / Lw;
-            }
-            const int64_t row = int64_t(q0 + t0 + tok) * a.num_heads + g * G + hg;
-            OutStore<OutT>::st(a.out, row * D + dim, o);
-        }
-        __syncthreads();
     }
 }
 
 template <typename T, int D, typename OutT, int BS>
 hipError_t launch_prefill(const PrefillArgs& a, int max_q_len, int num_kv_heads, int num_seqs,
                           hipStream_t s) {
-    constexpr int NC = 2;
-    const int qt_tokens = 16 * NC / a.group;
+    const int qt_tokens = kPrefillWaves * prefill_wave_tokens(a.group);
     const dim3 grid(unsigned((max_q_len + qt_tokens - 1) / qt_tokens), unsigned(num_kv_heads),
                     unsigned(num_seqs));
     const LaunchEvents ev = timer_events(PKV_TIMER_PREFILL);
-    hipExtLaunchKernelGGL((prefill_kernel<T, D, OutT, NC, BS>), grid, dim3(kPrefillWaves * 64),
+    hipExtLaunchKernelGGL((prefill_kernel<T, D, OutT, BS>), grid, dim3(kPrefillWaves * 64),
                           prefill_lds_bytes<D>(), s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
 }
@@ -412,9 +448,9 @@ extern "C" int paged_attention_prefill(void* out, const void* q, int64_t q_strid
     if (!out || !q || !q_start || !k_cache || !v_cache || !block_tables || !seq_lens)
         return fail(PKV_EINVAL, "%s: NULL pointer", who);
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
-         reinterpret_cast<uintptr_t>(v_cache)) & 15)
-        return fail(PKV_EINVAL, "%s: q and caches must be 16-byte aligned", who);
-    const int qt_tokens = 16 * 2 / G;
+         reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out)) & 15)
+        return fail(PKV_EINVAL, "%s: q, out and the caches must be 16-byte aligned", who);
+    const int qt_tokens = pkv::kPrefillWaves * pkv::prefill_wave_tokens(G);
     if ((int64_t(max_q_len) + qt_tokens - 1) / qt_tokens > 0x7fffffff)
         return fail(PKV_EINVAL, "%s: max_q_len too large", who);
     pkv::PrefillArgs a;
@@ -432,8 +468,12 @@ extern "C" int paged_attention_prefill(void* out, const void* q, int64_t q_strid
     a.group = G;
     a.max_blocks = max_blocks_per_seq;
     a.max_len = max_blocks_per_seq * block_size;
-    a.max_tiles = (a.max_len + 15) / 16;
-    a.scale_log2 = scale * 1.44269504088896340736f;
+    // the kernel takes the maximum of the raw logits and scales it, which needs a positive
+    // scale: a negative one flips the queries' signs instead (exact), and a zero one is
+    // raised to the smallest normal float (every weight still rounds to 1)
+    const float sl2 = scale * 1.44269504088896340736f;
+    a.scale_log2 = std::max(std::fabs(sl2), 1.17549435e-38f);
+    a.q_sign = sl2 < 0.f ? 0x80008000u : 0u;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err =
         block_size == 16
