@@ -30,6 +30,8 @@ SHAPES = {
                                       num_blocks=0),
     "bf16-d128-g16": dataclasses.replace(B8, num_heads=32, num_kv_heads=2, num_blocks=0),
     "bf16-d64-g1": dataclasses.replace(B8, num_heads=4, num_kv_heads=4, head_dim=64, num_blocks=0),
+    # a group that does not divide a wave's 32 columns: 5 tokens of 6 heads, 2 idle columns
+    "bf16-d128-g6": dataclasses.replace(B8, num_heads=24, num_kv_heads=4, num_blocks=0),
 }
 # (context length, chunk length) per sequence
 CASES = {
@@ -47,7 +49,7 @@ def device():
     return torch.device("cuda:0")
 
 
-def _run(w, spec, device, out_dtype=torch.float32, seed=0):
+def _run(w, spec, device, out_dtype=torch.float32, seed=0, scale=None):
     lens = [n for n, _ in spec]
     chunk = [L for _, L in spec]
     ob = paged_batch.build(w, lens=lens, seed_stream=seed)
@@ -55,10 +57,11 @@ def _run(w, spec, device, out_dtype=torch.float32, seed=0):
     q = workloads.draw_q(w, workloads.rng(w.seed, 60, seed), batch=int(sum(chunk)))
     qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
     out = torch.full(tuple(q.shape), float("nan"), dtype=out_dtype, device=device)
+    scale = w.scale if scale is None else scale
     pkv.paged_attention_prefill(out, q.to(device), torch.from_numpy(qs).to(device), gb.k_cache,
-                                gb.v_cache, gb.tables_d, gb.lens_d, w.scale, max(chunk))
+                                gb.v_cache, gb.tables_d, gb.lens_d, scale, max(chunk))
     torch.cuda.synchronize()
-    ref = oracle.prefill(q, qs, ob.k_cache, ob.v_cache, ob.tables, ob.lens, w.scale, w.dtype)
+    ref = oracle.prefill(q, qs, ob.k_cache, ob.v_cache, ob.tables, ob.lens, scale, w.dtype)
     return out, ref
 
 
@@ -78,6 +81,15 @@ def test_prefill_16bit_output(name, device):
     assert torch.equal(out_lp, out_32.to(tdt))
     got = out_lp.cpu().double().numpy()
     assert np.all(np.abs(got - ref) <= TOL[w.dtype] + 0.5 * _ulp(got, w.dtype))
+
+
+@pytest.mark.parametrize("factor", [-1.0, -0.5, 0.0])
+def test_prefill_scale_sign_and_zero(factor, device):
+    """A negative scale (the kernel flips the queries' signs and scales by |scale|) and a
+    zero one (every visible key weighs the same) against the oracle."""
+    w = SHAPES["bf16-d128-g4"]
+    out, ref = _run(w, CASES["chunks"], device, scale=factor * w.scale)
+    check_close(out.cpu().double().numpy(), ref, w.dtype, f"scale x {factor}")
 
 
 def test_a_prompt_in_chunks_equals_one_pass(device):
