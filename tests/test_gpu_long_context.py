@@ -1,18 +1,19 @@
-"""GPU parity at long contexts: the later block-id segments of every kernel.
+"""GPU parity at long contexts: the later block-id segments of the decode kernels, and
+the prefill kernel over contexts of up to 30,000 keys.
 
-Each wave of the decode and prefill kernels reads the block ids of its work one segment of
-64 at a time (one id per lane) and walks the segment before reading the next. A context
-reaches a wave's second segment past:
+Each wave of the decode kernels reads the block ids of its work one segment of 64 at a
+time (one id per lane) and walks the segment before reading the next. A context reaches a
+wave's second segment past:
   * 64 x 4 waves x 16 tokens = 4,096 tokens in the single-pass decode (and in a fixed
     partition longer than that);
-  * 64 x 4 x 32 = 8,192 tokens in the FP8 whole-block decode at 32 tokens per block;
-  * 64 x 4 x 32 = 8,192 keys in the prefill kernel (pairs of 32 positions).
+  * 64 x 4 x 32 = 8,192 tokens in the FP8 whole-block decode at 32 tokens per block.
 The lengths below put the newest token's tile in segment 1, 2 and 8 of the wave holding
 it, so the fused append's substitution of the new row (decided per segment) runs there
-too, and the prefill cases include the 30,000-token document of the chunked-prefill
-workload at its real chunk size ("vLLM Nedir? PagedAttention ile Production LLM
-Serving", section "Chunked prefill"; "Yerel LLM sistemlerinde backpressure ve
-ölçekleme", section "4. Prefill ve decode").
+too. The prefill kernel reads the ids of each 64-key stage as it stages it; its cases go
+past 8,192 keys and include the 30,000-token document of the chunked-prefill workload at
+its real chunk size ("vLLM Nedir? PagedAttention ile Production LLM Serving", section
+"Chunked prefill"; "Yerel LLM sistemlerinde backpressure ve ölçekleme", section
+"4. Prefill ve decode").
 
 Bars as everywhere: fp32 output within 2e-3 of the fp64 oracle and max|err| / max|ref|
 <= 1e-3; caches bit-exact.
@@ -155,7 +156,7 @@ def _prefill_rows(T, Hq, n_rows, seed):
 
 
 PREFILL_CASES = [
-    # (context, chunk): key_end crosses 8,192 keys; the 30,000-token document of the
+    # (context, chunk): contexts past 8,192 keys; the 30,000-token document of the
     # chunked-prefill workload at chunks 3 and 8 of 8 (3,750 queries each)
     (9000, 600), (8193, 64), (11250, 3750), (30000, 3750)]
 
