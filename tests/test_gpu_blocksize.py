@@ -90,6 +90,46 @@ def test_decode_matches_oracle(bs, name, P, device):
                     f"bs {bs} {name} P {P} lens {lens[:3]}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("P", [0, 16, AUTO], ids=["single", "p16", "auto"])
+def test_bs8_decode_over_caches_past_2gib(P, kv, device):
+    """At 8 tokens per block a 16-token tile spans two blocks, read through per-lane
+    addresses. Here the batch's blocks are spread over caches of just over 2 GiB each (ids
+    up to the top of the pool, so that tile offsets pass 31 bits and the two blocks of a
+    tile can lie more than 2 GiB apart), and the decode is checked against the oracle on
+    the compact pool."""
+    w = _w("bf16-d128-g4", 8)
+    w = _fp8(w) if kv == "fp8" else w
+    ob = paged_batch.build(w, lens=[1, 9, 17, 300, 700])
+    gb = gpu_batch.build(ob, device)
+    per_block = int(np.prod(gb.k_cache.shape[1:])) * gb.k_cache.element_size()
+    nb_big = (1 << 31) // per_block + 4099
+    assert nb_big * per_block > (1 << 31)
+    nb = gb.k_cache.shape[0]
+    big_ids = (np.arange(nb, dtype=np.int64) * 104729 + 4098) % nb_big
+    assert len(np.unique(big_ids)) == nb and big_ids.max() * per_block > (1 << 31)
+    fill = 0x7F if kv == "fp8" else float("nan")
+    kc, vc = pkv.alloc_caches(nb_big, w.num_kv_heads, w.head_dim, w.cache_dtype, device,
+                              fill=fill, block_size=8)
+    idx = torch.from_numpy(big_ids).to(device)
+    kc.index_copy_(0, idx, gb.k_cache)
+    vc.index_copy_(0, idx, gb.v_cache)
+    tab = np.where(gb.tables >= 0, big_ids[np.maximum(gb.tables, 0)], -1).astype(np.int32)
+    B, Hq, d = gb.q.shape
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=device)
+    parts = None
+    if P != 0:
+        maxp = pkv.max_partitions_for(tab.shape[1], P, 8)
+        parts = pkv.alloc_partials(B, Hq, d, maxp, device)
+    pkv.decode(out, gb.q, kc, vc, torch.from_numpy(tab).to(device), gb.lens_d, w.scale, P, parts,
+               kv_scales=gpu_batch.kv_scales(w))
+    torch.cuda.synchronize()
+    check_close(out.cpu().double().numpy(), _oracle_decode(ob, w), w.dtype,
+                f"bs 8 caches past 2 GiB {kv} P {P}")
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
 # at 32 tokens per block, FP8 caches walk whole blocks (single pass, partitions of whole
 # blocks) or 16-token tiles (partitions of 16 tokens): both paths are covered
 @pytest.mark.parametrize("P", [0, 16, 32, AUTO], ids=["single", "p16", "p32", "auto"])
