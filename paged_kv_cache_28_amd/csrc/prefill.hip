@@ -65,6 +65,7 @@ struct PrefillArgs {
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillNC = 2;       // column tiles per wave
 constexpr int kStageKeys = 64;      // keys per LDS stage (two pairs)
+constexpr float kSlack = 8.0f;      // lazy reference point, as in the decode kernel
 
 // One LDS stage: K and V of 64 keys, D dims, 16-bit elements; two stages in flight.
 template <int D>
@@ -82,6 +83,13 @@ __host__ __device__ constexpr int prefill_wave_tokens(int G) { return 16 * kPref
 // max of two logits, which are never NaN here (masked keys are -inf): the median of
 // (a, b, +inf) is their maximum, and unlike fmaxf it needs no quieting of its inputs
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+// max of three such logits in one instruction; written out because the compiler puts a
+// quieting max in front of each operand of the max it would select itself
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 // the maximum over the four lanes l % 16 + 16 k (the rows of one column)
 __device__ __forceinline__ float rows_max(float x) {
     const unsigned u = __builtin_bit_cast(unsigned, x);
@@ -159,15 +167,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
     for (int ct = 0; ct < NC; ++ct) wave_end = max(wave_end, tile_lim[ct]);
 
     f32x4 acc[NC][NPV];
-    float m_ref[NC], lsum[NC];
+    // m_ref: the column's reference point (log2 domain); nm: the offset its weights take,
+    // -m_ref, or 0 while the column has seen no real key (m_ref = -inf), where every
+    // logit is -inf too and the weights must stay 0 instead of exp2(-inf + inf)
+    float m_ref[NC], nm[NC], thr[NC], lsum[NC];   // thr = m_ref + kSlack
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
 #pragma unroll
         for (int c = 0; c < NPV; ++c) acc[ct][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_ref[ct] = -INFINITY;
+        nm[ct] = 0.f;
+        thr[ct] = -INFINITY;
         lsum[ct] = 0.f;
     }
-    constexpr float kSlack = 8.0f;   // lazy reference point, as in the decode kernel
 
     // ---- stage loads: thread t issues load i of K and of V at linear chunk t + 256 i of
     // the stage, in the cache's own order (a block's K tile [NG][BS][16 B], then its V tile
@@ -242,10 +254,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
         // V rows past the sequence may hold anything: zeroed, only in a pair that has such
         // rows, so that their zero weights give zero products
         if (kp + 32 > n) {
-            auto keep = [&](int q) {
-                return (q < n ? 0x0000ffffu : 0u) | (q + 1 < n ? 0xffff0000u : 0u);
+            const int rn = n - p0;      // this lane's positions p0 + e with e < rn are valid
+            auto keep = [&](int e) {
+                return (e < rn ? 0x0000ffffu : 0u) | (e + 1 < rn ? 0xffff0000u : 0u);
             };
-            const uint32_t k0 = keep(p0), k1 = keep(p0 + 2), k2 = keep(p0 + 4), k3 = keep(p0 + 6);
+            const uint32_t k0 = keep(0), k1 = keep(2), k2 = keep(4), k3 = keep(6);
 #pragma unroll
             for (int c = 0; c < NPV; ++c) {
                 v[c].x &= k0;
@@ -270,7 +283,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
         bool masked = false;
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) masked |= kp + 32 > tile_min[ct] || kp >= tile_lim[ct];
-        float x[NC][8], bm[NC];
+        // lm: the maximum of this lane's 8 raw logits; the column's maximum is that of its
+        // four lanes' lm, taken only when the reference point may move
+        float x[NC][8], lm[NC];
+        bool lane_move = false;
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
 #pragma unroll
@@ -279,39 +295,41 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
                 x[ct][4 + e] = sb[ct][e];
             }
             if (masked) {
+                const int rem = lim[ct] - p0;   // positions p0 + e with e < rem are visible
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[ct][e] = p0 + e < lim[ct] ? x[ct][e] : -INFINITY;
+                for (int e = 0; e < 8; ++e) x[ct][e] = e < rem ? x[ct][e] : -INFINITY;
             }
-            bm[ct] = rows_max(vmax(vmax(vmax(x[ct][0], x[ct][1]), vmax(x[ct][2], x[ct][3])),
-                                   vmax(vmax(x[ct][4], x[ct][5]), vmax(x[ct][6], x[ct][7])))) *
-                     a.scale_log2;
+            const float t0 = vmax3(x[ct][0], x[ct][1], x[ct][2]);
+            const float t1 = vmax3(x[ct][3], x[ct][4], x[ct][5]);
+            const float t2 = vmax3(x[ct][6], x[ct][7], t0);
+            lm[ct] = vmax3(t1, t2, t2);
+            // rounding is monotonic, so some lane of a column passes this test exactly when
+            // the column's maximum, scaled, passes it
+            lane_move |= lm[ct] * a.scale_log2 > thr[ct];
         }
-        bool any_move = false;
-#pragma unroll
-        for (int ct = 0; ct < NC; ++ct) any_move |= bm[ct] > m_ref[ct] + kSlack;
-        if (__builtin_amdgcn_ballot_w64(any_move)) {
+        if (__builtin_amdgcn_ballot_w64(lane_move)) {
 #pragma unroll
             for (int ct = 0; ct < NC; ++ct) {
-                // a lane that keeps its reference keeps factor 1 (also one whose column has
-                // seen no key yet, where m - m would be -inf - -inf)
-                const bool move = bm[ct] > m_ref[ct] + kSlack;
-                const float mn = move ? bm[ct] : m_ref[ct];
+                // a column that keeps its reference keeps factor 1 (also one that has seen
+                // no key yet, where m - m would be -inf - -inf)
+                const float bm = rows_max(lm[ct]) * a.scale_log2;
+                const bool move = bm > thr[ct];
+                const float mn = move ? bm : m_ref[ct];
                 const float alpha = move ? exp2_fast(m_ref[ct] - mn) : 1.0f;
                 lsum[ct] *= alpha;
 #pragma unroll
                 for (int c = 0; c < NPV; ++c) acc[ct][c] *= alpha;
                 m_ref[ct] = mn;
+                nm[ct] = mn == -INFINITY ? 0.f : -mn;
+                thr[ct] = mn + kSlack;
             }
         }
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
-            // 2^(x scale - m): 0 for x = -inf and a finite m; m is -inf only while the
-            // column has seen no real key, and then every x is -inf too, so one select per
-            // lane (not per element) keeps those weights 0 instead of exp2(-inf + inf)
-            const float nm = m_ref[ct] == -INFINITY ? 0.f : -m_ref[ct];
+            // 2^(x scale - m): 0 for x = -inf and a finite m
             float pe[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(__builtin_fmaf(x[ct][e], a.scale_log2, nm));
+            for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(__builtin_fmaf(x[ct][e], a.scale_log2, nm[ct]));
             lsum[ct] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
             uint16_t hi[8], lo[8];
 #pragma unroll
