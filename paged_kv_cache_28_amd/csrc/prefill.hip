@@ -25,15 +25,27 @@
 // 8 (r / 4) + r % 4 of the pair; of B: that + 4), so that lane l holds the logits of the
 // 8 consecutive positions 8 (l/16) .. + 7, which are its 8 k-slots of the PV step in both
 // operands: P stays in the lanes that produced it, and the lane's V operand is 8
-// consecutive positions of one dimension row. P is split in a high and a low bf16/fp16
-// part as in decode. The LDS layout is that of the operands, whatever the block size:
-// K as [pair][product][16-byte dim group][MFMA row], V as [pair][8-key group][dim], so
-// every operand read covers 128 contiguous bytes per 8 lanes, and the arithmetic (so the
-// result) is the same for 8, 16 and 32 tokens per block.
+// consecutive positions of one dimension row. The LDS layout is that of the operands,
+// whatever the block size: K as [pair][product][16-byte dim group][MFMA row], V as
+// [pair][8-key group][dim], so every operand read covers 128 contiguous bytes per 8 lanes,
+// and the arithmetic (so the result) is the same for 8, 16 and 32 tokens per block.
+//
+// The weights enter the PV product once, rounded to fp16 (relative error at most 2^-11;
+// they are 2^(x - m + 7) <= 2^15, so they reach fp16's subnormals only 21 binades below the
+// column's maximum), and V enters it in fp16 too: a bf16 cache's V is converted as it is
+// staged, which is exact for 2^-17 <= |v| <= 65,280 and moves smaller values by at most
+// 2^-25. A bf16 V at or beyond 2^16 becomes +-inf, and every product with it (weight 0
+// included) leaves the wave's accumulators non-finite; such a wave writes a NaN marker in
+// place of its rows, and a second launch redoes those workgroups with the weights split in
+// a high and a low bf16 part (two products, about 16 significant bits, as in decode). The
+// same launch returns at once from every workgroup without a marker. With bf16 weights
+// alone the error would reach about 3.7e-3 at a few keys and 1.7e-3 of max|out| at long
+// contexts for N(0, 1) data; fp16 weights stay near 5e-4 and 2e-4.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 
 #include "device.hpp"
@@ -66,6 +78,7 @@ constexpr int kPrefillWaves = 4;
 constexpr int kPrefillNC = 2;       // column tiles per wave
 constexpr int kStageKeys = 64;      // keys per LDS stage (two pairs)
 constexpr float kSlack = 8.0f;      // lazy reference point, as in the decode kernel
+constexpr float kPOffset = 7.0f;    // one-product form: weights 2^(x - m + 7) <= 2^15
 
 // One LDS stage: K and V of 64 keys, D dims, 16-bit elements; two stages in flight.
 template <int D>
@@ -75,6 +88,21 @@ __host__ __device__ constexpr size_t prefill_stage_bytes() {
 template <int D>
 __host__ __device__ constexpr size_t prefill_lds_bytes() {
     return 2 * prefill_stage_bytes<D>();
+}
+
+// How the PV product takes the weights (see the header comment):
+//   kSplitP: weights split into a high and a low part in the input type, two products;
+//   kHalfP:  weights rounded once to fp16 and V in fp16 (a bf16 cache's V converted as it
+//            is staged), one product; a wave whose accumulators end up non-finite writes a
+//            NaN marker instead of its rows;
+//   kRedo:   kSplitP, run only by workgroups whose rows carry such a marker.
+constexpr int kSplitP = 0, kHalfP = 1, kRedo = 2;
+
+// Two floats -> two fp16 (round to nearest even) in one word, lo in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 r = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // Query tokens per wave: the 16 * NC columns hold whole tokens' G heads.
@@ -100,7 +128,26 @@ __device__ __forceinline__ float rows_max(float x) {
     return vmax(__builtin_bit_cast(float, (unsigned)r32[0]), __builtin_bit_cast(float, (unsigned)r32[1]));
 }
 
-template <typename T, int D, typename OutT, int BS>
+// Element 0 of row `row` of out is NaN (the marker of a wave whose rows must be redone).
+template <typename OutT> __device__ __forceinline__ bool marked(const void* out, int64_t row, int D);
+template <> __device__ __forceinline__ bool marked<float>(const void* out, int64_t row, int D) {
+    return __builtin_isnan(static_cast<const float*>(out)[row * D]);
+}
+template <> __device__ __forceinline__ bool marked<bf16_t>(const void* out, int64_t row, int D) {
+    return (static_cast<const uint16_t*>(out)[row * D] & 0x7fff) > 0x7f80;
+}
+template <> __device__ __forceinline__ bool marked<f16_t>(const void* out, int64_t row, int D) {
+    return (static_cast<const uint16_t*>(out)[row * D] & 0x7fff) > 0x7c00;
+}
+
+template <typename OutT> __device__ __forceinline__ void put_marker(void* out, int64_t row, int D) {
+    if constexpr (std::is_same<OutT, float>::value)
+        static_cast<uint32_t*>(out)[row * D] = 0x7fc00000u;
+    else
+        static_cast<uint16_t*>(out)[row * D] = std::is_same<OutT, bf16_t>::value ? 0x7fc0 : 0x7e00;
+}
+
+template <typename T, int D, typename OutT, int BS, int kMode>
 __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
     constexpr int W = kPrefillWaves, NC = kPrefillNC;
     constexpr int NQK = D / 32, NPV = D / 16;
@@ -128,6 +175,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
     const int tw0 = t0 + wave * TW;                     // this wave's first token
     // keys any query of the workgroup sees: up to the last valid token's position
     const int wg_last = min(QT, L - t0) - 1;
+    if constexpr (kMode == kRedo) {
+        // redo only a workgroup one of whose waves left its marker (element 0 of the row of
+        // its first query token and the group's first head)
+        bool redo = false;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const int tw = t0 + w * TW;
+            if (tw < L) redo |= marked<OutT>(a.out, int64_t(q0 + tw) * a.num_heads + g * G, D);
+        }
+        if (!redo) return;
+    }
+    // the PV product's element type: fp16 in the one-product form
+    using PV = typename std::conditional<kMode == kHalfP, f16_t, T>::type;
+    constexpr bool kConvertV = kMode == kHalfP && std::is_same<T, bf16_t>::value;
     const int key_end = max(0, min(n, n - L + t0 + wg_last + 1));
 
     // This lane's column in each column tile: query token, head, causal limit (keys
@@ -231,7 +292,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
             {   // V chunk: dim d, 8 positions from row 8h -> 8-key group of the stage
                 const int d = within / (BS / 8), h = within - d * (BS / 8);
                 const int kl = bl * BS + 8 * h, m = kl >> 5, o = (kl & 31) >> 3;
-                buf[KCH + (m * 4 + o) * D + d] = vr[i];
+                u32x4 vv = vr[i];
+                if constexpr (kConvertV) {
+                    // bf16 -> fp16, exact for 2^-17 <= |v| <= 65280; |v| >= 65536 becomes
+                    // +-inf, which makes the accumulators of every column non-finite
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t u = vv[j];
+                        vv[j] = pack_f16x2(__builtin_bit_cast(float, u << 16),
+                                           __builtin_bit_cast(float, u & 0xffff0000u));
+                    }
+                }
+                buf[KCH + (m * 4 + o) * D + d] = vv;
             }
         }
     };
@@ -241,13 +313,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
     // pair), so that the scheduler can interleave one tile's softmax with the other's
     // matrix products. A tile whose queries see none of the pair goes through the masked
     // form, which gives it zero weights.
-    auto compute_pair = [&](const uint4* buf, int kp, int m) __attribute__((always_inline)) {
-        uint4 ka[NQK], kb[NQK], v[NPV];
+    auto load_k = [&](const uint4* buf, int m, uint4 (&ka)[NQK], uint4 (&kb)[NQK]) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < NQK; ++c) {
             ka[c] = buf[((m * 2 + 0) * NG + 4 * c + quad) * 16 + col];
             kb[c] = buf[((m * 2 + 1) * NG + 4 * c + quad) * 16 + col];
         }
+    };
+    auto compute_pair = [&](const uint4* buf, int kp, int m, uint4 (&ka)[NQK], uint4 (&kb)[NQK]) __attribute__((always_inline)) {
+        uint4 v[NPV];
 #pragma unroll
         for (int c = 0; c < NPV; ++c) v[c] = buf[KCH + (m * 4 + quad) * D + 16 * c + col];
         const int p0 = kp + 8 * quad;   // first of this lane's 8 positions
@@ -278,6 +352,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
                 sb[ct] = Mfma<T>::qk(kb[c], qf[ct][c], sb[ct]);
             }
         }
+        if (m == 0) load_k(buf, 1, ka, kb);   // the next pair's K, while this one's softmax runs
         // raw logits (scale applied below): the causal diagonal, the sequence end and tiles
         // that see none of the pair take -inf per key
         bool masked = false;
@@ -320,7 +395,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
                 for (int c = 0; c < NPV; ++c) acc[ct][c] *= alpha;
                 m_ref[ct] = mn;
-                nm[ct] = mn == -INFINITY ? 0.f : -mn;
+                nm[ct] = mn == -INFINITY ? 0.f : kPOffset - mn;
                 thr[ct] = mn + kSlack;
             }
         }
@@ -331,23 +406,41 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
             for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(__builtin_fmaf(x[ct][e], a.scale_log2, nm[ct]));
             lsum[ct] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-            uint16_t hi[8], lo[8];
+            if constexpr (kMode == kHalfP) {
+                // one fp16 rounding per weight (weights in (2^-21, 2^15] before underflow)
+                const uint4 ph = make_uint4(pack_f16x2(pe[0], pe[1]), pack_f16x2(pe[2], pe[3]),
+                                            pack_f16x2(pe[4], pe[5]), pack_f16x2(pe[6], pe[7]));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
-            const uint4 phi = make_uint4(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
-                                         uint32_t(hi[2]) | (uint32_t(hi[3]) << 16),
-                                         uint32_t(hi[4]) | (uint32_t(hi[5]) << 16),
-                                         uint32_t(hi[6]) | (uint32_t(hi[7]) << 16));
-            const uint4 plo = make_uint4(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
-                                         uint32_t(lo[2]) | (uint32_t(lo[3]) << 16),
-                                         uint32_t(lo[4]) | (uint32_t(lo[5]) << 16),
-                                         uint32_t(lo[6]) | (uint32_t(lo[7]) << 16));
+                for (int c = 0; c < NPV; ++c) acc[ct][c] = Mfma<PV>::qk(v[c], ph, acc[ct][c]);
+            } else {
+                uint16_t hi[8], lo[8];
 #pragma unroll
-            for (int c = 0; c < NPV; ++c) {
-                acc[ct][c] = Mfma<T>::qk(v[c], phi, acc[ct][c]);
-                acc[ct][c] = Mfma<T>::qk(v[c], plo, acc[ct][c]);
+                for (int e = 0; e < 8; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
+                const uint4 phi = make_uint4(uint32_t(hi[0]) | (uint32_t(hi[1]) << 16),
+                                             uint32_t(hi[2]) | (uint32_t(hi[3]) << 16),
+                                             uint32_t(hi[4]) | (uint32_t(hi[5]) << 16),
+                                             uint32_t(hi[6]) | (uint32_t(hi[7]) << 16));
+                const uint4 plo = make_uint4(uint32_t(lo[0]) | (uint32_t(lo[1]) << 16),
+                                             uint32_t(lo[2]) | (uint32_t(lo[3]) << 16),
+                                             uint32_t(lo[4]) | (uint32_t(lo[5]) << 16),
+                                             uint32_t(lo[6]) | (uint32_t(lo[7]) << 16));
+#pragma unroll
+                for (int c = 0; c < NPV; ++c) {
+                    acc[ct][c] = Mfma<T>::qk(v[c], phi, acc[ct][c]);
+                    acc[ct][c] = Mfma<T>::qk(v[c], plo, acc[ct][c]);
+                }
             }
         }
+        // tile 0's softmax, then tile 0's PV products one at a time between tile 1's
+        // softmax instructions, then tile 1's PV products
+        constexpr int kPVPerTile = kMode == kHalfP ? NPV : 2 * NPV;
+        __builtin_amdgcn_sched_group_barrier(0x402, kMode == kHalfP ? 28 : 48, 0);
+#pragma unroll
+        for (int i = 0; i < kPVPerTile; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPVPerTile, 0);
     };
 
     // ---- the stages: stage s + 1 is in flight in registers while stage s is computed from
@@ -365,16 +458,33 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
             const uint4* cur = lds4 + (s & 1) * STAGE_CH;
             issue(ids);                                 // stage min(s + 1, S - 1)
             ids = stage_ids(min(s + 2, S - 1));
+            uint4 ka[NQK], kb[NQK];
+            load_k(cur, 0, ka, kb);
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int kp = s * kStageKeys + 32 * m;
-                if (kp < wave_end) compute_pair(cur, kp, m);
+                if (kp < wave_end) compute_pair(cur, kp, m, ka, kb);
             }
             store(lds4 + ((s + 1) & 1) * STAGE_CH);
             __syncthreads();
         }
     }
 
+    if constexpr (kConvertV) {
+        // a V element at or beyond 2^16 became +-inf in fp16, and every product with it
+        // (weight 0 included) left this wave's accumulators non-finite (so would NaN or
+        // infinite inputs, which the exact form then reproduces): the wave writes the
+        // marker instead of its rows, and the kRedo pass computes them
+        float sum = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+            for (int c = 0; c < NPV; ++c) sum += (acc[ct][c][0] + acc[ct][c][1]) + (acc[ct][c][2] + acc[ct][c][3]);
+        if (__builtin_amdgcn_ballot_w64(!__builtin_isfinite(sum))) {
+            if (lane == 0 && tw0 < L) put_marker<OutT>(a.out, int64_t(q0 + tw0) * a.num_heads + g * G, D);
+            return;
+        }
+    }
     // ---- this wave's rows: lanes l, l^16, l^32, l^48 hold parts of the same column
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
@@ -396,6 +506,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
     }
 }
 
+// One call: the one-product kernel, then (bf16 caches) the pass that redoes, in the exact
+// split form, the workgroups whose waves met a V value beyond fp16's range; that pass's
+// workgroups read a few marker elements and exit otherwise. The timer's events span both.
 template <typename T, int D, typename OutT, int BS>
 hipError_t launch_prefill(const PrefillArgs& a, int max_q_len, int num_kv_heads, int num_seqs,
                           hipStream_t s) {
@@ -403,9 +516,18 @@ hipError_t launch_prefill(const PrefillArgs& a, int max_q_len, int num_kv_heads,
     const dim3 grid(unsigned((max_q_len + qt_tokens - 1) / qt_tokens), unsigned(num_kv_heads),
                     unsigned(num_seqs));
     const LaunchEvents ev = timer_events(PKV_TIMER_PREFILL);
-    hipExtLaunchKernelGGL((prefill_kernel<T, D, OutT, BS>), grid, dim3(kPrefillWaves * 64),
-                          prefill_lds_bytes<D>(), s, ev.start, ev.stop, 0, a);
-    return hipGetLastError();
+    constexpr bool redo = std::is_same<T, bf16_t>::value;
+    hipExtLaunchKernelGGL((prefill_kernel<T, D, OutT, BS, kHalfP>), grid, dim3(kPrefillWaves * 64),
+                          prefill_lds_bytes<D>(), s, ev.start, redo ? nullptr : ev.stop, 0, a);
+    hipError_t err = hipGetLastError();
+    if constexpr (redo) {
+        if (err != hipSuccess) return err;
+        hipExtLaunchKernelGGL((prefill_kernel<T, D, OutT, BS, kRedo>), grid,
+                              dim3(kPrefillWaves * 64), prefill_lds_bytes<D>(), s, nullptr, ev.stop,
+                              0, a);
+        err = hipGetLastError();
+    }
+    return err;
 }
 
 template <int BS>

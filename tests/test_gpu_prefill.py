@@ -7,7 +7,9 @@ the fp32 bar plus half an output ulp of the oracle. Cases: whole prompts, chunks
 longer contexts, single-query rows mixed with chunks, chunks longer than their sequence
 (zero rows), several shapes of GQA group and head size, and a prompt processed in chunks
 over several calls against one call over the whole prompt ("vLLM Nedir? PagedAttention ile
-Production LLM Serving", section "Chunked prefill").
+Production LLM Serving", section "Chunked prefill"). The kernel's one-product form takes V in
+fp16: bf16 V values at fp16's edges, beyond its range (the pass that redoes such workgroups
+with split weights) and in slots past a sequence's end are checked too.
 """
 import dataclasses
 
@@ -139,3 +141,90 @@ def test_prefill_rejects_bad_arguments(device):
     with pytest.raises(pkv.PkvError) as e:
         pkv.paged_attention_prefill(q, qb, qs, kc, vc, tab, ln, float("nan"), 3)
     assert e.value.code == pkv.PKV_EINVAL
+
+
+# ---- the one-product form: a bf16 cache's V is rounded to fp16 as it is staged, which is
+# exact from 2^-17 to 65,280 in magnitude; a wave that meets |v| >= 65,536 (fp16 +-inf) is
+# redone by the split-weight pass. Both are checked against the oracle here.
+
+def _set_v(ob, gb, b, pos, dims, value):
+    """V of sequence b at position pos, every KV head, the given dims, set to `value` (a
+    bf16 number) in the oracle's cache and in the GPU's."""
+    bs = ob.w.block_size
+    blk, off = int(ob.tables[b][pos // bs]), pos % bs
+    bits = int(torch.tensor([value], dtype=torch.bfloat16).view(torch.int16).item()) & 0xFFFF
+    for d in dims:
+        ob.v_cache[blk, :, d, off] = bits
+        gb.v_cache[blk, :, d, off] = value
+
+
+def _run_edited(w, spec, edits, device, out_dtype=torch.float32, gpu_only=()):
+    lens = [n for n, _ in spec]
+    chunk = [L for _, L in spec]
+    ob = paged_batch.build(w, lens=lens, seed_stream=5)
+    gb = gpu_batch.build(ob, device)
+    assert np.array_equal(gb.tables, ob.tables)
+    for b, pos, dims, value in edits:
+        _set_v(ob, gb, b, pos, dims, value)
+    for b, pos, dims, value in gpu_only:      # slots past a sequence's end: never read
+        bs = w.block_size
+        gb.v_cache[int(ob.tables[b][pos // bs]), :, dims, pos % bs] = value
+    q = workloads.draw_q(w, workloads.rng(w.seed, 62), batch=int(sum(chunk)))
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    out = torch.full(tuple(q.shape), float("nan"), dtype=out_dtype, device=device)
+    pkv.paged_attention_prefill(out, q.to(device), torch.from_numpy(qs).to(device), gb.k_cache,
+                                gb.v_cache, gb.tables_d, gb.lens_d, w.scale, max(chunk))
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q, qs, ob.k_cache, ob.v_cache, ob.tables, ob.lens, w.scale, w.dtype)
+    return out.cpu().double().numpy(), ref, qs
+
+
+def _check_seq(got, ref, qs, b, dtype, what, normalised_only=False, half_ulp=False):
+    g, r = got[qs[b]:qs[b + 1]], ref[qs[b]:qs[b + 1]]
+    slack = 0.5 * _ulp(g, dtype) if half_ulp else 0.0
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - r)
+    if not normalised_only:
+        assert np.all(err <= TOL[dtype] + slack), f"{what}: max|err| {err.max():.3e}"
+    scale = np.abs(r).max()
+    assert np.all(err <= 1e-3 * scale + slack), f"{what}: normalised {err.max() / scale:.3e}"
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("name", ["bf16-d128-g4", "bf16-d128-g6"])
+def test_prefill_v_beyond_fp16_range_is_redone(name, out_dtype, device):
+    """V values of 65,536 and -98,304 (beyond fp16) in two sequences: their rows match the
+    oracle within the normalised bar (the values make the outputs large), the other
+    sequences' rows within the usual bars, in one call."""
+    w = SHAPES[name]
+    spec = CASES["chunks"]            # contexts 40, 97, 300, 513, 1000
+    edits = [(2, 150, [5, 77], 65536.0), (4, 999, [127], -98304.0), (4, 3, [0], 131072.0)]
+    got, ref, qs = _run_edited(w, spec, edits, device, out_dtype)
+    half = out_dtype != torch.float32
+    for b in range(len(spec)):
+        _check_seq(got, ref, qs, b, w.dtype, f"{name} seq {b}", normalised_only=b in (2, 4),
+                   half_ulp=half)
+
+
+def test_prefill_v_at_fp16_edges(device):
+    """V values that fp16 holds exactly (+-65,280, 2^-14, 2^-17) and ones it rounds
+    (1.171875 * 2^-20, 3e-7: fp16 subnormals) take the one-product form; within the bars of
+    the oracle."""
+    w = SHAPES["bf16-d128-g4"]
+    spec = CASES["chunks"]
+    edits = [(1, 50, [3, 4], 65280.0), (1, 60, [3], -65280.0), (2, 10, [0, 1, 2], 2.0 ** -14),
+             (2, 11, [9], 2.0 ** -17), (3, 400, [100], 1.171875 * 2.0 ** -20), (3, 401, [101], -3e-7)]
+    got, ref, qs = _run_edited(w, spec, edits, device)
+    for b in range(len(spec)):
+        _check_seq(got, ref, qs, b, w.dtype, f"seq {b}", normalised_only=b == 1)
+
+
+def test_prefill_ignores_huge_values_past_the_sequence(device):
+    """Slots after a sequence's last token in its last block hold values beyond fp16 (never
+    read by the oracle): the rows stay within the usual bars."""
+    w = SHAPES["bf16-d128-g4"]
+    spec = CASES["chunks"]            # 97 and 513 end inside a block
+    gpu_only = [(1, 97, list(range(128)), 1e6), (1, 100, [7], -3e38), (3, 513, [0, 64], 2e5)]
+    got, ref, qs = _run_edited(w, spec, [], device, gpu_only=gpu_only)
+    for b in range(len(spec)):
+        _check_seq(got, ref, qs, b, w.dtype, f"seq {b}")
