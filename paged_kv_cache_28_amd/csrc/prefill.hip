@@ -431,16 +431,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
                 }
             }
         }
-        // tile 0's softmax, then tile 0's PV products one at a time between tile 1's
-        // softmax instructions, then tile 1's PV products
-        constexpr int kPVPerTile = kMode == kHalfP ? NPV : 2 * NPV;
-        __builtin_amdgcn_sched_group_barrier(0x402, kMode == kHalfP ? 28 : 48, 0);
+        if constexpr (kMode != kHalfP) {
+            // split weights: tile 0's softmax, then tile 0's PV products one at a time
+            // between tile 1's softmax instructions, then tile 1's PV products (measured
+            // 1.5% faster than the compiler's order; slower for the one-product form)
+            __builtin_amdgcn_sched_group_barrier(0x402, 48, 0);
 #pragma unroll
-        for (int i = 0; i < kPVPerTile; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+            for (int i = 0; i < 2 * NPV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * NPV, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, kPVPerTile, 0);
     };
 
     // ---- the stages: stage s + 1 is in flight in registers while stage s is computed from
