@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--cache-write-sweep", action="store_true",
                     help="only time reshape_and_cache / reshape_and_cache_fp8 over token counts "
                          "and slot patterns (8B shape) and exit")
+    ap.add_argument("--rates", action="store_true",
+                    help="only measure the unit rates (LDS reads, exponentials, FMAs, bf16 "
+                         "16x16x32 products, products mixed with exponentials or FMAs) at 1, 2, "
+                         "4 and 8 waves per SIMD and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer 8 times (a plain copy of known size, to "
                          "scale the HBM byte counters) and exit")
@@ -195,6 +199,50 @@ def traffic_summary(spec):
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))
+
+
+def bench_rates():
+    """Unit rates of the device's SIMDs (pkv_measure_rate), library timer, median of 5
+    launches of each kind at 1, 2, 4 and 8 waves per SIMD. Counts per launch: LDS bytes =
+    waves x 64 lanes x iters x 8 x 16; exponentials or FMAs = lanes x iters x 8 (16 FMAs in
+    the mixed kind); products = waves x iters x 4 (16,384 flops each). "overlap" is the mixed
+    kind's time over the sum of its two parts' times (0.5 = fully hidden, 1 = none)."""
+    import torch
+
+    import paged_kv_cache_28_amd as pkv
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4096
+    sink = torch.zeros(cus * 8 * 4, dtype=torch.int32, device=dev)
+
+    def timed(kind, wps):
+        pkv.measure_rate(kind, wps, iters, sink)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            pkv.timer_enable(True)
+            pkv.measure_rate(kind, wps, iters, sink)
+            ms, n = pkv.timer_read(pkv.PKV_TIMER_MEASURE)
+            pkv.timer_enable(False)
+            ts.append(ms / n)
+        return sorted(ts)[2]
+
+    rows = []
+    for wps in (1, 2, 4, 8):
+        waves = cus * 4 * wps
+        t = {k: timed(k, wps) for k in pkv.RATE_KINDS}
+        lanes = waves * 64
+        rows.append({
+            "waves_per_simd": wps, "ms": {k: round(v, 4) for k, v in t.items()},
+            "lds_TB/s": round(waves * 64 * iters * 8 * 16 / t["lds_read"] / 1e9, 1),
+            "exp_per_s": float(f"{lanes * iters * 8 / t['exp'] * 1e3:.4g}"),
+            "fma_per_s": float(f"{lanes * iters * 8 / t['fma'] * 1e3:.4g}"),
+            "mfma_TFLOP/s": round(waves * iters * 4 * 16384 / t["mfma"] / 1e9, 1),
+            "overlap_mfma_exp": round(t["mfma_exp"] / (t["mfma"] + t["exp"]), 3),
+            "overlap_mfma_16fma": round(t["mfma_fma"] / (t["mfma"] + 2 * t["fma"]), 3),
+        })
+    print(json.dumps({"rates": rows, "cus": cus, "iters": iters,
+                      "kernel": "pkv_measure_rate (library timer, median of 5)"}), flush=True)
 
 
 def calibrate_copy():
@@ -592,6 +640,9 @@ def main():
         return
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.rates:
+        bench_rates()
         return
     if args.cache_write_sweep:
         bench_cache_write_sweep(args)

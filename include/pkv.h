@@ -134,6 +134,18 @@ int pkv_measure_gather(const void* k_cache, const void* v_cache, const int32_t* 
                        int32_t max_blocks_per_seq, int64_t num_blocks, const int32_t* seq_order,
                        int32_t balanced, int32_t nontemporal, uint32_t* sink, int32_t sink_len,
                        void* stream);
+/* pkv_measure_rate: what the SIMDs sustain on the kernels' building blocks, with
+ * waves_per_simd (1 .. 8) waves on every SIMD of the device (CUs x waves_per_simd
+ * workgroups of 4 waves), each running iters iterations of: kind 0, 8 conflict-free 16-byte
+ * LDS reads per lane (chunk ((8t + j) * 257 + tid) mod 1024 of a workgroup-local 16 KiB
+ * array whose chunk i holds (i, 3i, 5i, 7i), folded by XOR); 1, 8 exponentials (v_exp_f32)
+ * in independent chains; 2, 8 FMAs; 3, 4 bf16 16x16x32 matrix products (4 accumulators);
+ * 4, kind 3's products with kind 1's exponentials between them; 5, the 4 products with 16
+ * FMAs between them. Used to set the prefill kernel's mix of matrix and vector work
+ * against what the hardware overlaps (the prefill steps of "vLLM Nedir? PagedAttention ile
+ * Production LLM Serving", section "Chunked prefill"). Errors: EINVAL, EHIP. */
+int pkv_measure_rate(int32_t kind, int32_t waves_per_simd, int32_t iters, uint32_t* sink,
+                     int32_t sink_len, void* stream);
 
 /* ---- KV bytes per token ------------------------------------------------------------
  * 2 (K and V) x layers x KV heads x head_dim x bytes per element

@@ -109,6 +109,7 @@ def lib():
         "pkv_measure_read": ([P, I64, I32, I32, I32, P, I32, P], ctypes.c_int),
         "pkv_measure_gather": ([P, P, P, P, I32, I32, I32, I32, I32, I32, I64, P, I32, I32, P, I32,
                                 P], ctypes.c_int),
+        "pkv_measure_rate": ([I32, I32, I32, P, I32, P], ctypes.c_int),
         "pkv_timer_enable": ([I32], ctypes.c_int),
         "pkv_timer_read": ([I32, P, P], ctypes.c_int),
     }
@@ -135,7 +136,8 @@ EXPORTED = ("pkv_last_error", "pkv_version", "kv_bytes_per_token", "kv_pool_crea
             "kv_pool_add_seq_prefix", "kv_pool_fork", "kv_pool_append_tokens",
             "kv_pool_append_batch_tokens", "copy_blocks", "paged_attention_prefill",
             "paged_attention_decode_plan", "paged_attention_decode_noalloc",
-            "paged_attention_decode_noalloc_workspace", "pkv_measure_read", "pkv_measure_gather")
+            "paged_attention_decode_noalloc_workspace", "pkv_measure_read", "pkv_measure_gather",
+            "pkv_measure_rate")
 
 
 def _check(rc: int):
@@ -794,6 +796,17 @@ def measure_gather(k_cache, v_cache, block_tables, seq_lens, sink, seq_order=Non
                                     1 if balanced else 0, 1 if nontemporal else 0,
                                     _dev(sink, "sink"), sink.numel(),
                                     _stream(k_cache, stream)))
+
+
+RATE_KINDS = ("lds_read", "exp", "fma", "mfma", "mfma_exp", "mfma_fma")
+
+
+def measure_rate(kind: str, waves_per_simd: int, iters: int, sink, stream=None):
+    """Unit rates (a measuring aid): kind in RATE_KINDS, waves_per_simd waves on every SIMD,
+    iters iterations each (timed under PKV_TIMER_MEASURE); see pkv_measure_rate."""
+    _index(sink, "sink")
+    _check(lib().pkv_measure_rate(RATE_KINDS.index(kind), int(waves_per_simd), int(iters),
+                                  _dev(sink, "sink"), sink.numel(), _stream(sink, stream)))
 
 
 def timer_enable(on: bool = True):

@@ -220,6 +220,92 @@ void launch_read(int loads_in_flight, dim3 grid, hipStream_t s, const LaunchEven
         default: hipExtLaunchKernelGGL((stream_read_kernel<16, NT>), grid, dim3(256), 0, s, ev.start, ev.stop, 0, b, n16, sink, sink_len); break;
     }
 }
+// ---- unit rates: what one CU's SIMDs sustain on the operations the kernels are made of
+// (LDS operand reads, exponentials, FMAs, 16x16x32 bf16 matrix products, and products mixed
+// in one wave with exponentials or FMAs that do not depend on them), at a chosen number of
+// waves per SIMD. Each lane folds its results into the wave's sink slot.
+constexpr int kRateLdsChunks = 1024;   // 16 KiB of LDS per workgroup: 8 fit on a CU
+
+__device__ __forceinline__ void rate_sink(uint32_t x, uint32_t* sink, int32_t sink_len) {
+    for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
+    if ((threadIdx.x & 63) == 0)
+        sink[(int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6)) % sink_len] = x;
+}
+
+// Workgroup-local LDS chunk i holds (i, 3i, 5i, 7i); iteration t, read j of thread tid reads
+// chunk ((8t + j) * 257 + tid) mod 1024: 8 conflict-free 16-byte reads per lane in flight
+// (a wave's 64 lanes read 1 KiB of consecutive chunks, wrapping at the array's end).
+__global__ __launch_bounds__(256) void rate_lds_kernel(int32_t iters, uint32_t* sink, int32_t sink_len) {
+    __shared__ uint4 buf[kRateLdsChunks];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kRateLdsChunks; i += 256) buf[i] = make_uint4(i, 3 * i, 5 * i, 7 * i);
+    __syncthreads();
+    uint32_t x = 0;
+    for (int t = 0; t < iters; ++t) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x ^= fold(buf[((t * 8 + j) * 257 + tid) & (kRateLdsChunks - 1)]);
+    }
+    rate_sink(x, sink, sink_len);
+}
+
+// Per iteration and lane: kind 1: 8 exponentials (independent chains); 2: 8 FMAs; 3: 4
+// products (4 accumulator chains); 4: 4 products and 8 exponentials; 5: 4 products and 16
+// FMAs, the vector instructions placed between the products.
+template <int KIND>
+__global__ __launch_bounds__(256) void rate_alu_kernel(int32_t iters, uint32_t* sink, int32_t sink_len) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    bf16x8_t a, b;
+    for (int k = 0; k < 8; ++k) {
+        a[k] = (__bf16)(threadIdx.x * 1e-3f);
+        b[k] = (__bf16)(k * 1e-2f);
+    }
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = threadIdx.x * 1e-3f + k;
+    for (int t = 0; t < iters; ++t) {
+        if constexpr (KIND == 1 || KIND == 4) {
+            if constexpr (KIND == 4) c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
+            y[0] = __builtin_amdgcn_exp2f(y[0]);
+            y[1] = __builtin_amdgcn_exp2f(y[1]);
+            if constexpr (KIND == 4) c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
+            y[2] = __builtin_amdgcn_exp2f(y[2]);
+            y[3] = __builtin_amdgcn_exp2f(y[3]);
+            if constexpr (KIND == 4) c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c2, 0, 0, 0);
+            y[4] = __builtin_amdgcn_exp2f(y[4]);
+            y[5] = __builtin_amdgcn_exp2f(y[5]);
+            if constexpr (KIND == 4) c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c3, 0, 0, 0);
+            y[6] = __builtin_amdgcn_exp2f(y[6]);
+            y[7] = __builtin_amdgcn_exp2f(y[7]);
+        } else if constexpr (KIND == 2 || KIND == 5) {
+            if constexpr (KIND == 5) c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[k] = __builtin_fmaf(y[k], 0.999f, 1e-3f);
+            if constexpr (KIND == 5) c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
+#pragma unroll
+            for (int k = 4; k < 8; ++k) y[k] = __builtin_fmaf(y[k], 0.999f, 1e-3f);
+            if constexpr (KIND == 5) {
+                c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c2, 0, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) y[k] = __builtin_fmaf(y[k], 0.999f, 1e-3f);
+                c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c3, 0, 0, 0);
+#pragma unroll
+                for (int k = 4; k < 8; ++k) y[k] = __builtin_fmaf(y[k], 0.999f, 1e-3f);
+            }
+        } else {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c3, 0, 0, 0);
+        }
+    }
+    const f32x4 c = (c0 + c1) + (c2 + c3);
+    float acc = (c[0] + c[1]) + (c[2] + c[3]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += y[k];
+    rate_sink(__builtin_bit_cast(uint32_t, acc), sink, sink_len);
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -324,6 +410,32 @@ extern "C" int pkv_measure_gather(const void* k_cache, const void* v_cache,
             default: err = pkv::launch_gather<8, false>(a, bal, s); break;
         }
     }
+    if (err != hipSuccess) return fail(PKV_EHIP, "%s: launch failed: %s", who, hipGetErrorString(err));
+    return pkv::ok();
+}
+
+extern "C" int pkv_measure_rate(int32_t kind, int32_t waves_per_simd, int32_t iters,
+                                uint32_t* sink, int32_t sink_len, void* stream) {
+    using pkv::fail;
+    const char* who = "pkv_measure_rate";
+    if (!sink || sink_len <= 0 || iters < 0)
+        return fail(PKV_EINVAL, "%s: NULL sink, bad sink_len or negative iters", who);
+    if (kind < 0 || kind > 5) return fail(PKV_EINVAL, "%s: kind must be 0 .. 5", who);
+    if (waves_per_simd < 1 || waves_per_simd > 8)
+        return fail(PKV_EINVAL, "%s: waves_per_simd must be 1 .. 8", who);
+    // workgroups of 4 waves, one per SIMD of a CU: waves_per_simd workgroups per CU
+    const dim3 grid(unsigned(pkv::device_cus() * waves_per_simd));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const pkv::LaunchEvents ev = pkv::timer_events(PKV_TIMER_MEASURE);
+    switch (kind) {
+    case 0: hipExtLaunchKernelGGL(pkv::rate_lds_kernel, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
+    case 1: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<1>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
+    case 2: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<2>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
+    case 3: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<3>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
+    case 4: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<4>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
+    default: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<5>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
+    }
+    const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(PKV_EHIP, "%s: launch failed: %s", who, hipGetErrorString(err));
     return pkv::ok();
 }

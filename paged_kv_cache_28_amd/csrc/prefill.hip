@@ -105,6 +105,14 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// acc + lo + hi of a word holding two fp16 values (one dot-product instruction, the two
+// products with 1.0 exact, the sum rounded once to fp32).
+__device__ __forceinline__ float sum_f16x2(uint32_t w, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), one, acc, false);
+}
+
 // Query tokens per wave: the 16 * NC columns hold whole tokens' G heads.
 __host__ __device__ constexpr int prefill_wave_tokens(int G) { return 16 * kPrefillNC / G; }
 
@@ -405,14 +413,16 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
             float pe[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(__builtin_fmaf(x[ct][e], a.scale_log2, nm[ct]));
-            lsum[ct] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
             if constexpr (kMode == kHalfP) {
-                // one fp16 rounding per weight (weights in (2^-21, 2^15] before underflow)
+                // one fp16 rounding per weight (weights in (2^-21, 2^15] before underflow);
+                // the sum is of the same rounded weights, two per dot-product instruction
                 const uint4 ph = make_uint4(pack_f16x2(pe[0], pe[1]), pack_f16x2(pe[2], pe[3]),
                                             pack_f16x2(pe[4], pe[5]), pack_f16x2(pe[6], pe[7]));
+                lsum[ct] = sum_f16x2(ph.w, sum_f16x2(ph.z, sum_f16x2(ph.y, sum_f16x2(ph.x, lsum[ct]))));
 #pragma unroll
                 for (int c = 0; c < NPV; ++c) acc[ct][c] = Mfma<PV>::qk(v[c], ph, acc[ct][c]);
             } else {
+                lsum[ct] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
                 uint16_t hi[8], lo[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) Mfma<T>::split(pe[e], hi[e], lo[e]);
@@ -456,8 +466,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
         ids = stage_ids(min(1, S - 1));
         store(lds4);
         __syncthreads();
-        for (int s = 0; s < S; ++s) {
-            const uint4* cur = lds4 + (s & 1) * STAGE_CH;
+        // stage s reads buffer s % 2 and writes the other; the loop takes two stages per
+        // iteration so that both buffers' addresses are constants folded into the LDS
+        // instructions' offsets
+        auto stage = [&](int s, auto parity) __attribute__((always_inline)) {
+            constexpr int P = decltype(parity)::value;
+            const uint4* cur = lds4 + P * STAGE_CH;
             issue(ids);                                 // stage min(s + 1, S - 1)
             ids = stage_ids(min(s + 2, S - 1));
             uint4 ka[NQK], kb[NQK];
@@ -467,8 +481,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
                 const int kp = s * kStageKeys + 32 * m;
                 if (kp < wave_end) compute_pair(cur, kp, m, ka, kb);
             }
-            store(lds4 + ((s + 1) & 1) * STAGE_CH);
+            store(lds4 + (1 - P) * STAGE_CH);
             __syncthreads();
+        };
+        for (int s = 0; s < S; s += 2) {
+            stage(s, std::integral_constant<int, 0>{});
+            if (s + 1 < S) stage(s + 1, std::integral_constant<int, 1>{});
         }
     }
 

@@ -96,3 +96,46 @@ def test_gather_reads_the_decode_tiles(dtype, bs, mode, nt, invalid, device):
                        balanced=(mode == "balanced"), nontemporal=nt)
     torch.cuda.synchronize()
     assert _sink_xor(sink) == want
+
+
+def _lds_rate_sink(iters):
+    """Host model of pkv_measure_rate kind 0: the XOR of every chunk word read by each of a
+    workgroup's 4 waves (chunk i holds (i, 3i, 5i, 7i) as 32-bit words)."""
+    tid = np.arange(256, dtype=np.int64)
+    x = np.zeros(256, dtype=np.uint32)
+    for k in range(8 * iters):
+        i = ((k * 257 + tid) & 1023).astype(np.uint32)
+        x ^= i ^ (np.uint32(3) * i) ^ (np.uint32(5) * i) ^ (np.uint32(7) * i)
+    return [int(np.bitwise_xor.reduce(x[64 * w:64 * (w + 1)])) for w in range(4)]
+
+
+@pytest.mark.parametrize("wps", [1, 2, 8])
+def test_rate_probes_read_and_write_what_they_claim(wps, device):
+    """LDS reads: every wave's sink slot equals the host model's XOR; the arithmetic kinds
+    write every wave's slot and nothing past them."""
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    waves = cus * 4 * wps
+    sentinel = 0x5A5A5A5A
+    sink = torch.full((waves + 64,), sentinel, dtype=torch.int32, device=device)
+    pkv.measure_rate("lds_read", wps, 5, sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    want = np.array(_lds_rate_sink(5) * (waves // 4), dtype=np.uint32)
+    assert np.array_equal(got[:waves], want)
+    assert np.all(got[waves:] == sentinel)
+    for kind in pkv.RATE_KINDS[1:]:
+        sink.fill_(sentinel)
+        pkv.measure_rate(kind, wps, 3, sink)
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32)
+        assert np.count_nonzero(got[:waves] == sentinel) == 0, kind
+        assert np.all(got[waves:] == sentinel), kind
+
+
+def test_rate_probe_rejects_bad_arguments(device):
+    sink = torch.zeros(16, dtype=torch.int32, device=device)
+    for kind, wps, iters in ((6, 1, 1), (-1, 1, 1), (0, 0, 1), (0, 9, 1), (1, 1, -1)):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv._check(pkv.lib().pkv_measure_rate(kind, wps, iters, pkv._dev(sink, "sink"),
+                                                  sink.numel(), pkv._stream(sink, None)))
+        assert e.value.code == pkv.PKV_EINVAL

@@ -31,16 +31,21 @@ def _errors(n, rows, seed):
     exact = (p @ v) / p.sum(1, keepdims=True)
     p32 = p.astype(np.float32)
     out = {}
-    for name, rounded in (("bf16", _bf16(p32)), ("f16", p32.astype(np.float16).astype(np.float32))):
-        got = (rounded.astype(np.float64) @ v) / p32.astype(np.float64).sum(1, keepdims=True)
+    f16 = p32.astype(np.float16).astype(np.float32)
+    # (weights in the product, weights in the sum): bf16 and fp16 roundings over the fp32
+    # sum, and fp16 weights in both (the prefill kernel's form: its sum is of the rounded
+    # weights, accumulated in fp32)
+    for name, num, den in (("bf16", _bf16(p32), p32), ("f16", f16, p32), ("f16_self", f16, f16)):
+        got = (num.astype(np.float64) @ v) / den.astype(np.float64).sum(1, keepdims=True)
         err = np.abs(got - exact).max()
         out[name] = (err, err / np.abs(exact).max())
     return out
 
 
 @pytest.mark.parametrize("n,rows", [(2, 2048), (3, 2048), (5, 2048), (256, 1024), (4096, 96)])
-def test_fp16_weights_meet_the_bars(n, rows):
-    err, norm = _errors(n, rows, seed=n)["f16"]
+@pytest.mark.parametrize("form", ["f16", "f16_self"])
+def test_fp16_weights_meet_the_bars(form, n, rows):
+    err, norm = _errors(n, rows, seed=n)[form]
     assert err <= 1e-3 and norm <= 5e-4, (err, norm)
 
 
