@@ -238,6 +238,7 @@ def bench_rates():
             "exp_per_s": float(f"{lanes * iters * 8 / t['exp'] * 1e3:.4g}"),
             "fma_per_s": float(f"{lanes * iters * 8 / t['fma'] * 1e3:.4g}"),
             "mfma_TFLOP/s": round(waves * iters * 4 * 16384 / t["mfma"] / 1e9, 1),
+            "mfma_16x16x16_TFLOP/s": round(waves * iters * 4 * 8192 / t["mfma_16x16x16"] / 1e9, 1),
             "overlap_mfma_exp": round(t["mfma_exp"] / (t["mfma"] + t["exp"]), 3),
             "overlap_mfma_16fma": round(t["mfma_fma"] / (t["mfma"] + 2 * t["fma"]), 3),
         })

@@ -141,7 +141,7 @@ int pkv_measure_gather(const void* k_cache, const void* v_cache, const int32_t* 
  * array whose chunk i holds (i, 3i, 5i, 7i), folded by XOR); 1, 8 exponentials (v_exp_f32)
  * in independent chains; 2, 8 FMAs; 3, 4 bf16 16x16x32 matrix products (4 accumulators);
  * 4, kind 3's products with kind 1's exponentials between them; 5, the 4 products with 16
- * FMAs between them. Used to set the prefill kernel's mix of matrix and vector work
+ * FMAs between them; 6, 4 bf16 16x16x16 products (half of kind 3's work per instruction). Used to set the prefill kernel's mix of matrix and vector work
  * against what the hardware overlaps (the prefill steps of "vLLM Nedir? PagedAttention ile
  * Production LLM Serving", section "Chunked prefill"). Errors: EINVAL, EHIP. */
 int pkv_measure_rate(int32_t kind, int32_t waves_per_simd, int32_t iters, uint32_t* sink,

@@ -798,7 +798,7 @@ def measure_gather(k_cache, v_cache, block_tables, seq_lens, sink, seq_order=Non
                                     _stream(k_cache, stream)))
 
 
-RATE_KINDS = ("lds_read", "exp", "fma", "mfma", "mfma_exp", "mfma_fma")
+RATE_KINDS = ("lds_read", "exp", "fma", "mfma", "mfma_exp", "mfma_fma", "mfma_16x16x16")
 
 
 def measure_rate(kind: str, waves_per_simd: int, iters: int, sink, stream=None):

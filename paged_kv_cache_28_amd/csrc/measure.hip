@@ -250,7 +250,8 @@ __global__ __launch_bounds__(256) void rate_lds_kernel(int32_t iters, uint32_t* 
 
 // Per iteration and lane: kind 1: 8 exponentials (independent chains); 2: 8 FMAs; 3: 4
 // products (4 accumulator chains); 4: 4 products and 8 exponentials; 5: 4 products and 16
-// FMAs, the vector instructions placed between the products.
+// FMAs, the vector instructions placed between the products; 6: 4 products of the
+// 16x16x16 bf16 form (half the work of kind 3's per instruction).
 template <int KIND>
 __global__ __launch_bounds__(256) void rate_alu_kernel(int32_t iters, uint32_t* sink, int32_t sink_len) {
     typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -292,6 +293,13 @@ __global__ __launch_bounds__(256) void rate_alu_kernel(int32_t iters, uint32_t* 
 #pragma unroll
                 for (int k = 4; k < 8; ++k) y[k] = __builtin_fmaf(y[k], 0.999f, 1e-3f);
             }
+        } else if constexpr (KIND == 6) {
+            typedef short i16x4_t __attribute__((ext_vector_type(4)));
+            const i16x4_t a4 = __builtin_bit_cast(i16x4_t, a.lo), b4 = __builtin_bit_cast(i16x4_t, b.lo);
+            c0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a4, b4, c3, 0, 0, 0);
         } else {
             c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
             c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
@@ -420,7 +428,7 @@ extern "C" int pkv_measure_rate(int32_t kind, int32_t waves_per_simd, int32_t it
     const char* who = "pkv_measure_rate";
     if (!sink || sink_len <= 0 || iters < 0)
         return fail(PKV_EINVAL, "%s: NULL sink, bad sink_len or negative iters", who);
-    if (kind < 0 || kind > 5) return fail(PKV_EINVAL, "%s: kind must be 0 .. 5", who);
+    if (kind < 0 || kind > 6) return fail(PKV_EINVAL, "%s: kind must be 0 .. 6", who);
     if (waves_per_simd < 1 || waves_per_simd > 8)
         return fail(PKV_EINVAL, "%s: waves_per_simd must be 1 .. 8", who);
     // workgroups of 4 waves, one per SIMD of a CU: waves_per_simd workgroups per CU
@@ -433,7 +441,8 @@ extern "C" int pkv_measure_rate(int32_t kind, int32_t waves_per_simd, int32_t it
     case 2: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<2>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
     case 3: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<3>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
     case 4: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<4>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
-    default: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<5>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
+    case 5: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<5>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
+    default: hipExtLaunchKernelGGL(pkv::rate_alu_kernel<6>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, iters, sink, sink_len); break;
     }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(PKV_EHIP, "%s: launch failed: %s", who, hipGetErrorString(err));

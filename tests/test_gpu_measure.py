@@ -134,7 +134,7 @@ def test_rate_probes_read_and_write_what_they_claim(wps, device):
 
 def test_rate_probe_rejects_bad_arguments(device):
     sink = torch.zeros(16, dtype=torch.int32, device=device)
-    for kind, wps, iters in ((6, 1, 1), (-1, 1, 1), (0, 0, 1), (0, 9, 1), (1, 1, -1)):
+    for kind, wps, iters in ((7, 1, 1), (-1, 1, 1), (0, 0, 1), (0, 9, 1), (1, 1, -1)):
         with pytest.raises(pkv.PkvError) as e:
             pkv._check(pkv.lib().pkv_measure_rate(kind, wps, iters, pkv._dev(sink, "sink"),
                                                   sink.numel(), pkv._stream(sink, None)))
