@@ -239,7 +239,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
     // m_ref: the column's reference point (log2 domain); nm: the offset its weights take,
     // -m_ref, or 0 while the column has seen no real key (m_ref = -inf), where every
     // logit is -inf too and the weights must stay 0 instead of exp2(-inf + inf)
-    float m_ref[NC], nm[NC], thr[NC], lsum[NC];   // thr = m_ref + kSlack
+    // thr = m_ref + kSlack; thr_raw = thr / scale_log2, against which each lane tests its
+    // raw maximum (a lane past it leads to the exact test bm > thr)
+    float m_ref[NC], nm[NC], thr[NC], thr_raw[NC], lsum[NC];
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
 #pragma unroll
@@ -247,6 +249,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
         m_ref[ct] = -INFINITY;
         nm[ct] = 0.f;
         thr[ct] = -INFINITY;
+        thr_raw[ct] = -INFINITY;
         lsum[ct] = 0.f;
     }
 
@@ -386,9 +389,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
             const float t1 = vmax3(x[ct][3], x[ct][4], x[ct][5]);
             const float t2 = vmax3(x[ct][6], x[ct][7], t0);
             lm[ct] = vmax3(t1, t2, t2);
-            // rounding is monotonic, so some lane of a column passes this test exactly when
-            // the column's maximum, scaled, passes it
-            lane_move |= lm[ct] * a.scale_log2 > thr[ct];
+            // while no lane passes, every visible x has x * scale <= thr * (1 + 2^-24), so the
+            // weights stay within 2^15 to an ulp (thr_raw overflows to +inf only where no
+            // finite x * scale can exceed thr)
+            lane_move |= lm[ct] > thr_raw[ct];
         }
         if (__builtin_amdgcn_ballot_w64(lane_move)) {
 #pragma unroll
@@ -405,6 +409,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
                 m_ref[ct] = mn;
                 nm[ct] = mn == -INFINITY ? 0.f : kPOffset - mn;
                 thr[ct] = mn + kSlack;
+                thr_raw[ct] = thr[ct] / a.scale_log2;
             }
         }
 #pragma unroll
