@@ -228,3 +228,58 @@ def test_prefill_ignores_huge_values_past_the_sequence(device):
     got, ref, qs = _run_edited(w, spec, [], device, gpu_only=gpu_only)
     for b in range(len(spec)):
         _check_seq(got, ref, qs, b, w.dtype, f"seq {b}")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_prefill_v_beyond_fp16_range_at_other_block_sizes(bs, device):
+    """The redo pass at 8 and 32 tokens per block (bf16 output): the marked waves' rows
+    against the oracle within the normalised bar, the others within the usual bars."""
+    w = dataclasses.replace(SHAPES["bf16-d128-g4"], block_size=bs)
+    spec = CASES["chunks"]
+    edits = [(2, 150, [5, 77], 65536.0), (4, 999, [127], -98304.0), (0, 39, [64], 70144.0)]
+    got, ref, qs = _run_edited(w, spec, edits, device, torch.bfloat16)
+    for b in range(len(spec)):
+        _check_seq(got, ref, qs, b, w.dtype, f"bs {bs} seq {b}", normalised_only=b in (0, 2, 4),
+                   half_ulp=True)
+
+
+def test_prefill_v_beyond_fp16_range_group_of_16(device):
+    """The redo pass with a GQA group of 16 (a wave's 32 columns are 2 tokens)."""
+    w = SHAPES["bf16-d128-g16"]
+    spec = CASES["mixed"]              # single-query rows beside chunks
+    edits = [(0, 500, [1], 65536.0), (3, 200, [100, 101], -131072.0)]
+    got, ref, qs = _run_edited(w, spec, edits, device)
+    for b in range(len(spec)):
+        _check_seq(got, ref, qs, b, w.dtype, f"g16 seq {b}", normalised_only=b in (0, 3))
+
+
+def test_prefill_fp16_cache_extremes(device):
+    """An fp16 cache goes through the one-product form directly (its V is fp16 already):
+    V at +-65504 and at subnormals against the oracle."""
+    w = SHAPES["f16-d64-g8"]
+    spec = CASES["chunks"]
+    got_edits = []
+    for b, pos, dims, value in [(1, 50, [3], 65504.0), (1, 51, [4], -65504.0),
+                                (3, 10, [0, 1], 2.0 ** -24), (3, 11, [2], -3 * 2.0 ** -24)]:
+        got_edits.append((b, pos, dims, value))
+    lens = [n for n, _ in spec]
+    chunk = [L for _, L in spec]
+    ob = paged_batch.build(w, lens=lens, seed_stream=5)
+    gb = gpu_batch.build(ob, device)
+    bs = w.block_size
+    for b, pos, dims, value in got_edits:
+        blk, off = int(ob.tables[b][pos // bs]), pos % bs
+        bits = int(torch.tensor([value], dtype=torch.float16).view(torch.int16).item()) & 0xFFFF
+        for d in dims:
+            ob.v_cache[blk, :, d, off] = bits
+            gb.v_cache[blk, :, d, off] = value
+    q = workloads.draw_q(w, workloads.rng(w.seed, 63), batch=int(sum(chunk)))
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32, device=device)
+    pkv.paged_attention_prefill(out, q.to(device), torch.from_numpy(qs).to(device), gb.k_cache,
+                                gb.v_cache, gb.tables_d, gb.lens_d, w.scale, max(chunk))
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q, qs, ob.k_cache, ob.v_cache, ob.tables, ob.lens, w.scale, w.dtype)
+    got = out.cpu().double().numpy()
+    for b in range(len(spec)):
+        _check_seq(got, ref, qs, b, w.dtype, f"f16 seq {b}", normalised_only=b == 1)
