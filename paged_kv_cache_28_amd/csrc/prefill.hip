@@ -6,17 +6,19 @@
 // ve ölçekleme", section "4. Prefill ve decode"). With many queries per sequence the work
 // is a dense contraction, so it runs on the matrix cores.
 //
-// Work decomposition: one workgroup of 4 waves per (query tile, KV head, sequence). The
+// Work decomposition: one workgroup of 8 waves per (query tile, KV head, sequence). The
 // 16 columns of the matrix products are (query token, head of the GQA group) pairs; each
 // wave owns NC column tiles of its own (16 * NC columns, 16 * NC / G query tokens), so a
-// workgroup covers 4 * 16 * NC columns. The context is walked in stages of 64 keys that
-// the workgroup stages in LDS once and all four waves read: each K/V byte fetched from L2
-// feeds 4 * 16 * NC columns. (A design in which the 4 waves shared one set of columns and
+// workgroup covers 8 * 16 * NC columns. The context is walked in stages of 64 keys that
+// the workgroup stages in LDS once and all eight waves read: each K/V byte fetched from
+// L2 feeds 8 * 16 * NC columns. (A design in which 4 waves shared one set of columns and
 // split the keys fed each fetched byte to 16 * NC columns only; it needed about the whole
 // L2 bandwidth to reach 23% of the matrix-core peak.) A stage is loaded into registers by
-// all 256 threads while the previous one is computed, and written to the other of two LDS
+// all 512 threads while the previous one is computed, and written to the other of two LDS
 // buffers after it: one barrier per stage. Each wave keeps its own online softmax per
-// column and writes its rows itself.
+// column and writes its rows itself. At two waves per SIMD (about 230 VGPRs) a CU holds
+// one such workgroup; with 4 waves per workgroup (two per CU) each thread staged twice
+// the bytes, and the kernel ran 8% slower.
 //
 // Per pair of 32 keys of a stage and column tile:
 //   S_A^T, S_B^T[16 keys][16 cols] = K_rows x Q^T          (16x16x32, d/32 steps each)
@@ -74,9 +76,9 @@ struct PrefillArgs {
     uint32_t q_sign;           // 0x80008000 when scale < 0: the queries' signs are flipped
 };
 
-constexpr int kPrefillWaves = 4;
+constexpr int kPrefillWaves = 8;
 constexpr int kPrefillNC = 2;       // column tiles per wave
-constexpr int kStageKeys = 64;      // keys per LDS stage (two pairs)
+constexpr int kStageKeys = 64;      // keys per LDS stage (kStageKeys / 32 pairs)
 constexpr float kSlack = 8.0f;      // lazy reference point, as in the decode kernel
 constexpr float kPOffset = 7.0f;    // one-product form: weights 2^(x - m + 7) <= 2^15
 
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
                 sb[ct] = Mfma<T>::qk(kb[c], qf[ct][c], sb[ct]);
             }
         }
-        if (m == 0) load_k(buf, 1, ka, kb);   // the next pair's K, while this one's softmax runs
+        if (m + 1 < kStageKeys / 32) load_k(buf, m + 1, ka, kb);
         // raw logits (scale applied below): the causal diagonal, the sequence end and tiles
         // that see none of the pair take -inf per key
         bool masked = false;
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
             uint4 ka[NQK], kb[NQK];
             load_k(cur, 0, ka, kb);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
+            for (int m = 0; m < kStageKeys / 32; ++m) {
                 const int kp = s * kStageKeys + 32 * m;
                 if (kp < wave_end) compute_pair(cur, kp, m, ka, kb);
             }
