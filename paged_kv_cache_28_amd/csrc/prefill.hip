@@ -78,14 +78,18 @@ struct PrefillArgs {
 
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillNC = 2;       // column tiles per wave
-constexpr int kStageKeys = 64;      // keys per LDS stage (kStageKeys / 32 pairs)
+// Keys per LDS stage (stage_keys / 32 pairs): 96 for head size 128, whose stage the 512
+// threads load in exactly three 16-byte loads each (2% faster than 64 keys); 64 for head
+// size 64 (one load each).
+template <int D>
+__host__ __device__ constexpr int stage_keys() { return D == 128 ? 96 : 64; }
 constexpr float kSlack = 8.0f;      // lazy reference point, as in the decode kernel
 constexpr float kPOffset = 7.0f;    // one-product form: weights 2^(x - m + 7) <= 2^15
 
 // One LDS stage: K and V of 64 keys, D dims, 16-bit elements; two stages in flight.
 template <int D>
 __host__ __device__ constexpr size_t prefill_stage_bytes() {
-    return size_t(2) * kStageKeys * D * 2;
+    return size_t(2) * stage_keys<D>() * D * 2;
 }
 template <int D>
 __host__ __device__ constexpr size_t prefill_lds_bytes() {
@@ -162,7 +166,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
     constexpr int W = kPrefillWaves, NC = kPrefillNC;
     constexpr int NQK = D / 32, NPV = D / 16;
     constexpr int NG = D / 8;                           // 16-byte K dim groups
+    constexpr int kStageKeys = stage_keys<D>();
     constexpr int NLD = kStageKeys * D * 2 / 16 / (W * 64);   // 16-byte loads per thread, K and V each
+    static_assert(NLD * 16 * W * 64 == kStageKeys * D * 2, "the threads' loads cover a stage exactly");
     constexpr int KCH = kStageKeys * NG;                // K chunks per stage
     constexpr int STAGE_CH = 2 * KCH;                   // K + V chunks per stage
     static_assert(NLD >= 1 && (NG * BS) % 64 == 0, "a load instruction stays in one block");
