@@ -524,8 +524,13 @@ int paged_attention_decode_noalloc(void* out, const void* q, int64_t q_stride, c
  *   out:     device [q_start[num_seqs]][num_heads][head_dim], out_dtype (in_dtype or F32),
  *            16-byte aligned.
  *   caches, block_tables, seq_lens as paged_attention_decode (16-bit caches).
- * Supported: head_dim 64 or 128, num_heads / num_kv_heads <= 16. The launch stages 64 KiB
- * (head_dim 128) or 32 KiB (64) of LDS per workgroup.
+ * Supported: head_dim 64 or 128, num_heads / num_kv_heads <= 16; max_q_len up to 65,535
+ * query tiles of 8 * floor(32 / G) tokens (G = num_heads / num_kv_heads; EINVAL beyond).
+ * The launch stages 96 KiB (head_dim 128) or 32 KiB (64) of LDS per workgroup. The
+ * weights enter the value product rounded once to fp16 (relative error at most 2^-11)
+ * and V in fp16; with a bf16 cache a second launch on the same stream redoes, with the
+ * weights split in two bf16 parts, any workgroup that met a V value of magnitude 2^16 or
+ * more (beyond fp16), so the result is defined for every finite input.
  * Errors: EINVAL, ENOTSUP (dtypes, head_dim, group size), EHIP. */
 int paged_attention_prefill(void* out, const void* q, int64_t q_stride, const int32_t* q_start,
                             const void* k_cache, const void* v_cache, const int32_t* block_tables,

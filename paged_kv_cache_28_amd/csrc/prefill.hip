@@ -176,9 +176,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int col = lane & 15, quad = lane >> 4;
-    // query tiles in reverse: under the causal mask a later tile sees more keys, so the
-    // longest workgroups are dispatched first and the short ones fill the tail
-    const int qt = int(gridDim.x) - 1 - int(blockIdx.x), g = blockIdx.y, b = blockIdx.z;
+    // KV heads fastest: consecutive workgroups go to the XCDs in turn, so (at 8 KV heads)
+    // each XCD's L2 serves one head's K/V stages to all of its CUs, which walk the keys in
+    // step (8% faster than query tiles fastest). Query tiles in reverse: under the causal
+    // mask a later tile sees more keys, so the longest workgroups are dispatched first and
+    // the short ones fill the tail.
+    const int qt = int(gridDim.y) - 1 - int(blockIdx.y), g = blockIdx.x, b = blockIdx.z;
     const int G = a.group;
     const int TW = prefill_wave_tokens(G);              // query tokens per wave
     const int QT = W * TW;                              // per workgroup
@@ -546,7 +549,7 @@ template <typename T, int D, typename OutT, int BS>
 hipError_t launch_prefill(const PrefillArgs& a, int max_q_len, int num_kv_heads, int num_seqs,
                           hipStream_t s) {
     const int qt_tokens = kPrefillWaves * prefill_wave_tokens(a.group);
-    const dim3 grid(unsigned((max_q_len + qt_tokens - 1) / qt_tokens), unsigned(num_kv_heads),
+    const dim3 grid(unsigned(num_kv_heads), unsigned((max_q_len + qt_tokens - 1) / qt_tokens),
                     unsigned(num_seqs));
     const LaunchEvents ev = timer_events(PKV_TIMER_PREFILL);
     constexpr bool redo = std::is_same<T, bf16_t>::value;
@@ -624,7 +627,7 @@ extern "C" int paged_attention_prefill(void* out, const void* q, int64_t q_strid
          reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out)) & 15)
         return fail(PKV_EINVAL, "%s: q, out and the caches must be 16-byte aligned", who);
     const int qt_tokens = pkv::kPrefillWaves * pkv::prefill_wave_tokens(G);
-    if ((int64_t(max_q_len) + qt_tokens - 1) / qt_tokens > 0x7fffffff)
+    if ((int64_t(max_q_len) + qt_tokens - 1) / qt_tokens > 65535)
         return fail(PKV_EINVAL, "%s: max_q_len too large", who);
     pkv::PrefillArgs a;
     a.out = out;
