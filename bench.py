@@ -300,26 +300,31 @@ def bench_copy_blocks(args):
 
 def bench_cache_write_sweep(args):
     """reshape_and_cache (and its FP8 form) on the 8B shape (8 KV heads, d 128, bf16 rows) for
-    prompt-sized and decode-sized token counts, with consecutive slots (a prompt or chunk) and
-    scattered ones (one token each of many sequences), timed with the library's kernel timer
-    (median of 20 launches over a pool larger than the Infinity Cache)."""
+    prompt-sized and decode-sized token counts, with consecutive slots (a prompt or chunk in
+    consecutive blocks), a prompt's slots in blocks placed at random (as the pool hands them
+    out after churn), and scattered ones (one token each of many sequences), timed with the
+    library's kernel timer (median of 20 launches over a pool larger than the Infinity
+    Cache)."""
     import numpy as np
     import torch
 
     import paged_kv_cache_28_amd as pkv
     dev = torch.device("cuda:0")
     Hkv, d = 8, 128
-    nb = 40000                                        # 655 MB per cache pair in bf16
+    nb = 70000                                        # 4.6 GB per cache pair in bf16
     rows = {}
     for cache in ("bf16", "fp8"):
         kc, vc = pkv.alloc_caches(nb, Hkv, d, cache, dev, fill=0)
-        for T in (64, 256, 1024, 4096, 16384):
+        for T in (64, 256, 1024, 4096, 16384, 65536):
             src = torch.randn((T, Hkv, d), device=dev).to(torch.bfloat16)
             gen = np.random.default_rng(T)
-            for pattern in ("consecutive", "scattered"):
+            for pattern in ("consecutive", "blocks", "scattered"):
                 if pattern == "consecutive":
                     start = int(gen.integers(0, nb * 16 - T))
                     slots = np.arange(start, start + T, dtype=np.int32)
+                elif pattern == "blocks":   # a prompt's slots: whole blocks, placed at random
+                    blk = gen.permutation(nb)[:-(-T // 16)]
+                    slots = (blk[:, None] * 16 + np.arange(16)).ravel()[:T].astype(np.int32)
                 else:
                     slots = (gen.permutation(nb)[:T] * 16 + gen.integers(0, 16, T)).astype(np.int32)
                 sl = torch.from_numpy(slots).to(dev)

@@ -82,8 +82,13 @@ __global__ __launch_bounds__(64) void reshape_and_cache_rows_kernel(
     const int vpad = nchunk + 1;            // LDS row pitch of V (uint4), padded
     uint4* Kl = s_rows;                     // group c of token r at c * 17 + r
     uint4* Vl = s_rows + nchunk * 17;       // token r's V row at r * vpad
-    const int g = blockIdx.y;
-    const int64_t t0 = int64_t(blockIdx.x) * 16;
+    // KV heads fastest: consecutive workgroups write the head tiles of the same blocks,
+    // which lie next to each other in the cache. With heads in the slow dimension, the
+    // waves running at once wrote one head's tiles of consecutive blocks, 32 KiB apart
+    // (bf16, 8 heads): 3.97 against 6.18 TB/s for 65,536 consecutive slots on MI355X.
+    const int64_t wg = blockIdx.x;
+    const int g = int(wg % hkv);
+    const int64_t t0 = (wg / hkv) * 16;
     const int lane = threadIdx.x;
     const int bs = 1 << lbs;
     // this lane's token for the writes (r = lane % 16) and its slot
@@ -331,11 +336,11 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
     // (pitch d/x + 1)
     const int64_t rtiles = (int64_t(num_tokens) + 15) / 16;
     const size_t rlds = sizeof(uint4) * size_t(head_dim / x) * (17 + 16) + sizeof(uint4) * 16;
-    const bool rows = rtiles * num_kv_heads >= pkv::device_cus() && rtiles <= 0x7fffffff &&
-                      num_kv_heads <= 65535 && rlds <= 65536;
+    const bool rows = rtiles * num_kv_heads >= pkv::device_cus() &&
+                      rtiles * num_kv_heads <= 0x7fffffff && rlds <= 65536;
     const int64_t kst = key_stride * e, vst = value_stride * e;
     if (rows) {
-        const dim3 rgrid{unsigned(rtiles), unsigned(num_kv_heads), 1u};
+        const dim3 rgrid{unsigned(rtiles * num_kv_heads), 1u, 1u};
         if (e == 2)
             hipExtLaunchKernelGGL(pkv::reshape_and_cache_rows_kernel<2>, rgrid, dim3(64), rlds, s,
                                   ev.start, ev.stop, 0, kp, vp, kcp, vcp, slot_mapping, num_tokens,
