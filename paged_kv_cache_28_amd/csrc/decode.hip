@@ -237,8 +237,9 @@ int decode_impl(const char* who, void* out, float* part_out, float* part_max, fl
     // 70B batch 397.5 -> 337.8 us, the 131K-262K-token batch 602-610 -> 573-580 us; the 8B
     // batch (at most 4 partitions per sequence, most sequences in one or two) 63.0 -> 64.4
     // us, so short tables keep the W waves per partition.
+    // (32-token blocks in partitions of whole blocks take the whole-block kernel instead)
     a.per_wave = !split && grid_parts >= 2 * pkv::kWaves && in_dtype != PKV_F32 &&
-                 !(fp8 && block_size == 32 && part_tiles % 2 == 0);
+                 !(block_size == 32 && part_tiles % 2 == 0);
     const int grid_slots = a.per_wave ? (grid_parts + pkv::kWaves - 1) / pkv::kWaves : grid_parts;
     a.heads_fastest = grid_slots < 8;
     a.lpt_round = 0;

@@ -655,29 +655,41 @@ __global__ __launch_bounds__(W * 64) void decode_mfma_kernel(DecodeArgs a) {
     merge_and_store<OutT, D, W>(a, sm_m, sm_l, sm_o, b, g, p, direct);
 }
 
-// ------------------------------------------------ FP8 cache, 32-token blocks, whole blocks
-// FP8 caches at 32 tokens per block, single pass or partitions of whole blocks. The 16-token
-// tiles of decode_mfma_kernel read half of every 32-byte V row there, so each V load
-// instruction touches twice the sectors of the 16-token case. Here a wave takes whole
-// blocks: the two QK products of a block read their K rows in a permuted order (MFMA row r
-// of product A: position 8 (r / 4) + r % 4 of the block, of product B that + 4), so lane l
-// holds the logits of positions 8 (l/16) .. + 7, which are its 8 k-slots of one 16x16x32
-// PV product in both operands. Its V operand is then one 8-byte load of those 8 positions
-// of a dimension row: the block's V rows are read whole, with half the load instructions.
+// ------------------------------------------------ 32-token blocks, whole blocks
+// Caches at 32 tokens per block (FP8 and 16-bit), single pass or partitions of whole
+// blocks. The 16-token tiles of decode_mfma_kernel read half of every V row there (32 of
+// 64 bytes at 16 bits, 16 of 32 at FP8), so each V load instruction touches twice the
+// sectors of the 16-token case and the other half is fetched again by another wave. Here
+// a wave takes whole blocks: the two QK products of a block read their K rows in a
+// permuted order (MFMA row r of product A: position 8 (r / 4) + r % 4 of the block, of
+// product B that + 4), so lane l holds the logits of positions 8 (l/16) .. + 7, which are
+// its 8 k-slots of one 16x16x32 PV product in both operands. Its V operand is then one
+// load of those 8 positions of a dimension row (8 bytes of codes, or 16 bytes at 16 bits):
+// the block's V rows are read whole, with half the load instructions.
 // Softmax, reference points, merging and the fused append are those of decode_mfma_kernel.
-template <int D> struct KvBlock32 {
+template <int D, bool F8> struct KvBlock32;
+template <int D> struct KvBlock32<D, true> {
     uint4 ka[D / 64];   // K rows of product A: 16 codes (dims 16 (4 i + quad) ..) each
     uint4 kb[D / 64];   // product B
     uint2 v[D / 16];    // positions 8 quad .. + 7 of dimension 16 c + col
 };
+template <int D> struct KvBlock32<D, false> {
+    uint4 ka[D / 32];   // K rows of product A: dims 32 c + 8 quad .. + 7 (QK step c)
+    uint4 kb[D / 32];   // product B
+    uint4 v[D / 16];    // positions 8 quad .. + 7 of dimension 16 c + col
+};
 
-template <typename T, int D, typename OutT, int W, bool Append>
-__global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) {
+// A wave keeps 16 KiB of blocks in flight: two FP8 blocks, or one 16-bit block. On MI355X
+// (8B batch at 32 tokens per block, bf16) two 16-bit blocks per wave, 64 MiB in flight over
+// the chip, took 59.1 us per launch and one 55.6; a gather of the 16-token tiles is also
+// fastest at 16-32 MiB in flight.
+template <typename T, int D, typename OutT, int W, bool Append, bool F8>
+__global__ __launch_bounds__(W * 64) void decode_blk32_kernel(DecodeArgs a) {
     static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
     constexpr int BS = 32;
     constexpr int NQK = D / 32;   // 16x16x32 steps for S
     constexpr int NPV = D / 16;   // 16x16x32 steps for O (32 positions each)
-    constexpr int NKL = D / 64;   // 16-byte K loads per product and lane
+    constexpr int NKL = F8 ? D / 64 : D / 32;   // 16-byte K loads per product and lane
     extern __shared__ float lds[];
     float* sm_m = lds;                  // [W][16]
     float* sm_l = lds + W * 16;         // [W][16]
@@ -711,15 +723,22 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
                                int64_t(g * G + col) * D;
 #pragma unroll
         for (int c = 0; c < NQK; ++c)
-            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + q_dim<true>(c, quad))
+            qf[c] = col < G ? *reinterpret_cast<const uint4*>(qrow + q_dim<F8>(c, quad))
                             : make_uint4(0, 0, 0, 0);
     }
-    // fused append: the new row's codes as this lane holds them for any row (nk: the K
-    // groups 4c + quad of the row; nv: the code of dimension 16c + col)
+    // fused append: every lane loads D/64 consecutive raw elements of the new K and V rows
+    // (nkr, nvr). FP8: the wave that stores the row quantises them, and every lane keeps
+    // the codes it holds in the tile layout (nk: K group 4c + quad; nv: dimension 16c +
+    // col). 16-bit: that wave puts the row into its slice of sm_o (free until the merge;
+    // K at elements [0, D), V at [D, 2D)), read only where the row is substituted or
+    // stored: held in registers through the loop it pushed the two blocks in flight into
+    // scratch.
     int slot = -1;
-    uint4 nk[Append ? NKL : 1];
-    uint32_t nv[Append ? NPV : 1];
+    constexpr bool kRegRow = Append && F8;
+    uint4 nk[kRegRow ? NKL : 1];
+    uint32_t nv[kRegRow ? NPV : 1];
     uint32_t nkr = 0, nvr = 0;
+    uint16_t* nrow = reinterpret_cast<uint16_t*>(sm_o + wave * G * D);
     if constexpr (Append) {
         slot = a.slot_mapping[b];
         const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + int64_t(b) * a.new_k_stride +
@@ -729,9 +748,27 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
         load_new_row_fp8<D>(krow, vrow, lane, nkr, nvr);
     }
     auto quantize_new = [&]() __attribute__((always_inline)) {
-        if constexpr (Append)
+        if constexpr (Append && F8) {
             quantize_new_row_fp8<T, D>(a, reinterpret_cast<uint8_t*>(sm_o + wave * G * D), lane,
                                        nkr, nvr, nk, nv);
+        } else if constexpr (Append) {
+            if constexpr (D == 128) {
+                *reinterpret_cast<uint32_t*>(nrow + 2 * lane) = nkr;
+                *reinterpret_cast<uint32_t*>(nrow + D + 2 * lane) = nvr;
+            } else {
+                nrow[lane] = uint16_t(nkr);
+                nrow[D + lane] = uint16_t(nvr);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
+    auto new_k = [&](int c) __attribute__((always_inline)) -> uint4 {   // K group 4c + quad
+        if constexpr (kRegRow) return nk[c];
+        else return *reinterpret_cast<const uint4*>(nrow + 32 * c + 8 * quad);
+    };
+    auto new_v = [&](int c) __attribute__((always_inline)) -> uint32_t {   // dimension 16c + col
+        if constexpr (kRegRow) return nv[c];
+        else return nrow[D + 16 * c + col];
     };
 
     int n = n_raw < 0 ? 0 : (n_raw > a.max_len ? a.max_len : n_raw);
@@ -740,7 +777,7 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
     if (blk_begin >= nblk) {
         if (p == 0) write_zero_rows<OutT, D>(a, b, g);
         if constexpr (Append)
-            if (p == 0 && n == 0) write_new_token<T, D, true, BS>(a, b, g, slot);
+            if (p == 0 && n == 0) write_new_token<T, D, F8, BS>(a, b, g, slot);
         return;
     }
     const int blk_end = min(nblk, blk_begin + part_blocks);
@@ -765,12 +802,16 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
             if (col == 0) {
 #pragma unroll
                 for (int c = 0; c < NKL; ++c)
-                    *reinterpret_cast<uint4*>(kc + ((tile * (NKL * 4) + 4 * c + quad) * BS + off) * 16) = nk[c];
+                    *reinterpret_cast<uint4*>(kc + ((tile * (NKL * 4) + 4 * c + quad) * BS + off) * 16) = new_k(c);
             }
             if (quad == 0) {
 #pragma unroll
-                for (int c = 0; c < NPV; ++c)
-                    reinterpret_cast<uint8_t*>(vc)[(tile * D + 16 * c + col) * BS + off] = uint8_t(nv[c]);
+                for (int c = 0; c < NPV; ++c) {
+                    if constexpr (F8)
+                        reinterpret_cast<uint8_t*>(vc)[(tile * D + 16 * c + col) * BS + off] = uint8_t(new_v(c));
+                    else
+                        reinterpret_cast<uint16_t*>(vc)[(tile * D + 16 * c + col) * BS + off] = uint16_t(new_v(c));
+                }
             }
         }
     };
@@ -783,40 +824,52 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
 
     const char* kbase = static_cast<const char*>(a.k_cache);
     const char* vbase = static_cast<const char*>(a.v_cache);
-    constexpr int64_t tile_bytes = int64_t(D) * BS;   // one block of one KV head (codes)
+    constexpr int64_t tile_bytes = int64_t(D) * BS * (F8 ? 1 : 2);   // one block of one KV head
     int tab = 0;
 
     // Issue the loads of segment block k; false if its id is invalid (a safe address is
     // read and the block is skipped).
     const uint32_t nb_lim = block_limit(a.num_blocks);
-    auto load = [&](KvBlock32<D>& t, int k) -> bool {
+    auto load = [&](KvBlock32<D, F8>& t, int k) -> bool {
         const int id = __builtin_amdgcn_readlane(tab, k);
         const bool ok = uint32_t(id) < nb_lim;
         const int64_t pa = ok ? id : 0;
         const buf_rsrc_t kr = tile_rsrc(kbase + (pa * a.num_kv_heads + g) * tile_bytes, int(tile_bytes));
         const buf_rsrc_t vr = tile_rsrc(vbase + (pa * a.num_kv_heads + g) * tile_bytes, int(tile_bytes));
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) {
+        for (int i = 0; i < NKL; ++i) {   // K group 4 i + quad of rows ra, rb
             t.ka[i] = bld16(kr, ((4 * i + quad) * BS + ra) * 16);
             t.kb[i] = bld16(kr, ((4 * i + quad) * BS + rb) * 16);
         }
 #pragma unroll
-        for (int c = 0; c < NPV; ++c) t.v[c] = bld8(vr, (16 * c + col) * BS + 8 * quad);
+        for (int c = 0; c < NPV; ++c) {
+            if constexpr (F8)
+                t.v[c] = bld8(vr, (16 * c + col) * BS + 8 * quad);
+            else
+                t.v[c] = bld16(vr, ((16 * c + col) * BS + 8 * quad) * 2);
+        }
         return ok;
     };
-    auto kop = [](const uint4& w, int c) {   // 8 codes of QK step c, widened
-        const uint2 lo = Fp8<T>::x4((c & 1) ? w.z : w.x), hi = Fp8<T>::x4((c & 1) ? w.w : w.y);
-        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    // the K operand of QK step c from the loaded groups (FP8: 8 of 16 codes, widened)
+    auto kop = [](const uint4* w, int c) {
+        if constexpr (F8) {
+            const uint4 q = w[c >> 1];
+            const uint2 lo = Fp8<T>::x4((c & 1) ? q.z : q.x), hi = Fp8<T>::x4((c & 1) ? q.w : q.y);
+            return make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            return w[c];
+        }
     };
 
     // block jb (positions 32 jb .. + 31); positions below lim are valid. An invalid block
     // id (read from block 0) is masked out by arithmetic, not skipped (see decode_mfma_kernel).
-    auto compute = [&](KvBlock32<D>& t, int jb, bool ok) __attribute__((always_inline)) {
+    auto compute = [&](KvBlock32<D, F8>& t, int jb, bool ok) __attribute__((always_inline)) {
         if constexpr (Append) {
             if (subst && jb == jl) {   // wave-uniform: position off of block jl is the new token
                 // MFMA row r of product A holds position 8 (r / 4) + r % 4, of product B that
-                // + 4; V word h of the lanes with quad == off / 8 holds positions 8 quad + 4 h
-                // .. + 3. Bit masks, not selects between arrays (see decode_mfma_kernel).
+                // + 4; in the lanes with quad == off / 8, V word h holds positions 8 quad +
+                // 4 h .. + 3 (codes) or 8 quad + 2 h, + 1 (16-bit). Bit masks, not selects
+                // between arrays (see decode_mfma_kernel).
                 const int off = (n - 1) % BS;
                 const int r = 4 * (off >> 3) + (off & 3);
                 const bool inb = (off & 7) >= 4;
@@ -824,24 +877,41 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
                 const uint32_t mb = col == r && inb ? 0xffffffffu : 0u;
 #pragma unroll
                 for (int c = 0; c < NKL; ++c) {
-                    t.ka[c].x = (t.ka[c].x & ~ma) | (nk[c].x & ma);
-                    t.ka[c].y = (t.ka[c].y & ~ma) | (nk[c].y & ma);
-                    t.ka[c].z = (t.ka[c].z & ~ma) | (nk[c].z & ma);
-                    t.ka[c].w = (t.ka[c].w & ~ma) | (nk[c].w & ma);
-                    t.kb[c].x = (t.kb[c].x & ~mb) | (nk[c].x & mb);
-                    t.kb[c].y = (t.kb[c].y & ~mb) | (nk[c].y & mb);
-                    t.kb[c].z = (t.kb[c].z & ~mb) | (nk[c].z & mb);
-                    t.kb[c].w = (t.kb[c].w & ~mb) | (nk[c].w & mb);
+                    const uint4 w = new_k(c);
+                    t.ka[c].x = (t.ka[c].x & ~ma) | (w.x & ma);
+                    t.ka[c].y = (t.ka[c].y & ~ma) | (w.y & ma);
+                    t.ka[c].z = (t.ka[c].z & ~ma) | (w.z & ma);
+                    t.ka[c].w = (t.ka[c].w & ~ma) | (w.w & ma);
+                    t.kb[c].x = (t.kb[c].x & ~mb) | (w.x & mb);
+                    t.kb[c].y = (t.kb[c].y & ~mb) | (w.y & mb);
+                    t.kb[c].z = (t.kb[c].z & ~mb) | (w.z & mb);
+                    t.kb[c].w = (t.kb[c].w & ~mb) | (w.w & mb);
                 }
-                const uint32_t sh = 8u * uint32_t(off & 3);
                 const bool vq = quad == (off >> 3);
-                const uint32_t mx = vq && !inb ? 0xffu << sh : 0u;
-                const uint32_t my = vq && inb ? 0xffu << sh : 0u;
+                if constexpr (F8) {
+                    const uint32_t sh = 8u * uint32_t(off & 3);
+                    const uint32_t mx = vq && !inb ? 0xffu << sh : 0u;
+                    const uint32_t my = vq && inb ? 0xffu << sh : 0u;
 #pragma unroll
-                for (int c = 0; c < NPV; ++c) {
-                    const uint32_t code = (nv[c] & 0xffu) << sh;
-                    t.v[c].x = (t.v[c].x & ~mx) | (code & mx);
-                    t.v[c].y = (t.v[c].y & ~my) | (code & my);
+                    for (int c = 0; c < NPV; ++c) {
+                        const uint32_t code = (new_v(c) & 0xffu) << sh;
+                        t.v[c].x = (t.v[c].x & ~mx) | (code & mx);
+                        t.v[c].y = (t.v[c].y & ~my) | (code & my);
+                    }
+                } else {
+                    const uint32_t sh = 16u * uint32_t(off & 1);
+                    const int h = (off & 7) >> 1;
+                    const uint32_t mw = 0xffffu << sh;
+                    const uint32_t m0 = vq && h == 0 ? mw : 0u, m1 = vq && h == 1 ? mw : 0u;
+                    const uint32_t m2 = vq && h == 2 ? mw : 0u, m3 = vq && h == 3 ? mw : 0u;
+#pragma unroll
+                    for (int c = 0; c < NPV; ++c) {
+                        const uint32_t e = (new_v(c) & 0xffffu) << sh;
+                        t.v[c].x = (t.v[c].x & ~m0) | (e & m0);
+                        t.v[c].y = (t.v[c].y & ~m1) | (e & m1);
+                        t.v[c].z = (t.v[c].z & ~m2) | (e & m2);
+                        t.v[c].w = (t.v[c].w & ~m3) | (e & m3);
+                    }
                 }
             }
         }
@@ -850,8 +920,8 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
         f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NQK; ++c) {
-            sa = Mfma<T>::qk(kop(t.ka[c >> 1], c), qf[c], sa);
-            sb = Mfma<T>::qk(kop(t.kb[c >> 1], c), qf[c], sb);
+            sa = Mfma<T>::qk(kop(t.ka, c), qf[c], sa);
+            sb = Mfma<T>::qk(kop(t.kb, c), qf[c], sb);
         }
         float x[8];
 #pragma unroll
@@ -876,16 +946,30 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
         for (int e = 0; e < 8; ++e) pe[e] = exp2_fast(x[e] - mref);
         lsum += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
         if (jb * BS + BS > lim_b) {   // partly valid block: rows from lim_b on may hold anything
-            uint32_t m0 = 0, m1 = 0;
+            if constexpr (F8) {
+                uint32_t m0 = 0, m1 = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                m0 |= (p0 + e < lim_b ? 0xffu : 0u) << (8 * e);
-                m1 |= (p0 + 4 + e < lim_b ? 0xffu : 0u) << (8 * e);
-            }
+                for (int e = 0; e < 4; ++e) {
+                    m0 |= (p0 + e < lim_b ? 0xffu : 0u) << (8 * e);
+                    m1 |= (p0 + 4 + e < lim_b ? 0xffu : 0u) << (8 * e);
+                }
 #pragma unroll
-            for (int c = 0; c < NPV; ++c) {
-                t.v[c].x &= m0;
-                t.v[c].y &= m1;
+                for (int c = 0; c < NPV; ++c) {
+                    t.v[c].x &= m0;
+                    t.v[c].y &= m1;
+                }
+            } else {
+                uint32_t mw[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    mw[h] = (p0 + 2 * h < lim_b ? 0xffffu : 0u) | (p0 + 2 * h + 1 < lim_b ? 0xffff0000u : 0u);
+#pragma unroll
+                for (int c = 0; c < NPV; ++c) {
+                    t.v[c].x &= mw[0];
+                    t.v[c].y &= mw[1];
+                    t.v[c].z &= mw[2];
+                    t.v[c].w &= mw[3];
+                }
             }
         }
         uint16_t hi[8], lo[8];
@@ -901,8 +985,13 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
                                      uint32_t(lo[6]) | (uint32_t(lo[7]) << 16));
 #pragma unroll
         for (int c = 0; c < NPV; ++c) {
-            const uint2 w0 = Fp8<T>::x4(t.v[c].x), w1 = Fp8<T>::x4(t.v[c].y);
-            const uint4 vv = make_uint4(w0.x, w0.y, w1.x, w1.y);
+            uint4 vv;
+            if constexpr (F8) {
+                const uint2 w0 = Fp8<T>::x4(t.v[c].x), w1 = Fp8<T>::x4(t.v[c].y);
+                vv = make_uint4(w0.x, w0.y, w1.x, w1.y);
+            } else {
+                vv = t.v[c];
+            }
             acc[c] = Mfma<T>::qk(vv, phi, acc[c]);
             acc[c] = Mfma<T>::qk(vv, plo, acc[c]);
         }
@@ -924,18 +1013,28 @@ __global__ __launch_bounds__(W * 64) void decode_fp8_blk32_kernel(DecodeArgs a) 
                         int64_t(slot) == phys_l * BS + (n - 1) % BS;
             }
         }
-        KvBlock32<D> X, Y;
         auto blk_of = [&](int k) { return first + (k0 + k) * W; };
-        bool okX = load(X, 0), okY = false;
-        if (k0 == 0 && wave == w_new) quantize_new();   // the codes, for block jl too
-        for (int k = 0; k < cnt; k += 2) {
-            const int k1 = min(k + 1, cnt - 1);
-            okY = load(Y, k1);
-            compute(X, blk_of(k), okX);
-            if (k + 1 >= cnt) break;
-            const int k2 = min(k + 2, cnt - 1);
-            okX = load(X, k2);
-            compute(Y, blk_of(k + 1), okY);
+        if constexpr (F8) {   // two blocks (8 KiB each) in flight
+            KvBlock32<D, F8> X, Y;
+            bool okX = load(X, 0), okY = false;
+            if (k0 == 0 && wave == w_new) quantize_new();   // the new row, for block jl too
+            for (int k = 0; k < cnt; k += 2) {
+                const int k1 = min(k + 1, cnt - 1);
+                okY = load(Y, k1);
+                compute(X, blk_of(k), okX);
+                if (k + 1 >= cnt) break;
+                const int k2 = min(k + 2, cnt - 1);
+                okX = load(X, k2);
+                compute(Y, blk_of(k + 1), okY);
+            }
+        } else {              // one block (16 KiB) in flight
+            KvBlock32<D, F8> X;
+            bool okX = load(X, 0);
+            if (k0 == 0 && wave == w_new) quantize_new();
+            for (int k = 0; k < cnt; ++k) {
+                if (k > 0) okX = load(X, k);
+                compute(X, blk_of(k), okX);
+            }
         }
     }
 
@@ -1403,13 +1502,13 @@ template <typename T, int D, typename OutT, bool F8, int BS>
 hipError_t launch_mfma(const DecodeArgs& a, dim3 grid, hipStream_t s) {
     const size_t lds = sizeof(float) * (2 * kWaves * 16 + size_t(kWaves) * a.group * D);
     const LaunchEvents ev = timer_events(PKV_TIMER_DECODE);
-    if constexpr (F8 && BS == 32) {
+    if constexpr (BS == 32) {
         if (a.part_tiles % 2 == 0) {   // partitions of whole blocks: the whole-block kernel
             if (a.new_k)
-                hipExtLaunchKernelGGL((decode_fp8_blk32_kernel<T, D, OutT, kWaves, true>), grid,
+                hipExtLaunchKernelGGL((decode_blk32_kernel<T, D, OutT, kWaves, true, F8>), grid,
                                       dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
             else
-                hipExtLaunchKernelGGL((decode_fp8_blk32_kernel<T, D, OutT, kWaves, false>), grid,
+                hipExtLaunchKernelGGL((decode_blk32_kernel<T, D, OutT, kWaves, false, F8>), grid,
                                       dim3(kWaves * 64), lds, s, ev.start, ev.stop, 0, a);
             return hipGetLastError();
         }

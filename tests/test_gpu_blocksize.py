@@ -1,16 +1,18 @@
 """GPU parity at block sizes 8 and 32 (the default 16 is covered everywhere else).
 
 "vLLM ve Triton ile maliyet optimizasyonu" (the paragraph on the costs of PagedAttention)
-names the block size as a tuning knob. The kernels keep their 16-token tile at every block
-size: a tile is half of a 32-token block, or two 8-token blocks. Checked here, against the
-oracle on the same seeded inputs:
+names the block size as a tuning knob. The kernels keep their 16-token tile at 8 tokens per
+block (two blocks per tile) and in the balanced split and partitions of 16-token multiples at
+32 (half a block per tile); the single pass and partitions of whole 32-token blocks walk
+whole blocks. Checked here, against the oracle on the same seeded inputs:
   * slots, block tables and caches bit-exact (16-bit and FP8 caches);
   * decode in the three launch modes (single pass, fixed partitions, including partitions
-    of half a 32-token block, balanced split), fused append, FP8 cache, chunked prefill,
-    with the bars of the 16-token tests;
+    of half a 32-token block, of whole blocks, balanced split), fused append, FP8 cache,
+    chunked prefill, with the bars of the 16-token tests;
   * the same logical K/V packed at 8, 16 and 32 tokens per block: bit-identical outputs
-    (only the addresses the tiles are read from change), including a table width that
-    leaves the last tile's second 8-token block outside the table row.
+    wherever the 16-token tiles are walked (only the addresses they are read from change),
+    including a table width that leaves the last tile's second 8-token block outside the
+    table row; the whole-block walk sums in 32-position steps and meets the oracle bars.
 """
 import dataclasses
 
@@ -76,7 +78,7 @@ def test_slots_tables_and_caches_are_bit_exact(bs, kv, device):
     assert np.array_equal(oracle.raw(gb.v_cache).view(np.uint8), ob.v_cache.view(np.uint8))
 
 
-@pytest.mark.parametrize("P", [0, 16, 48, AUTO], ids=["single", "p16", "p48", "auto"])
+@pytest.mark.parametrize("P", [0, 16, 48, 64, AUTO], ids=["single", "p16", "p48", "p64", "auto"])
 @pytest.mark.parametrize("name", list(SHAPES))
 @pytest.mark.parametrize("bs", [8, 32])
 def test_decode_matches_oracle(bs, name, P, device):
@@ -130,8 +132,8 @@ def test_bs8_decode_over_caches_past_2gib(P, kv, device):
     torch.cuda.empty_cache()
 
 
-# at 32 tokens per block, FP8 caches walk whole blocks (single pass, partitions of whole
-# blocks) or 16-token tiles (partitions of 16 tokens): both paths are covered
+# at 32 tokens per block, caches are walked in whole blocks (single pass, partitions of
+# whole blocks) or 16-token tiles (partitions of 16 tokens): both paths are covered
 @pytest.mark.parametrize("P", [0, 16, 32, AUTO], ids=["single", "p16", "p32", "auto"])
 @pytest.mark.parametrize("bs", [8, 32])
 def test_fp8_decode_matches_oracle(bs, P, device):
@@ -170,12 +172,14 @@ def test_fused_append_matches_oracle(bs, P, kv, device):
                 f"append {kv} bs {bs} P {P}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("append", [False, True], ids=["decode", "append"])
 @pytest.mark.parametrize("name", ["bf16-d128-g16", "bf16-d64-g1"])
-def test_fp8_whole_blocks_at_group_size_extremes(name, append, device):
-    """The whole-block kernel (FP8 at 32 tokens per block, single pass) with the largest
-    and the smallest GQA group, plain and with the fused append."""
-    w = _fp8(_w(name, 32))
+def test_whole_blocks_at_group_size_extremes(name, append, kv, device):
+    """The whole-block kernel (32 tokens per block, single pass) with the largest and the
+    smallest GQA group, plain and with the fused append, over 16-bit and FP8 caches."""
+    w = _w(name, 32)
+    w = _fp8(w) if kv == "fp8" else w
     ob = paged_batch.build(w, lens=LENS)
     gb = gpu_batch.build(ob, device, write_new=not append)
     B, Hq, d = gb.q.shape
@@ -262,9 +266,10 @@ def test_decode_is_bit_identical_across_block_sizes(P, kv, device):
     ref = _oracle_decode(ob, w)
     check_close(outs[1].double().numpy(), ref, w.dtype, "bs 16")
     assert torch.equal(outs[0], outs[1])
-    if kv == "fp8" and P != AUTO:
-        # an FP8 cache at 32 tokens per block walks whole blocks (32-position steps): the
-        # same values summed in another order, so it is held to the oracle's bars instead
+    if P != AUTO:
+        # at 32 tokens per block the single pass and partitions of whole blocks walk whole
+        # blocks (32-position steps): the same values summed in another order, so they are
+        # held to the oracle's bars instead
         check_close(outs[2].double().numpy(), ref, w.dtype, "bs 32")
     else:
         assert torch.equal(outs[2], outs[1])

@@ -6,7 +6,8 @@ time (one id per lane) and walks the segment before reading the next. A context 
 wave's second segment past:
   * 64 x 4 waves x 16 tokens = 4,096 tokens in the single-pass decode (and in a fixed
     partition longer than that);
-  * 64 x 4 x 32 = 8,192 tokens in the FP8 whole-block decode at 32 tokens per block.
+  * 64 x 4 x 32 = 8,192 tokens in the whole-block decode at 32 tokens per block (FP8 and
+    bf16 caches).
 The lengths below put the newest token's tile in segment 1, 2 and 8 of the wave holding
 it, so the fused append's substitution of the new row (decided per segment) runs there
 too. The prefill kernel reads the ids of each 64-key stage as it stages it; its cases go
@@ -39,14 +40,15 @@ W = workloads.WORKLOADS
 # list, i.e. segment index // 64: 4097 -> 1, 8193 -> 2, 9001 -> 2, 34000 -> 8. 4096 fills
 # exactly one segment per wave; the short rows share the launch with the long ones.
 LONG = [4097, 9001, 34000, 4096, 8193, 300, 1, 0]
-# 32-token blocks, FP8 whole blocks: newest block jb = (n - 1) // 32 in segment
+# 32-token blocks, whole blocks: newest block jb = (n - 1) // 32 in segment
 # ((jb - jb % 4) // 4) // 64: 8193 -> 1, 9001 -> 1, 34000 -> 4, 8192 fills one segment.
-LONG_FP8_BS32 = [8193, 9001, 34000, 8192, 700, 1]
+LONG_BS32 = [8193, 9001, 34000, 8192, 700, 1]
 
 SHAPE_8B = dataclasses.replace(W["llama8b"], num_blocks=0)
 SHAPE_70B = dataclasses.replace(W["llama70b"], num_blocks=0)
 SHAPE_FP8_BS32 = dataclasses.replace(W["llama8b_fp8"], num_blocks=0, block_size=32)
 SHAPE_FP8 = dataclasses.replace(W["llama8b_fp8"], num_blocks=0)
+SHAPE_8B_BS32 = dataclasses.replace(W["llama8b"], num_blocks=0, block_size=32)
 
 
 @pytest.fixture(scope="module")
@@ -80,7 +82,7 @@ def _decode(gb, w, P, append=None, plan=False):
 
 # (shape, lengths, partition size, host plan): the single pass with and without the plan,
 # fixed partitions of 8,192 and 16,384 tokens (two and four segments per wave inside one
-# partition; the FP8 whole-block kernel takes 16,384 for two), fixed partitions of 512 and
+# partition; the whole-block kernel takes 16,384 for two), fixed partitions of 512 and
 # 1,024 tokens, where the table holds enough partitions (67 and 34 at 34,000 tokens) for
 # one partition per wave (also over an FP8 cache), the balanced split, and the 70B shape
 # (G = 8, fp16)
@@ -88,8 +90,10 @@ DECODE_CASES = [("8b", LONG, 0, True), ("8b", LONG, 0, False), ("8b", LONG, 8192
                 ("8b", LONG, 16384, False), ("8b", LONG, 512, False), ("8b", LONG, AUTO, False),
                 ("70b", LONG, 0, True), ("70b", LONG, 8192, False), ("70b", LONG, 1024, False),
                 ("fp8", LONG, 512, False),
-                ("fp8-bs32", LONG_FP8_BS32, 0, True), ("fp8-bs32", LONG_FP8_BS32, 16384, False)]
-SHAPES = {"8b": SHAPE_8B, "70b": SHAPE_70B, "fp8": SHAPE_FP8, "fp8-bs32": SHAPE_FP8_BS32}
+                ("fp8-bs32", LONG_BS32, 0, True), ("fp8-bs32", LONG_BS32, 16384, False),
+                ("8b-bs32", LONG_BS32, 0, True), ("8b-bs32", LONG_BS32, 16384, False)]
+SHAPES = {"8b": SHAPE_8B, "70b": SHAPE_70B, "fp8": SHAPE_FP8, "fp8-bs32": SHAPE_FP8_BS32,
+          "8b-bs32": SHAPE_8B_BS32}
 
 
 def _ids(cases):
@@ -104,7 +108,7 @@ def batches():
     def get(shape):
         if shape not in cache:
             w = SHAPES[shape]
-            lens = LONG_FP8_BS32 if shape == "fp8-bs32" else LONG
+            lens = LONG_BS32 if shape.endswith("bs32") else LONG
             ob = paged_batch.build(w, lens=lens, seed_stream=5)
             cache[shape] = (ob, _oracle_decode(ob, w))
         return cache[shape]
@@ -121,8 +125,9 @@ def test_long_decode_matches_oracle(shape, lens, P, plan, device, batches):
 
 
 APPEND_CASES = [("8b", LONG, 0, True), ("8b", LONG, 0, False), ("8b", LONG, 8192, False), ("8b", LONG, 512, False),
-                ("70b", LONG, 0, True), ("fp8-bs32", LONG_FP8_BS32, 0, True),
-                ("fp8-bs32", LONG_FP8_BS32, 16384, False)]
+                ("70b", LONG, 0, True), ("fp8-bs32", LONG_BS32, 0, True),
+                ("fp8-bs32", LONG_BS32, 16384, False), ("8b-bs32", LONG_BS32, 0, True),
+                ("8b-bs32", LONG_BS32, 16384, False)]
 
 
 @pytest.mark.parametrize("shape,lens,P,plan", APPEND_CASES, ids=_ids(APPEND_CASES))

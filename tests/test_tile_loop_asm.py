@@ -148,7 +148,7 @@ def test_decode_kernels_keep_tiles_in_registers(src, asm16):
     """No decode kernel uses scratch memory: tiles, queries and the new token's rows stay in
     registers (a select between two such arrays, for one, would make the compiler keep
     both in scratch and load through a pointer, with a wait for every tile). Every block
-    size's translation unit, the FP8 whole-block kernel included."""
+    size's translation unit, the whole-block kernels included."""
     asm = asm16 if src == "decode.hip" else _asm(src)
     names = re.findall(r"^(_ZN3pkv\w*decode\w+):", asm, re.M)
     assert names
