@@ -679,10 +679,10 @@ template <int D> struct KvBlock32<D, false> {
     uint4 v[D / 16];    // positions 8 quad .. + 7 of dimension 16 c + col
 };
 
-// A wave keeps 16 KiB of blocks in flight: two FP8 blocks, or one 16-bit block. On MI355X
-// (8B batch at 32 tokens per block, bf16) two 16-bit blocks per wave, 64 MiB in flight over
-// the chip, took 59.1 us per launch and one 55.6; a gather of the 16-token tiles is also
-// fastest at 16-32 MiB in flight.
+// A wave keeps one block in flight (16 KiB at 16 bits, 8 KiB of codes). On MI355X, 8B
+// batch at 32 tokens per block: bf16 55.6 us per launch against 59.1 with two blocks per
+// wave (64 MiB in flight over the chip; a gather of the 16-token tiles is fastest at 16-32
+// MiB), FP8 30.2 against 31.4-32.3.
 template <typename T, int D, typename OutT, int W, bool Append, bool F8>
 __global__ __launch_bounds__(W * 64) void decode_blk32_kernel(DecodeArgs a) {
     static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
@@ -1014,27 +1014,12 @@ __global__ __launch_bounds__(W * 64) void decode_blk32_kernel(DecodeArgs a) {
             }
         }
         auto blk_of = [&](int k) { return first + (k0 + k) * W; };
-        if constexpr (F8) {   // two blocks (8 KiB each) in flight
-            KvBlock32<D, F8> X, Y;
-            bool okX = load(X, 0), okY = false;
-            if (k0 == 0 && wave == w_new) quantize_new();   // the new row, for block jl too
-            for (int k = 0; k < cnt; k += 2) {
-                const int k1 = min(k + 1, cnt - 1);
-                okY = load(Y, k1);
-                compute(X, blk_of(k), okX);
-                if (k + 1 >= cnt) break;
-                const int k2 = min(k + 2, cnt - 1);
-                okX = load(X, k2);
-                compute(Y, blk_of(k + 1), okY);
-            }
-        } else {              // one block (16 KiB) in flight
-            KvBlock32<D, F8> X;
-            bool okX = load(X, 0);
-            if (k0 == 0 && wave == w_new) quantize_new();
-            for (int k = 0; k < cnt; ++k) {
-                if (k > 0) okX = load(X, k);
-                compute(X, blk_of(k), okX);
-            }
+        KvBlock32<D, F8> X;   // one block in flight
+        bool okX = load(X, 0);
+        if (k0 == 0 && wave == w_new) quantize_new();   // the new row, for block jl too
+        for (int k = 0; k < cnt; ++k) {
+            if (k > 0) okX = load(X, k);
+            compute(X, blk_of(k), okX);
         }
     }
 
