@@ -41,7 +41,10 @@
  * K keeps 16-byte groups of x dimensions per token together, V keeps the BS tokens
  * of each dimension together. Both match the operand layout of the gfx950 matrix
  * instructions, so the kernels load tiles straight into registers; they walk the
- * context in 16-token tiles, one block, half a block (BS = 32) or two blocks (BS = 8).
+ * context in 16-token tiles (one block, half a block at BS = 32, two blocks at BS = 8),
+ * except the decode at BS = 32 in the single pass and in partitions of whole blocks,
+ * which walks whole blocks (results equal to fp32 summation order, not bit for bit,
+ * to those at 8 and 16).
  * A slot is physical_block * BS + row. Every call that takes block_size accepts 8, 16
  * or 32 (EINVAL otherwise); the caches, tables and slots passed must use that size.
  */
