@@ -125,6 +125,7 @@ def test_long_decode_matches_oracle(shape, lens, P, plan, device, batches):
 
 
 APPEND_CASES = [("8b", LONG, 0, True), ("8b", LONG, 0, False), ("8b", LONG, 8192, False), ("8b", LONG, 512, False),
+                ("8b", LONG, AUTO, False), ("70b", LONG, AUTO, False), ("8b-bs32", LONG_BS32, AUTO, False),
                 ("70b", LONG, 0, True), ("fp8-bs32", LONG_BS32, 0, True),
                 ("fp8-bs32", LONG_BS32, 16384, False), ("8b-bs32", LONG_BS32, 0, True),
                 ("8b-bs32", LONG_BS32, 16384, False)]
